@@ -1,0 +1,217 @@
+/*
+ * moe_layer.h - C ABI of libmoelayer.so: one GPU's share of an
+ * expert-parallel Mixture-of-Experts layer on AMD Instinct MI355X (gfx950).
+ *
+ * The layer (page "OverlapAdvisor: Modeling and Adapting Computation-
+ * Communication Overlap for Distributed MoE Serving", section 2.1: each token
+ * activates only its top-k experts; dispatch routes tokens to experts and
+ * combine returns the outputs to their origin) is split into the calls
+ *
+ *   moe_route        top-k softmax gate over router logits
+ *   moe_dispatch     expert-major permutation of the local (token, slot)
+ *                    pairs plus the gather of their activation rows
+ *   moe_grouped_ffn  gated SwiGLU FFN of every local expert over its segment
+ *   moe_combine      gate-weighted sum back to token order (+ shared expert)
+ *   moe_layer        all of the above in one call
+ *
+ * plus moe_quantize_fp8 (block-FP8 conversion of bf16 weights at load time and
+ * of activations) and the helpers moe_workspace_bytes / moe_status_str.
+ *
+ * Conventions for every call
+ *  - Problem sizes follow the pages' workload tuple (tokens, hidden size H,
+ *    experts E, top-k, intermediate size I) plus the local expert range
+ *    [expert_begin, expert_begin + num_local) of this rank (moe_problem).
+ *  - Every array argument is a DEVICE pointer to caller-owned memory, row
+ *    major, 16-byte aligned.  The library never allocates, keeps no state
+ *    between calls, is reentrant, and never synchronises the host: all work
+ *    is enqueued on `stream` (a hipStream_t; NULL = the default stream), and
+ *    data-dependent sizes (per-expert counts, tile lists) stay on the device.
+ *  - Arguments are validated before anything is enqueued.  On any error
+ *    nothing is enqueued and outputs are untouched.  A launch failure returns
+ *    MOE_ERR_HIP; faults of kernels surface at the caller's next sync.
+ *  - num_tokens == 0 is valid: MOE_OK, nothing enqueued.
+ *  - Logits must be finite (NaN/Inf logits give unspecified, but in-bounds,
+ *    routing).
+ *  - Capacity: the permuted buffers hold N_cap = T * min(k, E_L) rows; the
+ *    number of valid rows is offsets[E_L] on the device.
+ *
+ * Supported sizes: 1 <= E <= 1024, 1 <= k <= min(E, 32), 1 <= E_L <= 1024,
+ * 0 <= e_lo, e_lo + E_L <= E, 0 <= T <= 2^24, H % 128 == 0, I % 128 == 0
+ * (and shared_inter % 128 == 0), H, I <= 65536.
+ */
+#ifndef MOE_LAYER_H
+#define MOE_LAYER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,  /* null pointer, size out of range, misalignment */
+  MOE_ERR_UNSUPPORTED = 2,  /* valid request this build does not implement   */
+  MOE_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required     */
+  MOE_ERR_HIP = 4           /* a HIP launch or runtime call failed            */
+} moe_status;
+
+typedef enum {
+  MOE_BF16 = 0,      /* bf16 weights, bf16 GEMM activations                  */
+  MOE_FP8_E4M3 = 1   /* OCP E4M3FN weights with one fp32 scale per 128 x 128
+                        block; GEMM activations E4M3 with one fp32 scale per
+                        token per 128 consecutive elements                   */
+} moe_dtype;
+
+/* The workload tuple of one rank. */
+typedef struct {
+  int32_t num_tokens;    /* T: tokens in the batch                            */
+  int32_t hidden;        /* H: model hidden size                              */
+  int32_t num_experts;   /* E: routed experts of the whole layer              */
+  int32_t top_k;         /* k: experts per token                              */
+  int32_t expert_begin;  /* e_lo: first local expert (global id)              */
+  int32_t num_local;     /* E_L: local experts, global ids [e_lo, e_lo+E_L)   */
+  int32_t inter;         /* I: expert FFN intermediate size                   */
+  int32_t shared_inter;  /* I_s: shared-expert intermediate size, 0 = none    */
+  int32_t dtype;         /* moe_dtype                                          */
+} moe_problem;
+
+/* Expert weights, device pointers, K-contiguous ("[out, in]" row major).
+ *   w13  [E_L, 2I, H]: rows 0..I-1 gate projection, rows I..2I-1 up projection
+ *   w2   [E_L, H, I]:  down projection
+ *   ws13 [2 I_s, H], ws2 [H, I_s]: shared expert (NULL when I_s == 0)
+ * Element type: bf16 for MOE_BF16, E4M3 bytes for MOE_FP8_E4M3.
+ * fp8 only, fp32 block scales (NULL for bf16):
+ *   w13_scale [E_L, 2I/128, H/128], w2_scale [E_L, H/128, I/128],
+ *   ws13_scale [2 I_s/128, H/128],  ws2_scale [H/128, I_s/128].            */
+typedef struct {
+  const void* w13;
+  const void* w2;
+  const void* ws13;
+  const void* ws2;
+  const float* w13_scale;
+  const float* w2_scale;
+  const float* ws13_scale;
+  const float* ws2_scale;
+} moe_weights;
+
+/* Top-k gate.  Page "OverlapAdvisor ...", section 2.1 (top-k experts per
+ * token); the weights are the softmax of the router logits renormalised over
+ * the selected experts.
+ *   logits   [T, E] fp32 (input)
+ *   topk_ids [T, k] int32 (output): the k experts first in the order
+ *            (logit descending, expert id ascending; -0.0 == +0.0)
+ *   topk_w   [T, k] fp32 (output): exp(l_s - l_0) / sum_j exp(l_j - l_0)
+ * Routing is over all E experts; locality plays no part here.            */
+moe_status moe_route(const moe_problem* p, const float* logits,
+                     int32_t* topk_ids, float* topk_w, void* stream);
+
+/* Dispatch: permutation plus gather.  Page "CascadeEP: Asynchronous Expert
+ * Execution for MoE Prefill under Attention Imbalance", Appendix C, "Grouped
+ * FFN invocations" (per-expert row offsets from the selected counts, rows
+ * grouped by expert, activations packed with their quantisation metadata, an
+ * inverse map to token and routing slot); page "OverlapAdvisor ...", section
+ * 4.2.1 (permute groups tokens by expert).
+ *   x          [T, H] bf16 (input)
+ *   topk_ids   [T, k] int32 (input, e.g. from moe_route).  A slot that repeats
+ *              an expert already picked by an earlier slot of the same token
+ *              is ignored (treated as non-local).
+ *   counts     [E_L] int32: local pairs per local expert
+ *   offsets    [E_L + 1] int32: exclusive scan of counts; N = offsets[E_L]
+ *   row_token  [N_cap] int32, row_slot [N_cap] int32: token and slot of row j
+ *              (rows j >= N are left untouched)
+ *   token_slot_row [T, k] int32: row of pair (t, s), -1 if not local
+ *   x_perm     [N_cap, H]: row j = x[row_token[j]]; bf16, or for
+ *              MOE_FP8_E4M3 the E4M3 codes of that row with
+ *   x_perm_scale [N_cap, H/128] fp32 (fp8 only; NULL for bf16): scale of each
+ *              128-element group, amax/448 (1 for an all-zero group); code =
+ *              round-to-nearest-even(v / scale) saturated to +-448.
+ * Rows are ordered by local expert, then by token.  Bit-exact and
+ * deterministic.  Workspace: moe_workspace_bytes(p, MOE_STAGE_DISPATCH).   */
+moe_status moe_dispatch(const moe_problem* p, const void* x,
+                        const int32_t* topk_ids, int32_t* counts,
+                        int32_t* offsets, int32_t* row_token,
+                        int32_t* row_slot, int32_t* token_slot_row,
+                        void* x_perm, float* x_perm_scale, void* ws,
+                        size_t ws_bytes, void* stream);
+
+/* Grouped gated-SwiGLU FFN.  Page "OverlapAdvisor ...", section 4.2.2 and
+ * Eq. 8 (m = 2 first-layer matrices for a gated MLP; the up GroupGEMM is
+ * 2 m H I FLOPs per row, the down GroupGEMM 2 H I), Table 6 (gated SwiGLU);
+ * page "CascadeEP ...", Appendix C (the two expert GEMMs with the activation
+ * and quantisation between them, in stream order).
+ * For every local expert e and row j in [offsets[e], offsets[e+1]):
+ *   h[j]      = silu(x_perm[j] . W_gate,e^T) * (x_perm[j] . W_up,e^T)   [I]
+ *   y_perm[j] = h[j] . W2_e^T                                          [H]
+ * with silu(a) = a / (1 + exp(-a)), fp32 accumulation.
+ *   x_perm, x_perm_scale, offsets: as produced by moe_dispatch
+ *   h          [N_cap, I] (optional, NULL = kept in the workspace): bf16,
+ *              or E4M3 with h_scale [N_cap, I/128] fp32 for MOE_FP8_E4M3
+ *   y_perm     [N_cap, H] bf16 (output)
+ * Routing weights are NOT applied here (moe_combine applies them).
+ * Only rows j < offsets[E_L] are read or written.  With E_L = 1 and
+ * offsets = {0, T} this is a dense SwiGLU FFN (how a shared expert is run).
+ * Workspace: moe_workspace_bytes(p, MOE_STAGE_FFN).                        */
+moe_status moe_grouped_ffn(const moe_problem* p, const void* x_perm,
+                           const float* x_perm_scale, const int32_t* offsets,
+                           const moe_weights* w, void* h, float* h_scale,
+                           void* y_perm, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/* Combine.  Page "CascadeEP ...", Appendix C, "Output return and combine"
+ * (each routed contribution weighted by its routing coefficient exactly once,
+ * accumulated at the origin and added to the shared-expert output); page
+ * "OverlapAdvisor ...", section 4.2.1 (unpermute restores token order).
+ *   y[t] = sum over slots s with token_slot_row[t,s] >= 0, in slot order, of
+ *          topk_w[t,s] * y_perm[token_slot_row[t,s]]  (+ shared_out[t])
+ * accumulated in fp32 and rounded to bf16 once; a token with no local slot
+ * gets 0 (+ shared_out[t]).  Deterministic (no atomics).
+ *   y_perm [N_cap, H] bf16, token_slot_row [T, k] int32, topk_w [T, k] fp32,
+ *   shared_out [T, H] bf16 or NULL, y [T, H] bf16 (output).               */
+moe_status moe_combine(const moe_problem* p, const void* y_perm,
+                       const int32_t* token_slot_row, const float* topk_w,
+                       const void* shared_out, void* y, void* stream);
+
+/* The whole layer: route, dispatch, grouped FFN, shared expert (when
+ * shared_inter > 0, always on with weight 1) and combine.  Equal to the
+ * composed calls (bit-identical routing and permutation).
+ *   logits [T, E] fp32, x [T, H] bf16, y [T, H] bf16 (output).
+ * Workspace: moe_workspace_bytes(p, MOE_STAGE_LAYER).                      */
+moe_status moe_layer(const moe_problem* p, const float* logits, const void* x,
+                     const moe_weights* w, void* y, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/* Block-FP8 quantisation (page "OverlapAdvisor ...", section 4.4: BF16
+ * checkpoints are quantised to block-FP8 at load time; the same rule makes
+ * the per-token activation scales).  For each block_rows x 128 block of the
+ * [rows, cols] bf16 matrix `src`: scale = amax / 448 in fp32 (1 if the block
+ * is all zero), code = round-to-nearest-even(v / scale) (fp32 division),
+ * saturated to +-448, as OCP E4M3FN bytes.
+ *   block_rows: 1 (activations) or 128 (weights); cols % 128 == 0
+ *   codes [rows, cols] uint8, scales [ceil(rows/block_rows), cols/128] fp32
+ * A batch of `batch` equally shaped matrices (e.g. all experts' W13) is
+ * processed at once: src, codes and scales advance by one matrix each.     */
+moe_status moe_quantize_fp8(const void* src, int64_t batch, int64_t rows,
+                            int64_t cols, int32_t block_rows, void* codes,
+                            float* scales, void* stream);
+
+#define MOE_STAGE_LAYER 0
+#define MOE_STAGE_DISPATCH 1
+#define MOE_STAGE_FFN 2
+
+/* Bytes of workspace a stage needs for problem p (0 if p is invalid). */
+size_t moe_workspace_bytes(const moe_problem* p, int32_t stage);
+
+/* Static, human-readable name of a status code. */
+const char* moe_status_str(moe_status s);
+
+/* MOE_ABI_VERSION of the built library. */
+int32_t moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_LAYER_H */

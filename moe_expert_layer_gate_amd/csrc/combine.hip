@@ -1,0 +1,81 @@
+// Combine: gate-weighted sum of a token's expert outputs back in token order.
+//
+// Page "CascadeEP: Asynchronous Expert Execution for MoE Prefill under
+// Attention Imbalance", Appendix C, "Output return and combine": every routed
+// contribution is weighted by its routing coefficient exactly once, the
+// contributions are summed at the token's origin, and the shared-expert output
+// is added.  Page "OverlapAdvisor ...", section 4.2.1: unpermute restores the
+// token order.
+//
+// One wavefront per token gathers the token's (at most k) expert rows through
+// the inverse map -- a gather, not a scatter-add, so no atomics and a
+// deterministic result.  Each lane accumulates 8 columns at a time in fp32, in
+// slot order, and rounds to bf16 once.  All accesses are 16 bytes wide.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+__device__ __forceinline__ void unpack8(const uint4 v, float* f) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
+__global__ __launch_bounds__(256) void combine_kernel(
+    const uint4* __restrict__ y_perm, const int32_t* __restrict__ token_slot_row,
+    const float* __restrict__ topk_w, const uint4* __restrict__ shared_out, int T, int k,
+    int chunks, uint4* __restrict__ y) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int lane = lane_id();
+  // Slot rows and weights of this token: lane s < k holds slot s.
+  int my_row = -1;
+  float my_w = 0.0f;
+  if (lane < k) {
+    my_row = token_slot_row[static_cast<int64_t>(t) * k + lane];
+    my_w = topk_w[static_cast<int64_t>(t) * k + lane];
+  }
+  for (int c = lane; c < chunks; c += kWave) {
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+    for (int s = 0; s < k; ++s) {
+      const int r = __shfl(my_row, s);
+      if (r < 0) continue;  // uniform over the wave
+      const float ws = __shfl(my_w, s);
+      float f[8];
+      unpack8(y_perm[static_cast<int64_t>(r) * chunks + c], f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += ws * f[i];
+    }
+    if (shared_out) {
+      float f[8];
+      unpack8(shared_out[static_cast<int64_t>(t) * chunks + c], f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += f[i];
+    }
+    uint4 o;
+    o.x = pack_bf16x2(acc[0], acc[1]);
+    o.y = pack_bf16x2(acc[2], acc[3]);
+    o.z = pack_bf16x2(acc[4], acc[5]);
+    o.w = pack_bf16x2(acc[6], acc[7]);
+    y[static_cast<int64_t>(t) * chunks + c] = o;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const void* y_perm, const int32_t* token_slot_row, const float* topk_w,
+                          const void* shared_out, int T, int k, int H, void* y, hipStream_t s) {
+  hipLaunchKernelGGL(combine_kernel, dim3(ceil_div(T, 4)), dim3(256), 0, s,
+                     static_cast<const uint4*>(y_perm), token_slot_row, topk_w,
+                     static_cast<const uint4*>(shared_out), T, k, H / 8, static_cast<uint4*>(y));
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,292 @@
+// Dispatch: the expert-major permutation of the local (token, slot) pairs and
+// the gather of their activation rows.
+//
+// Page "CascadeEP: Asynchronous Expert Execution for MoE Prefill under
+// Attention Imbalance", Appendix C, "Grouped FFN invocations": per-expert row
+// offsets from the selected token counts, rows grouped contiguously by expert,
+// activations packed with their quantisation metadata, and an inverse map from
+// each row to its token and routing slot.  Page "OverlapAdvisor ...", section
+// 4.2.1: permute groups tokens by expert.
+//
+// The permutation is a stable counting sort done in three launches, with no
+// float and no order-dependent atomics (the result is deterministic):
+//   1. count:   each block of 256 tokens builds, in LDS, one 256-bit mask per
+//               local expert (bit i = token i of the block picked it) and
+//               writes the popcounts as its per-expert histogram;
+//   2. scan:    one block turns the [blocks x E_L] histogram into per-block
+//               bases (exclusive scan over blocks) and the expert offsets
+//               (exclusive scan over experts);
+//   3. scatter: each block rebuilds its masks; a pair's rank inside its block
+//               is the popcount of the mask bits below its token, so rows come
+//               out in token order inside every expert segment.
+// A slot that repeats an expert already picked by an earlier slot of the
+// same token is skipped, which keeps every (token, expert) at most once and so
+// every position in range whatever ids the caller passes.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int kTokBlock = 256;  // tokens per count/scatter block
+constexpr int kMaskWords = kTokBlock / 32;
+
+// Local expert of slot s of a token, or -1 (non-local or repeated expert).
+__device__ __forceinline__ int local_expert(const int32_t* ids, int s, int e_lo, int E_L) {
+  const int id = ids[s];
+  for (int q = 0; q < s; ++q)
+    if (ids[q] == id) return -1;
+  const int e = id - e_lo;
+  return (e >= 0 && e < E_L) ? e : -1;
+}
+
+// Build the per-expert token masks of block b in LDS.
+__device__ __forceinline__ void build_masks(uint32_t* mask, const int32_t* __restrict__ topk_ids,
+                                            int T, int k, int e_lo, int E_L, int b) {
+  for (int i = threadIdx.x; i < E_L * kMaskWords; i += blockDim.x) mask[i] = 0u;
+  __syncthreads();
+  const int t = b * kTokBlock + threadIdx.x;
+  if (t < T) {
+    int32_t ids[32];
+    for (int s = 0; s < k; ++s) ids[s] = topk_ids[static_cast<size_t>(t) * k + s];
+    for (int s = 0; s < k; ++s) {
+      const int e = local_expert(ids, s, e_lo, E_L);
+      if (e >= 0) atomicOr(&mask[e * kMaskWords + (threadIdx.x >> 5)], 1u << (threadIdx.x & 31));
+    }
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kTokBlock) void index_count_kernel(
+    const int32_t* __restrict__ topk_ids, int T, int k, int e_lo, int E_L,
+    int32_t* __restrict__ blk_hist) {
+  extern __shared__ uint32_t mask[];
+  build_masks(mask, topk_ids, T, k, e_lo, E_L, blockIdx.x);
+  for (int e = threadIdx.x; e < E_L; e += blockDim.x) {
+    int c = 0;
+#pragma unroll
+    for (int w = 0; w < kMaskWords; ++w) c += __popc(mask[e * kMaskWords + w]);
+    blk_hist[static_cast<size_t>(blockIdx.x) * E_L + e] = c;
+  }
+}
+
+__global__ __launch_bounds__(1024) void index_scan_kernel(
+    const int32_t* __restrict__ blk_hist, int nblk, int E_L,
+    int32_t* __restrict__ blk_base, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets) {
+  // E_L <= 1024 = blockDim.x: one expert per thread.
+  const int e = threadIdx.x;
+  int run = 0;
+  if (e < E_L) {
+    for (int b = 0; b < nblk; ++b) {
+      const int c = blk_hist[static_cast<size_t>(b) * E_L + e];
+      blk_base[static_cast<size_t>(b) * E_L + e] = run;
+      run += c;
+    }
+  }
+  int total;
+  const int off = block_exclusive_scan(e < E_L ? run : 0, &total);
+  if (e < E_L) {
+    counts[e] = run;
+    offsets[e] = off;
+  }
+  if (e == 0) offsets[E_L] = total;
+}
+
+__global__ __launch_bounds__(kTokBlock) void index_scatter_kernel(
+    const int32_t* __restrict__ topk_ids, int T, int k, int e_lo, int E_L,
+    const int32_t* __restrict__ blk_base, const int32_t* __restrict__ offsets,
+    int32_t* __restrict__ row_token, int32_t* __restrict__ row_slot,
+    int32_t* __restrict__ token_slot_row) {
+  extern __shared__ uint32_t mask[];
+  build_masks(mask, topk_ids, T, k, e_lo, E_L, blockIdx.x);
+  const int t = blockIdx.x * kTokBlock + threadIdx.x;
+  if (t >= T) return;
+  const int wi = threadIdx.x >> 5;
+  const uint32_t below = (1u << (threadIdx.x & 31)) - 1u;
+  int32_t ids[32];
+  for (int s = 0; s < k; ++s) ids[s] = topk_ids[static_cast<size_t>(t) * k + s];
+  for (int s = 0; s < k; ++s) {
+    const int e = local_expert(ids, s, e_lo, E_L);
+    int pos = -1;
+    if (e >= 0) {
+      const uint32_t* m = mask + e * kMaskWords;
+      int rank = __popc(m[wi] & below);
+      for (int w = 0; w < wi; ++w) rank += __popc(m[w]);
+      pos = offsets[e] + blk_base[static_cast<size_t>(blockIdx.x) * E_L + e] + rank;
+      row_token[pos] = t;
+      row_slot[pos] = s;
+    }
+    token_slot_row[static_cast<size_t>(t) * k + s] = pos;
+  }
+}
+
+// Row gather of bf16 activations: dst[j] = src[rows[j]] for j < *n_rows
+// (rows == nullptr: identity).  One wavefront per row, 16-byte accesses.
+__global__ __launch_bounds__(256) void gather_rows_bf16_kernel(
+    const uint4* __restrict__ src, const int32_t* __restrict__ rows,
+    const int32_t* __restrict__ n_rows, int n_rows_host, int chunks_per_row,
+    uint4* __restrict__ dst) {
+  const int n = n_rows ? *n_rows : n_rows_host;
+  const int wpb = blockDim.x >> 6;
+  for (int j = blockIdx.x * wpb + (threadIdx.x >> 6); j < n; j += gridDim.x * wpb) {
+    const int r = rows ? rows[j] : j;
+    const uint4* s = src + static_cast<size_t>(r) * chunks_per_row;
+    uint4* d = dst + static_cast<size_t>(j) * chunks_per_row;
+    for (int c = lane_id(); c < chunks_per_row; c += kWave) d[c] = s[c];
+  }
+}
+
+// Row gather with per-128 group E4M3 quantisation: scale = amax/448 (1 for an
+// all-zero group), code = RNE(v / scale) (IEEE fp32 division) saturated.
+// A group of 128 bf16 is 16 lanes x 8 values; a wave covers 4 groups per step.
+__global__ __launch_bounds__(256) void gather_rows_fp8_kernel(
+    const uint4* __restrict__ src, const int32_t* __restrict__ rows,
+    const int32_t* __restrict__ n_rows, int n_rows_host, int H,
+    uint2* __restrict__ dst, float* __restrict__ dst_scale) {
+  const int n = n_rows ? *n_rows : n_rows_host;
+  const int chunks = H >> 3;  // 8 bf16 per chunk
+  const int groups = H >> 7;
+  const int wpb = blockDim.x >> 6;
+  const int lane = lane_id();
+  for (int j = blockIdx.x * wpb + (threadIdx.x >> 6); j < n; j += gridDim.x * wpb) {
+    const int r = rows ? rows[j] : j;
+    const uint4* s = src + static_cast<size_t>(r) * chunks;
+    uint2* d = dst + static_cast<size_t>(j) * chunks;
+    // chunks is a multiple of 16, so the 16 lanes of a group are all active or
+    // all idle in every step, and the xor-shuffles below stay inside a group.
+    for (int c = lane; c < chunks; c += kWave) {
+      const uint4 v = s[c];
+      float f[8];
+      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __uint_as_float(wv[i] << 16);
+        f[2 * i + 1] = __uint_as_float(wv[i] & 0xFFFF0000u);
+      }
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+      const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+      uint2 q;
+      q.x = f32x4_to_e4m3x4(f[0] / sc, f[1] / sc, f[2] / sc, f[3] / sc);
+      q.y = f32x4_to_e4m3x4(f[4] / sc, f[5] / sc, f[6] / sc, f[7] / sc);
+      d[c] = q;
+      if ((lane & 15) == 0) dst_scale[static_cast<size_t>(j) * groups + (c >> 4)] = sc;
+    }
+  }
+}
+
+// 128 x 128 block quantisation of bf16 matrices (weights at load time).
+// One block of 256 threads per 128 x 128 tile; partial row tiles allowed.
+__global__ __launch_bounds__(256) void quant_blocks_kernel(
+    const uint16_t* __restrict__ src, int64_t rows, int64_t cols,
+    uint8_t* __restrict__ codes, float* __restrict__ scales) {
+  const int64_t mat = blockIdx.z;
+  const int64_t rb = blockIdx.y, cb = blockIdx.x;
+  const int64_t nrb = (rows + 127) / 128, ncb = cols / 128;
+  const uint16_t* s = src + mat * rows * cols;
+  uint8_t* q = codes + mat * rows * cols;
+  // Thread i handles row (i >> 1) of the tile, columns (i & 1) * 64 .. +64.
+  const int64_t r = rb * 128 + (threadIdx.x >> 1);
+  const int64_t c0 = cb * 128 + (threadIdx.x & 1) * 64;
+  const bool valid = r < rows;
+  float f[64];
+  float amax = 0.0f;
+  if (valid) {
+    const uint4* p = reinterpret_cast<const uint4*>(s + r * cols + c0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint4 v = p[i];
+      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f[8 * i + 2 * j] = __uint_as_float(wv[j] << 16);
+        f[8 * i + 2 * j + 1] = __uint_as_float(wv[j] & 0xFFFF0000u);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 64; ++i) amax = fmaxf(amax, fabsf(f[i]));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  __shared__ float wmax[4];
+  if (lane_id() == 0) wmax[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+  if (threadIdx.x == 0) scales[mat * nrb * ncb + rb * ncb + cb] = sc;
+  if (valid) {
+    uint4* d = reinterpret_cast<uint4*>(q + r * cols + c0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint4 o;
+      o.x = f32x4_to_e4m3x4(f[16 * i + 0] / sc, f[16 * i + 1] / sc, f[16 * i + 2] / sc, f[16 * i + 3] / sc);
+      o.y = f32x4_to_e4m3x4(f[16 * i + 4] / sc, f[16 * i + 5] / sc, f[16 * i + 6] / sc, f[16 * i + 7] / sc);
+      o.z = f32x4_to_e4m3x4(f[16 * i + 8] / sc, f[16 * i + 9] / sc, f[16 * i + 10] / sc, f[16 * i + 11] / sc);
+      o.w = f32x4_to_e4m3x4(f[16 * i + 12] / sc, f[16 * i + 13] / sc, f[16 * i + 14] / sc, f[16 * i + 15] / sc);
+      d[i] = o;
+    }
+  }
+}
+
+}  // namespace
+
+size_t index_scratch_bytes(int T, int E_L) {
+  const size_t nblk = static_cast<size_t>(ceil_div(T, kTokBlock));
+  return 2 * nblk * static_cast<size_t>(E_L) * sizeof(int32_t);
+}
+
+hipError_t launch_index_build(const int32_t* topk_ids, int T, int k, int e_lo, int E_L,
+                              int32_t* counts, int32_t* offsets, int32_t* row_token,
+                              int32_t* row_slot, int32_t* token_slot_row,
+                              void* scratch, hipStream_t s) {
+  const int nblk = ceil_div(T, kTokBlock);
+  int32_t* blk_hist = static_cast<int32_t*>(scratch);
+  int32_t* blk_base = blk_hist + static_cast<size_t>(nblk) * E_L;
+  const size_t lds = static_cast<size_t>(E_L) * kMaskWords * sizeof(uint32_t);
+  hipLaunchKernelGGL(index_count_kernel, dim3(nblk), dim3(kTokBlock), lds, s,
+                     topk_ids, T, k, e_lo, E_L, blk_hist);
+  hipLaunchKernelGGL(index_scan_kernel, dim3(1), dim3(1024), 0, s,
+                     blk_hist, nblk, E_L, blk_base, counts, offsets);
+  hipLaunchKernelGGL(index_scatter_kernel, dim3(nblk), dim3(kTokBlock), lds, s,
+                     topk_ids, T, k, e_lo, E_L, blk_base, offsets, row_token, row_slot,
+                     token_slot_row);
+  return hipGetLastError();
+}
+
+static int gather_grid(int64_t max_rows) {
+  const int64_t blocks = (max_rows + 3) / 4;
+  return static_cast<int>(blocks < 8192 ? (blocks > 0 ? blocks : 1) : 8192);
+}
+
+hipError_t launch_gather_bf16(const void* src, const int32_t* rows, const int32_t* n_rows,
+                              int64_t max_rows, int H, void* dst, hipStream_t s) {
+  hipLaunchKernelGGL(gather_rows_bf16_kernel, dim3(gather_grid(max_rows)), dim3(256), 0, s,
+                     static_cast<const uint4*>(src), rows, n_rows, static_cast<int>(max_rows),
+                     H / 8, static_cast<uint4*>(dst));
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_fp8(const void* src, const int32_t* rows, const int32_t* n_rows,
+                             int64_t max_rows, int H, void* dst, float* dst_scale,
+                             hipStream_t s) {
+  hipLaunchKernelGGL(gather_rows_fp8_kernel, dim3(gather_grid(max_rows)), dim3(256), 0, s,
+                     static_cast<const uint4*>(src), rows, n_rows, static_cast<int>(max_rows), H,
+                     static_cast<uint2*>(dst), dst_scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_blocks(const void* src, int64_t batch, int64_t rows, int64_t cols,
+                               void* codes, float* scales, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(cols / 128), static_cast<unsigned>((rows + 127) / 128),
+                  static_cast<unsigned>(batch));
+  hipLaunchKernelGGL(quant_blocks_kernel, grid, dim3(256), 0, s,
+                     static_cast<const uint16_t*>(src), rows, cols,
+                     static_cast<uint8_t*>(codes), scales);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,43 @@
+// Launchers of the library's kernels (internal; the public ABI is in
+// include/moe_layer.h).  Every launcher enqueues on stream `s` and returns
+// the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+                             hipStream_t s);
+
+size_t index_scratch_bytes(int T, int E_L);
+hipError_t launch_index_build(const int32_t* topk_ids, int T, int k, int e_lo, int E_L,
+                              int32_t* counts, int32_t* offsets, int32_t* row_token,
+                              int32_t* row_slot, int32_t* token_slot_row, void* scratch,
+                              hipStream_t s);
+// dst[j] = src[rows[j]] (rows == nullptr: identity) for j < *n_rows, or for
+// j < max_rows when n_rows == nullptr.
+hipError_t launch_gather_bf16(const void* src, const int32_t* rows, const int32_t* n_rows,
+                              int64_t max_rows, int H, void* dst, hipStream_t s);
+hipError_t launch_gather_fp8(const void* src, const int32_t* rows, const int32_t* n_rows,
+                             int64_t max_rows, int H, void* dst, float* dst_scale, hipStream_t s);
+hipError_t launch_quant_blocks(const void* src, int64_t batch, int64_t rows, int64_t cols,
+                               void* codes, float* scales, hipStream_t s);
+
+int64_t max_m_tiles(int64_t n_cap, int E_L);
+hipError_t launch_tile_schedule(const int32_t* offsets, int E_L, int4* info, int32_t* n_tiles,
+                                hipStream_t s);
+hipError_t launch_gemm_bf16(bool swiglu, const void* A, const void* W, void* C, const int4* info,
+                            const int32_t* n_tiles, int64_t max_tiles, int K, int Nout,
+                            int64_t w_expert_stride, hipStream_t s);
+hipError_t launch_gemm_fp8(bool swiglu, const void* A, const float* A_scale, const void* W,
+                           const float* W_scale, void* C, const int4* info,
+                           const int32_t* n_tiles, int64_t max_tiles, int K, int Nout,
+                           int64_t w_expert_stride, int64_t ws_expert_stride, hipStream_t s);
+
+hipError_t launch_combine(const void* y_perm, const int32_t* token_slot_row, const float* topk_w,
+                          const void* shared_out, int T, int k, int H, void* y, hipStream_t s);
+
+
+}  // namespace moe

@@ -1,0 +1,360 @@
+// Host side of the C ABI declared in include/moe_layer.h: argument checks,
+// workspace carving and stage sequencing on the caller's stream.  Nothing here
+// allocates device memory or synchronises the host.
+#include <string.h>
+
+#include "../../include/moe_layer.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+__global__ void fill_offsets_kernel(int32_t* offsets, int n) {
+  if (threadIdx.x == 0) {
+    offsets[0] = 0;
+    offsets[1] = n;
+  }
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Validate the problem; returns MOE_OK or MOE_ERR_INVALID_ARG/UNSUPPORTED.
+moe_status check_problem(const moe_problem* p) {
+  if (!p) return MOE_ERR_INVALID_ARG;
+  const int64_t T = p->num_tokens, H = p->hidden, E = p->num_experts, k = p->top_k,
+                lo = p->expert_begin, EL = p->num_local, I = p->inter, Is = p->shared_inter;
+  if (T < 0 || T > (1 << 24)) return MOE_ERR_INVALID_ARG;
+  if (E < 1 || E > 1024) return MOE_ERR_INVALID_ARG;
+  if (k < 1 || k > E || k > 32) return MOE_ERR_INVALID_ARG;
+  if (EL < 1 || EL > 1024 || lo < 0 || lo + EL > E) return MOE_ERR_INVALID_ARG;
+  if (H < 128 || H > 65536 || H % 128) return MOE_ERR_INVALID_ARG;
+  if (I < 128 || I > 65536 || I % 128) return MOE_ERR_INVALID_ARG;
+  if (Is < 0 || Is > 65536 || Is % 128) return MOE_ERR_INVALID_ARG;
+  if (p->dtype != MOE_BF16 && p->dtype != MOE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+int64_t n_cap(const moe_problem* p) {
+  const int64_t kk = p->top_k < p->num_local ? p->top_k : p->num_local;
+  return static_cast<int64_t>(p->num_tokens) * kk;
+}
+
+bool is_fp8(const moe_problem* p) { return p->dtype == MOE_FP8_E4M3; }
+
+// Bump allocator over the workspace; with base == nullptr it only measures.
+struct Carve {
+  uint8_t* base;
+  size_t used = 0;
+  explicit Carve(void* b) : base(static_cast<uint8_t*>(b)) {}
+  template <typename T>
+  T* take(size_t bytes) {
+    used = (used + 255) & ~size_t(255);
+    T* r = base ? reinterpret_cast<T*>(base + used) : nullptr;
+    used += bytes;
+    return r;
+  }
+};
+
+struct FfnScratch {
+  int4* info;
+  int32_t* n_tiles;
+  void* h;          // [N_cap, I] bf16 or e4m3
+  float* h_scale;   // fp8 only
+  void* h_wide;     // fp8 only: bf16 h before quantisation
+};
+
+FfnScratch carve_ffn(Carve& c, const moe_problem* p) {
+  const int64_t N = n_cap(p), I = p->inter;
+  FfnScratch f{};
+  f.info = c.take<int4>(sizeof(int4) * max_m_tiles(N, p->num_local));
+  f.n_tiles = c.take<int32_t>(sizeof(int32_t));
+  if (is_fp8(p)) {
+    f.h = c.take<void>(N * I);
+    f.h_scale = c.take<float>(sizeof(float) * N * (I / 128));
+    f.h_wide = c.take<void>(2 * N * I);
+  } else {
+    f.h = c.take<void>(2 * N * I);
+  }
+  return f;
+}
+
+struct LayerScratch {
+  int32_t* ids;
+  float* w;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* row_token;
+  int32_t* row_slot;
+  int32_t* tsr;
+  void* x_perm;
+  float* x_perm_scale;
+  void* y_perm;
+  void* index_scratch;
+  FfnScratch ffn;
+  // shared expert
+  int32_t* s_offsets;
+  void* s_x;
+  float* s_x_scale;
+  void* s_out;
+  FfnScratch s_ffn;
+};
+
+moe_problem shared_problem(const moe_problem* p) {
+  moe_problem q = *p;
+  q.num_experts = 1;
+  q.top_k = 1;
+  q.expert_begin = 0;
+  q.num_local = 1;
+  q.inter = p->shared_inter;
+  q.shared_inter = 0;
+  return q;
+}
+
+LayerScratch carve_layer(Carve& c, const moe_problem* p) {
+  const int64_t T = p->num_tokens, k = p->top_k, EL = p->num_local, H = p->hidden;
+  const int64_t N = n_cap(p);
+  LayerScratch s{};
+  s.ids = c.take<int32_t>(4 * T * k);
+  s.w = c.take<float>(4 * T * k);
+  s.counts = c.take<int32_t>(4 * EL);
+  s.offsets = c.take<int32_t>(4 * (EL + 1));
+  s.row_token = c.take<int32_t>(4 * N);
+  s.row_slot = c.take<int32_t>(4 * N);
+  s.tsr = c.take<int32_t>(4 * T * k);
+  s.x_perm = c.take<void>((is_fp8(p) ? 1 : 2) * N * H);
+  s.x_perm_scale = is_fp8(p) ? c.take<float>(4 * N * (H / 128)) : nullptr;
+  s.y_perm = c.take<void>(2 * N * H);
+  s.index_scratch = c.take<void>(index_scratch_bytes(static_cast<int>(T), static_cast<int>(EL)));
+  s.ffn = carve_ffn(c, p);
+  if (p->shared_inter > 0) {
+    const moe_problem q = shared_problem(p);
+    s.s_offsets = c.take<int32_t>(8);
+    if (is_fp8(p)) {
+      s.s_x = c.take<void>(T * H);
+      s.s_x_scale = c.take<float>(4 * T * (H / 128));
+    }
+    s.s_out = c.take<void>(2 * T * H);
+    s.s_ffn = carve_ffn(c, &q);
+  }
+  return s;
+}
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+#define MOE_TRY(expr)                                  \
+  do {                                                 \
+    const hipError_t err__ = (expr);                   \
+    if (err__ != hipSuccess) return MOE_ERR_HIP;       \
+  } while (0)
+
+// Enqueue the grouped FFN (no argument checks).
+moe_status run_ffn(const moe_problem* p, const void* x_perm, const float* x_perm_scale,
+                   const int32_t* offsets, const moe_weights* w, void* h, float* h_scale,
+                   void* y_perm, const FfnScratch& f, hipStream_t s) {
+  const int64_t N = n_cap(p);
+  const int E_L = p->num_local, H = p->hidden, I = p->inter;
+  const int64_t mt = max_m_tiles(N, E_L);
+  void* hb = h ? h : f.h;
+  float* hs = h ? h_scale : f.h_scale;
+  MOE_TRY(launch_tile_schedule(offsets, E_L, f.info, f.n_tiles, s));
+  if (!is_fp8(p)) {
+    MOE_TRY(launch_gemm_bf16(true, x_perm, w->w13, hb, f.info, f.n_tiles, mt, H, I,
+                             2ll * I * H, s));
+    MOE_TRY(launch_gemm_bf16(false, hb, w->w2, y_perm, f.info, f.n_tiles, mt, I, H,
+                             static_cast<int64_t>(H) * I, s));
+  } else {
+    MOE_TRY(launch_gemm_fp8(true, x_perm, x_perm_scale, w->w13, w->w13_scale, f.h_wide, f.info,
+                            f.n_tiles, mt, H, I, 2ll * I * H, (2ll * I / 128) * (H / 128), s));
+    MOE_TRY(launch_gather_fp8(f.h_wide, nullptr, offsets + E_L, N, I, hb, hs, s));
+    MOE_TRY(launch_gemm_fp8(false, hb, hs, w->w2, w->w2_scale, y_perm, f.info, f.n_tiles, mt, I,
+                            H, static_cast<int64_t>(H) * I, (static_cast<int64_t>(H) / 128) * (I / 128),
+                            s));
+  }
+  return MOE_OK;
+}
+
+moe_status run_dispatch(const moe_problem* p, const void* x, const int32_t* ids, int32_t* counts,
+                        int32_t* offsets, int32_t* row_token, int32_t* row_slot, int32_t* tsr,
+                        void* x_perm, float* x_perm_scale, void* scratch, hipStream_t s) {
+  const int T = p->num_tokens, E_L = p->num_local;
+  MOE_TRY(launch_index_build(ids, T, p->top_k, p->expert_begin, E_L, counts, offsets, row_token,
+                             row_slot, tsr, scratch, s));
+  if (is_fp8(p))
+    MOE_TRY(launch_gather_fp8(x, row_token, offsets + E_L, n_cap(p), p->hidden, x_perm,
+                              x_perm_scale, s));
+  else
+    MOE_TRY(launch_gather_bf16(x, row_token, offsets + E_L, n_cap(p), p->hidden, x_perm, s));
+  return MOE_OK;
+}
+
+bool weights_ok(const moe_problem* p, const moe_weights* w, bool need_shared) {
+  if (!w || !w->w13 || !w->w2 || !aligned16(w->w13) || !aligned16(w->w2)) return false;
+  if (is_fp8(p) && (!w->w13_scale || !w->w2_scale)) return false;
+  if (need_shared) {
+    if (!w->ws13 || !w->ws2 || !aligned16(w->ws13) || !aligned16(w->ws2)) return false;
+    if (is_fp8(p) && (!w->ws13_scale || !w->ws2_scale)) return false;
+  }
+  return true;
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+size_t moe_workspace_bytes(const moe_problem* p, int32_t stage) {
+  if (check_problem(p) != MOE_OK) return 0;
+  Carve c(nullptr);
+  switch (stage) {
+    case MOE_STAGE_LAYER: carve_layer(c, p); break;
+    case MOE_STAGE_DISPATCH:
+      c.take<void>(index_scratch_bytes(p->num_tokens, p->num_local));
+      break;
+    case MOE_STAGE_FFN: carve_ffn(c, p); break;
+    default: return 0;
+  }
+  return c.used + 256;  // room to round the base up to 256 bytes
+}
+
+moe_status moe_route(const moe_problem* p, const float* logits, int32_t* topk_ids,
+                     float* topk_w, void* stream) {
+  moe_status st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!logits || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(logits) || !aligned16(topk_ids) || !aligned16(topk_w)) return MOE_ERR_INVALID_ARG;
+  if (p->num_tokens == 0) return MOE_OK;
+  return hip_status(launch_route_topk(logits, p->num_tokens, p->num_experts, p->top_k, topk_ids,
+                                      topk_w, static_cast<hipStream_t>(stream)));
+}
+
+static void* align_ws(void* ws) {
+  const uintptr_t a = (reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255);
+  return reinterpret_cast<void*>(a);
+}
+
+moe_status moe_dispatch(const moe_problem* p, const void* x, const int32_t* topk_ids,
+                        int32_t* counts, int32_t* offsets, int32_t* row_token, int32_t* row_slot,
+                        int32_t* token_slot_row, void* x_perm, float* x_perm_scale, void* ws,
+                        size_t ws_bytes, void* stream) {
+  moe_status st = check_problem(p);
+  if (st != MOE_OK) return st;
+  const void* ptrs[] = {x, topk_ids, counts, offsets, row_token, row_slot, token_slot_row, x_perm};
+  for (const void* q : ptrs)
+    if (!q || !aligned16(q)) return MOE_ERR_INVALID_ARG;
+  if (is_fp8(p) && (!x_perm_scale || !aligned16(x_perm_scale))) return MOE_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < moe_workspace_bytes(p, MOE_STAGE_DISPATCH)) return MOE_ERR_WORKSPACE;
+  if (p->num_tokens == 0) return MOE_OK;
+  return run_dispatch(p, x, topk_ids, counts, offsets, row_token, row_slot, token_slot_row, x_perm,
+                      x_perm_scale, align_ws(ws), static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_grouped_ffn(const moe_problem* p, const void* x_perm, const float* x_perm_scale,
+                           const int32_t* offsets, const moe_weights* w, void* h, float* h_scale,
+                           void* y_perm, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!x_perm || !offsets || !y_perm || !aligned16(x_perm) || !aligned16(offsets) ||
+      !aligned16(y_perm))
+    return MOE_ERR_INVALID_ARG;
+  if (!weights_ok(p, w, false)) return MOE_ERR_INVALID_ARG;
+  if (is_fp8(p) && (!x_perm_scale || !aligned16(x_perm_scale))) return MOE_ERR_INVALID_ARG;
+  if (h && !aligned16(h)) return MOE_ERR_INVALID_ARG;
+  if (h && is_fp8(p) && (!h_scale || !aligned16(h_scale))) return MOE_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < moe_workspace_bytes(p, MOE_STAGE_FFN)) return MOE_ERR_WORKSPACE;
+  if (p->num_tokens == 0) return MOE_OK;
+  Carve c(align_ws(ws));
+  const FfnScratch f = carve_ffn(c, p);
+  return run_ffn(p, x_perm, x_perm_scale, offsets, w, h, h_scale, y_perm, f,
+                 static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_combine(const moe_problem* p, const void* y_perm, const int32_t* token_slot_row,
+                       const float* topk_w, const void* shared_out, void* y, void* stream) {
+  moe_status st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!y_perm || !token_slot_row || !topk_w || !y) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(y_perm) || !aligned16(token_slot_row) || !aligned16(topk_w) || !aligned16(y) ||
+      (shared_out && !aligned16(shared_out)))
+    return MOE_ERR_INVALID_ARG;
+  if (p->num_tokens == 0) return MOE_OK;
+  return hip_status(launch_combine(y_perm, token_slot_row, topk_w, shared_out, p->num_tokens,
+                                   p->top_k, p->hidden, y, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_layer(const moe_problem* p, const float* logits, const void* x,
+                     const moe_weights* w, void* y, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!logits || !x || !y || !aligned16(logits) || !aligned16(x) || !aligned16(y))
+    return MOE_ERR_INVALID_ARG;
+  if (!weights_ok(p, w, p->shared_inter > 0)) return MOE_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < moe_workspace_bytes(p, MOE_STAGE_LAYER)) return MOE_ERR_WORKSPACE;
+  if (p->num_tokens == 0) return MOE_OK;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  Carve c(align_ws(ws));
+  const LayerScratch L = carve_layer(c, p);
+  const int T = p->num_tokens;
+
+  MOE_TRY(launch_route_topk(logits, T, p->num_experts, p->top_k, L.ids, L.w, s));
+  st = run_dispatch(p, x, L.ids, L.counts, L.offsets, L.row_token, L.row_slot, L.tsr, L.x_perm,
+                    L.x_perm_scale, L.index_scratch, s);
+  if (st != MOE_OK) return st;
+  st = run_ffn(p, L.x_perm, L.x_perm_scale, L.offsets, w, nullptr, nullptr, L.y_perm, L.ffn, s);
+  if (st != MOE_OK) return st;
+  if (p->shared_inter > 0) {
+    const moe_problem q = shared_problem(p);
+    moe_weights sw{};
+    sw.w13 = w->ws13;
+    sw.w2 = w->ws2;
+    sw.w13_scale = w->ws13_scale;
+    sw.w2_scale = w->ws2_scale;
+    hipLaunchKernelGGL(fill_offsets_kernel, dim3(1), dim3(64), 0, s, L.s_offsets, T);
+    MOE_TRY(hipGetLastError());
+    const void* sx = x;
+    if (is_fp8(p)) {
+      MOE_TRY(launch_gather_fp8(x, nullptr, nullptr, T, p->hidden, L.s_x, L.s_x_scale, s));
+      sx = L.s_x;
+    }
+    st = run_ffn(&q, sx, L.s_x_scale, L.s_offsets, &sw, nullptr, nullptr, L.s_out, L.s_ffn, s);
+    if (st != MOE_OK) return st;
+  }
+  return hip_status(launch_combine(L.y_perm, L.tsr, L.w, p->shared_inter > 0 ? L.s_out : nullptr,
+                                   T, p->top_k, p->hidden, y, s));
+}
+
+moe_status moe_quantize_fp8(const void* src, int64_t batch, int64_t rows, int64_t cols,
+                            int32_t block_rows, void* codes, float* scales, void* stream) {
+  if (!src || !codes || !scales || !aligned16(src) || !aligned16(codes) || !aligned16(scales))
+    return MOE_ERR_INVALID_ARG;
+  if (batch < 0 || rows < 0 || cols < 128 || cols % 128 || cols > (1 << 20))
+    return MOE_ERR_INVALID_ARG;
+  if (block_rows != 1 && block_rows != 128) return MOE_ERR_INVALID_ARG;
+  if (batch * rows > (int64_t(1) << 31) - 1) return MOE_ERR_INVALID_ARG;
+  if (batch == 0 || rows == 0) return MOE_OK;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (block_rows == 1) {
+    if (cols > 65536) return MOE_ERR_INVALID_ARG;
+    return hip_status(launch_gather_fp8(src, nullptr, nullptr, batch * rows,
+                                        static_cast<int>(cols), codes, scales, s));
+  }
+  if ((rows + 127) / 128 > 65535 || batch > 65535) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_quant_blocks(src, batch, rows, cols, codes, scales, s));
+}
+
+}  // extern "C"

@@ -114,19 +114,25 @@ def e4m3_encode(v: np.ndarray) -> np.ndarray:
     rounded magnitude exactly.  A magnitude that rounds up into the next
     binade lands on its first value, which is also the right result.
     """
-    a = np.abs(np.asarray(v, dtype=np.float64))
-    if np.isnan(a).any():
+    v64 = np.asarray(v, dtype=np.float64)
+    if np.isnan(v64).any():
         raise ValueError("NaN has no E4M3 code here")
-    neg = np.signbit(np.asarray(v, dtype=np.float64))
+    neg = np.signbit(v64)
+    a = np.abs(v64)
     _, ex = np.frexp(a)                     # a = f * 2^ex, f in [0.5, 1)
     e = np.maximum(ex - 1, -6)              # binade exponent, floored at min normal
-    step = np.exp2(e.astype(np.float64) - 3.0)
-    q = np.rint(a / step) * step
+    # rint(a / 2^(e-3)) * 2^(e-3); the scalings by powers of two are exact.
+    q = np.ldexp(np.rint(np.ldexp(a, 3 - e)), e - 3)
     q = np.minimum(q, E4M3_MAX)
-    mag_code = np.searchsorted(_POS_VALUES, q).astype(np.int64)
-    assert np.all(_POS_VALUES[mag_code] == q)
+    # Code of the magnitude q: subnormals are q / 2^-9; a normal q = (1 + m/8)
+    # 2^eq has code (eq + 7) * 8 + m = (eq + 6) * 8 + q * 2^(3 - eq).
+    _, eq = np.frexp(q)
+    eq = eq - 1
+    mag = np.where(q < 2.0 ** -6, np.ldexp(q, 9), (eq + 6) * 8 + np.ldexp(q, 3 - eq))
+    mag_code = mag.astype(np.uint8)
+    assert np.all(_POS_VALUES[mag_code] == q)   # decodes back to q exactly
     # -0.0 keeps its sign bit (code 0x80), as the hardware's sign does.
-    return (mag_code | np.where(neg, 0x80, 0)).astype(np.uint8)
+    return mag_code | (neg.astype(np.uint8) << 7)
 
 
 def quantize_blocks(a: np.ndarray, block_rows: int, block_cols: int):
@@ -146,19 +152,16 @@ def quantize_blocks(a: np.ndarray, block_rows: int, block_cols: int):
     R, C = a.shape
     nbr = -(-R // block_rows)
     nbc = -(-C // block_cols)
-    codes = np.empty((R, C), dtype=np.uint8)
-    scales = np.empty((nbr, nbc), dtype=np.float32)
-    for i in range(nbr):
-        r0, r1 = i * block_rows, min(R, (i + 1) * block_rows)
-        for j in range(nbc):
-            c0, c1 = j * block_cols, min(C, (j + 1) * block_cols)
-            blk = a[r0:r1, c0:c1]
-            amax = np.float32(np.abs(blk).max()) if blk.size else np.float32(0)
-            s = np.float32(amax / np.float32(E4M3_MAX)) if amax > 0 else np.float32(1.0)
-            scales[i, j] = s
-            quot = blk.astype(np.float32) / s          # IEEE float32 division
-            codes[r0:r1, c0:c1] = e4m3_encode(quot)
-    return codes, scales
+    # Pad to whole blocks with zeros (a zero never raises a block's amax).
+    pad = np.zeros((nbr * block_rows, nbc * block_cols), dtype=np.float64)
+    pad[:R, :C] = a
+    blocks = pad.reshape(nbr, block_rows, nbc, block_cols)
+    amax = np.abs(blocks).max(axis=(1, 3)).astype(np.float32)          # [nbr, nbc]
+    scales = np.where(amax > 0, (amax / np.float32(E4M3_MAX)).astype(np.float32),
+                      np.float32(1.0)).astype(np.float32)
+    quot = blocks.astype(np.float32) / scales[:, None, :, None]        # IEEE float32 division
+    codes = e4m3_encode(quot).reshape(nbr * block_rows, nbc * block_cols)[:R, :C]
+    return np.ascontiguousarray(codes), scales
 
 
 def quantize_rows_groups(a: np.ndarray, group: int = 128):

@@ -1,0 +1,120 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, every
+function include/moe_layer.h declares is exported, workspace sizing, status
+names, and argument validation (which returns before anything is enqueued)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from moe_expert_layer_gate_amd import inputs as synth
+from moe_expert_layer_gate_amd import moelayer as ml
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = [os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+           if f.endswith(".h")]
+
+
+def declared_functions():
+    names = set()
+    for h in HEADERS:
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(moe_[a-z0-9_]+)\s*\(",
+                             src, flags=re.M):
+            names.add(m.group(1))
+    return names
+
+
+def test_header_declares_the_expected_calls():
+    assert {"moe_route", "moe_dispatch", "moe_grouped_ffn", "moe_combine", "moe_layer",
+            "moe_quantize_fp8", "moe_workspace_bytes", "moe_status_str",
+            "moe_abi_version"} <= declared_functions()
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(ml.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    # and the binding knows each of them
+    assert declared_functions() <= set(ml.SIGNATURES)
+
+
+def test_abi_version_and_status_strings():
+    assert ml.lib().moe_abi_version() == 1
+    assert ml.status_str(0) == "MOE_OK"
+    assert ml.status_str(3) == "MOE_ERR_WORKSPACE"
+    assert ml.status_str(99) == "MOE_ERR_UNKNOWN"
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+def test_workspace_sizes(cid):
+    p = ml.Problem.from_config(synth.config(cid))
+    layer = ml.workspace_bytes(p, ml.STAGE_LAYER)
+    disp = ml.workspace_bytes(p, ml.STAGE_DISPATCH)
+    ffn = ml.workspace_bytes(p, ml.STAGE_FFN)
+    assert layer > 0 and disp > 0 and ffn > 0
+    assert layer > disp and layer > ffn
+    # the layer workspace holds at least the permuted activations and outputs
+    beta = 1 if p.fp8 else 2
+    assert layer >= p.n_cap * p.H * (beta + 2)
+    assert ml.workspace_bytes(p, 7) == 0
+
+
+@pytest.mark.parametrize("bad", [
+    dict(T=-1), dict(E=0), dict(k=0), dict(k=9, E=8), dict(k=33, E=64), dict(E_L=0),
+    dict(e_lo=6, E_L=4), dict(e_lo=-1), dict(H=100), dict(I=96), dict(I_s=64), dict(H=0),
+    dict(E=2000, E_L=8)])
+def test_invalid_problems_rejected(bad):
+    base = dict(T=16, H=256, E=8, k=2, e_lo=0, E_L=8, I=256, I_s=0, fp8=False)
+    base.update(bad)
+    p = ml.Problem(**base)
+    assert ml.workspace_bytes(p) == 0
+    pc = p.c()
+    # validation fails before any pointer is looked at or anything enqueued
+    assert ml.lib().moe_route(ctypes.byref(pc), 16, 16, 16, None) == ml.MOE_ERR_INVALID_ARG
+
+
+def test_null_and_misaligned_pointers_rejected():
+    p = ml.Problem(T=16, H=256, E=8, k=2, e_lo=0, E_L=8, I=256)
+    pc = p.c()
+    L = ml.lib()
+    assert L.moe_route(ctypes.byref(pc), None, 256, 256, None) == ml.MOE_ERR_INVALID_ARG
+    assert L.moe_route(ctypes.byref(pc), 257, 256, 256, None) == ml.MOE_ERR_INVALID_ARG
+    assert L.moe_route(None, 256, 256, 256, None) == ml.MOE_ERR_INVALID_ARG
+    assert L.moe_combine(ctypes.byref(pc), 256, None, 256, None, 256, None) == ml.MOE_ERR_INVALID_ARG
+    w = ml.moe_weights(None, 256, None, None, None, None, None, None)
+    assert L.moe_layer(ctypes.byref(pc), 256, 256, ctypes.byref(w), 256, 256, 1 << 30,
+                       None) == ml.MOE_ERR_INVALID_ARG
+    w = ml.moe_weights(256, 256, None, None, None, None, None, None)
+    assert L.moe_layer(ctypes.byref(pc), 256, 256, ctypes.byref(w), 256, 256, 16,
+                       None) == ml.MOE_ERR_WORKSPACE
+    assert L.moe_dispatch(ctypes.byref(pc), *([256] * 8), None, None, 0, None) == ml.MOE_ERR_WORKSPACE
+    # fp8 needs its scale pointers
+    pf = ml.Problem(T=16, H=256, E=8, k=2, e_lo=0, E_L=8, I=256, fp8=True).c()
+    w = ml.moe_weights(256, 256, None, None, None, None, None, None)
+    assert L.moe_layer(ctypes.byref(pf), 256, 256, ctypes.byref(w), 256, 256, 1 << 40,
+                       None) == ml.MOE_ERR_INVALID_ARG
+    # shared expert needs its weights
+    ps = ml.Problem(T=16, H=256, E=8, k=2, e_lo=0, E_L=8, I=256, I_s=128).c()
+    w = ml.moe_weights(256, 256, None, None, None, None, None, None)
+    assert L.moe_layer(ctypes.byref(ps), 256, 256, ctypes.byref(w), 256, 256, 1 << 40,
+                       None) == ml.MOE_ERR_INVALID_ARG
+
+
+def test_empty_batch_enqueues_nothing():
+    """T = 0 is valid and returns before any HIP call (so it runs without a GPU)."""
+    p = ml.Problem(T=0, H=256, E=8, k=2, e_lo=0, E_L=8, I=256)
+    pc = p.c()
+    L = ml.lib()
+    assert L.moe_route(ctypes.byref(pc), 256, 256, 256, None) == ml.MOE_OK
+    w = ml.moe_weights(256, 256, None, None, None, None, None, None)
+    n = ml.workspace_bytes(p)
+    assert L.moe_layer(ctypes.byref(pc), 256, 256, ctypes.byref(w), 256, 256, n, None) == ml.MOE_OK
+
+
+def test_quantize_argument_checks():
+    L = ml.lib()
+    assert L.moe_quantize_fp8(256, 1, 128, 100, 128, 256, 256, None) == ml.MOE_ERR_INVALID_ARG
+    assert L.moe_quantize_fp8(256, 1, 128, 128, 64, 256, 256, None) == ml.MOE_ERR_INVALID_ARG
+    assert L.moe_quantize_fp8(None, 1, 128, 128, 128, 256, 256, None) == ml.MOE_ERR_INVALID_ARG
+    assert L.moe_quantize_fp8(256, 0, 128, 128, 128, 256, 256, None) == ml.MOE_OK

@@ -62,8 +62,8 @@ import numpy as np
 __all__ = [
     "bf16_to_f64", "route", "index_build", "tile_count", "dispatch", "silu",
     "expert_ffn", "grouped_ffn", "combine", "moe_layer", "moe_layer_tokens",
-    "e4m3_value", "e4m3_encode", "quantize_blocks", "dequantize_blocks",
-    "E4M3_MAX",
+    "e4m3_value", "e4m3_encode", "quantize_blocks", "quantize_rows_groups",
+    "dequantize_blocks", "fp8_activation", "E4M3_MAX",
 ]
 
 
@@ -285,7 +285,7 @@ def silu(a: np.ndarray) -> np.ndarray:
         return a / (1.0 + np.exp(-a))
 
 
-def expert_ffn(xr: np.ndarray, w13: np.ndarray, w2: np.ndarray):
+def expert_ffn(xr: np.ndarray, w13: np.ndarray, w2: np.ndarray, h_fn=None):
     """One expert's gated SwiGLU FFN on a block of rows.
 
     OverlapAdvisor section 4.2.2 (a gated MLP has m = 2 first-layer
@@ -294,16 +294,18 @@ def expert_ffn(xr: np.ndarray, w13: np.ndarray, w2: np.ndarray):
     sits between the two GroupGEMMs).
 
     xr [n, H]; w13 [2I, H] (gate rows then up rows); w2 [H, I].
+    ``h_fn``, if given, maps h before the down projection (the FP8 path's
+    activation quantisation).
     Returns (h [n, I], y [n, H]) in float64.
     """
     I = w13.shape[0] // 2
     g = xr @ w13[:I].T
     u = xr @ w13[I:].T
     h = silu(g) * u
-    return h, h @ w2.T
+    return h, (h if h_fn is None else h_fn(h)) @ w2.T
 
 
-def grouped_ffn(x_perm: np.ndarray, offsets: np.ndarray, w13, w2):
+def grouped_ffn(x_perm: np.ndarray, offsets: np.ndarray, w13, w2, h_fn=None):
     """Grouped FFN over the expert-major rows: segment e
     [offsets[e], offsets[e+1]) runs through local expert e.  ``w13``/``w2``
     are callables or arrays indexed by the local expert giving float64
@@ -322,7 +324,7 @@ def grouped_ffn(x_perm: np.ndarray, offsets: np.ndarray, w13, w2):
         we13, we2 = get13(e), get2(e)
         if h_all is None:
             h_all = np.zeros((N, we13.shape[0] // 2), dtype=np.float64)
-        h, y = expert_ffn(x_perm[a:b], we13, we2)
+        h, y = expert_ffn(x_perm[a:b], we13, we2, h_fn)
         h_all[a:b] = h
         y_perm[a:b] = y
     if h_all is None:
@@ -375,28 +377,47 @@ def _shared_weights(weights: dict, fp8: bool):
             dequantize_blocks(weights["ws2_q"], weights["ws2_s"], 128, 128))
 
 
+def fp8_activation(a: np.ndarray) -> np.ndarray:
+    """The value an activation row block carries after block-FP8 packing
+    (CascadeEP Appendix C: activations packed with their quantisation
+    metadata; OverlapAdvisor Table 6: FP8 activations): per token, per 128
+    consecutive elements, dequantise(quantise(a))."""
+    q, s = quantize_rows_groups(a, 128)
+    return dequantize_blocks(q, s, 1, 128)
+
+
 def moe_layer(logits: np.ndarray, x_bits: np.ndarray, weights: dict, *,
-              k: int, e_lo: int, E_L: int, fp8: bool = False) -> Dict[str, np.ndarray]:
+              k: int, e_lo: int, E_L: int, fp8: bool = False,
+              quantize_activations: bool = False) -> Dict[str, np.ndarray]:
     """The whole layer for one GPU's local experts, every stage kept.
 
     ``weights``: bf16 -> "w13" [E_L, 2I, H], "w2" [E_L, H, I] (bf16 bits),
     optional "ws13"/"ws2" (shared expert); fp8 -> the same names with
     suffixes "_q" (codes) and "_s" (128 x 128 block scales).
 
+    ``quantize_activations`` (fp8 only) also passes the inputs of both
+    GEMMs -- x and h -- through per-token 128-group block-FP8, as the FP8
+    path of the pages does between its GEMMs (CascadeEP Appendix C, the
+    activation and quantisation operations between the two expert GEMMs).
+    The default leaves them exact: the reference the output gate measures.
+
     Returns every stage: ids, w, counts, offsets, row_token, row_slot,
     token_slot_row, x_perm, h, y_perm, shared (or None) and y, as float64
-    for the floating-point ones.
+    for the floating-point ones (h before its own quantisation).
     """
     ids, w = route(logits, k)
     ix = index_build(ids, e_lo, E_L)
     x = bf16_to_f64(x_bits)
-    x_perm = dispatch(x, ix["row_token"])
+    qa = fp8 and quantize_activations
+    xq = fp8_activation(x) if qa else x
+    x_perm = dispatch(xq, ix["row_token"])
     g13, g2 = _expert_weights(weights, fp8)
-    h, y_perm = grouped_ffn(x_perm, ix["offsets"], g13, g2)
+    h_fn = fp8_activation if qa else None
+    h, y_perm = grouped_ffn(x_perm, ix["offsets"], g13, g2, h_fn)
     sw = _shared_weights(weights, fp8)
     shared = None
     if sw is not None:
-        shared = expert_ffn(x, sw[0], sw[1])[1]
+        shared = expert_ffn(xq, sw[0], sw[1], h_fn)[1]
     y = combine(y_perm, ix["token_slot_row"], w, shared, H=x.shape[1])
     out = dict(ix)
     out.update(ids=ids, w=w, x_perm=x_perm, h=h, y_perm=y_perm, shared=shared, y=y)
@@ -405,7 +426,7 @@ def moe_layer(logits: np.ndarray, x_bits: np.ndarray, weights: dict, *,
 
 def moe_layer_tokens(logits: np.ndarray, x_bits: np.ndarray, weights: dict,
                      tokens, *, k: int, e_lo: int, E_L: int,
-                     fp8: bool = False) -> np.ndarray:
+                     fp8: bool = False, quantize_activations: bool = False) -> np.ndarray:
     """Layer output rows for a few tokens only, one token at a time (for
     spot checks at sizes where the whole layer is too slow on the CPU).
     A token's output depends only on its own logits and activations, so
@@ -414,6 +435,10 @@ def moe_layer_tokens(logits: np.ndarray, x_bits: np.ndarray, weights: dict,
     tokens = np.asarray(tokens, dtype=np.int64)
     ids, w = route(logits[tokens], k)
     x = bf16_to_f64(x_bits[tokens])
+    qa = fp8 and quantize_activations
+    if qa:
+        x = fp8_activation(x)       # per-token groups: same rows as for the whole batch
+    h_fn = fp8_activation if qa else None
     g13, g2 = _expert_weights(weights, fp8)
     sw = _shared_weights(weights, fp8)
     y = np.zeros_like(x)
@@ -429,11 +454,11 @@ def moe_layer_tokens(logits: np.ndarray, x_bits: np.ndarray, weights: dict,
     for e, lst in sorted(by_expert.items()):
         we13, we2 = g13(e), g2(e)
         rows = np.array([i for i, _ in lst])
-        _, ye = expert_ffn(x[rows], we13, we2)
+        _, ye = expert_ffn(x[rows], we13, we2, h_fn)
         for (i, s), yr in zip(lst, ye):
             contrib[i, s] = w[i, s] * yr
     for s in range(k):                       # slot order, as in combine()
         y += contrib[:, s]
     if sw is not None:
-        y += expert_ffn(x, sw[0], sw[1])[1]
+        y += expert_ffn(x, sw[0], sw[1], h_fn)[1]
     return y

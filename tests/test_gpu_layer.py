@@ -124,9 +124,13 @@ def test_staged_and_fused_layer_small(name):
     say("layer small", name)
     st = run_staged(torch, p, dev)
     ow = OracleWeights(d, cfg.fp8)
+    # bf16: the exact oracle.  fp8: the oracle with the FP8 path's activation
+    # quantisation of x and h, so the kernels are held to bf16-level
+    # agreement (the 6e-2 gate against the exact oracle is checked at the
+    # workloads' own spreads below).
     ref = O.moe_layer(d["logits"], d["x"], ow.as_layer_dict(cfg.E_L), k=cfg.k, e_lo=cfg.e_lo,
-                      E_L=cfg.E_L, fp8=cfg.fp8)
-    tol = TOL_FP8 if cfg.fp8 else TOL_BF16
+                      E_L=cfg.E_L, fp8=cfg.fp8, quantize_activations=cfg.fp8)
+    tol = TOL_BF16
     # exact routing and permutation
     np.testing.assert_array_equal(st["ids"].cpu().numpy(), ref["ids"])
     np.testing.assert_array_equal(st["offsets"].cpu().numpy(), ref["offsets"])
@@ -134,7 +138,8 @@ def test_staged_and_fused_layer_small(name):
     np.testing.assert_array_equal(st["row_token"][:N].cpu().numpy(), ref["row_token"])
     np.testing.assert_array_equal(st["tsr"].cpu().numpy(), ref["token_slot_row"])
     # FFN stages
-    e_h = rel_rows(h_values(st, p), ref["h"])
+    ref_h = O.fp8_activation(ref["h"]) if cfg.fp8 else ref["h"]
+    e_h = rel_rows(h_values(st, p), ref_h)
     e_yp = rel_rows(f64(st["y_perm"][:N]), ref["y_perm"])
     e_y = rel_rows(f64(st["y"]), ref["y"])
     print(f"{name}: h {e_h:.2e}  y_perm {e_yp:.2e}  y {e_y:.2e}  global {global_rel(f64(st['y']), ref['y']):.2e}")
@@ -144,6 +149,25 @@ def test_staged_and_fused_layer_small(name):
     # fused layer: same routing, same numbers as the staged calls
     y = run_layer(torch, p, dev, guard=3)
     np.testing.assert_array_equal(dv.bits_from_bf16(y), dv.bits_from_bf16(st["y"]))
+
+
+@pytest.mark.parametrize("name", list(SMALL_FP8))
+def test_fp8_gate_at_workload_spread(name):
+    """Block-FP8 against the exact oracle (activations not quantised) at the
+    workloads' N(0, 0.02) spreads: the 6e-2 output gate."""
+    torch = torch_cuda()
+    ml, dv = _mods()
+    cfg, seed = SMALL_FP8[name]
+    d, dev = upload(cfg, seed)
+    p = ml.Problem.from_config(cfg)
+    say("fp8 gate", name)
+    y = f64(run_layer(torch, p, dev))
+    ow = OracleWeights(d, True)
+    ref = O.moe_layer(d["logits"], d["x"], ow.as_layer_dict(cfg.E_L), k=cfg.k, e_lo=cfg.e_lo,
+                      E_L=cfg.E_L, fp8=True)
+    e = rel_rows(y, ref["y"])
+    print(f"{name}: y vs exact oracle {e:.2e}  global {global_rel(y, ref['y']):.2e}")
+    assert e <= TOL_FP8
 
 
 @pytest.mark.parametrize("name", ["tiny", "decode"])
@@ -237,15 +261,19 @@ def test_workload_fp8_full_size_sampled():
     ow = OracleWeights(d, True)
     x = O.bf16_to_f64(d["x"])
     rng = np.random.default_rng(4)
-    got, ref = [], []
+    got, ref, ref_q = [], [], []
     for e in (0, 3, 17, 31):
         a, b = int(ix["offsets"][e]), int(ix["offsets"][e + 1])
         rows = sorted({a, min(a + 127, b - 1), min(a + 128, b - 1), b - 1,
                        *rng.integers(a, b, 4).tolist()})
         for r in rows:
-            ref.append(O.expert_ffn(x[ix["row_token"][r]][None], ow.w("w13", e), ow.w("w2", e))[1][0])
+            xr = x[ix["row_token"][r]][None]
+            ref.append(O.expert_ffn(xr, ow.w("w13", e), ow.w("w2", e))[1][0])
+            ref_q.append(O.expert_ffn(O.fp8_activation(xr), ow.w("w13", e), ow.w("w2", e),
+                                      O.fp8_activation)[1][0])
             got.append(f64(st["y_perm"][r]))
     e_yp = rel_rows(np.array(got), np.array(ref))
+    e_yq = rel_rows(np.array(got), np.array(ref_q))
     toks = rng.integers(0, cfg.T, 16)
     e_sh = rel_rows(f64(st["shared"][torch.from_numpy(toks).cuda()]),
                     O.expert_ffn(x[toks], ow.w("ws13"), ow.w("ws2"))[1])
@@ -255,8 +283,9 @@ def test_workload_fp8_full_size_sampled():
     ref_y = O.moe_layer_tokens(d["logits"], d["x"], ow.as_layer_dict(cfg.E_L), toks, k=cfg.k,
                                e_lo=cfg.e_lo, E_L=cfg.E_L, fp8=True)
     e_y = rel_rows(f64(st["y"][torch.from_numpy(toks).cuda()]), ref_y)
-    print(f"fp8 full: y_perm rows {e_yp:.2e}  shared {e_sh:.2e}  y tokens {e_y:.2e}")
-    assert e_yp <= TOL_FP8 and e_sh <= TOL_FP8 and e_y <= TOL_FP8
+    print(f"fp8 full: y_perm rows {e_yp:.2e} (vs quantised-activation oracle {e_yq:.2e})  "
+          f"shared {e_sh:.2e}  y tokens {e_y:.2e}")
+    assert e_yp <= TOL_FP8 and e_sh <= TOL_FP8 and e_y <= TOL_FP8 and e_yq <= TOL_BF16
     say("full size fp8 fused")
     y = run_layer(torch, p, dev)
     np.testing.assert_array_equal(dv.bits_from_bf16(y), dv.bits_from_bf16(st["y"]))

@@ -121,3 +121,74 @@ def test_fp8_layer_close_to_bf16_layer():
     y8 = O.moe_layer(d["logits"], d["x"], qd, k=2, e_lo=0, E_L=8, fp8=True)["y"]
     rel = np.linalg.norm(y8 - y16, axis=1) / np.linalg.norm(y16, axis=1)
     assert rel.max() < 0.08
+
+
+def _fp8_layer_inputs(cfg, seed, std, x_std):
+    d = synth.make_inputs(cfg, seed, std=std, x_std=x_std)
+    qd = {}
+    for name in ("w13", "w2", "ws13", "ws2"):
+        if name not in d:
+            continue
+        if d[name].ndim == 3:
+            qs = [O.quantize_blocks(O.bf16_to_f64(m), 128, 128) for m in d[name]]
+            qd[name + "_q"] = np.stack([q for q, _ in qs])
+            qd[name + "_s"] = np.stack([s for _, s in qs])
+        else:
+            qd[name + "_q"], qd[name + "_s"] = O.quantize_blocks(O.bf16_to_f64(d[name]), 128, 128)
+    return d, qd
+
+
+def test_activation_quantisation_is_identity_on_representable_groups():
+    """Groups whose values are E4M3 values times 2^j with amax 448 * 2^j
+    (scale exactly 2^j) pass through unchanged."""
+    rng = np.random.default_rng(5)
+    vals = O.e4m3_value(np.array([c for c in range(0x7F)], np.uint8))
+    a = rng.choice(vals, size=(6, 256)) * rng.choice([-1, 1], size=(6, 256))
+    a[:, 0] = 448.0
+    a[:, 128] = -448.0
+    a *= np.exp2(rng.integers(-20, 5, size=(6, 1)))
+    np.testing.assert_array_equal(O.fp8_activation(a), a)
+
+
+def test_activation_quantisation_sits_before_each_gemm(monkeypatch):
+    """With quantize_activations the layer passes exactly two kinds of
+    arrays through the activation quantiser: the token activations x (all
+    tokens, before the up GEMM) and each expert's h (before the down GEMM),
+    never the outputs."""
+    cfg = synth.MoEConfig("t", T=24, H=256, E=4, E_L=4, e_lo=0, k=2, I=384, I_s=128)
+    d, qd = _fp8_layer_inputs(cfg, 8, std=0.05, x_std=1.0)
+    seen = []
+    real = O.fp8_activation
+    monkeypatch.setattr(O, "fp8_activation", lambda a: (seen.append(np.array(a)), real(a))[1])
+    out = O.moe_layer(d["logits"], d["x"], qd, k=2, e_lo=0, E_L=4, fp8=True,
+                      quantize_activations=True)
+    x = O.bf16_to_f64(d["x"])
+    np.testing.assert_array_equal(seen[0], x)                       # x, whole batch, first
+    h_shapes = [a.shape for a in seen[1:]]
+    assert all(sh[1] in (384, 128) for sh in h_shapes)              # h widths (I or I_s)
+    assert sum(sh[0] for sh in h_shapes if sh[1] == 384) == out["offsets"][-1]
+    # the routed h seen are the layer's h rows, segment by segment
+    np.testing.assert_array_equal(np.concatenate([a for a in seen[1:] if a.shape[1] == 384]),
+                                  out["h"])
+    # and those h come from the quantised x
+    e0 = int(np.nonzero(out["counts"])[0][0])
+    a0, b0 = out["offsets"][e0], out["offsets"][e0 + 1]
+    w13 = O.dequantize_blocks(qd["w13_q"][e0], qd["w13_s"][e0], 128, 128)
+    xq = real(x)[out["row_token"][a0:b0]]
+    np.testing.assert_allclose(out["h"][a0:b0],
+                               O.silu(xq @ w13[:384].T) * (xq @ w13[384:].T), rtol=1e-12)
+
+
+@pytest.mark.parametrize("shared", [0, 128])
+def test_quantised_activations_move_the_output_a_little(shared):
+    cfg = synth.MoEConfig("t", T=40, H=256, E=8, E_L=8, e_lo=0, k=2, I=256, I_s=shared)
+    d, qd = _fp8_layer_inputs(cfg, 7, std=0.05, x_std=1.0)
+    a = O.moe_layer(d["logits"], d["x"], qd, k=2, e_lo=0, E_L=8, fp8=True)["y"]
+    b = O.moe_layer(d["logits"], d["x"], qd, k=2, e_lo=0, E_L=8, fp8=True,
+                    quantize_activations=True)["y"]
+    rel = np.linalg.norm(a - b, axis=1) / np.linalg.norm(a, axis=1)
+    assert 1e-3 < rel.min() and rel.max() < 0.12
+    toks = [0, 17, 39]
+    np.testing.assert_allclose(
+        O.moe_layer_tokens(d["logits"], d["x"], qd, toks, k=2, e_lo=0, E_L=8, fp8=True,
+                           quantize_activations=True), b[toks], rtol=1e-12, atol=1e-300)

@@ -28,13 +28,22 @@ hipError_t launch_quant_blocks(const void* src, int64_t batch, int64_t rows, int
 int64_t max_m_tiles(int64_t n_cap, int E_L);
 hipError_t launch_tile_schedule(const int32_t* offsets, int E_L, int4* info, int32_t* n_tiles,
                                 hipStream_t s);
-hipError_t launch_gemm_bf16(bool swiglu, const void* A, const void* W, void* C, const int4* info,
-                            const int32_t* n_tiles, int64_t max_tiles, int K, int Nout,
-                            int64_t w_expert_stride, hipStream_t s);
-hipError_t launch_gemm_fp8(bool swiglu, const void* A, const float* A_scale, const void* W,
-                           const float* W_scale, void* C, const int4* info,
-                           const int32_t* n_tiles, int64_t max_tiles, int K, int Nout,
-                           int64_t w_expert_stride, int64_t ws_expert_stride, hipStream_t s);
+struct GemmLaunch {
+  bool fp8;              // e4m3 operands with block scales, else bf16
+  bool swiglu;           // up GEMM with the SwiGLU epilogue, else plain
+  const void* A;         // [N_cap, K] permuted activations
+  const float* A_scale;  // fp8: [N_cap, K/128]
+  const void* W;         // [E_L, NW, K]
+  const float* W_scale;  // fp8: [E_L, NW/128, K/128]
+  void* C;               // [N_cap, Nout]: bf16, or e4m3 when C_scale != nullptr
+  float* C_scale;        // fp8 SwiGLU only: [N_cap, Nout/128] per-row group scales
+  const int32_t* offsets;
+  const int4* info;
+  const int32_t* n_tiles;
+  int64_t max_tiles;
+  int K, Nout;
+};
+hipError_t launch_grouped_gemm(const GemmLaunch& L, hipStream_t s);
 
 hipError_t launch_combine(const void* y_perm, const int32_t* token_slot_row, const float* topk_w,
                           const void* shared_out, int T, int k, int H, void* y, hipStream_t s);

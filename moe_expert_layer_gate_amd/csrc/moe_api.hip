@@ -61,7 +61,6 @@ struct FfnScratch {
   int32_t* n_tiles;
   void* h;          // [N_cap, I] bf16 or e4m3
   float* h_scale;   // fp8 only
-  void* h_wide;     // fp8 only: bf16 h before quantisation
 };
 
 FfnScratch carve_ffn(Carve& c, const moe_problem* p) {
@@ -72,7 +71,6 @@ FfnScratch carve_ffn(Carve& c, const moe_problem* p) {
   if (is_fp8(p)) {
     f.h = c.take<void>(N * I);
     f.h_scale = c.take<float>(sizeof(float) * N * (I / 128));
-    f.h_wide = c.take<void>(2 * N * I);
   } else {
     f.h = c.take<void>(2 * N * I);
   }
@@ -158,19 +156,33 @@ moe_status run_ffn(const moe_problem* p, const void* x_perm, const float* x_perm
   void* hb = h ? h : f.h;
   float* hs = h ? h_scale : f.h_scale;
   MOE_TRY(launch_tile_schedule(offsets, E_L, f.info, f.n_tiles, s));
-  if (!is_fp8(p)) {
-    MOE_TRY(launch_gemm_bf16(true, x_perm, w->w13, hb, f.info, f.n_tiles, mt, H, I,
-                             2ll * I * H, s));
-    MOE_TRY(launch_gemm_bf16(false, hb, w->w2, y_perm, f.info, f.n_tiles, mt, I, H,
-                             static_cast<int64_t>(H) * I, s));
-  } else {
-    MOE_TRY(launch_gemm_fp8(true, x_perm, x_perm_scale, w->w13, w->w13_scale, f.h_wide, f.info,
-                            f.n_tiles, mt, H, I, 2ll * I * H, (2ll * I / 128) * (H / 128), s));
-    MOE_TRY(launch_gather_fp8(f.h_wide, nullptr, offsets + E_L, N, I, hb, hs, s));
-    MOE_TRY(launch_gemm_fp8(false, hb, hs, w->w2, w->w2_scale, y_perm, f.info, f.n_tiles, mt, I,
-                            H, static_cast<int64_t>(H) * I, (static_cast<int64_t>(H) / 128) * (I / 128),
-                            s));
-  }
+  GemmLaunch up{};
+  up.fp8 = is_fp8(p);
+  up.swiglu = true;
+  up.A = x_perm;
+  up.A_scale = x_perm_scale;
+  up.W = w->w13;
+  up.W_scale = w->w13_scale;
+  up.C = hb;
+  up.C_scale = is_fp8(p) ? hs : nullptr;
+  up.offsets = offsets;
+  up.info = f.info;
+  up.n_tiles = f.n_tiles;
+  up.max_tiles = mt;
+  up.K = H;
+  up.Nout = I;
+  MOE_TRY(launch_grouped_gemm(up, s));
+  GemmLaunch down = up;
+  down.swiglu = false;
+  down.A = hb;
+  down.A_scale = hs;
+  down.W = w->w2;
+  down.W_scale = w->w2_scale;
+  down.C = y_perm;
+  down.C_scale = nullptr;
+  down.K = I;
+  down.Nout = H;
+  MOE_TRY(launch_grouped_gemm(down, s));
   return MOE_OK;
 }
 

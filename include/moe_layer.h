@@ -37,7 +37,9 @@
  *
  * Supported sizes: 1 <= E <= 1024, 1 <= k <= min(E, 32), 1 <= E_L <= 1024,
  * 0 <= e_lo, e_lo + E_L <= E, 0 <= T <= 2^24, H % 128 == 0, I % 128 == 0
- * (and shared_inter % 128 == 0), H, I <= 65536.
+ * (and shared_inter % 128 == 0), H, I <= 65536, and one expert's up
+ * projection below 2 GiB in bf16 (4 I H < 2^31, likewise for shared_inter);
+ * larger experts return MOE_ERR_UNSUPPORTED.
  */
 #ifndef MOE_LAYER_H
 #define MOE_LAYER_H

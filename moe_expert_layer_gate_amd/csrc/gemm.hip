@@ -70,12 +70,12 @@ struct GemmArgs {
 };
 
 __global__ __launch_bounds__(1024) void tile_schedule_kernel(
-    const int32_t* __restrict__ offsets, int E_L, int4* __restrict__ info,
+    const int32_t* __restrict__ offsets, int E_L, int tile_m, int4* __restrict__ info,
     int32_t* __restrict__ n_tiles) {
   const int e = threadIdx.x;
   int cnt = 0;
   if (e < E_L) cnt = offsets[e + 1] - offsets[e];
-  const int tiles = ceil_div(cnt, kBM);
+  const int tiles = ceil_div(cnt, tile_m);
   int total;
   const int start = block_exclusive_scan(tiles, &total);
   if (e < E_L)
@@ -87,285 +87,10 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
   return g / (1.0f + __expf(-g)) * u;
 }
 
-template <int ROWB>
-struct Stage {
-  static constexpr int kPitch = ROWB + 16;
-  static constexpr int kBytes = (kBM + kBN) * kPitch;
-  static constexpr int kChunks = ROWB / 16;            // 16-byte chunks per row
-  static constexpr int kLdA = kBM * kChunks / kThreads;
-  static constexpr int kLdW = kBN * kChunks / kThreads;
-};
-
-// Global -> register -> LDS staging of one K step of both tiles.
-template <int ROWB>
-struct Loader {
-  using S = Stage<ROWB>;
-  const uint8_t* gA[S::kLdA];
-  const uint8_t* gW[S::kLdW];
-  int oA[S::kLdA], oW[S::kLdW];
-  uint4 rA[S::kLdA], rW[S::kLdW];
-
-  __device__ __forceinline__ void init(const GemmArgs& g, int swiglu, const uint8_t* We,
-                                       int64_t ldb, int nt, int row0, int row_end) {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < S::kLdA; ++i) {
-      const int c = tid + kThreads * i;
-      const int r = c / S::kChunks, col = (c % S::kChunks) * 16;
-      gA[i] = g.A + static_cast<int64_t>(min(row0 + r, row_end - 1)) * ldb + col;
-      oA[i] = r * S::kPitch + col;
-    }
-#pragma unroll
-    for (int i = 0; i < S::kLdW; ++i) {
-      const int c = tid + kThreads * i;
-      const int r = c / S::kChunks, col = (c % S::kChunks) * 16;
-      int wrow;
-      if (swiglu)
-        wrow = r < kBN / 2 ? nt * (kBN / 2) + r : g.Nout + nt * (kBN / 2) + (r - kBN / 2);
-      else
-        wrow = min(nt * kBN + r, g.NW - 1);
-      gW[i] = We + static_cast<int64_t>(wrow) * ldb + col;
-      oW[i] = (kBM + r) * S::kPitch + col;
-    }
-  }
-  __device__ __forceinline__ void load(int64_t kbyte) {
-#pragma unroll
-    for (int i = 0; i < S::kLdW; ++i) rW[i] = *reinterpret_cast<const uint4*>(gW[i] + kbyte);
-#pragma unroll
-    for (int i = 0; i < S::kLdA; ++i) rA[i] = *reinterpret_cast<const uint4*>(gA[i] + kbyte);
-  }
-  __device__ __forceinline__ void store(uint8_t* s) {
-#pragma unroll
-    for (int i = 0; i < S::kLdW; ++i) *reinterpret_cast<uint4*>(s + oW[i]) = rW[i];
-#pragma unroll
-    for (int i = 0; i < S::kLdA; ++i) *reinterpret_cast<uint4*>(s + oA[i]) = rA[i];
-  }
-};
-
 // LDS row (within the weight tile) of the wave's weight block i (0..3).
 __device__ __forceinline__ int wblock_row(int swiglu, int wn, int i) {
   if (swiglu) return (i < 2 ? 0 : kBN / 2) + wn * 64 + (i & 1) * 32;
   return wn * 128 + i * 32;
-}
-
-template <bool FP8, int MODE, int ROWB>
-__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArgs g) {
-  using S = Stage<ROWB>;
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  __shared__ float row_amax[2][kBM];
-  constexpr bool kSwiglu = MODE != MODE_PLAIN;
-
-  // ---- which tile ----
-  const int total = *g.n_tiles * g.nt_n;
-  const int per_xcd = ceil_div(total, kXcds);
-  const int slot = blockIdx.x / kXcds;
-  if (slot >= per_xcd) return;
-  const int t = (blockIdx.x % kXcds) * per_xcd + slot;
-  if (t >= total) return;
-  const int4 inf = g.info[t / g.nt_n];
-  const int e = inf.x, u = t - inf.y * g.nt_n;
-  const int nt = u / inf.z, mt = u % inf.z;
-  const int seg_end = g.offsets[e + 1];
-  const int row0 = g.offsets[e] + mt * kBM;
-
-  const int64_t ldb = FP8 ? g.K : 2ll * g.K;  // bytes per row of A and W
-  const uint8_t* We = g.W + e * g.w_stride;
-  Loader<ROWB> ld;
-  ld.init(g, kSwiglu, We, ldb, nt, row0, seg_end);
-
-  const int lane = lane_id(), w = threadIdx.x >> 6;
-  const int wm = w & 1, wn = w >> 1;
-  const int lr = lane & 31;
-  const int kq = (lane >> 5) * (FP8 ? 32 : 16);  // byte offset of the lane's k values
-  int offW[4], offA[2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) offW[i] = (kBM + wblock_row(kSwiglu, wn, i) + lr) * S::kPitch + kq;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) offA[j] = (wm * 64 + j * 32 + lr) * S::kPitch + kq;
-
-  // fp8 scale rows
-  const float* swp[4];
-  const float* sxp[2];
-  if (FP8) {
-    const int kb_n = g.K / 128;
-    const float* wsc = g.W_scale + e * g.ws_stride;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int lrow = wblock_row(kSwiglu, wn, i);
-      int grow;
-      if (kSwiglu)
-        grow = lrow < kBN / 2 ? nt * (kBN / 2) + lrow : g.Nout + nt * (kBN / 2) + (lrow - kBN / 2);
-      else
-        grow = min(nt * kBN + lrow, g.NW - 1);
-      swp[i] = wsc + static_cast<int64_t>(grow / 128) * kb_n;
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      sxp[j] = g.A_scale + static_cast<int64_t>(min(row0 + wm * 64 + j * 32 + lr, seg_end - 1)) * kb_n;
-  }
-
-  f32x16 acc[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  const int nk = static_cast<int>(ldb / ROWB);
-  ld.load(0);
-  ld.store(smem);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const uint8_t* s = smem + (kt & 1) * S::kBytes;
-    if (kt + 1 < nk) ld.load(static_cast<int64_t>(kt + 1) * ROWB);
-    if constexpr (!FP8) {
-#pragma unroll
-      for (int kk = 0; kk < ROWB / 32; ++kk) {  // 16 bf16 (32 bytes) per MFMA
-        bf16x8 a[4], b[2];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8*>(s + offW[i] + kk * 32);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) b[j] = *reinterpret_cast<const bf16x8*>(s + offA[j] + kk * 32);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-      }
-    } else {
-      float sw[4], sx[2];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sw[i] = swp[i][kt];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) sx[j] = sxp[j][kt];
-      f32x16 tmp[4][2];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) tmp[i][j][r] = 0.0f;
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {  // 64 e4m3 (64 bytes) per MFMA
-        i32x8 a[4], b[2];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const i32x4 lo = *reinterpret_cast<const i32x4*>(s + offW[i] + kk * 64);
-          const i32x4 hi = *reinterpret_cast<const i32x4*>(s + offW[i] + kk * 64 + 16);
-          a[i] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const i32x4 lo = *reinterpret_cast<const i32x4*>(s + offA[j] + kk * 64);
-          const i32x4 hi = *reinterpret_cast<const i32x4*>(s + offA[j] + kk * 64 + 16);
-          b[j] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            tmp[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], tmp[i][j], 0,
-                                                                        0, 0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const float sc = sw[i] * sx[j];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[i][j][r] += tmp[i][j][r] * sc;
-        }
-    }
-    if (kt + 1 < nk) ld.store(smem + ((kt + 1) & 1) * S::kBytes);
-    __syncthreads();
-  }
-
-  // ---- epilogue ----
-  // Accumulator element q*4 + r of a 32x32 tile is weight row q*8 + (lane/32)*4
-  // + r and token row lane % 32.
-  const int cq = (lane >> 5) * 4;
-  if constexpr (MODE == MODE_PLAIN) {
-    uint16_t* C = static_cast<uint16_t*>(g.C);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int m = row0 + wm * 64 + j * 32 + lr;
-      if (m >= seg_end) continue;
-      uint16_t* crow = C + static_cast<int64_t>(m) * g.Nout;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = nt * kBN + wn * 128 + i * 32 + q * 8 + cq;
-          if (col >= g.Nout) continue;
-          uint2 o;
-          o.x = pack_bf16x2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]);
-          o.y = pack_bf16x2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
-          *reinterpret_cast<uint2*>(crow + col) = o;
-        }
-    }
-  } else {
-    // h = silu(gate) * up, kept in acc[hb][j] (hb = 0, 1).
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[hb][j][r] = silu_mul(acc[hb][j][r], acc[hb + 2][j][r]);
-    if constexpr (MODE == MODE_SWIGLU) {
-      uint16_t* C = static_cast<uint16_t*>(g.C);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int m = row0 + wm * 64 + j * 32 + lr;
-        if (m >= seg_end) continue;
-        uint16_t* crow = C + static_cast<int64_t>(m) * g.Nout;
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            uint2 o;
-            o.x = pack_bf16x2(acc[hb][j][q * 4 + 0], acc[hb][j][q * 4 + 1]);
-            o.y = pack_bf16x2(acc[hb][j][q * 4 + 2], acc[hb][j][q * 4 + 3]);
-            *reinterpret_cast<uint2*>(crow + nt * 128 + wn * 64 + hb * 32 + q * 8 + cq) = o;
-          }
-      }
-    } else {
-      // One 128-column group per row: this wave holds 64 of its columns.
-      float amax[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        float m = 0.0f;
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(acc[hb][j][r]));
-        m = fmaxf(m, __shfl_xor(m, 32));
-        amax[j] = m;
-        if (lane < 32) row_amax[wn][wm * 64 + j * 32 + lr] = m;
-      }
-      __syncthreads();
-      uint8_t* C = static_cast<uint8_t*>(g.C);
-      const int groups = g.Nout / 128;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int lrow = wm * 64 + j * 32 + lr;
-        const float am = fmaxf(amax[j], row_amax[wn ^ 1][lrow]);
-        const float sc = am > 0.0f ? am / 448.0f : 1.0f;
-        const int m = row0 + lrow;
-        if (m >= seg_end) continue;
-        uint8_t* crow = C + static_cast<int64_t>(m) * g.Nout;
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint32_t v = f32x4_to_e4m3x4(acc[hb][j][q * 4 + 0] / sc, acc[hb][j][q * 4 + 1] / sc,
-                                               acc[hb][j][q * 4 + 2] / sc, acc[hb][j][q * 4 + 3] / sc);
-            *reinterpret_cast<uint32_t*>(crow + nt * 128 + wn * 64 + hb * 32 + q * 8 + cq) = v;
-          }
-        if (wn == 0 && lane < 32) g.C_scale[static_cast<int64_t>(m) * groups + nt] = sc;
-      }
-    }
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -390,7 +115,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(const GemmArg
 constexpr int kBufFlags = 0x00020000;  // raw buffer, 32-bit data format
 constexpr int kStages = 3;
 constexpr int kRowBytes = 128;                           // K bytes per row per step
-constexpr int kStageBytes = (kBM + kBN) * kRowBytes;     // 48 KB
+constexpr int kScaleRegion = (kBM + kBN) * kRowBytes;    // fp8 token scales of the step
+constexpr int kStageBytes = kScaleRegion + kBM * 4;      // 48 KB + 512 B
 constexpr int kWRegion = kBM * kRowBytes;                // weight rows start here
 constexpr int kDmaPerWave = (kBM + kBN) / 8 / 4;         // 12 loads of 8 rows per wave
 
@@ -417,8 +143,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pipelined_kernel(const GemmA
   __shared__ float row_amax[2][kBM];
   constexpr bool kSwiglu = MODE != MODE_PLAIN;
   constexpr int kKK = FP8 ? 2 : 4;             // MFMA sub-steps per K step
-  constexpr int kScaleLoads = FP8 ? 6 : 0;     // per-step scale loads per lane
-  constexpr int kWaitStep = kDmaPerWave + kScaleLoads;
+  // Direct loads per wave and step: 12 x 8 rows of operands, plus (fp8) one
+  // 4-byte-per-lane load of token scales.  Every load that the step waits
+  // count tracks is a direct load, so they retire in issue order.
+  constexpr int kDmaStep = kDmaPerWave + (FP8 ? 1 : 0);
 
   const int total = *g.n_tiles * g.nt_n;
   const int per_xcd = ceil_div(total, kXcds);
@@ -434,8 +162,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pipelined_kernel(const GemmA
 
   const int ldb = FP8 ? g.K : 2 * g.K;  // bytes per row of A and W
   const int nk = ldb / kRowBytes;
-  const __amdgpu_buffer_rsrc_t rA =
-      make_rsrc(g.A + static_cast<int64_t>(row0) * ldb, static_cast<int64_t>(seg_end - row0) * ldb);
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(g.A + static_cast<int64_t>(row0) * ldb,
+                                              static_cast<int64_t>(min(seg_end - row0, kBM)) * ldb);
   const __amdgpu_buffer_rsrc_t rW =
       make_rsrc(g.W + e * g.w_stride, static_cast<int64_t>(g.NW) * ldb);
 
@@ -462,13 +190,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pipelined_kernel(const GemmA
     voff[q] = grow * ldb + chunk * 16;
     ldst[q] = grp * 1024;
   }
+  // fp8: token scales of the step, 128 rows x 4 bytes, land beside the
+  // operands (waves 0/1 and 2/3 load the same two halves; the duplicate
+  // writes carry identical values).
+  const int kb_n = g.K / 128;
+  const __amdgpu_buffer_rsrc_t rS =
+      FP8 ? make_rsrc(g.A_scale + static_cast<int64_t>(row0) * kb_n,
+                      static_cast<int64_t>(min(seg_end - row0, kBM)) * kb_n * 4)
+          : make_rsrc(g.A, 0);
+  const int soffs = ((w & 1) * 64 + lane) * kb_n * 4;
   auto dma = [&](int step, int stage) {
-    const int soff = min(step, nk - 1) * kRowBytes;
+    const int k = min(step, nk - 1);
     uint8_t* base = smem + stage * kStageBytes;
 #pragma unroll
     for (int q = 0; q < kDmaPerWave; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(q < 4 ? rA : rW, (lds_ptr_t)(base + ldst[q]), 16,
-                                               voff[q], soff, 0, 0);
+                                               voff[q], k * kRowBytes, 0, 0);
+    if (FP8)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_ptr_t)(base + kScaleRegion + (w & 1) * 256),
+                                               4, soffs, k * 4, 0, 0);
   };
 
   // ---- fragment addressing
@@ -492,16 +232,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pipelined_kernel(const GemmA
 #pragma unroll
   for (int j = 0; j < 2; ++j) abase[j] = (wm * 64 + j * 32) * kRowBytes;
 
-  // ---- fp8 scales
+  // ---- fp8 scales: weight block scales are uniform per wave (scalar
+  // loads); token group scales come from the stage in LDS.
   const float* swp[4];
-  const float* sxp[2];
   float sw[4], sx[2];
   if (FP8) {
-    const int kb_n = g.K / 128;
+    const int wnu = __builtin_amdgcn_readfirstlane(wn);
     const float* wsc = g.W_scale + e * g.ws_stride;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int lrow = wblock_row(kSwiglu, wn, i);
+      const int lrow = wblock_row(kSwiglu, wnu, i);
       int grow;
       if (kSwiglu)
         grow = lrow < kBN / 2 ? nt * (kBN / 2) + lrow : g.Nout + nt * (kBN / 2) + (lrow - kBN / 2);
@@ -509,18 +249,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pipelined_kernel(const GemmA
         grow = min(nt * kBN + lrow, g.NW - 1);
       swp[i] = wsc + static_cast<int64_t>(grow / 128) * kb_n;
     }
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      sxp[j] = g.A_scale +
-               static_cast<int64_t>(min(row0 + wm * 64 + j * 32 + lr, seg_end - 1)) * kb_n;
   }
-  auto load_scales = [&](int step) {
+  auto load_wscales = [&](int step) {
     if (FP8) {
+      // Through the constant address space: uniform loads become scalar
+      // loads, which the step's vector-memory wait count does not see.
       const int k = min(step, nk - 1);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sw[i] = swp[i][k];
+      for (int i = 0; i < 4; ++i)
+        sw[i] = ((const __attribute__((address_space(4))) float*)(uintptr_t)swp[i])[k];
+    }
+  };
+  auto read_xscales = [&](const uint8_t* st) {
+    if (FP8) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) sx[j] = sxp[j][k];
+      for (int j = 0; j < 2; ++j)
+        sx[j] = *reinterpret_cast<const float*>(st + kScaleRegion + (wm * 64 + j * 32 + lr) * 4);
     }
   };
 
@@ -588,12 +332,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pipelined_kernel(const GemmA
     }
   };
 
-  // ---- prologue: steps 0, 1 (+ scales of step 0), 2 in flight
+  // ---- prologue: steps 0, 1, 2 in flight
   dma(0, 0);
   dma(1, 1);
-  load_scales(0);
   dma(2, 2);
-  WAIT_VMCNT(kDmaPerWave + kScaleLoads + kDmaPerWave);
+  load_wscales(0);
+  WAIT_VMCNT(2 * kDmaStep);
   __builtin_amdgcn_s_barrier();
   lfrag(smem, 0, 0);
 
@@ -614,18 +358,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pipelined_kernel(const GemmA
       if (!FP8) SCHED(kSchedMfma, 2);
     }
     constexpr int last = (kKK - 1) & 1;
+    read_xscales(cur);
     mma(last, 0, 4);
-    // Step boundary: this wave's loads of step kt+1 have landed once at most
-    // the later group (scales of kt+1 if fp8, loads of kt+2) is in flight,
-    // and its own reads of stage kt are done before anyone refills it.
-    WAIT_VMCNT_LDS(kWaitStep);
+    // Step boundary: this wave's loads of step kt+1 have landed once only
+    // those of step kt+2 are in flight, and its own reads of stage kt are
+    // done before anyone refills it.
+    WAIT_VMCNT_LDS(kDmaStep);
     __builtin_amdgcn_s_barrier();
     // Stage kt is free in every wave now; refill it with step kt+3.
     lfrag(nxt, 0, 0);
     mma(last, 4, 4);
     if (FP8) {
       scale_acc();
-      load_scales(kt + 1);
+      load_wscales(kt + 1);
     }
     dma(kt + 3, cur_stage);
 #pragma unroll
@@ -738,12 +483,216 @@ hipError_t launch_pipelined(const GemmArgs& g, int64_t max_tiles, hipStream_t s)
   return hipGetLastError();
 }
 
-template <bool FP8, int MODE, int ROWB>
-hipError_t launch_one(const GemmArgs& g, int64_t max_tiles, hipStream_t s) {
-  auto kern = grouped_gemm_kernel<FP8, MODE, ROWB>;
-  const size_t lds = 2 * Stage<ROWB>::kBytes;
-  // Allow more than 64 KB of dynamic LDS (gfx950 has 160 KB per CU).  If
-  // the runtime refuses, the launch below reports the problem.
+// ---------------------------------------------------------------------------
+// Large-tile bf16 kernel: 256 token rows x 256 weight rows per block, 4 waves
+// in a 2 x 2 arrangement with 128 x 128 per wave (4 x 4 MFMA 32x32 tiles).
+// The 128 x 256 tile is bound by the L2's request rate (its L2 stays busy
+// while the matrix cores wait); this tile needs a third fewer 128-byte L2
+// requests per FLOP.  A K step is 64 bf16 (one full 128-byte line of each
+// row), staged through two 64 KB LDS buffers fed by direct-to-LDS loads: the
+// loads of step kt+1 go out at the start of step kt, behind 64 MFMAs per wave.
+// Rows use the same chunk ^ ((row >> 1) & 7) swizzle as the 128 x 256 kernel.
+// ---------------------------------------------------------------------------
+constexpr int kBigBM = 256, kBigBN = 256;
+constexpr int kBigRowBytes = 128;
+constexpr int kBigStages = 2;
+constexpr int kBigStageBytes = (kBigBM + kBigBN) * kBigRowBytes;  // 64 KB
+constexpr int kBigWRegion = kBigBM * kBigRowBytes;
+constexpr int kBigDmaPerWave = (kBigBM + kBigBN) / 8 / 4;       // 16 loads of 8 rows per wave
+
+__device__ __forceinline__ int big_wblock_row(int swiglu, int wn, int i) {
+  if (swiglu) return (i < 2 ? 0 : kBigBN / 2) + wn * 64 + (i & 1) * 32;
+  return wn * 128 + i * 32;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(const GemmArgs g) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  constexpr bool kSwiglu = MODE != MODE_PLAIN;
+
+  const int total = *g.n_tiles * g.nt_n;
+  const int per_xcd = ceil_div(total, kXcds);
+  const int slot = blockIdx.x / kXcds;
+  if (slot >= per_xcd) return;
+  const int t = (blockIdx.x % kXcds) * per_xcd + slot;
+  if (t >= total) return;
+  const int4 inf = g.info[t / g.nt_n];
+  const int e = inf.x, u = t - inf.y * g.nt_n;
+  const int nt = u / inf.z, mt = u % inf.z;
+  const int seg_end = g.offsets[e + 1];
+  const int row0 = g.offsets[e] + mt * kBigBM;
+
+  const int ldb = 2 * g.K;
+  const int nk = ldb / kBigRowBytes;
+  // Only this tile's rows are in range; the rest of the tile reads as zero.
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(g.A + static_cast<int64_t>(row0) * ldb,
+                                              static_cast<int64_t>(min(seg_end - row0, kBigBM)) * ldb);
+  const __amdgpu_buffer_rsrc_t rW =
+      make_rsrc(g.W + e * g.w_stride, static_cast<int64_t>(g.NW) * ldb);
+
+  const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
+  // direct loads: wave w moves 8-row groups w*8+q of A (q < 8) and
+  // 32 + w*8 + (q-8) of W.
+  int voff[kBigDmaPerWave], ldst[kBigDmaPerWave];
+#pragma unroll
+  for (int q = 0; q < kBigDmaPerWave; ++q) {
+    const int grp = q < 8 ? w * 8 + q : 32 + w * 8 + (q - 8);
+    const int rr = grp * 8 + (lane >> 3);
+    const int chunk = (lane & 7) ^ ((rr >> 1) & 7);
+    int grow;
+    if (rr < kBigBM) {
+      grow = rr;
+    } else {
+      const int r = rr - kBigBM;
+      if (kSwiglu)
+        grow = r < kBigBN / 2 ? min(nt * (kBigBN / 2) + r, g.Nout - 1)
+                              : g.Nout + min(nt * (kBigBN / 2) + (r - kBigBN / 2), g.Nout - 1);
+      else
+        grow = min(nt * kBigBN + r, g.NW - 1);
+    }
+    voff[q] = grow * ldb + chunk * 16;
+    ldst[q] = grp * 1024;
+  }
+  auto dma = [&](int step, int stage) {
+    const int soff = min(step, nk - 1) * kBigRowBytes;
+    uint8_t* base = smem + stage * kBigStageBytes;
+#pragma unroll
+    for (int q = 0; q < kBigDmaPerWave; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(q < 8 ? rA : rW, (lds_ptr_t)(base + ldst[q]), 16,
+                                               voff[q], soff, 0, 0);
+  };
+
+  const int wm = w & 1, wn = w >> 1;
+  const int lr = lane & 31, hi = lane >> 5, sl = (lr >> 1) & 7;
+  int foff[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) foff[kk] = lr * kBigRowBytes + (((2 * kk) | hi) ^ sl) * 16;
+  int wbase[4], abase[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) wbase[i] = kBigWRegion + big_wblock_row(kSwiglu, wn, i) * kBigRowBytes;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) abase[j] = (wm * 128 + j * 32) * kBigRowBytes;
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  bf16x8 fa[2][4], fb[2][4];
+  auto lfrag = [&](const uint8_t* st, int kk, int set) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[set][i] = *reinterpret_cast<const bf16x8*>(st + wbase[i] + foff[kk]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fb[set][j] = *reinterpret_cast<const bf16x8*>(st + abase[j] + foff[kk]);
+  };
+  auto mma = [&](int set, int first, int count) {
+#pragma unroll
+    for (int q = first; q < first + count; ++q) {
+      const int i = q >> 2, j = q & 3;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  dma(0, 0);
+  WAIT_VMCNT(0);
+  __builtin_amdgcn_s_barrier();
+  lfrag(smem, 0, 0);
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const uint8_t* cur = smem + (kt & 1) * kBigStageBytes;
+    const uint8_t* nxt = smem + ((kt + 1) & 1) * kBigStageBytes;
+    // The other stage was released by the barrier that ended step kt - 1.
+    dma(kt + 1, (kt + 1) & 1);
+    lfrag(cur, 1, 1);
+    mma(0, 0, 16);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      SCHED(kSchedMfma, 1);
+      SCHED(kSchedVmemRead, 2);
+      SCHED(kSchedDsRead, 1);
+    }
+    SCHED(kSchedMfma, 8);
+    lfrag(cur, 2, 0);
+    mma(1, 0, 16);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      SCHED(kSchedMfma, 2);
+      SCHED(kSchedDsRead, 1);
+    }
+    lfrag(cur, 3, 1);
+    mma(0, 0, 16);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      SCHED(kSchedMfma, 2);
+      SCHED(kSchedDsRead, 1);
+    }
+    mma(1, 0, 8);
+    // Step boundary: step kt+1 has landed; this wave's reads of stage kt are done.
+    WAIT_VMCNT_LDS(0);
+    __builtin_amdgcn_s_barrier();
+    lfrag(nxt, 0, 0);
+    mma(1, 8, 8);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      SCHED(kSchedDsRead, 1);
+      SCHED(kSchedMfma, 1);
+    }
+  }
+
+  const int cq = (lane >> 5) * 4;
+  uint16_t* C = static_cast<uint16_t*>(g.C);
+  if constexpr (MODE == MODE_PLAIN) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int m = row0 + wm * 128 + j * 32 + lr;
+      if (m >= seg_end) continue;
+      uint16_t* crow = C + static_cast<int64_t>(m) * g.Nout;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = nt * kBigBN + wn * 128 + i * 32 + q * 8 + cq;
+          if (col >= g.Nout) continue;
+          uint2 o;
+          o.x = pack_bf16x2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]);
+          o.y = pack_bf16x2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
+          *reinterpret_cast<uint2*>(crow + col) = o;
+        }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int m = row0 + wm * 128 + j * 32 + lr;
+      if (m >= seg_end) continue;
+      uint16_t* crow = C + static_cast<int64_t>(m) * g.Nout;
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = nt * (kBigBN / 2) + wn * 64 + hb * 32 + q * 8 + cq;
+          if (col >= g.Nout) continue;
+          float hv[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float gt = acc[hb][j][q * 4 + r], up = acc[hb + 2][j][q * 4 + r];
+            hv[r] = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
+          }
+          uint2 o;
+          o.x = pack_bf16x2(hv[0], hv[1]);
+          o.y = pack_bf16x2(hv[2], hv[3]);
+          *reinterpret_cast<uint2*>(crow + col) = o;
+        }
+    }
+  }
+}
+
+template <int MODE>
+hipError_t launch_big(const GemmArgs& g, int64_t max_tiles, hipStream_t s) {
+  auto kern = gemm_big_kernel<MODE>;
+  const size_t lds = kBigStages * kBigStageBytes;
   static bool attr_set = false;
   if (!attr_set) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -752,7 +701,6 @@ hipError_t launch_one(const GemmArgs& g, int64_t max_tiles, hipStream_t s) {
       (void)hipGetLastError();
     attr_set = true;
   }
-  // Enough blocks for every live tile after the per-XCD split.
   const int64_t blocks = (max_tiles * g.nt_n + kXcds - 1) / kXcds * kXcds + kXcds;
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), lds, s, g);
   return hipGetLastError();
@@ -760,11 +708,16 @@ hipError_t launch_one(const GemmArgs& g, int64_t max_tiles, hipStream_t s) {
 
 }  // namespace
 
-int64_t max_m_tiles(int64_t n_cap, int E_L) { return ceil_div<int64_t>(n_cap, kBM) + E_L; }
+int64_t max_m_tiles(int64_t n_cap, int E_L, int tile_m) {
+  return ceil_div<int64_t>(n_cap, tile_m) + E_L;
+}
 
-hipError_t launch_tile_schedule(const int32_t* offsets, int E_L, int4* info, int32_t* n_tiles,
-                                hipStream_t s) {
-  hipLaunchKernelGGL(tile_schedule_kernel, dim3(1), dim3(1024), 0, s, offsets, E_L, info, n_tiles);
+int gemm_tile_m(bool fp8) { return fp8 ? kBM : kBigBM; }
+
+hipError_t launch_tile_schedule(const int32_t* offsets, int E_L, int tile_m, int4* info,
+                                int32_t* n_tiles, hipStream_t s) {
+  hipLaunchKernelGGL(tile_schedule_kernel, dim3(1), dim3(1024), 0, s, offsets, E_L, tile_m, info,
+                     n_tiles);
   return hipGetLastError();
 }
 
@@ -782,13 +735,14 @@ hipError_t launch_grouped_gemm(const GemmLaunch& L, hipStream_t s) {
   g.K = L.K;
   g.Nout = L.Nout;
   g.NW = L.swiglu ? 2 * L.Nout : L.Nout;
-  g.nt_n = L.swiglu ? L.Nout / (kBN / 2) : ceil_div(L.Nout, kBN);
+  const int bn = L.fp8 ? kBN : kBigBN;
+  g.nt_n = L.swiglu ? ceil_div(L.Nout, bn / 2) : ceil_div(L.Nout, bn);
   const int64_t elem = L.fp8 ? 1 : 2;
   g.w_stride = static_cast<int64_t>(g.NW) * L.K * elem;
   g.ws_stride = L.fp8 ? static_cast<int64_t>(g.NW / 128) * (L.K / 128) : 0;
   if (!L.fp8) {
-    if (L.swiglu) return launch_pipelined<false, MODE_SWIGLU>(g, L.max_tiles, s);
-    return launch_pipelined<false, MODE_PLAIN>(g, L.max_tiles, s);
+    if (L.swiglu) return launch_big<MODE_SWIGLU>(g, L.max_tiles, s);
+    return launch_big<MODE_PLAIN>(g, L.max_tiles, s);
   }
   if (L.swiglu) {
     if (L.C_scale) return launch_pipelined<true, MODE_SWIGLU_FP8OUT>(g, L.max_tiles, s);

@@ -25,9 +25,11 @@ hipError_t launch_gather_fp8(const void* src, const int32_t* rows, const int32_t
 hipError_t launch_quant_blocks(const void* src, int64_t batch, int64_t rows, int64_t cols,
                                void* codes, float* scales, hipStream_t s);
 
-int64_t max_m_tiles(int64_t n_cap, int E_L);
-hipError_t launch_tile_schedule(const int32_t* offsets, int E_L, int4* info, int32_t* n_tiles,
-                                hipStream_t s);
+// Row tile of the grouped GEMM kernels (the m-tile list must be built with it).
+int gemm_tile_m(bool fp8);
+int64_t max_m_tiles(int64_t n_cap, int E_L, int tile_m);
+hipError_t launch_tile_schedule(const int32_t* offsets, int E_L, int tile_m, int4* info,
+                                int32_t* n_tiles, hipStream_t s);
 struct GemmLaunch {
   bool fp8;              // e4m3 operands with block scales, else bf16
   bool swiglu;           // up GEMM with the SwiGLU epilogue, else plain

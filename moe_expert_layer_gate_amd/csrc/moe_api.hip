@@ -32,6 +32,9 @@ moe_status check_problem(const moe_problem* p) {
   if (I < 128 || I > 65536 || I % 128) return MOE_ERR_INVALID_ARG;
   if (Is < 0 || Is > 65536 || Is % 128) return MOE_ERR_INVALID_ARG;
   if (p->dtype != MOE_BF16 && p->dtype != MOE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
+  // One expert's weight matrix must stay below 2 GiB (32-bit buffer offsets).
+  if (4 * I * H >= (int64_t(1) << 31) || 4 * Is * H >= (int64_t(1) << 31))
+    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -66,7 +69,7 @@ struct FfnScratch {
 FfnScratch carve_ffn(Carve& c, const moe_problem* p) {
   const int64_t N = n_cap(p), I = p->inter;
   FfnScratch f{};
-  f.info = c.take<int4>(sizeof(int4) * max_m_tiles(N, p->num_local));
+  f.info = c.take<int4>(sizeof(int4) * max_m_tiles(N, p->num_local, gemm_tile_m(is_fp8(p))));
   f.n_tiles = c.take<int32_t>(sizeof(int32_t));
   if (is_fp8(p)) {
     f.h = c.take<void>(N * I);
@@ -152,10 +155,11 @@ moe_status run_ffn(const moe_problem* p, const void* x_perm, const float* x_perm
                    void* y_perm, const FfnScratch& f, hipStream_t s) {
   const int64_t N = n_cap(p);
   const int E_L = p->num_local, H = p->hidden, I = p->inter;
-  const int64_t mt = max_m_tiles(N, E_L);
+  const int tile_m = gemm_tile_m(is_fp8(p));
+  const int64_t mt = max_m_tiles(N, E_L, tile_m);
   void* hb = h ? h : f.h;
   float* hs = h ? h_scale : f.h_scale;
-  MOE_TRY(launch_tile_schedule(offsets, E_L, f.info, f.n_tiles, s));
+  MOE_TRY(launch_tile_schedule(offsets, E_L, tile_m, f.info, f.n_tiles, s));
   GemmLaunch up{};
   up.fp8 = is_fp8(p);
   up.swiglu = true;

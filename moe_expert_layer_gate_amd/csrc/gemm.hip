@@ -484,21 +484,27 @@ hipError_t launch_pipelined(const GemmArgs& g, int64_t max_tiles, hipStream_t s)
 }
 
 // ---------------------------------------------------------------------------
-// Large-tile bf16 kernel: 256 token rows x 256 weight rows per block, 4 waves
-// in a 2 x 2 arrangement with 128 x 128 per wave (4 x 4 MFMA 32x32 tiles).
-// The 128 x 256 tile is bound by the L2's request rate (its L2 stays busy
-// while the matrix cores wait); this tile needs a third fewer 128-byte L2
-// requests per FLOP.  A K step is 64 bf16 (one full 128-byte line of each
-// row), staged through two 64 KB LDS buffers fed by direct-to-LDS loads: the
-// loads of step kt+1 go out at the start of step kt, behind 64 MFMAs per wave.
-// Rows use the same chunk ^ ((row >> 1) & 7) swizzle as the 128 x 256 kernel.
+// Large-tile bf16 kernel: 256 token rows x 256 weight rows per block, 8 waves
+// (two per SIMD) in a 4 (rows) x 2 (weights) arrangement, 64 x 128 per wave
+// (2 x 4 MFMA 32x32 tiles).
+//  * Tile size: relative to a 128 x 256 tile it moves a third fewer bytes
+//    from L2 per FLOP.
+//  * Eight waves: direct-to-LDS loads complete at a rate set by how many
+//    waves have loads in flight (about 30 B/clk per CU from four waves, 50
+//    from eight, measured on the MI355X), and this tile needs ~32 B/clk per
+//    CU at the full MFMA rate.
+//  * K advances 32 bf16 (a 64-byte row piece) per step through a four-stage
+//    LDS ring; loads run three steps ahead.  The swizzle for 64-byte rows is
+//    chunk ^ ((row >> 2) & 3): the 16 rows read together by one fragment load
+//    cover every (row mod 4, chunk) pair, i.e. all LDS banks once.
 // ---------------------------------------------------------------------------
 constexpr int kBigBM = 256, kBigBN = 256;
-constexpr int kBigRowBytes = 128;
-constexpr int kBigStages = 2;
-constexpr int kBigStageBytes = (kBigBM + kBigBN) * kBigRowBytes;  // 64 KB
+constexpr int kBigThreads = 512;
+constexpr int kBigRowBytes = 64;
+constexpr int kBigStages = 4;
+constexpr int kBigStageBytes = (kBigBM + kBigBN) * kBigRowBytes;  // 32 KB
 constexpr int kBigWRegion = kBigBM * kBigRowBytes;
-constexpr int kBigDmaPerWave = (kBigBM + kBigBN) / 8 / 4;       // 16 loads of 8 rows per wave
+constexpr int kBigDmaPerWave = (kBigBM + kBigBN) / 16 / 8;      // 4 loads of 16 rows per wave
 
 __device__ __forceinline__ int big_wblock_row(int swiglu, int wn, int i) {
   if (swiglu) return (i < 2 ? 0 : kBigBN / 2) + wn * 64 + (i & 1) * 32;
@@ -506,7 +512,7 @@ __device__ __forceinline__ int big_wblock_row(int swiglu, int wn, int i) {
 }
 
 template <int MODE>
-__global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(const GemmArgs g) {
+__global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const GemmArgs g) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   constexpr bool kSwiglu = MODE != MODE_PLAIN;
 
@@ -531,14 +537,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(const GemmArgs g)
       make_rsrc(g.W + e * g.w_stride, static_cast<int64_t>(g.NW) * ldb);
 
   const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
-  // direct loads: wave w moves 8-row groups w*8+q of A (q < 8) and
-  // 32 + w*8 + (q-8) of W.
+  // direct loads: wave w moves 16-row groups 2w, 2w+1 of A and 16+2w, 17+2w
+  // of W (A rows 0..255 are groups 0..15, W rows groups 16..31).
   int voff[kBigDmaPerWave], ldst[kBigDmaPerWave];
 #pragma unroll
   for (int q = 0; q < kBigDmaPerWave; ++q) {
-    const int grp = q < 8 ? w * 8 + q : 32 + w * 8 + (q - 8);
-    const int rr = grp * 8 + (lane >> 3);
-    const int chunk = (lane & 7) ^ ((rr >> 1) & 7);
+    const int grp = q < 2 ? w * 2 + q : 16 + w * 2 + (q - 2);
+    const int rr = grp * 16 + (lane >> 2);
+    const int chunk = (lane & 3) ^ ((rr >> 2) & 3);
     int grow;
     if (rr < kBigBM) {
       grow = rr;
@@ -558,96 +564,86 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(const GemmArgs g)
     uint8_t* base = smem + stage * kBigStageBytes;
 #pragma unroll
     for (int q = 0; q < kBigDmaPerWave; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(q < 8 ? rA : rW, (lds_ptr_t)(base + ldst[q]), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(q < 2 ? rA : rW, (lds_ptr_t)(base + ldst[q]), 16,
                                                voff[q], soff, 0, 0);
   };
 
-  const int wm = w & 1, wn = w >> 1;
-  const int lr = lane & 31, hi = lane >> 5, sl = (lr >> 1) & 7;
-  int foff[4];
+  const int wm = w & 3, wn = w >> 2;
+  const int lr = lane & 31, hi = lane >> 5, sl = (lr >> 2) & 3;
+  int foff[2];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) foff[kk] = lr * kBigRowBytes + (((2 * kk) | hi) ^ sl) * 16;
-  int wbase[4], abase[4];
+  for (int kk = 0; kk < 2; ++kk) foff[kk] = lr * kBigRowBytes + (((2 * kk) | hi) ^ sl) * 16;
+  int wbase[4], abase[2];
 #pragma unroll
   for (int i = 0; i < 4; ++i) wbase[i] = kBigWRegion + big_wblock_row(kSwiglu, wn, i) * kBigRowBytes;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) abase[j] = (wm * 128 + j * 32) * kBigRowBytes;
+  for (int j = 0; j < 2; ++j) abase[j] = (wm * 64 + j * 32) * kBigRowBytes;
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  bf16x8 fa[2][4], fb[2][4];
+  bf16x8 fa[2][4], fb[2][2];
   auto lfrag = [&](const uint8_t* st, int kk, int set) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) fa[set][i] = *reinterpret_cast<const bf16x8*>(st + wbase[i] + foff[kk]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) fb[set][j] = *reinterpret_cast<const bf16x8*>(st + abase[j] + foff[kk]);
+    for (int j = 0; j < 2; ++j) fb[set][j] = *reinterpret_cast<const bf16x8*>(st + abase[j] + foff[kk]);
   };
   auto mma = [&](int set, int first, int count) {
 #pragma unroll
     for (int q = first; q < first + count; ++q) {
-      const int i = q >> 2, j = q & 3;
+      const int i = q >> 1, j = q & 1;
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j], acc[i][j], 0, 0, 0);
     }
   };
 
   dma(0, 0);
-  WAIT_VMCNT(0);
+  dma(1, 1);
+  dma(2, 2);
+  WAIT_VMCNT(2 * kBigDmaPerWave);
   __builtin_amdgcn_s_barrier();
   lfrag(smem, 0, 0);
 
   for (int kt = 0; kt < nk; ++kt) {
-    const uint8_t* cur = smem + (kt & 1) * kBigStageBytes;
-    const uint8_t* nxt = smem + ((kt + 1) & 1) * kBigStageBytes;
-    // The other stage was released by the barrier that ended step kt - 1.
-    dma(kt + 1, (kt + 1) & 1);
+    const uint8_t* cur = smem + (kt % kBigStages) * kBigStageBytes;
+    const uint8_t* nxt = smem + ((kt + 1) % kBigStages) * kBigStageBytes;
+    // Stage (kt + 3) % 4 was released by the barrier that ended step kt - 1.
+    dma(kt + 3, (kt + 3) % kBigStages);
     lfrag(cur, 1, 1);
-    mma(0, 0, 16);
+    mma(0, 0, 8);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < 6; ++q) {
       SCHED(kSchedMfma, 1);
-      SCHED(kSchedVmemRead, 2);
       SCHED(kSchedDsRead, 1);
+      SCHED(kSchedVmemRead, 1);
     }
-    SCHED(kSchedMfma, 8);
-    lfrag(cur, 2, 0);
-    mma(1, 0, 16);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      SCHED(kSchedMfma, 2);
-      SCHED(kSchedDsRead, 1);
-    }
-    lfrag(cur, 3, 1);
-    mma(0, 0, 16);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      SCHED(kSchedMfma, 2);
-      SCHED(kSchedDsRead, 1);
-    }
-    mma(1, 0, 8);
-    // Step boundary: step kt+1 has landed; this wave's reads of stage kt are done.
-    WAIT_VMCNT_LDS(0);
+    SCHED(kSchedMfma, 2);
+    mma(1, 0, 4);
+    // Step boundary: step kt+1 has landed once only steps kt+2 and kt+3 are
+    // in flight; this wave's reads of stage kt are done.
+    WAIT_VMCNT_LDS(2 * kBigDmaPerWave);
     __builtin_amdgcn_s_barrier();
     lfrag(nxt, 0, 0);
-    mma(1, 8, 8);
+    mma(1, 4, 4);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      SCHED(kSchedDsRead, 1);
+    for (int q = 0; q < 4; ++q) {
+      SCHED(kSchedDsRead, 2);
       SCHED(kSchedMfma, 1);
     }
   }
+  WAIT_VMCNT(0);
 
   const int cq = (lane >> 5) * 4;
   uint16_t* C = static_cast<uint16_t*>(g.C);
   if constexpr (MODE == MODE_PLAIN) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int m = row0 + wm * 128 + j * 32 + lr;
+    for (int j = 0; j < 2; ++j) {
+      const int m = row0 + wm * 64 + j * 32 + lr;
       if (m >= seg_end) continue;
       uint16_t* crow = C + static_cast<int64_t>(m) * g.Nout;
 #pragma unroll
@@ -664,8 +660,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(const GemmArgs g)
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int m = row0 + wm * 128 + j * 32 + lr;
+    for (int j = 0; j < 2; ++j) {
+      const int m = row0 + wm * 64 + j * 32 + lr;
       if (m >= seg_end) continue;
       uint16_t* crow = C + static_cast<int64_t>(m) * g.Nout;
 #pragma unroll
@@ -702,7 +698,7 @@ hipError_t launch_big(const GemmArgs& g, int64_t max_tiles, hipStream_t s) {
     attr_set = true;
   }
   const int64_t blocks = (max_tiles * g.nt_n + kXcds - 1) / kXcds * kXcds + kXcds;
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), lds, s, g);
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(kBigThreads), lds, s, g);
   return hipGetLastError();
 }
 

@@ -708,7 +708,11 @@ int64_t max_m_tiles(int64_t n_cap, int E_L, int tile_m) {
   return ceil_div<int64_t>(n_cap, tile_m) + E_L;
 }
 
-int gemm_tile_m(bool fp8) { return fp8 ? kBM : kBigBM; }
+int gemm_tile_m(bool fp8, int64_t rows_per_expert) {
+  // Few rows per expert (decode-sized batches): the 256-row tile would spend
+  // most of its matrix-core time on padding while the work is weight streaming.
+  return (fp8 || rows_per_expert <= 2 * kBM) ? kBM : kBigBM;
+}
 
 hipError_t launch_tile_schedule(const int32_t* offsets, int E_L, int tile_m, int4* info,
                                 int32_t* n_tiles, hipStream_t s) {
@@ -731,14 +735,18 @@ hipError_t launch_grouped_gemm(const GemmLaunch& L, hipStream_t s) {
   g.K = L.K;
   g.Nout = L.Nout;
   g.NW = L.swiglu ? 2 * L.Nout : L.Nout;
-  const int bn = L.fp8 ? kBN : kBigBN;
+  const int bn = L.tile_m == kBigBM ? kBigBN : kBN;
   g.nt_n = L.swiglu ? ceil_div(L.Nout, bn / 2) : ceil_div(L.Nout, bn);
   const int64_t elem = L.fp8 ? 1 : 2;
   g.w_stride = static_cast<int64_t>(g.NW) * L.K * elem;
   g.ws_stride = L.fp8 ? static_cast<int64_t>(g.NW / 128) * (L.K / 128) : 0;
   if (!L.fp8) {
-    if (L.swiglu) return launch_big<MODE_SWIGLU>(g, L.max_tiles, s);
-    return launch_big<MODE_PLAIN>(g, L.max_tiles, s);
+    if (L.tile_m == kBigBM) {
+      if (L.swiglu) return launch_big<MODE_SWIGLU>(g, L.max_tiles, s);
+      return launch_big<MODE_PLAIN>(g, L.max_tiles, s);
+    }
+    if (L.swiglu) return launch_pipelined<false, MODE_SWIGLU>(g, L.max_tiles, s);
+    return launch_pipelined<false, MODE_PLAIN>(g, L.max_tiles, s);
   }
   if (L.swiglu) {
     if (L.C_scale) return launch_pipelined<true, MODE_SWIGLU_FP8OUT>(g, L.max_tiles, s);

@@ -25,8 +25,9 @@ hipError_t launch_gather_fp8(const void* src, const int32_t* rows, const int32_t
 hipError_t launch_quant_blocks(const void* src, int64_t batch, int64_t rows, int64_t cols,
                                void* codes, float* scales, hipStream_t s);
 
-// Row tile of the grouped GEMM kernels (the m-tile list must be built with it).
-int gemm_tile_m(bool fp8);
+// Row tile of the grouped GEMM for a problem (the m-tile list must be built
+// with it): 128 for block-FP8 and for few rows per expert, else 256.
+int gemm_tile_m(bool fp8, int64_t rows_per_expert);
 int64_t max_m_tiles(int64_t n_cap, int E_L, int tile_m);
 hipError_t launch_tile_schedule(const int32_t* offsets, int E_L, int tile_m, int4* info,
                                 int32_t* n_tiles, hipStream_t s);
@@ -43,6 +44,7 @@ struct GemmLaunch {
   const int4* info;
   const int32_t* n_tiles;
   int64_t max_tiles;
+  int tile_m;            // gemm_tile_m() of the problem
   int K, Nout;
 };
 hipError_t launch_grouped_gemm(const GemmLaunch& L, hipStream_t s);

@@ -69,7 +69,8 @@ struct FfnScratch {
 FfnScratch carve_ffn(Carve& c, const moe_problem* p) {
   const int64_t N = n_cap(p), I = p->inter;
   FfnScratch f{};
-  f.info = c.take<int4>(sizeof(int4) * max_m_tiles(N, p->num_local, gemm_tile_m(is_fp8(p))));
+  f.info = c.take<int4>(sizeof(int4) *
+                        max_m_tiles(N, p->num_local, gemm_tile_m(is_fp8(p), N / p->num_local)));
   f.n_tiles = c.take<int32_t>(sizeof(int32_t));
   if (is_fp8(p)) {
     f.h = c.take<void>(N * I);
@@ -155,7 +156,7 @@ moe_status run_ffn(const moe_problem* p, const void* x_perm, const float* x_perm
                    void* y_perm, const FfnScratch& f, hipStream_t s) {
   const int64_t N = n_cap(p);
   const int E_L = p->num_local, H = p->hidden, I = p->inter;
-  const int tile_m = gemm_tile_m(is_fp8(p));
+  const int tile_m = gemm_tile_m(is_fp8(p), N / E_L);
   const int64_t mt = max_m_tiles(N, E_L, tile_m);
   void* hb = h ? h : f.h;
   float* hs = h ? h_scale : f.h_scale;
@@ -173,6 +174,7 @@ moe_status run_ffn(const moe_problem* p, const void* x_perm, const float* x_perm
   up.info = f.info;
   up.n_tiles = f.n_tiles;
   up.max_tiles = mt;
+  up.tile_m = tile_m;
   up.K = H;
   up.Nout = I;
   MOE_TRY(launch_grouped_gemm(up, s));

@@ -99,6 +99,10 @@ SMALL = {
     "shard": (small_cfg(T=257, H=512, E=16, E_L=4, e_lo=4, k=4, I=256), 6),
     "k_eq_E": (small_cfg(T=130, H=128, E=4, E_L=4, k=4, I=128), 7),
     "qwen3_shape_T512": (dataclasses.replace(synth.config(2), T=512), 2),
+    # enough rows per expert for the 256-row tile; ragged N in both GEMMs
+    "big_tile_ragged": (small_cfg(T=2048, H=384, E=8, E_L=8, k=2, I=384), 10),
+    "big_tile_shard": (small_cfg(T=1500, H=512, E=16, E_L=4, e_lo=12, k=4, I=640,
+                                 logits="gumbel_zipf"), 11),
 }
 SMALL_FP8 = {
     "fp8_small": (small_cfg(T=200, H=512, E=16, E_L=8, e_lo=0, k=4, I=256, fp8=True), 8),

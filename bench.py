@@ -34,6 +34,10 @@ def parse():
     ap.add_argument("--cpu-sample-tokens", type=int, default=None,
                     help="tokens of the workload the CPU oracle runs on (0 = skip)")
     ap.add_argument("--ffn-reps", type=int, default=None)
+    ap.add_argument("--layout", choices=("panel", "rows"), default="panel",
+                    help="bf16 storage: panel = weights packed once at load time and panel "
+                         "activations in the staged calls (moe_layer always keeps its own "
+                         "activations in panel layout); rows = everything row major")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="finish with three 1 GiB device copies (a known-size reference "
                          "for the FETCH_SIZE / WRITE_SIZE counters)")
@@ -85,8 +89,12 @@ def main():
     dev_id = int(os.environ.get("LOCAL_RANK", "0"))
     torch.cuda.set_device(dev_id)
     d = synth.make_inputs(cfg, seed)
-    dev = dv.upload(d, cfg.fp8)
-    p = ml.Problem.from_config(cfg)
+    panel = args.layout == "panel" and not cfg.fp8
+    dev = dv.upload(d, cfg.fp8, panel=panel)   # load-time packing, outside any timing
+    p = ml.Problem.from_config(cfg, layout=ml.LAYOUT_PANEL_WEIGHTS if panel else 0)
+    # the staged calls run with the layouts moe_layer uses inside
+    p_st = ml.Problem.from_config(
+        cfg, layout=(ml.LAYOUT_PANEL_WEIGHTS | ml.LAYOUT_PANEL_ACTS) if panel else 0)
     W = dv.weights_of(dev, cfg.fp8)
     ws = dv.workspace(p)
     y = torch.empty((p.T, p.H), dtype=torch.bfloat16, device="cuda")
@@ -130,13 +138,13 @@ def main():
     for it in range(max(3, min(args.steps, 10))):
         e = [ev() for _ in range(5)]
         e[0].record(stream)
-        ml.moe_route(p, dev["logits"], ids, tw, stream)
+        ml.moe_route(p_st, dev["logits"], ids, tw, stream)
         e[1].record(stream)
-        ml.moe_dispatch(p, dev["x"], ids, counts, offsets, rt, rs, tsr, xp, xs, ws_d, stream)
+        ml.moe_dispatch(p_st, dev["x"], ids, counts, offsets, rt, rs, tsr, xp, xs, ws_d, stream)
         e[2].record(stream)
-        ml.moe_grouped_ffn(p, xp, xs, offsets, W, None, None, yp, ws_f, stream)
+        ml.moe_grouped_ffn(p_st, xp, xs, offsets, W, None, None, yp, ws_f, stream)
         e[3].record(stream)
-        ml.moe_combine(p, yp, tsr, tw, None, y, stream)
+        ml.moe_combine(p_st, yp, tsr, tw, None, y, stream)
         e[4].record(stream)
         torch.cuda.synchronize()
         if it == 0:
@@ -150,7 +158,7 @@ def main():
     starts, ends = [ev() for _ in range(reps)], [ev() for _ in range(reps)]
     for i in range(reps):
         starts[i].record(stream)
-        ml.moe_grouped_ffn(p, xp, xs, offsets, W, None, None, yp, ws_f, stream)
+        ml.moe_grouped_ffn(p_st, xp, xs, offsets, W, None, None, yp, ws_f, stream)
         ends[i].record(stream)
     torch.cuda.synchronize()
     ffn_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(starts, ends)]))
@@ -209,7 +217,8 @@ def main():
         "data": "synthetic (seeded N(0,0.02) activations/weights, generated routing logits)",
         "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.H, "experts": cfg.E,
                    "local_experts": cfg.E_L, "expert_begin": cfg.e_lo, "top_k": cfg.k,
-                   "inter": cfg.I, "shared_inter": cfg.I_s, "seed": seed},
+                   "inter": cfg.I, "shared_inter": cfg.I_s, "seed": seed,
+                   "layout": "panel" if panel else "rows"},
         "grouped_ffn_tflops": round(ffn_tflops, 2),
         "grouped_ffn_frac_of_peak": round(ffn_tflops / PEAK_TFLOPS[dtype], 4),
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},

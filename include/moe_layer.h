@@ -22,8 +22,9 @@
  *    experts E, top-k, intermediate size I) plus the local expert range
  *    [expert_begin, expert_begin + num_local) of this rank (moe_problem).
  *  - Every array argument is a DEVICE pointer to caller-owned memory, row
- *    major, 16-byte aligned.  The library never allocates, keeps no state
- *    between calls, is reentrant, and never synchronises the host: all work
+ *    major unless moe_problem.layout says otherwise, 16-byte aligned.  The
+ *    library never allocates, keeps no state between calls, is reentrant,
+ *    and never synchronises the host: all work
  *    is enqueued on `stream` (a hipStream_t; NULL = the default stream), and
  *    data-dependent sizes (per-expert counts, tile lists) stay on the device.
  *  - Arguments are validated before anything is enqueued.  On any error
@@ -51,7 +52,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef enum {
   MOE_OK = 0,
@@ -68,6 +69,24 @@ typedef enum {
                         token per 128 consecutive elements                   */
 } moe_dtype;
 
+/* Storage layouts (moe_problem.layout bits; bf16 problems only, values are
+ * never changed by a layout).  The panel layout of an [R, K] bf16 matrix
+ * cuts its columns into panels of 32 consecutive elements (64 bytes) and
+ * stores the panels one after another, each as an [R, 32] row-major block:
+ *   element (r, c) lives at index ((c / 32) * R + r) * 32 + c % 32.
+ * A GEMM step over 32 columns then reads one contiguous block per operand
+ * tile instead of 64 bytes from each of hundreds of rows, which keeps the
+ * HBM and L2 traffic of the grouped GEMM in long runs.
+ *   MOE_LAYOUT_PANEL_WEIGHTS: each expert's w13 [2I, H] and w2 [H, I] (and
+ *     ws13 / ws2) is in panel layout (R = 2I, H, 2 I_s, H); see
+ *     moe_pack_panel.
+ *   MOE_LAYOUT_PANEL_ACTS: x_perm [N_cap, H] written by moe_dispatch and read
+ *     by moe_grouped_ffn, and h [N_cap, I], are in panel layout with
+ *     R = N_cap.  moe_layer keeps its own x_perm and h in panel layout
+ *     whatever this bit says.                                               */
+#define MOE_LAYOUT_PANEL_WEIGHTS 1
+#define MOE_LAYOUT_PANEL_ACTS 2
+
 /* The workload tuple of one rank. */
 typedef struct {
   int32_t num_tokens;    /* T: tokens in the batch                            */
@@ -79,6 +98,8 @@ typedef struct {
   int32_t inter;         /* I: expert FFN intermediate size                   */
   int32_t shared_inter;  /* I_s: shared-expert intermediate size, 0 = none    */
   int32_t dtype;         /* moe_dtype                                          */
+  int32_t layout;        /* MOE_LAYOUT_* bits, 0 = all row major; must be 0
+                            for MOE_FP8_E4M3                                   */
 } moe_problem;
 
 /* Expert weights, device pointers, K-contiguous ("[out, in]" row major).
@@ -199,6 +220,14 @@ moe_status moe_layer(const moe_problem* p, const float* logits, const void* x,
 moe_status moe_quantize_fp8(const void* src, int64_t batch, int64_t rows,
                             int64_t cols, int32_t block_rows, void* codes,
                             float* scales, void* stream);
+
+/* Panel packing of bf16 matrices (see MOE_LAYOUT_PANEL_WEIGHTS): for each of
+ * `batch` matrices src [rows, cols] (row major), dst receives the same values
+ * in panel layout, [cols / 32, rows, 32].  cols % 32 == 0, 0 < cols <= 2^20,
+ * batch * rows * cols < 2^40; src and dst must not overlap.  Meant for load
+ * time, like moe_quantize_fp8: the weights are packed once.               */
+moe_status moe_pack_panel(const void* src, int64_t batch, int64_t rows,
+                          int64_t cols, void* dst, void* stream);
 
 #define MOE_STAGE_LAYER 0
 #define MOE_STAGE_DISPATCH 1

@@ -137,6 +137,61 @@ __global__ __launch_bounds__(256) void gather_rows_bf16_kernel(
   }
 }
 
+// The same gather into panel layout [H/32][panel_rows][32].  A work item is
+// 16 consecutive destination rows x 8 panels; lane l of the wavefront moves
+// the 16 bytes l % 4 of row l / 4 in each panel, so every store instruction
+// writes one contiguous kilobyte (16 rows of a panel) and the source rows
+// are read in 64-byte runs.
+__global__ __launch_bounds__(256) void gather_rows_panel_kernel(
+    const uint4* __restrict__ src, const int32_t* __restrict__ rows,
+    const int32_t* __restrict__ n_rows, int n_rows_host, int chunks_per_row,
+    int64_t panel_rows, uint4* __restrict__ dst) {
+  constexpr int kPanelsPerItem = 8;
+  const int n = n_rows ? *n_rows : n_rows_host;
+  const int wpb = blockDim.x >> 6;
+  const int lane = lane_id(), sub = lane & 3;
+  const int panels = chunks_per_row >> 2;
+  const int pblocks = (panels + kPanelsPerItem - 1) / kPanelsPerItem;
+  const int64_t items = static_cast<int64_t>((n + 15) >> 4) * pblocks;
+  for (int64_t it = static_cast<int64_t>(blockIdx.x) * wpb + (threadIdx.x >> 6); it < items;
+       it += static_cast<int64_t>(gridDim.x) * wpb) {
+    const int grp = static_cast<int>(it / pblocks);
+    const int p0 = static_cast<int>(it - static_cast<int64_t>(grp) * pblocks) * kPanelsPerItem;
+    const int j = grp * 16 + (lane >> 2);
+    if (j >= n) continue;
+    const int r = rows ? rows[j] : j;
+    const uint4* s = src + static_cast<size_t>(r) * chunks_per_row + sub;
+    uint4* d = dst + static_cast<size_t>(j) * 4 + sub;
+    if (p0 + kPanelsPerItem <= panels) {
+      uint4 v[kPanelsPerItem];
+#pragma unroll
+      for (int u = 0; u < kPanelsPerItem; ++u) v[u] = s[(p0 + u) * 4];
+#pragma unroll
+      for (int u = 0; u < kPanelsPerItem; ++u) d[(p0 + u) * panel_rows * 4] = v[u];
+    } else {
+      for (int p = p0; p < panels; ++p) d[p * panel_rows * 4] = s[p * 4];
+    }
+  }
+}
+
+// Panel packing, [batch][rows][cols] -> [batch][cols/32][rows][32] (bf16).
+// Threads walk the destination in order (16 bytes each), so writes are
+// contiguous and each group of four threads reads one 64-byte run.
+__global__ __launch_bounds__(256) void pack_panel_kernel(const uint4* __restrict__ src,
+                                                         int64_t batch, int64_t rows,
+                                                         int64_t cols, uint4* __restrict__ dst) {
+  const int64_t units = cols / 8;               // 16-byte units per row
+  const int64_t per_mat = rows * units;
+  const int64_t total = batch * per_mat;
+  for (int64_t u = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; u < total;
+       u += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t b = u / per_mat, v = u - b * per_mat;
+    const int64_t panel = v / (rows * 4), w = v - panel * rows * 4;
+    const int64_t r = w >> 2, sub = w & 3;
+    dst[u] = src[b * per_mat + r * units + panel * 4 + sub];
+  }
+}
+
 // Row gather with per-128 group E4M3 quantisation: scale = amax/448 (1 for an
 // all-zero group), code = RNE(v / scale) (IEEE fp32 division) saturated.
 // A group of 128 bf16 is 16 lanes x 8 values; a wave covers 4 groups per step.
@@ -263,10 +318,27 @@ static int gather_grid(int64_t max_rows) {
 }
 
 hipError_t launch_gather_bf16(const void* src, const int32_t* rows, const int32_t* n_rows,
-                              int64_t max_rows, int H, void* dst, hipStream_t s) {
-  hipLaunchKernelGGL(gather_rows_bf16_kernel, dim3(gather_grid(max_rows)), dim3(256), 0, s,
-                     static_cast<const uint4*>(src), rows, n_rows, static_cast<int>(max_rows),
-                     H / 8, static_cast<uint4*>(dst));
+                              int64_t max_rows, int H, void* dst, int64_t panel_rows,
+                              hipStream_t s) {
+  if (panel_rows > 0)
+    hipLaunchKernelGGL(gather_rows_panel_kernel,
+                       dim3(gather_grid((max_rows + 15) / 16 * ((H / 32 + 7) / 8))),
+                       dim3(256), 0, s, static_cast<const uint4*>(src), rows, n_rows,
+                       static_cast<int>(max_rows), H / 8, panel_rows, static_cast<uint4*>(dst));
+  else
+    hipLaunchKernelGGL(gather_rows_bf16_kernel, dim3(gather_grid(max_rows)), dim3(256), 0, s,
+                       static_cast<const uint4*>(src), rows, n_rows, static_cast<int>(max_rows),
+                       H / 8, static_cast<uint4*>(dst));
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_panel(const void* src, int64_t batch, int64_t rows, int64_t cols,
+                             void* dst, hipStream_t s) {
+  const int64_t units = batch * rows * (cols / 8);
+  const int64_t blocks = (units + 255) / 256;
+  hipLaunchKernelGGL(pack_panel_kernel, dim3(static_cast<unsigned>(blocks < 16384 ? blocks : 16384)),
+                     dim3(256), 0, s, static_cast<const uint4*>(src), batch, rows, cols,
+                     static_cast<uint4*>(dst));
   return hipGetLastError();
 }
 

@@ -67,7 +67,20 @@ struct GemmArgs {
   int K, Nout, NW, nt_n;   // NW = 2 Nout (SwiGLU) or Nout; nt_n n-tiles per expert
   int64_t w_stride;        // bytes per expert of W
   int64_t ws_stride;       // floats per expert of W_scale
+  // Operand addressing: byte (row, c) of A or W is at row * rs + (c / 64) * cs
+  // + c % 64 -- row major: rs = row bytes, cs = 64; panel layout: rs = 64,
+  // cs = 64 * rows of the matrix.
+  int a_rs, w_rs;
+  int64_t a_cs, w_cs;
+  int64_t a_bytes;         // size of the A buffer
+  int64_t c_cs;            // SwiGLU bf16 output: 0 = row major, else panel stride
 };
+
+// Byte offset of element (m, col) of a bf16 output with Nout columns.
+__device__ __forceinline__ int64_t out_offset(const GemmArgs& g, int m, int col) {
+  if (g.c_cs) return (col >> 5) * g.c_cs + static_cast<int64_t>(m) * 64 + (col & 31) * 2;
+  return (static_cast<int64_t>(m) * g.Nout + col) * 2;
+}
 
 __global__ __launch_bounds__(1024) void tile_schedule_kernel(
     const int32_t* __restrict__ offsets, int E_L, int tile_m, int4* __restrict__ info,
@@ -109,8 +122,10 @@ __device__ __forceinline__ int wblock_row(int swiglu, int wn, int i) {
 //     sub-step kk+1 are issued between the MFMAs of sub-step kk), and the
 //     last sub-step's MFMAs straddle the step barrier so that they cover the
 //     first fragment reads of the next stage;
-//   * buffer loads take a scalar base and 32-bit lane offsets; rows past the
-//     expert's segment lie outside the buffer's range and read as zero.
+//   * buffer loads take a scalar base, moved on by one K step per step, and
+//     32-bit lane offsets; the lanes of token rows past the expert's segment
+//     get an offset past the buffer's range and read zeros without a memory
+//     access.
 // ---------------------------------------------------------------------------
 constexpr int kBufFlags = 0x00020000;  // raw buffer, 32-bit data format
 constexpr int kStages = 3;
@@ -120,8 +135,14 @@ constexpr int kStageBytes = kScaleRegion + kBM * 4;      // 48 KB + 512 B
 constexpr int kWRegion = kBM * kRowBytes;                // weight rows start here
 constexpr int kDmaPerWave = (kBM + kBN) / 8 / 4;         // 12 loads of 8 rows per wave
 
+// Buffer ranges are capped below kOobOffset, so a lane offset of kOobOffset
+// is out of range: the load returns zeros without touching memory (used for
+// token rows past the expert's segment).
+constexpr int kBufMax = 0x7ffffe00;
+constexpr int kOobOffset = 0x7fffff00;
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const int n = bytes > 0x7fffffff ? 0x7fffffff : static_cast<int>(bytes);
+  const int n = bytes > kBufMax ? kBufMax : (bytes < 0 ? 0 : static_cast<int>(bytes));
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), n,
                                            kBufFlags);
 }
@@ -162,10 +183,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pipelined_kernel(const GemmA
 
   const int ldb = FP8 ? g.K : 2 * g.K;  // bytes per row of A and W
   const int nk = ldb / kRowBytes;
-  const __amdgpu_buffer_rsrc_t rA = make_rsrc(g.A + static_cast<int64_t>(row0) * ldb,
-                                              static_cast<int64_t>(min(seg_end - row0, kBM)) * ldb);
-  const __amdgpu_buffer_rsrc_t rW =
-      make_rsrc(g.W + e * g.w_stride, static_cast<int64_t>(g.NW) * ldb);
+  // Buffer views advance by one K step at a time.
+  const uint8_t* a_base = g.A + static_cast<int64_t>(row0) * g.a_rs;
+  const int64_t a_left = g.a_bytes - static_cast<int64_t>(row0) * g.a_rs;
+  const uint8_t* w_base = g.W + e * g.w_stride;
 
   const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
   // ---- direct-load assignment: wave w moves 8-row groups w*4+q (A) and
@@ -187,7 +208,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pipelined_kernel(const GemmA
       else
         grow = min(nt * kBN + r, g.NW - 1);
     }
-    voff[q] = grow * ldb + chunk * 16;
+    // 16-byte chunk c of the step's 128 bytes is in 64-byte piece c / 4
+    // (piece strides fit 32 bits: the host checks 64 N_cap < 2^31).
+    const int cs = static_cast<int>(rr < kBM ? g.a_cs : g.w_cs);
+    voff[q] = (rr < kBM ? rr * g.a_rs : grow * g.w_rs) + (chunk >> 2) * cs + (chunk & 3) * 16;
+    if (rr < kBM && row0 + rr >= seg_end) voff[q] = kOobOffset;
     ldst[q] = grp * 1024;
   }
   // fp8: token scales of the step, 128 rows x 4 bytes, land beside the
@@ -201,11 +226,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pipelined_kernel(const GemmA
   const int soffs = ((w & 1) * 64 + lane) * kb_n * 4;
   auto dma = [&](int step, int stage) {
     const int k = min(step, nk - 1);
+    const int64_t p = 2 * k;  // 64-byte K pieces before this step
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(a_base + p * g.a_cs, a_left - p * g.a_cs);
+    const __amdgpu_buffer_rsrc_t rW = make_rsrc(w_base + p * g.w_cs, g.w_stride - p * g.w_cs);
     uint8_t* base = smem + stage * kStageBytes;
 #pragma unroll
     for (int q = 0; q < kDmaPerWave; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(q < 4 ? rA : rW, (lds_ptr_t)(base + ldst[q]), 16,
-                                               voff[q], k * kRowBytes, 0, 0);
+                                               voff[q], 0, 0, 0);
     if (FP8)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_ptr_t)(base + kScaleRegion + (w & 1) * 256),
                                                4, soffs, k * 4, 0, 0);
@@ -417,7 +445,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pipelined_kernel(const GemmA
       for (int j = 0; j < 2; ++j) {
         const int m = row0 + wm * 64 + j * 32 + lr;
         if (m >= seg_end) continue;
-        uint16_t* crow = C + static_cast<int64_t>(m) * g.Nout;
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
@@ -425,7 +452,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pipelined_kernel(const GemmA
             uint2 o;
             o.x = pack_bf16x2(acc[hb][j][q * 4 + 0], acc[hb][j][q * 4 + 1]);
             o.y = pack_bf16x2(acc[hb][j][q * 4 + 2], acc[hb][j][q * 4 + 3]);
-            *reinterpret_cast<uint2*>(crow + nt * 128 + wn * 64 + hb * 32 + q * 8 + cq) = o;
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(C) +
+                                      out_offset(g, m, nt * 128 + wn * 64 + hb * 32 + q * 8 + cq)) = o;
           }
       }
     } else {
@@ -530,11 +558,11 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const GemmArgs
 
   const int ldb = 2 * g.K;
   const int nk = ldb / kBigRowBytes;
-  // Only this tile's rows are in range; the rest of the tile reads as zero.
-  const __amdgpu_buffer_rsrc_t rA = make_rsrc(g.A + static_cast<int64_t>(row0) * ldb,
-                                              static_cast<int64_t>(min(seg_end - row0, kBigBM)) * ldb);
-  const __amdgpu_buffer_rsrc_t rW =
-      make_rsrc(g.W + e * g.w_stride, static_cast<int64_t>(g.NW) * ldb);
+  // Buffer views advance one 64-byte K piece per step (see the pipelined
+  // kernel); rows past the segment read zeros.
+  const uint8_t* a_base = g.A + static_cast<int64_t>(row0) * g.a_rs;
+  const int64_t a_left = g.a_bytes - static_cast<int64_t>(row0) * g.a_rs;
+  const uint8_t* w_base = g.W + e * g.w_stride;
 
   const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
   // direct loads: wave w moves 16-row groups 2w, 2w+1 of A and 16+2w, 17+2w
@@ -556,16 +584,19 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const GemmArgs
       else
         grow = min(nt * kBigBN + r, g.NW - 1);
     }
-    voff[q] = grow * ldb + chunk * 16;
+    voff[q] = (rr < kBigBM ? rr * g.a_rs : grow * g.w_rs) + chunk * 16;
+    if (rr < kBigBM && row0 + rr >= seg_end) voff[q] = kOobOffset;
     ldst[q] = grp * 1024;
   }
   auto dma = [&](int step, int stage) {
-    const int soff = min(step, nk - 1) * kBigRowBytes;
+    const int64_t k = min(step, nk - 1);
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(a_base + k * g.a_cs, a_left - k * g.a_cs);
+    const __amdgpu_buffer_rsrc_t rW = make_rsrc(w_base + k * g.w_cs, g.w_stride - k * g.w_cs);
     uint8_t* base = smem + stage * kBigStageBytes;
 #pragma unroll
     for (int q = 0; q < kBigDmaPerWave; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(q < 2 ? rA : rW, (lds_ptr_t)(base + ldst[q]), 16,
-                                               voff[q], soff, 0, 0);
+                                               voff[q], 0, 0, 0);
   };
 
   const int wm = w & 3, wn = w >> 2;
@@ -663,7 +694,6 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const GemmArgs
     for (int j = 0; j < 2; ++j) {
       const int m = row0 + wm * 64 + j * 32 + lr;
       if (m >= seg_end) continue;
-      uint16_t* crow = C + static_cast<int64_t>(m) * g.Nout;
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
@@ -679,7 +709,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const GemmArgs
           uint2 o;
           o.x = pack_bf16x2(hv[0], hv[1]);
           o.y = pack_bf16x2(hv[2], hv[3]);
-          *reinterpret_cast<uint2*>(crow + col) = o;
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(C) + out_offset(g, m, col)) = o;
         }
     }
   }
@@ -738,8 +768,15 @@ hipError_t launch_grouped_gemm(const GemmLaunch& L, hipStream_t s) {
   const int bn = L.tile_m == kBigBM ? kBigBN : kBN;
   g.nt_n = L.swiglu ? ceil_div(L.Nout, bn / 2) : ceil_div(L.Nout, bn);
   const int64_t elem = L.fp8 ? 1 : 2;
-  g.w_stride = static_cast<int64_t>(g.NW) * L.K * elem;
+  const int64_t ldb = L.K * elem;
+  g.w_stride = static_cast<int64_t>(g.NW) * ldb;
   g.ws_stride = L.fp8 ? static_cast<int64_t>(g.NW / 128) * (L.K / 128) : 0;
+  g.a_rs = L.a_panel ? 64 : static_cast<int>(ldb);
+  g.a_cs = L.a_panel ? 64 * L.a_rows : 64;
+  g.w_rs = L.w_panel ? 64 : static_cast<int>(ldb);
+  g.w_cs = L.w_panel ? 64 * static_cast<int64_t>(g.NW) : 64;
+  g.a_bytes = L.a_rows * ldb;
+  g.c_cs = L.c_panel ? 64 * L.a_rows : 0;
   if (!L.fp8) {
     if (L.tile_m == kBigBM) {
       if (L.swiglu) return launch_big<MODE_SWIGLU>(g, L.max_tiles, s);

@@ -18,8 +18,13 @@ hipError_t launch_index_build(const int32_t* topk_ids, int T, int k, int e_lo, i
                               hipStream_t s);
 // dst[j] = src[rows[j]] (rows == nullptr: identity) for j < *n_rows, or for
 // j < max_rows when n_rows == nullptr.
+// With panel_rows > 0, dst is in panel layout [H/32][panel_rows][32].
 hipError_t launch_gather_bf16(const void* src, const int32_t* rows, const int32_t* n_rows,
-                              int64_t max_rows, int H, void* dst, hipStream_t s);
+                              int64_t max_rows, int H, void* dst, int64_t panel_rows,
+                              hipStream_t s);
+// bf16 [batch][rows][cols] row major -> [batch][cols/32][rows][32].
+hipError_t launch_pack_panel(const void* src, int64_t batch, int64_t rows, int64_t cols,
+                             void* dst, hipStream_t s);
 hipError_t launch_gather_fp8(const void* src, const int32_t* rows, const int32_t* n_rows,
                              int64_t max_rows, int H, void* dst, float* dst_scale, hipStream_t s);
 hipError_t launch_quant_blocks(const void* src, int64_t batch, int64_t rows, int64_t cols,
@@ -46,6 +51,11 @@ struct GemmLaunch {
   int64_t max_tiles;
   int tile_m;            // gemm_tile_m() of the problem
   int K, Nout;
+  // Storage layouts (bf16 only): panel = [K/32][R][32], see moe_layer.h.
+  bool a_panel;          // A in panel layout with R = a_rows
+  bool w_panel;          // each expert's W in panel layout with R = NW
+  bool c_panel;          // SwiGLU output h in panel layout with R = a_rows
+  int64_t a_rows;        // rows of the A (and C) buffers: N_cap
 };
 hipError_t launch_grouped_gemm(const GemmLaunch& L, hipStream_t s);
 

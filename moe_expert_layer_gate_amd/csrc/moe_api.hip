@@ -32,8 +32,14 @@ moe_status check_problem(const moe_problem* p) {
   if (I < 128 || I > 65536 || I % 128) return MOE_ERR_INVALID_ARG;
   if (Is < 0 || Is > 65536 || Is % 128) return MOE_ERR_INVALID_ARG;
   if (p->dtype != MOE_BF16 && p->dtype != MOE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
+  if (p->layout & ~(MOE_LAYOUT_PANEL_WEIGHTS | MOE_LAYOUT_PANEL_ACTS)) return MOE_ERR_INVALID_ARG;
+  if (p->layout && p->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   // One expert's weight matrix must stay below 2 GiB (32-bit buffer offsets).
   if (4 * I * H >= (int64_t(1) << 31) || 4 * Is * H >= (int64_t(1) << 31))
+    return MOE_ERR_UNSUPPORTED;
+  // Panel activations: the panel stride 64 N_cap is a 32-bit buffer offset.
+  const int64_t N = T * (k < EL ? k : EL);
+  if ((p->layout & MOE_LAYOUT_PANEL_ACTS) && 64 * N >= (int64_t(1) << 31))
     return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
@@ -44,6 +50,17 @@ int64_t n_cap(const moe_problem* p) {
 }
 
 bool is_fp8(const moe_problem* p) { return p->dtype == MOE_FP8_E4M3; }
+bool panel_weights(const moe_problem* p) { return p->layout & MOE_LAYOUT_PANEL_WEIGHTS; }
+bool panel_acts(const moe_problem* p) { return p->layout & MOE_LAYOUT_PANEL_ACTS; }
+
+// moe_layer's own x_perm and h: panel layout for bf16 whenever the panel
+// stride fits (the caller's layout bit for activations plays no part).
+moe_problem layer_internal(const moe_problem* p) {
+  moe_problem q = *p;
+  q.layout &= ~MOE_LAYOUT_PANEL_ACTS;
+  if (!is_fp8(p) && 64 * n_cap(p) < (int64_t(1) << 31)) q.layout |= MOE_LAYOUT_PANEL_ACTS;
+  return q;
+}
 
 // Bump allocator over the workspace; with base == nullptr it only measures.
 struct Carve {
@@ -150,10 +167,12 @@ moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
     if (err__ != hipSuccess) return MOE_ERR_HIP;       \
   } while (0)
 
-// Enqueue the grouped FFN (no argument checks).
+// Enqueue the grouped FFN (no argument checks).  x_perm and h follow
+// p->layout's activation bit unless x_rows_major forces x_perm row major
+// (the shared expert reads x itself).
 moe_status run_ffn(const moe_problem* p, const void* x_perm, const float* x_perm_scale,
                    const int32_t* offsets, const moe_weights* w, void* h, float* h_scale,
-                   void* y_perm, const FfnScratch& f, hipStream_t s) {
+                   void* y_perm, const FfnScratch& f, hipStream_t s, bool x_rows_major = false) {
   const int64_t N = n_cap(p);
   const int E_L = p->num_local, H = p->hidden, I = p->inter;
   const int tile_m = gemm_tile_m(is_fp8(p), N / E_L);
@@ -177,6 +196,10 @@ moe_status run_ffn(const moe_problem* p, const void* x_perm, const float* x_perm
   up.tile_m = tile_m;
   up.K = H;
   up.Nout = I;
+  up.a_panel = panel_acts(p) && !x_rows_major;
+  up.w_panel = panel_weights(p);
+  up.c_panel = panel_acts(p);
+  up.a_rows = N;
   MOE_TRY(launch_grouped_gemm(up, s));
   GemmLaunch down = up;
   down.swiglu = false;
@@ -188,6 +211,8 @@ moe_status run_ffn(const moe_problem* p, const void* x_perm, const float* x_perm
   down.C_scale = nullptr;
   down.K = I;
   down.Nout = H;
+  down.a_panel = panel_acts(p);
+  down.c_panel = false;
   MOE_TRY(launch_grouped_gemm(down, s));
   return MOE_OK;
 }
@@ -202,7 +227,8 @@ moe_status run_dispatch(const moe_problem* p, const void* x, const int32_t* ids,
     MOE_TRY(launch_gather_fp8(x, row_token, offsets + E_L, n_cap(p), p->hidden, x_perm,
                               x_perm_scale, s));
   else
-    MOE_TRY(launch_gather_bf16(x, row_token, offsets + E_L, n_cap(p), p->hidden, x_perm, s));
+    MOE_TRY(launch_gather_bf16(x, row_token, offsets + E_L, n_cap(p), p->hidden, x_perm,
+                               panel_acts(p) ? n_cap(p) : 0, s));
   return MOE_OK;
 }
 
@@ -328,15 +354,17 @@ moe_status moe_layer(const moe_problem* p, const float* logits, const void* x,
   Carve c(align_ws(ws));
   const LayerScratch L = carve_layer(c, p);
   const int T = p->num_tokens;
+  const moe_problem pi = layer_internal(p);
 
   MOE_TRY(launch_route_topk(logits, T, p->num_experts, p->top_k, L.ids, L.w, s));
-  st = run_dispatch(p, x, L.ids, L.counts, L.offsets, L.row_token, L.row_slot, L.tsr, L.x_perm,
+  st = run_dispatch(&pi, x, L.ids, L.counts, L.offsets, L.row_token, L.row_slot, L.tsr, L.x_perm,
                     L.x_perm_scale, L.index_scratch, s);
   if (st != MOE_OK) return st;
-  st = run_ffn(p, L.x_perm, L.x_perm_scale, L.offsets, w, nullptr, nullptr, L.y_perm, L.ffn, s);
+  st = run_ffn(&pi, L.x_perm, L.x_perm_scale, L.offsets, w, nullptr, nullptr, L.y_perm, L.ffn, s);
   if (st != MOE_OK) return st;
   if (p->shared_inter > 0) {
-    const moe_problem q = shared_problem(p);
+    const moe_problem sq = shared_problem(p);
+    const moe_problem q = layer_internal(&sq);
     moe_weights sw{};
     sw.w13 = w->ws13;
     sw.w2 = w->ws2;
@@ -349,7 +377,8 @@ moe_status moe_layer(const moe_problem* p, const float* logits, const void* x,
       MOE_TRY(launch_gather_fp8(x, nullptr, nullptr, T, p->hidden, L.s_x, L.s_x_scale, s));
       sx = L.s_x;
     }
-    st = run_ffn(&q, sx, L.s_x_scale, L.s_offsets, &sw, nullptr, nullptr, L.s_out, L.s_ffn, s);
+    st = run_ffn(&q, sx, L.s_x_scale, L.s_offsets, &sw, nullptr, nullptr, L.s_out, L.s_ffn, s,
+                 /*x_rows_major=*/true);
     if (st != MOE_OK) return st;
   }
   return hip_status(launch_combine(L.y_perm, L.tsr, L.w, p->shared_inter > 0 ? L.s_out : nullptr,
@@ -373,6 +402,19 @@ moe_status moe_quantize_fp8(const void* src, int64_t batch, int64_t rows, int64_
   }
   if ((rows + 127) / 128 > 65535 || batch > 65535) return MOE_ERR_INVALID_ARG;
   return hip_status(launch_quant_blocks(src, batch, rows, cols, codes, scales, s));
+}
+
+moe_status moe_pack_panel(const void* src, int64_t batch, int64_t rows, int64_t cols, void* dst,
+                          void* stream) {
+  if (!src || !dst || !aligned16(src) || !aligned16(dst)) return MOE_ERR_INVALID_ARG;
+  if (batch < 0 || rows < 0 || cols < 32 || cols % 32 || cols > (1 << 20))
+    return MOE_ERR_INVALID_ARG;
+  if (rows > 0 && batch > ((int64_t(1) << 40) / cols) / rows) return MOE_ERR_INVALID_ARG;
+  const int64_t bytes = 2 * batch * rows * cols;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+  if (bytes > 0 && a < b + bytes && b < a + bytes) return MOE_ERR_INVALID_ARG;
+  if (batch == 0 || rows == 0) return MOE_OK;
+  return hip_status(launch_pack_panel(src, batch, rows, cols, dst, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

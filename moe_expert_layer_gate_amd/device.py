@@ -43,10 +43,23 @@ def quantize_fp8(w: torch.Tensor, block_rows: int = 128):
     return codes, scales
 
 
-def upload(d: Dict[str, np.ndarray], fp8: bool, keep_bf16: bool = False) -> Dict[str, torch.Tensor]:
+def pack_panel(w: torch.Tensor) -> torch.Tensor:
+    """[B, R, C] or [R, C] bf16 -> the same values in panel layout
+    ([B, C/32, R, 32]), made by moe_pack_panel; returned with w's shape."""
+    w3 = w.unsqueeze(0) if w.dim() == 2 else w
+    B, R, C = w3.shape
+    out = torch.empty_like(w)
+    ml.moe_pack_panel(w3.contiguous(), B, R, C, out)
+    return out
+
+
+def upload(d: Dict[str, np.ndarray], fp8: bool, keep_bf16: bool = False,
+           panel: bool = False) -> Dict[str, torch.Tensor]:
     """Move a make_inputs() batch to the GPU.  With fp8, the weights are
     converted to E4M3 + 128x128 block scales on the device (load-time
-    conversion) and the bf16 copies are dropped unless keep_bf16."""
+    conversion) and the bf16 copies are dropped unless keep_bf16.  With
+    panel (bf16 only), the weights are repacked into panel layout at load
+    time (use the problem's LAYOUT_PANEL_WEIGHTS bit with them)."""
     out: Dict[str, torch.Tensor] = {}
     out["logits"] = torch.from_numpy(d["logits"]).cuda()
     out["x"] = bf16_from_bits(d["x"])
@@ -61,6 +74,9 @@ def upload(d: Dict[str, np.ndarray], fp8: bool, keep_bf16: bool = False) -> Dict
                 out[name] = wb
             else:
                 del wb
+        elif panel:
+            out[name] = pack_panel(wb)
+            del wb
         else:
             out[name] = wb
     return out

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libmoelayer.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_BF16, MOE_FP8_E4M3 = 0, 1
+LAYOUT_PANEL_WEIGHTS, LAYOUT_PANEL_ACTS = 1, 2
 STAGE_LAYER, STAGE_DISPATCH, STAGE_FFN = 0, 1, 2
 
 # Every function the header declares, with its ctypes signature.
@@ -27,7 +28,8 @@ _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c
 class moe_problem(ctypes.Structure):
     _fields_ = [("num_tokens", _i32), ("hidden", _i32), ("num_experts", _i32),
                 ("top_k", _i32), ("expert_begin", _i32), ("num_local", _i32),
-                ("inter", _i32), ("shared_inter", _i32), ("dtype", _i32)]
+                ("inter", _i32), ("shared_inter", _i32), ("dtype", _i32),
+                ("layout", _i32)]
 
 
 class moe_weights(ctypes.Structure):
@@ -45,6 +47,7 @@ SIGNATURES = {
     "moe_combine": (_i32, [_P, _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_layer": (_i32, [_P, _vp, _vp, _W, _vp, _vp, _sz, _vp]),
     "moe_quantize_fp8": (_i32, [_vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp]),
+    "moe_pack_panel": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp]),
     "moe_workspace_bytes": (_sz, [_P, _i32]),
     "moe_status_str": (ctypes.c_char_p, [_i32]),
     "moe_abi_version": (_i32, []),
@@ -90,19 +93,20 @@ class Problem:
     I: int
     I_s: int = 0
     fp8: bool = False
+    layout: int = 0   # LAYOUT_* bits
 
     def c(self) -> moe_problem:
         return moe_problem(self.T, self.H, self.E, self.k, self.e_lo, self.E_L, self.I,
-                           self.I_s, MOE_FP8_E4M3 if self.fp8 else MOE_BF16)
+                           self.I_s, MOE_FP8_E4M3 if self.fp8 else MOE_BF16, self.layout)
 
     @property
     def n_cap(self) -> int:
         return self.T * min(self.k, self.E_L)
 
     @classmethod
-    def from_config(cls, cfg, T: Optional[int] = None) -> "Problem":
+    def from_config(cls, cfg, T: Optional[int] = None, layout: int = 0) -> "Problem":
         return cls(T=cfg.T if T is None else T, H=cfg.H, E=cfg.E, k=cfg.k, e_lo=cfg.e_lo,
-                   E_L=cfg.E_L, I=cfg.I, I_s=cfg.I_s, fp8=cfg.fp8)
+                   E_L=cfg.E_L, I=cfg.I, I_s=cfg.I_s, fp8=cfg.fp8, layout=layout)
 
 
 def _ptr(t) -> Optional[int]:
@@ -184,3 +188,8 @@ def moe_quantize_fp8(src, batch: int, rows: int, cols: int, block_rows: int, cod
                      stream=None) -> None:
     _check("moe_quantize_fp8", lib().moe_quantize_fp8(
         _ptr(src), batch, rows, cols, block_rows, _ptr(codes), _ptr(scales), _stream(stream)))
+
+
+def moe_pack_panel(src, batch: int, rows: int, cols: int, dst, stream=None) -> None:
+    _check("moe_pack_panel", lib().moe_pack_panel(
+        _ptr(src), batch, rows, cols, _ptr(dst), _stream(stream)))

@@ -53,6 +53,12 @@ def global_rel(got, ref) -> float:
     return float(d / n) if n > 0 else float(d)
 
 
+def unpanel(t, rows: int, cols: int):
+    """A [rows, cols] matrix stored in panel layout ([cols/32][rows][32],
+    element (r, c) at ((c // 32) * rows + r) * 32 + c % 32) -> row major."""
+    return t.reshape(cols // 32, rows, 32).permute(1, 0, 2).reshape(rows, cols)
+
+
 def small_cfg(**kw) -> synth.MoEConfig:
     base = dict(name="t", T=64, H=256, E=8, E_L=8, e_lo=0, k=2, I=256)
     base.update(kw)

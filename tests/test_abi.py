@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_header_declares_the_expected_calls():
     assert {"moe_route", "moe_dispatch", "moe_grouped_ffn", "moe_combine", "moe_layer",
-            "moe_quantize_fp8", "moe_workspace_bytes", "moe_status_str",
+            "moe_quantize_fp8", "moe_pack_panel", "moe_workspace_bytes", "moe_status_str",
             "moe_abi_version"} <= declared_functions()
 
 
@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert ml.lib().moe_abi_version() == 1
+    assert ml.lib().moe_abi_version() == 2
     assert ml.status_str(0) == "MOE_OK"
     assert ml.status_str(3) == "MOE_ERR_WORKSPACE"
     assert ml.status_str(99) == "MOE_ERR_UNKNOWN"
@@ -63,7 +63,7 @@ def test_workspace_sizes(cid):
 @pytest.mark.parametrize("bad", [
     dict(T=-1), dict(E=0), dict(k=0), dict(k=9, E=8), dict(k=33, E=64), dict(E_L=0),
     dict(e_lo=6, E_L=4), dict(e_lo=-1), dict(H=100), dict(I=96), dict(I_s=64), dict(H=0),
-    dict(E=2000, E_L=8)])
+    dict(E=2000, E_L=8), dict(layout=4), dict(layout=-1)])
 def test_invalid_problems_rejected(bad):
     base = dict(T=16, H=256, E=8, k=2, e_lo=0, E_L=8, I=256, I_s=0, fp8=False)
     base.update(bad)
@@ -118,3 +118,35 @@ def test_quantize_argument_checks():
     assert L.moe_quantize_fp8(256, 1, 128, 128, 64, 256, 256, None) == ml.MOE_ERR_INVALID_ARG
     assert L.moe_quantize_fp8(None, 1, 128, 128, 128, 256, 256, None) == ml.MOE_ERR_INVALID_ARG
     assert L.moe_quantize_fp8(256, 0, 128, 128, 128, 256, 256, None) == ml.MOE_OK
+
+
+def test_layout_checks():
+    L = ml.lib()
+    # panel layouts are bf16-only
+    pf = ml.Problem(T=16, H=256, E=8, k=2, e_lo=0, E_L=8, I=256, fp8=True,
+                    layout=ml.LAYOUT_PANEL_WEIGHTS)
+    assert ml.workspace_bytes(pf) == 0
+    pc = pf.c()
+    assert L.moe_route(ctypes.byref(pc), 16, 16, 16, None) == ml.MOE_ERR_UNSUPPORTED
+    for lay in (ml.LAYOUT_PANEL_WEIGHTS, ml.LAYOUT_PANEL_ACTS, 3):
+        p = ml.Problem(T=16, H=256, E=8, k=2, e_lo=0, E_L=8, I=256, layout=lay)
+        assert ml.workspace_bytes(p) == ml.workspace_bytes(
+            ml.Problem(T=16, H=256, E=8, k=2, e_lo=0, E_L=8, I=256))
+    # panel activations need 64 N_cap < 2^31 (N_cap = T min(k, E_L))
+    big = dict(T=1 << 22, H=128, E=8, k=8, e_lo=0, E_L=8, I=128)
+    assert ml.workspace_bytes(ml.Problem(**big)) > 0
+    pb = ml.Problem(**big, layout=ml.LAYOUT_PANEL_ACTS).c()
+    assert L.moe_route(ctypes.byref(pb), 16, 16, 16, None) == ml.MOE_ERR_UNSUPPORTED
+
+
+def test_pack_panel_argument_checks():
+    L = ml.lib()
+    assert L.moe_pack_panel(256, 1, 4, 48, 1 << 20, None) == ml.MOE_ERR_INVALID_ARG    # cols % 32
+    assert L.moe_pack_panel(256, 1, 4, 0, 1 << 20, None) == ml.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_panel(None, 1, 4, 64, 1 << 20, None) == ml.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_panel(264, 1, 4, 64, 1 << 20, None) == ml.MOE_ERR_INVALID_ARG   # misaligned
+    assert L.moe_pack_panel(256, 1, 4, 64, 512, None) == ml.MOE_ERR_INVALID_ARG       # overlap
+    assert L.moe_pack_panel(256, -1, 4, 64, 1 << 20, None) == ml.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_panel(256, 1 << 20, 1 << 20, 64, 1 << 40, None) == ml.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_panel(256, 0, 4, 64, 1 << 20, None) == ml.MOE_OK
+    assert L.moe_pack_panel(256, 3, 0, 64, 1 << 20, None) == ml.MOE_OK

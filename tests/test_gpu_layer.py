@@ -10,7 +10,7 @@ import pytest
 from moe_expert_layer_gate_amd import inputs as synth
 from oracle import moe_oracle as O
 from tests.gpu_util import (TOL_BF16, TOL_FP8, OracleWeights, global_rel, rel_rows, say,
-                            small_cfg, torch_cuda)
+                            small_cfg, torch_cuda, unpanel)
 
 pytestmark = pytest.mark.gpu
 
@@ -39,7 +39,8 @@ def run_layer(torch, p, dev, guard=0):
 
 
 def run_staged(torch, p, dev):
-    """route -> dispatch -> grouped FFN (+ shared) -> combine, all via the ABI."""
+    """route -> dispatch -> grouped FFN (+ shared) -> combine, all via the ABI.
+    x_perm and h come back row major whatever p.layout says."""
     ml, dv = _mods()
     T, k, H, I, N = p.T, p.k, p.H, p.I, p.n_cap
     i32 = dict(dtype=torch.int32, device="cuda")
@@ -64,9 +65,12 @@ def run_staged(torch, p, dev):
     y_perm = torch.empty((N, H), dtype=torch.bfloat16, device="cuda")
     ml.moe_grouped_ffn(p, xp, xs, offsets, dv.weights_of(dev, p.fp8), h, hs, y_perm,
                        dv.workspace(p, ml.STAGE_FFN))
+    if p.layout & ml.LAYOUT_PANEL_ACTS:
+        xp, h = unpanel(xp, N, H), unpanel(h, N, I)
     shared = None
     if p.I_s > 0:
-        q = ml.Problem(T=T, H=H, E=1, k=1, e_lo=0, E_L=1, I=p.I_s, fp8=p.fp8)
+        q = ml.Problem(T=T, H=H, E=1, k=1, e_lo=0, E_L=1, I=p.I_s, fp8=p.fp8,
+                       layout=p.layout & ml.LAYOUT_PANEL_WEIGHTS)
         off2 = torch.tensor([0, T], **i32)
         sw = (ml.weights_struct(dev["ws13_q"], dev["ws2_q"], None, None, dev["ws13_s"],
                                 dev["ws2_s"]) if p.fp8 else
@@ -103,6 +107,7 @@ SMALL = {
     "big_tile_ragged": (small_cfg(T=2048, H=384, E=8, E_L=8, k=2, I=384), 10),
     "big_tile_shard": (small_cfg(T=1500, H=512, E=16, E_L=4, e_lo=12, k=4, I=640,
                                  logits="gumbel_zipf"), 11),
+    "bf16_shared": (small_cfg(T=200, H=256, E=8, E_L=4, e_lo=2, k=2, I=256, I_s=384), 12),
 }
 SMALL_FP8 = {
     "fp8_small": (small_cfg(T=200, H=512, E=16, E_L=8, e_lo=0, k=4, I=256, fp8=True), 8),
@@ -152,6 +157,26 @@ def test_staged_and_fused_layer_small(name):
         assert rel_rows(f64(st["shared"]), ref["shared"]) <= tol
     # fused layer: same routing, same numbers as the staged calls
     y = run_layer(torch, p, dev, guard=3)
+    np.testing.assert_array_equal(dv.bits_from_bf16(y), dv.bits_from_bf16(st["y"]))
+    if not cfg.fp8:
+        check_panel_layouts(torch, p, d, st)
+
+
+def check_panel_layouts(torch, p, d, st):
+    """The panel storage layouts change where values live, never the values:
+    staged calls with panel weights and panel activations, and the fused
+    layer with panel weights, reproduce the row-major results bit for bit."""
+    ml, dv = _mods()
+    devp = dv.upload(d, False, panel=True)
+    pp = dataclasses.replace(p, layout=ml.LAYOUT_PANEL_WEIGHTS | ml.LAYOUT_PANEL_ACTS)
+    say("panel layouts staged", p)
+    sp = run_staged(torch, pp, devp)
+    N = int(st["offsets"][-1])
+    for key in ("x_perm", "h", "y_perm"):
+        np.testing.assert_array_equal(dv.bits_from_bf16(sp[key][:N]), dv.bits_from_bf16(st[key][:N]))
+    np.testing.assert_array_equal(dv.bits_from_bf16(sp["y"]), dv.bits_from_bf16(st["y"]))
+    say("panel weights fused", p)
+    y = run_layer(torch, dataclasses.replace(p, layout=ml.LAYOUT_PANEL_WEIGHTS), devp, guard=2)
     np.testing.assert_array_equal(dv.bits_from_bf16(y), dv.bits_from_bf16(st["y"]))
 
 
@@ -244,6 +269,11 @@ def test_workload_full_size_sampled(cid):
     np.testing.assert_array_equal(dv.bits_from_bf16(y), dv.bits_from_bf16(st["y"]))
     y2 = run_layer(torch, p, dev)
     np.testing.assert_array_equal(dv.bits_from_bf16(y), dv.bits_from_bf16(y2))   # deterministic
+    del dev
+    say("full size fused, panel weights", cfg.name)
+    devp = dv.upload(d, False, panel=True)
+    y3 = run_layer(torch, dataclasses.replace(p, layout=ml.LAYOUT_PANEL_WEIGHTS), devp)
+    np.testing.assert_array_equal(dv.bits_from_bf16(y3), dv.bits_from_bf16(st["y"]))
 
 
 def test_workload_fp8_full_size_sampled():
@@ -341,3 +371,31 @@ def test_empty_batch_is_a_no_op():
     ml.moe_layer(p, lg, x, ml.weights_struct(w, w2), y, dv.workspace(p))
     torch.cuda.synchronize()
     assert torch.all(y == 5.0)
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 32), (3, 5, 96), (2, 384, 256), (4, 130, 7168)])
+def test_pack_panel_layout(shape):
+    """moe_pack_panel places element (r, c) of each matrix at
+    ((c // 32) * R + r) * 32 + c % 32 and changes no value."""
+    torch = torch_cuda()
+    ml, dv = _mods()
+    B, R, C = shape
+    g = torch.Generator(device="cuda").manual_seed(B * R + C)
+    src = torch.randn((B, R, C), generator=g, device="cuda").to(torch.bfloat16)
+    guard = torch.full((B * R * C + 64,), 7.0, dtype=torch.bfloat16, device="cuda")
+    dst = guard[:B * R * C]
+    say("pack panel", shape)
+    ml.moe_pack_panel(src, B, R, C, dst)
+    torch.cuda.synchronize()
+    assert torch.all(guard[B * R * C:] == 7.0)
+    got = dst.view(B, C // 32, R, 32)
+    for b in range(B):
+        np.testing.assert_array_equal(dv.bits_from_bf16(unpanel(got[b], R, C)),
+                                      dv.bits_from_bf16(src[b]))
+    # element by element on a few positions, from the formula
+    flat = dv.bits_from_bf16(dst)
+    rng = np.random.default_rng(0)
+    ref = dv.bits_from_bf16(src)
+    for _ in range(50):
+        b, r, c = rng.integers(B), rng.integers(R), rng.integers(C)
+        assert flat[b * R * C + ((c // 32) * R + r) * 32 + c % 32] == ref[b, r, c]

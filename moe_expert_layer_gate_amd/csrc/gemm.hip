@@ -74,6 +74,7 @@ struct GemmArgs {
   int64_t a_cs, w_cs;
   int64_t a_bytes;         // size of the A buffer
   int64_t c_cs;            // SwiGLU bf16 output: 0 = row major, else panel stride
+  const int32_t* a_index;  // fused gather: GEMM row j reads A row a_index[j]
 };
 
 // Byte offset of element (m, col) of a bf16 output with Nout columns.
@@ -183,9 +184,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pipelined_kernel(const GemmA
 
   const int ldb = FP8 ? g.K : 2 * g.K;  // bytes per row of A and W
   const int nk = ldb / kRowBytes;
-  // Buffer views advance by one K step at a time.
-  const uint8_t* a_base = g.A + static_cast<int64_t>(row0) * g.a_rs;
-  const int64_t a_left = g.a_bytes - static_cast<int64_t>(row0) * g.a_rs;
+  // Buffer views advance by one K step at a time.  With a fused gather the
+  // view spans the whole source and each lane's offset names its row.
+  const int64_t a_skip = g.a_index ? 0 : static_cast<int64_t>(row0) * g.a_rs;
+  const uint8_t* a_base = g.A + a_skip;
+  const int64_t a_left = g.a_bytes - a_skip;
   const uint8_t* w_base = g.W + e * g.w_stride;
 
   const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
@@ -211,7 +214,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pipelined_kernel(const GemmA
     // 16-byte chunk c of the step's 128 bytes is in 64-byte piece c / 4
     // (piece strides fit 32 bits: the host checks 64 N_cap < 2^31).
     const int cs = static_cast<int>(rr < kBM ? g.a_cs : g.w_cs);
-    voff[q] = (rr < kBM ? rr * g.a_rs : grow * g.w_rs) + (chunk >> 2) * cs + (chunk & 3) * 16;
+    const int arow = rr < kBM && g.a_index && row0 + rr < seg_end ? g.a_index[row0 + rr] : rr;
+    voff[q] = (rr < kBM ? arow * g.a_rs : grow * g.w_rs) + (chunk >> 2) * cs + (chunk & 3) * 16;
     if (rr < kBM && row0 + rr >= seg_end) voff[q] = kOobOffset;
     ldst[q] = grp * 1024;
   }
@@ -560,8 +564,9 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const GemmArgs
   const int nk = ldb / kBigRowBytes;
   // Buffer views advance one 64-byte K piece per step (see the pipelined
   // kernel); rows past the segment read zeros.
-  const uint8_t* a_base = g.A + static_cast<int64_t>(row0) * g.a_rs;
-  const int64_t a_left = g.a_bytes - static_cast<int64_t>(row0) * g.a_rs;
+  const int64_t a_skip = g.a_index ? 0 : static_cast<int64_t>(row0) * g.a_rs;
+  const uint8_t* a_base = g.A + a_skip;
+  const int64_t a_left = g.a_bytes - a_skip;
   const uint8_t* w_base = g.W + e * g.w_stride;
 
   const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
@@ -584,7 +589,9 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const GemmArgs
       else
         grow = min(nt * kBigBN + r, g.NW - 1);
     }
-    voff[q] = (rr < kBigBM ? rr * g.a_rs : grow * g.w_rs) + chunk * 16;
+    const int arow =
+        rr < kBigBM && g.a_index && row0 + rr < seg_end ? g.a_index[row0 + rr] : rr;
+    voff[q] = (rr < kBigBM ? arow * g.a_rs : grow * g.w_rs) + chunk * 16;
     if (rr < kBigBM && row0 + rr >= seg_end) voff[q] = kOobOffset;
     ldst[q] = grp * 1024;
   }
@@ -752,6 +759,11 @@ hipError_t launch_tile_schedule(const int32_t* offsets, int E_L, int tile_m, int
 }
 
 hipError_t launch_grouped_gemm(const GemmLaunch& L, hipStream_t s) {
+  // The fused gather reads bf16 row-major sources whose lane offsets fit
+  // below the buffer cap.
+  static_assert(kGemmGatherMaxBytes <= kBufMax, "gather offsets must stay below the range cap");
+  if (L.a_index && (L.fp8 || L.a_panel || L.a_rows * 2 * L.K > kGemmGatherMaxBytes))
+    return hipErrorInvalidValue;
   GemmArgs g{};
   g.A = static_cast<const uint8_t*>(L.A);
   g.A_scale = L.A_scale;
@@ -776,7 +788,8 @@ hipError_t launch_grouped_gemm(const GemmLaunch& L, hipStream_t s) {
   g.w_rs = L.w_panel ? 64 : static_cast<int>(ldb);
   g.w_cs = L.w_panel ? 64 * static_cast<int64_t>(g.NW) : 64;
   g.a_bytes = L.a_rows * ldb;
-  g.c_cs = L.c_panel ? 64 * L.a_rows : 0;
+  g.c_cs = L.c_panel ? 64 * L.c_rows : 0;
+  g.a_index = L.a_index;
   if (!L.fp8) {
     if (L.tile_m == kBigBM) {
       if (L.swiglu) return launch_big<MODE_SWIGLU>(g, L.max_tiles, s);

@@ -54,10 +54,16 @@ struct GemmLaunch {
   // Storage layouts (bf16 only): panel = [K/32][R][32], see moe_layer.h.
   bool a_panel;          // A in panel layout with R = a_rows
   bool w_panel;          // each expert's W in panel layout with R = NW
-  bool c_panel;          // SwiGLU output h in panel layout with R = a_rows
-  int64_t a_rows;        // rows of the A (and C) buffers: N_cap
+  bool c_panel;          // SwiGLU output h in panel layout with R = c_rows
+  int64_t a_rows;        // rows of the A buffer (N_cap, or T with a_index)
+  int64_t c_rows;        // rows of the C buffer: N_cap
+  // Fused gather (bf16, row-major A only): permuted row j of the GEMM is row
+  // a_index[j] of A, e.g. A = the layer input x and a_index = row_token.
+  const int32_t* a_index;
 };
 hipError_t launch_grouped_gemm(const GemmLaunch& L, hipStream_t s);
+// Largest fused-gather source (bytes) the GEMM's 32-bit lane offsets reach.
+constexpr int64_t kGemmGatherMaxBytes = 0x7ffffe00;
 
 hipError_t launch_combine(const void* y_perm, const int32_t* token_slot_row, const float* topk_w,
                           const void* shared_out, int T, int k, int H, void* y, hipStream_t s);

@@ -76,6 +76,13 @@ struct Carve {
   }
 };
 
+// Fused gather of bf16 sources whose byte size fits the GEMM's 32-bit lane
+// offsets.
+bool can_fuse_gather(const moe_problem* p) {
+  return !is_fp8(p) &&
+         static_cast<int64_t>(p->num_tokens) * p->hidden * 2 <= kGemmGatherMaxBytes;
+}
+
 struct FfnScratch {
   int4* info;
   int32_t* n_tiles;
@@ -141,7 +148,8 @@ LayerScratch carve_layer(Carve& c, const moe_problem* p) {
   s.row_token = c.take<int32_t>(4 * N);
   s.row_slot = c.take<int32_t>(4 * N);
   s.tsr = c.take<int32_t>(4 * T * k);
-  s.x_perm = c.take<void>((is_fp8(p) ? 1 : 2) * N * H);
+  // x_perm only where the up GEMM does not gather from x itself
+  s.x_perm = can_fuse_gather(p) ? nullptr : c.take<void>((is_fp8(p) ? 1 : 2) * N * H);
   s.x_perm_scale = is_fp8(p) ? c.take<float>(4 * N * (H / 128)) : nullptr;
   s.y_perm = c.take<void>(2 * N * H);
   s.index_scratch = c.take<void>(index_scratch_bytes(static_cast<int>(T), static_cast<int>(EL)));
@@ -167,12 +175,26 @@ moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
     if (err__ != hipSuccess) return MOE_ERR_HIP;       \
   } while (0)
 
-// Enqueue the grouped FFN (no argument checks).  x_perm and h follow
-// p->layout's activation bit unless x_rows_major forces x_perm row major
-// (the shared expert reads x itself).
-moe_status run_ffn(const moe_problem* p, const void* x_perm, const float* x_perm_scale,
-                   const int32_t* offsets, const moe_weights* w, void* h, float* h_scale,
-                   void* y_perm, const FfnScratch& f, hipStream_t s, bool x_rows_major = false) {
+// Source rows of the up GEMM (no argument checks):
+//   index == nullptr, rows_major == false: x_perm as p->layout says;
+//   index == nullptr, rows_major == true:  a row-major [N_cap, H] matrix
+//                                          (the shared expert reads x itself);
+//   index != nullptr: fused gather, row j is row index[j] of the row-major
+//                     [src_rows, H] matrix x (the permutation is never
+//                     written out).
+struct FfnSource {
+  const void* x;
+  const float* x_scale;
+  bool rows_major;
+  const int32_t* index;
+  int64_t src_rows;
+};
+
+// Enqueue the grouped FFN (no argument checks).  h follows p->layout's
+// activation bit.
+moe_status run_ffn(const moe_problem* p, const FfnSource& src, const int32_t* offsets,
+                   const moe_weights* w, void* h, float* h_scale, void* y_perm,
+                   const FfnScratch& f, hipStream_t s) {
   const int64_t N = n_cap(p);
   const int E_L = p->num_local, H = p->hidden, I = p->inter;
   const int tile_m = gemm_tile_m(is_fp8(p), N / E_L);
@@ -183,8 +205,8 @@ moe_status run_ffn(const moe_problem* p, const void* x_perm, const float* x_perm
   GemmLaunch up{};
   up.fp8 = is_fp8(p);
   up.swiglu = true;
-  up.A = x_perm;
-  up.A_scale = x_perm_scale;
+  up.A = src.x;
+  up.A_scale = src.x_scale;
   up.W = w->w13;
   up.W_scale = w->w13_scale;
   up.C = hb;
@@ -196,10 +218,12 @@ moe_status run_ffn(const moe_problem* p, const void* x_perm, const float* x_perm
   up.tile_m = tile_m;
   up.K = H;
   up.Nout = I;
-  up.a_panel = panel_acts(p) && !x_rows_major;
+  up.a_panel = panel_acts(p) && !src.rows_major && !src.index;
   up.w_panel = panel_weights(p);
   up.c_panel = panel_acts(p);
-  up.a_rows = N;
+  up.a_rows = src.index ? src.src_rows : N;
+  up.c_rows = N;
+  up.a_index = src.index;
   MOE_TRY(launch_grouped_gemm(up, s));
   GemmLaunch down = up;
   down.swiglu = false;
@@ -213,16 +237,20 @@ moe_status run_ffn(const moe_problem* p, const void* x_perm, const float* x_perm
   down.Nout = H;
   down.a_panel = panel_acts(p);
   down.c_panel = false;
+  down.a_rows = N;
+  down.a_index = nullptr;
   MOE_TRY(launch_grouped_gemm(down, s));
   return MOE_OK;
 }
 
+// Index build, then (x_perm != nullptr) the gather of the activation rows.
 moe_status run_dispatch(const moe_problem* p, const void* x, const int32_t* ids, int32_t* counts,
                         int32_t* offsets, int32_t* row_token, int32_t* row_slot, int32_t* tsr,
                         void* x_perm, float* x_perm_scale, void* scratch, hipStream_t s) {
   const int T = p->num_tokens, E_L = p->num_local;
   MOE_TRY(launch_index_build(ids, T, p->top_k, p->expert_begin, E_L, counts, offsets, row_token,
                              row_slot, tsr, scratch, s));
+  if (!x_perm) return MOE_OK;
   if (is_fp8(p))
     MOE_TRY(launch_gather_fp8(x, row_token, offsets + E_L, n_cap(p), p->hidden, x_perm,
                               x_perm_scale, s));
@@ -324,8 +352,8 @@ moe_status moe_grouped_ffn(const moe_problem* p, const void* x_perm, const float
   if (p->num_tokens == 0) return MOE_OK;
   Carve c(align_ws(ws));
   const FfnScratch f = carve_ffn(c, p);
-  return run_ffn(p, x_perm, x_perm_scale, offsets, w, h, h_scale, y_perm, f,
-                 static_cast<hipStream_t>(stream));
+  const FfnSource src{x_perm, x_perm_scale, false, nullptr, 0};
+  return run_ffn(p, src, offsets, w, h, h_scale, y_perm, f, static_cast<hipStream_t>(stream));
 }
 
 moe_status moe_combine(const moe_problem* p, const void* y_perm, const int32_t* token_slot_row,
@@ -356,11 +384,16 @@ moe_status moe_layer(const moe_problem* p, const float* logits, const void* x,
   const int T = p->num_tokens;
   const moe_problem pi = layer_internal(p);
 
+  // bf16: the up GEMM gathers its rows from x through row_token, so the
+  // permuted activations are never written; fp8 gathers and quantises first.
+  const bool fuse = can_fuse_gather(p);
   MOE_TRY(launch_route_topk(logits, T, p->num_experts, p->top_k, L.ids, L.w, s));
-  st = run_dispatch(&pi, x, L.ids, L.counts, L.offsets, L.row_token, L.row_slot, L.tsr, L.x_perm,
-                    L.x_perm_scale, L.index_scratch, s);
+  st = run_dispatch(&pi, x, L.ids, L.counts, L.offsets, L.row_token, L.row_slot, L.tsr,
+                    fuse ? nullptr : L.x_perm, L.x_perm_scale, L.index_scratch, s);
   if (st != MOE_OK) return st;
-  st = run_ffn(&pi, L.x_perm, L.x_perm_scale, L.offsets, w, nullptr, nullptr, L.y_perm, L.ffn, s);
+  const FfnSource rsrc = fuse ? FfnSource{x, nullptr, true, L.row_token, T}
+                              : FfnSource{L.x_perm, L.x_perm_scale, false, nullptr, 0};
+  st = run_ffn(&pi, rsrc, L.offsets, w, nullptr, nullptr, L.y_perm, L.ffn, s);
   if (st != MOE_OK) return st;
   if (p->shared_inter > 0) {
     const moe_problem sq = shared_problem(p);
@@ -377,8 +410,8 @@ moe_status moe_layer(const moe_problem* p, const float* logits, const void* x,
       MOE_TRY(launch_gather_fp8(x, nullptr, nullptr, T, p->hidden, L.s_x, L.s_x_scale, s));
       sx = L.s_x;
     }
-    st = run_ffn(&q, sx, L.s_x_scale, L.s_offsets, &sw, nullptr, nullptr, L.s_out, L.s_ffn, s,
-                 /*x_rows_major=*/true);
+    const FfnSource ssrc{sx, L.s_x_scale, true, nullptr, 0};
+    st = run_ffn(&q, ssrc, L.s_offsets, &sw, nullptr, nullptr, L.s_out, L.s_ffn, s);
     if (st != MOE_OK) return st;
   }
   return hip_status(launch_combine(L.y_perm, L.tsr, L.w, p->shared_inter > 0 ? L.s_out : nullptr,

@@ -516,50 +516,94 @@ hipError_t launch_pipelined(const GemmArgs& g, int64_t max_tiles, hipStream_t s)
 }
 
 // ---------------------------------------------------------------------------
-// Large-tile bf16 kernel: 256 token rows x 256 weight rows per block, 8 waves
-// (two per SIMD) in a 4 (rows) x 2 (weights) arrangement, 64 x 128 per wave
-// (2 x 4 MFMA 32x32 tiles).
-//  * Tile size: relative to a 128 x 256 tile it moves a third fewer bytes
-//    from L2 per FLOP.
+// Large-tile bf16 kernel, 8 waves (two per SIMD), each wave 64 x 128 output
+// elements (2 x 4 MFMA 32x32 tiles).  Two block shapes share the code:
+//   full tile: 256 token rows x 256 weight rows, waves 4 (rows) x 2 (weights);
+//   wide tile: 128 token rows x 512 weight rows, waves 2 x 4 -- used for the
+//              last 1..128 rows of an expert's segment, which a full tile
+//              would cover with as much padding as work.
+//  * Tile size: relative to a 128 x 256 tile the full tile moves a third
+//    fewer bytes from L2 per FLOP.
 //  * Eight waves: direct-to-LDS loads complete at a rate set by how many
 //    waves have loads in flight (about 30 B/clk per CU from four waves, 50
 //    from eight, measured on the MI355X), and this tile needs ~32 B/clk per
 //    CU at the full MFMA rate.
 //  * K advances 32 bf16 (a 64-byte row piece) per step through a four-stage
-//    LDS ring; loads run three steps ahead.  The swizzle for 64-byte rows is
+//    LDS ring of 40 KB stages (room for the wide tile's 640 rows); loads run
+//    three steps ahead.  The swizzle for 64-byte rows is
 //    chunk ^ ((row >> 2) & 3): the 16 rows read together by one fragment load
 //    cover every (row mod 4, chunk) pair, i.e. all LDS banks once.
+//  * Work table: one entry per (tile, n-range) unit, built on the device:
+//    for each expert, its full tiles for every n-tile (m-tile fastest), then
+//    its wide tile for every 512-row n-range, so an expert's units run
+//    together on one XCD and share its weights in L2.
 // ---------------------------------------------------------------------------
 constexpr int kBigBM = 256, kBigBN = 256;
+constexpr int kWideBM = 128, kWideBN = 512;
 constexpr int kBigThreads = 512;
 constexpr int kBigRowBytes = 64;
 constexpr int kBigStages = 4;
-constexpr int kBigStageBytes = (kBigBM + kBigBN) * kBigRowBytes;  // 32 KB
-constexpr int kBigWRegion = kBigBM * kBigRowBytes;
-constexpr int kBigDmaPerWave = (kBigBM + kBigBN) / 16 / 8;      // 4 loads of 16 rows per wave
+constexpr int kBigStageBytes = (kWideBM + kWideBN) * kBigRowBytes;  // 40 KB
 
-__device__ __forceinline__ int big_wblock_row(int swiglu, int wn, int i) {
-  if (swiglu) return (i < 2 ? 0 : kBigBN / 2) + wn * 64 + (i & 1) * 32;
-  return wn * 128 + i * 32;
+// Work units of the large-tile GEMMs (see above).  Entry {expert, first row,
+// n-index, wide}: the n-index counts 256-row weight tiles of a full tile or
+// 512-row ranges of a wide one.  An expert with 129..255 rows past its last
+// full tile gets one more full tile instead of a wide one.
+__device__ __forceinline__ void expert_units(int cnt, int& full, int& wide) {
+  full = cnt / kBigBM;
+  const int rem = cnt - full * kBigBM;
+  wide = rem > 0 && rem <= kWideBM;
+  if (rem > kWideBM) ++full;
 }
 
-template <int MODE>
-__global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const GemmArgs g) {
-  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+__global__ __launch_bounds__(1024) void unit_schedule_kernel(
+    const int32_t* __restrict__ offsets, int E_L, int nt_a, int nt_b, int4* __restrict__ units_a,
+    int32_t* __restrict__ n_a, int4* __restrict__ units_b, int32_t* __restrict__ n_b) {
+  const int e = threadIdx.x;
+  int cnt = 0, off = 0;
+  if (e < E_L) {
+    off = offsets[e];
+    cnt = offsets[e + 1] - off;
+  }
+  int full, wide;
+  expert_units(cnt, full, wide);
+  const int nw_a = (nt_a + 1) / 2, nw_b = (nt_b + 1) / 2;
+  int tot_a, tot_b;
+  const int sa = block_exclusive_scan(full * nt_a + wide * nw_a, &tot_a);
+  const int sb = block_exclusive_scan(full * nt_b + wide * nw_b, &tot_b);
+  if (e < E_L) {
+    for (int n = 0; n < nt_a; ++n)
+      for (int m = 0; m < full; ++m)
+        units_a[sa + n * full + m] = make_int4(e, off + m * kBigBM, n, 0);
+    for (int n = 0; n < nt_b; ++n)
+      for (int m = 0; m < full; ++m)
+        units_b[sb + n * full + m] = make_int4(e, off + m * kBigBM, n, 0);
+    if (wide) {
+      for (int r = 0; r < nw_a; ++r)
+        units_a[sa + full * nt_a + r] = make_int4(e, off + full * kBigBM, r, 1);
+      for (int r = 0; r < nw_b; ++r)
+        units_b[sb + full * nt_b + r] = make_int4(e, off + full * kBigBM, r, 1);
+    }
+  }
+  if (e == 0) {
+    *n_a = tot_a;
+    *n_b = tot_b;
+  }
+}
+
+template <int MODE, bool WIDE>
+__device__ __forceinline__ void big_tile(const GemmArgs& g, const int4 unit, uint8_t* smem) {
   constexpr bool kSwiglu = MODE != MODE_PLAIN;
+  constexpr int BM = WIDE ? kWideBM : kBigBM;
+  constexpr int BN = WIDE ? kWideBN : kBigBN;
+  constexpr int kWRegion = BM * kBigRowBytes;
+  constexpr int kAGroups = BM / 16;                        // 16-row load groups
+  constexpr int kLoads = (BM + BN) / 16 / 8;               // per wave and step: 4 or 5
+  constexpr int kALoads = kAGroups / 8;                    // of which A: 2 or 1
+  constexpr int kWaveRows = BM / 64;                       // waves along the token rows
 
-  const int total = *g.n_tiles * g.nt_n;
-  const int per_xcd = ceil_div(total, kXcds);
-  const int slot = blockIdx.x / kXcds;
-  if (slot >= per_xcd) return;
-  const int t = (blockIdx.x % kXcds) * per_xcd + slot;
-  if (t >= total) return;
-  const int4 inf = g.info[t / g.nt_n];
-  const int e = inf.x, u = t - inf.y * g.nt_n;
-  const int nt = u / inf.z, mt = u % inf.z;
+  const int e = unit.x, row0 = unit.y, nidx = unit.z;
   const int seg_end = g.offsets[e + 1];
-  const int row0 = g.offsets[e] + mt * kBigBM;
-
   const int ldb = 2 * g.K;
   const int nk = ldb / kBigRowBytes;
   // Buffer views advance one 64-byte K piece per step (see the pipelined
@@ -568,31 +612,32 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const GemmArgs
   const uint8_t* a_base = g.A + a_skip;
   const int64_t a_left = g.a_bytes - a_skip;
   const uint8_t* w_base = g.W + e * g.w_stride;
+  // first output column (SwiGLU: of h) and first weight row of the unit
+  const int nbase = kSwiglu ? nidx * (BN / 2) : nidx * BN;
 
   const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
-  // direct loads: wave w moves 16-row groups 2w, 2w+1 of A and 16+2w, 17+2w
-  // of W (A rows 0..255 are groups 0..15, W rows groups 16..31).
-  int voff[kBigDmaPerWave], ldst[kBigDmaPerWave];
+  // direct loads: wave w moves A groups w*kALoads.. and W groups
+  // kAGroups + w*(kLoads - kALoads)..; A rows come first in the stage.
+  int voff[kLoads], ldst[kLoads];
 #pragma unroll
-  for (int q = 0; q < kBigDmaPerWave; ++q) {
-    const int grp = q < 2 ? w * 2 + q : 16 + w * 2 + (q - 2);
+  for (int q = 0; q < kLoads; ++q) {
+    const int grp = q < kALoads ? w * kALoads + q : kAGroups + w * (kLoads - kALoads) + (q - kALoads);
     const int rr = grp * 16 + (lane >> 2);
     const int chunk = (lane & 3) ^ ((rr >> 2) & 3);
-    int grow;
-    if (rr < kBigBM) {
-      grow = rr;
+    if (rr < BM) {
+      const bool valid = row0 + rr < seg_end;
+      const int arow = g.a_index && valid ? g.a_index[row0 + rr] : rr;
+      voff[q] = valid ? arow * g.a_rs + chunk * 16 : kOobOffset;
     } else {
-      const int r = rr - kBigBM;
+      const int r = rr - BM;
+      int grow;
       if (kSwiglu)
-        grow = r < kBigBN / 2 ? min(nt * (kBigBN / 2) + r, g.Nout - 1)
-                              : g.Nout + min(nt * (kBigBN / 2) + (r - kBigBN / 2), g.Nout - 1);
+        grow = r < BN / 2 ? min(nbase + r, g.Nout - 1)
+                          : g.Nout + min(nbase + (r - BN / 2), g.Nout - 1);
       else
-        grow = min(nt * kBigBN + r, g.NW - 1);
+        grow = min(nbase + r, g.NW - 1);
+      voff[q] = grow * g.w_rs + chunk * 16;
     }
-    const int arow =
-        rr < kBigBM && g.a_index && row0 + rr < seg_end ? g.a_index[row0 + rr] : rr;
-    voff[q] = (rr < kBigBM ? arow * g.a_rs : grow * g.w_rs) + chunk * 16;
-    if (rr < kBigBM && row0 + rr >= seg_end) voff[q] = kOobOffset;
     ldst[q] = grp * 1024;
   }
   auto dma = [&](int step, int stage) {
@@ -601,19 +646,23 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const GemmArgs
     const __amdgpu_buffer_rsrc_t rW = make_rsrc(w_base + k * g.w_cs, g.w_stride - k * g.w_cs);
     uint8_t* base = smem + stage * kBigStageBytes;
 #pragma unroll
-    for (int q = 0; q < kBigDmaPerWave; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(q < 2 ? rA : rW, (lds_ptr_t)(base + ldst[q]), 16,
-                                               voff[q], 0, 0, 0);
+    for (int q = 0; q < kLoads; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(q < kALoads ? rA : rW, (lds_ptr_t)(base + ldst[q]),
+                                               16, voff[q], 0, 0, 0);
   };
 
-  const int wm = w & 3, wn = w >> 2;
+  const int wm = w % kWaveRows, wn = w / kWaveRows;
   const int lr = lane & 31, hi = lane >> 5, sl = (lr >> 2) & 3;
   int foff[2];
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) foff[kk] = lr * kBigRowBytes + (((2 * kk) | hi) ^ sl) * 16;
+  // LDS row (in the weight region) of the wave's weight block i
   int wbase[4], abase[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) wbase[i] = kBigWRegion + big_wblock_row(kSwiglu, wn, i) * kBigRowBytes;
+  for (int i = 0; i < 4; ++i) {
+    const int row = kSwiglu ? (i < 2 ? 0 : BN / 2) + wn * 64 + (i & 1) * 32 : wn * 128 + i * 32;
+    wbase[i] = kWRegion + row * kBigRowBytes;
+  }
 #pragma unroll
   for (int j = 0; j < 2; ++j) abase[j] = (wm * 64 + j * 32) * kBigRowBytes;
 
@@ -643,7 +692,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const GemmArgs
   dma(0, 0);
   dma(1, 1);
   dma(2, 2);
-  WAIT_VMCNT(2 * kBigDmaPerWave);
+  WAIT_VMCNT(2 * kLoads);
   __builtin_amdgcn_s_barrier();
   lfrag(smem, 0, 0);
 
@@ -658,13 +707,13 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const GemmArgs
     for (int q = 0; q < 6; ++q) {
       SCHED(kSchedMfma, 1);
       SCHED(kSchedDsRead, 1);
-      SCHED(kSchedVmemRead, 1);
+      if (q < kLoads) SCHED(kSchedVmemRead, 1);
     }
     SCHED(kSchedMfma, 2);
     mma(1, 0, 4);
     // Step boundary: step kt+1 has landed once only steps kt+2 and kt+3 are
     // in flight; this wave's reads of stage kt are done.
-    WAIT_VMCNT_LDS(2 * kBigDmaPerWave);
+    WAIT_VMCNT_LDS(2 * kLoads);
     __builtin_amdgcn_s_barrier();
     lfrag(nxt, 0, 0);
     mma(1, 4, 4);
@@ -688,7 +737,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const GemmArgs
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int col = nt * kBigBN + wn * 128 + i * 32 + q * 8 + cq;
+          const int col = nbase + wn * 128 + i * 32 + q * 8 + cq;
           if (col >= g.Nout) continue;
           uint2 o;
           o.x = pack_bf16x2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]);
@@ -705,7 +754,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const GemmArgs
       for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int col = nt * (kBigBN / 2) + wn * 64 + hb * 32 + q * 8 + cq;
+          const int col = nbase + wn * 64 + hb * 32 + q * 8 + cq;
           if (col >= g.Nout) continue;
           float hv[4];
 #pragma unroll
@@ -723,7 +772,23 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const GemmArgs
 }
 
 template <int MODE>
-hipError_t launch_big(const GemmArgs& g, int64_t max_tiles, hipStream_t s) {
+__global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const GemmArgs g) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  const int total = *g.n_tiles;
+  const int per_xcd = ceil_div(total, kXcds);
+  const int slot = blockIdx.x / kXcds;
+  if (slot >= per_xcd) return;
+  const int t = (blockIdx.x % kXcds) * per_xcd + slot;
+  if (t >= total) return;
+  const int4 unit = g.info[t];
+  if (unit.w)
+    big_tile<MODE, true>(g, unit, smem);
+  else
+    big_tile<MODE, false>(g, unit, smem);
+}
+
+template <int MODE>
+hipError_t launch_big(const GemmArgs& g, int64_t max_units, hipStream_t s) {
   auto kern = gemm_big_kernel<MODE>;
   const size_t lds = kBigStages * kBigStageBytes;
   static bool attr_set = false;
@@ -734,16 +799,12 @@ hipError_t launch_big(const GemmArgs& g, int64_t max_tiles, hipStream_t s) {
       (void)hipGetLastError();
     attr_set = true;
   }
-  const int64_t blocks = (max_tiles * g.nt_n + kXcds - 1) / kXcds * kXcds + kXcds;
+  const int64_t blocks = (max_units + kXcds - 1) / kXcds * kXcds + kXcds;
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(kBigThreads), lds, s, g);
   return hipGetLastError();
 }
 
 }  // namespace
-
-int64_t max_m_tiles(int64_t n_cap, int E_L, int tile_m) {
-  return ceil_div<int64_t>(n_cap, tile_m) + E_L;
-}
 
 int gemm_tile_m(bool fp8, int64_t rows_per_expert) {
   // Few rows per expert (decode-sized batches): the 256-row tile would spend
@@ -751,10 +812,25 @@ int gemm_tile_m(bool fp8, int64_t rows_per_expert) {
   return (fp8 || rows_per_expert <= 2 * kBM) ? kBM : kBigBM;
 }
 
-hipError_t launch_tile_schedule(const int32_t* offsets, int E_L, int tile_m, int4* info,
-                                int32_t* n_tiles, hipStream_t s) {
-  hipLaunchKernelGGL(tile_schedule_kernel, dim3(1), dim3(1024), 0, s, offsets, E_L, tile_m, info,
-                     n_tiles);
+int gemm_n_tiles(int tile_m, bool swiglu, int Nout) {
+  const int bn = tile_m == kBigBM ? kBigBN : kBN;
+  return swiglu ? ceil_div(Nout, bn / 2) : ceil_div(Nout, bn);
+}
+
+int64_t schedule_entries(int64_t n_cap, int E_L, int tile_m, int nt) {
+  if (tile_m == kBigBM) return (n_cap / kBigBM + E_L) * nt;
+  return ceil_div<int64_t>(n_cap, tile_m) + E_L;
+}
+
+hipError_t launch_schedule(const int32_t* offsets, int E_L, int tile_m, int nt_up, int nt_dn,
+                           int4* tab_up, int32_t* n_up, int4* tab_dn, int32_t* n_dn,
+                           hipStream_t s) {
+  if (tile_m == kBigBM)
+    hipLaunchKernelGGL(unit_schedule_kernel, dim3(1), dim3(1024), 0, s, offsets, E_L, nt_up, nt_dn,
+                       tab_up, n_up, tab_dn, n_dn);
+  else
+    hipLaunchKernelGGL(tile_schedule_kernel, dim3(1), dim3(1024), 0, s, offsets, E_L, tile_m,
+                       tab_up, n_up);
   return hipGetLastError();
 }
 
@@ -777,8 +853,7 @@ hipError_t launch_grouped_gemm(const GemmLaunch& L, hipStream_t s) {
   g.K = L.K;
   g.Nout = L.Nout;
   g.NW = L.swiglu ? 2 * L.Nout : L.Nout;
-  const int bn = L.tile_m == kBigBM ? kBigBN : kBN;
-  g.nt_n = L.swiglu ? ceil_div(L.Nout, bn / 2) : ceil_div(L.Nout, bn);
+  g.nt_n = gemm_n_tiles(L.tile_m, L.swiglu, L.Nout);
   const int64_t elem = L.fp8 ? 1 : 2;
   const int64_t ldb = L.K * elem;
   g.w_stride = static_cast<int64_t>(g.NW) * ldb;

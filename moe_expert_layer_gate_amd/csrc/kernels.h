@@ -30,12 +30,21 @@ hipError_t launch_gather_fp8(const void* src, const int32_t* rows, const int32_t
 hipError_t launch_quant_blocks(const void* src, int64_t batch, int64_t rows, int64_t cols,
                                void* codes, float* scales, hipStream_t s);
 
-// Row tile of the grouped GEMM for a problem (the m-tile list must be built
-// with it): 128 for block-FP8 and for few rows per expert, else 256.
+// Row tile of the grouped GEMM for a problem: 128 (the pipelined kernel, for
+// block-FP8 and for few rows per expert) or 256 (the large-tile kernel, which
+// covers segment remainders of up to 128 rows with 128 x 512 tiles).
 int gemm_tile_m(bool fp8, int64_t rows_per_expert);
-int64_t max_m_tiles(int64_t n_cap, int E_L, int tile_m);
-hipError_t launch_tile_schedule(const int32_t* offsets, int E_L, int tile_m, int4* info,
-                                int32_t* n_tiles, hipStream_t s);
+// n-tiles per expert of one GEMM.
+int gemm_n_tiles(int tile_m, bool swiglu, int Nout);
+// Capacity of a GEMM's work table: m-tiles (tile_m 128; the up and down
+// GEMMs share one table) or (tile, n-range) units (tile_m 256; one table per
+// GEMM, nt = gemm_n_tiles of that GEMM).
+int64_t schedule_entries(int64_t n_cap, int E_L, int tile_m, int nt);
+// Builds the work tables on the device from the expert offsets (tile_m 128:
+// only tab_up / n_up are written).
+hipError_t launch_schedule(const int32_t* offsets, int E_L, int tile_m, int nt_up, int nt_dn,
+                           int4* tab_up, int32_t* n_up, int4* tab_dn, int32_t* n_dn,
+                           hipStream_t s);
 struct GemmLaunch {
   bool fp8;              // e4m3 operands with block scales, else bf16
   bool swiglu;           // up GEMM with the SwiGLU epilogue, else plain
@@ -46,10 +55,10 @@ struct GemmLaunch {
   void* C;               // [N_cap, Nout]: bf16, or e4m3 when C_scale != nullptr
   float* C_scale;        // fp8 SwiGLU only: [N_cap, Nout/128] per-row group scales
   const int32_t* offsets;
-  const int4* info;
-  const int32_t* n_tiles;
-  int64_t max_tiles;
-  int tile_m;            // gemm_tile_m() of the problem
+  const int4* info;       // work table of this GEMM (launch_schedule)
+  const int32_t* n_tiles; // live entries of the table
+  int64_t max_tiles;      // its capacity (schedule_entries)
+  int tile_m;             // gemm_tile_m() of the problem
   int K, Nout;
   // Storage layouts (bf16 only): panel = [K/32][R][32], see moe_layer.h.
   bool a_panel;          // A in panel layout with R = a_rows

@@ -84,18 +84,43 @@ bool can_fuse_gather(const moe_problem* p) {
 }
 
 struct FfnScratch {
-  int4* info;
-  int32_t* n_tiles;
+  int4* tab_up;     // work tables of the two GEMMs (one shared table for tile_m 128)
+  int4* tab_dn;
+  int32_t* n_up;
+  int32_t* n_dn;
   void* h;          // [N_cap, I] bf16 or e4m3
   float* h_scale;   // fp8 only
 };
 
+struct FfnShape {
+  int tile_m, nt_up, nt_dn;
+  int64_t cap_up, cap_dn;
+};
+
+FfnShape ffn_shape(const moe_problem* p) {
+  const int64_t N = n_cap(p);
+  FfnShape f{};
+  f.tile_m = gemm_tile_m(is_fp8(p), N / p->num_local);
+  f.nt_up = gemm_n_tiles(f.tile_m, true, p->inter);
+  f.nt_dn = gemm_n_tiles(f.tile_m, false, p->hidden);
+  f.cap_up = schedule_entries(N, p->num_local, f.tile_m, f.nt_up);
+  f.cap_dn = schedule_entries(N, p->num_local, f.tile_m, f.nt_dn);
+  return f;
+}
+
 FfnScratch carve_ffn(Carve& c, const moe_problem* p) {
   const int64_t N = n_cap(p), I = p->inter;
+  const FfnShape sh = ffn_shape(p);
   FfnScratch f{};
-  f.info = c.take<int4>(sizeof(int4) *
-                        max_m_tiles(N, p->num_local, gemm_tile_m(is_fp8(p), N / p->num_local)));
-  f.n_tiles = c.take<int32_t>(sizeof(int32_t));
+  f.tab_up = c.take<int4>(sizeof(int4) * sh.cap_up);
+  f.n_up = c.take<int32_t>(sizeof(int32_t));
+  if (sh.tile_m == 128) {
+    f.tab_dn = f.tab_up;
+    f.n_dn = f.n_up;
+  } else {
+    f.tab_dn = c.take<int4>(sizeof(int4) * sh.cap_dn);
+    f.n_dn = c.take<int32_t>(sizeof(int32_t));
+  }
   if (is_fp8(p)) {
     f.h = c.take<void>(N * I);
     f.h_scale = c.take<float>(sizeof(float) * N * (I / 128));
@@ -197,11 +222,11 @@ moe_status run_ffn(const moe_problem* p, const FfnSource& src, const int32_t* of
                    const FfnScratch& f, hipStream_t s) {
   const int64_t N = n_cap(p);
   const int E_L = p->num_local, H = p->hidden, I = p->inter;
-  const int tile_m = gemm_tile_m(is_fp8(p), N / E_L);
-  const int64_t mt = max_m_tiles(N, E_L, tile_m);
+  const FfnShape sh = ffn_shape(p);
   void* hb = h ? h : f.h;
   float* hs = h ? h_scale : f.h_scale;
-  MOE_TRY(launch_tile_schedule(offsets, E_L, tile_m, f.info, f.n_tiles, s));
+  MOE_TRY(launch_schedule(offsets, E_L, sh.tile_m, sh.nt_up, sh.nt_dn, f.tab_up, f.n_up, f.tab_dn,
+                          f.n_dn, s));
   GemmLaunch up{};
   up.fp8 = is_fp8(p);
   up.swiglu = true;
@@ -212,10 +237,10 @@ moe_status run_ffn(const moe_problem* p, const FfnSource& src, const int32_t* of
   up.C = hb;
   up.C_scale = is_fp8(p) ? hs : nullptr;
   up.offsets = offsets;
-  up.info = f.info;
-  up.n_tiles = f.n_tiles;
-  up.max_tiles = mt;
-  up.tile_m = tile_m;
+  up.info = f.tab_up;
+  up.n_tiles = f.n_up;
+  up.max_tiles = sh.cap_up;
+  up.tile_m = sh.tile_m;
   up.K = H;
   up.Nout = I;
   up.a_panel = panel_acts(p) && !src.rows_major && !src.index;
@@ -231,6 +256,9 @@ moe_status run_ffn(const moe_problem* p, const FfnSource& src, const int32_t* of
   down.A_scale = hs;
   down.W = w->w2;
   down.W_scale = w->w2_scale;
+  down.info = f.tab_dn;
+  down.n_tiles = f.n_dn;
+  down.max_tiles = sh.cap_dn;
   down.C = y_perm;
   down.C_scale = nullptr;
   down.K = I;

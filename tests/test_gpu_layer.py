@@ -124,11 +124,37 @@ def upload(cfg, seed, x_std=None, std=None):
 
 @pytest.mark.parametrize("name", list(SMALL) + list(SMALL_FP8))
 def test_staged_and_fused_layer_small(name):
-    torch = torch_cuda()
-    ml, dv = _mods()
+    torch_cuda()
     cfg, seed = {**SMALL, **SMALL_FP8}[name]
     # Larger spreads than the 0.02 workload default push SiLU off its linear part.
     d, dev = upload(cfg, seed, x_std=1.0, std=0.05)
+    check_small_case(name, cfg, d, dev)
+
+
+@pytest.mark.parametrize("H,I", [(384, 384), (640, 256)])
+def test_large_tile_segment_remainders(H, I):
+    """Expert segments whose remainders past the last 256-row tile are 1, 44,
+    128 (128-row wide tiles), 129, 255 (one more full tile) and 0, with odd
+    n-tile counts in one GEMM or the other (I / 128 = 3, H / 256 = 2.5), so
+    the last 512-row range of a wide tile runs past the weights."""
+    torch_cuda()
+    ml, dv = _mods()
+    counts = [257, 300, 384, 385, 511, 512, 513, 640]
+    cfg = small_cfg(T=sum(counts), H=H, E=8, E_L=8, k=1, I=I)
+    d = synth.make_inputs(cfg, 13, x_std=1.0, std=0.05)
+    rng = np.random.default_rng(13)
+    expert = np.repeat(np.arange(8), counts)
+    rng.shuffle(expert)
+    lg = rng.normal(size=(cfg.T, 8)).astype(np.float32)
+    lg[np.arange(cfg.T), expert] += 20.0
+    d["logits"] = lg
+    dev = dv.upload(d, False)
+    check_small_case(f"remainders H={H} I={I}", cfg, d, dev)
+
+
+def check_small_case(name, cfg, d, dev):
+    torch = torch_cuda()
+    ml, dv = _mods()
     p = ml.Problem.from_config(cfg)
     say("layer small", name)
     st = run_staged(torch, p, dev)

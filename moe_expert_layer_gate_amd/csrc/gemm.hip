@@ -556,9 +556,29 @@ __device__ __forceinline__ void expert_units(int cnt, int& full, int& wide) {
   if (rem > kWideBM) ++full;
 }
 
+// Writes one table; every thread takes units u = tid, tid + 1024, ... and
+// finds the unit's expert by binary search over the experts' first units.
+__device__ __forceinline__ void write_units(const int* s_start, const int* s_off,
+                                            const int* s_full, int E_L, int nt, int total,
+                                            int4* __restrict__ units) {
+  for (int u = threadIdx.x; u < total; u += blockDim.x) {
+    int lo = 0, hi = E_L - 1;  // last expert whose first unit is <= u
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_start[mid] <= u) lo = mid; else hi = mid - 1;
+    }
+    const int e = lo, v = u - s_start[e], full = s_full[e];
+    if (v < full * nt)
+      units[u] = make_int4(e, s_off[e] + (v % full) * kBigBM, v / full, 0);
+    else
+      units[u] = make_int4(e, s_off[e] + full * kBigBM, v - full * nt, 1);
+  }
+}
+
 __global__ __launch_bounds__(1024) void unit_schedule_kernel(
     const int32_t* __restrict__ offsets, int E_L, int nt_a, int nt_b, int4* __restrict__ units_a,
     int32_t* __restrict__ n_a, int4* __restrict__ units_b, int32_t* __restrict__ n_b) {
+  __shared__ int s_off[1024], s_full[1024], s_sa[1024], s_sb[1024];
   const int e = threadIdx.x;
   int cnt = 0, off = 0;
   if (e < E_L) {
@@ -572,19 +592,14 @@ __global__ __launch_bounds__(1024) void unit_schedule_kernel(
   const int sa = block_exclusive_scan(full * nt_a + wide * nw_a, &tot_a);
   const int sb = block_exclusive_scan(full * nt_b + wide * nw_b, &tot_b);
   if (e < E_L) {
-    for (int n = 0; n < nt_a; ++n)
-      for (int m = 0; m < full; ++m)
-        units_a[sa + n * full + m] = make_int4(e, off + m * kBigBM, n, 0);
-    for (int n = 0; n < nt_b; ++n)
-      for (int m = 0; m < full; ++m)
-        units_b[sb + n * full + m] = make_int4(e, off + m * kBigBM, n, 0);
-    if (wide) {
-      for (int r = 0; r < nw_a; ++r)
-        units_a[sa + full * nt_a + r] = make_int4(e, off + full * kBigBM, r, 1);
-      for (int r = 0; r < nw_b; ++r)
-        units_b[sb + full * nt_b + r] = make_int4(e, off + full * kBigBM, r, 1);
-    }
+    s_off[e] = off;
+    s_full[e] = full;
+    s_sa[e] = sa;
+    s_sb[e] = sb;
   }
+  __syncthreads();
+  write_units(s_sa, s_off, s_full, E_L, nt_a, tot_a, units_a);
+  write_units(s_sb, s_off, s_full, E_L, nt_b, tot_b, units_b);
   if (e == 0) {
     *n_a = tot_a;
     *n_b = tot_b;
@@ -728,22 +743,33 @@ __device__ __forceinline__ void big_tile(const GemmArgs& g, const int4 unit, uin
   const int cq = (lane >> 5) * 4;
   uint16_t* C = static_cast<uint16_t*>(g.C);
   if constexpr (MODE == MODE_PLAIN) {
+    // The wave's 64 x 128 result goes through LDS so that the stores write
+    // whole 256-byte row pieces (16 lanes per row, 4 rows per instruction)
+    // instead of 16 bytes of 32 rows each.  Every wave is past its last
+    // fragment read and direct load once all have reached the barrier.
+    constexpr int kPitch = 272;  // 256 bytes + 16: rows start 4 banks apart
+    static_assert(8 * 64 * kPitch <= kBigStages * kBigStageBytes, "epilogue tile fits the ring");
+    __builtin_amdgcn_s_barrier();
+    uint8_t* stile = smem + w * 64 * kPitch;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int m = row0 + wm * 64 + j * 32 + lr;
-      if (m >= seg_end) continue;
-      uint16_t* crow = C + static_cast<int64_t>(m) * g.Nout;
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int col = nbase + wn * 128 + i * 32 + q * 8 + cq;
-          if (col >= g.Nout) continue;
           uint2 o;
           o.x = pack_bf16x2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]);
           o.y = pack_bf16x2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
-          *reinterpret_cast<uint2*>(crow + col) = o;
+          *reinterpret_cast<uint2*>(stile + (j * 32 + lr) * kPitch + (i * 32 + q * 8 + cq) * 2) = o;
         }
+    const int col = nbase + wn * 128 + (lane & 15) * 8;
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int rl = it * 4 + (lane >> 4);
+      const uint4 v = *reinterpret_cast<const uint4*>(stile + rl * kPitch + (lane & 15) * 16);
+      const int m = row0 + wm * 64 + rl;
+      if (m < seg_end && col < g.Nout)
+        *reinterpret_cast<uint4*>(C + static_cast<int64_t>(m) * g.Nout + col) = v;
     }
   } else {
 #pragma unroll

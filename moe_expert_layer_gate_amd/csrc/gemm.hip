@@ -549,11 +549,11 @@ constexpr int kBigStageBytes = (kWideBM + kWideBN) * kBigRowBytes;  // 40 KB
 // n-index, wide}: the n-index counts 256-row weight tiles of a full tile or
 // 512-row ranges of a wide one.  An expert with 129..255 rows past its last
 // full tile gets one more full tile instead of a wide one.
-__device__ __forceinline__ void expert_units(int cnt, int& full, int& wide) {
+__device__ __forceinline__ void expert_units(int cnt, bool allow_wide, int& full, int& wide) {
   full = cnt / kBigBM;
   const int rem = cnt - full * kBigBM;
-  wide = rem > 0 && rem <= kWideBM;
-  if (rem > kWideBM) ++full;
+  wide = allow_wide && rem > 0 && rem <= kWideBM;
+  if (rem > 0 && !wide) ++full;
 }
 
 // Writes one table; every thread takes units u = tid, tid + 1024, ... and
@@ -576,8 +576,9 @@ __device__ __forceinline__ void write_units(const int* s_start, const int* s_off
 }
 
 __global__ __launch_bounds__(1024) void unit_schedule_kernel(
-    const int32_t* __restrict__ offsets, int E_L, int nt_a, int nt_b, int4* __restrict__ units_a,
-    int32_t* __restrict__ n_a, int4* __restrict__ units_b, int32_t* __restrict__ n_b) {
+    const int32_t* __restrict__ offsets, int E_L, int nt_a, int nt_b, bool allow_wide,
+    int4* __restrict__ units_a, int32_t* __restrict__ n_a, int4* __restrict__ units_b,
+    int32_t* __restrict__ n_b) {
   __shared__ int s_off[1024], s_full[1024], s_sa[1024], s_sb[1024];
   const int e = threadIdx.x;
   int cnt = 0, off = 0;
@@ -586,7 +587,7 @@ __global__ __launch_bounds__(1024) void unit_schedule_kernel(
     cnt = offsets[e + 1] - off;
   }
   int full, wide;
-  expert_units(cnt, full, wide);
+  expert_units(cnt, allow_wide, full, wide);
   const int nw_a = (nt_a + 1) / 2, nw_b = (nt_b + 1) / 2;
   int tot_a, tot_b;
   const int sa = block_exclusive_scan(full * nt_a + wide * nw_a, &tot_a);
@@ -830,12 +831,285 @@ hipError_t launch_big(const GemmArgs& g, int64_t max_units, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Large-tile block-FP8 kernel: 256 token rows x 256 weight rows, 4 waves (one
+// per SIMD) as 2 (rows) x 2 (weights), each wave 128 x 128 (4 x 4 MFMA 32x32
+// tiles).  One K step is one 128-wide scale block: 128 bytes of every row
+// through a two-stage LDS ring (65 KB stages: codes plus the step's 256 token
+// scales, all by direct loads), loads one step ahead.
+//  * Scales: for each 32x32 tile the two MFMAs of the step (K 0..63, 64..127)
+//    run into a fresh accumulator that is then added to the tile's sum times
+//    (weight block scale x token group scale) -- 16 FMAs per two MFMAs,
+//    which the SIMD overlaps with the following tiles' MFMAs.
+//  * A wave's 128 x 128 block reads 512 bytes of fragments per lane and step
+//    from LDS for 32 MFMAs; tokens and weights each cross L2 once per 256 x
+//    256 tile.
+//  * Fused gather: with a_index, token row j is row a_index[j] of the codes
+//    and of the scales.
+// ---------------------------------------------------------------------------
+constexpr int kF8BM = 256, kF8BN = 256, kF8Threads = 256;
+constexpr int kF8RowBytes = 128;
+constexpr int kF8ScaleOff = (kF8BM + kF8BN) * kF8RowBytes;     // 64 KB
+constexpr int kF8StageBytes = kF8ScaleOff + kF8BM * 4 + 1024;  // + token scales, padded
+constexpr int kF8Pitch = 272;                                  // bf16 epilogue rows
+constexpr int kF8Lds = 4 * 128 * kF8Pitch;                     // >= 2 stages
+static_assert(2 * kF8StageBytes <= kF8Lds, "two stages fit the epilogue area");
+
+template <int MODE>
+__global__ __launch_bounds__(kF8Threads, 1) void gemm_big_fp8_kernel(const GemmArgs g) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  __shared__ float row_amax[2][kF8BM];
+  constexpr bool kSwiglu = MODE != MODE_PLAIN;
+  constexpr int kLoads = (kF8BM + kF8BN) / 8 / 4;  // 16 loads of 8 rows per wave and step
+
+  const int total = *g.n_tiles;
+  const int per_xcd = ceil_div(total, kXcds);
+  const int slot = blockIdx.x / kXcds;
+  if (slot >= per_xcd) return;
+  const int t = (blockIdx.x % kXcds) * per_xcd + slot;
+  if (t >= total) return;
+  const int4 unit = g.info[t];
+  const int e = unit.x, row0 = unit.y, nt = unit.z;
+  const int seg_end = g.offsets[e + 1];
+  const int ldb = g.K;               // bytes per row of A and W
+  const int nk = g.K / 128;
+  const int kb_n = g.K / 128;        // scale blocks per row
+
+  const uint8_t* a_base = g.A + (g.a_index ? 0 : static_cast<int64_t>(row0) * ldb);
+  const int64_t a_left = g.a_bytes - (g.a_index ? 0 : static_cast<int64_t>(row0) * ldb);
+  const float* s_base = g.A_scale + (g.a_index ? 0 : static_cast<int64_t>(row0) * kb_n);
+  const int64_t s_left = (g.a_bytes / ldb - (g.a_index ? 0 : row0)) * kb_n * 4;
+  const uint8_t* w_base = g.W + e * g.w_stride;
+  const int nbase = kSwiglu ? nt * (kF8BN / 2) : nt * kF8BN;
+
+  const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
+  // direct loads: wave w moves A groups w*8 .. w*8+7 and W groups
+  // 32 + w*8 .. (8 rows of 128 bytes each), and the token scales of rows
+  // w*64 .. w*64+63.
+  int voff[kLoads], ldst[kLoads];
+#pragma unroll
+  for (int q = 0; q < kLoads; ++q) {
+    const int grp = q < 8 ? w * 8 + q : 32 + w * 8 + (q - 8);
+    const int rr = grp * 8 + (lane >> 3);
+    const int chunk = (lane & 7) ^ ((rr >> 1) & 7);
+    if (rr < kF8BM) {
+      const bool valid = row0 + rr < seg_end;
+      const int arow = g.a_index && valid ? g.a_index[row0 + rr] : rr;
+      voff[q] = valid ? arow * ldb + chunk * 16 : kOobOffset;
+    } else {
+      const int r = rr - kF8BM;
+      int grow;
+      if (kSwiglu)
+        grow = r < kF8BN / 2 ? min(nbase + r, g.Nout - 1)
+                             : g.Nout + min(nbase + (r - kF8BN / 2), g.Nout - 1);
+      else
+        grow = min(nbase + r, g.NW - 1);
+      voff[q] = grow * ldb + chunk * 16;
+    }
+    ldst[q] = grp * 1024;
+  }
+  int soff;
+  {
+    const int rr = w * 64 + lane;
+    const bool valid = row0 + rr < seg_end;
+    const int arow = g.a_index && valid ? g.a_index[row0 + rr] : rr;
+    soff = valid ? arow * kb_n * 4 : kOobOffset;
+  }
+  auto dma = [&](int step, int stage) {
+    const int64_t k = step;
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(a_base + k * 128, a_left - k * 128);
+    const __amdgpu_buffer_rsrc_t rW = make_rsrc(w_base + k * 128, g.w_stride - k * 128);
+    const __amdgpu_buffer_rsrc_t rS = make_rsrc(s_base + k, s_left - k * 4);
+    uint8_t* base = smem + stage * kF8StageBytes;
+#pragma unroll
+    for (int q = 0; q < kLoads; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(q < 8 ? rA : rW, (lds_ptr_t)(base + ldst[q]), 16,
+                                               voff[q], 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_ptr_t)(base + kF8ScaleOff + w * 256), 4,
+                                             soff, 0, 0, 0);
+  };
+
+  // ---- fragments: lane reads 32 bytes (K 32 hi .. 32 hi + 31 of the
+  // sub-step's 64) of row lr of a 32-row block, as two swizzled 16-byte chunks
+  const int wm = w & 1, wn = w >> 1;
+  const int lr = lane & 31, hi = lane >> 5, sl = (lr >> 1) & 7;
+  int foff[2][2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const int c0 = (4 * kk + 2 * hi) ^ sl;
+    foff[kk][0] = lr * kF8RowBytes + c0 * 16;
+    foff[kk][1] = lr * kF8RowBytes + (c0 ^ 1) * 16;
+  }
+  int wbase[4], abase[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = kSwiglu ? (i < 2 ? 0 : kF8BN / 2) + wn * 64 + (i & 1) * 32 : wn * 128 + i * 32;
+    wbase[i] = kF8BM * kF8RowBytes + row * kF8RowBytes;
+    abase[i] = (wm * 128 + i * 32) * kF8RowBytes;
+  }
+  // weight block scales: uniform per wave, scalar loads
+  const float* wsc = g.W_scale + e * g.ws_stride;
+  const float* swp[2];
+  if (kSwiglu) {
+    swp[0] = wsc + static_cast<int64_t>(min(nbase, g.Nout - 1) / 128) * kb_n;
+    swp[1] = wsc + static_cast<int64_t>((g.Nout + min(nbase, g.Nout - 1)) / 128) * kb_n;
+  } else {
+    swp[0] = swp[1] =
+        wsc + static_cast<int64_t>(min(nbase + __builtin_amdgcn_readfirstlane(wn) * 128, g.NW - 1) / 128) * kb_n;
+  }
+  auto wscale = [&](int which, int k) {
+    return ((const __attribute__((address_space(4))) float*)(uintptr_t)swp[which])[k];
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  auto rd32 = [&](const uint8_t* p0, const uint8_t* p1) {
+    const i32x4 lo = *reinterpret_cast<const i32x4*>(p0), h4 = *reinterpret_cast<const i32x4*>(p1);
+    return i32x8{lo[0], lo[1], lo[2], lo[3], h4[0], h4[1], h4[2], h4[3]};
+  };
+
+  dma(0, 0);
+  WAIT_VMCNT(0);
+  __builtin_amdgcn_s_barrier();
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const uint8_t* st = smem + (kt & 1) * kF8StageBytes;
+    // the other stage was released by the barrier that ended step kt - 1
+    if (kt + 1 < nk) dma(kt + 1, (kt + 1) & 1);
+    const float sw0 = wscale(0, kt), sw1 = wscale(1, kt);
+    i32x8 fa[2][4], fb[2][4];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        fb[kk][j] = rd32(st + abase[j] + foff[kk][0], st + abase[j] + foff[kk][1]);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        fa[kk][i] = rd32(st + wbase[i] + foff[kk][0], st + wbase[i] + foff[kk][1]);
+    float sx[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      sx[j] = *reinterpret_cast<const float*>(st + kF8ScaleOff + (wm * 128 + j * 32 + lr) * 4);
+    const f32x16 zero = {0};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f32x16 tt = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[0][i], fb[0][j], zero, 0, 0,
+                                                                   0, 0, 0, 0);
+        tt = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[1][i], fb[1][j], tt, 0, 0, 0, 0, 0,
+                                                            0);
+        const float c = (kSwiglu && i >= 2 ? sw1 : sw0) * sx[j];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] += tt[r] * c;
+      }
+    // Step boundary: this wave's loads of step kt+1 have landed and its reads
+    // of stage kt are done; the barrier publishes both.
+    WAIT_VMCNT_LDS(0);
+    __builtin_amdgcn_s_barrier();
+  }
+
+  const int cq = (lane >> 5) * 4;
+  if constexpr (MODE == MODE_PLAIN) {
+    // bf16 rows through LDS: 256-byte row pieces per 16 lanes (see the
+    // bf16 large-tile kernel); the last barrier of the loop freed the ring.
+    uint16_t* C = static_cast<uint16_t*>(g.C);
+    uint8_t* stile = smem + w * 128 * kF8Pitch;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint2 o;
+          o.x = pack_bf16x2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]);
+          o.y = pack_bf16x2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
+          *reinterpret_cast<uint2*>(stile + (j * 32 + lr) * kF8Pitch + (i * 32 + q * 8 + cq) * 2) = o;
+        }
+    const int col = nbase + wn * 128 + (lane & 15) * 8;
+#pragma unroll 4
+    for (int it = 0; it < 32; ++it) {
+      const int rl = it * 4 + (lane >> 4);
+      const uint4 v = *reinterpret_cast<const uint4*>(stile + rl * kF8Pitch + (lane & 15) * 16);
+      const int m = row0 + wm * 128 + rl;
+      if (m < seg_end && col < g.Nout)
+        *reinterpret_cast<uint4*>(C + static_cast<int64_t>(m) * g.Nout + col) = v;
+    }
+  } else {
+    static_assert(MODE == MODE_SWIGLU_FP8OUT, "block-FP8 h output only");
+    // h = silu(gate) * up; the block's 128 h columns are one quantisation
+    // group, split over the two waves of a row range (64 columns each)
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[hb][j][r] = silu_mul(acc[hb][j][r], acc[hb + 2][j][r]);
+    float amax[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float m = 0.0f;
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(acc[hb][j][r]));
+      m = fmaxf(m, __shfl_xor(m, 32));
+      amax[j] = m;
+      if (lane < 32) row_amax[wn][wm * 128 + j * 32 + lr] = m;
+    }
+    __syncthreads();
+    uint8_t* C = static_cast<uint8_t*>(g.C);
+    const int groups = g.Nout / 128;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int lrow = wm * 128 + j * 32 + lr;
+      const float am = fmaxf(amax[j], row_amax[wn ^ 1][lrow]);
+      const float sc = am > 0.0f ? am / 448.0f : 1.0f;
+      const int m = row0 + lrow;
+      if (m >= seg_end) continue;
+      uint8_t* crow = C + static_cast<int64_t>(m) * g.Nout;
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t v = f32x4_to_e4m3x4(acc[hb][j][q * 4 + 0] / sc, acc[hb][j][q * 4 + 1] / sc,
+                                             acc[hb][j][q * 4 + 2] / sc, acc[hb][j][q * 4 + 3] / sc);
+          *reinterpret_cast<uint32_t*>(crow + nbase + wn * 64 + hb * 32 + q * 8 + cq) = v;
+        }
+      if (wn == 0 && lane < 32) g.C_scale[static_cast<int64_t>(m) * groups + nt] = sc;
+    }
+  }
+}
+
+template <int MODE>
+hipError_t launch_big_fp8(const GemmArgs& g, int64_t max_units, hipStream_t s) {
+  auto kern = gemm_big_fp8_kernel<MODE>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kF8Lds) != hipSuccess)
+      (void)hipGetLastError();
+    attr_set = true;
+  }
+  const int64_t blocks = (max_units + kXcds - 1) / kXcds * kXcds + kXcds;
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(kF8Threads), kF8Lds, s, g);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 int gemm_tile_m(bool fp8, int64_t rows_per_expert) {
   // Few rows per expert (decode-sized batches): the 256-row tile would spend
   // most of its matrix-core time on padding while the work is weight streaming.
-  return (fp8 || rows_per_expert <= 2 * kBM) ? kBM : kBigBM;
+  return rows_per_expert <= 2 * kBM ? kBM : kBigBM;
 }
 
 int gemm_n_tiles(int tile_m, bool swiglu, int Nout) {
@@ -848,12 +1122,12 @@ int64_t schedule_entries(int64_t n_cap, int E_L, int tile_m, int nt) {
   return ceil_div<int64_t>(n_cap, tile_m) + E_L;
 }
 
-hipError_t launch_schedule(const int32_t* offsets, int E_L, int tile_m, int nt_up, int nt_dn,
-                           int4* tab_up, int32_t* n_up, int4* tab_dn, int32_t* n_dn,
+hipError_t launch_schedule(const int32_t* offsets, int E_L, int tile_m, bool fp8, int nt_up,
+                           int nt_dn, int4* tab_up, int32_t* n_up, int4* tab_dn, int32_t* n_dn,
                            hipStream_t s) {
-  if (tile_m == kBigBM)
+  if (tile_m == kBigBM)  // the block-FP8 kernel has no wide tiles
     hipLaunchKernelGGL(unit_schedule_kernel, dim3(1), dim3(1024), 0, s, offsets, E_L, nt_up, nt_dn,
-                       tab_up, n_up, tab_dn, n_dn);
+                       !fp8, tab_up, n_up, tab_dn, n_dn);
   else
     hipLaunchKernelGGL(tile_schedule_kernel, dim3(1), dim3(1024), 0, s, offsets, E_L, tile_m,
                        tab_up, n_up);
@@ -898,6 +1172,11 @@ hipError_t launch_grouped_gemm(const GemmLaunch& L, hipStream_t s) {
     }
     if (L.swiglu) return launch_pipelined<false, MODE_SWIGLU>(g, L.max_tiles, s);
     return launch_pipelined<false, MODE_PLAIN>(g, L.max_tiles, s);
+  }
+  if (L.tile_m == kBigBM) {
+    if (!L.swiglu) return launch_big_fp8<MODE_PLAIN>(g, L.max_tiles, s);
+    if (!L.C_scale) return hipErrorInvalidValue;  // block-FP8 h only
+    return launch_big_fp8<MODE_SWIGLU_FP8OUT>(g, L.max_tiles, s);
   }
   if (L.swiglu) {
     if (L.C_scale) return launch_pipelined<true, MODE_SWIGLU_FP8OUT>(g, L.max_tiles, s);

@@ -31,8 +31,8 @@ hipError_t launch_quant_blocks(const void* src, int64_t batch, int64_t rows, int
                                void* codes, float* scales, hipStream_t s);
 
 // Row tile of the grouped GEMM for a problem: 128 (the pipelined kernel, for
-// block-FP8 and for few rows per expert) or 256 (the large-tile kernel, which
-// covers segment remainders of up to 128 rows with 128 x 512 tiles).
+// few rows per expert) or 256 (the large-tile kernels; the bf16 one covers
+// segment remainders of up to 128 rows with 128 x 512 tiles).
 int gemm_tile_m(bool fp8, int64_t rows_per_expert);
 // n-tiles per expert of one GEMM.
 int gemm_n_tiles(int tile_m, bool swiglu, int Nout);
@@ -42,8 +42,8 @@ int gemm_n_tiles(int tile_m, bool swiglu, int Nout);
 int64_t schedule_entries(int64_t n_cap, int E_L, int tile_m, int nt);
 // Builds the work tables on the device from the expert offsets (tile_m 128:
 // only tab_up / n_up are written).
-hipError_t launch_schedule(const int32_t* offsets, int E_L, int tile_m, int nt_up, int nt_dn,
-                           int4* tab_up, int32_t* n_up, int4* tab_dn, int32_t* n_dn,
+hipError_t launch_schedule(const int32_t* offsets, int E_L, int tile_m, bool fp8, int nt_up,
+                           int nt_dn, int4* tab_up, int32_t* n_up, int4* tab_dn, int32_t* n_dn,
                            hipStream_t s);
 struct GemmLaunch {
   bool fp8;              // e4m3 operands with block scales, else bf16

@@ -225,8 +225,8 @@ moe_status run_ffn(const moe_problem* p, const FfnSource& src, const int32_t* of
   const FfnShape sh = ffn_shape(p);
   void* hb = h ? h : f.h;
   float* hs = h ? h_scale : f.h_scale;
-  MOE_TRY(launch_schedule(offsets, E_L, sh.tile_m, sh.nt_up, sh.nt_dn, f.tab_up, f.n_up, f.tab_dn,
-                          f.n_dn, s));
+  MOE_TRY(launch_schedule(offsets, E_L, sh.tile_m, is_fp8(p), sh.nt_up, sh.nt_dn, f.tab_up, f.n_up,
+                          f.tab_dn, f.n_dn, s));
   GemmLaunch up{};
   up.fp8 = is_fp8(p);
   up.swiglu = true;

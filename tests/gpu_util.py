@@ -46,6 +46,20 @@ def rel_rows(got: np.ndarray, ref: np.ndarray) -> float:
     return float((num / den).max())
 
 
+def rel_rows_all(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """Per-row relative l2 errors (rows whose reference is exactly zero: 0 if
+    the row is exactly zero too, else inf)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    num = np.linalg.norm(got - ref, axis=1)
+    den = np.linalg.norm(ref, axis=1)
+    zero = den == 0
+    out = num / np.where(zero, 1.0, den)
+    out[zero & (num != 0)] = np.inf
+    return out
+
+
 def global_rel(got, ref) -> float:
     ref = np.asarray(ref, dtype=np.float64)
     d = np.linalg.norm(np.asarray(got, dtype=np.float64) - ref)

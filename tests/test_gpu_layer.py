@@ -9,8 +9,8 @@ import pytest
 
 from moe_expert_layer_gate_amd import inputs as synth
 from oracle import moe_oracle as O
-from tests.gpu_util import (TOL_BF16, TOL_FP8, OracleWeights, global_rel, rel_rows, say,
-                            small_cfg, torch_cuda, unpanel)
+from tests.gpu_util import (TOL_BF16, TOL_FP8, OracleWeights, global_rel, rel_rows,
+                            rel_rows_all, say, small_cfg, torch_cuda, unpanel)
 
 pytestmark = pytest.mark.gpu
 
@@ -113,6 +113,10 @@ SMALL_FP8 = {
     "fp8_small": (small_cfg(T=200, H=512, E=16, E_L=8, e_lo=0, k=4, I=256, fp8=True), 8),
     "fp8_shared": (small_cfg(T=150, H=1024, E=64, E_L=16, e_lo=16, k=8, I=512, I_s=256,
                              fp8=True, logits="gumbel_zipf"), 9),
+    # more than 256 rows per expert: the large-tile block-FP8 kernel, ragged
+    # segments, and a shared expert over all 1300 tokens
+    "fp8_big_tiles": (small_cfg(T=1300, H=512, E=8, E_L=4, e_lo=2, k=2, I=384, I_s=256,
+                                fp8=True, logits="gumbel_zipf"), 14),
 }
 
 
@@ -131,8 +135,9 @@ def test_staged_and_fused_layer_small(name):
     check_small_case(name, cfg, d, dev)
 
 
+@pytest.mark.parametrize("fp8", [False, True])
 @pytest.mark.parametrize("H,I", [(384, 384), (640, 256)])
-def test_large_tile_segment_remainders(H, I):
+def test_large_tile_segment_remainders(H, I, fp8):
     """Expert segments whose remainders past the last 256-row tile are 1, 44,
     128 (128-row wide tiles), 129, 255 (one more full tile) and 0, with odd
     n-tile counts in one GEMM or the other (I / 128 = 3, H / 256 = 2.5), so
@@ -140,7 +145,7 @@ def test_large_tile_segment_remainders(H, I):
     torch_cuda()
     ml, dv = _mods()
     counts = [257, 300, 384, 385, 511, 512, 513, 640]
-    cfg = small_cfg(T=sum(counts), H=H, E=8, E_L=8, k=1, I=I)
+    cfg = small_cfg(T=sum(counts), H=H, E=8, E_L=8, k=1, I=I, fp8=fp8)
     d = synth.make_inputs(cfg, 13, x_std=1.0, std=0.05)
     rng = np.random.default_rng(13)
     expert = np.repeat(np.arange(8), counts)
@@ -148,8 +153,8 @@ def test_large_tile_segment_remainders(H, I):
     lg = rng.normal(size=(cfg.T, 8)).astype(np.float32)
     lg[np.arange(cfg.T), expert] += 20.0
     d["logits"] = lg
-    dev = dv.upload(d, False)
-    check_small_case(f"remainders H={H} I={I}", cfg, d, dev)
+    dev = dv.upload(d, fp8)
+    check_small_case(f"remainders H={H} I={I} fp8={fp8}", cfg, d, dev)
 
 
 def check_small_case(name, cfg, d, dev):
@@ -165,7 +170,19 @@ def check_small_case(name, cfg, d, dev):
     # workloads' own spreads below).
     ref = O.moe_layer(d["logits"], d["x"], ow.as_layer_dict(cfg.E_L), k=cfg.k, e_lo=cfg.e_lo,
                       E_L=cfg.E_L, fp8=cfg.fp8, quantize_activations=cfg.fp8)
-    tol = TOL_BF16
+    # bf16: every row within 2e-2.  fp8: h is rounded to E4M3 on both sides,
+    # from fp32 sums on the GPU and fp64 sums in the oracle, so an element
+    # that sits on a rounding boundary can land one code apart (a 6-12 %
+    # change of that element); a row dominated by such an element exceeds
+    # 2e-2 although both are correct.  There the gate is the block-FP8
+    # one (6e-2) on every row, and 2e-2 on 99 % of the rows.
+    def ok(got, ref):
+        e = rel_rows_all(got, ref)
+        if e.size == 0:
+            return True
+        if not cfg.fp8:
+            return e.max() <= TOL_BF16
+        return e.max() <= TOL_FP8 and np.percentile(e, 99) <= TOL_BF16
     # exact routing and permutation
     np.testing.assert_array_equal(st["ids"].cpu().numpy(), ref["ids"])
     np.testing.assert_array_equal(st["offsets"].cpu().numpy(), ref["offsets"])
@@ -178,9 +195,11 @@ def check_small_case(name, cfg, d, dev):
     e_yp = rel_rows(f64(st["y_perm"][:N]), ref["y_perm"])
     e_y = rel_rows(f64(st["y"]), ref["y"])
     print(f"{name}: h {e_h:.2e}  y_perm {e_yp:.2e}  y {e_y:.2e}  global {global_rel(f64(st['y']), ref['y']):.2e}")
-    assert e_h <= tol and e_yp <= tol and e_y <= tol
+    assert ok(h_values(st, p), ref_h)
+    assert ok(f64(st["y_perm"][:N]), ref["y_perm"])
+    assert ok(f64(st["y"]), ref["y"])
     if ref["shared"] is not None:
-        assert rel_rows(f64(st["shared"]), ref["shared"]) <= tol
+        assert ok(f64(st["shared"]), ref["shared"])
     # fused layer: same routing, same numbers as the staged calls
     y = run_layer(torch, p, dev, guard=3)
     np.testing.assert_array_equal(dv.bits_from_bf16(y), dv.bits_from_bf16(st["y"]))

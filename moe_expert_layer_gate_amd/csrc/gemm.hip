@@ -71,7 +71,7 @@ struct GemmArgs {
   // + c % 64 -- row major: rs = row bytes, cs = 64; panel layout: rs = 64,
   // cs = 64 * rows of the matrix.
   int a_rs, w_rs;
-  int64_t a_cs, w_cs;
+  int a_cs, w_cs;          // (a buffer's whole span stays below 2 GiB, see the host)
   int64_t a_bytes;         // size of the A buffer
   int64_t c_cs;            // SwiGLU bf16 output: 0 = row major, else panel stride
   const int32_t* a_index;  // fused gather: GEMM row j reads A row a_index[j]
@@ -228,16 +228,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pipelined_kernel(const GemmA
                       static_cast<int64_t>(min(seg_end - row0, kBM)) * kb_n * 4)
           : make_rsrc(g.A, 0);
   const int soffs = ((w & 1) * 64 + lane) * kb_n * 4;
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(a_base, a_left);
+  const __amdgpu_buffer_rsrc_t rW = make_rsrc(w_base, g.w_stride);
   auto dma = [&](int step, int stage) {
-    const int k = min(step, nk - 1);
-    const int64_t p = 2 * k;  // 64-byte K pieces before this step
-    const __amdgpu_buffer_rsrc_t rA = make_rsrc(a_base + p * g.a_cs, a_left - p * g.a_cs);
-    const __amdgpu_buffer_rsrc_t rW = make_rsrc(w_base + p * g.w_cs, g.w_stride - p * g.w_cs);
+    const int k = min(step, nk - 1);  // step k starts at 64-byte K piece 2k
     uint8_t* base = smem + stage * kStageBytes;
 #pragma unroll
     for (int q = 0; q < kDmaPerWave; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(q < 4 ? rA : rW, (lds_ptr_t)(base + ldst[q]), 16,
-                                               voff[q], 0, 0, 0);
+                                               voff[q], 2 * k * (q < 4 ? g.a_cs : g.w_cs), 0, 0);
     if (FP8)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_ptr_t)(base + kScaleRegion + (w & 1) * 256),
                                                4, soffs, k * 4, 0, 0);
@@ -656,15 +655,16 @@ __device__ __forceinline__ void big_tile(const GemmArgs& g, const int4 unit, uin
     }
     ldst[q] = grp * 1024;
   }
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(a_base, a_left);
+  const __amdgpu_buffer_rsrc_t rW = make_rsrc(w_base, g.w_stride);
   auto dma = [&](int step, int stage) {
-    const int64_t k = min(step, nk - 1);
-    const __amdgpu_buffer_rsrc_t rA = make_rsrc(a_base + k * g.a_cs, a_left - k * g.a_cs);
-    const __amdgpu_buffer_rsrc_t rW = make_rsrc(w_base + k * g.w_cs, g.w_stride - k * g.w_cs);
+    const int k = min(step, nk - 1);
     uint8_t* base = smem + stage * kBigStageBytes;
 #pragma unroll
     for (int q = 0; q < kLoads; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(q < kALoads ? rA : rW, (lds_ptr_t)(base + ldst[q]),
-                                               16, voff[q], 0, 0, 0);
+                                               16, voff[q], k * (q < kALoads ? g.a_cs : g.w_cs), 0,
+                                               0);
   };
 
   const int wm = w % kWaveRows, wn = w / kWaveRows;
@@ -915,18 +915,17 @@ __global__ __launch_bounds__(kF8Threads, 1) void gemm_big_fp8_kernel(const GemmA
     const int arow = g.a_index && valid ? g.a_index[row0 + rr] : rr;
     soff = valid ? arow * kb_n * 4 : kOobOffset;
   }
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(a_base, a_left);
+  const __amdgpu_buffer_rsrc_t rW = make_rsrc(w_base, g.w_stride);
+  const __amdgpu_buffer_rsrc_t rS = make_rsrc(s_base, s_left);
   auto dma = [&](int step, int stage) {
-    const int64_t k = step;
-    const __amdgpu_buffer_rsrc_t rA = make_rsrc(a_base + k * 128, a_left - k * 128);
-    const __amdgpu_buffer_rsrc_t rW = make_rsrc(w_base + k * 128, g.w_stride - k * 128);
-    const __amdgpu_buffer_rsrc_t rS = make_rsrc(s_base + k, s_left - k * 4);
     uint8_t* base = smem + stage * kF8StageBytes;
 #pragma unroll
     for (int q = 0; q < kLoads; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(q < 8 ? rA : rW, (lds_ptr_t)(base + ldst[q]), 16,
-                                               voff[q], 0, 0, 0);
+                                               voff[q], step * 128, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_ptr_t)(base + kF8ScaleOff + w * 256), 4,
-                                             soff, 0, 0, 0);
+                                             soff, step * 4, 0, 0);
   };
 
   // ---- fragments: lane reads 32 bytes (K 32 hi .. 32 hi + 31 of the
@@ -1158,10 +1157,13 @@ hipError_t launch_grouped_gemm(const GemmLaunch& L, hipStream_t s) {
   const int64_t ldb = L.K * elem;
   g.w_stride = static_cast<int64_t>(g.NW) * ldb;
   g.ws_stride = L.fp8 ? static_cast<int64_t>(g.NW / 128) * (L.K / 128) : 0;
+  // Per-step buffer offsets are 32-bit: a panel-layout A must span less than
+  // the range cap (row-major A is addressed from its tile's first row).
+  if (L.a_panel && L.a_rows * ldb > kBufMax) return hipErrorInvalidValue;
   g.a_rs = L.a_panel ? 64 : static_cast<int>(ldb);
-  g.a_cs = L.a_panel ? 64 * L.a_rows : 64;
+  g.a_cs = L.a_panel ? static_cast<int>(64 * L.a_rows) : 64;
   g.w_rs = L.w_panel ? 64 : static_cast<int>(ldb);
-  g.w_cs = L.w_panel ? 64 * static_cast<int64_t>(g.NW) : 64;
+  g.w_cs = L.w_panel ? 64 * g.NW : 64;
   g.a_bytes = L.a_rows * ldb;
   g.c_cs = L.c_panel ? 64 * L.c_rows : 0;
   g.a_index = L.a_index;

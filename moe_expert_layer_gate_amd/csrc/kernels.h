@@ -71,8 +71,10 @@ struct GemmLaunch {
   const int32_t* a_index;
 };
 hipError_t launch_grouped_gemm(const GemmLaunch& L, hipStream_t s);
-// Largest fused-gather source (bytes) the GEMM's 32-bit lane offsets reach.
+// Largest fused-gather source and largest panel-layout activation matrix
+// (bytes) that the GEMM's 32-bit buffer offsets reach.
 constexpr int64_t kGemmGatherMaxBytes = 0x7ffffe00;
+constexpr int64_t kGemmPanelMaxBytes = 0x7ffffe00;
 
 hipError_t launch_combine(const void* y_perm, const int32_t* token_slot_row, const float* topk_w,
                           const void* shared_out, int T, int k, int H, void* y, hipStream_t s);

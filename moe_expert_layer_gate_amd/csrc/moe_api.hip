@@ -37,9 +37,9 @@ moe_status check_problem(const moe_problem* p) {
   // One expert's weight matrix must stay below 2 GiB (32-bit buffer offsets).
   if (4 * I * H >= (int64_t(1) << 31) || 4 * Is * H >= (int64_t(1) << 31))
     return MOE_ERR_UNSUPPORTED;
-  // Panel activations: the panel stride 64 N_cap is a 32-bit buffer offset.
+  // Panel activations: the GEMMs address x_perm and h with 32-bit offsets.
   const int64_t N = T * (k < EL ? k : EL);
-  if ((p->layout & MOE_LAYOUT_PANEL_ACTS) && 64 * N >= (int64_t(1) << 31))
+  if ((p->layout & MOE_LAYOUT_PANEL_ACTS) && 2 * N * (H > I ? H : I) > kGemmPanelMaxBytes)
     return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
@@ -53,12 +53,13 @@ bool is_fp8(const moe_problem* p) { return p->dtype == MOE_FP8_E4M3; }
 bool panel_weights(const moe_problem* p) { return p->layout & MOE_LAYOUT_PANEL_WEIGHTS; }
 bool panel_acts(const moe_problem* p) { return p->layout & MOE_LAYOUT_PANEL_ACTS; }
 
-// moe_layer's own x_perm and h: panel layout for bf16 whenever the panel
-// stride fits (the caller's layout bit for activations plays no part).
+// moe_layer's own x_perm and h: panel layout for bf16 whenever the GEMMs can
+// address it (the caller's layout bit for activations plays no part).
 moe_problem layer_internal(const moe_problem* p) {
   moe_problem q = *p;
   q.layout &= ~MOE_LAYOUT_PANEL_ACTS;
-  if (!is_fp8(p) && 64 * n_cap(p) < (int64_t(1) << 31)) q.layout |= MOE_LAYOUT_PANEL_ACTS;
+  const int64_t wide = p->hidden > p->inter ? p->hidden : p->inter;
+  if (!is_fp8(p) && 2 * n_cap(p) * wide <= kGemmPanelMaxBytes) q.layout |= MOE_LAYOUT_PANEL_ACTS;
   return q;
 }
 

@@ -53,6 +53,14 @@ def build(verbose: bool = True) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
+    # A kernel whose host-side stub was not emitted links "successfully" and
+    # only fails when the library is loaded: refuse any undefined symbol of
+    # the library's own namespace.
+    nm = subprocess.run(["nm", "-C", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [l.split(None, 1)[-1] for l in nm.stdout.splitlines() if "moe::" in l]
+    if missing:
+        os.remove(tmp)
+        raise RuntimeError("library has undefined symbols:\n  " + "\n  ".join(missing))
     os.replace(tmp, OUT)
     if verbose:
         print(f"built {OUT}")

@@ -499,6 +499,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pipelined_kernel(const GemmA
 
 template <bool FP8, int MODE>
 hipError_t launch_pipelined(const GemmArgs& g, int64_t max_tiles, hipStream_t s) {
+  static_assert(kStages * kStageBytes + 2 * kBM * 4 <= 160 * 1024, "the ring fits the CU's LDS");
   auto kern = gemm_pipelined_kernel<FP8, MODE>;
   const size_t lds = kStages * kStageBytes;
   static bool attr_set = false;
@@ -548,9 +549,10 @@ constexpr int kBigStageBytes = (kWideBM + kWideBN) * kBigRowBytes;  // 40 KB
 // n-index, wide}: the n-index counts 256-row weight tiles of a full tile or
 // 512-row ranges of a wide one.  An expert with 129..255 rows past its last
 // full tile gets one more full tile instead of a wide one.
-__device__ __forceinline__ void expert_units(int cnt, bool allow_wide, int& full, int& wide) {
-  full = cnt / kBigBM;
-  const int rem = cnt - full * kBigBM;
+__device__ __forceinline__ void expert_units(int cnt, int bm, bool allow_wide, int& full,
+                                             int& wide) {
+  full = cnt / bm;
+  const int rem = cnt - full * bm;
   wide = allow_wide && rem > 0 && rem <= kWideBM;
   if (rem > 0 && !wide) ++full;
 }
@@ -558,7 +560,7 @@ __device__ __forceinline__ void expert_units(int cnt, bool allow_wide, int& full
 // Writes one table; every thread takes units u = tid, tid + 1024, ... and
 // finds the unit's expert by binary search over the experts' first units.
 __device__ __forceinline__ void write_units(const int* s_start, const int* s_off,
-                                            const int* s_full, int E_L, int nt, int total,
+                                            const int* s_full, int E_L, int nt, int total, int bm,
                                             int4* __restrict__ units) {
   for (int u = threadIdx.x; u < total; u += blockDim.x) {
     int lo = 0, hi = E_L - 1;  // last expert whose first unit is <= u
@@ -568,14 +570,14 @@ __device__ __forceinline__ void write_units(const int* s_start, const int* s_off
     }
     const int e = lo, v = u - s_start[e], full = s_full[e];
     if (v < full * nt)
-      units[u] = make_int4(e, s_off[e] + (v % full) * kBigBM, v / full, 0);
+      units[u] = make_int4(e, s_off[e] + (v % full) * bm, v / full, 0);
     else
-      units[u] = make_int4(e, s_off[e] + full * kBigBM, v - full * nt, 1);
+      units[u] = make_int4(e, s_off[e] + full * bm, v - full * nt, 1);
   }
 }
 
 __global__ __launch_bounds__(1024) void unit_schedule_kernel(
-    const int32_t* __restrict__ offsets, int E_L, int nt_a, int nt_b, bool allow_wide,
+    const int32_t* __restrict__ offsets, int E_L, int nt_a, int nt_b, int bm, bool allow_wide,
     int4* __restrict__ units_a, int32_t* __restrict__ n_a, int4* __restrict__ units_b,
     int32_t* __restrict__ n_b) {
   __shared__ int s_off[1024], s_full[1024], s_sa[1024], s_sb[1024];
@@ -586,7 +588,7 @@ __global__ __launch_bounds__(1024) void unit_schedule_kernel(
     cnt = offsets[e + 1] - off;
   }
   int full, wide;
-  expert_units(cnt, allow_wide, full, wide);
+  expert_units(cnt, bm, allow_wide, full, wide);
   const int nw_a = (nt_a + 1) / 2, nw_b = (nt_b + 1) / 2;
   int tot_a, tot_b;
   const int sa = block_exclusive_scan(full * nt_a + wide * nw_a, &tot_a);
@@ -598,8 +600,8 @@ __global__ __launch_bounds__(1024) void unit_schedule_kernel(
     s_sb[e] = sb;
   }
   __syncthreads();
-  write_units(s_sa, s_off, s_full, E_L, nt_a, tot_a, units_a);
-  write_units(s_sb, s_off, s_full, E_L, nt_b, tot_b, units_b);
+  write_units(s_sa, s_off, s_full, E_L, nt_a, tot_a, bm, units_a);
+  write_units(s_sb, s_off, s_full, E_L, nt_b, tot_b, bm, units_b);
   if (e == 0) {
     *n_a = tot_a;
     *n_b = tot_b;
@@ -816,6 +818,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const GemmArgs
 
 template <int MODE>
 hipError_t launch_big(const GemmArgs& g, int64_t max_units, hipStream_t s) {
+  static_assert(kBigStages * kBigStageBytes <= 160 * 1024, "the ring fits the CU's LDS");
   auto kern = gemm_big_kernel<MODE>;
   const size_t lds = kBigStages * kBigStageBytes;
   static bool attr_set = false;
@@ -832,35 +835,54 @@ hipError_t launch_big(const GemmArgs& g, int64_t max_units, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// Large-tile block-FP8 kernel: 256 token rows x 256 weight rows, 4 waves (one
-// per SIMD) as 2 (rows) x 2 (weights), each wave 128 x 128 (4 x 4 MFMA 32x32
-// tiles).  One K step is one 128-wide scale block: 128 bytes of every row
-// through a two-stage LDS ring (65 KB stages: codes plus the step's 256 token
-// scales, all by direct loads), loads one step ahead.
+// Large-tile block-FP8 kernel: 4 waves (one per SIMD) as 2 (token rows) x 2
+// (weight rows) over a BM x 256 tile, each wave WM x 128 (WM/32 x 4 MFMA
+// 32x32 tiles; BM = 2 WM).  One K step is one 128-wide scale block: 128 bytes
+// of every row through an LDS ring (codes plus the step's token scales, all
+// by direct loads).
 //  * Scales: for each 32x32 tile the two MFMAs of the step (K 0..63, 64..127)
-//    run into a fresh accumulator that is then added to the tile's sum times
-//    (weight block scale x token group scale) -- 16 FMAs per two MFMAs,
-//    which the SIMD overlaps with the following tiles' MFMAs.
-//  * A wave's 128 x 128 block reads 512 bytes of fragments per lane and step
-//    from LDS for 32 MFMAs; tokens and weights each cross L2 once per 256 x
-//    256 tile.
+//    run into a fresh accumulator (the MFMA's zero input) that is then added
+//    to the tile's sum times (weight block scale x token group scale).  With
+//    WM = 128 the sums (256 registers per lane) live in AGPRs and each add
+//    moves them through VGPRs; WM = 64 would keep them in VGPRs but moves
+//    twice the operand bytes per FLOP, and measures slower.
 //  * Fused gather: with a_index, token row j is row a_index[j] of the codes
 //    and of the scales.
 // ---------------------------------------------------------------------------
-constexpr int kF8BM = 256, kF8BN = 256, kF8Threads = 256;
+constexpr int kF8BN = 256, kF8Threads = 256;
 constexpr int kF8RowBytes = 128;
-constexpr int kF8ScaleOff = (kF8BM + kF8BN) * kF8RowBytes;     // 64 KB
-constexpr int kF8StageBytes = kF8ScaleOff + kF8BM * 4 + 1024;  // + token scales, padded
-constexpr int kF8Pitch = 272;                                  // bf16 epilogue rows
-constexpr int kF8Lds = 4 * 128 * kF8Pitch;                     // >= 2 stages
-static_assert(2 * kF8StageBytes <= kF8Lds, "two stages fit the epilogue area");
+constexpr int kF8Pitch = 272;  // bf16 epilogue rows
+constexpr int kCuLds = 160 * 1024;  // LDS of a CU: static plus dynamic must fit
 
-template <int MODE>
-__global__ __launch_bounds__(kF8Threads, 1) void gemm_big_fp8_kernel(const GemmArgs g) {
+template <int WM>
+struct F8Tile {
+  static constexpr int BM = 2 * WM;
+  static constexpr int kScaleOff = (BM + kF8BN) * kF8RowBytes;
+  static constexpr int kStageBytes = kScaleOff + BM * 4 + 512;
+  static constexpr int kStatic = 2 * BM * 4;         // row_amax
+  static constexpr int kRoom = kCuLds - kStatic;
+  static constexpr int kStages = kRoom / kStageBytes < 3 ? kRoom / kStageBytes : 3;
+  static constexpr int kEpilogue = 4 * WM * kF8Pitch;
+  // dynamic LDS: the ring, or the bf16 epilogue tile if larger
+  static constexpr int kLds =
+      kStages * kStageBytes > kEpilogue ? kStages * kStageBytes : kEpilogue;
+  static constexpr int kALoads = BM / 8 / 4;          // 8-row groups of A per wave
+  static constexpr int kLoads = kALoads + kF8BN / 8 / 4;
+  static constexpr int kJ = WM / 32;                  // token blocks per wave
+  static_assert(kStages >= 2, "LDS ring");
+  static_assert(kLds + kStatic <= kCuLds, "static plus dynamic LDS fit the CU");
+};
+
+template <int MODE, int WM>
+__device__ __forceinline__ void big_fp8_tile(const GemmArgs& g) {
+  using TT = F8Tile<WM>;
+  constexpr int BM = TT::BM;
+  constexpr int kStages = TT::kStages, kAhead = kStages - 1;
+  constexpr int kLoads = TT::kLoads, kALoads = TT::kALoads, kJ = TT::kJ;
+  constexpr int kDma = kLoads + 1;  // + the token-scale load
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
-  __shared__ float row_amax[2][kF8BM];
+  __shared__ float row_amax[2][BM];
   constexpr bool kSwiglu = MODE != MODE_PLAIN;
-  constexpr int kLoads = (kF8BM + kF8BN) / 8 / 4;  // 16 loads of 8 rows per wave and step
 
   const int total = *g.n_tiles;
   const int per_xcd = ceil_div(total, kXcds);
@@ -875,29 +897,30 @@ __global__ __launch_bounds__(kF8Threads, 1) void gemm_big_fp8_kernel(const GemmA
   const int nk = g.K / 128;
   const int kb_n = g.K / 128;        // scale blocks per row
 
-  const uint8_t* a_base = g.A + (g.a_index ? 0 : static_cast<int64_t>(row0) * ldb);
-  const int64_t a_left = g.a_bytes - (g.a_index ? 0 : static_cast<int64_t>(row0) * ldb);
-  const float* s_base = g.A_scale + (g.a_index ? 0 : static_cast<int64_t>(row0) * kb_n);
-  const int64_t s_left = (g.a_bytes / ldb - (g.a_index ? 0 : row0)) * kb_n * 4;
-  const uint8_t* w_base = g.W + e * g.w_stride;
+  const int64_t a_skip = g.a_index ? 0 : static_cast<int64_t>(row0) * ldb;
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(g.A + a_skip, g.a_bytes - a_skip);
+  const __amdgpu_buffer_rsrc_t rW = make_rsrc(g.W + e * g.w_stride, g.w_stride);
+  const __amdgpu_buffer_rsrc_t rS =
+      make_rsrc(g.A_scale + (g.a_index ? 0 : static_cast<int64_t>(row0) * kb_n),
+                (g.a_bytes / ldb - (g.a_index ? 0 : row0)) * kb_n * 4);
   const int nbase = kSwiglu ? nt * (kF8BN / 2) : nt * kF8BN;
 
   const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
-  // direct loads: wave w moves A groups w*8 .. w*8+7 and W groups
-  // 32 + w*8 .. (8 rows of 128 bytes each), and the token scales of rows
-  // w*64 .. w*64+63.
+  // direct loads: wave w moves A groups w*kALoads.. and W groups
+  // BM/8 + w*8 .. (8 rows of 128 bytes each), and the token scales of 64 rows
+  // ((w % (BM/64)) * 64 ..; with BM = 128 two waves load the same rows).
   int voff[kLoads], ldst[kLoads];
 #pragma unroll
   for (int q = 0; q < kLoads; ++q) {
-    const int grp = q < 8 ? w * 8 + q : 32 + w * 8 + (q - 8);
+    const int grp = q < kALoads ? w * kALoads + q : BM / 8 + w * 8 + (q - kALoads);
     const int rr = grp * 8 + (lane >> 3);
     const int chunk = (lane & 7) ^ ((rr >> 1) & 7);
-    if (rr < kF8BM) {
+    if (rr < BM) {
       const bool valid = row0 + rr < seg_end;
       const int arow = g.a_index && valid ? g.a_index[row0 + rr] : rr;
       voff[q] = valid ? arow * ldb + chunk * 16 : kOobOffset;
     } else {
-      const int r = rr - kF8BM;
+      const int r = rr - BM;
       int grow;
       if (kSwiglu)
         grow = r < kF8BN / 2 ? min(nbase + r, g.Nout - 1)
@@ -908,24 +931,23 @@ __global__ __launch_bounds__(kF8Threads, 1) void gemm_big_fp8_kernel(const GemmA
     }
     ldst[q] = grp * 1024;
   }
+  const int srow = (w % (BM / 64)) * 64;
   int soff;
   {
-    const int rr = w * 64 + lane;
+    const int rr = srow + lane;
     const bool valid = row0 + rr < seg_end;
     const int arow = g.a_index && valid ? g.a_index[row0 + rr] : rr;
     soff = valid ? arow * kb_n * 4 : kOobOffset;
   }
-  const __amdgpu_buffer_rsrc_t rA = make_rsrc(a_base, a_left);
-  const __amdgpu_buffer_rsrc_t rW = make_rsrc(w_base, g.w_stride);
-  const __amdgpu_buffer_rsrc_t rS = make_rsrc(s_base, s_left);
   auto dma = [&](int step, int stage) {
-    uint8_t* base = smem + stage * kF8StageBytes;
+    const int k = min(step, nk - 1);
+    uint8_t* base = smem + stage * TT::kStageBytes;
 #pragma unroll
     for (int q = 0; q < kLoads; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(q < 8 ? rA : rW, (lds_ptr_t)(base + ldst[q]), 16,
-                                               voff[q], step * 128, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_ptr_t)(base + kF8ScaleOff + w * 256), 4,
-                                             soff, step * 4, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(q < kALoads ? rA : rW, (lds_ptr_t)(base + ldst[q]),
+                                               16, voff[q], k * 128, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_ptr_t)(base + TT::kScaleOff + srow * 4), 4,
+                                             soff, k * 4, 0, 0);
   };
 
   // ---- fragments: lane reads 32 bytes (K 32 hi .. 32 hi + 31 of the
@@ -939,13 +961,14 @@ __global__ __launch_bounds__(kF8Threads, 1) void gemm_big_fp8_kernel(const GemmA
     foff[kk][0] = lr * kF8RowBytes + c0 * 16;
     foff[kk][1] = lr * kF8RowBytes + (c0 ^ 1) * 16;
   }
-  int wbase[4], abase[4];
+  int wbase[4], abase[kJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = kSwiglu ? (i < 2 ? 0 : kF8BN / 2) + wn * 64 + (i & 1) * 32 : wn * 128 + i * 32;
-    wbase[i] = kF8BM * kF8RowBytes + row * kF8RowBytes;
-    abase[i] = (wm * 128 + i * 32) * kF8RowBytes;
+    wbase[i] = BM * kF8RowBytes + row * kF8RowBytes;
   }
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) abase[j] = (wm * WM + j * 32) * kF8RowBytes;
   // weight block scales: uniform per wave, scalar loads
   const float* wsc = g.W_scale + e * g.ws_stride;
   const float* swp[2];
@@ -960,11 +983,11 @@ __global__ __launch_bounds__(kF8Threads, 1) void gemm_big_fp8_kernel(const GemmA
     return ((const __attribute__((address_space(4))) float*)(uintptr_t)swp[which])[k];
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][kJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < kJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
@@ -973,33 +996,36 @@ __global__ __launch_bounds__(kF8Threads, 1) void gemm_big_fp8_kernel(const GemmA
     return i32x8{lo[0], lo[1], lo[2], lo[3], h4[0], h4[1], h4[2], h4[3]};
   };
 
-  dma(0, 0);
-  WAIT_VMCNT(0);
+#pragma unroll
+  for (int st = 0; st < kAhead; ++st) dma(st, st);
+  WAIT_VMCNT((kAhead - 1) * kDma);
   __builtin_amdgcn_s_barrier();
 
+  int s_cur = 0;
   for (int kt = 0; kt < nk; ++kt) {
-    const uint8_t* st = smem + (kt & 1) * kF8StageBytes;
-    // the other stage was released by the barrier that ended step kt - 1
-    if (kt + 1 < nk) dma(kt + 1, (kt + 1) & 1);
+    const uint8_t* st = smem + s_cur * TT::kStageBytes;
+    // the stage before this one was released by the barrier that ended
+    // step kt - 1; it takes step kt + kAhead
+    dma(kt + kAhead, s_cur == 0 ? kStages - 1 : s_cur - 1);
     const float sw0 = wscale(0, kt), sw1 = wscale(1, kt);
-    i32x8 fa[2][4], fb[2][4];
+    i32x8 fa[2][4], fb[2][kJ];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < kJ; ++j)
         fb[kk][j] = rd32(st + abase[j] + foff[kk][0], st + abase[j] + foff[kk][1]);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         fa[kk][i] = rd32(st + wbase[i] + foff[kk][0], st + wbase[i] + foff[kk][1]);
-    float sx[4];
+    float sx[kJ];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      sx[j] = *reinterpret_cast<const float*>(st + kF8ScaleOff + (wm * 128 + j * 32 + lr) * 4);
+    for (int j = 0; j < kJ; ++j)
+      sx[j] = *reinterpret_cast<const float*>(st + TT::kScaleOff + (wm * WM + j * 32 + lr) * 4);
     const f32x16 zero = {0};
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < kJ; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         f32x16 tt = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[0][i], fb[0][j], zero, 0, 0,
@@ -1010,20 +1036,24 @@ __global__ __launch_bounds__(kF8Threads, 1) void gemm_big_fp8_kernel(const GemmA
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] += tt[r] * c;
       }
-    // Step boundary: this wave's loads of step kt+1 have landed and its reads
-    // of stage kt are done; the barrier publishes both.
-    WAIT_VMCNT_LDS(0);
+    // Step boundary: step kt+1 has landed once only the later steps' loads
+    // are in flight, and this wave's reads of stage kt are done; the barrier
+    // publishes both.
+    WAIT_VMCNT_LDS((kAhead - 1) * kDma);
     __builtin_amdgcn_s_barrier();
+    s_cur = s_cur + 1 == kStages ? 0 : s_cur + 1;
   }
+  WAIT_VMCNT(0);
+  __builtin_amdgcn_s_barrier();
 
   const int cq = (lane >> 5) * 4;
   if constexpr (MODE == MODE_PLAIN) {
     // bf16 rows through LDS: 256-byte row pieces per 16 lanes (see the
-    // bf16 large-tile kernel); the last barrier of the loop freed the ring.
+    // bf16 large-tile kernel); the barrier above freed the ring.
     uint16_t* C = static_cast<uint16_t*>(g.C);
-    uint8_t* stile = smem + w * 128 * kF8Pitch;
+    uint8_t* stile = smem + w * WM * kF8Pitch;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < kJ; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -1035,10 +1065,10 @@ __global__ __launch_bounds__(kF8Threads, 1) void gemm_big_fp8_kernel(const GemmA
         }
     const int col = nbase + wn * 128 + (lane & 15) * 8;
 #pragma unroll 4
-    for (int it = 0; it < 32; ++it) {
+    for (int it = 0; it < WM / 4; ++it) {
       const int rl = it * 4 + (lane >> 4);
       const uint4 v = *reinterpret_cast<const uint4*>(stile + rl * kF8Pitch + (lane & 15) * 16);
-      const int m = row0 + wm * 128 + rl;
+      const int m = row0 + wm * WM + rl;
       if (m < seg_end && col < g.Nout)
         *reinterpret_cast<uint4*>(C + static_cast<int64_t>(m) * g.Nout + col) = v;
     }
@@ -1049,12 +1079,12 @@ __global__ __launch_bounds__(kF8Threads, 1) void gemm_big_fp8_kernel(const GemmA
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < kJ; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[hb][j][r] = silu_mul(acc[hb][j][r], acc[hb + 2][j][r]);
-    float amax[4];
+    float amax[kJ];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kJ; ++j) {
       float m = 0.0f;
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb)
@@ -1062,14 +1092,14 @@ __global__ __launch_bounds__(kF8Threads, 1) void gemm_big_fp8_kernel(const GemmA
         for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(acc[hb][j][r]));
       m = fmaxf(m, __shfl_xor(m, 32));
       amax[j] = m;
-      if (lane < 32) row_amax[wn][wm * 128 + j * 32 + lr] = m;
+      if (lane < 32) row_amax[wn][wm * WM + j * 32 + lr] = m;
     }
     __syncthreads();
     uint8_t* C = static_cast<uint8_t*>(g.C);
     const int groups = g.Nout / 128;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int lrow = wm * 128 + j * 32 + lr;
+    for (int j = 0; j < kJ; ++j) {
+      const int lrow = wm * WM + j * 32 + lr;
       const float am = fmaxf(amax[j], row_amax[wn ^ 1][lrow]);
       const float sc = am > 0.0f ? am / 448.0f : 1.0f;
       const int m = row0 + lrow;
@@ -1088,45 +1118,65 @@ __global__ __launch_bounds__(kF8Threads, 1) void gemm_big_fp8_kernel(const GemmA
   }
 }
 
+// Rows per wave of the block-FP8 large-tile kernel (its row tile is twice
+// that).  128 (a 256 x 256 tile) against 64 (128 x 256, three stages, the
+// sums in VGPRs): 5.6 ms against 7.0 ms for the DeepSeek-V3 fp8 shard's FFN.
+constexpr int kF8WM = 128;
+constexpr int kF8BM = 2 * kF8WM;
+
+// (A kernel template over MODE only: the tile body takes the geometry.)
+template <int MODE>
+__global__ __launch_bounds__(kF8Threads, 1) void gemm_big_fp8_kernel(const GemmArgs g) {
+  big_fp8_tile<MODE, kF8WM>(g);
+}
+
 template <int MODE>
 hipError_t launch_big_fp8(const GemmArgs& g, int64_t max_units, hipStream_t s) {
   auto kern = gemm_big_fp8_kernel<MODE>;
   static bool attr_set = false;
   if (!attr_set) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kF8Lds) != hipSuccess)
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            F8Tile<kF8WM>::kLds) != hipSuccess)
       (void)hipGetLastError();
     attr_set = true;
   }
   const int64_t blocks = (max_units + kXcds - 1) / kXcds * kXcds + kXcds;
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(kF8Threads), kF8Lds, s, g);
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(kF8Threads),
+                     F8Tile<kF8WM>::kLds, s, g);
   return hipGetLastError();
 }
 
 }  // namespace
 
+// Work tables: the large-tile kernels run from (tile, n-range) unit tables,
+// the pipelined kernel from an m-tile table shared by both GEMMs.
+static bool unit_path(int tile_m, bool fp8) { return fp8 ? tile_m == kF8BM : tile_m == kBigBM; }
+bool gemm_unit_tables(int tile_m, bool fp8) { return unit_path(tile_m, fp8); }
+
 int gemm_tile_m(bool fp8, int64_t rows_per_expert) {
   // Few rows per expert (decode-sized batches): the 256-row tile would spend
   // most of its matrix-core time on padding while the work is weight streaming.
+  if (fp8) return (kF8BM == kBM || rows_per_expert > 2 * kBM) ? kF8BM : kBM;
   return rows_per_expert <= 2 * kBM ? kBM : kBigBM;
 }
 
 int gemm_n_tiles(int tile_m, bool swiglu, int Nout) {
-  const int bn = tile_m == kBigBM ? kBigBN : kBN;
-  return swiglu ? ceil_div(Nout, bn / 2) : ceil_div(Nout, bn);
+  (void)tile_m;  // every kernel's block covers 256 weight rows
+  return swiglu ? ceil_div(Nout, kBN / 2) : ceil_div(Nout, kBN);
 }
 
-int64_t schedule_entries(int64_t n_cap, int E_L, int tile_m, int nt) {
-  if (tile_m == kBigBM) return (n_cap / kBigBM + E_L) * nt;
+int64_t schedule_entries(int64_t n_cap, int E_L, int tile_m, bool fp8, int nt) {
+  if (unit_path(tile_m, fp8)) return (n_cap / tile_m + E_L) * nt;
   return ceil_div<int64_t>(n_cap, tile_m) + E_L;
 }
 
 hipError_t launch_schedule(const int32_t* offsets, int E_L, int tile_m, bool fp8, int nt_up,
                            int nt_dn, int4* tab_up, int32_t* n_up, int4* tab_dn, int32_t* n_dn,
                            hipStream_t s) {
-  if (tile_m == kBigBM)  // the block-FP8 kernel has no wide tiles
+  if (unit_path(tile_m, fp8))  // the block-FP8 kernel has no wide tiles
     hipLaunchKernelGGL(unit_schedule_kernel, dim3(1), dim3(1024), 0, s, offsets, E_L, nt_up, nt_dn,
-                       !fp8, tab_up, n_up, tab_dn, n_dn);
+                       tile_m, !fp8, tab_up, n_up, tab_dn, n_dn);
   else
     hipLaunchKernelGGL(tile_schedule_kernel, dim3(1), dim3(1024), 0, s, offsets, E_L, tile_m,
                        tab_up, n_up);
@@ -1168,14 +1218,14 @@ hipError_t launch_grouped_gemm(const GemmLaunch& L, hipStream_t s) {
   g.c_cs = L.c_panel ? 64 * L.c_rows : 0;
   g.a_index = L.a_index;
   if (!L.fp8) {
-    if (L.tile_m == kBigBM) {
+    if (unit_path(L.tile_m, false)) {
       if (L.swiglu) return launch_big<MODE_SWIGLU>(g, L.max_tiles, s);
       return launch_big<MODE_PLAIN>(g, L.max_tiles, s);
     }
     if (L.swiglu) return launch_pipelined<false, MODE_SWIGLU>(g, L.max_tiles, s);
     return launch_pipelined<false, MODE_PLAIN>(g, L.max_tiles, s);
   }
-  if (L.tile_m == kBigBM) {
+  if (unit_path(L.tile_m, true)) {
     if (!L.swiglu) return launch_big_fp8<MODE_PLAIN>(g, L.max_tiles, s);
     if (!L.C_scale) return hipErrorInvalidValue;  // block-FP8 h only
     return launch_big_fp8<MODE_SWIGLU_FP8OUT>(g, L.max_tiles, s);

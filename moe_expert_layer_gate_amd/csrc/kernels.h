@@ -30,18 +30,22 @@ hipError_t launch_gather_fp8(const void* src, const int32_t* rows, const int32_t
 hipError_t launch_quant_blocks(const void* src, int64_t batch, int64_t rows, int64_t cols,
                                void* codes, float* scales, hipStream_t s);
 
-// Row tile of the grouped GEMM for a problem: 128 (the pipelined kernel, for
-// few rows per expert) or 256 (the large-tile kernels; the bf16 one covers
-// segment remainders of up to 128 rows with 128 x 512 tiles).
+// Row tile of the grouped GEMM for a problem: bf16 128 (the pipelined kernel,
+// for few rows per expert) or 256 (the large-tile kernel, which covers
+// segment remainders of up to 128 rows with 128 x 512 tiles); block-FP8: the
+// row tile of its large-tile kernel.
 int gemm_tile_m(bool fp8, int64_t rows_per_expert);
+// Whether the GEMMs of a problem run from per-GEMM unit tables (large-tile
+// kernels) or from one shared m-tile table (pipelined kernel).
+bool gemm_unit_tables(int tile_m, bool fp8);
 // n-tiles per expert of one GEMM.
 int gemm_n_tiles(int tile_m, bool swiglu, int Nout);
-// Capacity of a GEMM's work table: m-tiles (tile_m 128; the up and down
-// GEMMs share one table) or (tile, n-range) units (tile_m 256; one table per
-// GEMM, nt = gemm_n_tiles of that GEMM).
-int64_t schedule_entries(int64_t n_cap, int E_L, int tile_m, int nt);
-// Builds the work tables on the device from the expert offsets (tile_m 128:
-// only tab_up / n_up are written).
+// Capacity of a GEMM's work table: m-tiles (pipelined kernel; the up and down
+// GEMMs share one table) or (tile, n-range) units (large-tile kernels; one
+// table per GEMM, nt = gemm_n_tiles of that GEMM).
+int64_t schedule_entries(int64_t n_cap, int E_L, int tile_m, bool fp8, int nt);
+// Builds the work tables on the device from the expert offsets (pipelined
+// kernel: only tab_up / n_up are written).
 hipError_t launch_schedule(const int32_t* offsets, int E_L, int tile_m, bool fp8, int nt_up,
                            int nt_dn, int4* tab_up, int32_t* n_up, int4* tab_dn, int32_t* n_dn,
                            hipStream_t s);

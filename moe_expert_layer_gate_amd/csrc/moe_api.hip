@@ -104,8 +104,8 @@ FfnShape ffn_shape(const moe_problem* p) {
   f.tile_m = gemm_tile_m(is_fp8(p), N / p->num_local);
   f.nt_up = gemm_n_tiles(f.tile_m, true, p->inter);
   f.nt_dn = gemm_n_tiles(f.tile_m, false, p->hidden);
-  f.cap_up = schedule_entries(N, p->num_local, f.tile_m, f.nt_up);
-  f.cap_dn = schedule_entries(N, p->num_local, f.tile_m, f.nt_dn);
+  f.cap_up = schedule_entries(N, p->num_local, f.tile_m, is_fp8(p), f.nt_up);
+  f.cap_dn = schedule_entries(N, p->num_local, f.tile_m, is_fp8(p), f.nt_dn);
   return f;
 }
 
@@ -115,7 +115,7 @@ FfnScratch carve_ffn(Carve& c, const moe_problem* p) {
   FfnScratch f{};
   f.tab_up = c.take<int4>(sizeof(int4) * sh.cap_up);
   f.n_up = c.take<int32_t>(sizeof(int32_t));
-  if (sh.tile_m == 128) {
+  if (!gemm_unit_tables(sh.tile_m, is_fp8(p))) {  // one m-tile table for both GEMMs
     f.tab_dn = f.tab_up;
     f.n_dn = f.n_up;
   } else {

@@ -557,6 +557,8 @@ __device__ __forceinline__ void expert_units(int cnt, int bm, bool allow_wide, i
   if (rem > 0 && !wide) ++full;
 }
 
+constexpr int kGroupM = 8;
+
 // Writes one table; every thread takes units u = tid, tid + 1024, ... and
 // finds the unit's expert by binary search over the experts' first units.
 __device__ __forceinline__ void write_units(const int* s_start, const int* s_off,
@@ -569,9 +571,14 @@ __device__ __forceinline__ void write_units(const int* s_start, const int* s_off
       if (s_start[mid] <= u) lo = mid; else hi = mid - 1;
     }
     const int e = lo, v = u - s_start[e], full = s_full[e];
-    if (v < full * nt)
-      units[u] = make_int4(e, s_off[e] + (v % full) * bm, v / full, 0);
-    else
+    if (v < full * nt) {
+      // groups of kGroupM m-tiles, n-tile-major inside a group, so the 32
+      // CUs of an XCD work on about 8 m-tiles x 4 n-tiles of an expert at
+      // a time and each operand slab leaves L2 fewer times
+      const int g = v / (kGroupM * nt), m0 = g * kGroupM;
+      const int gm = min(kGroupM, full - m0), r = v - g * kGroupM * nt;
+      units[u] = make_int4(e, s_off[e] + (m0 + r % gm) * bm, r / gm, 0);
+    } else
       units[u] = make_int4(e, s_off[e] + full * bm, v - full * nt, 1);
   }
 }

@@ -70,6 +70,23 @@ def stored_traffic(workload: str):
     return rec.get("bytes_per_launch")
 
 
+def gemm_rows(counts, fp8: bool, n_cap: int, E_L: int) -> int:
+    """Token rows the GEMMs compute, padding included, under the library's
+    tile choice: 128-row tiles for up to 256 rows per expert on average, else
+    256-row tiles (bf16: a last remainder of 1..128 rows takes a 128-row wide
+    tile)."""
+    rows = 0
+    for c in (int(x) for x in counts):
+        if n_cap // E_L <= 256:
+            rows += -(-c // 128) * 128
+        elif fp8:
+            rows += -(-c // 256) * 256
+        else:
+            rem = c % 256
+            rows += c - rem + (256 if rem > 128 else 128 if rem else 0)
+    return rows
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -170,8 +187,7 @@ def main():
     beta_w = 1 if cfg.fp8 else 2
     active = int((cnt > 0).sum())
     ffn_tflops = flops / (ffn_ms * 1e-3) / 1e12
-    tile_m = 128
-    padded_rows = int(sum(-(-int(c) // tile_m) * tile_m for c in cnt))
+    padded_rows = gemm_rows(cnt, cfg.fp8, p.n_cap, p.E_L)
 
     traffic = stored_traffic(cfg.name)
     # Few rows per expert: the FFN streams weights and is bound by HBM.
@@ -224,7 +240,8 @@ def main():
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "routing": {"local_pairs": n_pairs, "active_experts": active,
                     "rows_per_expert_max": int(cnt.max()), "rows_per_expert_mean": round(float(cnt.mean()), 1),
-                    "padded_rows_at_128": padded_rows},
+                    "gemm_rows_computed": padded_rows,
+                    "padding_frac": round(padded_rows / max(n_pairs, 1) - 1.0, 4)},
         "roofline": roof,
         "cpu_baseline": cpu,
     }

@@ -26,6 +26,10 @@ __device__ __forceinline__ void unpack8(const uint4 v, float* f) {
   }
 }
 
+// KMAX > 0: k <= KMAX, the slot loop is unrolled so that the (at most KMAX)
+// row loads of a chunk are all in flight before the first is added; the sum
+// is still formed in slot order.  KMAX == 0: any k, one slot at a time.
+template <int KMAX>
 __global__ __launch_bounds__(256) void combine_kernel(
     const uint4* __restrict__ y_perm, const int32_t* __restrict__ token_slot_row,
     const float* __restrict__ topk_w, const uint4* __restrict__ shared_out, int T, int k,
@@ -40,18 +44,42 @@ __global__ __launch_bounds__(256) void combine_kernel(
     my_row = token_slot_row[static_cast<int64_t>(t) * k + lane];
     my_w = topk_w[static_cast<int64_t>(t) * k + lane];
   }
+  int rows[KMAX > 0 ? KMAX : 1];
+  float ws[KMAX > 0 ? KMAX : 1];
+  if constexpr (KMAX > 0) {
+#pragma unroll
+    for (int s = 0; s < KMAX; ++s) {
+      rows[s] = s < k ? __shfl(my_row, s) : -1;
+      ws[s] = __shfl(my_w, s);
+    }
+  }
   for (int c = lane; c < chunks; c += kWave) {
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-    for (int s = 0; s < k; ++s) {
-      const int r = __shfl(my_row, s);
-      if (r < 0) continue;  // uniform over the wave
-      const float ws = __shfl(my_w, s);
-      float f[8];
-      unpack8(y_perm[static_cast<int64_t>(r) * chunks + c], f);
+    if constexpr (KMAX > 0) {
+      uint4 v[KMAX];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += ws * f[i];
+      for (int s = 0; s < KMAX; ++s)
+        if (rows[s] >= 0) v[s] = y_perm[static_cast<int64_t>(rows[s]) * chunks + c];
+#pragma unroll
+      for (int s = 0; s < KMAX; ++s) {
+        if (rows[s] < 0) continue;  // uniform over the wave
+        float f[8];
+        unpack8(v[s], f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += ws[s] * f[i];
+      }
+    } else {
+      for (int s = 0; s < k; ++s) {
+        const int r = __shfl(my_row, s);
+        if (r < 0) continue;  // uniform over the wave
+        const float w = __shfl(my_w, s);
+        float f[8];
+        unpack8(y_perm[static_cast<int64_t>(r) * chunks + c], f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += w * f[i];
+      }
     }
     if (shared_out) {
       float f[8];
@@ -72,7 +100,9 @@ __global__ __launch_bounds__(256) void combine_kernel(
 
 hipError_t launch_combine(const void* y_perm, const int32_t* token_slot_row, const float* topk_w,
                           const void* shared_out, int T, int k, int H, void* y, hipStream_t s) {
-  hipLaunchKernelGGL(combine_kernel, dim3(ceil_div(T, 4)), dim3(256), 0, s,
+  auto kern = k <= 2 ? combine_kernel<2> : k <= 4 ? combine_kernel<4> : k <= 8 ? combine_kernel<8>
+                                                                             : combine_kernel<0>;
+  hipLaunchKernelGGL(kern, dim3(ceil_div(T, 4)), dim3(256), 0, s,
                      static_cast<const uint4*>(y_perm), token_slot_row, topk_w,
                      static_cast<const uint4*>(shared_out), T, k, H / 8, static_cast<uint4*>(y));
   return hipGetLastError();

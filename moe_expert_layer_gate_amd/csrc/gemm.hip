@@ -516,6 +516,165 @@ hipError_t launch_pipelined(const GemmArgs& g, int64_t max_tiles, hipStream_t s)
 }
 
 // ---------------------------------------------------------------------------
+// Skinny bf16 kernel for a few rows per expert (decode): 32 token rows x 256
+// weight rows per block, 4 waves each holding 32 x 64 (two MFMA 32x32 tiles;
+// SwiGLU: the gate and up rows of the same 32 h columns).  The work is weight
+// streaming, so the LDS goes to depth instead of token rows: four 36 KB
+// stages of 128-byte K steps, loads three steps ahead (96 KB of weights in
+// flight per CU).  Same addressing, gather and output layouts as the other
+// kernels; rows past the segment load nothing.
+// ---------------------------------------------------------------------------
+constexpr int kSkBM = 32, kSkBN = 256, kSkThreads = 256;
+constexpr int kSkStages = 4;
+constexpr int kSkStageBytes = (kSkBM + kSkBN) * kRowBytes;  // 36 KB
+constexpr int kSkLoads = (kSkBM + kSkBN) / 8 / 4;            // 1 A + 8 W per wave
+
+template <int MODE>
+__global__ __launch_bounds__(kSkThreads, 1) void gemm_skinny_kernel(const GemmArgs g) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  constexpr bool kSwiglu = MODE != MODE_PLAIN;
+  const int total = *g.n_tiles * g.nt_n;
+  const int per_xcd = ceil_div(total, kXcds);
+  const int slot = blockIdx.x / kXcds;
+  if (slot >= per_xcd) return;
+  const int t = (blockIdx.x % kXcds) * per_xcd + slot;
+  if (t >= total) return;
+  const int4 inf = g.info[t / g.nt_n];
+  const int e = inf.x, u = t - inf.y * g.nt_n;
+  const int nt = u / inf.z, mt = u % inf.z;
+  const int seg_end = g.offsets[e + 1];
+  const int row0 = g.offsets[e] + mt * kSkBM;
+  const int ldb = 2 * g.K;
+  const int nk = ldb / kRowBytes;
+  const int64_t a_skip = g.a_index ? 0 : static_cast<int64_t>(row0) * g.a_rs;
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(g.A + a_skip, g.a_bytes - a_skip);
+  const __amdgpu_buffer_rsrc_t rW = make_rsrc(g.W + e * g.w_stride, g.w_stride);
+  const int nbase = kSwiglu ? nt * (kSkBN / 2) : nt * kSkBN;
+
+  const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
+  // direct loads: wave w moves A group w (8 of the 32 rows) and W groups
+  // 4 + 8w .. 4 + 8w + 7
+  int voff[kSkLoads], ldst[kSkLoads];
+#pragma unroll
+  for (int q = 0; q < kSkLoads; ++q) {
+    const int grp = q == 0 ? w : kSkBM / 8 + w * 8 + (q - 1);
+    const int rr = grp * 8 + (lane >> 3);
+    const int chunk = (lane & 7) ^ ((rr >> 1) & 7);
+    if (rr < kSkBM) {
+      const bool valid = row0 + rr < seg_end;
+      const int arow = g.a_index && valid ? g.a_index[row0 + rr] : rr;
+      voff[q] = valid ? arow * g.a_rs + (chunk >> 2) * g.a_cs + (chunk & 3) * 16 : kOobOffset;
+    } else {
+      const int r = rr - kSkBM;
+      int grow;
+      if (kSwiglu)
+        grow = r < kSkBN / 2 ? min(nbase + r, g.Nout - 1)
+                             : g.Nout + min(nbase + (r - kSkBN / 2), g.Nout - 1);
+      else
+        grow = min(nbase + r, g.NW - 1);
+      voff[q] = grow * g.w_rs + (chunk >> 2) * g.w_cs + (chunk & 3) * 16;
+    }
+    ldst[q] = grp * 1024;
+  }
+  auto dma = [&](int step, int stage) {
+    const int k = min(step, nk - 1);  // step k starts at 64-byte K piece 2k
+    uint8_t* base = smem + stage * kSkStageBytes;
+#pragma unroll
+    for (int q = 0; q < kSkLoads; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(q == 0 ? rA : rW, (lds_ptr_t)(base + ldst[q]), 16,
+                                               voff[q], 2 * k * (q == 0 ? g.a_cs : g.w_cs), 0, 0);
+  };
+
+  const int lr = lane & 31, hi = lane >> 5, sl = (lr >> 1) & 7;
+  int foff[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) foff[kk] = lr * kRowBytes + (((2 * kk) | hi) ^ sl) * 16;
+  int wbase[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    wbase[i] = (kSkBM + (kSwiglu ? i * (kSkBN / 2) + w * 32 : w * 64 + i * 32)) * kRowBytes;
+
+  f32x16 acc[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.0f;
+
+#pragma unroll
+  for (int st = 0; st < kSkStages - 1; ++st) dma(st, st);
+  WAIT_VMCNT((kSkStages - 2) * kSkLoads);
+  __builtin_amdgcn_s_barrier();
+
+  int s_cur = 0;
+  for (int kt = 0; kt < nk; ++kt) {
+    const uint8_t* st = smem + s_cur * kSkStageBytes;
+    dma(kt + kSkStages - 1, s_cur == 0 ? kSkStages - 1 : s_cur - 1);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const bf16x8 fb = *reinterpret_cast<const bf16x8*>(st + foff[kk]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const bf16x8 fa = *reinterpret_cast<const bf16x8*>(st + wbase[i] + foff[kk]);
+        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb, acc[i], 0, 0, 0);
+      }
+    }
+    WAIT_VMCNT_LDS((kSkStages - 2) * kSkLoads);
+    __builtin_amdgcn_s_barrier();
+    s_cur = s_cur + 1 == kSkStages ? 0 : s_cur + 1;
+  }
+  WAIT_VMCNT(0);
+
+  // accumulator element q*4 + r: weight row q*8 + (lane/32)*4 + r of the
+  // block, token row lane % 32
+  const int cq = (lane >> 5) * 4;
+  const int m = row0 + lr;
+  if (m >= seg_end) return;
+  uint8_t* C8 = static_cast<uint8_t*>(g.C);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if constexpr (MODE == MODE_PLAIN) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int col = nbase + w * 64 + i * 32 + q * 8 + cq;
+        if (col >= g.Nout) continue;
+        uint2 o;
+        o.x = pack_bf16x2(acc[i][q * 4 + 0], acc[i][q * 4 + 1]);
+        o.y = pack_bf16x2(acc[i][q * 4 + 2], acc[i][q * 4 + 3]);
+        *reinterpret_cast<uint2*>(C8 + (static_cast<int64_t>(m) * g.Nout + col) * 2) = o;
+      }
+    } else {
+      const int col = nbase + w * 32 + q * 8 + cq;
+      if (col >= g.Nout) continue;
+      float hv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) hv[r] = silu_mul(acc[0][q * 4 + r], acc[1][q * 4 + r]);
+      uint2 o;
+      o.x = pack_bf16x2(hv[0], hv[1]);
+      o.y = pack_bf16x2(hv[2], hv[3]);
+      *reinterpret_cast<uint2*>(C8 + out_offset(g, m, col)) = o;
+    }
+  }
+}
+
+template <int MODE>
+hipError_t launch_skinny(const GemmArgs& g, int64_t max_tiles, hipStream_t s) {
+  static_assert(kSkStages * kSkStageBytes <= 160 * 1024, "the ring fits the CU's LDS");
+  auto kern = gemm_skinny_kernel<MODE>;
+  const size_t lds = kSkStages * kSkStageBytes;
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(lds)) != hipSuccess)
+      (void)hipGetLastError();
+    attr_set = true;
+  }
+  const int64_t blocks = (max_tiles * g.nt_n + kXcds - 1) / kXcds * kXcds + kXcds;
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(kSkThreads), lds, s, g);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Large-tile bf16 kernel, 8 waves (two per SIMD), each wave 64 x 128 output
 // elements (2 x 4 MFMA 32x32 tiles).  Two block shapes share the code:
 //   full tile: 256 token rows x 256 weight rows, waves 4 (rows) x 2 (weights);
@@ -1165,6 +1324,7 @@ int gemm_tile_m(bool fp8, int64_t rows_per_expert) {
   // Few rows per expert (decode-sized batches): the 256-row tile would spend
   // most of its matrix-core time on padding while the work is weight streaming.
   if (fp8) return (kF8BM == kBM || rows_per_expert > 2 * kBM) ? kF8BM : kBM;
+  if (rows_per_expert <= kSkBM) return kSkBM;
   return rows_per_expert <= 2 * kBM ? kBM : kBigBM;
 }
 
@@ -1228,6 +1388,10 @@ hipError_t launch_grouped_gemm(const GemmLaunch& L, hipStream_t s) {
     if (unit_path(L.tile_m, false)) {
       if (L.swiglu) return launch_big<MODE_SWIGLU>(g, L.max_tiles, s);
       return launch_big<MODE_PLAIN>(g, L.max_tiles, s);
+    }
+    if (L.tile_m == kSkBM) {
+      if (L.swiglu) return launch_skinny<MODE_SWIGLU>(g, L.max_tiles, s);
+      return launch_skinny<MODE_PLAIN>(g, L.max_tiles, s);
     }
     if (L.swiglu) return launch_pipelined<false, MODE_SWIGLU>(g, L.max_tiles, s);
     return launch_pipelined<false, MODE_PLAIN>(g, L.max_tiles, s);

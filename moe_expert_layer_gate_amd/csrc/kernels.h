@@ -30,10 +30,11 @@ hipError_t launch_gather_fp8(const void* src, const int32_t* rows, const int32_t
 hipError_t launch_quant_blocks(const void* src, int64_t batch, int64_t rows, int64_t cols,
                                void* codes, float* scales, hipStream_t s);
 
-// Row tile of the grouped GEMM for a problem: bf16 128 (the pipelined kernel,
-// for few rows per expert) or 256 (the large-tile kernel, which covers
-// segment remainders of up to 128 rows with 128 x 512 tiles); block-FP8: the
-// row tile of its large-tile kernel.
+// Row tile of the grouped GEMM for a problem, from the mean rows per expert:
+// bf16 32 (the skinny kernel, up to 32 rows: decode), 128 (the pipelined
+// kernel, up to 256) or 256 (the large-tile kernel, which covers segment
+// remainders of up to 128 rows with 128 x 512 tiles); block-FP8 128
+// (pipelined, up to 256) or the row tile of its large-tile kernel.
 int gemm_tile_m(bool fp8, int64_t rows_per_expert);
 // Whether the GEMMs of a problem run from per-GEMM unit tables (large-tile
 // kernels) or from one shared m-tile table (pipelined kernel).

@@ -108,6 +108,11 @@ SMALL = {
     "big_tile_shard": (small_cfg(T=1500, H=512, E=16, E_L=4, e_lo=12, k=4, I=640,
                                  logits="gumbel_zipf"), 11),
     "bf16_shared": (small_cfg(T=200, H=256, E=8, E_L=4, e_lo=2, k=2, I=256, I_s=384), 12),
+    # at most 32 rows per expert on average (the skinny decode kernel); Zipf
+    # routing gives the hot experts several 32-row tiles
+    "skinny_ragged": (small_cfg(T=60, H=384, E=16, E_L=8, e_lo=0, k=4, I=384,
+                                logits="gumbel_zipf"), 15),
+    "skinny_shard": (small_cfg(T=33, H=256, E=32, E_L=8, e_lo=8, k=8, I=640), 16),
 }
 SMALL_FP8 = {
     "fp8_small": (small_cfg(T=200, H=512, E=16, E_L=8, e_lo=0, k=4, I=256, fp8=True), 8),

@@ -2,12 +2,16 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-One step is one moe_layer call -- route, dispatch, grouped SwiGLU FFN (and
+One step is one pass of the layer -- route, dispatch, grouped SwiGLU FFN (and
 shared expert), combine -- over one batch of the workload, with inputs
-already resident in HBM.  Prints ONE JSON line: MoE-layer tokens/s as
-`value`, the grouped FFN's TFLOP/s against the MFMA peak (or, for the
-decode workload, its bytes/s against HBM) as `roofline`, and the CPU
-oracle on a bounded sample of the same workload as `cpu_baseline`.
+already resident in HBM, issued as moe_layer's kernels one library call per
+stage so that the grouped FFN's launches in the timed region are bracketed by
+HIP events on their stream (the line also reports the one-call moe_layer's
+throughput and that it gives the same output bits).  Prints ONE JSON line:
+MoE-layer tokens/s as `value`, the grouped FFN's TFLOP/s against the MFMA
+peak (or, for the decode workload, its bytes/s against HBM) as `roofline`,
+and the CPU oracle on a bounded sample of the same workload as
+`cpu_baseline`.
 """
 from __future__ import annotations
 
@@ -33,7 +37,6 @@ def parse():
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--cpu-sample-tokens", type=int, default=None,
                     help="tokens of the workload the CPU oracle runs on (0 = skip)")
-    ap.add_argument("--ffn-reps", type=int, default=None)
     ap.add_argument("--layout", choices=("panel", "rows"), default="panel",
                     help="bf16 storage: panel = weights packed once at load time and panel "
                          "activations in the staged calls (moe_layer always keeps its own "
@@ -72,12 +75,14 @@ def stored_traffic(workload: str):
 
 def gemm_rows(counts, fp8: bool, n_cap: int, E_L: int) -> int:
     """Token rows the GEMMs compute, padding included, under the library's
-    tile choice: 128-row tiles for up to 256 rows per expert on average, else
-    256-row tiles (bf16: a last remainder of 1..128 rows takes a 128-row wide
-    tile)."""
+    tile choice: bf16 32-row tiles for up to 32 rows per expert on average;
+    128-row tiles up to 256; else 256-row tiles (bf16: a last remainder of
+    1..128 rows takes a 128-row wide tile)."""
     rows = 0
     for c in (int(x) for x in counts):
-        if n_cap // E_L <= 256:
+        if not fp8 and n_cap // E_L <= 32:
+            rows += -(-c // 32) * 32
+        elif n_cap // E_L <= 256:
             rows += -(-c // 128) * 128
         elif fp8:
             rows += -(-c // 256) * 256
@@ -108,81 +113,99 @@ def main():
     d = synth.make_inputs(cfg, seed)
     panel = args.layout == "panel" and not cfg.fp8
     dev = dv.upload(d, cfg.fp8, panel=panel)   # load-time packing, outside any timing
-    p = ml.Problem.from_config(cfg, layout=ml.LAYOUT_PANEL_WEIGHTS if panel else 0)
-    # the staged calls run with the layouts moe_layer uses inside
-    p_st = ml.Problem.from_config(
+    # Layouts of moe_layer's own path: panel weights as loaded, panel h.
+    p = ml.Problem.from_config(
         cfg, layout=(ml.LAYOUT_PANEL_WEIGHTS | ml.LAYOUT_PANEL_ACTS) if panel else 0)
+    p_layer = ml.Problem.from_config(cfg, layout=ml.LAYOUT_PANEL_WEIGHTS if panel else 0)
     W = dv.weights_of(dev, cfg.fp8)
-    ws = dv.workspace(p)
-    y = torch.empty((p.T, p.H), dtype=torch.bfloat16, device="cuda")
     stream = torch.cuda.current_stream()
+    T, k, H, N = p.T, p.k, p.H, p.n_cap
+    i32 = dict(dtype=torch.int32, device="cuda")
+    ids = torch.empty((T, k), **i32)
+    tw = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    counts, offsets = torch.empty(p.E_L, **i32), torch.empty(p.E_L + 1, **i32)
+    rt, rs, tsr = torch.empty(N, **i32), torch.empty(N, **i32), torch.empty((T, k), **i32)
+    yp = torch.empty((N, H), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    ws_d = dv.workspace(p, ml.STAGE_DISPATCH)
+    ws_f = dv.workspace(p, ml.STAGE_FFN)
+    if cfg.fp8:
+        xp = torch.empty((N, H), dtype=torch.uint8, device="cuda")
+        xs = torch.empty((N, H // 128), dtype=torch.float32, device="cuda")
+        if p.I_s:
+            q = ml.Problem(T=T, H=H, E=1, k=1, e_lo=0, E_L=1, I=p.I_s, fp8=True)
+            off2 = torch.tensor([0, T], **i32)
+            sw = ml.weights_struct(dev["ws13_q"], dev["ws2_q"], None, None, dev["ws13_s"],
+                                   dev["ws2_s"])
+            sx = torch.empty((T, H), dtype=torch.uint8, device="cuda")
+            sxs = torch.empty((T, H // 128), dtype=torch.float32, device="cuda")
+            shared = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+            ws_s = dv.workspace(q, ml.STAGE_FFN)
 
-    def step():
-        ml.moe_layer(p, dev["logits"], dev["x"], W, y, ws, stream)
+    # One step: moe_layer's kernels, one library call per stage, so that the
+    # grouped FFN's launches inside the timed region can be bracketed with
+    # HIP events on the stream they run on.  bf16: route, index-only
+    # dispatch, the FFN gathering its rows from x, combine.  fp8: route,
+    # dispatch with quantisation, FFN, shared expert (quantise x, dense FFN),
+    # combine.
+    def step(ev=None):
+        rec = (lambda i: ev[i].record(stream)) if ev else (lambda i: None)
+        rec(0)
+        ml.moe_route(p, dev["logits"], ids, tw, stream)
+        rec(1)
+        if not cfg.fp8:
+            ml.moe_dispatch(p, dev["x"], ids, counts, offsets, rt, rs, tsr, None, None, ws_d,
+                            stream)
+            rec(2)
+            ml.moe_grouped_ffn_gather(p, dev["x"], rt, offsets, W, None, yp, ws_f, stream)
+            rec(3)
+            sh = None
+        else:
+            ml.moe_dispatch(p, dev["x"], ids, counts, offsets, rt, rs, tsr, xp, xs, ws_d, stream)
+            rec(2)
+            ml.moe_grouped_ffn(p, xp, xs, offsets, W, None, None, yp, ws_f, stream)
+            sh = None
+            if p.I_s:
+                ml.moe_quantize_fp8(dev["x"], 1, T, H, 1, sx, sxs, stream)
+                ml.moe_grouped_ffn(q, sx, sxs, off2, sw, None, None, shared, ws_s, stream)
+                sh = shared
+            rec(3)
+        ml.moe_combine(p, yp, tsr, tw, sh, y, stream)
+        rec(4)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        step(evs[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
-    tokens_per_s = p.T * args.steps / elapsed
+    tokens_per_s = T * args.steps / elapsed
+    names = ("route", "dispatch", "grouped_ffn", "combine")
+    per = {n: [e[i].elapsed_time(e[i + 1]) for e in evs] for i, n in enumerate(names)}
+    stage_ms = {n: float(np.median(v)) for n, v in per.items()}
+    ffn_ms = float(np.mean(per["grouped_ffn"]))   # the FFN launches of the timed region
 
-    # ---- staged calls: per-stage times and the grouped FFN on its own ----
-    i32 = dict(dtype=torch.int32, device="cuda")
-    N = p.n_cap
-    ids = torch.empty((p.T, p.k), **i32)
-    tw = torch.empty((p.T, p.k), dtype=torch.float32, device="cuda")
-    counts, offsets = torch.empty(p.E_L, **i32), torch.empty(p.E_L + 1, **i32)
-    rt, rs, tsr = torch.empty(N, **i32), torch.empty(N, **i32), torch.empty((p.T, p.k), **i32)
-    if cfg.fp8:
-        xp = torch.empty((N, p.H), dtype=torch.uint8, device="cuda")
-        xs = torch.empty((N, p.H // 128), dtype=torch.float32, device="cuda")
-    else:
-        xp = torch.empty((N, p.H), dtype=torch.bfloat16, device="cuda")
-        xs = None
-    yp = torch.empty((N, p.H), dtype=torch.bfloat16, device="cuda")
-    ws_d = dv.workspace(p, ml.STAGE_DISPATCH)
-    ws_f = dv.workspace(p, ml.STAGE_FFN)
-
-    def ev():
-        return torch.cuda.Event(enable_timing=True)
-
-    stages = {"route": [], "dispatch": [], "grouped_ffn": [], "combine": []}
-    for it in range(max(3, min(args.steps, 10))):
-        e = [ev() for _ in range(5)]
-        e[0].record(stream)
-        ml.moe_route(p_st, dev["logits"], ids, tw, stream)
-        e[1].record(stream)
-        ml.moe_dispatch(p_st, dev["x"], ids, counts, offsets, rt, rs, tsr, xp, xs, ws_d, stream)
-        e[2].record(stream)
-        ml.moe_grouped_ffn(p_st, xp, xs, offsets, W, None, None, yp, ws_f, stream)
-        e[3].record(stream)
-        ml.moe_combine(p_st, yp, tsr, tw, None, y, stream)
-        e[4].record(stream)
-        torch.cuda.synchronize()
-        if it == 0:
-            continue  # first pass warms the staged buffers
-        for name, a, b in zip(stages, e[:-1], e[1:]):
-            stages[name].append(a.elapsed_time(b))
-    stage_ms = {k: float(np.median(v)) for k, v in stages.items()}
-
-    # The grouped FFN timed launch by launch on the stream it runs on.
-    reps = args.ffn_reps or max(args.steps, 20)
-    starts, ends = [ev() for _ in range(reps)], [ev() for _ in range(reps)]
-    for i in range(reps):
-        starts[i].record(stream)
-        ml.moe_grouped_ffn(p_st, xp, xs, offsets, W, None, None, yp, ws_f, stream)
-        ends[i].record(stream)
+    # The same work through the one-call moe_layer: same output bits, and its
+    # own throughput for reference.
+    y_steps = y.clone()
+    ws_l = dv.workspace(p_layer)
+    y_l = torch.empty_like(y)
+    ml.moe_layer(p_layer, dev["logits"], dev["x"], W, y_l, ws_l, stream)
     torch.cuda.synchronize()
-    ffn_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(starts, ends)]))
+    same = bool(torch.equal(y_l.view(torch.int16), y_steps.view(torch.int16)))
+    t1 = time.perf_counter()
+    for _ in range(args.steps):
+        ml.moe_layer(p_layer, dev["logits"], dev["x"], W, y_l, ws_l, stream)
+    torch.cuda.synchronize()
+    layer_tps = T * args.steps / (time.perf_counter() - t1)
 
     n_pairs = int(offsets[-1].item())
     cnt = counts.cpu().numpy()
-    flops = 6.0 * p.H * p.I * n_pairs
+    flops = 6.0 * p.H * p.I * n_pairs + 6.0 * p.H * p.I_s * p.T
     dtype = "fp8" if cfg.fp8 else "bf16"
     beta_w = 1 if cfg.fp8 else 2
     active = int((cnt > 0).sum())
@@ -190,24 +213,26 @@ def main():
     padded_rows = gemm_rows(cnt, cfg.fp8, p.n_cap, p.E_L)
 
     traffic = stored_traffic(cfg.name)
+    kernel = ("grouped FFN: work table + up GEMM/SwiGLU + down GEMM"
+              + (" (+ shared expert: x quantisation and its FFN)" if p.I_s else ""))
     # Few rows per expert: the FFN streams weights and is bound by HBM.
     decode = n_pairs < 64 * max(active, 1)
     if decode:
         # weight streaming: every active expert's W13 and W2 once, plus the
-        # permuted activations in and out of both GEMMs
+        # token rows in and out of both GEMMs
         bytes_ = (active * 3 * p.H * p.I * beta_w
                   + n_pairs * (p.H * beta_w + 2 * p.I * beta_w + 2 * p.H))
         achieved = bytes_ / (ffn_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-                "kernel": "moe_grouped_ffn (tile schedule + up GEMM/SwiGLU + down GEMM)",
-                "work_per_launch": {"bytes": bytes_}, "avg_launch_ms": round(ffn_ms, 4)}
+                "kernel": kernel, "work_per_launch": {"bytes": bytes_},
+                "avg_launch_ms": round(ffn_ms, 4)}
     else:
         peak = PEAK_TFLOPS[dtype]
         roof = {"bound": "mfma", "achieved": round(ffn_tflops, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(ffn_tflops / peak, 4), "traffic": traffic,
-                "kernel": "moe_grouped_ffn (tile schedule + up GEMM/SwiGLU + down GEMM)",
-                "work_per_launch": {"flops": flops}, "avg_launch_ms": round(ffn_ms, 4)}
+                "kernel": kernel, "work_per_launch": {"flops": flops},
+                "avg_launch_ms": round(ffn_ms, 4)}
 
     # ---- CPU baseline: the oracle on a bounded sample of the same workload ----
     cpu = None
@@ -237,7 +262,8 @@ def main():
                    "layout": "panel" if panel else "rows"},
         "grouped_ffn_tflops": round(ffn_tflops, 2),
         "grouped_ffn_frac_of_peak": round(ffn_tflops / PEAK_TFLOPS[dtype], 4),
-        "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "stage_ms": {k2: round(v, 4) for k2, v in stage_ms.items()},
+        "moe_layer_call": {"tokens_per_s": round(layer_tps, 1), "same_output_bits": same},
         "routing": {"local_pairs": n_pairs, "active_experts": active,
                     "rows_per_expert_max": int(cnt.max()), "rows_per_expert_mean": round(float(cnt.mean()), 1),
                     "gemm_rows_computed": padded_rows,

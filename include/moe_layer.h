@@ -153,7 +153,9 @@ moe_status moe_route(const moe_problem* p, const float* logits,
  *              128-element group, amax/448 (1 for an all-zero group); code =
  *              round-to-nearest-even(v / scale) saturated to +-448.
  * Rows are ordered by local expert, then by token.  Bit-exact and
- * deterministic.  Workspace: moe_workspace_bytes(p, MOE_STAGE_DISPATCH).   */
+ * deterministic.  x_perm == NULL builds the index only (x_perm_scale is then
+ * ignored; see moe_grouped_ffn_gather).
+ * Workspace: moe_workspace_bytes(p, MOE_STAGE_DISPATCH).                   */
 moe_status moe_dispatch(const moe_problem* p, const void* x,
                         const int32_t* topk_ids, int32_t* counts,
                         int32_t* offsets, int32_t* row_token,
@@ -183,6 +185,22 @@ moe_status moe_grouped_ffn(const moe_problem* p, const void* x_perm,
                            const moe_weights* w, void* h, float* h_scale,
                            void* y_perm, void* ws, size_t ws_bytes,
                            void* stream);
+
+/* The grouped FFN reading its rows straight from the layer input: row j of
+ * the permutation is x[row_token[j]] (bf16 only; the page passages are those
+ * of moe_grouped_ffn).  Together with moe_dispatch(..., x_perm = NULL, ...)
+ * this is the bf16 path of moe_layer, kernel for kernel: the permuted
+ * activations are never written.
+ *   x [T, H] bf16 row major, row_token [N_cap] (from moe_dispatch), offsets,
+ *   w, h (optional, as in moe_grouped_ffn, layout per MOE_LAYOUT_PANEL_ACTS),
+ *   y_perm [N_cap, H] bf16 (output).
+ * MOE_ERR_UNSUPPORTED for MOE_FP8_E4M3 and for x of 2 GiB or more.
+ * Workspace: moe_workspace_bytes(p, MOE_STAGE_FFN).                        */
+moe_status moe_grouped_ffn_gather(const moe_problem* p, const void* x,
+                                  const int32_t* row_token,
+                                  const int32_t* offsets, const moe_weights* w,
+                                  void* h, void* y_perm, void* ws,
+                                  size_t ws_bytes, void* stream);
 
 /* Combine.  Page "CascadeEP ...", Appendix C, "Output return and combine"
  * (each routed contribution weighted by its routing coefficient exactly once,

@@ -355,10 +355,14 @@ moe_status moe_dispatch(const moe_problem* p, const void* x, const int32_t* topk
                         size_t ws_bytes, void* stream) {
   moe_status st = check_problem(p);
   if (st != MOE_OK) return st;
-  const void* ptrs[] = {x, topk_ids, counts, offsets, row_token, row_slot, token_slot_row, x_perm};
+  const void* ptrs[] = {x, topk_ids, counts, offsets, row_token, row_slot, token_slot_row};
   for (const void* q : ptrs)
     if (!q || !aligned16(q)) return MOE_ERR_INVALID_ARG;
-  if (is_fp8(p) && (!x_perm_scale || !aligned16(x_perm_scale))) return MOE_ERR_INVALID_ARG;
+  // x_perm == NULL: index only (the rows are gathered later, e.g. by
+  // moe_grouped_ffn_gather)
+  if (x_perm && !aligned16(x_perm)) return MOE_ERR_INVALID_ARG;
+  if (x_perm && is_fp8(p) && (!x_perm_scale || !aligned16(x_perm_scale)))
+    return MOE_ERR_INVALID_ARG;
   if (!ws || ws_bytes < moe_workspace_bytes(p, MOE_STAGE_DISPATCH)) return MOE_ERR_WORKSPACE;
   if (p->num_tokens == 0) return MOE_OK;
   return run_dispatch(p, x, topk_ids, counts, offsets, row_token, row_slot, token_slot_row, x_perm,
@@ -383,6 +387,25 @@ moe_status moe_grouped_ffn(const moe_problem* p, const void* x_perm, const float
   const FfnScratch f = carve_ffn(c, p);
   const FfnSource src{x_perm, x_perm_scale, false, nullptr, 0};
   return run_ffn(p, src, offsets, w, h, h_scale, y_perm, f, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_grouped_ffn_gather(const moe_problem* p, const void* x, const int32_t* row_token,
+                                  const int32_t* offsets, const moe_weights* w, void* h,
+                                  void* y_perm, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (is_fp8(p) || !can_fuse_gather(p)) return MOE_ERR_UNSUPPORTED;
+  const void* ptrs[] = {x, row_token, offsets, y_perm};
+  for (const void* q : ptrs)
+    if (!q || !aligned16(q)) return MOE_ERR_INVALID_ARG;
+  if (!weights_ok(p, w, false)) return MOE_ERR_INVALID_ARG;
+  if (h && !aligned16(h)) return MOE_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < moe_workspace_bytes(p, MOE_STAGE_FFN)) return MOE_ERR_WORKSPACE;
+  if (p->num_tokens == 0) return MOE_OK;
+  Carve c(align_ws(ws));
+  const FfnScratch f = carve_ffn(c, p);
+  const FfnSource src{x, nullptr, true, row_token, p->num_tokens};
+  return run_ffn(p, src, offsets, w, h, nullptr, y_perm, f, static_cast<hipStream_t>(stream));
 }
 
 moe_status moe_combine(const moe_problem* p, const void* y_perm, const int32_t* token_slot_row,

@@ -26,7 +26,8 @@ def declared_functions():
 
 
 def test_header_declares_the_expected_calls():
-    assert {"moe_route", "moe_dispatch", "moe_grouped_ffn", "moe_combine", "moe_layer",
+    assert {"moe_route", "moe_dispatch", "moe_grouped_ffn", "moe_grouped_ffn_gather",
+            "moe_combine", "moe_layer",
             "moe_quantize_fp8", "moe_pack_panel", "moe_workspace_bytes", "moe_status_str",
             "moe_abi_version"} <= declared_functions()
 
@@ -151,3 +152,31 @@ def test_pack_panel_argument_checks():
     assert L.moe_pack_panel(256, 1 << 20, 1 << 20, 64, 1 << 40, None) == ml.MOE_ERR_INVALID_ARG
     assert L.moe_pack_panel(256, 0, 4, 64, 1 << 20, None) == ml.MOE_OK
     assert L.moe_pack_panel(256, 3, 0, 64, 1 << 20, None) == ml.MOE_OK
+
+
+def test_gather_ffn_argument_checks():
+    L = ml.lib()
+    p = ml.Problem(T=16, H=256, E=8, k=2, e_lo=0, E_L=8, I=256).c()
+    w = ml.moe_weights(256, 256, None, None, None, None, None, None)
+    n = ml.workspace_bytes(ml.Problem(T=16, H=256, E=8, k=2, e_lo=0, E_L=8, I=256), ml.STAGE_FFN)
+    ok_args = [256, 256, 256, ctypes.byref(w), None, 256, 256, n, None]
+    # fp8 is not supported by the gathering FFN
+    pf = ml.Problem(T=16, H=256, E=8, k=2, e_lo=0, E_L=8, I=256, fp8=True).c()
+    assert L.moe_grouped_ffn_gather(ctypes.byref(pf), *ok_args) == ml.MOE_ERR_UNSUPPORTED
+    for i in (0, 1, 2, 5):      # x, row_token, offsets, y_perm
+        bad = list(ok_args)
+        bad[i] = None
+        assert L.moe_grouped_ffn_gather(ctypes.byref(p), *bad) == ml.MOE_ERR_INVALID_ARG
+    bad = list(ok_args)
+    bad[7] = 16                 # workspace too small
+    assert L.moe_grouped_ffn_gather(ctypes.byref(p), *bad) == ml.MOE_ERR_WORKSPACE
+    # T = 0: nothing to do
+    p0 = ml.Problem(T=0, H=256, E=8, k=2, e_lo=0, E_L=8, I=256).c()
+    assert L.moe_grouped_ffn_gather(ctypes.byref(p0), *ok_args) == ml.MOE_OK
+    # index-only dispatch (x_perm = NULL) still checks the other pointers
+    pd = ml.Problem(T=16, H=256, E=8, k=2, e_lo=0, E_L=8, I=256)
+    nd = ml.workspace_bytes(pd, ml.STAGE_DISPATCH)
+    assert L.moe_dispatch(ctypes.byref(p), None, *([256] * 6), None, None, 256, nd,
+                          None) == ml.MOE_ERR_INVALID_ARG
+    assert L.moe_dispatch(ctypes.byref(p), *([256] * 6), 264, None, None, 256, nd,
+                          None) == ml.MOE_ERR_INVALID_ARG   # misaligned token_slot_row

@@ -704,6 +704,21 @@ constexpr int kBigRowBytes = 64;
 constexpr int kBigStages = 4;
 constexpr int kBigStageBytes = (kWideBM + kWideBN) * kBigRowBytes;  // 40 KB
 
+// Block shapes of the large-tile kernel body: token rows, weight rows, waves
+// (each 64 x 128), LDS stage size and ring depth.  Full and wide tiles share
+// one kernel and so one ring (40 KB stages).  (A 128 x 256 shape with four
+// waves and 72 KB, two blocks per CU so that one block's first loads and
+// epilogue overlap the other's main loop, measured 5-7 % slower.)
+template <int BM_, int BN_, int NW_, int STAGE_, int STAGES_>
+struct TileShape {
+  static constexpr int BM = BM_, BN = BN_, NW = NW_, kStageBytes = STAGE_, kStages = STAGES_;
+  static_assert((BM / 64) * (BN / 128) == NW, "64 x 128 per wave");
+  static_assert((BM + BN) * kBigRowBytes <= STAGE_, "a K step fits a stage");
+};
+using FullShape = TileShape<kBigBM, kBigBN, 8, kBigStageBytes, kBigStages>;
+using WideShape = TileShape<kWideBM, kWideBN, 8, kBigStageBytes, kBigStages>;
+
+
 // Work units of the large-tile GEMMs (see above).  Entry {expert, first row,
 // n-index, wide}: the n-index counts 256-row weight tiles of a full tile or
 // 512-row ranges of a wide one.  An expert with 129..255 rows past its last
@@ -774,15 +789,15 @@ __global__ __launch_bounds__(1024) void unit_schedule_kernel(
   }
 }
 
-template <int MODE, bool WIDE>
+template <int MODE, class SH>
 __device__ __forceinline__ void big_tile(const GemmArgs& g, const int4 unit, uint8_t* smem) {
   constexpr bool kSwiglu = MODE != MODE_PLAIN;
-  constexpr int BM = WIDE ? kWideBM : kBigBM;
-  constexpr int BN = WIDE ? kWideBN : kBigBN;
+  constexpr int BM = SH::BM, BN = SH::BN, NW = SH::NW;
+  constexpr int kStages = SH::kStages, kStageBytes = SH::kStageBytes, kAhead = kStages - 1;
   constexpr int kWRegion = BM * kBigRowBytes;
   constexpr int kAGroups = BM / 16;                        // 16-row load groups
-  constexpr int kLoads = (BM + BN) / 16 / 8;               // per wave and step: 4 or 5
-  constexpr int kALoads = kAGroups / 8;                    // of which A: 2 or 1
+  constexpr int kLoads = (BM + BN) / 16 / NW;              // per wave and step: 4, 5 or 6
+  constexpr int kALoads = kAGroups / NW;                   // of which A: 2, 1 or 2
   constexpr int kWaveRows = BM / 64;                       // waves along the token rows
 
   const int e = unit.x, row0 = unit.y, nidx = unit.z;
@@ -827,7 +842,7 @@ __device__ __forceinline__ void big_tile(const GemmArgs& g, const int4 unit, uin
   const __amdgpu_buffer_rsrc_t rW = make_rsrc(w_base, g.w_stride);
   auto dma = [&](int step, int stage) {
     const int k = min(step, nk - 1);
-    uint8_t* base = smem + stage * kBigStageBytes;
+    uint8_t* base = smem + stage * kStageBytes;
 #pragma unroll
     for (int q = 0; q < kLoads; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(q < kALoads ? rA : rW, (lds_ptr_t)(base + ldst[q]),
@@ -873,18 +888,20 @@ __device__ __forceinline__ void big_tile(const GemmArgs& g, const int4 unit, uin
     }
   };
 
-  dma(0, 0);
-  dma(1, 1);
-  dma(2, 2);
-  WAIT_VMCNT(2 * kLoads);
+#pragma unroll
+  for (int st = 0; st < kAhead; ++st) dma(st, st);
+  WAIT_VMCNT((kAhead - 1) * kLoads);
   __builtin_amdgcn_s_barrier();
   lfrag(smem, 0, 0);
 
+  int s_cur = 0;  // stage of step kt
   for (int kt = 0; kt < nk; ++kt) {
-    const uint8_t* cur = smem + (kt % kBigStages) * kBigStageBytes;
-    const uint8_t* nxt = smem + ((kt + 1) % kBigStages) * kBigStageBytes;
-    // Stage (kt + 3) % 4 was released by the barrier that ended step kt - 1.
-    dma(kt + 3, (kt + 3) % kBigStages);
+    const int s_nxt = s_cur + 1 == kStages ? 0 : s_cur + 1;
+    const uint8_t* cur = smem + s_cur * kStageBytes;
+    const uint8_t* nxt = smem + s_nxt * kStageBytes;
+    // The stage of step kt - 1 was released by the barrier that ended that
+    // step; it takes step kt + kAhead.
+    dma(kt + kAhead, s_cur == 0 ? kStages - 1 : s_cur - 1);
     lfrag(cur, 1, 1);
     mma(0, 0, 8);
 #pragma unroll
@@ -895,9 +912,9 @@ __device__ __forceinline__ void big_tile(const GemmArgs& g, const int4 unit, uin
     }
     SCHED(kSchedMfma, 2);
     mma(1, 0, 4);
-    // Step boundary: step kt+1 has landed once only steps kt+2 and kt+3 are
-    // in flight; this wave's reads of stage kt are done.
-    WAIT_VMCNT_LDS(2 * kLoads);
+    // Step boundary: step kt+1 has landed once only the later steps are in
+    // flight; this wave's reads of stage kt are done.
+    WAIT_VMCNT_LDS((kAhead - 1) * kLoads);
     __builtin_amdgcn_s_barrier();
     lfrag(nxt, 0, 0);
     mma(1, 4, 4);
@@ -906,6 +923,7 @@ __device__ __forceinline__ void big_tile(const GemmArgs& g, const int4 unit, uin
       SCHED(kSchedDsRead, 2);
       SCHED(kSchedMfma, 1);
     }
+    s_cur = s_nxt;
   }
   WAIT_VMCNT(0);
 
@@ -917,7 +935,7 @@ __device__ __forceinline__ void big_tile(const GemmArgs& g, const int4 unit, uin
     // instead of 16 bytes of 32 rows each.  Every wave is past its last
     // fragment read and direct load once all have reached the barrier.
     constexpr int kPitch = 272;  // 256 bytes + 16: rows start 4 banks apart
-    static_assert(8 * 64 * kPitch <= kBigStages * kBigStageBytes, "epilogue tile fits the ring");
+    static_assert(NW * 64 * kPitch <= kStages * kStageBytes, "epilogue tile fits the ring");
     __builtin_amdgcn_s_barrier();
     uint8_t* stile = smem + w * 64 * kPitch;
 #pragma unroll
@@ -977,10 +995,11 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const GemmArgs
   if (t >= total) return;
   const int4 unit = g.info[t];
   if (unit.w)
-    big_tile<MODE, true>(g, unit, smem);
+    big_tile<MODE, WideShape>(g, unit, smem);
   else
-    big_tile<MODE, false>(g, unit, smem);
+    big_tile<MODE, FullShape>(g, unit, smem);
 }
+
 
 template <int MODE>
 hipError_t launch_big(const GemmArgs& g, int64_t max_units, hipStream_t s) {
@@ -1315,38 +1334,49 @@ hipError_t launch_big_fp8(const GemmArgs& g, int64_t max_units, hipStream_t s) {
 
 }  // namespace
 
-// Work tables: the large-tile kernels run from (tile, n-range) unit tables,
-// the pipelined kernel from an m-tile table shared by both GEMMs.
-static bool unit_path(int tile_m, bool fp8) { return fp8 ? tile_m == kF8BM : tile_m == kBigBM; }
-bool gemm_unit_tables(int tile_m, bool fp8) { return unit_path(tile_m, fp8); }
-
-int gemm_tile_m(bool fp8, int64_t rows_per_expert) {
-  // Few rows per expert (decode-sized batches): the 256-row tile would spend
-  // most of its matrix-core time on padding while the work is weight streaming.
-  if (fp8) return (kF8BM == kBM || rows_per_expert > 2 * kBM) ? kF8BM : kBM;
-  if (rows_per_expert <= kSkBM) return kSkBM;
-  return rows_per_expert <= 2 * kBM ? kBM : kBigBM;
+GemmPath gemm_path(bool fp8, int64_t rows_per_expert) {
+  // Few rows per expert (decode-sized batches): large tiles would spend most
+  // of their matrix-core time on padding while the work is weight streaming.
+  if (fp8) return (kF8BM == kBM || rows_per_expert > 2 * kBM) ? GEMM_LARGE_FP8 : GEMM_PIPELINED;
+  if (rows_per_expert <= kSkBM) return GEMM_SKINNY;
+  if (rows_per_expert <= 2 * kBM) return GEMM_PIPELINED;
+  return GEMM_LARGE;
 }
 
-int gemm_n_tiles(int tile_m, bool swiglu, int Nout) {
-  (void)tile_m;  // every kernel's block covers 256 weight rows
+int gemm_path_rows(GemmPath path) {
+  switch (path) {
+    case GEMM_SKINNY: return kSkBM;
+    case GEMM_PIPELINED: return kBM;
+    case GEMM_LARGE: return kBigBM;
+    case GEMM_LARGE_FP8: return kF8BM;
+  }
+  return kBM;
+}
+
+bool gemm_unit_tables(GemmPath path) {
+  return path == GEMM_LARGE || path == GEMM_LARGE_FP8;
+}
+
+int gemm_n_tiles(bool swiglu, int Nout) {
   return swiglu ? ceil_div(Nout, kBN / 2) : ceil_div(Nout, kBN);
 }
 
-int64_t schedule_entries(int64_t n_cap, int E_L, int tile_m, bool fp8, int nt) {
-  if (unit_path(tile_m, fp8)) return (n_cap / tile_m + E_L) * nt;
-  return ceil_div<int64_t>(n_cap, tile_m) + E_L;
+int64_t schedule_entries(int64_t n_cap, int E_L, GemmPath path, int nt) {
+  const int bm = gemm_path_rows(path);
+  if (gemm_unit_tables(path)) return (n_cap / bm + E_L) * nt;
+  return ceil_div<int64_t>(n_cap, bm) + E_L;
 }
 
-hipError_t launch_schedule(const int32_t* offsets, int E_L, int tile_m, bool fp8, int nt_up,
-                           int nt_dn, int4* tab_up, int32_t* n_up, int4* tab_dn, int32_t* n_dn,
+hipError_t launch_schedule(const int32_t* offsets, int E_L, GemmPath path, int nt_up, int nt_dn,
+                           int4* tab_up, int32_t* n_up, int4* tab_dn, int32_t* n_dn,
                            hipStream_t s) {
-  if (unit_path(tile_m, fp8))  // the block-FP8 kernel has no wide tiles
+  const int bm = gemm_path_rows(path);
+  if (gemm_unit_tables(path))  // only the bf16 256-row path has wide tiles
     hipLaunchKernelGGL(unit_schedule_kernel, dim3(1), dim3(1024), 0, s, offsets, E_L, nt_up, nt_dn,
-                       tile_m, !fp8, tab_up, n_up, tab_dn, n_dn);
+                       bm, path == GEMM_LARGE, tab_up, n_up, tab_dn, n_dn);
   else
-    hipLaunchKernelGGL(tile_schedule_kernel, dim3(1), dim3(1024), 0, s, offsets, E_L, tile_m,
-                       tab_up, n_up);
+    hipLaunchKernelGGL(tile_schedule_kernel, dim3(1), dim3(1024), 0, s, offsets, E_L, bm, tab_up,
+                       n_up);
   return hipGetLastError();
 }
 
@@ -1369,7 +1399,7 @@ hipError_t launch_grouped_gemm(const GemmLaunch& L, hipStream_t s) {
   g.K = L.K;
   g.Nout = L.Nout;
   g.NW = L.swiglu ? 2 * L.Nout : L.Nout;
-  g.nt_n = gemm_n_tiles(L.tile_m, L.swiglu, L.Nout);
+  g.nt_n = gemm_n_tiles(L.swiglu, L.Nout);
   const int64_t elem = L.fp8 ? 1 : 2;
   const int64_t ldb = L.K * elem;
   g.w_stride = static_cast<int64_t>(g.NW) * ldb;
@@ -1384,22 +1414,25 @@ hipError_t launch_grouped_gemm(const GemmLaunch& L, hipStream_t s) {
   g.a_bytes = L.a_rows * ldb;
   g.c_cs = L.c_panel ? 64 * L.c_rows : 0;
   g.a_index = L.a_index;
-  if (!L.fp8) {
-    if (unit_path(L.tile_m, false)) {
-      if (L.swiglu) return launch_big<MODE_SWIGLU>(g, L.max_tiles, s);
-      return launch_big<MODE_PLAIN>(g, L.max_tiles, s);
-    }
-    if (L.tile_m == kSkBM) {
-      if (L.swiglu) return launch_skinny<MODE_SWIGLU>(g, L.max_tiles, s);
-      return launch_skinny<MODE_PLAIN>(g, L.max_tiles, s);
-    }
-    if (L.swiglu) return launch_pipelined<false, MODE_SWIGLU>(g, L.max_tiles, s);
-    return launch_pipelined<false, MODE_PLAIN>(g, L.max_tiles, s);
+  const bool fp8_path = L.path == GEMM_LARGE_FP8 || L.path == GEMM_PIPELINED;
+  if ((L.fp8 && !fp8_path) || (!L.fp8 && L.path == GEMM_LARGE_FP8)) return hipErrorInvalidValue;
+  switch (L.path) {
+    case GEMM_LARGE:
+      return L.swiglu ? launch_big<MODE_SWIGLU>(g, L.max_tiles, s)
+                      : launch_big<MODE_PLAIN>(g, L.max_tiles, s);
+    case GEMM_SKINNY:
+      return L.swiglu ? launch_skinny<MODE_SWIGLU>(g, L.max_tiles, s)
+                      : launch_skinny<MODE_PLAIN>(g, L.max_tiles, s);
+    case GEMM_LARGE_FP8:
+      if (!L.swiglu) return launch_big_fp8<MODE_PLAIN>(g, L.max_tiles, s);
+      if (!L.C_scale) return hipErrorInvalidValue;  // block-FP8 h only
+      return launch_big_fp8<MODE_SWIGLU_FP8OUT>(g, L.max_tiles, s);
+    case GEMM_PIPELINED:
+      break;
   }
-  if (unit_path(L.tile_m, true)) {
-    if (!L.swiglu) return launch_big_fp8<MODE_PLAIN>(g, L.max_tiles, s);
-    if (!L.C_scale) return hipErrorInvalidValue;  // block-FP8 h only
-    return launch_big_fp8<MODE_SWIGLU_FP8OUT>(g, L.max_tiles, s);
+  if (!L.fp8) {
+    return L.swiglu ? launch_pipelined<false, MODE_SWIGLU>(g, L.max_tiles, s)
+                    : launch_pipelined<false, MODE_PLAIN>(g, L.max_tiles, s);
   }
   if (L.swiglu) {
     if (L.C_scale) return launch_pipelined<true, MODE_SWIGLU_FP8OUT>(g, L.max_tiles, s);

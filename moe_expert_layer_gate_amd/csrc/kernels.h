@@ -30,25 +30,27 @@ hipError_t launch_gather_fp8(const void* src, const int32_t* rows, const int32_t
 hipError_t launch_quant_blocks(const void* src, int64_t batch, int64_t rows, int64_t cols,
                                void* codes, float* scales, hipStream_t s);
 
-// Row tile of the grouped GEMM for a problem, from the mean rows per expert:
-// bf16 32 (the skinny kernel, up to 32 rows: decode), 128 (the pipelined
-// kernel, up to 256) or 256 (the large-tile kernel, which covers segment
-// remainders of up to 128 rows with 128 x 512 tiles); block-FP8 128
-// (pipelined, up to 256) or the row tile of its large-tile kernel.
-int gemm_tile_m(bool fp8, int64_t rows_per_expert);
-// Whether the GEMMs of a problem run from per-GEMM unit tables (large-tile
-// kernels) or from one shared m-tile table (pipelined kernel).
-bool gemm_unit_tables(int tile_m, bool fp8);
-// n-tiles per expert of one GEMM.
-int gemm_n_tiles(int tile_m, bool swiglu, int Nout);
-// Capacity of a GEMM's work table: m-tiles (pipelined kernel; the up and down
-// GEMMs share one table) or (tile, n-range) units (large-tile kernels; one
-// table per GEMM, nt = gemm_n_tiles of that GEMM).
-int64_t schedule_entries(int64_t n_cap, int E_L, int tile_m, bool fp8, int nt);
-// Builds the work tables on the device from the expert offsets (pipelined
-// kernel: only tab_up / n_up are written).
-hipError_t launch_schedule(const int32_t* offsets, int E_L, int tile_m, bool fp8, int nt_up,
-                           int nt_dn, int4* tab_up, int32_t* n_up, int4* tab_dn, int32_t* n_dn,
+// GEMM kernels, chosen per problem from the mean rows per expert.
+enum GemmPath {
+  GEMM_SKINNY = 0,     // bf16, up to 32 rows: 32 x 256 tiles (decode)
+  GEMM_PIPELINED = 1,  // up to 256 rows: 128 x 256 tiles (bf16 and block-FP8)
+  GEMM_LARGE = 2,      // bf16: 256 x 256 tiles, 128 x 512 for segment remainders
+  GEMM_LARGE_FP8 = 3,  // block-FP8: 256 x 256 tiles
+};
+GemmPath gemm_path(bool fp8, int64_t rows_per_expert);
+// Token rows of the path's tiles (of its full tiles, for GEMM_LARGE).
+int gemm_path_rows(GemmPath path);
+// Whether the GEMMs run from per-GEMM unit tables (large-tile kernels) or
+// from one m-tile table shared by both GEMMs (skinny and pipelined kernels).
+bool gemm_unit_tables(GemmPath path);
+// n-tiles per expert of one GEMM (every kernel covers 256 weight rows).
+int gemm_n_tiles(bool swiglu, int Nout);
+// Capacity of a GEMM's work table (nt = gemm_n_tiles of that GEMM).
+int64_t schedule_entries(int64_t n_cap, int E_L, GemmPath path, int nt);
+// Builds the work tables on the device from the expert offsets (m-tile
+// table: only tab_up / n_up are written).
+hipError_t launch_schedule(const int32_t* offsets, int E_L, GemmPath path, int nt_up, int nt_dn,
+                           int4* tab_up, int32_t* n_up, int4* tab_dn, int32_t* n_dn,
                            hipStream_t s);
 struct GemmLaunch {
   bool fp8;              // e4m3 operands with block scales, else bf16
@@ -63,7 +65,7 @@ struct GemmLaunch {
   const int4* info;       // work table of this GEMM (launch_schedule)
   const int32_t* n_tiles; // live entries of the table
   int64_t max_tiles;      // its capacity (schedule_entries)
-  int tile_m;             // gemm_tile_m() of the problem
+  GemmPath path;          // gemm_path() of the problem
   int K, Nout;
   // Storage layouts (bf16 only): panel = [K/32][R][32], see moe_layer.h.
   bool a_panel;          // A in panel layout with R = a_rows

@@ -85,7 +85,7 @@ bool can_fuse_gather(const moe_problem* p) {
 }
 
 struct FfnScratch {
-  int4* tab_up;     // work tables of the two GEMMs (one shared table for tile_m 128)
+  int4* tab_up;     // work tables of the two GEMMs (or one shared m-tile table)
   int4* tab_dn;
   int32_t* n_up;
   int32_t* n_dn;
@@ -94,18 +94,19 @@ struct FfnScratch {
 };
 
 struct FfnShape {
-  int tile_m, nt_up, nt_dn;
+  GemmPath path;
+  int nt_up, nt_dn;
   int64_t cap_up, cap_dn;
 };
 
 FfnShape ffn_shape(const moe_problem* p) {
   const int64_t N = n_cap(p);
   FfnShape f{};
-  f.tile_m = gemm_tile_m(is_fp8(p), N / p->num_local);
-  f.nt_up = gemm_n_tiles(f.tile_m, true, p->inter);
-  f.nt_dn = gemm_n_tiles(f.tile_m, false, p->hidden);
-  f.cap_up = schedule_entries(N, p->num_local, f.tile_m, is_fp8(p), f.nt_up);
-  f.cap_dn = schedule_entries(N, p->num_local, f.tile_m, is_fp8(p), f.nt_dn);
+  f.path = gemm_path(is_fp8(p), N / p->num_local);
+  f.nt_up = gemm_n_tiles(true, p->inter);
+  f.nt_dn = gemm_n_tiles(false, p->hidden);
+  f.cap_up = schedule_entries(N, p->num_local, f.path, f.nt_up);
+  f.cap_dn = schedule_entries(N, p->num_local, f.path, f.nt_dn);
   return f;
 }
 
@@ -115,7 +116,7 @@ FfnScratch carve_ffn(Carve& c, const moe_problem* p) {
   FfnScratch f{};
   f.tab_up = c.take<int4>(sizeof(int4) * sh.cap_up);
   f.n_up = c.take<int32_t>(sizeof(int32_t));
-  if (!gemm_unit_tables(sh.tile_m, is_fp8(p))) {  // one m-tile table for both GEMMs
+  if (!gemm_unit_tables(sh.path)) {  // one m-tile table for both GEMMs
     f.tab_dn = f.tab_up;
     f.n_dn = f.n_up;
   } else {
@@ -226,8 +227,8 @@ moe_status run_ffn(const moe_problem* p, const FfnSource& src, const int32_t* of
   const FfnShape sh = ffn_shape(p);
   void* hb = h ? h : f.h;
   float* hs = h ? h_scale : f.h_scale;
-  MOE_TRY(launch_schedule(offsets, E_L, sh.tile_m, is_fp8(p), sh.nt_up, sh.nt_dn, f.tab_up, f.n_up,
-                          f.tab_dn, f.n_dn, s));
+  MOE_TRY(launch_schedule(offsets, E_L, sh.path, sh.nt_up, sh.nt_dn, f.tab_up, f.n_up, f.tab_dn,
+                          f.n_dn, s));
   GemmLaunch up{};
   up.fp8 = is_fp8(p);
   up.swiglu = true;
@@ -241,7 +242,7 @@ moe_status run_ffn(const moe_problem* p, const FfnSource& src, const int32_t* of
   up.info = f.tab_up;
   up.n_tiles = f.n_up;
   up.max_tiles = sh.cap_up;
-  up.tile_m = sh.tile_m;
+  up.path = sh.path;
   up.K = H;
   up.Nout = I;
   up.a_panel = panel_acts(p) && !src.rows_major && !src.index;

@@ -56,6 +56,12 @@ class MoEConfig:
     zipf_s: float = 1.1
     replicas: int = 0          # >0: Dirichlet(0.5) split of the rows over replicas
     std: float = 0.02
+    act: str = "swiglu"        # "swiglu" (gated, m = 2) | "gelu" (standard MLP, m = 1)
+
+    @property
+    def m(self) -> int:
+        """First-layer matrices per expert."""
+        return 2 if self.act == "swiglu" else 1
 
     @property
     def dtype(self) -> str:
@@ -82,6 +88,10 @@ CONFIGS: Dict[str, MoEConfig] = {
     # Decode-sized batch on the same shard shape with uniform routing.
     "dsv3_ep8_decode": MoEConfig("dsv3_ep8_decode", T=64, H=7168, E=256, E_L=32,
                                  e_lo=0, k=8, I=2048),
+    # The Qwen3-30B-A3B prefill shape with a standard (non-gated) GELU MLP:
+    # the pages' BF16 group runs its models with a standard MLP.
+    "qwen3_30b_prefill_gelu": MoEConfig("qwen3_30b_prefill_gelu", T=8192, H=2048, E=128,
+                                        E_L=128, e_lo=0, k=8, I=768, act="gelu"),
 }
 # Numbered aliases in the order the workloads are usually listed.
 _ORDER = ["tiny", "qwen3_30b_prefill", "dsv3_ep8_prefill",
@@ -181,9 +191,10 @@ def make_inputs(cfg: MoEConfig, seed: int, *, weights: bool = True,
     Returns a dict with
       logits  float32 [T, E]
       x       uint16 (bf16 bits) [T, H]
-      w13     uint16 [E_L, 2I, H]   rows 0..I-1 gate, I..2I-1 up (K-contiguous)
+      w13     uint16 [E_L, m I, H]  SwiGLU (m = 2): rows 0..I-1 gate, I..2I-1 up;
+                                    GELU (m = 1): the first-layer matrix
       w2      uint16 [E_L, H, I]
-      ws13    uint16 [2I_s, H]      (only when I_s > 0)
+      ws13    uint16 [m I_s, H]     (only when I_s > 0)
       ws2     uint16 [H, I_s]       (only when I_s > 0)
       replica_offsets int64 [R + 1] (only when cfg.replicas > 0)
     ``weights=False`` skips the weight draws.
@@ -200,9 +211,9 @@ def make_inputs(cfg: MoEConfig, seed: int, *, weights: bool = True,
         out["replica_offsets"] = replica_split(stream(4), cfg.T, cfg.replicas)
     if not weights:
         return out
-    out["w13"] = _normal_bf16([seed, 2, 0], (cfg.E_L, 2 * cfg.I, cfg.H), w_std)
+    out["w13"] = _normal_bf16([seed, 2, 0], (cfg.E_L, cfg.m * cfg.I, cfg.H), w_std)
     out["w2"] = _normal_bf16([seed, 2, 1], (cfg.E_L, cfg.H, cfg.I), w_std)
     if cfg.I_s > 0:
-        out["ws13"] = _normal_bf16([seed, 3, 0], (2 * cfg.I_s, cfg.H), w_std)
+        out["ws13"] = _normal_bf16([seed, 3, 0], (cfg.m * cfg.I_s, cfg.H), w_std)
         out["ws2"] = _normal_bf16([seed, 3, 1], (cfg.H, cfg.I_s), w_std)
     return out

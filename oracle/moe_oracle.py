@@ -44,6 +44,11 @@ the design notes of the repository):
   ascending token (a stable counting sort of token-major (token, slot) pairs).
 * SwiGLU: h = silu(gate) * up with silu(a) = a / (1 + exp(-a)); rows
   0..I-1 of W13 are the gate projection and rows I..2I-1 the up projection.
+* Standard (non-gated) MLP, the pages' BF16 group: one first-layer matrix
+  (m = 1, OverlapAdvisor Eq. 8) and GELU between the GEMMs (OverlapAdvisor
+  Table 6); the pages give no formula, and the plainest reading is the
+  exact GELU, gelu(a) = a * Phi(a) = a (1 + erf(a / sqrt 2)) / 2 (not the
+  tanh approximation).  W1 [I, H] takes the place of W13.
 * FP8: OCP E4M3FN codes (largest finite 448, no infinities); per-block scale
   s = amax / 448 in float32 (s = 1 for an all-zero block); code =
   round-to-nearest-even(v / s) with the quotient formed in float32 and
@@ -285,27 +290,56 @@ def silu(a: np.ndarray) -> np.ndarray:
         return a / (1.0 + np.exp(-a))
 
 
-def expert_ffn(xr: np.ndarray, w13: np.ndarray, w2: np.ndarray, h_fn=None):
-    """One expert's gated SwiGLU FFN on a block of rows.
+def gelu(a: np.ndarray) -> np.ndarray:
+    """Exact GELU: a * Phi(a), Phi the standard normal distribution
+    function, written with the complementary error function:
+    Phi(a) = (1 + erf(a / sqrt 2)) / 2 = erfc(-a / sqrt 2) / 2 (the erfc form
+    keeps full relative precision in the negative tail)."""
+    from scipy.special import erfc
+    a = np.asarray(a, dtype=np.float64)
+    return 0.5 * a * erfc(-a / np.sqrt(2.0))
 
-    OverlapAdvisor section 4.2.2 (a gated MLP has m = 2 first-layer
-    matrices), Eq. 8 (the up GroupGEMM has 2*m*H*I FLOPs per row, the down
-    GroupGEMM 2*H*I), Table 6 (gated SwiGLU), section 4.2.1 (the activation
-    sits between the two GroupGEMMs).
 
+ACTIVATIONS = ("swiglu", "gelu")
+
+
+def up_rows(I: int, activation: str = "swiglu") -> int:
+    """Rows of an expert's first-layer weight: m * I, m = 2 first-layer
+    matrices for the gated MLP, 1 for the standard one (OverlapAdvisor Eq. 8)."""
+    return (2 if activation == "swiglu" else 1) * I
+
+
+def expert_ffn(xr: np.ndarray, w13: np.ndarray, w2: np.ndarray, h_fn=None,
+               activation: str = "swiglu"):
+    """One expert's FFN on a block of rows.
+
+    Gated SwiGLU (default): OverlapAdvisor section 4.2.2 (a gated MLP has
+    m = 2 first-layer matrices), Eq. 8 (the up GroupGEMM has 2*m*H*I FLOPs
+    per row, the down GroupGEMM 2*H*I), Table 6 (gated SwiGLU), section
+    4.2.1 (the activation sits between the two GroupGEMMs).
     xr [n, H]; w13 [2I, H] (gate rows then up rows); w2 [H, I].
+
+    Standard MLP (activation="gelu"): m = 1 (Eq. 8), Table 6 (BF16 standard
+    MLP with GELU): h = gelu(xr @ w1.T) with w13 = w1 [I, H].
+
     ``h_fn``, if given, maps h before the down projection (the FP8 path's
     activation quantisation).
     Returns (h [n, I], y [n, H]) in float64.
     """
-    I = w13.shape[0] // 2
-    g = xr @ w13[:I].T
-    u = xr @ w13[I:].T
-    h = silu(g) * u
+    if activation == "swiglu":
+        I = w13.shape[0] // 2
+        g = xr @ w13[:I].T
+        u = xr @ w13[I:].T
+        h = silu(g) * u
+    elif activation == "gelu":
+        h = gelu(xr @ w13.T)
+    else:
+        raise ValueError(activation)
     return h, (h if h_fn is None else h_fn(h)) @ w2.T
 
 
-def grouped_ffn(x_perm: np.ndarray, offsets: np.ndarray, w13, w2, h_fn=None):
+def grouped_ffn(x_perm: np.ndarray, offsets: np.ndarray, w13, w2, h_fn=None,
+                activation: str = "swiglu"):
     """Grouped FFN over the expert-major rows: segment e
     [offsets[e], offsets[e+1]) runs through local expert e.  ``w13``/``w2``
     are callables or arrays indexed by the local expert giving float64
@@ -323,8 +357,8 @@ def grouped_ffn(x_perm: np.ndarray, offsets: np.ndarray, w13, w2, h_fn=None):
             continue
         we13, we2 = get13(e), get2(e)
         if h_all is None:
-            h_all = np.zeros((N, we13.shape[0] // 2), dtype=np.float64)
-        h, y = expert_ffn(x_perm[a:b], we13, we2, h_fn)
+            h_all = np.zeros((N, we2.shape[1]), dtype=np.float64)
+        h, y = expert_ffn(x_perm[a:b], we13, we2, h_fn, activation)
         h_all[a:b] = h
         y_perm[a:b] = y
     if h_all is None:
@@ -388,10 +422,12 @@ def fp8_activation(a: np.ndarray) -> np.ndarray:
 
 def moe_layer(logits: np.ndarray, x_bits: np.ndarray, weights: dict, *,
               k: int, e_lo: int, E_L: int, fp8: bool = False,
-              quantize_activations: bool = False) -> Dict[str, np.ndarray]:
+              quantize_activations: bool = False,
+              activation: str = "swiglu") -> Dict[str, np.ndarray]:
     """The whole layer for one GPU's local experts, every stage kept.
 
-    ``weights``: bf16 -> "w13" [E_L, 2I, H], "w2" [E_L, H, I] (bf16 bits),
+    ``weights``: bf16 -> "w13" [E_L, m*I, H] (m = 2 for SwiGLU, 1 for the
+    standard GELU MLP), "w2" [E_L, H, I] (bf16 bits),
     optional "ws13"/"ws2" (shared expert); fp8 -> the same names with
     suffixes "_q" (codes) and "_s" (128 x 128 block scales).
 
@@ -413,11 +449,11 @@ def moe_layer(logits: np.ndarray, x_bits: np.ndarray, weights: dict, *,
     x_perm = dispatch(xq, ix["row_token"])
     g13, g2 = _expert_weights(weights, fp8)
     h_fn = fp8_activation if qa else None
-    h, y_perm = grouped_ffn(x_perm, ix["offsets"], g13, g2, h_fn)
+    h, y_perm = grouped_ffn(x_perm, ix["offsets"], g13, g2, h_fn, activation)
     sw = _shared_weights(weights, fp8)
     shared = None
     if sw is not None:
-        shared = expert_ffn(xq, sw[0], sw[1], h_fn)[1]
+        shared = expert_ffn(xq, sw[0], sw[1], h_fn, activation)[1]
     y = combine(y_perm, ix["token_slot_row"], w, shared, H=x.shape[1])
     out = dict(ix)
     out.update(ids=ids, w=w, x_perm=x_perm, h=h, y_perm=y_perm, shared=shared, y=y)
@@ -426,7 +462,8 @@ def moe_layer(logits: np.ndarray, x_bits: np.ndarray, weights: dict, *,
 
 def moe_layer_tokens(logits: np.ndarray, x_bits: np.ndarray, weights: dict,
                      tokens, *, k: int, e_lo: int, E_L: int,
-                     fp8: bool = False, quantize_activations: bool = False) -> np.ndarray:
+                     fp8: bool = False, quantize_activations: bool = False,
+                     activation: str = "swiglu") -> np.ndarray:
     """Layer output rows for a few tokens only, one token at a time (for
     spot checks at sizes where the whole layer is too slow on the CPU).
     A token's output depends only on its own logits and activations, so
@@ -454,11 +491,11 @@ def moe_layer_tokens(logits: np.ndarray, x_bits: np.ndarray, weights: dict,
     for e, lst in sorted(by_expert.items()):
         we13, we2 = g13(e), g2(e)
         rows = np.array([i for i, _ in lst])
-        _, ye = expert_ffn(x[rows], we13, we2, h_fn)
+        _, ye = expert_ffn(x[rows], we13, we2, h_fn, activation)
         for (i, s), yr in zip(lst, ye):
             contrib[i, s] = w[i, s] * yr
     for s in range(k):                       # slot order, as in combine()
         y += contrib[:, s]
     if sw is not None:
-        y += expert_ffn(x, sw[0], sw[1], h_fn)[1]
+        y += expert_ffn(x, sw[0], sw[1], h_fn, activation)[1]
     return y

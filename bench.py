@@ -205,7 +205,9 @@ def main():
 
     n_pairs = int(offsets[-1].item())
     cnt = counts.cpu().numpy()
-    flops = 6.0 * p.H * p.I * n_pairs + 6.0 * p.H * p.I_s * p.T
+    # 2 m H I (up, m first-layer matrices) + 2 H I (down) per row (Eq. 8)
+    mm = 2.0 * (p.m + 1)
+    flops = mm * p.H * p.I * n_pairs + mm * p.H * p.I_s * p.T
     dtype = "fp8" if cfg.fp8 else "bf16"
     beta_w = 1 if cfg.fp8 else 2
     active = int((cnt > 0).sum())
@@ -220,7 +222,7 @@ def main():
     if decode:
         # weight streaming: every active expert's W13 and W2 once, plus the
         # token rows in and out of both GEMMs
-        bytes_ = (active * 3 * p.H * p.I * beta_w
+        bytes_ = (active * (p.m + 1) * p.H * p.I * beta_w
                   + n_pairs * (p.H * beta_w + 2 * p.I * beta_w + 2 * p.H))
         achieved = bytes_ / (ffn_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
@@ -259,6 +261,7 @@ def main():
         "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.H, "experts": cfg.E,
                    "local_experts": cfg.E_L, "expert_begin": cfg.e_lo, "top_k": cfg.k,
                    "inter": cfg.I, "shared_inter": cfg.I_s, "seed": seed,
+                   "mlp": "gated SwiGLU" if cfg.act == "swiglu" else "standard GELU",
                    "layout": "panel" if panel else "rows"},
         "grouped_ffn_tflops": round(ffn_tflops, 2),
         "grouped_ffn_frac_of_peak": round(ffn_tflops / PEAK_TFLOPS[dtype], 4),

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 typedef enum {
   MOE_OK = 0,
@@ -87,6 +87,16 @@ typedef enum {
 #define MOE_LAYOUT_PANEL_WEIGHTS 1
 #define MOE_LAYOUT_PANEL_ACTS 2
 
+/* Expert MLP form (moe_problem.activation).  Page "OverlapAdvisor ...",
+ * Eq. 8 (m first-layer matrices: 2 for a gated MLP, 1 for a standard one)
+ * and Table 6 (the FP8 group runs gated SwiGLU, the BF16 group a standard
+ * MLP with GELU).
+ *   MOE_ACT_SWIGLU (m = 2): h = silu(x Wg^T) * (x Wu^T), silu(a) = a/(1+e^-a)
+ *   MOE_ACT_GELU   (m = 1): h = gelu(x W1^T), gelu(a) = a * Phi(a) (exact,
+ *                  Phi the standard normal distribution function); bf16 only */
+#define MOE_ACT_SWIGLU 0
+#define MOE_ACT_GELU 1
+
 /* The workload tuple of one rank. */
 typedef struct {
   int32_t num_tokens;    /* T: tokens in the batch                            */
@@ -100,12 +110,15 @@ typedef struct {
   int32_t dtype;         /* moe_dtype                                          */
   int32_t layout;        /* MOE_LAYOUT_* bits, 0 = all row major; must be 0
                             for MOE_FP8_E4M3                                   */
+  int32_t activation;    /* MOE_ACT_SWIGLU (0) or MOE_ACT_GELU                 */
 } moe_problem;
 
 /* Expert weights, device pointers, K-contiguous ("[out, in]" row major).
- *   w13  [E_L, 2I, H]: rows 0..I-1 gate projection, rows I..2I-1 up projection
+ *   w13  [E_L, m I, H]: SwiGLU (m = 2): rows 0..I-1 gate projection, rows
+ *        I..2I-1 up projection; GELU (m = 1): the first-layer matrix W1
  *   w2   [E_L, H, I]:  down projection
- *   ws13 [2 I_s, H], ws2 [H, I_s]: shared expert (NULL when I_s == 0)
+ *   ws13 [m I_s, H], ws2 [H, I_s]: shared expert (NULL when I_s == 0), same
+ *        form as the routed experts
  * Element type: bf16 for MOE_BF16, E4M3 bytes for MOE_FP8_E4M3.
  * fp8 only, fp32 block scales (NULL for bf16):
  *   w13_scale [E_L, 2I/128, H/128], w2_scale [E_L, H/128, I/128],
@@ -163,15 +176,16 @@ moe_status moe_dispatch(const moe_problem* p, const void* x,
                         void* x_perm, float* x_perm_scale, void* ws,
                         size_t ws_bytes, void* stream);
 
-/* Grouped gated-SwiGLU FFN.  Page "OverlapAdvisor ...", section 4.2.2 and
- * Eq. 8 (m = 2 first-layer matrices for a gated MLP; the up GroupGEMM is
- * 2 m H I FLOPs per row, the down GroupGEMM 2 H I), Table 6 (gated SwiGLU);
+/* Grouped expert FFN.  Page "OverlapAdvisor ...", section 4.2.2 and Eq. 8
+ * (m first-layer matrices; the up GroupGEMM is 2 m H I FLOPs per row, the
+ * down GroupGEMM 2 H I), Table 6 (gated SwiGLU; standard MLP with GELU);
  * page "CascadeEP ...", Appendix C (the two expert GEMMs with the activation
  * and quantisation between them, in stream order).
  * For every local expert e and row j in [offsets[e], offsets[e+1]):
- *   h[j]      = silu(x_perm[j] . W_gate,e^T) * (x_perm[j] . W_up,e^T)   [I]
+ *   SwiGLU: h[j] = silu(x_perm[j] . W_gate,e^T) * (x_perm[j] . W_up,e^T) [I]
+ *   GELU:   h[j] = gelu(x_perm[j] . W1_e^T)                              [I]
  *   y_perm[j] = h[j] . W2_e^T                                          [H]
- * with silu(a) = a / (1 + exp(-a)), fp32 accumulation.
+ * with fp32 accumulation (see MOE_ACT_*).
  *   x_perm, x_perm_scale, offsets: as produced by moe_dispatch
  *   h          [N_cap, I] (optional, NULL = kept in the workspace): bf16,
  *              or E4M3 with h_scale [N_cap, I/128] fp32 for MOE_FP8_E4M3

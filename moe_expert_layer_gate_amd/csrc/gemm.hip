@@ -52,7 +52,19 @@ constexpr int kBN = 256;      // weight rows per block
 constexpr int kThreads = 256;
 constexpr int kXcds = 8;
 
-enum { MODE_PLAIN = 0, MODE_SWIGLU = 1, MODE_SWIGLU_FP8OUT = 2 };
+enum { MODE_PLAIN = 0, MODE_SWIGLU = 1, MODE_SWIGLU_FP8OUT = 2, MODE_GELU = 3 };
+
+// Exact GELU, a * Phi(a) = a erfc(-a / sqrt 2) / 2, in fp32 (the up GEMM's
+// epilogue of the standard MLP).
+__device__ __forceinline__ float gelu_f(float a) {
+  return 0.5f * a * erfcf(-a * 0.70710678118654752f);
+}
+// The epilogue value of the plain-geometry modes: y as is, or gelu(h).
+template <int MODE>
+__device__ __forceinline__ float plain_act(float v) {
+  if constexpr (MODE == MODE_GELU) return gelu_f(v);
+  return v;
+}
 
 struct GemmArgs {
   const uint8_t* A;        // activations [N_cap, K] (bf16 or e4m3)
@@ -163,7 +175,7 @@ template <bool FP8, int MODE>
 __global__ __launch_bounds__(kThreads, 1) void gemm_pipelined_kernel(const GemmArgs g) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   __shared__ float row_amax[2][kBM];
-  constexpr bool kSwiglu = MODE != MODE_PLAIN;
+  constexpr bool kSwiglu = MODE == MODE_SWIGLU || MODE == MODE_SWIGLU_FP8OUT;
   constexpr int kKK = FP8 ? 2 : 4;             // MFMA sub-steps per K step
   // Direct loads per wave and step: 12 x 8 rows of operands, plus (fp8) one
   // 4-byte-per-lane load of token scales.  Every load that the step waits
@@ -416,13 +428,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pipelined_kernel(const GemmA
   // ---- epilogue (accumulator element q*4 + r of a 32x32 tile is weight row
   // q*8 + (lane/32)*4 + r and token row lane % 32)
   const int cq = (lane >> 5) * 4;
-  if constexpr (MODE == MODE_PLAIN) {
-    uint16_t* C = static_cast<uint16_t*>(g.C);
+  if constexpr (MODE == MODE_PLAIN || MODE == MODE_GELU) {
+    uint8_t* C8 = static_cast<uint8_t*>(g.C);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int m = row0 + wm * 64 + j * 32 + lr;
       if (m >= seg_end) continue;
-      uint16_t* crow = C + static_cast<int64_t>(m) * g.Nout;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -430,9 +441,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pipelined_kernel(const GemmA
           const int col = nt * kBN + wn * 128 + i * 32 + q * 8 + cq;
           if (col >= g.Nout) continue;
           uint2 o;
-          o.x = pack_bf16x2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]);
-          o.y = pack_bf16x2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
-          *reinterpret_cast<uint2*>(crow + col) = o;
+          o.x = pack_bf16x2(plain_act<MODE>(acc[i][j][q * 4 + 0]), plain_act<MODE>(acc[i][j][q * 4 + 1]));
+          o.y = pack_bf16x2(plain_act<MODE>(acc[i][j][q * 4 + 2]), plain_act<MODE>(acc[i][j][q * 4 + 3]));
+          *reinterpret_cast<uint2*>(C8 + out_offset(g, m, col)) = o;
         }
     }
   } else {
@@ -532,7 +543,7 @@ constexpr int kSkLoads = (kSkBM + kSkBN) / 8 / 4;            // 1 A + 8 W per wa
 template <int MODE>
 __global__ __launch_bounds__(kSkThreads, 1) void gemm_skinny_kernel(const GemmArgs g) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
-  constexpr bool kSwiglu = MODE != MODE_PLAIN;
+  constexpr bool kSwiglu = MODE == MODE_SWIGLU || MODE == MODE_SWIGLU_FP8OUT;
   const int total = *g.n_tiles * g.nt_n;
   const int per_xcd = ceil_div(total, kXcds);
   const int slot = blockIdx.x / kXcds;
@@ -632,15 +643,15 @@ __global__ __launch_bounds__(kSkThreads, 1) void gemm_skinny_kernel(const GemmAr
   uint8_t* C8 = static_cast<uint8_t*>(g.C);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    if constexpr (MODE == MODE_PLAIN) {
+    if constexpr (MODE == MODE_PLAIN || MODE == MODE_GELU) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int col = nbase + w * 64 + i * 32 + q * 8 + cq;
         if (col >= g.Nout) continue;
         uint2 o;
-        o.x = pack_bf16x2(acc[i][q * 4 + 0], acc[i][q * 4 + 1]);
-        o.y = pack_bf16x2(acc[i][q * 4 + 2], acc[i][q * 4 + 3]);
-        *reinterpret_cast<uint2*>(C8 + (static_cast<int64_t>(m) * g.Nout + col) * 2) = o;
+        o.x = pack_bf16x2(plain_act<MODE>(acc[i][q * 4 + 0]), plain_act<MODE>(acc[i][q * 4 + 1]));
+        o.y = pack_bf16x2(plain_act<MODE>(acc[i][q * 4 + 2]), plain_act<MODE>(acc[i][q * 4 + 3]));
+        *reinterpret_cast<uint2*>(C8 + out_offset(g, m, col)) = o;
       }
     } else {
       const int col = nbase + w * 32 + q * 8 + cq;
@@ -791,7 +802,7 @@ __global__ __launch_bounds__(1024) void unit_schedule_kernel(
 
 template <int MODE, class SH>
 __device__ __forceinline__ void big_tile(const GemmArgs& g, const int4 unit, uint8_t* smem) {
-  constexpr bool kSwiglu = MODE != MODE_PLAIN;
+  constexpr bool kSwiglu = MODE == MODE_SWIGLU || MODE == MODE_SWIGLU_FP8OUT;
   constexpr int BM = SH::BM, BN = SH::BN, NW = SH::NW;
   constexpr int kStages = SH::kStages, kStageBytes = SH::kStageBytes, kAhead = kStages - 1;
   constexpr int kWRegion = BM * kBigRowBytes;
@@ -958,6 +969,25 @@ __device__ __forceinline__ void big_tile(const GemmArgs& g, const int4 unit, uin
       if (m < seg_end && col < g.Nout)
         *reinterpret_cast<uint4*>(C + static_cast<int64_t>(m) * g.Nout + col) = v;
     }
+  } else if constexpr (MODE == MODE_GELU) {
+    // h = gelu(x W1^T), panel or row major
+    uint8_t* C8 = reinterpret_cast<uint8_t*>(C);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int m = row0 + wm * 64 + j * 32 + lr;
+      if (m >= seg_end) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = nbase + wn * 128 + i * 32 + q * 8 + cq;
+          if (col >= g.Nout) continue;
+          uint2 o;
+          o.x = pack_bf16x2(gelu_f(acc[i][j][q * 4 + 0]), gelu_f(acc[i][j][q * 4 + 1]));
+          o.y = pack_bf16x2(gelu_f(acc[i][j][q * 4 + 2]), gelu_f(acc[i][j][q * 4 + 3]));
+          *reinterpret_cast<uint2*>(C8 + out_offset(g, m, col)) = o;
+        }
+    }
   } else {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -1067,7 +1097,7 @@ __device__ __forceinline__ void big_fp8_tile(const GemmArgs& g) {
   constexpr int kDma = kLoads + 1;  // + the token-scale load
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   __shared__ float row_amax[2][BM];
-  constexpr bool kSwiglu = MODE != MODE_PLAIN;
+  constexpr bool kSwiglu = MODE == MODE_SWIGLU || MODE == MODE_SWIGLU_FP8OUT;
 
   const int total = *g.n_tiles;
   const int per_xcd = ceil_div(total, kXcds);
@@ -1416,11 +1446,14 @@ hipError_t launch_grouped_gemm(const GemmLaunch& L, hipStream_t s) {
   g.a_index = L.a_index;
   const bool fp8_path = L.path == GEMM_LARGE_FP8 || L.path == GEMM_PIPELINED;
   if ((L.fp8 && !fp8_path) || (!L.fp8 && L.path == GEMM_LARGE_FP8)) return hipErrorInvalidValue;
+  if (L.gelu && (L.fp8 || L.swiglu)) return hipErrorInvalidValue;
   switch (L.path) {
     case GEMM_LARGE:
+      if (L.gelu) return launch_big<MODE_GELU>(g, L.max_tiles, s);
       return L.swiglu ? launch_big<MODE_SWIGLU>(g, L.max_tiles, s)
                       : launch_big<MODE_PLAIN>(g, L.max_tiles, s);
     case GEMM_SKINNY:
+      if (L.gelu) return launch_skinny<MODE_GELU>(g, L.max_tiles, s);
       return L.swiglu ? launch_skinny<MODE_SWIGLU>(g, L.max_tiles, s)
                       : launch_skinny<MODE_PLAIN>(g, L.max_tiles, s);
     case GEMM_LARGE_FP8:
@@ -1431,6 +1464,7 @@ hipError_t launch_grouped_gemm(const GemmLaunch& L, hipStream_t s) {
       break;
   }
   if (!L.fp8) {
+    if (L.gelu) return launch_pipelined<false, MODE_GELU>(g, L.max_tiles, s);
     return L.swiglu ? launch_pipelined<false, MODE_SWIGLU>(g, L.max_tiles, s)
                     : launch_pipelined<false, MODE_PLAIN>(g, L.max_tiles, s);
   }

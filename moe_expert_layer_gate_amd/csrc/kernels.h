@@ -54,7 +54,8 @@ hipError_t launch_schedule(const int32_t* offsets, int E_L, GemmPath path, int n
                            hipStream_t s);
 struct GemmLaunch {
   bool fp8;              // e4m3 operands with block scales, else bf16
-  bool swiglu;           // up GEMM with the SwiGLU epilogue, else plain
+  bool swiglu;           // up GEMM with the SwiGLU epilogue (W = gate and up rows)
+  bool gelu;             // up GEMM with the GELU epilogue (bf16); neither: plain
   const void* A;         // [N_cap, K] permuted activations
   const float* A_scale;  // fp8: [N_cap, K/128]
   const void* W;         // [E_L, NW, K]

@@ -34,6 +34,8 @@ moe_status check_problem(const moe_problem* p) {
   if (p->dtype != MOE_BF16 && p->dtype != MOE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
   if (p->layout & ~(MOE_LAYOUT_PANEL_WEIGHTS | MOE_LAYOUT_PANEL_ACTS)) return MOE_ERR_INVALID_ARG;
   if (p->layout && p->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (p->activation != MOE_ACT_SWIGLU && p->activation != MOE_ACT_GELU) return MOE_ERR_INVALID_ARG;
+  if (p->activation == MOE_ACT_GELU && p->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   // One expert's weight matrix must stay below 2 GiB (32-bit buffer offsets).
   if (4 * I * H >= (int64_t(1) << 31) || 4 * Is * H >= (int64_t(1) << 31))
     return MOE_ERR_UNSUPPORTED;
@@ -50,6 +52,7 @@ int64_t n_cap(const moe_problem* p) {
 }
 
 bool is_fp8(const moe_problem* p) { return p->dtype == MOE_FP8_E4M3; }
+bool is_gelu(const moe_problem* p) { return p->activation == MOE_ACT_GELU; }
 bool panel_weights(const moe_problem* p) { return p->layout & MOE_LAYOUT_PANEL_WEIGHTS; }
 bool panel_acts(const moe_problem* p) { return p->layout & MOE_LAYOUT_PANEL_ACTS; }
 
@@ -103,7 +106,7 @@ FfnShape ffn_shape(const moe_problem* p) {
   const int64_t N = n_cap(p);
   FfnShape f{};
   f.path = gemm_path(is_fp8(p), N / p->num_local);
-  f.nt_up = gemm_n_tiles(true, p->inter);
+  f.nt_up = gemm_n_tiles(!is_gelu(p), p->inter);
   f.nt_dn = gemm_n_tiles(false, p->hidden);
   f.cap_up = schedule_entries(N, p->num_local, f.path, f.nt_up);
   f.cap_dn = schedule_entries(N, p->num_local, f.path, f.nt_dn);
@@ -231,7 +234,8 @@ moe_status run_ffn(const moe_problem* p, const FfnSource& src, const int32_t* of
                           f.n_dn, s));
   GemmLaunch up{};
   up.fp8 = is_fp8(p);
-  up.swiglu = true;
+  up.swiglu = !is_gelu(p);
+  up.gelu = is_gelu(p);
   up.A = src.x;
   up.A_scale = src.x_scale;
   up.W = w->w13;
@@ -254,6 +258,7 @@ moe_status run_ffn(const moe_problem* p, const FfnSource& src, const int32_t* of
   MOE_TRY(launch_grouped_gemm(up, s));
   GemmLaunch down = up;
   down.swiglu = false;
+  down.gelu = false;
   down.A = hb;
   down.A_scale = hs;
   down.W = w->w2;

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libmoelayer.so")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_BF16, MOE_FP8_E4M3 = 0, 1
 LAYOUT_PANEL_WEIGHTS, LAYOUT_PANEL_ACTS = 1, 2
+ACT_SWIGLU, ACT_GELU = 0, 1
 STAGE_LAYER, STAGE_DISPATCH, STAGE_FFN = 0, 1, 2
 
 # Every function the header declares, with its ctypes signature.
@@ -29,7 +30,7 @@ class moe_problem(ctypes.Structure):
     _fields_ = [("num_tokens", _i32), ("hidden", _i32), ("num_experts", _i32),
                 ("top_k", _i32), ("expert_begin", _i32), ("num_local", _i32),
                 ("inter", _i32), ("shared_inter", _i32), ("dtype", _i32),
-                ("layout", _i32)]
+                ("layout", _i32), ("activation", _i32)]
 
 
 class moe_weights(ctypes.Structure):
@@ -95,10 +96,17 @@ class Problem:
     I_s: int = 0
     fp8: bool = False
     layout: int = 0   # LAYOUT_* bits
+    act: str = "swiglu"  # "swiglu" | "gelu"
 
     def c(self) -> moe_problem:
         return moe_problem(self.T, self.H, self.E, self.k, self.e_lo, self.E_L, self.I,
-                           self.I_s, MOE_FP8_E4M3 if self.fp8 else MOE_BF16, self.layout)
+                           self.I_s, MOE_FP8_E4M3 if self.fp8 else MOE_BF16, self.layout,
+                           ACT_GELU if self.act == "gelu" else ACT_SWIGLU)
+
+    @property
+    def m(self) -> int:
+        """First-layer matrices per expert (2 gated, 1 standard)."""
+        return 1 if self.act == "gelu" else 2
 
     @property
     def n_cap(self) -> int:
@@ -107,7 +115,7 @@ class Problem:
     @classmethod
     def from_config(cls, cfg, T: Optional[int] = None, layout: int = 0) -> "Problem":
         return cls(T=cfg.T if T is None else T, H=cfg.H, E=cfg.E, k=cfg.k, e_lo=cfg.e_lo,
-                   E_L=cfg.E_L, I=cfg.I, I_s=cfg.I_s, fp8=cfg.fp8, layout=layout)
+                   E_L=cfg.E_L, I=cfg.I, I_s=cfg.I_s, fp8=cfg.fp8, layout=layout, act=cfg.act)
 
 
 def _ptr(t) -> Optional[int]:

@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert ml.lib().moe_abi_version() == 2
+    assert ml.lib().moe_abi_version() == 3
     assert ml.status_str(0) == "MOE_OK"
     assert ml.status_str(3) == "MOE_ERR_WORKSPACE"
     assert ml.status_str(99) == "MOE_ERR_UNKNOWN"
@@ -180,3 +180,14 @@ def test_gather_ffn_argument_checks():
                           None) == ml.MOE_ERR_INVALID_ARG
     assert L.moe_dispatch(ctypes.byref(p), *([256] * 6), 264, None, None, 256, nd,
                           None) == ml.MOE_ERR_INVALID_ARG   # misaligned token_slot_row
+
+
+def test_activation_checks():
+    L = ml.lib()
+    base = dict(T=16, H=256, E=8, k=2, e_lo=0, E_L=8, I=256)
+    assert ml.workspace_bytes(ml.Problem(**base, act="gelu")) > 0
+    pc = ml.Problem(**base, act="gelu").c()
+    pc.activation = 2
+    assert L.moe_route(ctypes.byref(pc), 16, 16, 16, None) == ml.MOE_ERR_INVALID_ARG
+    pf = ml.Problem(**base, fp8=True, act="gelu").c()     # the standard MLP is bf16 only
+    assert L.moe_route(ctypes.byref(pf), 16, 16, 16, None) == ml.MOE_ERR_UNSUPPORTED

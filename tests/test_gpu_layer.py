@@ -69,7 +69,7 @@ def run_staged(torch, p, dev):
         xp, h = unpanel(xp, N, H), unpanel(h, N, I)
     shared = None
     if p.I_s > 0:
-        q = ml.Problem(T=T, H=H, E=1, k=1, e_lo=0, E_L=1, I=p.I_s, fp8=p.fp8,
+        q = ml.Problem(T=T, H=H, E=1, k=1, e_lo=0, E_L=1, I=p.I_s, fp8=p.fp8, act=p.act,
                        layout=p.layout & ml.LAYOUT_PANEL_WEIGHTS)
         off2 = torch.tensor([0, T], **i32)
         sw = (ml.weights_struct(dev["ws13_q"], dev["ws2_q"], None, None, dev["ws13_s"],
@@ -113,6 +113,12 @@ SMALL = {
     "skinny_ragged": (small_cfg(T=60, H=384, E=16, E_L=8, e_lo=0, k=4, I=384,
                                 logits="gumbel_zipf"), 15),
     "skinny_shard": (small_cfg(T=33, H=256, E=32, E_L=8, e_lo=8, k=8, I=640), 16),
+    # the standard GELU MLP (m = 1) through the three bf16 kernels, with a
+    # shared expert and odd n-tile counts (I / 256 = 1.5)
+    "gelu_large": (small_cfg(T=2048, H=384, E=8, E_L=8, k=2, I=384, act="gelu"), 18),
+    "gelu_pipelined": (small_cfg(T=300, H=256, E=8, E_L=8, k=2, I=640, I_s=256, act="gelu"), 19),
+    "gelu_skinny": (small_cfg(T=60, H=384, E=16, E_L=8, e_lo=0, k=4, I=384, act="gelu",
+                              logits="gumbel_zipf"), 20),
 }
 SMALL_FP8 = {
     "fp8_small": (small_cfg(T=200, H=512, E=16, E_L=8, e_lo=0, k=4, I=256, fp8=True), 8),
@@ -174,7 +180,7 @@ def check_small_case(name, cfg, d, dev):
     # agreement (the 6e-2 gate against the exact oracle is checked at the
     # workloads' own spreads below).
     ref = O.moe_layer(d["logits"], d["x"], ow.as_layer_dict(cfg.E_L), k=cfg.k, e_lo=cfg.e_lo,
-                      E_L=cfg.E_L, fp8=cfg.fp8, quantize_activations=cfg.fp8)
+                      E_L=cfg.E_L, fp8=cfg.fp8, quantize_activations=cfg.fp8, activation=cfg.act)
     # bf16: every row within 2e-2.  fp8: h is rounded to E4M3 on both sides,
     # from fp32 sums on the GPU and fp64 sums in the oracle, so an element
     # that sits on a rounding boundary can land one code apart (a 6-12 %
@@ -319,14 +325,15 @@ def sample_rows(offsets, rng, extra=24):
     return np.array(sorted(rows))
 
 
-@pytest.mark.parametrize("cid", [2, 3])
+@pytest.mark.parametrize("cid", [2, 3, "qwen3_30b_prefill_gelu"])
 def test_workload_full_size_sampled(cid):
     """Full-size bf16 workloads: routing and permutation exact over the
     whole batch; FFN rows and layer outputs on sampled rows/tokens."""
     torch = torch_cuda()
     ml, dv = _mods()
     cfg = synth.config(cid)
-    d, dev = upload(cfg, cid)
+    seed = cid if isinstance(cid, int) else 17
+    d, dev = upload(cfg, seed)
     p = ml.Problem.from_config(cfg)
     say("full size staged", cfg.name)
     st = run_staged(torch, p, dev)
@@ -337,7 +344,7 @@ def test_workload_full_size_sampled(cid):
     N = int(ix["offsets"][-1])
     np.testing.assert_array_equal(st["row_token"][:N].cpu().numpy(), ix["row_token"])
     np.testing.assert_array_equal(st["tsr"].cpu().numpy(), ix["token_slot_row"])
-    rng = np.random.default_rng(cid)
+    rng = np.random.default_rng(seed)
     rows = sample_rows(ix["offsets"], rng)
     x = O.bf16_to_f64(d["x"])
     ref_rows, got_rows = [], []
@@ -345,11 +352,13 @@ def test_workload_full_size_sampled(cid):
     for r, e in zip(rows, seg):
         w13 = O.bf16_to_f64(d["w13"][e])
         w2 = O.bf16_to_f64(d["w2"][e])
-        ref_rows.append(O.expert_ffn(x[ix["row_token"][r]][None], w13, w2)[1][0])
+        ref_rows.append(O.expert_ffn(x[ix["row_token"][r]][None], w13, w2,
+                                     activation=cfg.act)[1][0])
         got_rows.append(f64(st["y_perm"][int(r)])[None][0])
     e_yp = rel_rows(np.array(got_rows), np.array(ref_rows))
     toks = np.unique(np.concatenate([[0, cfg.T - 1], rng.integers(0, cfg.T, 30)]))
-    ref_y = O.moe_layer_tokens(d["logits"], d["x"], d, toks, k=cfg.k, e_lo=cfg.e_lo, E_L=cfg.E_L)
+    ref_y = O.moe_layer_tokens(d["logits"], d["x"], d, toks, k=cfg.k, e_lo=cfg.e_lo, E_L=cfg.E_L,
+                               activation=cfg.act)
     e_y = rel_rows(f64(st["y"][torch.from_numpy(toks).cuda()]), ref_y)
     print(f"{cfg.name}: y_perm rows {e_yp:.2e}  y tokens {e_y:.2e}")
     assert e_yp <= TOL_BF16 and e_y <= TOL_BF16

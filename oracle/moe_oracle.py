@@ -57,6 +57,15 @@ the design notes of the repository):
   The oracle's FP8 layer uses the dequantised weights (code * scale) as the
   layer's parameters and does not quantise x or h.
 * Shared expert: always on, weight 1, same SwiGLU form, added in combine.
+* Masked (fixed-capacity) layout, the decode-time alternative to the
+  contiguous one (the ExpertPlex page's masked grouped-GEMM layout; the
+  OverlapAdvisor page's Table 7, where the low-latency dispatch feeds the
+  GroupGEMM with no permute step, and Table 6 note b, low latency for small
+  batches): the pages give no capacity rule.  Reading: local expert e owns
+  the fixed row block [e*C, (e+1)*C) and its pairs fill the first counts[e]
+  rows, ascending token as in the contiguous layout; C >= every count (C >=
+  T always suffices, a token picks an expert at most once); unused rows
+  hold no pair.
 """
 from __future__ import annotations
 
@@ -67,6 +76,7 @@ import numpy as np
 __all__ = [
     "bf16_to_f64", "route", "index_build", "tile_count", "dispatch", "silu",
     "expert_ffn", "grouped_ffn", "combine", "moe_layer", "moe_layer_tokens",
+    "index_build_masked", "grouped_ffn_masked",
     "e4m3_value", "e4m3_encode", "quantize_blocks", "quantize_rows_groups",
     "dequantize_blocks", "fp8_activation", "E4M3_MAX",
 ]
@@ -265,6 +275,43 @@ def index_build(ids: np.ndarray, e_lo: int, E_L: int) -> Dict[str, np.ndarray]:
             "row_slot": row_slot, "token_slot_row": tsr.reshape(T, k)}
 
 
+def index_build_masked(ids: np.ndarray, e_lo: int, E_L: int,
+                       capacity: int) -> Dict[str, np.ndarray]:
+    """Masked (fixed-capacity) layout of the local (token, slot) pairs: the
+    ExpertPlex page's masked grouped-GEMM layout, fed without a permute step
+    (OverlapAdvisor Table 7, low-latency dispatch).
+
+    Local expert e owns rows [e * capacity, (e + 1) * capacity); its pairs
+    take the first counts[e] of them, tokens ascending.  Row r of that block
+    is therefore the r-th token, in token order, that picked expert e.
+
+    Returns counts [E_L], offsets [E_L + 1] (the block starts e * capacity),
+    row_token and row_slot [E_L * capacity] (-1 in rows that hold no pair)
+    and token_slot_row [T, k] (-1 where the expert is not local), int32.
+    Raises ValueError if an expert has more pairs than ``capacity``.
+    """
+    ids = np.asarray(ids, dtype=np.int64)
+    T, k = ids.shape
+    C = int(capacity)
+    row_token = np.full(E_L * C, -1, dtype=np.int32)
+    row_slot = np.full(E_L * C, -1, dtype=np.int32)
+    tsr = np.full((T, k), -1, dtype=np.int32)
+    counts = np.zeros(E_L, dtype=np.int32)
+    for e in range(E_L):
+        hit_t, hit_s = np.nonzero(ids == e_lo + e)    # row-major: tokens ascending
+        n = len(hit_t)
+        if n > C:
+            raise ValueError(f"expert {e} has {n} pairs, capacity {C}")
+        counts[e] = n
+        rows = e * C + np.arange(n)
+        row_token[rows] = hit_t
+        row_slot[rows] = hit_s
+        tsr[hit_t, hit_s] = rows
+    offsets = (np.arange(E_L + 1) * C).astype(np.int32)
+    return {"counts": counts, "offsets": offsets, "row_token": row_token,
+            "row_slot": row_slot, "token_slot_row": tsr}
+
+
 def tile_count(counts: np.ndarray, tile_m: int) -> int:
     """Tile-aware row count of the ExpertPlex page's Eq. 3: the number of
     tile_m-row tiles covering every expert that has tokens,
@@ -366,6 +413,35 @@ def grouped_ffn(x_perm: np.ndarray, offsets: np.ndarray, w13, w2, h_fn=None,
     return h_all, y_perm
 
 
+def grouped_ffn_masked(x_perm: np.ndarray, counts: np.ndarray, capacity: int,
+                       w13, w2, h_fn=None, activation: str = "swiglu"):
+    """Grouped FFN over the masked layout: rows [e * capacity,
+    e * capacity + counts[e]) run through local expert e; the other rows of
+    each block are not computed and stay zero.  Weights as in grouped_ffn.
+    Returns (h [E_L * capacity, I], y_perm [E_L * capacity, H])."""
+    E_L = len(counts)
+    C = int(capacity)
+    get13 = w13 if callable(w13) else (lambda e: w13[e])
+    get2 = w2 if callable(w2) else (lambda e: w2[e])
+    H = x_perm.shape[1]
+    h_all = None
+    y_perm = np.zeros((E_L * C, H), dtype=np.float64)
+    for e in range(E_L):
+        n = int(counts[e])
+        if n == 0:
+            continue
+        we13, we2 = get13(e), get2(e)
+        if h_all is None:
+            h_all = np.zeros((E_L * C, we2.shape[1]), dtype=np.float64)
+        a = e * C
+        h, y = expert_ffn(x_perm[a:a + n], we13, we2, h_fn, activation)
+        h_all[a:a + n] = h
+        y_perm[a:a + n] = y
+    if h_all is None:
+        h_all = np.zeros((E_L * C, 0), dtype=np.float64)
+    return h_all, y_perm
+
+
 def combine(y_perm: np.ndarray, token_slot_row: np.ndarray, w: np.ndarray,
             shared: Optional[np.ndarray] = None, H: Optional[int] = None) -> np.ndarray:
     """Unpermute and weighted combine (CascadeEP Appendix C, "Output return
@@ -423,7 +499,8 @@ def fp8_activation(a: np.ndarray) -> np.ndarray:
 def moe_layer(logits: np.ndarray, x_bits: np.ndarray, weights: dict, *,
               k: int, e_lo: int, E_L: int, fp8: bool = False,
               quantize_activations: bool = False,
-              activation: str = "swiglu") -> Dict[str, np.ndarray]:
+              activation: str = "swiglu",
+              capacity: Optional[int] = None) -> Dict[str, np.ndarray]:
     """The whole layer for one GPU's local experts, every stage kept.
 
     ``weights``: bf16 -> "w13" [E_L, m*I, H] (m = 2 for SwiGLU, 1 for the
@@ -437,19 +514,32 @@ def moe_layer(logits: np.ndarray, x_bits: np.ndarray, weights: dict, *,
     activation and quantisation operations between the two expert GEMMs).
     The default leaves them exact: the reference the output gate measures.
 
+    ``capacity`` (optional) runs the layer over the masked fixed-capacity
+    layout (index_build_masked / grouped_ffn_masked) instead of the
+    contiguous one; the stage arrays are then in that layout.
+
     Returns every stage: ids, w, counts, offsets, row_token, row_slot,
     token_slot_row, x_perm, h, y_perm, shared (or None) and y, as float64
     for the floating-point ones (h before its own quantisation).
     """
     ids, w = route(logits, k)
-    ix = index_build(ids, e_lo, E_L)
+    masked = capacity is not None
+    ix = index_build_masked(ids, e_lo, E_L, capacity) if masked else index_build(ids, e_lo, E_L)
     x = bf16_to_f64(x_bits)
     qa = fp8 and quantize_activations
     xq = fp8_activation(x) if qa else x
-    x_perm = dispatch(xq, ix["row_token"])
+    if masked:                                   # unused rows of a block stay zero
+        x_perm = np.zeros((len(ix["row_token"]), x.shape[1]), dtype=np.float64)
+        used = ix["row_token"] >= 0
+        x_perm[used] = dispatch(xq, ix["row_token"][used])
+    else:
+        x_perm = dispatch(xq, ix["row_token"])
     g13, g2 = _expert_weights(weights, fp8)
     h_fn = fp8_activation if qa else None
-    h, y_perm = grouped_ffn(x_perm, ix["offsets"], g13, g2, h_fn, activation)
+    if masked:
+        h, y_perm = grouped_ffn_masked(x_perm, ix["counts"], capacity, g13, g2, h_fn, activation)
+    else:
+        h, y_perm = grouped_ffn(x_perm, ix["offsets"], g13, g2, h_fn, activation)
     sw = _shared_weights(weights, fp8)
     shared = None
     if sw is not None:

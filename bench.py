@@ -41,6 +41,9 @@ def parse():
                     help="bf16 storage: panel = weights packed once at load time and panel "
                          "activations in the staged calls (moe_layer always keeps its own "
                          "activations in panel layout); rows = everything row major")
+    ap.add_argument("--masked", action="store_true",
+                    help="masked fixed-capacity expert layout (capacity = tokens) instead of "
+                         "contiguous segments")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="finish with three 1 GiB device copies (a known-size reference "
                          "for the FETCH_SIZE / WRITE_SIZE counters)")
@@ -73,16 +76,16 @@ def stored_traffic(workload: str):
     return rec.get("bytes_per_launch")
 
 
-def gemm_rows(counts, fp8: bool, n_cap: int, E_L: int) -> int:
+def gemm_rows(counts, fp8: bool, max_pairs: int, E_L: int) -> int:
     """Token rows the GEMMs compute, padding included, under the library's
-    tile choice: bf16 32-row tiles for up to 32 rows per expert on average;
-    128-row tiles up to 256; else 256-row tiles (bf16: a last remainder of
-    1..128 rows takes a 128-row wide tile)."""
+    tile choice (from the most pairs per expert on average, T min(k, E_L) /
+    E_L): bf16 32-row tiles up to 32; 128-row tiles up to 256; else 256-row
+    tiles (bf16: a last remainder of 1..128 rows takes a 128-row wide tile)."""
     rows = 0
     for c in (int(x) for x in counts):
-        if not fp8 and n_cap // E_L <= 32:
+        if not fp8 and max_pairs // E_L <= 32:
             rows += -(-c // 32) * 32
-        elif n_cap // E_L <= 256:
+        elif max_pairs // E_L <= 256:
             rows += -(-c // 128) * 128
         elif fp8:
             rows += -(-c // 256) * 256
@@ -114,9 +117,12 @@ def main():
     panel = args.layout == "panel" and not cfg.fp8
     dev = dv.upload(d, cfg.fp8, panel=panel)   # load-time packing, outside any timing
     # Layouts of moe_layer's own path: panel weights as loaded, panel h.
+    cap = cfg.T if args.masked else 0
     p = ml.Problem.from_config(
-        cfg, layout=(ml.LAYOUT_PANEL_WEIGHTS | ml.LAYOUT_PANEL_ACTS) if panel else 0)
-    p_layer = ml.Problem.from_config(cfg, layout=ml.LAYOUT_PANEL_WEIGHTS if panel else 0)
+        cfg, layout=(ml.LAYOUT_PANEL_WEIGHTS | ml.LAYOUT_PANEL_ACTS) if panel else 0,
+        capacity=cap)
+    p_layer = ml.Problem.from_config(cfg, layout=ml.LAYOUT_PANEL_WEIGHTS if panel else 0,
+                                     capacity=cap)
     W = dv.weights_of(dev, cfg.fp8)
     stream = torch.cuda.current_stream()
     T, k, H, N = p.T, p.k, p.H, p.n_cap
@@ -142,6 +148,8 @@ def main():
             shared = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
             ws_s = dv.workspace(q, ml.STAGE_FFN)
 
+    seg = counts if cap else offsets   # segment table of the FFN calls (masked: counts)
+
     # One step: moe_layer's kernels, one library call per stage, so that the
     # grouped FFN's launches inside the timed region can be bracketed with
     # HIP events on the stream they run on.  bf16: route, index-only
@@ -157,13 +165,13 @@ def main():
             ml.moe_dispatch(p, dev["x"], ids, counts, offsets, rt, rs, tsr, None, None, ws_d,
                             stream)
             rec(2)
-            ml.moe_grouped_ffn_gather(p, dev["x"], rt, offsets, W, None, yp, ws_f, stream)
+            ml.moe_grouped_ffn_gather(p, dev["x"], rt, seg, W, None, yp, ws_f, stream)
             rec(3)
             sh = None
         else:
             ml.moe_dispatch(p, dev["x"], ids, counts, offsets, rt, rs, tsr, xp, xs, ws_d, stream)
             rec(2)
-            ml.moe_grouped_ffn(p, xp, xs, offsets, W, None, None, yp, ws_f, stream)
+            ml.moe_grouped_ffn(p, xp, xs, seg, W, None, None, yp, ws_f, stream)
             sh = None
             if p.I_s:
                 ml.moe_quantize_fp8(dev["x"], 1, T, H, 1, sx, sxs, stream)
@@ -203,8 +211,8 @@ def main():
     torch.cuda.synchronize()
     layer_tps = T * args.steps / (time.perf_counter() - t1)
 
-    n_pairs = int(offsets[-1].item())
     cnt = counts.cpu().numpy()
+    n_pairs = int(cnt.sum())
     # 2 m H I (up, m first-layer matrices) + 2 H I (down) per row (Eq. 8)
     mm = 2.0 * (p.m + 1)
     flops = mm * p.H * p.I * n_pairs + mm * p.H * p.I_s * p.T
@@ -212,10 +220,13 @@ def main():
     beta_w = 1 if cfg.fp8 else 2
     active = int((cnt > 0).sum())
     ffn_tflops = flops / (ffn_ms * 1e-3) / 1e12
-    padded_rows = gemm_rows(cnt, cfg.fp8, p.n_cap, p.E_L)
+    padded_rows = gemm_rows(cnt, cfg.fp8, p.T * min(p.k, p.E_L), p.E_L)
 
-    traffic = stored_traffic(cfg.name)
-    kernel = ("grouped FFN: work table + up GEMM/SwiGLU + down GEMM"
+    traffic = stored_traffic(cfg.name + ("_masked" if cap else ""))
+    act = "SwiGLU" if cfg.act == "swiglu" else "GELU"
+    skinny = not cfg.fp8 and p.T * min(p.k, p.E_L) // p.E_L <= 32
+    kernel = ((f"grouped FFN: work table + one launch of up GEMM/{act} and down GEMM" if skinny
+               else f"grouped FFN: work table + up GEMM/{act} + down GEMM")
               + (" (+ shared expert: x quantisation and its FFN)" if p.I_s else ""))
     # Few rows per expert: the FFN streams weights and is bound by HBM.
     decode = n_pairs < 64 * max(active, 1)
@@ -262,7 +273,8 @@ def main():
                    "local_experts": cfg.E_L, "expert_begin": cfg.e_lo, "top_k": cfg.k,
                    "inter": cfg.I, "shared_inter": cfg.I_s, "seed": seed,
                    "mlp": "gated SwiGLU" if cfg.act == "swiglu" else "standard GELU",
-                   "layout": "panel" if panel else "rows"},
+                   "layout": "panel" if panel else "rows",
+                   "expert_layout": f"masked (capacity {cap})" if cap else "contiguous"},
         "grouped_ffn_tflops": round(ffn_tflops, 2),
         "grouped_ffn_frac_of_peak": round(ffn_tflops / PEAK_TFLOPS[dtype], 4),
         "stage_ms": {k2: round(v, 4) for k2, v in stage_ms.items()},

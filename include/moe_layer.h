@@ -33,8 +33,9 @@
  *  - num_tokens == 0 is valid: MOE_OK, nothing enqueued.
  *  - Logits must be finite (NaN/Inf logits give unspecified, but in-bounds,
  *    routing).
- *  - Capacity: the permuted buffers hold N_cap = T * min(k, E_L) rows; the
- *    number of valid rows is offsets[E_L] on the device.
+ *  - Capacity: the permuted buffers hold N_cap rows: T * min(k, E_L) in the
+ *    contiguous layout (the number of valid rows is offsets[E_L] on the
+ *    device), E_L * capacity in the masked layout (moe_problem.capacity).
  *
  * Supported sizes: 1 <= E <= 1024, 1 <= k <= min(E, 32), 1 <= E_L <= 1024,
  * 0 <= e_lo, e_lo + E_L <= E, 0 <= T <= 2^24, H % 128 == 0, I % 128 == 0
@@ -52,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 typedef enum {
   MOE_OK = 0,
@@ -111,7 +112,21 @@ typedef struct {
   int32_t layout;        /* MOE_LAYOUT_* bits, 0 = all row major; must be 0
                             for MOE_FP8_E4M3                                   */
   int32_t activation;    /* MOE_ACT_SWIGLU (0) or MOE_ACT_GELU                 */
+  int32_t capacity;      /* 0: contiguous expert segments.  C > 0: masked
+                            fixed-capacity layout (see below); C >= T,
+                            C <= 2^24, E_L * C < 2^31                         */
 } moe_problem;
+
+/* Masked (fixed-capacity) layout, moe_problem.capacity = C > 0.  Page
+ * "ExpertPlex": masked grouped-GEMM layout; page "OverlapAdvisor ...",
+ * Table 7 and Table 6 note b: the low-latency dispatch used for small batches
+ * feeds the GroupGEMM with no permute step.  Local expert e owns the rows
+ * [e C, (e + 1) C) of x_perm, h and y_perm, and its counts[e] pairs fill the
+ * first counts[e] of them, tokens ascending (the same order as in the
+ * contiguous layout, so every per-row result is the same); the other rows
+ * are neither read nor written.  Buffers keep one shape for every T <= C.
+ * Where a call takes the segment table of the grouped FFN, the masked layout
+ * passes counts [E_L] (from moe_dispatch) instead of offsets.              */
 
 /* Expert weights, device pointers, K-contiguous ("[out, in]" row major).
  *   w13  [E_L, m I, H]: SwiGLU (m = 2): rows 0..I-1 gate projection, rows
@@ -157,16 +172,17 @@ moe_status moe_route(const moe_problem* p, const float* logits,
  *              is ignored (treated as non-local).
  *   counts     [E_L] int32: local pairs per local expert
  *   offsets    [E_L + 1] int32: exclusive scan of counts; N = offsets[E_L]
+ *              (masked layout: the block starts e C, offsets[E_L] = E_L C)
  *   row_token  [N_cap] int32, row_slot [N_cap] int32: token and slot of row j
- *              (rows j >= N are left untouched)
+ *              (rows holding no pair are left untouched)
  *   token_slot_row [T, k] int32: row of pair (t, s), -1 if not local
  *   x_perm     [N_cap, H]: row j = x[row_token[j]]; bf16, or for
  *              MOE_FP8_E4M3 the E4M3 codes of that row with
  *   x_perm_scale [N_cap, H/128] fp32 (fp8 only; NULL for bf16): scale of each
  *              128-element group, amax/448 (1 for an all-zero group); code =
  *              round-to-nearest-even(v / scale) saturated to +-448.
- * Rows are ordered by local expert, then by token.  Bit-exact and
- * deterministic.  x_perm == NULL builds the index only (x_perm_scale is then
+ * Rows are ordered by local expert, then by token (contiguous segments, or
+ * the expert's block in the masked layout).  Bit-exact and deterministic.  x_perm == NULL builds the index only (x_perm_scale is then
  * ignored; see moe_grouped_ffn_gather).
  * Workspace: moe_workspace_bytes(p, MOE_STAGE_DISPATCH).                   */
 moe_status moe_dispatch(const moe_problem* p, const void* x,
@@ -181,17 +197,20 @@ moe_status moe_dispatch(const moe_problem* p, const void* x,
  * down GroupGEMM 2 H I), Table 6 (gated SwiGLU; standard MLP with GELU);
  * page "CascadeEP ...", Appendix C (the two expert GEMMs with the activation
  * and quantisation between them, in stream order).
- * For every local expert e and row j in [offsets[e], offsets[e+1]):
+ * For every local expert e and row j of its segment, [offsets[e],
+ * offsets[e+1]) (masked layout: [e C, e C + counts[e]), with `offsets`
+ * carrying counts [E_L]):
  *   SwiGLU: h[j] = silu(x_perm[j] . W_gate,e^T) * (x_perm[j] . W_up,e^T) [I]
  *   GELU:   h[j] = gelu(x_perm[j] . W1_e^T)                              [I]
  *   y_perm[j] = h[j] . W2_e^T                                          [H]
  * with fp32 accumulation (see MOE_ACT_*).
- *   x_perm, x_perm_scale, offsets: as produced by moe_dispatch
+ *   x_perm, x_perm_scale, offsets: as produced by moe_dispatch (counts for
+ *              the masked layout)
  *   h          [N_cap, I] (optional, NULL = kept in the workspace): bf16,
  *              or E4M3 with h_scale [N_cap, I/128] fp32 for MOE_FP8_E4M3
  *   y_perm     [N_cap, H] bf16 (output)
  * Routing weights are NOT applied here (moe_combine applies them).
- * Only rows j < offsets[E_L] are read or written.  With E_L = 1 and
+ * Only the segments' rows are read or written.  With E_L = 1 and
  * offsets = {0, T} this is a dense SwiGLU FFN (how a shared expert is run).
  * Workspace: moe_workspace_bytes(p, MOE_STAGE_FFN).                        */
 moe_status moe_grouped_ffn(const moe_problem* p, const void* x_perm,
@@ -205,7 +224,8 @@ moe_status moe_grouped_ffn(const moe_problem* p, const void* x_perm,
  * of moe_grouped_ffn).  Together with moe_dispatch(..., x_perm = NULL, ...)
  * this is the bf16 path of moe_layer, kernel for kernel: the permuted
  * activations are never written.
- *   x [T, H] bf16 row major, row_token [N_cap] (from moe_dispatch), offsets,
+ *   x [T, H] bf16 row major, row_token [N_cap] (from moe_dispatch), offsets
+ *   (counts for the masked layout),
  *   w, h (optional, as in moe_grouped_ffn, layout per MOE_LAYOUT_PANEL_ACTS),
  *   y_perm [N_cap, H] bf16 (output).
  * MOE_ERR_UNSUPPORTED for MOE_FP8_E4M3 and for x of 2 GiB or more.

@@ -7,7 +7,9 @@
 // is added.  Page "OverlapAdvisor ...", section 4.2.1: unpermute restores the
 // token order.
 //
-// One wavefront per token gathers the token's (at most k) expert rows through
+// wpt wavefronts per token (one for large batches; for small ones, such as
+// decode, enough to give the chip thousands of waves with one or two 16-byte
+// chunks per lane each) gather the token's (at most k) expert rows through
 // the inverse map -- a gather, not a scatter-add, so no atomics and a
 // deterministic result.  Each lane accumulates 8 columns at a time in fp32, in
 // slot order, and rounds to bf16 once.  All accesses are 16 bytes wide.
@@ -33,8 +35,9 @@ template <int KMAX>
 __global__ __launch_bounds__(256) void combine_kernel(
     const uint4* __restrict__ y_perm, const int32_t* __restrict__ token_slot_row,
     const float* __restrict__ topk_w, const uint4* __restrict__ shared_out, int T, int k,
-    int chunks, uint4* __restrict__ y) {
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    int chunks, int wpt, uint4* __restrict__ y) {
+  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int t = gw / wpt, part = gw - t * wpt;
   if (t >= T) return;
   const int lane = lane_id();
   // Slot rows and weights of this token: lane s < k holds slot s.
@@ -53,7 +56,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
       ws[s] = __shfl(my_w, s);
     }
   }
-  for (int c = lane; c < chunks; c += kWave) {
+  for (int c = part * kWave + lane; c < chunks; c += wpt * kWave) {
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
@@ -102,9 +105,15 @@ hipError_t launch_combine(const void* y_perm, const int32_t* token_slot_row, con
                           const void* shared_out, int T, int k, int H, void* y, hipStream_t s) {
   auto kern = k <= 2 ? combine_kernel<2> : k <= 4 ? combine_kernel<4> : k <= 8 ? combine_kernel<8>
                                                                              : combine_kernel<0>;
-  hipLaunchKernelGGL(kern, dim3(ceil_div(T, 4)), dim3(256), 0, s,
-                     static_cast<const uint4*>(y_perm), token_slot_row, topk_w,
-                     static_cast<const uint4*>(shared_out), T, k, H / 8, static_cast<uint4*>(y));
+  const int chunks = H / 8;
+  const int per_row = ceil_div(chunks, kWave);          // 64-lane passes over one row
+  const int want = ceil_div(4096, T);                   // waves per token for ~4096 waves
+  const int wpt = want < 1 ? 1 : (want < per_row ? want : per_row);
+  const int64_t waves = static_cast<int64_t>(T) * wpt;
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(ceil_div<int64_t>(waves, 4))), dim3(256), 0,
+                     s, static_cast<const uint4*>(y_perm), token_slot_row, topk_w,
+                     static_cast<const uint4*>(shared_out), T, k, chunks, wpt,
+                     static_cast<uint4*>(y));
   return hipGetLastError();
 }
 

@@ -22,6 +22,15 @@
 // A slot that repeats an expert already picked by an earlier slot of the
 // same token is skipped, which keeps every (token, expert) at most once and so
 // every position in range whatever ids the caller passes.
+// Up to 256 tokens (decode batches) the three steps run in one block and one
+// launch.
+//
+// Masked (fixed-capacity) layout, cap > 0 (page "ExpertPlex": masked grouped-
+// GEMM layout; page "OverlapAdvisor ...", Table 7: low-latency dispatch feeds
+// the GroupGEMM with no permute step): expert e's rows start at e * cap instead
+// of at the scan of the counts; everything else is the same sort, so a row's
+// rank inside its expert, and hence every per-row result, is the same in both
+// layouts.
 #include "common.h"
 #include "kernels.h"
 
@@ -71,7 +80,7 @@ __global__ __launch_bounds__(kTokBlock) void index_count_kernel(
 }
 
 __global__ __launch_bounds__(1024) void index_scan_kernel(
-    const int32_t* __restrict__ blk_hist, int nblk, int E_L,
+    const int32_t* __restrict__ blk_hist, int nblk, int E_L, int cap,
     int32_t* __restrict__ blk_base, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets) {
   // E_L <= 1024 = blockDim.x: one expert per thread.
@@ -88,9 +97,59 @@ __global__ __launch_bounds__(1024) void index_scan_kernel(
   const int off = block_exclusive_scan(e < E_L ? run : 0, &total);
   if (e < E_L) {
     counts[e] = run;
-    offsets[e] = off;
+    offsets[e] = cap ? e * cap : off;
   }
-  if (e == 0) offsets[E_L] = total;
+  if (e == 0) offsets[E_L] = cap ? E_L * cap : total;
+}
+
+// Rank of token slot t (bit t % 256 of the block) among the block's tokens
+// that picked the expert whose mask starts at m.
+__device__ __forceinline__ int mask_rank(const uint32_t* m, int tb) {
+  const int wi = tb >> 5;
+  int rank = __popc(m[wi] & ((1u << (tb & 31)) - 1u));
+  for (int w = 0; w < wi; ++w) rank += __popc(m[w]);
+  return rank;
+}
+
+// Count, scan and scatter of at most 256 tokens in one block of 1024 threads
+// (thread e < E_L owns expert e in the scan; thread t < T owns token t).
+__global__ __launch_bounds__(1024) void index_small_kernel(
+    const int32_t* __restrict__ topk_ids, int T, int k, int e_lo, int E_L, int cap,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ row_token, int32_t* __restrict__ row_slot,
+    int32_t* __restrict__ token_slot_row) {
+  extern __shared__ uint32_t mask[];
+  int* s_off = reinterpret_cast<int*>(mask + E_L * kMaskWords);
+  build_masks(mask, topk_ids, T, k, e_lo, E_L, 0);
+  const int e = threadIdx.x;
+  int c = 0;
+  if (e < E_L)
+#pragma unroll
+    for (int w = 0; w < kMaskWords; ++w) c += __popc(mask[e * kMaskWords + w]);
+  int total;
+  const int off = block_exclusive_scan(c, &total);
+  if (e < E_L) {
+    const int o = cap ? e * cap : off;
+    counts[e] = c;
+    offsets[e] = o;
+    s_off[e] = o;
+  }
+  if (e == 0) offsets[E_L] = cap ? E_L * cap : total;
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t >= T) return;
+  int32_t ids[32];
+  for (int s = 0; s < k; ++s) ids[s] = topk_ids[static_cast<size_t>(t) * k + s];
+  for (int s = 0; s < k; ++s) {
+    const int le = local_expert(ids, s, e_lo, E_L);
+    int pos = -1;
+    if (le >= 0) {
+      pos = s_off[le] + mask_rank(mask + le * kMaskWords, t);
+      row_token[pos] = t;
+      row_slot[pos] = s;
+    }
+    token_slot_row[static_cast<size_t>(t) * k + s] = pos;
+  }
 }
 
 __global__ __launch_bounds__(kTokBlock) void index_scatter_kernel(
@@ -102,18 +161,14 @@ __global__ __launch_bounds__(kTokBlock) void index_scatter_kernel(
   build_masks(mask, topk_ids, T, k, e_lo, E_L, blockIdx.x);
   const int t = blockIdx.x * kTokBlock + threadIdx.x;
   if (t >= T) return;
-  const int wi = threadIdx.x >> 5;
-  const uint32_t below = (1u << (threadIdx.x & 31)) - 1u;
   int32_t ids[32];
   for (int s = 0; s < k; ++s) ids[s] = topk_ids[static_cast<size_t>(t) * k + s];
   for (int s = 0; s < k; ++s) {
     const int e = local_expert(ids, s, e_lo, E_L);
     int pos = -1;
     if (e >= 0) {
-      const uint32_t* m = mask + e * kMaskWords;
-      int rank = __popc(m[wi] & below);
-      for (int w = 0; w < wi; ++w) rank += __popc(m[w]);
-      pos = offsets[e] + blk_base[static_cast<size_t>(blockIdx.x) * E_L + e] + rank;
+      pos = offsets[e] + blk_base[static_cast<size_t>(blockIdx.x) * E_L + e] +
+            mask_rank(mask + e * kMaskWords, threadIdx.x);
       row_token[pos] = t;
       row_slot[pos] = s;
     }
@@ -121,15 +176,25 @@ __global__ __launch_bounds__(kTokBlock) void index_scatter_kernel(
   }
 }
 
+// Whether row j of a masked layout (cap > 0) holds a pair: the first
+// counts[e] rows of expert e's block [e cap, (e + 1) cap) do.
+__device__ __forceinline__ bool masked_row_used(const int32_t* counts, int cap, int j) {
+  if (!cap) return true;
+  const int e = j / cap;
+  return j - e * cap < counts[e];
+}
+
 // Row gather of bf16 activations: dst[j] = src[rows[j]] for j < *n_rows
-// (rows == nullptr: identity).  One wavefront per row, 16-byte accesses.
+// (rows == nullptr: identity), skipping unused rows of a masked layout.  One
+// wavefront per row, 16-byte accesses.
 __global__ __launch_bounds__(256) void gather_rows_bf16_kernel(
     const uint4* __restrict__ src, const int32_t* __restrict__ rows,
     const int32_t* __restrict__ n_rows, int n_rows_host, int chunks_per_row,
-    uint4* __restrict__ dst) {
+    const int32_t* __restrict__ counts, int cap, uint4* __restrict__ dst) {
   const int n = n_rows ? *n_rows : n_rows_host;
   const int wpb = blockDim.x >> 6;
   for (int j = blockIdx.x * wpb + (threadIdx.x >> 6); j < n; j += gridDim.x * wpb) {
+    if (!masked_row_used(counts, cap, j)) continue;  // uniform over the wave
     const int r = rows ? rows[j] : j;
     const uint4* s = src + static_cast<size_t>(r) * chunks_per_row;
     uint4* d = dst + static_cast<size_t>(j) * chunks_per_row;
@@ -145,7 +210,7 @@ __global__ __launch_bounds__(256) void gather_rows_bf16_kernel(
 __global__ __launch_bounds__(256) void gather_rows_panel_kernel(
     const uint4* __restrict__ src, const int32_t* __restrict__ rows,
     const int32_t* __restrict__ n_rows, int n_rows_host, int chunks_per_row,
-    int64_t panel_rows, uint4* __restrict__ dst) {
+    int64_t panel_rows, const int32_t* __restrict__ counts, int cap, uint4* __restrict__ dst) {
   constexpr int kPanelsPerItem = 8;
   const int n = n_rows ? *n_rows : n_rows_host;
   const int wpb = blockDim.x >> 6;
@@ -158,7 +223,7 @@ __global__ __launch_bounds__(256) void gather_rows_panel_kernel(
     const int grp = static_cast<int>(it / pblocks);
     const int p0 = static_cast<int>(it - static_cast<int64_t>(grp) * pblocks) * kPanelsPerItem;
     const int j = grp * 16 + (lane >> 2);
-    if (j >= n) continue;
+    if (j >= n || !masked_row_used(counts, cap, j)) continue;
     const int r = rows ? rows[j] : j;
     const uint4* s = src + static_cast<size_t>(r) * chunks_per_row + sub;
     uint4* d = dst + static_cast<size_t>(j) * 4 + sub;
@@ -198,6 +263,7 @@ __global__ __launch_bounds__(256) void pack_panel_kernel(const uint4* __restrict
 __global__ __launch_bounds__(256) void gather_rows_fp8_kernel(
     const uint4* __restrict__ src, const int32_t* __restrict__ rows,
     const int32_t* __restrict__ n_rows, int n_rows_host, int H,
+    const int32_t* __restrict__ counts, int cap,
     uint2* __restrict__ dst, float* __restrict__ dst_scale) {
   const int n = n_rows ? *n_rows : n_rows_host;
   const int chunks = H >> 3;  // 8 bf16 per chunk
@@ -205,6 +271,7 @@ __global__ __launch_bounds__(256) void gather_rows_fp8_kernel(
   const int wpb = blockDim.x >> 6;
   const int lane = lane_id();
   for (int j = blockIdx.x * wpb + (threadIdx.x >> 6); j < n; j += gridDim.x * wpb) {
+    if (!masked_row_used(counts, cap, j)) continue;  // uniform over the wave
     const int r = rows ? rows[j] : j;
     const uint4* s = src + static_cast<size_t>(r) * chunks;
     uint2* d = dst + static_cast<size_t>(j) * chunks;
@@ -294,10 +361,16 @@ size_t index_scratch_bytes(int T, int E_L) {
   return 2 * nblk * static_cast<size_t>(E_L) * sizeof(int32_t);
 }
 
-hipError_t launch_index_build(const int32_t* topk_ids, int T, int k, int e_lo, int E_L,
+hipError_t launch_index_build(const int32_t* topk_ids, int T, int k, int e_lo, int E_L, int cap,
                               int32_t* counts, int32_t* offsets, int32_t* row_token,
                               int32_t* row_slot, int32_t* token_slot_row,
                               void* scratch, hipStream_t s) {
+  if (T <= kTokBlock) {
+    const size_t lds = static_cast<size_t>(E_L) * (kMaskWords + 1) * sizeof(uint32_t);
+    hipLaunchKernelGGL(index_small_kernel, dim3(1), dim3(1024), lds, s, topk_ids, T, k, e_lo, E_L,
+                       cap, counts, offsets, row_token, row_slot, token_slot_row);
+    return hipGetLastError();
+  }
   const int nblk = ceil_div(T, kTokBlock);
   int32_t* blk_hist = static_cast<int32_t*>(scratch);
   int32_t* blk_base = blk_hist + static_cast<size_t>(nblk) * E_L;
@@ -305,7 +378,7 @@ hipError_t launch_index_build(const int32_t* topk_ids, int T, int k, int e_lo, i
   hipLaunchKernelGGL(index_count_kernel, dim3(nblk), dim3(kTokBlock), lds, s,
                      topk_ids, T, k, e_lo, E_L, blk_hist);
   hipLaunchKernelGGL(index_scan_kernel, dim3(1), dim3(1024), 0, s,
-                     blk_hist, nblk, E_L, blk_base, counts, offsets);
+                     blk_hist, nblk, E_L, cap, blk_base, counts, offsets);
   hipLaunchKernelGGL(index_scatter_kernel, dim3(nblk), dim3(kTokBlock), lds, s,
                      topk_ids, T, k, e_lo, E_L, blk_base, offsets, row_token, row_slot,
                      token_slot_row);
@@ -319,16 +392,17 @@ static int gather_grid(int64_t max_rows) {
 
 hipError_t launch_gather_bf16(const void* src, const int32_t* rows, const int32_t* n_rows,
                               int64_t max_rows, int H, void* dst, int64_t panel_rows,
-                              hipStream_t s) {
+                              hipStream_t s, const int32_t* counts, int cap) {
   if (panel_rows > 0)
     hipLaunchKernelGGL(gather_rows_panel_kernel,
                        dim3(gather_grid((max_rows + 15) / 16 * ((H / 32 + 7) / 8))),
                        dim3(256), 0, s, static_cast<const uint4*>(src), rows, n_rows,
-                       static_cast<int>(max_rows), H / 8, panel_rows, static_cast<uint4*>(dst));
+                       static_cast<int>(max_rows), H / 8, panel_rows, counts, cap,
+                       static_cast<uint4*>(dst));
   else
     hipLaunchKernelGGL(gather_rows_bf16_kernel, dim3(gather_grid(max_rows)), dim3(256), 0, s,
                        static_cast<const uint4*>(src), rows, n_rows, static_cast<int>(max_rows),
-                       H / 8, static_cast<uint4*>(dst));
+                       H / 8, counts, cap, static_cast<uint4*>(dst));
   return hipGetLastError();
 }
 
@@ -344,10 +418,10 @@ hipError_t launch_pack_panel(const void* src, int64_t batch, int64_t rows, int64
 
 hipError_t launch_gather_fp8(const void* src, const int32_t* rows, const int32_t* n_rows,
                              int64_t max_rows, int H, void* dst, float* dst_scale,
-                             hipStream_t s) {
+                             hipStream_t s, const int32_t* counts, int cap) {
   hipLaunchKernelGGL(gather_rows_fp8_kernel, dim3(gather_grid(max_rows)), dim3(256), 0, s,
                      static_cast<const uint4*>(src), rows, n_rows, static_cast<int>(max_rows), H,
-                     static_cast<uint2*>(dst), dst_scale);
+                     counts, cap, static_cast<uint2*>(dst), dst_scale);
   return hipGetLastError();
 }
 

@@ -12,21 +12,26 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* 
                              hipStream_t s);
 
 size_t index_scratch_bytes(int T, int E_L);
-hipError_t launch_index_build(const int32_t* topk_ids, int T, int k, int e_lo, int E_L,
+// cap == 0: contiguous layout (offsets = exclusive scan of counts); cap > 0:
+// masked layout, expert e's rows start at e * cap (offsets[e] = e * cap).
+hipError_t launch_index_build(const int32_t* topk_ids, int T, int k, int e_lo, int E_L, int cap,
                               int32_t* counts, int32_t* offsets, int32_t* row_token,
                               int32_t* row_slot, int32_t* token_slot_row, void* scratch,
                               hipStream_t s);
 // dst[j] = src[rows[j]] (rows == nullptr: identity) for j < *n_rows, or for
 // j < max_rows when n_rows == nullptr.
-// With panel_rows > 0, dst is in panel layout [H/32][panel_rows][32].
+// With panel_rows > 0, dst is in panel layout [H/32][panel_rows][32].  With
+// cap > 0, rows of a masked layout that hold no pair (past counts[e] in expert
+// e's block) are skipped.
 hipError_t launch_gather_bf16(const void* src, const int32_t* rows, const int32_t* n_rows,
                               int64_t max_rows, int H, void* dst, int64_t panel_rows,
-                              hipStream_t s);
+                              hipStream_t s, const int32_t* counts = nullptr, int cap = 0);
 // bf16 [batch][rows][cols] row major -> [batch][cols/32][rows][32].
 hipError_t launch_pack_panel(const void* src, int64_t batch, int64_t rows, int64_t cols,
                              void* dst, hipStream_t s);
 hipError_t launch_gather_fp8(const void* src, const int32_t* rows, const int32_t* n_rows,
-                             int64_t max_rows, int H, void* dst, float* dst_scale, hipStream_t s);
+                             int64_t max_rows, int H, void* dst, float* dst_scale, hipStream_t s,
+                             const int32_t* counts = nullptr, int cap = 0);
 hipError_t launch_quant_blocks(const void* src, int64_t batch, int64_t rows, int64_t cols,
                                void* codes, float* scales, hipStream_t s);
 
@@ -45,13 +50,19 @@ int gemm_path_rows(GemmPath path);
 bool gemm_unit_tables(GemmPath path);
 // n-tiles per expert of one GEMM (every kernel covers 256 weight rows).
 int gemm_n_tiles(bool swiglu, int Nout);
-// Capacity of a GEMM's work table (nt = gemm_n_tiles of that GEMM).
-int64_t schedule_entries(int64_t n_cap, int E_L, GemmPath path, int nt);
-// Builds the work tables on the device from the expert offsets (m-tile
-// table: only tab_up / n_up are written).
-hipError_t launch_schedule(const int32_t* offsets, int E_L, GemmPath path, int nt_up, int nt_dn,
-                           int4* tab_up, int32_t* n_up, int4* tab_dn, int32_t* n_dn,
-                           hipStream_t s);
+// Capacity of a GEMM's work table (nt = gemm_n_tiles of that GEMM) for at
+// most n_pairs live rows.
+int64_t schedule_entries(int64_t n_pairs, int E_L, GemmPath path, int nt);
+// Segment table of the grouped GEMMs: seg_cap == 0: seg = offsets [E_L + 1]
+// (contiguous layout, expert e's rows [offsets[e], offsets[e+1])); seg_cap > 0:
+// seg = counts [E_L] (masked layout, rows [e seg_cap, e seg_cap + counts[e])).
+// Builds the work tables on the device (m-tile table: only tab_up / n_up are
+// written).  sync (GEMM_SKINNY only, else null): the fused FFN's ticket and
+// per-m-tile counters, [1 + schedule_entries], cleared here for the launch
+// that follows.
+hipError_t launch_schedule(const int32_t* seg, int seg_cap, int E_L, GemmPath path, int nt_up,
+                           int nt_dn, int4* tab_up, int32_t* n_up, int4* tab_dn, int32_t* n_dn,
+                           int32_t* sync, hipStream_t s);
 struct GemmLaunch {
   bool fp8;              // e4m3 operands with block scales, else bf16
   bool swiglu;           // up GEMM with the SwiGLU epilogue (W = gate and up rows)
@@ -62,7 +73,8 @@ struct GemmLaunch {
   const float* W_scale;  // fp8: [E_L, NW/128, K/128]
   void* C;               // [N_cap, Nout]: bf16, or e4m3 when C_scale != nullptr
   float* C_scale;        // fp8 SwiGLU only: [N_cap, Nout/128] per-row group scales
-  const int32_t* offsets;
+  const int32_t* seg;     // segment table and its layout (see launch_schedule)
+  int seg_cap;
   const int4* info;       // work table of this GEMM (launch_schedule)
   const int32_t* n_tiles; // live entries of the table
   int64_t max_tiles;      // its capacity (schedule_entries)
@@ -79,6 +91,12 @@ struct GemmLaunch {
   const int32_t* a_index;
 };
 hipError_t launch_grouped_gemm(const GemmLaunch& L, hipStream_t s);
+// Both GEMMs of the FFN in one launch (GEMM_SKINNY only): up tiles first, and
+// each down tile starts once every up tile of its rows has published h.
+// `up` and `down` as for two launch_grouped_gemm calls sharing one m-tile
+// table; sync as cleared by launch_schedule.
+hipError_t launch_ffn_fused(const GemmLaunch& up, const GemmLaunch& down, int32_t* sync,
+                            hipStream_t s);
 // Largest fused-gather source and largest panel-layout activation matrix
 // (bytes) that the GEMM's 32-bit buffer offsets reach.
 constexpr int64_t kGemmGatherMaxBytes = 0x7ffffe00;

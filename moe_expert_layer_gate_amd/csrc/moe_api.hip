@@ -39,16 +39,29 @@ moe_status check_problem(const moe_problem* p) {
   // One expert's weight matrix must stay below 2 GiB (32-bit buffer offsets).
   if (4 * I * H >= (int64_t(1) << 31) || 4 * Is * H >= (int64_t(1) << 31))
     return MOE_ERR_UNSUPPORTED;
+  // Masked layout: every expert's block must hold all T tokens; row indices
+  // are 32-bit.
+  const int64_t C = p->capacity;
+  if (C < 0 || C > (1 << 24) || (C > 0 && C < T)) return MOE_ERR_INVALID_ARG;
+  if (C * EL >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
   // Panel activations: the GEMMs address x_perm and h with 32-bit offsets.
-  const int64_t N = T * (k < EL ? k : EL);
+  const int64_t N = C > 0 ? C * EL : T * (k < EL ? k : EL);
   if ((p->layout & MOE_LAYOUT_PANEL_ACTS) && 2 * N * (H > I ? H : I) > kGemmPanelMaxBytes)
     return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
-int64_t n_cap(const moe_problem* p) {
+// Most live (token, local expert) pairs: T min(k, E_L).
+int64_t n_pairs(const moe_problem* p) {
   const int64_t kk = p->top_k < p->num_local ? p->top_k : p->num_local;
   return static_cast<int64_t>(p->num_tokens) * kk;
+}
+
+// Rows of the permuted buffers: the pairs (contiguous layout) or E_L blocks
+// of `capacity` rows (masked layout).
+int64_t n_cap(const moe_problem* p) {
+  if (p->capacity > 0) return static_cast<int64_t>(p->capacity) * p->num_local;
+  return n_pairs(p);
 }
 
 bool is_fp8(const moe_problem* p) { return p->dtype == MOE_FP8_E4M3; }
@@ -92,6 +105,7 @@ struct FfnScratch {
   int4* tab_dn;
   int32_t* n_up;
   int32_t* n_dn;
+  int32_t* sync;    // fused decode FFN: ticket + per-m-tile counters
   void* h;          // [N_cap, I] bf16 or e4m3
   float* h_scale;   // fp8 only
 };
@@ -103,7 +117,9 @@ struct FfnShape {
 };
 
 FfnShape ffn_shape(const moe_problem* p) {
-  const int64_t N = n_cap(p);
+  // the kernel family follows the mean live rows per expert, whatever the
+  // layout of the buffers
+  const int64_t N = n_pairs(p);
   FfnShape f{};
   f.path = gemm_path(is_fp8(p), N / p->num_local);
   f.nt_up = gemm_n_tiles(!is_gelu(p), p->inter);
@@ -119,6 +135,7 @@ FfnScratch carve_ffn(Carve& c, const moe_problem* p) {
   FfnScratch f{};
   f.tab_up = c.take<int4>(sizeof(int4) * sh.cap_up);
   f.n_up = c.take<int32_t>(sizeof(int32_t));
+  if (sh.path == GEMM_SKINNY) f.sync = c.take<int32_t>(sizeof(int32_t) * (1 + sh.cap_up));
   if (!gemm_unit_tables(sh.path)) {  // one m-tile table for both GEMMs
     f.tab_dn = f.tab_up;
     f.n_dn = f.n_up;
@@ -164,6 +181,7 @@ moe_problem shared_problem(const moe_problem* p) {
   q.num_local = 1;
   q.inter = p->shared_inter;
   q.shared_inter = 0;
+  q.capacity = 0;
   return q;
 }
 
@@ -221,8 +239,9 @@ struct FfnSource {
 };
 
 // Enqueue the grouped FFN (no argument checks).  h follows p->layout's
-// activation bit.
-moe_status run_ffn(const moe_problem* p, const FfnSource& src, const int32_t* offsets,
+// activation bit.  seg: offsets [E_L + 1], or counts [E_L] when p->capacity
+// > 0 (masked layout).
+moe_status run_ffn(const moe_problem* p, const FfnSource& src, const int32_t* seg,
                    const moe_weights* w, void* h, float* h_scale, void* y_perm,
                    const FfnScratch& f, hipStream_t s) {
   const int64_t N = n_cap(p);
@@ -230,8 +249,8 @@ moe_status run_ffn(const moe_problem* p, const FfnSource& src, const int32_t* of
   const FfnShape sh = ffn_shape(p);
   void* hb = h ? h : f.h;
   float* hs = h ? h_scale : f.h_scale;
-  MOE_TRY(launch_schedule(offsets, E_L, sh.path, sh.nt_up, sh.nt_dn, f.tab_up, f.n_up, f.tab_dn,
-                          f.n_dn, s));
+  MOE_TRY(launch_schedule(seg, p->capacity, E_L, sh.path, sh.nt_up, sh.nt_dn, f.tab_up, f.n_up,
+                          f.tab_dn, f.n_dn, f.sync, s));
   GemmLaunch up{};
   up.fp8 = is_fp8(p);
   up.swiglu = !is_gelu(p);
@@ -242,7 +261,8 @@ moe_status run_ffn(const moe_problem* p, const FfnSource& src, const int32_t* of
   up.W_scale = w->w13_scale;
   up.C = hb;
   up.C_scale = is_fp8(p) ? hs : nullptr;
-  up.offsets = offsets;
+  up.seg = seg;
+  up.seg_cap = p->capacity;
   up.info = f.tab_up;
   up.n_tiles = f.n_up;
   up.max_tiles = sh.cap_up;
@@ -255,7 +275,6 @@ moe_status run_ffn(const moe_problem* p, const FfnSource& src, const int32_t* of
   up.a_rows = src.index ? src.src_rows : N;
   up.c_rows = N;
   up.a_index = src.index;
-  MOE_TRY(launch_grouped_gemm(up, s));
   GemmLaunch down = up;
   down.swiglu = false;
   down.gelu = false;
@@ -274,7 +293,12 @@ moe_status run_ffn(const moe_problem* p, const FfnSource& src, const int32_t* of
   down.c_panel = false;
   down.a_rows = N;
   down.a_index = nullptr;
-  MOE_TRY(launch_grouped_gemm(down, s));
+  if (sh.path == GEMM_SKINNY) {
+    MOE_TRY(launch_ffn_fused(up, down, f.sync, s));
+  } else {
+    MOE_TRY(launch_grouped_gemm(up, s));
+    MOE_TRY(launch_grouped_gemm(down, s));
+  }
   return MOE_OK;
 }
 
@@ -282,16 +306,16 @@ moe_status run_ffn(const moe_problem* p, const FfnSource& src, const int32_t* of
 moe_status run_dispatch(const moe_problem* p, const void* x, const int32_t* ids, int32_t* counts,
                         int32_t* offsets, int32_t* row_token, int32_t* row_slot, int32_t* tsr,
                         void* x_perm, float* x_perm_scale, void* scratch, hipStream_t s) {
-  const int T = p->num_tokens, E_L = p->num_local;
-  MOE_TRY(launch_index_build(ids, T, p->top_k, p->expert_begin, E_L, counts, offsets, row_token,
-                             row_slot, tsr, scratch, s));
+  const int T = p->num_tokens, E_L = p->num_local, C = p->capacity;
+  MOE_TRY(launch_index_build(ids, T, p->top_k, p->expert_begin, E_L, C, counts, offsets,
+                             row_token, row_slot, tsr, scratch, s));
   if (!x_perm) return MOE_OK;
   if (is_fp8(p))
     MOE_TRY(launch_gather_fp8(x, row_token, offsets + E_L, n_cap(p), p->hidden, x_perm,
-                              x_perm_scale, s));
+                              x_perm_scale, s, counts, C));
   else
     MOE_TRY(launch_gather_bf16(x, row_token, offsets + E_L, n_cap(p), p->hidden, x_perm,
-                               panel_acts(p) ? n_cap(p) : 0, s));
+                               panel_acts(p) ? n_cap(p) : 0, s, counts, C));
   return MOE_OK;
 }
 
@@ -451,7 +475,8 @@ moe_status moe_layer(const moe_problem* p, const float* logits, const void* x,
   if (st != MOE_OK) return st;
   const FfnSource rsrc = fuse ? FfnSource{x, nullptr, true, L.row_token, T}
                               : FfnSource{L.x_perm, L.x_perm_scale, false, nullptr, 0};
-  st = run_ffn(&pi, rsrc, L.offsets, w, nullptr, nullptr, L.y_perm, L.ffn, s);
+  st = run_ffn(&pi, rsrc, p->capacity > 0 ? L.counts : L.offsets, w, nullptr, nullptr, L.y_perm,
+               L.ffn, s);
   if (st != MOE_OK) return st;
   if (p->shared_inter > 0) {
     const moe_problem sq = shared_problem(p);

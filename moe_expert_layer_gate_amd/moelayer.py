@@ -30,7 +30,7 @@ class moe_problem(ctypes.Structure):
     _fields_ = [("num_tokens", _i32), ("hidden", _i32), ("num_experts", _i32),
                 ("top_k", _i32), ("expert_begin", _i32), ("num_local", _i32),
                 ("inter", _i32), ("shared_inter", _i32), ("dtype", _i32),
-                ("layout", _i32), ("activation", _i32)]
+                ("layout", _i32), ("activation", _i32), ("capacity", _i32)]
 
 
 class moe_weights(ctypes.Structure):
@@ -97,11 +97,12 @@ class Problem:
     fp8: bool = False
     layout: int = 0   # LAYOUT_* bits
     act: str = "swiglu"  # "swiglu" | "gelu"
+    capacity: int = 0    # 0: contiguous segments; C >= T: masked fixed-capacity layout
 
     def c(self) -> moe_problem:
         return moe_problem(self.T, self.H, self.E, self.k, self.e_lo, self.E_L, self.I,
                            self.I_s, MOE_FP8_E4M3 if self.fp8 else MOE_BF16, self.layout,
-                           ACT_GELU if self.act == "gelu" else ACT_SWIGLU)
+                           ACT_GELU if self.act == "gelu" else ACT_SWIGLU, self.capacity)
 
     @property
     def m(self) -> int:
@@ -110,12 +111,17 @@ class Problem:
 
     @property
     def n_cap(self) -> int:
+        """Rows of the permuted buffers."""
+        if self.capacity > 0:
+            return self.capacity * self.E_L
         return self.T * min(self.k, self.E_L)
 
     @classmethod
-    def from_config(cls, cfg, T: Optional[int] = None, layout: int = 0) -> "Problem":
+    def from_config(cls, cfg, T: Optional[int] = None, layout: int = 0,
+                    capacity: Optional[int] = None) -> "Problem":
         return cls(T=cfg.T if T is None else T, H=cfg.H, E=cfg.E, k=cfg.k, e_lo=cfg.e_lo,
-                   E_L=cfg.E_L, I=cfg.I, I_s=cfg.I_s, fp8=cfg.fp8, layout=layout, act=cfg.act)
+                   E_L=cfg.E_L, I=cfg.I, I_s=cfg.I_s, fp8=cfg.fp8, layout=layout, act=cfg.act,
+                   capacity=getattr(cfg, "capacity", 0) if capacity is None else capacity)
 
 
 def _ptr(t) -> Optional[int]:

@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert ml.lib().moe_abi_version() == 3
+    assert ml.lib().moe_abi_version() == 4
     assert ml.status_str(0) == "MOE_OK"
     assert ml.status_str(3) == "MOE_ERR_WORKSPACE"
     assert ml.status_str(99) == "MOE_ERR_UNKNOWN"
@@ -191,3 +191,28 @@ def test_activation_checks():
     assert L.moe_route(ctypes.byref(pc), 16, 16, 16, None) == ml.MOE_ERR_INVALID_ARG
     pf = ml.Problem(**base, fp8=True, act="gelu").c()     # the standard MLP is bf16 only
     assert L.moe_route(ctypes.byref(pf), 16, 16, 16, None) == ml.MOE_ERR_UNSUPPORTED
+
+
+def test_capacity_checks():
+    """Masked layout: capacity 0 (contiguous) or >= T; E_L * capacity rows."""
+    L = ml.lib()
+    base = dict(T=16, H=256, E=8, k=2, e_lo=0, E_L=8, I=256)
+    for cap, want in ((-1, ml.MOE_ERR_INVALID_ARG), (15, ml.MOE_ERR_INVALID_ARG),
+                      ((1 << 24) + 1, ml.MOE_ERR_INVALID_ARG)):
+        pc = ml.Problem(**base, capacity=cap).c()
+        assert L.moe_route(ctypes.byref(pc), 16, 16, 16, None) == want
+        assert ml.workspace_bytes(ml.Problem(**base, capacity=cap)) == 0
+    # E_L * capacity must stay below 2^31 rows
+    pc = ml.Problem(**dict(base, E=1024, E_L=1024), capacity=1 << 21).c()
+    assert L.moe_route(ctypes.byref(pc), 16, 16, 16, None) == ml.MOE_ERR_UNSUPPORTED
+    # the buffers grow to E_L * capacity rows
+    small = ml.workspace_bytes(ml.Problem(**base))
+    masked = ml.workspace_bytes(ml.Problem(**base, capacity=64))
+    assert masked > small
+    p = ml.Problem(**base, capacity=64)
+    assert p.n_cap == 8 * 64
+    assert masked >= p.n_cap * (2 * p.H + 2 * p.I)
+    # a capacity of exactly T is valid; T = 0 is always a no-op
+    assert ml.workspace_bytes(ml.Problem(**base, capacity=16)) > 0
+    p0 = ml.Problem(**dict(base, T=0), capacity=16).c()
+    assert L.moe_route(ctypes.byref(p0), 16, 16, 16, None) == ml.MOE_OK

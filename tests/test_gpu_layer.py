@@ -63,7 +63,8 @@ def run_staged(torch, p, dev):
     ml.moe_dispatch(p, dev["x"], ids, counts, offsets, row_token, row_slot, tsr, xp, xs,
                     dv.workspace(p, ml.STAGE_DISPATCH))
     y_perm = torch.empty((N, H), dtype=torch.bfloat16, device="cuda")
-    ml.moe_grouped_ffn(p, xp, xs, offsets, dv.weights_of(dev, p.fp8), h, hs, y_perm,
+    seg = counts if p.capacity else offsets      # the masked layout passes counts
+    ml.moe_grouped_ffn(p, xp, xs, seg, dv.weights_of(dev, p.fp8), h, hs, y_perm,
                        dv.workspace(p, ml.STAGE_FFN))
     if p.layout & ml.LAYOUT_PANEL_ACTS:
         xp, h = unpanel(xp, N, H), unpanel(h, N, I)
@@ -234,7 +235,8 @@ def run_gather_path(torch, p, dev, shared=None):
     ml.moe_dispatch(p, dev["x"], ids, counts, offsets, row_token, row_slot, tsr, None, None,
                     dv.workspace(p, ml.STAGE_DISPATCH))
     y_perm = torch.empty((N, p.H), dtype=torch.bfloat16, device="cuda")
-    ml.moe_grouped_ffn_gather(p, dev["x"], row_token, offsets, dv.weights_of(dev, False), None,
+    seg = counts if p.capacity else offsets
+    ml.moe_grouped_ffn_gather(p, dev["x"], row_token, seg, dv.weights_of(dev, False), None,
                               y_perm, dv.workspace(p, ml.STAGE_FFN))
     y = torch.empty((T, p.H), dtype=torch.bfloat16, device="cuda")
     ml.moe_combine(p, y_perm, tsr, w, shared, y)

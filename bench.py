@@ -44,6 +44,12 @@ def parse():
     ap.add_argument("--masked", action="store_true",
                     help="masked fixed-capacity expert layout (capacity = tokens) instead of "
                          "contiguous segments")
+    ap.add_argument("--stream", action="store_true",
+                    help="also measure the streaming FFN (workloads with replicas): the FFN "
+                         "throughput curve, the launch threshold at rho, and the streamed layer "
+                         "against the one-call layer")
+    ap.add_argument("--rho", type=float, default=0.90)
+    ap.add_argument("--streams", type=int, default=2)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="finish with three 1 GiB device copies (a known-size reference "
                          "for the FETCH_SIZE / WRITE_SIZE counters)")
@@ -286,6 +292,8 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+    if args.stream:
+        out["streamffn"] = stream_bench(args, cfg, d, p_layer, W, dev)
     print(json.dumps(out), flush=True)
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -293,6 +301,122 @@ def main():
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
+
+
+def _time_ms(fn, reps):
+    """Median wall time of fn() on the GPU, bracketed by synchronisations."""
+    import torch
+    ts = []
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        fn()
+        torch.cuda.synchronize()
+        ts.append((time.perf_counter() - t0) * 1e3)
+    return sorted(ts)[len(ts) // 2]
+
+
+def stream_bench(args, cfg, d, p_layer, W, dev):
+    """Streaming FFN on one GPU (CascadeEP section 3.2): the replicas' rows
+    arrive in ascending order of size; the FFN throughput curve over
+    arrival-order prefixes gives the launch threshold theta at rho; the
+    threshold plan's invocations run as moe_layer_streamed on several streams
+    and are timed against the one-call layer (synchronous) and one invocation
+    per replica on one stream (asynchronous without threshold)."""
+    import dataclasses
+
+    import numpy as np
+    import torch
+
+    from moe_expert_layer_gate_amd import device as dv
+    from moe_expert_layer_gate_amd import inputs as synth
+    from moe_expert_layer_gate_amd import moelayer as ml
+
+    if "replica_offsets" not in d:
+        return {"error": "workload has no replica split"}
+    off = d["replica_offsets"]
+    perm = torch.from_numpy(synth.arrival_permutation(off)).cuda()
+    logits = dev["logits"][perm].contiguous()
+    x = dev["x"][perm].contiguous()
+    T, k, H = p_layer.T, p_layer.k, p_layer.H
+    sizes = [int(off[r + 1] - off[r]) for r in synth.replica_arrival(off)]
+    bounds = np.concatenate([[0], np.cumsum(sizes)]).astype(int)
+    i32 = dict(dtype=torch.int32, device="cuda")
+    ids = torch.empty((T, k), **i32)
+    tw = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    ml.moe_route(p_layer, logits, ids, tw)
+    loc = ((ids >= p_layer.e_lo) & (ids < p_layer.e_lo + p_layer.E_L)).sum(1).cpu().numpy()
+    ready = [int(loc[bounds[i]:bounds[i + 1]].sum()) for i in range(len(sizes))]
+
+    # FFN throughput against expert-token count (rows of one invocation)
+    pf = dataclasses.replace(p_layer, layout=p_layer.layout | ml.LAYOUT_PANEL_ACTS) \
+        if not p_layer.fp8 else p_layer
+    curve = []
+    t_pts = sorted({t for t in (256, 512, 1024, 2048, 3072, 4096, 6144, 8192, 12288, T) if t <= T})
+    for tp in t_pts:
+        q = dataclasses.replace(pf, T=tp)
+        N = q.n_cap
+        cnt, offs = torch.empty(q.E_L, **i32), torch.empty(q.E_L + 1, **i32)
+        rt, rs, tsr = torch.empty(N, **i32), torch.empty(N, **i32), torch.empty((tp, k), **i32)
+        yp = torch.empty((N, H), dtype=torch.bfloat16, device="cuda")
+        if q.fp8:
+            xp = torch.empty((N, H), dtype=torch.uint8, device="cuda")
+            xs = torch.empty((N, H // 128), dtype=torch.float32, device="cuda")
+            ml.moe_dispatch(q, x, ids, cnt, offs, rt, rs, tsr, xp, xs,
+                            dv.workspace(q, ml.STAGE_DISPATCH))
+            wsf = dv.workspace(q, ml.STAGE_FFN)
+            fn = lambda: ml.moe_grouped_ffn(q, xp, xs, offs, W, None, None, yp, wsf)
+        else:
+            ml.moe_dispatch(q, x, ids, cnt, offs, rt, rs, tsr, None, None,
+                            dv.workspace(q, ml.STAGE_DISPATCH))
+            wsf = dv.workspace(q, ml.STAGE_FFN)
+            fn = lambda: ml.moe_grouped_ffn_gather(q, x, rt, offs, W, None, yp, wsf)
+        fn()
+        ms = _time_ms(fn, 7)
+        pairs = int(cnt.sum().item())
+        tfl = 2.0 * (q.m + 1) * H * q.I * pairs / (ms * 1e-3) / 1e12
+        curve.append({"tokens": tp, "expert_tokens": pairs, "ffn_ms": round(ms, 4),
+                      "tflops": round(tfl, 1)})
+        del yp, rt, rs, tsr, wsf
+    theta = ml.stream_threshold([c["expert_tokens"] for c in curve],
+                                [c["tflops"] for c in curve], args.rho)
+    ends = ml.stream_plan(ready, theta)
+    groups = [0] + [int(bounds[e]) for e in ends]
+    per_replica = [int(b) for b in bounds]
+
+    y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    ws_l = dv.workspace(p_layer)
+    cur = torch.cuda.current_stream()
+    streams = [torch.cuda.Stream() for _ in range(max(1, args.streams))]
+
+    def streamed(g, ns):
+        gmax = max(b - a for a, b in zip(g[:-1], g[1:]))
+        ws = torch.empty(ml.workspace_bytes_streamed(p_layer, gmax, ns), dtype=torch.uint8,
+                         device="cuda")
+
+        def run():
+            for st in streams[:ns]:
+                st.wait_stream(cur)
+            ml.moe_layer_streamed(p_layer, logits, x, W, y, g, streams[:ns], ws)
+            for st in streams[:ns]:
+                cur.wait_stream(st)
+        return run
+
+    reps = max(5, args.steps // 2)
+    sync_fn = lambda: ml.moe_layer(p_layer, logits, x, W, y, ws_l)
+    runs = {"sync": sync_fn, f"stream_{len(streams)}": streamed(groups, len(streams)),
+            "stream_1": streamed(groups, 1), "async_per_replica_1": streamed(per_replica, 1)}
+    res = {}
+    for name, fn in runs.items():
+        fn()
+        res[name] = round(_time_ms(fn, reps), 4)
+    best = res[f"stream_{len(streams)}"]
+    return {"rho": args.rho, "theta_expert_tokens": theta, "curve": curve,
+            "arrival_replica_tokens": sizes, "arrival_expert_tokens": ready,
+            "invocations_tokens": groups, "layer_ms": res,
+            "retained_throughput": round(res["sync"] / best, 4),
+            "retained_throughput_1_stream": round(res["sync"] / res["stream_1"], 4),
+            "retained_throughput_async": round(res["sync"] / res["async_per_replica_1"], 4)}
 
 
 def cpu_baseline(cfg, d, sample):

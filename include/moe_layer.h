@@ -13,6 +13,9 @@
  *   moe_grouped_ffn  gated SwiGLU FFN of every local expert over its segment
  *   moe_combine      gate-weighted sum back to token order (+ shared expert)
  *   moe_layer        all of the above in one call
+ *   moe_layer_streamed  the layer in invocations over consecutive token
+ *                    groups on several streams (streaming FFN), planned by
+ *                    moe_stream_threshold / moe_stream_plan
  *
  * plus moe_quantize_fp8 (block-FP8 conversion of bf16 weights at load time and
  * of activations) and the helpers moe_workspace_bytes / moe_status_str.
@@ -53,7 +56,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 
 typedef enum {
   MOE_OK = 0,
@@ -280,6 +283,54 @@ moe_status moe_quantize_fp8(const void* src, int64_t batch, int64_t rows,
  * time, like moe_quantize_fp8: the weights are packed once.               */
 moe_status moe_pack_panel(const void* src, int64_t batch, int64_t rows,
                           int64_t cols, void* dst, void* stream);
+
+/* Streaming FFN, host side (page "CascadeEP ...", section 3.2 "Launch
+ * threshold" and Appendix C: ready work accumulates, an invocation is launched
+ * once it reaches the threshold, and after the last arrival the rest is
+ * flushed; independent invocations run on separate streams).
+ *
+ * moe_stream_threshold: theta = the smallest profiled expert-token count
+ * whose measured FFN throughput reaches rho times the highest throughput
+ * observed.  counts [n], throughput [n] are host arrays (the profile, any
+ * order), n >= 1, 0 <= rho <= 1, throughputs finite and >= 0.  Returns theta,
+ * or -1 for invalid arguments.  No GPU work.                              */
+int64_t moe_stream_threshold(const int64_t* counts, const double* throughput,
+                             int32_t n, double rho);
+
+/* moe_stream_plan: threshold batching of n arrivals.  ready_rows[i] (host,
+ * >= 0) is the number of routed rows that become ready with arrival i; rows
+ * accumulate until the ready, unlaunched count reaches theta (>= theta
+ * launches), and after the last arrival the remainder is launched whatever
+ * its size.  Writes the exclusive end arrival of each invocation to
+ * group_end [n] (host) and their number to *n_groups.  theta = 0 launches
+ * every arrival on its own; a theta above the total gives one invocation.
+ * MOE_ERR_INVALID_ARG for negative counts or theta.  No GPU work.          */
+moe_status moe_stream_plan(const int64_t* ready_rows, int32_t n, int64_t theta,
+                           int32_t* group_end, int32_t* n_groups);
+
+/* Workspace of moe_layer_streamed for groups of at most max_group_tokens
+ * tokens on n_streams streams (1 <= n_streams <= 64); 0 if invalid.        */
+size_t moe_workspace_bytes_streamed(const moe_problem* p, int32_t max_group_tokens,
+                                    int32_t n_streams);
+
+/* Streamed layer: the tokens are in arrival order (the destination's receive
+ * order), and invocation j is moe_layer on tokens [group_tokens[j],
+ * group_tokens[j+1]) -- its own route, dispatch, grouped FFN, shared expert
+ * and combine, writing rows [group_tokens[j], group_tokens[j+1]) of y -- on
+ * streams[j % n_streams] with that stream's own workspace slice.  The output
+ * equals moe_layer over all T tokens (each token's result depends on its own
+ * row only).
+ *   group_tokens [n_groups + 1] host int32: 0 = g_0 <= g_1 <= ... = T
+ *   streams [n_streams] hipStream_t handles (NULL entries = default stream)
+ *   ws: moe_workspace_bytes_streamed(p, max group length, n_streams) bytes
+ * Ordering is the caller's: the inputs must be ready on every stream before
+ * the call (e.g. each stream waits on the producer's event), and consumers of
+ * y wait on all streams.  All streams at the default priority.             */
+moe_status moe_layer_streamed(const moe_problem* p, const float* logits,
+                              const void* x, const moe_weights* w, void* y,
+                              const int32_t* group_tokens, int32_t n_groups,
+                              void* const* streams, int32_t n_streams,
+                              void* ws, size_t ws_bytes);
 
 #define MOE_STAGE_LAYER 0
 #define MOE_STAGE_DISPATCH 1

@@ -19,6 +19,8 @@ __global__ void fill_offsets_kernel(int32_t* offsets, int n) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+constexpr int32_t kMaxStreams = 64;  // streams of one streamed layer call
+
 // Validate the problem; returns MOE_OK or MOE_ERR_INVALID_ARG/UNSUPPORTED.
 moe_status check_problem(const moe_problem* p) {
   if (!p) return MOE_ERR_INVALID_ARG;
@@ -329,6 +331,9 @@ bool weights_ok(const moe_problem* p, const moe_weights* w, bool need_shared) {
   return true;
 }
 
+moe_status enqueue_layer(const moe_problem* p, const float* logits, const void* x,
+                         const moe_weights* w, void* y, void* ws, hipStream_t s);
+
 }  // namespace
 }  // namespace moe
 
@@ -460,8 +465,20 @@ moe_status moe_layer(const moe_problem* p, const float* logits, const void* x,
   if (!weights_ok(p, w, p->shared_inter > 0)) return MOE_ERR_INVALID_ARG;
   if (!ws || ws_bytes < moe_workspace_bytes(p, MOE_STAGE_LAYER)) return MOE_ERR_WORKSPACE;
   if (p->num_tokens == 0) return MOE_OK;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  Carve c(align_ws(ws));
+  return enqueue_layer(p, logits, x, w, y, align_ws(ws), static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+namespace moe {
+namespace {
+
+// The whole layer on `s` (arguments already checked; ws 256-byte aligned and
+// at least moe_workspace_bytes(p, MOE_STAGE_LAYER) - 256 bytes).
+moe_status enqueue_layer(const moe_problem* p, const float* logits, const void* x,
+                         const moe_weights* w, void* y, void* ws, hipStream_t s) {
+  moe_status st = MOE_OK;
+  Carve c(ws);
   const LayerScratch L = carve_layer(c, p);
   const int T = p->num_tokens;
   const moe_problem pi = layer_internal(p);
@@ -501,6 +518,11 @@ moe_status moe_layer(const moe_problem* p, const float* logits, const void* x,
                                    T, p->top_k, p->hidden, y, s));
 }
 
+}  // namespace
+}  // namespace moe
+
+extern "C" {
+
 moe_status moe_quantize_fp8(const void* src, int64_t batch, int64_t rows, int64_t cols,
                             int32_t block_rows, void* codes, float* scales, void* stream) {
   if (!src || !codes || !scales || !aligned16(src) || !aligned16(codes) || !aligned16(scales))
@@ -531,6 +553,115 @@ moe_status moe_pack_panel(const void* src, int64_t batch, int64_t rows, int64_t 
   if (bytes > 0 && a < b + bytes && b < a + bytes) return MOE_ERR_INVALID_ARG;
   if (batch == 0 || rows == 0) return MOE_OK;
   return hip_status(launch_pack_panel(src, batch, rows, cols, dst, static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------------------
+// Streaming FFN (page "CascadeEP ...", section 3.2 and Appendix C): the host
+// side of the launch threshold and of threshold batching, and the streamed
+// layer that runs each invocation on its own stream.
+// ---------------------------------------------------------------------------
+
+int64_t moe_stream_threshold(const int64_t* counts, const double* throughput, int32_t n,
+                             double rho) {
+  if (!counts || !throughput || n < 1 || !(rho >= 0.0 && rho <= 1.0)) return -1;
+  double peak = 0.0;
+  for (int32_t i = 0; i < n; ++i) {
+    if (!(throughput[i] >= 0.0) || throughput[i] > 1e300 || counts[i] < 0) return -1;
+    if (throughput[i] > peak) peak = throughput[i];
+  }
+  int64_t best = -1;
+  for (int32_t i = 0; i < n; ++i)
+    if (throughput[i] >= rho * peak && (best < 0 || counts[i] < best)) best = counts[i];
+  return best;
+}
+
+moe_status moe_stream_plan(const int64_t* ready_rows, int32_t n, int64_t theta,
+                           int32_t* group_end, int32_t* n_groups) {
+  if (!n_groups || n < 0 || theta < 0 || (n > 0 && (!ready_rows || !group_end)))
+    return MOE_ERR_INVALID_ARG;
+  for (int32_t i = 0; i < n; ++i)
+    if (ready_rows[i] < 0) return MOE_ERR_INVALID_ARG;
+  int32_t g = 0;
+  int64_t pending = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    pending += ready_rows[i];
+    if (pending >= theta || i == n - 1) {  // threshold reached, or the final flush
+      group_end[g++] = i + 1;
+      pending = 0;
+    }
+  }
+  *n_groups = g;
+  return MOE_OK;
+}
+
+// Workspace of one stream's slice: enough for the layer on any group of up to
+// max_group_tokens tokens.  Within one GEMM path the layer's workspace grows
+// with the token count, but the work tables change form where the path does,
+// so the largest count of every smaller path is measured too.
+static size_t streamed_slice(const moe_problem* p, int32_t max_group_tokens) {
+  moe_problem q = *p;
+  q.num_tokens = max_group_tokens;
+  size_t b = moe_workspace_bytes(&q, MOE_STAGE_LAYER);
+  const bool fp8 = p->dtype == MOE_FP8_E4M3;
+  const int64_t kk = p->top_k < p->num_local ? p->top_k : p->num_local;
+  for (int64_t r = 0; r < 4096; ++r) {
+    if (gemm_path(fp8, r) == gemm_path(fp8, r + 1)) continue;
+    // routed experts: rows per expert T kk / E_L; the shared expert: T
+    const int64_t cands[2] = {((r + 1) * p->num_local - 1) / kk, r};
+    for (const int64_t t : cands) {
+      if (t <= 0 || t >= max_group_tokens) continue;
+      q.num_tokens = static_cast<int32_t>(t);
+      const size_t bt = moe_workspace_bytes(&q, MOE_STAGE_LAYER);
+      if (bt > b) b = bt;
+    }
+  }
+  return (b + 255) & ~size_t(255);
+}
+
+size_t moe_workspace_bytes_streamed(const moe_problem* p, int32_t max_group_tokens,
+                                    int32_t n_streams) {
+  if (check_problem(p) != MOE_OK || max_group_tokens < 0 ||
+      max_group_tokens > p->num_tokens || n_streams < 1 || n_streams > kMaxStreams)
+    return 0;
+  return streamed_slice(p, max_group_tokens) * static_cast<size_t>(n_streams);
+}
+
+moe_status moe_layer_streamed(const moe_problem* p, const float* logits, const void* x,
+                              const moe_weights* w, void* y, const int32_t* group_tokens,
+                              int32_t n_groups, void* const* streams, int32_t n_streams,
+                              void* ws, size_t ws_bytes) {
+  moe_status st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!logits || !x || !y || !aligned16(logits) || !aligned16(x) || !aligned16(y))
+    return MOE_ERR_INVALID_ARG;
+  if (!weights_ok(p, w, p->shared_inter > 0)) return MOE_ERR_INVALID_ARG;
+  if (!streams || n_streams < 1 || n_streams > kMaxStreams || n_groups < 0 || !group_tokens)
+    return MOE_ERR_INVALID_ARG;
+  // group_tokens: 0 = g_0 <= g_1 <= ... <= g_n = T
+  if (group_tokens[0] != 0 || group_tokens[n_groups] != p->num_tokens) return MOE_ERR_INVALID_ARG;
+  int32_t max_g = 0;
+  for (int32_t j = 0; j < n_groups; ++j) {
+    const int32_t len = group_tokens[j + 1] - group_tokens[j];
+    if (len < 0) return MOE_ERR_INVALID_ARG;
+    if (len > max_g) max_g = len;
+  }
+  const size_t slice = streamed_slice(p, max_g);
+  if (!ws || ws_bytes < slice * static_cast<size_t>(n_streams)) return MOE_ERR_WORKSPACE;
+  uint8_t* base = static_cast<uint8_t*>(align_ws(ws));
+  // the 256 bytes of slack in each slice absorb the base's rounding
+  const int64_t E = p->num_experts, H = p->hidden;
+  for (int32_t j = 0; j < n_groups; ++j) {
+    const int32_t t0 = group_tokens[j], len = group_tokens[j + 1] - t0;
+    if (len == 0) continue;
+    moe_problem q = *p;
+    q.num_tokens = len;
+    const int32_t si = j % n_streams;
+    st = enqueue_layer(&q, logits + t0 * E, static_cast<const uint16_t*>(x) + t0 * H, w,
+                       static_cast<uint16_t*>(y) + t0 * H, base + si * slice,
+                       static_cast<hipStream_t>(streams[si]));
+    if (st != MOE_OK) return st;
+  }
+  return MOE_OK;
 }
 
 }  // extern "C"

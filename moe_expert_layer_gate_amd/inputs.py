@@ -27,7 +27,7 @@ from __future__ import annotations
 
 import dataclasses
 import os
-from typing import Dict, Optional
+from typing import List, Dict, Optional
 
 import numpy as np
 
@@ -181,6 +181,24 @@ def replica_split(rng: np.random.Generator, T: int, replicas: int) -> np.ndarray
     order = np.argsort(-(raw - base), kind="stable")
     base[order[:rem]] += 1
     return np.concatenate([[0], np.cumsum(base)]).astype(np.int64)
+
+
+def replica_arrival(replica_offsets: np.ndarray) -> List[int]:
+    """Arrival model of the synthetic prefill batches: a replica's attention
+    time grows with its token count, so replicas arrive in ascending order of
+    size (ties by index)."""
+    off = np.asarray(replica_offsets, dtype=np.int64)
+    sizes = (off[1:] - off[:-1]).tolist()
+    return sorted(range(len(sizes)), key=lambda r: (sizes[r], r))
+
+
+def arrival_permutation(replica_offsets: np.ndarray) -> np.ndarray:
+    """Token permutation that puts the rows in arrival order (the order in
+    which the destination receives them): the replicas' token ranges one
+    after another in replica_arrival order."""
+    off = np.asarray(replica_offsets, dtype=np.int64)
+    return np.concatenate([np.arange(off[r], off[r + 1]) for r in replica_arrival(off)]
+                          + [np.zeros(0, dtype=np.int64)])
 
 
 def make_inputs(cfg: MoEConfig, seed: int, *, weights: bool = True,

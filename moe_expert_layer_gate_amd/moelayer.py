@@ -51,6 +51,10 @@ SIGNATURES = {
     "moe_quantize_fp8": (_i32, [_vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp]),
     "moe_pack_panel": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp]),
     "moe_workspace_bytes": (_sz, [_P, _i32]),
+    "moe_stream_threshold": (_i64, [_vp, _vp, _i32, ctypes.c_double]),
+    "moe_stream_plan": (_i32, [_vp, _i32, _i64, _vp, _vp]),
+    "moe_workspace_bytes_streamed": (_sz, [_P, _i32, _i32]),
+    "moe_layer_streamed": (_i32, [_P, _vp, _vp, _W, _vp, _vp, _i32, _vp, _i32, _vp, _sz]),
     "moe_status_str": (ctypes.c_char_p, [_i32]),
     "moe_abi_version": (_i32, []),
 }
@@ -216,3 +220,39 @@ def moe_quantize_fp8(src, batch: int, rows: int, cols: int, block_rows: int, cod
 def moe_pack_panel(src, batch: int, rows: int, cols: int, dst, stream=None) -> None:
     _check("moe_pack_panel", lib().moe_pack_panel(
         _ptr(src), batch, rows, cols, _ptr(dst), _stream(stream)))
+
+
+def stream_threshold(counts, throughput, rho: float) -> int:
+    """moe_stream_threshold on host sequences (-1 if invalid)."""
+    n = len(counts)
+    c = (ctypes.c_int64 * max(n, 1))(*[int(v) for v in counts])
+    t = (ctypes.c_double * max(n, 1))(*[float(v) for v in throughput])
+    return int(lib().moe_stream_threshold(c, t, n, float(rho)))
+
+
+def stream_plan(ready_rows, theta: int):
+    """moe_stream_plan: the exclusive end arrival of each invocation."""
+    n = len(ready_rows)
+    r = (ctypes.c_int64 * max(n, 1))(*[int(v) for v in ready_rows])
+    ends = (ctypes.c_int32 * max(n, 1))()
+    ng = ctypes.c_int32(0)
+    _check("moe_stream_plan", lib().moe_stream_plan(r, n, int(theta), ends, ctypes.byref(ng)))
+    return [int(ends[i]) for i in range(ng.value)]
+
+
+def workspace_bytes_streamed(p: Problem, max_group_tokens: int, n_streams: int) -> int:
+    pc = p.c()
+    return int(lib().moe_workspace_bytes_streamed(ctypes.byref(pc), int(max_group_tokens),
+                                                  int(n_streams)))
+
+
+def moe_layer_streamed(p: Problem, logits, x, weights: moe_weights, y, group_tokens, streams,
+                       ws) -> None:
+    """moe_layer over token groups [group_tokens[j], group_tokens[j+1]), group
+    j on streams[j % len(streams)] (torch streams or raw handles)."""
+    pc = p.c()
+    g = (ctypes.c_int32 * len(group_tokens))(*[int(v) for v in group_tokens])
+    hs = (ctypes.c_void_p * len(streams))(*[_stream(st) for st in streams])
+    _check("moe_layer_streamed", lib().moe_layer_streamed(
+        ctypes.byref(pc), _ptr(logits), _ptr(x), ctypes.byref(weights), _ptr(y), g,
+        len(group_tokens) - 1, hs, len(streams), _ptr(ws), ws.numel() * ws.element_size()))

@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert ml.lib().moe_abi_version() == 4
+    assert ml.lib().moe_abi_version() == 5
     assert ml.status_str(0) == "MOE_OK"
     assert ml.status_str(3) == "MOE_ERR_WORKSPACE"
     assert ml.status_str(99) == "MOE_ERR_UNKNOWN"

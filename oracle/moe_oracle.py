@@ -57,6 +57,14 @@ the design notes of the repository):
   The oracle's FP8 layer uses the dequantised weights (code * scale) as the
   layer's parameters and does not quantise x or h.
 * Shared expert: always on, weight 1, same SwiGLU form, added in combine.
+* MXFP4 (CascadeEP section 4.1 names MXFP4 routed-expert weights; the
+  format is the OCP MX one): E2M1 elements with one E8M0 scale per 32
+  consecutive elements of a weight row (along K), converted with the MX
+  rule (shared exponent floor(log2 amax) - 2, round to nearest even,
+  saturate at 6).  The GEMM inputs that go with them are MXFP8 (E4M3, one
+  E8M0 scale per 32 elements of a token row, shared exponent floor(log2
+  amax) - 8), the MX form of the FP8 activations.  As for block-FP8, the
+  dequantised weights are the layer's parameters.
 * Masked (fixed-capacity) layout, the decode-time alternative to the
   contiguous one (the ExpertPlex page's masked grouped-GEMM layout; the
   OverlapAdvisor page's Table 7, where the low-latency dispatch feeds the
@@ -78,7 +86,8 @@ __all__ = [
     "expert_ffn", "grouped_ffn", "combine", "moe_layer", "moe_layer_tokens",
     "index_build_masked", "grouped_ffn_masked",
     "e4m3_value", "e4m3_encode", "quantize_blocks", "quantize_rows_groups",
-    "dequantize_blocks", "fp8_activation", "E4M3_MAX",
+    "dequantize_blocks", "fp8_activation", "E4M3_MAX", "e2m1_value", "e2m1_encode",
+    "e8m0_value", "mx_quantize", "mx_dequantize", "mx8_activation",
 ]
 
 
@@ -148,6 +157,91 @@ def e4m3_encode(v: np.ndarray) -> np.ndarray:
     assert np.all(_POS_VALUES[mag_code] == q)   # decodes back to q exactly
     # -0.0 keeps its sign bit (code 0x80), as the hardware's sign does.
     return mag_code | (neg.astype(np.uint8) << 7)
+
+
+# MX formats (OCP Microscaling Formats (MX) v1.0): blocks of 32 elements along
+# a row share one E8M0 scale 2^(e - 127); elements are E2M1 (MXFP4) or E4M3
+# (MXFP8).  The pages name MXFP4 routed-expert weights only (CascadeEP
+# section 4.1); the format itself comes from the public OCP specification.
+
+MX_BLOCK = 32
+E2M1_MAX = 6.0
+_E2M1_EMAX = 2     # exponent of the largest normal E2M1 value (6 = 1.5 * 2^2)
+_E4M3_EMAX = 8     # 448 = 1.75 * 2^8
+
+
+def e2m1_value(codes: np.ndarray) -> np.ndarray:
+    """Value of 4-bit E2M1 codes (0..15): sign bit 3, exponent bits 2..1
+    (bias 1), mantissa bit 0; exponent field 0 is subnormal (m * 0.5)."""
+    c = np.asarray(codes, dtype=np.int64)
+    s = (c >> 3) & 1
+    e = (c >> 1) & 3
+    m = c & 1
+    mag = np.where(e == 0, 0.5 * m, (1.0 + 0.5 * m) * np.ldexp(1.0, e - 1))
+    return np.where(s == 1, -mag, mag)
+
+
+def e2m1_encode(v: np.ndarray) -> np.ndarray:
+    """Round to E2M1 codes: nearest representable value, ties to the code
+    with an even mantissa bit, magnitudes beyond 6 saturate to 6.  Within a
+    binade [2^e, 2^(e+1)), e >= 0, the spacing is 2^(e-1); below 1 (the
+    subnormal range) it is 0.5."""
+    v64 = np.asarray(v, dtype=np.float64)
+    if np.isnan(v64).any():
+        raise ValueError("NaN has no E2M1 code")
+    neg = np.signbit(v64)
+    a = np.abs(v64)
+    _, ex = np.frexp(a)
+    e = np.maximum(ex - 1, 0)
+    q = np.minimum(np.ldexp(np.rint(np.ldexp(a, 1 - e)), e - 1), E2M1_MAX)
+    # code of the magnitude: subnormal/zero q in {0, 0.5} -> 2q; normal
+    # q = (1 + m/2) 2^eq -> (eq + 1) * 2 + m
+    _, eq = np.frexp(q)
+    eq = eq - 1
+    mag = np.where(q < 1.0, 2.0 * q, (eq + 1) * 2 + (np.ldexp(q, -eq) - 1.0) * 2)
+    mag_code = mag.astype(np.int64)
+    assert np.all(e2m1_value(mag_code) == q)
+    return (mag_code | (neg.astype(np.int64) << 3)).astype(np.uint8)
+
+
+def e8m0_value(codes: np.ndarray) -> np.ndarray:
+    """Value of E8M0 scale codes: 2^(code - 127) (code 255, NaN, is never
+    produced here)."""
+    c = np.asarray(codes, dtype=np.int64)
+    if np.any(c == 255):
+        raise ValueError("E8M0 NaN")
+    return np.ldexp(1.0, c - 127)
+
+
+def mx_quantize(a: np.ndarray, elem: str):
+    """MX conversion of a [R, C] array (C % 32 == 0) along its rows, as the
+    OCP MX specification defines it: per block of 32, shared exponent
+    floor(log2(amax)) - emax_elem (clamped to the E8M0 range [-127, 127];
+    an all-zero block takes -127), X = 2^shared; element = the element
+    format's rounding of v / X (round to nearest even, saturating to its
+    largest normal).  elem: "e2m1" (MXFP4) or "e4m3" (MXFP8).
+    Returns (element codes uint8 [R, C], E8M0 codes uint8 [R, C/32])."""
+    a = np.asarray(a, dtype=np.float64)
+    R, C = a.shape
+    assert C % MX_BLOCK == 0
+    g = a.reshape(R, C // MX_BLOCK, MX_BLOCK)
+    amax = np.abs(g).max(axis=2)
+    emax = _E2M1_EMAX if elem == "e2m1" else _E4M3_EMAX
+    _, ex = np.frexp(np.where(amax > 0, amax, 1.0))
+    shared = np.where(amax > 0, ex - 1 - emax, -127)
+    shared = np.clip(shared, -127, 127)
+    quot = np.ldexp(g, -shared[:, :, None])               # exact: a power of two
+    enc = e2m1_encode if elem == "e2m1" else e4m3_encode
+    codes = enc(quot).reshape(R, C)
+    return codes, (shared + 127).astype(np.uint8)
+
+
+def mx_dequantize(codes: np.ndarray, scales: np.ndarray, elem: str) -> np.ndarray:
+    """code value * 2^(scale - 127) per block of 32 along the rows."""
+    val = e2m1_value(codes) if elem == "e2m1" else e4m3_value(codes)
+    R, C = val.shape
+    x = np.repeat(e8m0_value(scales), MX_BLOCK, axis=1)
+    return val * x
 
 
 def quantize_blocks(a: np.ndarray, block_rows: int, block_cols: int):
@@ -467,10 +561,14 @@ def combine(y_perm: np.ndarray, token_slot_row: np.ndarray, w: np.ndarray,
 # Whole layer
 # ----------------------------------------------------------------------------
 
-def _expert_weights(weights: dict, fp8: bool):
+def _expert_weights(weights: dict, fp8: bool, mx: bool = False):
     """Float64 weight accessors.  bf16: the exact values.  fp8: the exact
     dequantisation (code * block scale) of the block-FP8 weights, which are
-    the layer's parameters."""
+    the layer's parameters.  mx: the same for MXFP4 weights (E2M1 codes
+    "w13_q"/"w2_q" and E8M0 scales "w13_s"/"w2_s" per 32 along K)."""
+    if mx:
+        return (lambda e: mx_dequantize(weights["w13_q"][e], weights["w13_s"][e], "e2m1"),
+                lambda e: mx_dequantize(weights["w2_q"][e], weights["w2_s"][e], "e2m1"))
     if not fp8:
         return (lambda e: bf16_to_f64(weights["w13"][e]),
                 lambda e: bf16_to_f64(weights["w2"][e]))
@@ -478,9 +576,12 @@ def _expert_weights(weights: dict, fp8: bool):
             lambda e: dequantize_blocks(weights["w2_q"][e], weights["w2_s"][e], 128, 128))
 
 
-def _shared_weights(weights: dict, fp8: bool):
+def _shared_weights(weights: dict, fp8: bool, mx: bool = False):
     if "ws13" not in weights and "ws13_q" not in weights:
         return None
+    if mx:
+        return (mx_dequantize(weights["ws13_q"], weights["ws13_s"], "e2m1"),
+                mx_dequantize(weights["ws2_q"], weights["ws2_s"], "e2m1"))
     if not fp8:
         return bf16_to_f64(weights["ws13"]), bf16_to_f64(weights["ws2"])
     return (dequantize_blocks(weights["ws13_q"], weights["ws13_s"], 128, 128),
@@ -496,11 +597,20 @@ def fp8_activation(a: np.ndarray) -> np.ndarray:
     return dequantize_blocks(q, s, 1, 128)
 
 
+def mx8_activation(a: np.ndarray) -> np.ndarray:
+    """The value an activation row block carries after MXFP8 packing (E4M3
+    elements, one E8M0 scale per 32 consecutive elements of a token): the
+    activation format that goes with MXFP4 weights here."""
+    q, s = mx_quantize(a, "e4m3")
+    return mx_dequantize(q, s, "e4m3")
+
+
 def moe_layer(logits: np.ndarray, x_bits: np.ndarray, weights: dict, *,
               k: int, e_lo: int, E_L: int, fp8: bool = False,
               quantize_activations: bool = False,
               activation: str = "swiglu",
-              capacity: Optional[int] = None) -> Dict[str, np.ndarray]:
+              capacity: Optional[int] = None,
+              mx: bool = False) -> Dict[str, np.ndarray]:
     """The whole layer for one GPU's local experts, every stage kept.
 
     ``weights``: bf16 -> "w13" [E_L, m*I, H] (m = 2 for SwiGLU, 1 for the
@@ -514,6 +624,10 @@ def moe_layer(logits: np.ndarray, x_bits: np.ndarray, weights: dict, *,
     activation and quantisation operations between the two expert GEMMs).
     The default leaves them exact: the reference the output gate measures.
 
+    ``mx`` takes MXFP4 weights (see _expert_weights); with
+    ``quantize_activations`` x and h then pass through MXFP8 (per-token
+    blocks of 32 with E8M0 scales) instead of block-FP8.
+
     ``capacity`` (optional) runs the layer over the masked fixed-capacity
     layout (index_build_masked / grouped_ffn_masked) instead of the
     contiguous one; the stage arrays are then in that layout.
@@ -526,21 +640,22 @@ def moe_layer(logits: np.ndarray, x_bits: np.ndarray, weights: dict, *,
     masked = capacity is not None
     ix = index_build_masked(ids, e_lo, E_L, capacity) if masked else index_build(ids, e_lo, E_L)
     x = bf16_to_f64(x_bits)
-    qa = fp8 and quantize_activations
-    xq = fp8_activation(x) if qa else x
+    qa = (fp8 or mx) and quantize_activations
+    act_q = mx8_activation if mx else fp8_activation
+    xq = act_q(x) if qa else x
     if masked:                                   # unused rows of a block stay zero
         x_perm = np.zeros((len(ix["row_token"]), x.shape[1]), dtype=np.float64)
         used = ix["row_token"] >= 0
         x_perm[used] = dispatch(xq, ix["row_token"][used])
     else:
         x_perm = dispatch(xq, ix["row_token"])
-    g13, g2 = _expert_weights(weights, fp8)
-    h_fn = fp8_activation if qa else None
+    g13, g2 = _expert_weights(weights, fp8, mx)
+    h_fn = act_q if qa else None
     if masked:
         h, y_perm = grouped_ffn_masked(x_perm, ix["counts"], capacity, g13, g2, h_fn, activation)
     else:
         h, y_perm = grouped_ffn(x_perm, ix["offsets"], g13, g2, h_fn, activation)
-    sw = _shared_weights(weights, fp8)
+    sw = _shared_weights(weights, fp8, mx)
     shared = None
     if sw is not None:
         shared = expert_ffn(xq, sw[0], sw[1], h_fn, activation)[1]
@@ -553,7 +668,7 @@ def moe_layer(logits: np.ndarray, x_bits: np.ndarray, weights: dict, *,
 def moe_layer_tokens(logits: np.ndarray, x_bits: np.ndarray, weights: dict,
                      tokens, *, k: int, e_lo: int, E_L: int,
                      fp8: bool = False, quantize_activations: bool = False,
-                     activation: str = "swiglu") -> np.ndarray:
+                     activation: str = "swiglu", mx: bool = False) -> np.ndarray:
     """Layer output rows for a few tokens only, one token at a time (for
     spot checks at sizes where the whole layer is too slow on the CPU).
     A token's output depends only on its own logits and activations, so
@@ -562,12 +677,13 @@ def moe_layer_tokens(logits: np.ndarray, x_bits: np.ndarray, weights: dict,
     tokens = np.asarray(tokens, dtype=np.int64)
     ids, w = route(logits[tokens], k)
     x = bf16_to_f64(x_bits[tokens])
-    qa = fp8 and quantize_activations
+    qa = (fp8 or mx) and quantize_activations
+    act_q = mx8_activation if mx else fp8_activation
     if qa:
-        x = fp8_activation(x)       # per-token groups: same rows as for the whole batch
-    h_fn = fp8_activation if qa else None
-    g13, g2 = _expert_weights(weights, fp8)
-    sw = _shared_weights(weights, fp8)
+        x = act_q(x)                # per-token groups: same rows as for the whole batch
+    h_fn = act_q if qa else None
+    g13, g2 = _expert_weights(weights, fp8, mx)
+    sw = _shared_weights(weights, fp8, mx)
     y = np.zeros_like(x)
     # Group the requested tokens by local expert so each expert's weights are
     # decoded once.

@@ -24,7 +24,9 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}   # MI355X dense MFMA
+# MI355X dense MFMA; the MX path runs E2M1 x E4M3 instructions, priced at the
+# fp8 rate (the 10.1 PF fp4 figure needs both operands in fp4)
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "mxfp4": 5000.0}
 PEAK_HBM_GBS = 8000.0
 
 
@@ -82,14 +84,16 @@ def stored_traffic(workload: str):
     return rec.get("bytes_per_launch")
 
 
-def gemm_rows(counts, fp8: bool, max_pairs: int, E_L: int) -> int:
+def gemm_rows(counts, fp8: bool, max_pairs: int, E_L: int, mx: bool = False) -> int:
     """Token rows the GEMMs compute, padding included, under the library's
     tile choice (from the most pairs per expert on average, T min(k, E_L) /
     E_L): bf16 32-row tiles up to 32; 128-row tiles up to 256; else 256-row
     tiles (bf16: a last remainder of 1..128 rows takes a 128-row wide tile)."""
     rows = 0
     for c in (int(x) for x in counts):
-        if not fp8 and max_pairs // E_L <= 32:
+        if mx:                                   # MX: 128-row tiles throughout
+            rows += -(-c // 128) * 128
+        elif not fp8 and max_pairs // E_L <= 32:
             rows += -(-c // 32) * 32
         elif max_pairs // E_L <= 256:
             rows += -(-c // 128) * 128
@@ -120,8 +124,9 @@ def main():
     dev_id = int(os.environ.get("LOCAL_RANK", "0"))
     torch.cuda.set_device(dev_id)
     d = synth.make_inputs(cfg, seed)
-    panel = args.layout == "panel" and not cfg.fp8
-    dev = dv.upload(d, cfg.fp8, panel=panel)   # load-time packing, outside any timing
+    quant = cfg.fp8 or cfg.mx          # quantised GEMM activations with per-row scales
+    panel = args.layout == "panel" and not quant
+    dev = dv.upload(d, cfg.fp8, panel=panel, mx=cfg.mx)   # load-time conversion, untimed
     # Layouts of moe_layer's own path: panel weights as loaded, panel h.
     cap = cfg.T if args.masked else 0
     p = ml.Problem.from_config(
@@ -129,7 +134,7 @@ def main():
         capacity=cap)
     p_layer = ml.Problem.from_config(cfg, layout=ml.LAYOUT_PANEL_WEIGHTS if panel else 0,
                                      capacity=cap)
-    W = dv.weights_of(dev, cfg.fp8)
+    W = dv.weights_of(dev, quant)
     stream = torch.cuda.current_stream()
     T, k, H, N = p.T, p.k, p.H, p.n_cap
     i32 = dict(dtype=torch.int32, device="cuda")
@@ -141,16 +146,20 @@ def main():
     y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
     ws_d = dv.workspace(p, ml.STAGE_DISPATCH)
     ws_f = dv.workspace(p, ml.STAGE_FFN)
-    if cfg.fp8:
+    if quant:
+        # activation scales: fp32 per 128 (block-FP8) or E8M0 bytes per 32 (MX)
+        sc = dict(dtype=torch.uint8, device="cuda") if cfg.mx else \
+            dict(dtype=torch.float32, device="cuda")
+        g = 32 if cfg.mx else 128
         xp = torch.empty((N, H), dtype=torch.uint8, device="cuda")
-        xs = torch.empty((N, H // 128), dtype=torch.float32, device="cuda")
+        xs = torch.empty((N, H // g), **sc)
         if p.I_s:
-            q = ml.Problem(T=T, H=H, E=1, k=1, e_lo=0, E_L=1, I=p.I_s, fp8=True)
+            q = ml.Problem(T=T, H=H, E=1, k=1, e_lo=0, E_L=1, I=p.I_s, fp8=cfg.fp8, mx=cfg.mx)
             off2 = torch.tensor([0, T], **i32)
             sw = ml.weights_struct(dev["ws13_q"], dev["ws2_q"], None, None, dev["ws13_s"],
                                    dev["ws2_s"])
             sx = torch.empty((T, H), dtype=torch.uint8, device="cuda")
-            sxs = torch.empty((T, H // 128), dtype=torch.float32, device="cuda")
+            sxs = torch.empty((T, H // g), **sc)
             shared = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
             ws_s = dv.workspace(q, ml.STAGE_FFN)
 
@@ -167,7 +176,7 @@ def main():
         rec(0)
         ml.moe_route(p, dev["logits"], ids, tw, stream)
         rec(1)
-        if not cfg.fp8:
+        if not quant:
             ml.moe_dispatch(p, dev["x"], ids, counts, offsets, rt, rs, tsr, None, None, ws_d,
                             stream)
             rec(2)
@@ -180,7 +189,10 @@ def main():
             ml.moe_grouped_ffn(p, xp, xs, seg, W, None, None, yp, ws_f, stream)
             sh = None
             if p.I_s:
-                ml.moe_quantize_fp8(dev["x"], 1, T, H, 1, sx, sxs, stream)
+                if cfg.mx:
+                    ml.moe_quantize_mx(dev["x"], 1, T, H, ml.MX_E4M3, sx, sxs, stream)
+                else:
+                    ml.moe_quantize_fp8(dev["x"], 1, T, H, 1, sx, sxs, stream)
                 ml.moe_grouped_ffn(q, sx, sxs, off2, sw, None, None, shared, ws_s, stream)
                 sh = shared
             rec(3)
@@ -222,15 +234,17 @@ def main():
     # 2 m H I (up, m first-layer matrices) + 2 H I (down) per row (Eq. 8)
     mm = 2.0 * (p.m + 1)
     flops = mm * p.H * p.I * n_pairs + mm * p.H * p.I_s * p.T
-    dtype = "fp8" if cfg.fp8 else "bf16"
-    beta_w = 1 if cfg.fp8 else 2
+    dtype = "mxfp4" if cfg.mx else "fp8" if cfg.fp8 else "bf16"
+    # bytes per weight element (MXFP4: half a byte plus one E8M0 byte per 32)
+    beta_w = 0.5 + 1 / 32 if cfg.mx else 1 if cfg.fp8 else 2
+    beta_a = 1 + 1 / 32 if cfg.mx else 1 if cfg.fp8 else 2   # GEMM activation bytes
     active = int((cnt > 0).sum())
     ffn_tflops = flops / (ffn_ms * 1e-3) / 1e12
-    padded_rows = gemm_rows(cnt, cfg.fp8, p.T * min(p.k, p.E_L), p.E_L)
+    padded_rows = gemm_rows(cnt, quant, p.T * min(p.k, p.E_L), p.E_L, cfg.mx)
 
     traffic = stored_traffic(cfg.name + ("_masked" if cap else ""))
     act = "SwiGLU" if cfg.act == "swiglu" else "GELU"
-    skinny = not cfg.fp8 and p.T * min(p.k, p.E_L) // p.E_L <= 32
+    skinny = not quant and p.T * min(p.k, p.E_L) // p.E_L <= 32
     kernel = ((f"grouped FFN: work table + one launch of up GEMM/{act} and down GEMM" if skinny
                else f"grouped FFN: work table + up GEMM/{act} + down GEMM")
               + (" (+ shared expert: x quantisation and its FFN)" if p.I_s else ""))
@@ -239,8 +253,8 @@ def main():
     if decode:
         # weight streaming: every active expert's W13 and W2 once, plus the
         # token rows in and out of both GEMMs
-        bytes_ = (active * (p.m + 1) * p.H * p.I * beta_w
-                  + n_pairs * (p.H * beta_w + 2 * p.I * beta_w + 2 * p.H))
+        bytes_ = int(active * (p.m + 1) * p.H * p.I * beta_w
+                     + n_pairs * (p.H * beta_a + 2 * p.I * beta_a + 2 * p.H))
         achieved = bytes_ / (ffn_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
@@ -258,7 +272,8 @@ def main():
     sample = args.cpu_sample_tokens
     if sample is None:
         sample = {"tiny": 256, "qwen3_30b_prefill": 4096, "dsv3_ep8_prefill": 128,
-                  "dsv3_ep8_prefill_fp8": 64, "dsv3_ep8_decode": 64}.get(cfg.name, 256)
+                  "dsv3_ep8_prefill_fp8": 64, "dsv3_ep8_decode": 64,
+                  "dsv3_ep8_prefill_mxfp4": 64, "dsv3_ep8_decode_mxfp4": 64}.get(cfg.name, 256)
     if sample > 0:
         cpu = cpu_baseline(cfg, d, sample)
 
@@ -431,7 +446,16 @@ def cpu_baseline(cfg, d, sample):
         threads = os.cpu_count() or 1
     T = min(sample, cfg.T)
     wd = d
-    if cfg.fp8:
+    if cfg.mx:
+        wd = {}
+        for name in ("w13", "w2"):
+            qs = [O.mx_quantize(O.bf16_to_f64(m), "e2m1") for m in d[name]]
+            wd[name + "_q"] = np.stack([q for q, _ in qs])
+            wd[name + "_s"] = np.stack([s for _, s in qs])
+        for name in ("ws13", "ws2"):
+            if name in d:
+                wd[name + "_q"], wd[name + "_s"] = O.mx_quantize(O.bf16_to_f64(d[name]), "e2m1")
+    elif cfg.fp8:
         wd = {}
         for name in ("w13", "w2"):
             qs = [O.quantize_blocks(O.bf16_to_f64(m), 128, 128) for m in d[name]]
@@ -441,7 +465,8 @@ def cpu_baseline(cfg, d, sample):
             if name in d:
                 wd[name + "_q"], wd[name + "_s"] = O.quantize_blocks(O.bf16_to_f64(d[name]), 128, 128)
     t0 = time.perf_counter()
-    O.moe_layer(d["logits"][:T], d["x"][:T], wd, k=cfg.k, e_lo=cfg.e_lo, E_L=cfg.E_L, fp8=cfg.fp8)
+    O.moe_layer(d["logits"][:T], d["x"][:T], wd, k=cfg.k, e_lo=cfg.e_lo, E_L=cfg.E_L, fp8=cfg.fp8,
+                mx=cfg.mx)
     dt = time.perf_counter() - t0
     return {"value": round(T / dt, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"first {T} of {cfg.T} tokens of {cfg.name}, whole layer (float64 numpy), "

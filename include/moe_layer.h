@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 5
+#define MOE_ABI_VERSION 6
 
 typedef enum {
   MOE_OK = 0,
@@ -68,10 +68,19 @@ typedef enum {
 
 typedef enum {
   MOE_BF16 = 0,      /* bf16 weights, bf16 GEMM activations                  */
-  MOE_FP8_E4M3 = 1   /* OCP E4M3FN weights with one fp32 scale per 128 x 128
+  MOE_FP8_E4M3 = 1,  /* OCP E4M3FN weights with one fp32 scale per 128 x 128
                         block; GEMM activations E4M3 with one fp32 scale per
                         token per 128 consecutive elements                   */
+  MOE_MXFP4 = 2      /* MXFP4 weights (OCP MX: E2M1 elements, one E8M0 scale
+                        per 32 consecutive K elements of a row); GEMM
+                        activations MXFP8 (E4M3, one E8M0 scale per token per
+                        32 elements).  Page "CascadeEP ...", section 4.1
+                        (MXFP4 routed-expert weights).  Layout 0, SwiGLU.   */
 } moe_dtype;
+
+/* MX element formats of moe_quantize_mx. */
+#define MOE_MX_E2M1 0
+#define MOE_MX_E4M3 1
 
 /* Storage layouts (moe_problem.layout bits; bf16 problems only, values are
  * never changed by a layout).  The panel layout of an [R, K] bf16 matrix
@@ -137,10 +146,16 @@ typedef struct {
  *   w2   [E_L, H, I]:  down projection
  *   ws13 [m I_s, H], ws2 [H, I_s]: shared expert (NULL when I_s == 0), same
  *        form as the routed experts
- * Element type: bf16 for MOE_BF16, E4M3 bytes for MOE_FP8_E4M3.
+ * Element type: bf16 for MOE_BF16, E4M3 bytes for MOE_FP8_E4M3; for MOE_MXFP4
+ * E2M1 codes two per byte, low nibble first ([E_L, m I, H/2] and
+ * [E_L, H, I/2]).
  * fp8 only, fp32 block scales (NULL for bf16):
  *   w13_scale [E_L, 2I/128, H/128], w2_scale [E_L, H/128, I/128],
- *   ws13_scale [2 I_s/128, H/128],  ws2_scale [H/128, I_s/128].            */
+ *   ws13_scale [2 I_s/128, H/128],  ws2_scale [H/128, I_s/128].
+ * MOE_MXFP4: the scale pointers carry E8M0 bytes (uint8, value 2^(e-127)),
+ * one per 32 K elements of a row: w13_scale [E_L, 2I, H/32], w2_scale
+ * [E_L, H, I/32], ws13_scale [2 I_s, H/32], ws2_scale [H, I_s/32] (see
+ * moe_quantize_mx).                                                        */
 typedef struct {
   const void* w13;
   const void* w2;
@@ -184,6 +199,8 @@ moe_status moe_route(const moe_problem* p, const float* logits,
  *   x_perm_scale [N_cap, H/128] fp32 (fp8 only; NULL for bf16): scale of each
  *              128-element group, amax/448 (1 for an all-zero group); code =
  *              round-to-nearest-even(v / scale) saturated to +-448.
+ *              MOE_MXFP4: x_perm holds MXFP8 (E4M3) codes and x_perm_scale
+ *              E8M0 bytes [N_cap, H/32] (moe_quantize_mx's rule).
  * Rows are ordered by local expert, then by token (contiguous segments, or
  * the expert's block in the masked layout).  Bit-exact and deterministic.  x_perm == NULL builds the index only (x_perm_scale is then
  * ignored; see moe_grouped_ffn_gather).
@@ -275,6 +292,20 @@ moe_status moe_layer(const moe_problem* p, const float* logits, const void* x,
 moe_status moe_quantize_fp8(const void* src, int64_t batch, int64_t rows,
                             int64_t cols, int32_t block_rows, void* codes,
                             float* scales, void* stream);
+
+/* MX conversion (OCP MX): for each block of 32 consecutive elements of a
+ * row of the [batch * rows, cols] bf16 matrix src, the E8M0 scale
+ * 2^(c - 127) with c = floor(log2 amax) - emax + 127, clamped to [0, 254]
+ * (an all-zero block takes 0; emax = 2 for E2M1, 8 for E4M3), and the
+ * elements round-to-nearest-even(v / 2^(c - 127)) saturated to the largest
+ * normal (6 or 448).  Page "CascadeEP ...", section 4.1 (MXFP4 routed-expert
+ * weights, converted at load time); the format is the OCP MX one.
+ *   elem MOE_MX_E2M1: codes [.., cols/2] (two per byte, low nibble first)
+ *   elem MOE_MX_E4M3: codes [.., cols] (cols % 128 == 0)
+ *   scales [.., cols/32] uint8.  cols % 32 == 0, cols <= 2^20.              */
+moe_status moe_quantize_mx(const void* src, int64_t batch, int64_t rows,
+                           int64_t cols, int32_t elem, void* codes,
+                           void* scales, void* stream);
 
 /* Panel packing of bf16 matrices (see MOE_LAYOUT_PANEL_WEIGHTS): for each of
  * `batch` matrices src [rows, cols] (row major), dst receives the same values

@@ -354,6 +354,109 @@ __global__ __launch_bounds__(256) void quant_blocks_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// MX formats (OCP MX): blocks of 32 consecutive elements of a row share one
+// E8M0 scale 2^(c - 127), c = floor(log2 amax) - emax + 127 clamped to
+// [0, 254] (an all-zero block takes c = 0); elements are the element
+// format's round-to-nearest-even of v / 2^(c - 127), saturated.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int mx_code(float amax, int emax) {
+  const int e = static_cast<int>((__float_as_uint(amax) >> 23) & 0xff);
+  if (e == 0) return 0;  // zero or subnormal: at or below 2^-127
+  const int s = e - 127 - emax;
+  return (s < -127 ? -127 : s) + 127;
+}
+
+// E2M1 code of v (already divided by the block scale): nearest of 0, 0.5, 1,
+// 1.5, 2, 3, 4, 6, a tie going to the even mantissa bit, beyond 6 saturated.
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  const float a = fabsf(v);
+  uint32_t c;
+  if (a <= 0.25f) c = 0;
+  else if (a < 0.75f) c = 1;
+  else if (a <= 1.25f) c = 2;
+  else if (a < 1.75f) c = 3;
+  else if (a <= 2.5f) c = 4;
+  else if (a < 3.5f) c = 5;
+  else if (a <= 5.0f) c = 6;
+  else c = 7;
+  return c | (__float_as_uint(v) >> 31 << 3);
+}
+
+// MXFP4 conversion of bf16 rows (weights at load time): one thread per block
+// of 32 elements; codes two per byte, low nibble first.
+__global__ __launch_bounds__(256) void quant_mx4_kernel(const uint4* __restrict__ src,
+                                                        int64_t blocks, uint4* __restrict__ codes,
+                                                        uint8_t* __restrict__ scales) {
+  for (int64_t b = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; b < blocks;
+       b += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    float f[32];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 v = src[b * 4 + i];
+      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f[8 * i + 2 * j] = __uint_as_float(wv[j] << 16);
+        f[8 * i + 2 * j + 1] = __uint_as_float(wv[j] & 0xFFFF0000u);
+      }
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(f[i]));
+    const int c = mx_code(amax, 2);
+    uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 32; ++i) w[i / 8] |= e2m1_code(ldexpf(f[i], 127 - c)) << (4 * (i % 8));
+    codes[b] = make_uint4(w[0], w[1], w[2], w[3]);
+    scales[b] = static_cast<uint8_t>(c);
+  }
+}
+
+// Row gather with MXFP8 packing: dst[j] = E4M3 codes of src[rows[j]] with one
+// E8M0 scale per 32 elements (rows == nullptr: identity); masked-layout rows
+// that hold no pair are skipped.  One wavefront per row; four lanes (8
+// elements each) make a block.
+__global__ __launch_bounds__(256) void gather_rows_mx8_kernel(
+    const uint4* __restrict__ src, const int32_t* __restrict__ rows,
+    const int32_t* __restrict__ n_rows, int n_rows_host, int H,
+    const int32_t* __restrict__ counts, int cap,
+    uint2* __restrict__ dst, uint8_t* __restrict__ dst_scale) {
+  const int n = n_rows ? *n_rows : n_rows_host;
+  const int chunks = H >> 3;
+  const int wpb = blockDim.x >> 6;
+  const int lane = lane_id();
+  for (int j = blockIdx.x * wpb + (threadIdx.x >> 6); j < n; j += gridDim.x * wpb) {
+    if (!masked_row_used(counts, cap, j)) continue;  // uniform over the wave
+    const int r = rows ? rows[j] : j;
+    const uint4* s = src + static_cast<size_t>(r) * chunks;
+    uint2* d = dst + static_cast<size_t>(j) * chunks;
+    // chunks is a multiple of 16, so the four lanes of a block are all active
+    for (int c = lane; c < chunks; c += kWave) {
+      const uint4 v = s[c];
+      float f[8];
+      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __uint_as_float(wv[i] << 16);
+        f[2 * i + 1] = __uint_as_float(wv[i] & 0xFFFF0000u);
+      }
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+      amax = fmaxf(amax, __shfl_xor(amax, 1));
+      amax = fmaxf(amax, __shfl_xor(amax, 2));
+      const int code = mx_code(amax, 8);
+      const int sh = 127 - code;
+      uint2 q;
+      q.x = f32x4_to_e4m3x4(ldexpf(f[0], sh), ldexpf(f[1], sh), ldexpf(f[2], sh), ldexpf(f[3], sh));
+      q.y = f32x4_to_e4m3x4(ldexpf(f[4], sh), ldexpf(f[5], sh), ldexpf(f[6], sh), ldexpf(f[7], sh));
+      d[c] = q;
+      if ((lane & 3) == 0) dst_scale[static_cast<size_t>(j) * (H >> 5) + (c >> 2)] = code;
+    }
+  }
+}
+
 }  // namespace
 
 size_t index_scratch_bytes(int T, int E_L) {
@@ -432,6 +535,25 @@ hipError_t launch_quant_blocks(const void* src, int64_t batch, int64_t rows, int
   hipLaunchKernelGGL(quant_blocks_kernel, grid, dim3(256), 0, s,
                      static_cast<const uint16_t*>(src), rows, cols,
                      static_cast<uint8_t*>(codes), scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_mx4(const void* src, int64_t rows, int64_t cols, void* codes,
+                            uint8_t* scales, hipStream_t s) {
+  const int64_t blocks = rows * (cols / 32);
+  const int64_t grid = (blocks + 255) / 256;
+  hipLaunchKernelGGL(quant_mx4_kernel, dim3(static_cast<unsigned>(grid < 65536 ? grid : 65536)),
+                     dim3(256), 0, s, static_cast<const uint4*>(src), blocks,
+                     static_cast<uint4*>(codes), scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_mx8(const void* src, const int32_t* rows, const int32_t* n_rows,
+                             int64_t max_rows, int H, void* dst, uint8_t* dst_scale,
+                             hipStream_t s, const int32_t* counts, int cap) {
+  hipLaunchKernelGGL(gather_rows_mx8_kernel, dim3(gather_grid(max_rows)), dim3(256), 0, s,
+                     static_cast<const uint4*>(src), rows, n_rows, static_cast<int>(max_rows), H,
+                     counts, cap, static_cast<uint2*>(dst), dst_scale);
   return hipGetLastError();
 }
 

@@ -52,7 +52,8 @@ constexpr int kBN = 256;      // weight rows per block
 constexpr int kThreads = 256;
 constexpr int kXcds = 8;
 
-enum { MODE_PLAIN = 0, MODE_SWIGLU = 1, MODE_SWIGLU_FP8OUT = 2, MODE_GELU = 3 };
+enum { MODE_PLAIN = 0, MODE_SWIGLU = 1, MODE_SWIGLU_FP8OUT = 2, MODE_GELU = 3,
+       MODE_SWIGLU_MX8OUT = 4 };
 
 // Exact GELU, a * Phi(a) = a erfc(-a / sqrt 2) / 2, in fp32 (the up GEMM's
 // epilogue of the standard MLP).
@@ -776,6 +777,257 @@ hipError_t launch_fused(const GemmArgs& gu, const GemmArgs& gd, int64_t max_tile
 }
 
 // ---------------------------------------------------------------------------
+// MXFP4 weights x MXFP8 activations (OCP MX formats: E2M1 and E4M3 elements,
+// one E8M0 scale 2^(e - 127) per 32 consecutive K elements of a row) on the
+// block-scaled matrix instruction v_mfma_scale_f32_32x32x64_f8f6f4, which
+// applies both operands' scales inside the matrix core: no promotion step.
+// Operand placement of one 32 x 32 x 64 instruction (measured on gfx950):
+//   weights (A, E2M1): lane l holds weight row l % 32 and K [32 (l/32), +32),
+//     16 bytes, low nibble first, and the E8M0 scale of that block;
+//   tokens (B, E4M3): lane l holds token l % 32 and K [16 (l/32), +16) and
+//     [32 + 16 (l/32), +16), and the E8M0 scale of block l / 32.
+// Block tile 128 tokens x 256 weight rows, 4 waves of 64 x 128 (2 x 4 tiles,
+// SwiGLU: the gate and up rows of the same 64 h columns); K steps of 128
+// (64 bytes of E2M1 and 128 of E4M3 per row, 4 scale bytes each) through a
+// four-stage LDS ring fed three steps ahead by direct-to-LDS loads.  The up
+// GEMM's epilogue writes h as MXFP8: each 32-column block of one token is one
+// instruction tile, split over lanes l and l ^ 32.
+// ---------------------------------------------------------------------------
+constexpr int kMxBM = 128, kMxBN = 256, kMxThreads = 256, kMxStages = 4;
+constexpr int kMxK = 128;                                  // K elements per step
+constexpr int kMxWOff = kMxBM * kMxK;                      // token rows [128][128 B] first
+constexpr int kMxSAOff = kMxWOff + kMxBN * (kMxK / 2);     // weight rows [256][64 B]
+constexpr int kMxSWOff = kMxSAOff + kMxBM * 4;             // token scales [128] dwords
+constexpr int kMxStageBytes = kMxSWOff + kMxBN * 4;        // weight scales [256] dwords
+constexpr int kMxLoads = 4 + 4 + 1 + 1;                    // direct loads per wave and step
+static_assert(kMxStages * kMxStageBytes <= 160 * 1024, "the ring fits the CU's LDS");
+
+// E8M0 exponent (biased) of a block whose largest magnitude is amax, for an
+// element format whose largest normal has exponent emax: floor(log2 amax) -
+// emax, clamped to the scale's range (an all-zero block takes 2^-127).
+__device__ __forceinline__ int mx_scale_code(float amax, int emax) {
+  const int e = static_cast<int>((__float_as_uint(amax) >> 23) & 0xff);
+  if (e == 0) return 0;                       // zero or subnormal: at or below 2^-127
+  const int s = e - 127 - emax;
+  return (s < -127 ? -127 : s) + 127;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kMxThreads, 1) void gemm_mx_kernel(const GemmArgs g) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  constexpr bool kSwiglu = MODE == MODE_SWIGLU_MX8OUT;
+  const int total = *g.n_tiles * g.nt_n;
+  const int per_xcd = ceil_div(total, kXcds);
+  const int slot = blockIdx.x / kXcds;
+  if (slot >= per_xcd) return;
+  const int t = (blockIdx.x % kXcds) * per_xcd + slot;
+  if (t >= total) return;
+  const int4 inf = g.info[t / g.nt_n];
+  const int e = inf.x, u = t - inf.y * g.nt_n;
+  const int nt = u / inf.z, mt = u % inf.z;
+  const int2 sg = segment(g.seg, g.seg_cap, e);
+  const int seg_end = sg.y;
+  const int row0 = sg.x + mt * kMxBM;
+  const int K = g.K, kb = K / 32;                 // scale bytes per row
+  const int nk = K / kMxK;
+  const uint8_t* As = reinterpret_cast<const uint8_t*>(g.A_scale);
+  const uint8_t* Ws = reinterpret_cast<const uint8_t*>(g.W_scale);
+  const int64_t a_skip = static_cast<int64_t>(row0) * K;
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(g.A + a_skip, g.a_bytes - a_skip);
+  const __amdgpu_buffer_rsrc_t rW = make_rsrc(g.W + e * g.w_stride, g.w_stride);
+  const __amdgpu_buffer_rsrc_t rAS =
+      make_rsrc(As + static_cast<int64_t>(row0) * kb, (g.a_bytes / K - row0) * kb);
+  const __amdgpu_buffer_rsrc_t rWS = make_rsrc(Ws + e * g.ws_stride, g.ws_stride);
+  const int nbase = kSwiglu ? nt * (kMxBN / 2) : nt * kMxBN;
+  auto wrow = [&](int r) {  // weight row (within the expert) of tile row r
+    if (kSwiglu)
+      return r < kMxBN / 2 ? min(nbase + r, g.Nout - 1)
+                           : g.Nout + min(nbase + (r - kMxBN / 2), g.Nout - 1);
+    return min(nbase + r, g.NW - 1);
+  };
+
+  const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
+  // Direct loads of wave w per step: token row groups (8 rows of 128 B)
+  // 4w..4w+3, weight row groups (16 rows of 64 B) 4w..4w+3, 64 weight scale
+  // dwords (rows 64w..) and 64 token scale dwords (rows 64 (w & 1)..; waves
+  // w and w ^ 2 write the same values to the same place).  A direct load
+  // writes one dword per lane, so scales move as whole dwords.
+  int voff[kMxLoads];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int rr = (w * 4 + q) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((rr >> 1) & 7);
+    voff[q] = row0 + rr < seg_end ? rr * K + c * 16 : kOobOffset;
+    const int r = (w * 4 + q) * 16 + (lane >> 2);
+    const int cw = (lane & 3) ^ ((r >> 2) & 3);
+    voff[4 + q] = wrow(r) * (K / 2) + cw * 16;
+  }
+  voff[8] = wrow(w * 64 + lane) * kb;
+  {
+    const int rr = (w & 1) * 64 + lane;
+    voff[9] = row0 + rr < seg_end ? rr * kb : kOobOffset;
+  }
+  auto dma = [&](int step, int stage) {
+    const int k = min(step, nk - 1);
+    uint8_t* base = smem + stage * kMxStageBytes;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr_t)(base + (w * 4 + q) * 1024), 16,
+                                               voff[q], k * kMxK, 0, 0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, (lds_ptr_t)(base + kMxWOff + (w * 4 + q) * 1024),
+                                               16, voff[4 + q], k * (kMxK / 2), 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rWS, (lds_ptr_t)(base + kMxSWOff + w * 256), 4,
+                                             voff[8], k * 4, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rAS, (lds_ptr_t)(base + kMxSAOff + (w & 1) * 256),
+                                             4, voff[9], k * 4, 0, 0);
+  };
+
+  // Fragment addresses: wave (wm, wn) holds tokens wm*64.. and weight rows
+  // wblock_row(i) + (lane % 32) for its four weight tiles.
+  const int wm = w >> 1, wn = w & 1;
+  const int lr = lane & 31, hi = lane >> 5;
+  int wfr[4][2], wsc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = wblock_row(kSwiglu, wn, i) + lr;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+      wfr[i][hh] = kMxWOff + r * 64 + (((2 * hh + hi) ^ ((r >> 2) & 3)) * 16);
+    wsc[i] = kMxSWOff + r * 4;
+  }
+  int tfr[2][2][2], tsc[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int rr = wm * 64 + j * 32 + lr;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      tfr[j][hh][0] = rr * kMxK + (((4 * hh + hi) ^ ((rr >> 1) & 7)) * 16);
+      tfr[j][hh][1] = rr * kMxK + (((4 * hh + 2 + hi) ^ ((rr >> 1) & 7)) * 16);
+    }
+    tsc[j] = kMxSAOff + rr * 4;
+  }
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+#pragma unroll
+  for (int st = 0; st < kMxStages - 1; ++st) dma(st, st);
+  WAIT_VMCNT((kMxStages - 2) * kMxLoads);
+  __builtin_amdgcn_s_barrier();
+
+  int s_cur = 0;
+  for (int kt = 0; kt < nk; ++kt) {
+    const uint8_t* st = smem + s_cur * kMxStageBytes;
+    dma(kt + kMxStages - 1, s_cur == 0 ? kMxStages - 1 : s_cur - 1);
+    uint32_t ws[4], ts[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ws[i] = *reinterpret_cast<const uint32_t*>(st + wsc[i]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) ts[j] = *reinterpret_cast<const uint32_t*>(st + tsc[j]);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      i32x8 tb[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const i32x4 p0 = *reinterpret_cast<const i32x4*>(st + tfr[j][hh][0]);
+        const i32x4 p1 = *reinterpret_cast<const i32x4*>(st + tfr[j][hh][1]);
+        tb[j] = i32x8{p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const i32x4 p = *reinterpret_cast<const i32x4*>(st + wfr[i][hh]);
+        const i32x8 wa = i32x8{p[0], p[1], p[2], p[3], 0, 0, 0, 0};
+        const int sa = static_cast<int>((ws[i] >> (16 * hh + 8 * hi)) & 0xff);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int sb = static_cast<int>((ts[j] >> (16 * hh + 8 * hi)) & 0xff);
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wa, tb[j], acc[i][j], 4, 0,
+                                                                       0, sa, 0, sb);
+        }
+      }
+    }
+    WAIT_VMCNT_LDS((kMxStages - 2) * kMxLoads);
+    __builtin_amdgcn_s_barrier();
+    s_cur = s_cur + 1 == kMxStages ? 0 : s_cur + 1;
+  }
+  WAIT_VMCNT(0);
+
+  // accumulator element q*4 + r: weight row q*8 + (lane/32)*4 + r of the
+  // tile, token lane % 32
+  const int cq = hi * 4;
+  uint8_t* C8 = static_cast<uint8_t*>(g.C);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int m = row0 + wm * 64 + j * 32 + lr;
+    const bool live = m < seg_end;
+    if constexpr (MODE == MODE_PLAIN) {
+      if (!live) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = nbase + wn * 128 + i * 32 + q * 8 + cq;
+          if (col >= g.Nout) continue;
+          uint2 o;
+          o.x = pack_bf16x2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]);
+          o.y = pack_bf16x2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
+          *reinterpret_cast<uint2*>(C8 + (static_cast<int64_t>(m) * g.Nout + col) * 2) = o;
+        }
+    } else {
+      // h = silu(gate) * up; one 32-column MX block per (i, token), held by
+      // lanes l and l ^ 32 (shuffles run in every lane, live or not)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        float hv[16];
+        float amax = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          hv[r] = silu_mul(acc[i][j][r], acc[i + 2][j][r]);
+          amax = fmaxf(amax, fabsf(hv[r]));
+        }
+        amax = fmaxf(amax, __shfl_xor(amax, 32));
+        const int code = mx_scale_code(amax, 8);
+        const int c0 = nbase + wn * 64 + i * 32;   // first h column of the block
+        if (!live || c0 >= g.Nout) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float* v = hv + q * 4;
+          const uint32_t p = f32x4_to_e4m3x4(ldexpf(v[0], 127 - code), ldexpf(v[1], 127 - code),
+                                             ldexpf(v[2], 127 - code), ldexpf(v[3], 127 - code));
+          *reinterpret_cast<uint32_t*>(C8 + static_cast<int64_t>(m) * g.Nout + c0 + q * 8 + cq) = p;
+        }
+        if (hi == 0) reinterpret_cast<uint8_t*>(g.C_scale)[static_cast<int64_t>(m) * (g.Nout / 32) + c0 / 32] =
+            static_cast<uint8_t>(code);
+      }
+    }
+  }
+}
+
+template <int MODE>
+hipError_t launch_mx(const GemmArgs& g, int64_t max_tiles, hipStream_t s) {
+  auto kern = gemm_mx_kernel<MODE>;
+  const size_t lds = kMxStages * kMxStageBytes;
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(lds)) != hipSuccess)
+      (void)hipGetLastError();
+    attr_set = true;
+  }
+  const int64_t blocks = (max_tiles * g.nt_n + kXcds - 1) / kXcds * kXcds + kXcds;
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(kMxThreads), lds, s, g);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Large-tile bf16 kernel, 8 waves (two per SIMD), each wave 64 x 128 output
 // elements (2 x 4 MFMA 32x32 tiles).  Two block shapes share the code:
 //   full tile: 256 token rows x 256 weight rows, waves 4 (rows) x 2 (weights);
@@ -1470,6 +1722,7 @@ int gemm_path_rows(GemmPath path) {
     case GEMM_PIPELINED: return kBM;
     case GEMM_LARGE: return kBigBM;
     case GEMM_LARGE_FP8: return kF8BM;
+    case GEMM_MX: return kMxBM;
   }
   return kBM;
 }
@@ -1524,6 +1777,20 @@ static hipError_t make_args(const GemmLaunch& L, GemmArgs& g) {
   g.Nout = L.Nout;
   g.NW = L.swiglu ? 2 * L.Nout : L.Nout;
   g.nt_n = gemm_n_tiles(L.swiglu, L.Nout);
+  if (L.mx != (L.path == GEMM_MX)) return hipErrorInvalidValue;
+  if (L.mx) {  // E4M3 tokens, E2M1 weights, E8M0 bytes per 32 along K; row major
+    if (L.fp8 || L.a_panel || L.w_panel || L.c_panel || L.a_index || L.gelu || L.K % kMxK)
+      return hipErrorInvalidValue;
+    if (L.swiglu && !L.C_scale) return hipErrorInvalidValue;
+    g.w_stride = static_cast<int64_t>(g.NW) * (L.K / 2);
+    g.ws_stride = static_cast<int64_t>(g.NW) * (L.K / 32);
+    g.a_rs = L.K;
+    g.a_cs = 64;
+    g.w_rs = L.K / 2;
+    g.w_cs = 64;
+    g.a_bytes = L.a_rows * L.K;
+    return hipSuccess;
+  }
   const int64_t elem = L.fp8 ? 1 : 2;
   const int64_t ldb = L.K * elem;
   g.w_stride = static_cast<int64_t>(g.NW) * ldb;
@@ -1555,6 +1822,9 @@ hipError_t launch_grouped_gemm(const GemmLaunch& L, hipStream_t s) {
                       : launch_big<MODE_PLAIN>(g, L.max_tiles, s);
     case GEMM_SKINNY:
       return hipErrorInvalidValue;  // both GEMMs at once: launch_ffn_fused
+    case GEMM_MX:
+      return L.swiglu ? launch_mx<MODE_SWIGLU_MX8OUT>(g, L.max_tiles, s)
+                      : launch_mx<MODE_PLAIN>(g, L.max_tiles, s);
     case GEMM_LARGE_FP8:
       if (!L.swiglu) return launch_big_fp8<MODE_PLAIN>(g, L.max_tiles, s);
       if (!L.C_scale) return hipErrorInvalidValue;  // block-FP8 h only

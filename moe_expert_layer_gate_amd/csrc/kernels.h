@@ -32,6 +32,15 @@ hipError_t launch_pack_panel(const void* src, int64_t batch, int64_t rows, int64
 hipError_t launch_gather_fp8(const void* src, const int32_t* rows, const int32_t* n_rows,
                              int64_t max_rows, int H, void* dst, float* dst_scale, hipStream_t s,
                              const int32_t* counts = nullptr, int cap = 0);
+// MXFP4 conversion of bf16 rows [rows, cols] (cols % 32 == 0): E2M1 codes
+// two per byte [rows, cols / 2], E8M0 scales [rows, cols / 32].
+hipError_t launch_quant_mx4(const void* src, int64_t rows, int64_t cols, void* codes,
+                            uint8_t* scales, hipStream_t s);
+// Gather with MXFP8 packing (E4M3 [.., H] + E8M0 [.., H / 32]); arguments as
+// launch_gather_fp8.
+hipError_t launch_gather_mx8(const void* src, const int32_t* rows, const int32_t* n_rows,
+                             int64_t max_rows, int H, void* dst, uint8_t* dst_scale,
+                             hipStream_t s, const int32_t* counts = nullptr, int cap = 0);
 hipError_t launch_quant_blocks(const void* src, int64_t batch, int64_t rows, int64_t cols,
                                void* codes, float* scales, hipStream_t s);
 
@@ -41,6 +50,7 @@ enum GemmPath {
   GEMM_PIPELINED = 1,  // up to 256 rows: 128 x 256 tiles (bf16 and block-FP8)
   GEMM_LARGE = 2,      // bf16: 256 x 256 tiles, 128 x 512 for segment remainders
   GEMM_LARGE_FP8 = 3,  // block-FP8: 256 x 256 tiles
+  GEMM_MX = 4,         // MXFP4 weights x MXFP8 activations: 128 x 256 tiles
 };
 GemmPath gemm_path(bool fp8, int64_t rows_per_expert);
 // Token rows of the path's tiles (of its full tiles, for GEMM_LARGE).
@@ -65,6 +75,9 @@ hipError_t launch_schedule(const int32_t* seg, int seg_cap, int E_L, GemmPath pa
                            int32_t* sync, hipStream_t s);
 struct GemmLaunch {
   bool fp8;              // e4m3 operands with block scales, else bf16
+  bool mx;               // MXFP4 weights (E2M1, two per byte) x MXFP8 activations,
+                         // scales E8M0 bytes per 32 along K (A_scale / W_scale /
+                         // C_scale point to bytes); path GEMM_MX
   bool swiglu;           // up GEMM with the SwiGLU epilogue (W = gate and up rows)
   bool gelu;             // up GEMM with the GELU epilogue (bf16); neither: plain
   const void* A;         // [N_cap, K] permuted activations

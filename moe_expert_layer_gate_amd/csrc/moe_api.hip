@@ -33,7 +33,8 @@ moe_status check_problem(const moe_problem* p) {
   if (H < 128 || H > 65536 || H % 128) return MOE_ERR_INVALID_ARG;
   if (I < 128 || I > 65536 || I % 128) return MOE_ERR_INVALID_ARG;
   if (Is < 0 || Is > 65536 || Is % 128) return MOE_ERR_INVALID_ARG;
-  if (p->dtype != MOE_BF16 && p->dtype != MOE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
+  if (p->dtype != MOE_BF16 && p->dtype != MOE_FP8_E4M3 && p->dtype != MOE_MXFP4)
+    return MOE_ERR_INVALID_ARG;
   if (p->layout & ~(MOE_LAYOUT_PANEL_WEIGHTS | MOE_LAYOUT_PANEL_ACTS)) return MOE_ERR_INVALID_ARG;
   if (p->layout && p->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (p->activation != MOE_ACT_SWIGLU && p->activation != MOE_ACT_GELU) return MOE_ERR_INVALID_ARG;
@@ -67,6 +68,13 @@ int64_t n_cap(const moe_problem* p) {
 }
 
 bool is_fp8(const moe_problem* p) { return p->dtype == MOE_FP8_E4M3; }
+bool is_mx(const moe_problem* p) { return p->dtype == MOE_MXFP4; }
+// Quantised GEMM activations with per-row scales (block-FP8 or MXFP8).
+bool quant_acts(const moe_problem* p) { return p->dtype != MOE_BF16; }
+// Bytes of the activation scales of an [R, C] matrix.
+int64_t act_scale_bytes(const moe_problem* p, int64_t R, int64_t C) {
+  return is_mx(p) ? R * (C / 32) : 4 * R * (C / 128);
+}
 bool is_gelu(const moe_problem* p) { return p->activation == MOE_ACT_GELU; }
 bool panel_weights(const moe_problem* p) { return p->layout & MOE_LAYOUT_PANEL_WEIGHTS; }
 bool panel_acts(const moe_problem* p) { return p->layout & MOE_LAYOUT_PANEL_ACTS; }
@@ -77,7 +85,7 @@ moe_problem layer_internal(const moe_problem* p) {
   moe_problem q = *p;
   q.layout &= ~MOE_LAYOUT_PANEL_ACTS;
   const int64_t wide = p->hidden > p->inter ? p->hidden : p->inter;
-  if (!is_fp8(p) && 2 * n_cap(p) * wide <= kGemmPanelMaxBytes) q.layout |= MOE_LAYOUT_PANEL_ACTS;
+  if (!quant_acts(p) && 2 * n_cap(p) * wide <= kGemmPanelMaxBytes) q.layout |= MOE_LAYOUT_PANEL_ACTS;
   return q;
 }
 
@@ -98,7 +106,7 @@ struct Carve {
 // Fused gather of bf16 sources whose byte size fits the GEMM's 32-bit lane
 // offsets.
 bool can_fuse_gather(const moe_problem* p) {
-  return !is_fp8(p) &&
+  return !quant_acts(p) &&
          static_cast<int64_t>(p->num_tokens) * p->hidden * 2 <= kGemmGatherMaxBytes;
 }
 
@@ -123,7 +131,7 @@ FfnShape ffn_shape(const moe_problem* p) {
   // layout of the buffers
   const int64_t N = n_pairs(p);
   FfnShape f{};
-  f.path = gemm_path(is_fp8(p), N / p->num_local);
+  f.path = is_mx(p) ? GEMM_MX : gemm_path(is_fp8(p), N / p->num_local);
   f.nt_up = gemm_n_tiles(!is_gelu(p), p->inter);
   f.nt_dn = gemm_n_tiles(false, p->hidden);
   f.cap_up = schedule_entries(N, p->num_local, f.path, f.nt_up);
@@ -145,9 +153,9 @@ FfnScratch carve_ffn(Carve& c, const moe_problem* p) {
     f.tab_dn = c.take<int4>(sizeof(int4) * sh.cap_dn);
     f.n_dn = c.take<int32_t>(sizeof(int32_t));
   }
-  if (is_fp8(p)) {
+  if (quant_acts(p)) {
     f.h = c.take<void>(N * I);
-    f.h_scale = c.take<float>(sizeof(float) * N * (I / 128));
+    f.h_scale = c.take<float>(act_scale_bytes(p, N, I));
   } else {
     f.h = c.take<void>(2 * N * I);
   }
@@ -199,17 +207,17 @@ LayerScratch carve_layer(Carve& c, const moe_problem* p) {
   s.row_slot = c.take<int32_t>(4 * N);
   s.tsr = c.take<int32_t>(4 * T * k);
   // x_perm only where the up GEMM does not gather from x itself
-  s.x_perm = can_fuse_gather(p) ? nullptr : c.take<void>((is_fp8(p) ? 1 : 2) * N * H);
-  s.x_perm_scale = is_fp8(p) ? c.take<float>(4 * N * (H / 128)) : nullptr;
+  s.x_perm = can_fuse_gather(p) ? nullptr : c.take<void>((quant_acts(p) ? 1 : 2) * N * H);
+  s.x_perm_scale = quant_acts(p) ? c.take<float>(act_scale_bytes(p, N, H)) : nullptr;
   s.y_perm = c.take<void>(2 * N * H);
   s.index_scratch = c.take<void>(index_scratch_bytes(static_cast<int>(T), static_cast<int>(EL)));
   s.ffn = carve_ffn(c, p);
   if (p->shared_inter > 0) {
     const moe_problem q = shared_problem(p);
     s.s_offsets = c.take<int32_t>(8);
-    if (is_fp8(p)) {
+    if (quant_acts(p)) {
       s.s_x = c.take<void>(T * H);
-      s.s_x_scale = c.take<float>(4 * T * (H / 128));
+      s.s_x_scale = c.take<float>(act_scale_bytes(p, T, H));
     }
     s.s_out = c.take<void>(2 * T * H);
     s.s_ffn = carve_ffn(c, &q);
@@ -255,6 +263,7 @@ moe_status run_ffn(const moe_problem* p, const FfnSource& src, const int32_t* se
                           f.tab_dn, f.n_dn, f.sync, s));
   GemmLaunch up{};
   up.fp8 = is_fp8(p);
+  up.mx = is_mx(p);
   up.swiglu = !is_gelu(p);
   up.gelu = is_gelu(p);
   up.A = src.x;
@@ -262,7 +271,7 @@ moe_status run_ffn(const moe_problem* p, const FfnSource& src, const int32_t* se
   up.W = w->w13;
   up.W_scale = w->w13_scale;
   up.C = hb;
-  up.C_scale = is_fp8(p) ? hs : nullptr;
+  up.C_scale = quant_acts(p) ? hs : nullptr;
   up.seg = seg;
   up.seg_cap = p->capacity;
   up.info = f.tab_up;
@@ -312,7 +321,10 @@ moe_status run_dispatch(const moe_problem* p, const void* x, const int32_t* ids,
   MOE_TRY(launch_index_build(ids, T, p->top_k, p->expert_begin, E_L, C, counts, offsets,
                              row_token, row_slot, tsr, scratch, s));
   if (!x_perm) return MOE_OK;
-  if (is_fp8(p))
+  if (is_mx(p))
+    MOE_TRY(launch_gather_mx8(x, row_token, offsets + E_L, n_cap(p), p->hidden, x_perm,
+                              reinterpret_cast<uint8_t*>(x_perm_scale), s, counts, C));
+  else if (is_fp8(p))
     MOE_TRY(launch_gather_fp8(x, row_token, offsets + E_L, n_cap(p), p->hidden, x_perm,
                               x_perm_scale, s, counts, C));
   else
@@ -323,10 +335,10 @@ moe_status run_dispatch(const moe_problem* p, const void* x, const int32_t* ids,
 
 bool weights_ok(const moe_problem* p, const moe_weights* w, bool need_shared) {
   if (!w || !w->w13 || !w->w2 || !aligned16(w->w13) || !aligned16(w->w2)) return false;
-  if (is_fp8(p) && (!w->w13_scale || !w->w2_scale)) return false;
+  if (quant_acts(p) && (!w->w13_scale || !w->w2_scale)) return false;
   if (need_shared) {
     if (!w->ws13 || !w->ws2 || !aligned16(w->ws13) || !aligned16(w->ws2)) return false;
-    if (is_fp8(p) && (!w->ws13_scale || !w->ws2_scale)) return false;
+    if (quant_acts(p) && (!w->ws13_scale || !w->ws2_scale)) return false;
   }
   return true;
 }
@@ -396,7 +408,7 @@ moe_status moe_dispatch(const moe_problem* p, const void* x, const int32_t* topk
   // x_perm == NULL: index only (the rows are gathered later, e.g. by
   // moe_grouped_ffn_gather)
   if (x_perm && !aligned16(x_perm)) return MOE_ERR_INVALID_ARG;
-  if (x_perm && is_fp8(p) && (!x_perm_scale || !aligned16(x_perm_scale)))
+  if (x_perm && quant_acts(p) && (!x_perm_scale || !aligned16(x_perm_scale)))
     return MOE_ERR_INVALID_ARG;
   if (!ws || ws_bytes < moe_workspace_bytes(p, MOE_STAGE_DISPATCH)) return MOE_ERR_WORKSPACE;
   if (p->num_tokens == 0) return MOE_OK;
@@ -413,9 +425,9 @@ moe_status moe_grouped_ffn(const moe_problem* p, const void* x_perm, const float
       !aligned16(y_perm))
     return MOE_ERR_INVALID_ARG;
   if (!weights_ok(p, w, false)) return MOE_ERR_INVALID_ARG;
-  if (is_fp8(p) && (!x_perm_scale || !aligned16(x_perm_scale))) return MOE_ERR_INVALID_ARG;
+  if (quant_acts(p) && (!x_perm_scale || !aligned16(x_perm_scale))) return MOE_ERR_INVALID_ARG;
   if (h && !aligned16(h)) return MOE_ERR_INVALID_ARG;
-  if (h && is_fp8(p) && (!h_scale || !aligned16(h_scale))) return MOE_ERR_INVALID_ARG;
+  if (h && quant_acts(p) && (!h_scale || !aligned16(h_scale))) return MOE_ERR_INVALID_ARG;
   if (!ws || ws_bytes < moe_workspace_bytes(p, MOE_STAGE_FFN)) return MOE_ERR_WORKSPACE;
   if (p->num_tokens == 0) return MOE_OK;
   Carve c(align_ws(ws));
@@ -429,7 +441,7 @@ moe_status moe_grouped_ffn_gather(const moe_problem* p, const void* x, const int
                                   void* y_perm, void* ws, size_t ws_bytes, void* stream) {
   moe_status st = check_problem(p);
   if (st != MOE_OK) return st;
-  if (is_fp8(p) || !can_fuse_gather(p)) return MOE_ERR_UNSUPPORTED;
+  if (quant_acts(p) || !can_fuse_gather(p)) return MOE_ERR_UNSUPPORTED;
   const void* ptrs[] = {x, row_token, offsets, y_perm};
   for (const void* q : ptrs)
     if (!q || !aligned16(q)) return MOE_ERR_INVALID_ARG;
@@ -506,7 +518,11 @@ moe_status enqueue_layer(const moe_problem* p, const float* logits, const void* 
     hipLaunchKernelGGL(fill_offsets_kernel, dim3(1), dim3(64), 0, s, L.s_offsets, T);
     MOE_TRY(hipGetLastError());
     const void* sx = x;
-    if (is_fp8(p)) {
+    if (is_mx(p)) {
+      MOE_TRY(launch_gather_mx8(x, nullptr, nullptr, T, p->hidden, L.s_x,
+                                reinterpret_cast<uint8_t*>(L.s_x_scale), s));
+      sx = L.s_x;
+    } else if (is_fp8(p)) {
       MOE_TRY(launch_gather_fp8(x, nullptr, nullptr, T, p->hidden, L.s_x, L.s_x_scale, s));
       sx = L.s_x;
     }
@@ -540,6 +556,24 @@ moe_status moe_quantize_fp8(const void* src, int64_t batch, int64_t rows, int64_
   }
   if ((rows + 127) / 128 > 65535 || batch > 65535) return MOE_ERR_INVALID_ARG;
   return hip_status(launch_quant_blocks(src, batch, rows, cols, codes, scales, s));
+}
+
+moe_status moe_quantize_mx(const void* src, int64_t batch, int64_t rows, int64_t cols,
+                           int32_t elem, void* codes, void* scales, void* stream) {
+  if (!src || !codes || !scales || !aligned16(src) || !aligned16(codes) || !aligned16(scales))
+    return MOE_ERR_INVALID_ARG;
+  if (batch < 0 || rows < 0 || cols < 32 || cols % 32 || cols > (1 << 20))
+    return MOE_ERR_INVALID_ARG;
+  if (elem != MOE_MX_E2M1 && elem != MOE_MX_E4M3) return MOE_ERR_INVALID_ARG;
+  if (batch * rows > (int64_t(1) << 31) - 1) return MOE_ERR_INVALID_ARG;
+  if (batch == 0 || rows == 0) return MOE_OK;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (elem == MOE_MX_E2M1)
+    return hip_status(launch_quant_mx4(src, batch * rows, cols, codes,
+                                       static_cast<uint8_t*>(scales), s));
+  if (cols % 128 || cols > 65536) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_gather_mx8(src, nullptr, nullptr, batch * rows, static_cast<int>(cols),
+                                      codes, static_cast<uint8_t*>(scales), s));
 }
 
 moe_status moe_pack_panel(const void* src, int64_t batch, int64_t rows, int64_t cols, void* dst,
@@ -602,7 +636,7 @@ static size_t streamed_slice(const moe_problem* p, int32_t max_group_tokens) {
   moe_problem q = *p;
   q.num_tokens = max_group_tokens;
   size_t b = moe_workspace_bytes(&q, MOE_STAGE_LAYER);
-  const bool fp8 = p->dtype == MOE_FP8_E4M3;
+  const bool fp8 = p->dtype != MOE_BF16;
   const int64_t kk = p->top_k < p->num_local ? p->top_k : p->num_local;
   for (int64_t r = 0; r < 4096; ++r) {
     if (gemm_path(fp8, r) == gemm_path(fp8, r + 1)) continue;

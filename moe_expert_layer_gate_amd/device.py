@@ -43,6 +43,20 @@ def quantize_fp8(w: torch.Tensor, block_rows: int = 128):
     return codes, scales
 
 
+def quantize_mx4(w: torch.Tensor):
+    """[B, R, C] or [R, C] bf16 -> (E2M1 codes uint8 [.., R, C/2], two per
+    byte, E8M0 scales uint8 [.., R, C/32]) using moe_quantize_mx."""
+    squeeze = w.dim() == 2
+    w3 = w.unsqueeze(0) if squeeze else w
+    B, R, C = w3.shape
+    codes = torch.empty((B, R, C // 2), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((B, R, C // 32), dtype=torch.uint8, device=w.device)
+    ml.moe_quantize_mx(w3.contiguous(), B, R, C, ml.MX_E2M1, codes, scales)
+    if squeeze:
+        return codes[0], scales[0]
+    return codes, scales
+
+
 def pack_panel(w: torch.Tensor) -> torch.Tensor:
     """[B, R, C] or [R, C] bf16 -> the same values in panel layout
     ([B, C/32, R, 32]), made by moe_pack_panel; returned with w's shape."""
@@ -54,12 +68,14 @@ def pack_panel(w: torch.Tensor) -> torch.Tensor:
 
 
 def upload(d: Dict[str, np.ndarray], fp8: bool, keep_bf16: bool = False,
-           panel: bool = False) -> Dict[str, torch.Tensor]:
+           panel: bool = False, mx: bool = False) -> Dict[str, torch.Tensor]:
     """Move a make_inputs() batch to the GPU.  With fp8, the weights are
     converted to E4M3 + 128x128 block scales on the device (load-time
     conversion) and the bf16 copies are dropped unless keep_bf16.  With
     panel (bf16 only), the weights are repacked into panel layout at load
-    time (use the problem's LAYOUT_PANEL_WEIGHTS bit with them)."""
+    time (use the problem's LAYOUT_PANEL_WEIGHTS bit with them).  With mx,
+    the weights become MXFP4 (E2M1 codes and E8M0 scales, load-time
+    conversion by the library)."""
     out: Dict[str, torch.Tensor] = {}
     out["logits"] = torch.from_numpy(d["logits"]).cuda()
     out["x"] = bf16_from_bits(d["x"])
@@ -67,7 +83,13 @@ def upload(d: Dict[str, np.ndarray], fp8: bool, keep_bf16: bool = False,
         if name not in d:
             continue
         wb = bf16_from_bits(d[name])
-        if fp8:
+        if mx:
+            out[name + "_q"], out[name + "_s"] = quantize_mx4(wb)
+            if keep_bf16:
+                out[name] = wb
+            else:
+                del wb
+        elif fp8:
             q, s = quantize_fp8(wb, 128)
             out[name + "_q"], out[name + "_s"] = q, s
             if keep_bf16:
@@ -83,6 +105,8 @@ def upload(d: Dict[str, np.ndarray], fp8: bool, keep_bf16: bool = False,
 
 
 def weights_of(dev: Dict[str, torch.Tensor], fp8: bool) -> ml.moe_weights:
+    """The weights struct; quantised weights (block-FP8 or MXFP4, whichever
+    upload made) when fp8 is set."""
     if fp8:
         return ml.weights_struct(dev["w13_q"], dev["w2_q"], dev.get("ws13_q"), dev.get("ws2_q"),
                                  dev["w13_s"], dev["w2_s"], dev.get("ws13_s"), dev.get("ws2_s"))

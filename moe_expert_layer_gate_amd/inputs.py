@@ -52,6 +52,7 @@ class MoEConfig:
     I: int            # expert intermediate size
     I_s: int = 0      # shared-expert intermediate size (0 = no shared expert)
     fp8: bool = False  # block-FP8 weights and GEMM activations
+    mx: bool = False   # MXFP4 weights, MXFP8 GEMM activations
     logits: str = "normal"     # "normal" | "gumbel_zipf"
     zipf_s: float = 1.1
     replicas: int = 0          # >0: Dirichlet(0.5) split of the rows over replicas
@@ -65,7 +66,7 @@ class MoEConfig:
 
     @property
     def dtype(self) -> str:
-        return "fp8_e4m3" if self.fp8 else "bf16"
+        return "mxfp4" if self.mx else "fp8_e4m3" if self.fp8 else "bf16"
 
 
 CONFIGS: Dict[str, MoEConfig] = {
@@ -88,6 +89,15 @@ CONFIGS: Dict[str, MoEConfig] = {
     # Decode-sized batch on the same shard shape with uniform routing.
     "dsv3_ep8_decode": MoEConfig("dsv3_ep8_decode", T=64, H=7168, E=256, E_L=32,
                                  e_lo=0, k=8, I=2048),
+    # The same shard with MXFP4 routed-expert weights (MXFP8 activations) and
+    # its shared expert in the same format.
+    "dsv3_ep8_prefill_mxfp4": MoEConfig("dsv3_ep8_prefill_mxfp4", T=16384, H=7168,
+                                        E=256, E_L=32, e_lo=0, k=8, I=2048,
+                                        I_s=2048, mx=True, logits="gumbel_zipf",
+                                        replicas=8),
+    # The decode batch with MXFP4 weights.
+    "dsv3_ep8_decode_mxfp4": MoEConfig("dsv3_ep8_decode_mxfp4", T=64, H=7168, E=256, E_L=32,
+                                       e_lo=0, k=8, I=2048, mx=True),
     # The Qwen3-30B-A3B prefill shape with a standard (non-gated) GELU MLP:
     # the pages' BF16 group runs its models with a standard MLP.
     "qwen3_30b_prefill_gelu": MoEConfig("qwen3_30b_prefill_gelu", T=8192, H=2048, E=128,

@@ -17,7 +17,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoelayer.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
-MOE_BF16, MOE_FP8_E4M3 = 0, 1
+MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4 = 0, 1, 2
+MX_E2M1, MX_E4M3 = 0, 1
 LAYOUT_PANEL_WEIGHTS, LAYOUT_PANEL_ACTS = 1, 2
 ACT_SWIGLU, ACT_GELU = 0, 1
 STAGE_LAYER, STAGE_DISPATCH, STAGE_FFN = 0, 1, 2
@@ -50,6 +51,7 @@ SIGNATURES = {
     "moe_layer": (_i32, [_P, _vp, _vp, _W, _vp, _vp, _sz, _vp]),
     "moe_quantize_fp8": (_i32, [_vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp]),
     "moe_pack_panel": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp]),
+    "moe_quantize_mx": (_i32, [_vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp]),
     "moe_workspace_bytes": (_sz, [_P, _i32]),
     "moe_stream_threshold": (_i64, [_vp, _vp, _i32, ctypes.c_double]),
     "moe_stream_plan": (_i32, [_vp, _i32, _i64, _vp, _vp]),
@@ -102,10 +104,20 @@ class Problem:
     layout: int = 0   # LAYOUT_* bits
     act: str = "swiglu"  # "swiglu" | "gelu"
     capacity: int = 0    # 0: contiguous segments; C >= T: masked fixed-capacity layout
+    mx: bool = False     # MXFP4 weights, MXFP8 activations (fp8 must be False)
+
+    @property
+    def dtype(self) -> int:
+        return MOE_MXFP4 if self.mx else MOE_FP8_E4M3 if self.fp8 else MOE_BF16
+
+    @property
+    def quantized(self) -> bool:
+        """GEMM activations are quantised with per-row scales (fp8 or MX)."""
+        return self.fp8 or self.mx
 
     def c(self) -> moe_problem:
         return moe_problem(self.T, self.H, self.E, self.k, self.e_lo, self.E_L, self.I,
-                           self.I_s, MOE_FP8_E4M3 if self.fp8 else MOE_BF16, self.layout,
+                           self.I_s, self.dtype, self.layout,
                            ACT_GELU if self.act == "gelu" else ACT_SWIGLU, self.capacity)
 
     @property
@@ -125,6 +137,7 @@ class Problem:
                     capacity: Optional[int] = None) -> "Problem":
         return cls(T=cfg.T if T is None else T, H=cfg.H, E=cfg.E, k=cfg.k, e_lo=cfg.e_lo,
                    E_L=cfg.E_L, I=cfg.I, I_s=cfg.I_s, fp8=cfg.fp8, layout=layout, act=cfg.act,
+                   mx=getattr(cfg, "mx", False),
                    capacity=getattr(cfg, "capacity", 0) if capacity is None else capacity)
 
 
@@ -256,3 +269,9 @@ def moe_layer_streamed(p: Problem, logits, x, weights: moe_weights, y, group_tok
     _check("moe_layer_streamed", lib().moe_layer_streamed(
         ctypes.byref(pc), _ptr(logits), _ptr(x), ctypes.byref(weights), _ptr(y), g,
         len(group_tokens) - 1, hs, len(streams), _ptr(ws), ws.numel() * ws.element_size()))
+
+
+def moe_quantize_mx(src, batch: int, rows: int, cols: int, elem: int, codes, scales,
+                    stream=None) -> None:
+    _check("moe_quantize_mx", lib().moe_quantize_mx(
+        _ptr(src), batch, rows, cols, elem, _ptr(codes), _ptr(scales), _stream(stream)))

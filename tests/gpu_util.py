@@ -81,14 +81,16 @@ def small_cfg(**kw) -> synth.MoEConfig:
 
 class OracleWeights:
     """The oracle's own view of the weights, decoded per expert on demand
-    (fp8: quantised by the oracle itself from the bf16 draws), cached."""
+    (fp8 / MXFP4: quantised by the oracle itself from the bf16 draws), cached."""
 
-    def __init__(self, d, fp8: bool):
-        self.d, self.fp8 = d, fp8
+    def __init__(self, d, fp8: bool, mx: bool = False):
+        self.d, self.fp8, self.mx = d, fp8 or mx, mx
 
     @functools.lru_cache(maxsize=None)
     def _q(self, name, e):
         m = self.d[name] if e is None else self.d[name][e]
+        if self.mx:
+            return O.mx_quantize(O.bf16_to_f64(m), "e2m1")
         return O.quantize_blocks(O.bf16_to_f64(m), 128, 128)
 
     def codes(self, name, e=None):
@@ -96,6 +98,9 @@ class OracleWeights:
 
     @functools.lru_cache(maxsize=64)
     def w(self, name, e=None):
+        if self.mx:
+            q, s = self._q(name, e)
+            return O.mx_dequantize(q, s, "e2m1")
         if self.fp8:
             q, s = self._q(name, e)
             return O.dequantize_blocks(q, s, 128, 128)
@@ -126,3 +131,9 @@ class _ExpertView:
 
     def __len__(self):
         return self.n
+
+
+def pack_e2m1(codes):
+    """E2M1 codes [.., C] -> bytes [.., C/2], two per byte, low nibble first."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)

@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert ml.lib().moe_abi_version() == 5
+    assert ml.lib().moe_abi_version() == 6
     assert ml.status_str(0) == "MOE_OK"
     assert ml.status_str(3) == "MOE_ERR_WORKSPACE"
     assert ml.status_str(99) == "MOE_ERR_UNKNOWN"
@@ -216,3 +216,35 @@ def test_capacity_checks():
     assert ml.workspace_bytes(ml.Problem(**base, capacity=16)) > 0
     p0 = ml.Problem(**dict(base, T=0), capacity=16).c()
     assert L.moe_route(ctypes.byref(p0), 16, 16, 16, None) == ml.MOE_OK
+
+
+def test_mxfp4_checks():
+    """MXFP4: row-major layouts and the gated MLP only; scale pointers are
+    required like block-FP8's; moe_quantize_mx argument checks."""
+    L = ml.lib()
+    base = dict(T=16, H=256, E=8, k=2, e_lo=0, E_L=8, I=256, mx=True)
+    assert ml.workspace_bytes(ml.Problem(**base)) > 0
+    for bad, want in ((dict(layout=ml.LAYOUT_PANEL_WEIGHTS), ml.MOE_ERR_UNSUPPORTED),
+                      (dict(act="gelu"), ml.MOE_ERR_UNSUPPORTED)):
+        pc = ml.Problem(**base, **bad).c()
+        assert L.moe_route(ctypes.byref(pc), 16, 16, 16, None) == want
+    pc = ml.Problem(**base).c()
+    pc.dtype = 3
+    assert L.moe_route(ctypes.byref(pc), 16, 16, 16, None) == ml.MOE_ERR_INVALID_ARG
+    # the gathering FFN is bf16 only
+    p = ml.Problem(**base).c()
+    w = ml.moe_weights(256, 256, None, None, 256, 256, None, None)
+    n = ml.workspace_bytes(ml.Problem(**base), ml.STAGE_FFN)
+    assert L.moe_grouped_ffn_gather(ctypes.byref(p), 256, 256, 256, ctypes.byref(w), None, 256,
+                                    256, n, None) == ml.MOE_ERR_UNSUPPORTED
+    # moe_grouped_ffn needs the activation scales
+    assert L.moe_grouped_ffn(ctypes.byref(p), 256, None, 256, ctypes.byref(w), None, None, 256,
+                             256, n, None) == ml.MOE_ERR_INVALID_ARG
+    w0 = ml.moe_weights(256, 256, None, None, None, None, None, None)   # no weight scales
+    assert L.moe_grouped_ffn(ctypes.byref(p), 256, 256, 256, ctypes.byref(w0), None, None, 256,
+                             256, n, None) == ml.MOE_ERR_INVALID_ARG
+    assert L.moe_quantize_mx(256, 1, 4, 48, 0, 256, 256, None) == ml.MOE_ERR_INVALID_ARG   # cols % 32
+    assert L.moe_quantize_mx(256, 1, 4, 64, 2, 256, 256, None) == ml.MOE_ERR_INVALID_ARG   # elem
+    assert L.moe_quantize_mx(256, 1, 4, 64, 1, 256, 256, None) == ml.MOE_ERR_INVALID_ARG   # e4m3: cols % 128
+    assert L.moe_quantize_mx(None, 1, 4, 64, 0, 256, 256, None) == ml.MOE_ERR_INVALID_ARG
+    assert L.moe_quantize_mx(256, 0, 4, 64, 0, 256, 256, None) == ml.MOE_OK

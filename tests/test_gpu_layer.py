@@ -31,7 +31,8 @@ def run_layer(torch, p, dev, guard=0):
     ml, dv = _mods()
     y = torch.full((p.T + 2 * guard, p.H), 3.0, dtype=torch.bfloat16, device="cuda")
     ws = dv.workspace(p)
-    ml.moe_layer(p, dev["logits"], dev["x"], dv.weights_of(dev, p.fp8), y[guard:guard + p.T], ws)
+    ml.moe_layer(p, dev["logits"], dev["x"], dv.weights_of(dev, p.quantized), y[guard:guard + p.T],
+                 ws)
     torch.cuda.synchronize()
     if guard:
         assert torch.all(y[:guard] == 3.0) and torch.all(y[guard + p.T:] == 3.0)
@@ -50,7 +51,12 @@ def run_staged(torch, p, dev):
     counts, offsets = torch.empty(p.E_L, **i32), torch.empty(p.E_L + 1, **i32)
     row_token, row_slot = torch.empty(N, **i32), torch.empty(N, **i32)
     tsr = torch.empty((T, k), **i32)
-    if p.fp8:
+    if p.mx:       # MXFP8 activations: E4M3 codes, E8M0 bytes per 32
+        xp = torch.empty((N, H), dtype=torch.uint8, device="cuda")
+        xs = torch.empty((N, H // 32), dtype=torch.uint8, device="cuda")
+        h = torch.empty((N, I), dtype=torch.uint8, device="cuda")
+        hs = torch.empty((N, I // 32), dtype=torch.uint8, device="cuda")
+    elif p.fp8:
         xp = torch.empty((N, H), dtype=torch.uint8, device="cuda")
         xs = torch.empty((N, H // 128), dtype=torch.float32, device="cuda")
         h = torch.empty((N, I), dtype=torch.uint8, device="cuda")
@@ -64,20 +70,24 @@ def run_staged(torch, p, dev):
                     dv.workspace(p, ml.STAGE_DISPATCH))
     y_perm = torch.empty((N, H), dtype=torch.bfloat16, device="cuda")
     seg = counts if p.capacity else offsets      # the masked layout passes counts
-    ml.moe_grouped_ffn(p, xp, xs, seg, dv.weights_of(dev, p.fp8), h, hs, y_perm,
+    ml.moe_grouped_ffn(p, xp, xs, seg, dv.weights_of(dev, p.quantized), h, hs, y_perm,
                        dv.workspace(p, ml.STAGE_FFN))
     if p.layout & ml.LAYOUT_PANEL_ACTS:
         xp, h = unpanel(xp, N, H), unpanel(h, N, I)
     shared = None
     if p.I_s > 0:
         q = ml.Problem(T=T, H=H, E=1, k=1, e_lo=0, E_L=1, I=p.I_s, fp8=p.fp8, act=p.act,
-                       layout=p.layout & ml.LAYOUT_PANEL_WEIGHTS)
+                       layout=p.layout & ml.LAYOUT_PANEL_WEIGHTS, mx=p.mx)
         off2 = torch.tensor([0, T], **i32)
         sw = (ml.weights_struct(dev["ws13_q"], dev["ws2_q"], None, None, dev["ws13_s"],
-                                dev["ws2_s"]) if p.fp8 else
+                                dev["ws2_s"]) if p.quantized else
               ml.weights_struct(dev["ws13"], dev["ws2"]))
         sx, sxs = dev["x"], None
-        if p.fp8:
+        if p.mx:
+            sx = torch.empty((T, H), dtype=torch.uint8, device="cuda")
+            sxs = torch.empty((T, H // 32), dtype=torch.uint8, device="cuda")
+            ml.moe_quantize_mx(dev["x"], 1, T, H, ml.MX_E4M3, sx, sxs)
+        elif p.fp8:
             sx = torch.empty((T, H), dtype=torch.uint8, device="cuda")
             sxs = torch.empty((T, H // 128), dtype=torch.float32, device="cuda")
             ml.moe_quantize_fp8(dev["x"], 1, T, H, 1, sx, sxs)
@@ -92,6 +102,8 @@ def run_staged(torch, p, dev):
 
 def h_values(st, p):
     N = int(st["offsets"][-1])
+    if p.mx:
+        return O.mx_dequantize(st["h"][:N].cpu().numpy(), st["h_scale"][:N].cpu().numpy(), "e4m3")
     if p.fp8:
         return (O.e4m3_value(st["h"][:N].cpu().numpy()) *
                 np.repeat(st["h_scale"][:N].cpu().numpy().astype(np.float64), 128, axis=1))
@@ -135,7 +147,7 @@ SMALL_FP8 = {
 def upload(cfg, seed, x_std=None, std=None):
     ml, dv = _mods()
     d = synth.make_inputs(cfg, seed, x_std=x_std, std=std)
-    return d, dv.upload(d, cfg.fp8)
+    return d, dv.upload(d, cfg.fp8, mx=cfg.mx)
 
 
 @pytest.mark.parametrize("name", list(SMALL) + list(SMALL_FP8))
@@ -175,13 +187,15 @@ def check_small_case(name, cfg, d, dev):
     p = ml.Problem.from_config(cfg)
     say("layer small", name)
     st = run_staged(torch, p, dev)
-    ow = OracleWeights(d, cfg.fp8)
+    quant = cfg.fp8 or cfg.mx
+    ow = OracleWeights(d, cfg.fp8, cfg.mx)
     # bf16: the exact oracle.  fp8: the oracle with the FP8 path's activation
     # quantisation of x and h, so the kernels are held to bf16-level
     # agreement (the 6e-2 gate against the exact oracle is checked at the
     # workloads' own spreads below).
     ref = O.moe_layer(d["logits"], d["x"], ow.as_layer_dict(cfg.E_L), k=cfg.k, e_lo=cfg.e_lo,
-                      E_L=cfg.E_L, fp8=cfg.fp8, quantize_activations=cfg.fp8, activation=cfg.act)
+                      E_L=cfg.E_L, fp8=cfg.fp8, quantize_activations=quant, activation=cfg.act,
+                      mx=cfg.mx)
     # bf16: every row within 2e-2.  fp8: h is rounded to E4M3 on both sides,
     # from fp32 sums on the GPU and fp64 sums in the oracle, so an element
     # that sits on a rounding boundary can land one code apart (a 6-12 %
@@ -192,7 +206,7 @@ def check_small_case(name, cfg, d, dev):
         e = rel_rows_all(got, ref)
         if e.size == 0:
             return True
-        if not cfg.fp8:
+        if not quant:
             return e.max() <= TOL_BF16
         return e.max() <= TOL_FP8 and np.percentile(e, 99) <= TOL_BF16
     # exact routing and permutation
@@ -202,7 +216,8 @@ def check_small_case(name, cfg, d, dev):
     np.testing.assert_array_equal(st["row_token"][:N].cpu().numpy(), ref["row_token"])
     np.testing.assert_array_equal(st["tsr"].cpu().numpy(), ref["token_slot_row"])
     # FFN stages
-    ref_h = O.fp8_activation(ref["h"]) if cfg.fp8 else ref["h"]
+    ref_h = (O.mx8_activation(ref["h"]) if cfg.mx else O.fp8_activation(ref["h"]) if cfg.fp8
+             else ref["h"])
     e_h = rel_rows(h_values(st, p), ref_h)
     e_yp = rel_rows(f64(st["y_perm"][:N]), ref["y_perm"])
     e_y = rel_rows(f64(st["y"]), ref["y"])
@@ -215,7 +230,7 @@ def check_small_case(name, cfg, d, dev):
     # fused layer: same routing, same numbers as the staged calls
     y = run_layer(torch, p, dev, guard=3)
     np.testing.assert_array_equal(dv.bits_from_bf16(y), dv.bits_from_bf16(st["y"]))
-    if not cfg.fp8:
+    if not quant:
         check_panel_layouts(torch, p, d, st)
         check_gather_path(torch, p, dev, st)
 

@@ -1,0 +1,153 @@
+"""GPU parity of the MXFP4 path (OCP MX: E2M1 weights and E4M3 activations,
+E8M0 scales per 32 along K) against the oracle: the load-time weight
+conversion and the activation packing bit-exact; the layer within 2e-2 on
+99 % of rows and 6e-2 on all against the oracle that quantises x and h the
+same way, and within 6e-2 of the exact-activation oracle at the workload
+spread; the full DeepSeek-V3 shard on sampled rows.  Calls go through the
+C ABI."""
+import numpy as np
+import pytest
+
+from moe_expert_layer_gate_amd import inputs as synth
+from oracle import moe_oracle as O
+from tests.gpu_util import (TOL_FP8, OracleWeights, global_rel, pack_e2m1, rel_rows, say,
+                            small_cfg, torch_cuda)
+from tests.test_gpu_layer import check_small_case, f64, run_layer
+from tests.test_gpu_route_dispatch import run_dispatch
+
+pytestmark = pytest.mark.gpu
+
+
+def _mods():
+    from moe_expert_layer_gate_amd import device as dv
+    from moe_expert_layer_gate_amd import moelayer as ml
+    return ml, dv
+
+
+def bf16_case(rng, R, C):
+    a = rng.standard_normal((R, C)).astype(np.float32) * np.exp(
+        rng.uniform(-8, 8, (R, 1))).astype(np.float32)
+    a[0, :32] = 0.0                                   # an all-zero block
+    if R > 2:
+        a[1, :32] = np.float32(3.0) * (np.arange(32) % 2)  # ties of the element grid
+        a[2, 32:64] = np.float32(1e30)                     # one huge block
+    return synth.f32_to_bf16_bits(a)
+
+
+@pytest.mark.parametrize("R,C", [(5, 64), (300, 7168), (1, 2048)])
+def test_mx4_weight_conversion_bit_exact(R, C):
+    torch = torch_cuda()
+    ml, dv = _mods()
+    bits = bf16_case(np.random.default_rng(R + C), R, C)
+    say("mx4 conversion", R, C)
+    codes, scales = dv.quantize_mx4(dv.bf16_from_bits(bits))
+    torch.cuda.synchronize()
+    rc, rs = O.mx_quantize(O.bf16_to_f64(bits), "e2m1")
+    np.testing.assert_array_equal(codes.cpu().numpy(), pack_e2m1(rc))
+    np.testing.assert_array_equal(scales.cpu().numpy(), rs)
+
+
+@pytest.mark.parametrize("R,C", [(7, 128), (257, 7168)])
+def test_mx8_activation_packing_bit_exact(R, C):
+    torch = torch_cuda()
+    ml, dv = _mods()
+    bits = bf16_case(np.random.default_rng(R * 3 + C), R, C)
+    x = dv.bf16_from_bits(bits)
+    codes = torch.empty((R, C), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((R, C // 32), dtype=torch.uint8, device="cuda")
+    say("mx8 packing", R, C)
+    ml.moe_quantize_mx(x, 1, R, C, ml.MX_E4M3, codes, scales)
+    torch.cuda.synchronize()
+    rc, rs = O.mx_quantize(O.bf16_to_f64(bits), "e4m3")
+    np.testing.assert_array_equal(codes.cpu().numpy(), rc)
+    np.testing.assert_array_equal(scales.cpu().numpy(), rs)
+
+
+def test_mx_dispatch_rows_bit_exact():
+    torch = torch_cuda()
+    ml, dv = _mods()
+    rng = np.random.default_rng(17)
+    T, E, k, H = 300, 16, 4, 512
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    x = synth.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    p = ml.Problem(T=T, H=H, E=E, k=k, e_lo=4, E_L=8, I=128, mx=True)
+    say("mx dispatch")
+    g = run_dispatch(torch, p, x, ids)
+    r = O.index_build(ids, 4, 8)
+    N = int(r["offsets"][-1])
+    np.testing.assert_array_equal(g["row_token"][:N], r["row_token"])
+    qx, sx = O.mx_quantize(O.bf16_to_f64(x), "e4m3")
+    np.testing.assert_array_equal(g["x_perm"][:N].cpu().numpy(), qx[r["row_token"]])
+    np.testing.assert_array_equal(g["x_perm_scale"][:N].cpu().numpy(), sx[r["row_token"]])
+
+
+SMALL_MX = {
+    "mx_small": (small_cfg(T=200, H=512, E=16, E_L=8, e_lo=0, k=4, I=256, mx=True), 41),
+    "mx_ragged": (small_cfg(T=333, H=384, E=8, E_L=4, e_lo=2, k=2, I=640, mx=True), 42),
+    "mx_shared": (small_cfg(T=150, H=1024, E=64, E_L=16, e_lo=16, k=8, I=512, I_s=256,
+                            mx=True), 43),
+    "mx_decode": (small_cfg(T=16, H=1024, E=64, E_L=16, e_lo=0, k=8, I=256, mx=True), 44),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL_MX))
+def test_mx_layer_small(name):
+    torch_cuda()
+    ml, dv = _mods()
+    cfg, seed = SMALL_MX[name]
+    d = synth.make_inputs(cfg, seed, x_std=1.0, std=0.05)
+    dev = dv.upload(d, False, mx=True)
+    check_small_case(name, cfg, d, dev)
+
+
+# Output gate of the MX path against the exact-activation oracle (the MXFP4
+# weights are the parameters, so the error is that of packing x and h as
+# MXFP8): E4M3 rounding is within 1/16 of each element, and the MX scale, a
+# power of two, puts a block's largest magnitude in [256, 512) before the
+# E4M3 range ends at 448, so a block maximum may also lose up to 1/8 to
+# saturation.  Two such packings (x, then h) give per-row errors of a few
+# percent with tails near 1e-1; the block-FP8 path's scale amax / 448 never
+# saturates, which is why its gate is 6e-2.
+TOL_MX = 1e-1
+
+
+@pytest.mark.parametrize("name", list(SMALL_MX))
+def test_mx_gate_at_workload_spread(name):
+    """Against the exact-activation oracle (MXFP4 weights as the parameters)
+    at the workloads' N(0, 0.02) spreads: the MX output gate."""
+    torch = torch_cuda()
+    ml, dv = _mods()
+    cfg, seed = SMALL_MX[name]
+    d = synth.make_inputs(cfg, seed)
+    dev = dv.upload(d, False, mx=True)
+    p = ml.Problem.from_config(cfg)
+    say("mx gate", name)
+    y = f64(run_layer(torch, p, dev))
+    ow = OracleWeights(d, False, mx=True)
+    ref = O.moe_layer(d["logits"], d["x"], ow.as_layer_dict(cfg.E_L), k=cfg.k, e_lo=cfg.e_lo,
+                      E_L=cfg.E_L, mx=True)
+    e = rel_rows(y, ref["y"])
+    print(f"{name}: y vs exact-activation oracle {e:.2e}  global {global_rel(y, ref['y']):.2e}")
+    assert e <= TOL_MX
+
+
+def test_mx_dsv3_shard_full_size_sampled():
+    """The DeepSeek-V3 EP8 shard with MXFP4 weights and its shared expert at
+    full size: sampled rows (segment edges and random tokens) against the
+    oracle with the same activation quantisation."""
+    torch = torch_cuda()
+    ml, dv = _mods()
+    cfg = synth.config("dsv3_ep8_prefill_mxfp4")
+    d = synth.make_inputs(cfg, 2)
+    dev = dv.upload(d, False, mx=True)
+    p = ml.Problem.from_config(cfg)
+    say("mx dsv3 shard full size")
+    y = run_layer(torch, p, dev)
+    rng = np.random.default_rng(8)
+    toks = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, 30, replace=False)]))
+    ow = OracleWeights(d, False, mx=True)
+    ref = O.moe_layer_tokens(d["logits"], d["x"], ow.as_layer_dict(cfg.E_L), toks, k=cfg.k,
+                             e_lo=cfg.e_lo, E_L=cfg.E_L, mx=True, quantize_activations=True)
+    e = rel_rows(y[toks].float().cpu().numpy().astype(np.float64), ref)
+    print(f"mx dsv3 sampled rows: {e:.2e}")
+    assert e <= TOL_FP8

@@ -82,7 +82,10 @@ def run_dispatch(torch, p, x_bits, ids_np):
              row_token=torch.full((max(N, 1),), -5, dtype=torch.int32, device="cuda"),
              row_slot=torch.full((max(N, 1),), -5, dtype=torch.int32, device="cuda"),
              tsr=torch.full((p.T, p.k), -5, dtype=torch.int32, device="cuda"))
-    if p.fp8:
+    if p.mx:
+        xp = torch.zeros((max(N, 1), p.H), dtype=torch.uint8, device="cuda")
+        xs = torch.zeros((max(N, 1), p.H // 32), dtype=torch.uint8, device="cuda")
+    elif p.fp8:
         xp = torch.zeros((max(N, 1), p.H), dtype=torch.uint8, device="cuda")
         xs = torch.zeros((max(N, 1), p.H // 128), dtype=torch.float32, device="cuda")
     else:

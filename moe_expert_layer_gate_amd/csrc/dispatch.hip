@@ -40,37 +40,50 @@ namespace {
 constexpr int kTokBlock = 256;  // tokens per count/scatter block
 constexpr int kMaskWords = kTokBlock / 32;
 
-// Local expert of slot s of a token, or -1 (non-local or repeated expert).
-__device__ __forceinline__ int local_expert(const int32_t* ids, int s, int e_lo, int E_L) {
-  const int id = ids[s];
-  for (int q = 0; q < s; ++q)
-    if (ids[q] == id) return -1;
-  const int e = id - e_lo;
-  return (e >= 0 && e < E_L) ? e : -1;
+// Local expert of every slot of token t (slots s < k), -1 where the expert
+// is not local or repeats one of an earlier slot.  KMAX >= k is a compile-time
+// bound, so the slots live in registers (fully unrolled, no indexed arrays).
+template <int KMAX>
+__device__ __forceinline__ void token_local_experts(const int32_t* __restrict__ topk_ids, int t,
+                                                    int k, int e_lo, int E_L, int* le) {
+  int ids[KMAX];
+#pragma unroll
+  for (int s = 0; s < KMAX; ++s) ids[s] = s < k ? topk_ids[static_cast<size_t>(t) * k + s] : -1;
+#pragma unroll
+  for (int s = 0; s < KMAX; ++s) {
+    bool rep = false;
+#pragma unroll
+    for (int q = 0; q < s; ++q) rep |= ids[q] == ids[s];
+    const int e = ids[s] - e_lo;
+    le[s] = (s < k && !rep && e >= 0 && e < E_L) ? e : -1;
+  }
 }
 
-// Build the per-expert token masks of block b in LDS.
-__device__ __forceinline__ void build_masks(uint32_t* mask, const int32_t* __restrict__ topk_ids,
-                                            int T, int k, int e_lo, int E_L, int b) {
+// Build the per-expert token masks of block b in LDS from the local experts
+// of this thread's token (t < T).
+template <int KMAX>
+__device__ __forceinline__ void build_masks(uint32_t* mask, const int* le, bool has_token,
+                                            int E_L) {
   for (int i = threadIdx.x; i < E_L * kMaskWords; i += blockDim.x) mask[i] = 0u;
   __syncthreads();
-  const int t = b * kTokBlock + threadIdx.x;
-  if (t < T) {
-    int32_t ids[32];
-    for (int s = 0; s < k; ++s) ids[s] = topk_ids[static_cast<size_t>(t) * k + s];
-    for (int s = 0; s < k; ++s) {
-      const int e = local_expert(ids, s, e_lo, E_L);
-      if (e >= 0) atomicOr(&mask[e * kMaskWords + (threadIdx.x >> 5)], 1u << (threadIdx.x & 31));
-    }
+  if (has_token) {
+#pragma unroll
+    for (int s = 0; s < KMAX; ++s)
+      if (le[s] >= 0)
+        atomicOr(&mask[le[s] * kMaskWords + (threadIdx.x >> 5)], 1u << (threadIdx.x & 31));
   }
   __syncthreads();
 }
 
+template <int KMAX>
 __global__ __launch_bounds__(kTokBlock) void index_count_kernel(
     const int32_t* __restrict__ topk_ids, int T, int k, int e_lo, int E_L,
     int32_t* __restrict__ blk_hist) {
   extern __shared__ uint32_t mask[];
-  build_masks(mask, topk_ids, T, k, e_lo, E_L, blockIdx.x);
+  const int t = blockIdx.x * kTokBlock + threadIdx.x;
+  int le[KMAX];
+  if (t < T) token_local_experts<KMAX>(topk_ids, t, k, e_lo, E_L, le);
+  build_masks<KMAX>(mask, le, t < T, E_L);
   for (int e = threadIdx.x; e < E_L; e += blockDim.x) {
     int c = 0;
 #pragma unroll
@@ -83,23 +96,40 @@ __global__ __launch_bounds__(1024) void index_scan_kernel(
     const int32_t* __restrict__ blk_hist, int nblk, int E_L, int cap,
     int32_t* __restrict__ blk_base, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets) {
-  // E_L <= 1024 = blockDim.x: one expert per thread.
-  const int e = threadIdx.x;
-  int run = 0;
-  if (e < E_L) {
-    for (int b = 0; b < nblk; ++b) {
-      const int c = blk_hist[static_cast<size_t>(b) * E_L + e];
-      blk_base[static_cast<size_t>(b) * E_L + e] = run;
-      run += c;
+  // E_L <= 1024 = blockDim.x.  Thread (part, e) owns expert e over the part's
+  // run of blocks; the parts' sums are scanned in LDS, then every part writes
+  // its bases.  Part 0 of expert e is thread e.
+  __shared__ int part_sum[1024];
+  const int parts = 1024 / E_L;
+  const int e = threadIdx.x % E_L, part = threadIdx.x / E_L;
+  const int chunk = ceil_div(nblk, parts);
+  const int b0 = part * chunk, b1 = min(nblk, b0 + chunk);
+  const bool mine = part < parts;
+  int sum = 0;
+  if (mine)
+    for (int b = b0; b < b1; ++b) sum += blk_hist[static_cast<size_t>(b) * E_L + e];
+  part_sum[threadIdx.x] = mine ? sum : 0;
+  __syncthreads();
+  int base = 0, run = 0;
+  if (mine) {
+    for (int q = 0; q < parts; ++q) {
+      const int v = part_sum[q * E_L + e];
+      if (q < part) base += v;
+      run += v;
+    }
+    int acc = base;
+    for (int b = b0; b < b1; ++b) {
+      blk_base[static_cast<size_t>(b) * E_L + e] = acc;
+      acc += blk_hist[static_cast<size_t>(b) * E_L + e];
     }
   }
   int total;
-  const int off = block_exclusive_scan(e < E_L ? run : 0, &total);
-  if (e < E_L) {
+  const int off = block_exclusive_scan(threadIdx.x < E_L ? run : 0, &total);
+  if (threadIdx.x < E_L) {
     counts[e] = run;
     offsets[e] = cap ? e * cap : off;
   }
-  if (e == 0) offsets[E_L] = cap ? E_L * cap : total;
+  if (threadIdx.x == 0) offsets[E_L] = cap ? E_L * cap : total;
 }
 
 // Rank of token slot t (bit t % 256 of the block) among the block's tokens
@@ -113,6 +143,7 @@ __device__ __forceinline__ int mask_rank(const uint32_t* m, int tb) {
 
 // Count, scan and scatter of at most 256 tokens in one block of 1024 threads
 // (thread e < E_L owns expert e in the scan; thread t < T owns token t).
+template <int KMAX>
 __global__ __launch_bounds__(1024) void index_small_kernel(
     const int32_t* __restrict__ topk_ids, int T, int k, int e_lo, int E_L, int cap,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
@@ -120,7 +151,9 @@ __global__ __launch_bounds__(1024) void index_small_kernel(
     int32_t* __restrict__ token_slot_row) {
   extern __shared__ uint32_t mask[];
   int* s_off = reinterpret_cast<int*>(mask + E_L * kMaskWords);
-  build_masks(mask, topk_ids, T, k, e_lo, E_L, 0);
+  int le[KMAX];
+  if (static_cast<int>(threadIdx.x) < T) token_local_experts<KMAX>(topk_ids, threadIdx.x, k, e_lo, E_L, le);
+  build_masks<KMAX>(mask, le, static_cast<int>(threadIdx.x) < T, E_L);
   const int e = threadIdx.x;
   int c = 0;
   if (e < E_L)
@@ -138,41 +171,45 @@ __global__ __launch_bounds__(1024) void index_small_kernel(
   __syncthreads();
   const int t = threadIdx.x;
   if (t >= T) return;
-  int32_t ids[32];
-  for (int s = 0; s < k; ++s) ids[s] = topk_ids[static_cast<size_t>(t) * k + s];
-  for (int s = 0; s < k; ++s) {
-    const int le = local_expert(ids, s, e_lo, E_L);
-    int pos = -1;
-    if (le >= 0) {
-      pos = s_off[le] + mask_rank(mask + le * kMaskWords, t);
-      row_token[pos] = t;
-      row_slot[pos] = s;
+#pragma unroll
+  for (int s = 0; s < KMAX; ++s) {
+    if (s < k) {
+      int pos = -1;
+      if (le[s] >= 0) {
+        pos = s_off[le[s]] + mask_rank(mask + le[s] * kMaskWords, t);
+        row_token[pos] = t;
+        row_slot[pos] = s;
+      }
+      token_slot_row[static_cast<size_t>(t) * k + s] = pos;
     }
-    token_slot_row[static_cast<size_t>(t) * k + s] = pos;
   }
 }
 
+template <int KMAX>
 __global__ __launch_bounds__(kTokBlock) void index_scatter_kernel(
     const int32_t* __restrict__ topk_ids, int T, int k, int e_lo, int E_L,
     const int32_t* __restrict__ blk_base, const int32_t* __restrict__ offsets,
     int32_t* __restrict__ row_token, int32_t* __restrict__ row_slot,
     int32_t* __restrict__ token_slot_row) {
   extern __shared__ uint32_t mask[];
-  build_masks(mask, topk_ids, T, k, e_lo, E_L, blockIdx.x);
   const int t = blockIdx.x * kTokBlock + threadIdx.x;
+  int le[KMAX];
+  if (t < T) token_local_experts<KMAX>(topk_ids, t, k, e_lo, E_L, le);
+  build_masks<KMAX>(mask, le, t < T, E_L);
   if (t >= T) return;
-  int32_t ids[32];
-  for (int s = 0; s < k; ++s) ids[s] = topk_ids[static_cast<size_t>(t) * k + s];
-  for (int s = 0; s < k; ++s) {
-    const int e = local_expert(ids, s, e_lo, E_L);
-    int pos = -1;
-    if (e >= 0) {
-      pos = offsets[e] + blk_base[static_cast<size_t>(blockIdx.x) * E_L + e] +
-            mask_rank(mask + e * kMaskWords, threadIdx.x);
-      row_token[pos] = t;
-      row_slot[pos] = s;
+#pragma unroll
+  for (int s = 0; s < KMAX; ++s) {
+    if (s < k) {
+      const int e = le[s];
+      int pos = -1;
+      if (e >= 0) {
+        pos = offsets[e] + blk_base[static_cast<size_t>(blockIdx.x) * E_L + e] +
+              mask_rank(mask + e * kMaskWords, threadIdx.x);
+        row_token[pos] = t;
+        row_slot[pos] = s;
+      }
+      token_slot_row[static_cast<size_t>(t) * k + s] = pos;
     }
-    token_slot_row[static_cast<size_t>(t) * k + s] = pos;
   }
 }
 
@@ -470,19 +507,22 @@ hipError_t launch_index_build(const int32_t* topk_ids, int T, int k, int e_lo, i
                               void* scratch, hipStream_t s) {
   if (T <= kTokBlock) {
     const size_t lds = static_cast<size_t>(E_L) * (kMaskWords + 1) * sizeof(uint32_t);
-    hipLaunchKernelGGL(index_small_kernel, dim3(1), dim3(1024), lds, s, topk_ids, T, k, e_lo, E_L,
-                       cap, counts, offsets, row_token, row_slot, token_slot_row);
+    hipLaunchKernelGGL(k <= 8 ? index_small_kernel<8> : index_small_kernel<32>, dim3(1), dim3(1024),
+                       lds, s, topk_ids, T, k, e_lo, E_L, cap, counts, offsets, row_token,
+                       row_slot, token_slot_row);
     return hipGetLastError();
   }
   const int nblk = ceil_div(T, kTokBlock);
   int32_t* blk_hist = static_cast<int32_t*>(scratch);
   int32_t* blk_base = blk_hist + static_cast<size_t>(nblk) * E_L;
   const size_t lds = static_cast<size_t>(E_L) * kMaskWords * sizeof(uint32_t);
-  hipLaunchKernelGGL(index_count_kernel, dim3(nblk), dim3(kTokBlock), lds, s,
+  hipLaunchKernelGGL(k <= 8 ? index_count_kernel<8> : index_count_kernel<32>, dim3(nblk),
+                     dim3(kTokBlock), lds, s,
                      topk_ids, T, k, e_lo, E_L, blk_hist);
   hipLaunchKernelGGL(index_scan_kernel, dim3(1), dim3(1024), 0, s,
                      blk_hist, nblk, E_L, cap, blk_base, counts, offsets);
-  hipLaunchKernelGGL(index_scatter_kernel, dim3(nblk), dim3(kTokBlock), lds, s,
+  hipLaunchKernelGGL(k <= 8 ? index_scatter_kernel<8> : index_scatter_kernel<32>, dim3(nblk),
+                     dim3(kTokBlock), lds, s,
                      topk_ids, T, k, e_lo, E_L, blk_base, offsets, row_token, row_slot,
                      token_slot_row);
   return hipGetLastError();

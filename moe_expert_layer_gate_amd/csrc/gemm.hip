@@ -1195,13 +1195,16 @@ __device__ __forceinline__ void big_tile(const GemmArgs& g, const int4 unit, uin
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(a_base, a_left);
   const __amdgpu_buffer_rsrc_t rW = make_rsrc(w_base, g.w_stride);
   auto dma = [&](int step, int stage) {
-    const int k = min(step, nk - 1);
+    // steps past the last one load nothing (out-of-range offsets), which
+    // keeps the per-step load count that the waits rely on
+    const bool live = step < nk;
+    const int k = live ? step : 0;
     uint8_t* base = smem + stage * kStageBytes;
 #pragma unroll
     for (int q = 0; q < kLoads; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(q < kALoads ? rA : rW, (lds_ptr_t)(base + ldst[q]),
-                                               16, voff[q], k * (q < kALoads ? g.a_cs : g.w_cs), 0,
-                                               0);
+                                               16, live ? voff[q] : kOobOffset,
+                                               k * (q < kALoads ? g.a_cs : g.w_cs), 0, 0);
   };
 
   const int wm = w % kWaveRows, wn = w / kWaveRows;

@@ -34,9 +34,28 @@ __device__ __forceinline__ int key_expert(uint64_t key) {
   return static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(key));
 }
 
+// One max step against lane permutation CTRL (a DPP control): every lane
+// combines its key with the key of its partner lane.
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_max_u64(uint64_t v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(v)), CTRL,
+                                             0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(v >> 32)),
+                                             CTRL, 0xF, 0xF, false);
+  const uint64_t o = (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
+  return o > v ? o : v;
+}
+
+// Max of a 64-bit key over the wave: within rows of 16 lanes by DPP (swap
+// neighbours, swap pairs, mirror halves of 8, mirror the row), then across
+// the four rows through two lane exchanges.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = dpp_max_u64<0xB1>(v);   // quad_perm [1,0,3,2]
+  v = dpp_max_u64<0x4E>(v);   // quad_perm [2,3,0,1]
+  v = dpp_max_u64<0x141>(v);  // row_half_mirror
+  v = dpp_max_u64<0x140>(v);  // row_mirror
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
+  for (int off = 16; off <= 32; off <<= 1) {
     uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), off);
     uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), off);
     uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;

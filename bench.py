@@ -91,8 +91,9 @@ def gemm_rows(counts, fp8: bool, max_pairs: int, E_L: int, mx: bool = False) -> 
     tiles (bf16: a last remainder of 1..128 rows takes a 128-row wide tile)."""
     rows = 0
     for c in (int(x) for x in counts):
-        if mx:                                   # MX: 128-row tiles throughout
-            rows += -(-c // 128) * 128
+        if mx:                   # MX: 128-row tiles, 256-row beyond 256 rows per expert
+            tm = 256 if max_pairs // E_L > 256 else 128
+            rows += -(-c // tm) * tm
         elif not fp8 and max_pairs // E_L <= 32:
             rows += -(-c // 32) * 32
         elif max_pairs // E_L <= 256:

@@ -793,14 +793,27 @@ hipError_t launch_fused(const GemmArgs& gu, const GemmArgs& gd, int64_t max_tile
 // GEMM's epilogue writes h as MXFP8: each 32-column block of one token is one
 // instruction tile, split over lanes l and l ^ 32.
 // ---------------------------------------------------------------------------
-constexpr int kMxBM = 128, kMxBN = 256, kMxThreads = 256, kMxStages = 4;
+constexpr int kMxBN = 256;
 constexpr int kMxK = 128;                                  // K elements per step
-constexpr int kMxWOff = kMxBM * kMxK;                      // token rows [128][128 B] first
-constexpr int kMxSAOff = kMxWOff + kMxBN * (kMxK / 2);     // weight rows [256][64 B]
-constexpr int kMxSWOff = kMxSAOff + kMxBM * 4;             // token scales [128] dwords
-constexpr int kMxStageBytes = kMxSWOff + kMxBN * 4;        // weight scales [256] dwords
-constexpr int kMxLoads = 4 + 4 + 1 + 1;                    // direct loads per wave and step
-static_assert(kMxStages * kMxStageBytes <= 160 * 1024, "the ring fits the CU's LDS");
+
+// Two block shapes: 128 token rows with 4 waves and a four-stage ring, or
+// (many rows per expert) 256 token rows with 8 waves (two per SIMD) and three
+// 50 KB stages.  A stage holds the token rows [BM][128 B], the weight rows
+// [256][64 B], then one scale dword per token row and per weight row.
+template <int BM_>
+struct MxShape {
+  static constexpr int BM = BM_, NW = BM / 64 * 2, THREADS = NW * 64;
+  static constexpr int STAGES = BM == 128 ? 4 : 3;
+  static constexpr int WOFF = BM * kMxK;
+  static constexpr int SAOFF = WOFF + kMxBN * (kMxK / 2);
+  static constexpr int SWOFF = SAOFF + BM * 4;
+  static constexpr int STAGE_BYTES = SWOFF + kMxBN * 4;
+  // direct loads per wave and step: token row groups (8 rows of 128 B),
+  // weight row groups (16 rows of 64 B), scale dwords
+  static constexpr int TL = BM / 8 / NW, WL = kMxBN / 16 / NW;
+  static constexpr int LOADS = TL + WL + (BM == 128 ? 2 : 1);
+  static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "the ring fits the CU's LDS");
+};
 
 // E8M0 exponent (biased) of a block whose largest magnitude is amax, for an
 // element format whose largest normal has exponent emax: floor(log2 amax) -
@@ -812,10 +825,12 @@ __device__ __forceinline__ int mx_scale_code(float amax, int emax) {
   return (s < -127 ? -127 : s) + 127;
 }
 
-template <int MODE>
-__global__ __launch_bounds__(kMxThreads, 1) void gemm_mx_kernel(const GemmArgs g) {
-  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+template <int MODE, class SH>
+__device__ __forceinline__ void mx_tile(const GemmArgs& g, uint8_t* smem) {
   constexpr bool kSwiglu = MODE == MODE_SWIGLU_MX8OUT;
+  constexpr int kMxBM = SH::BM, kMxStages = SH::STAGES, kMxStageBytes = SH::STAGE_BYTES;
+  constexpr int kMxWOff = SH::WOFF, kMxSAOff = SH::SAOFF, kMxSWOff = SH::SWOFF;
+  constexpr int kMxLoads = SH::LOADS, TL = SH::TL, WL = SH::WL;
   const int total = *g.n_tiles * g.nt_n;
   const int per_xcd = ceil_div(total, kXcds);
   const int slot = blockIdx.x / kXcds;
@@ -847,41 +862,68 @@ __global__ __launch_bounds__(kMxThreads, 1) void gemm_mx_kernel(const GemmArgs g
   };
 
   const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
-  // Direct loads of wave w per step: token row groups (8 rows of 128 B)
-  // 4w..4w+3, weight row groups (16 rows of 64 B) 4w..4w+3, 64 weight scale
-  // dwords (rows 64w..) and 64 token scale dwords (rows 64 (w & 1)..; waves
-  // w and w ^ 2 write the same values to the same place).  A direct load
-  // writes one dword per lane, so scales move as whole dwords.
+  // Direct loads of wave w per step: token row groups TL w.., weight row
+  // groups WL w.., and scale dwords (a direct load writes one dword per lane,
+  // so scales move as whole dwords).  128 rows: 64 weight scales (rows 64w..)
+  // and 64 token scales (rows 64 (w & 1)..; waves w and w ^ 2 write the same
+  // values to the same place).  256 rows: waves 0-3 the token scales of rows
+  // 64w.., waves 4-7 the weight scales of rows 64 (w - 4)...
   int voff[kMxLoads];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int rr = (w * 4 + q) * 8 + (lane >> 3);
+  for (int q = 0; q < TL; ++q) {
+    const int rr = (w * TL + q) * 8 + (lane >> 3);
     const int c = (lane & 7) ^ ((rr >> 1) & 7);
     voff[q] = row0 + rr < seg_end ? rr * K + c * 16 : kOobOffset;
-    const int r = (w * 4 + q) * 16 + (lane >> 2);
-    const int cw = (lane & 3) ^ ((r >> 2) & 3);
-    voff[4 + q] = wrow(r) * (K / 2) + cw * 16;
   }
-  voff[8] = wrow(w * 64 + lane) * kb;
-  {
+#pragma unroll
+  for (int q = 0; q < WL; ++q) {
+    const int r = (w * WL + q) * 16 + (lane >> 2);
+    const int cw = (lane & 3) ^ ((r >> 2) & 3);
+    voff[TL + q] = wrow(r) * (K / 2) + cw * 16;
+  }
+  bool s_tok;      // 256 rows: this wave's scale load is a token-scale one
+  int s_lds;
+  if constexpr (kMxBM == 128) {
+    voff[TL + WL] = wrow(w * 64 + lane) * kb;
     const int rr = (w & 1) * 64 + lane;
-    voff[9] = row0 + rr < seg_end ? rr * kb : kOobOffset;
+    voff[TL + WL + 1] = row0 + rr < seg_end ? rr * kb : kOobOffset;
+    s_tok = false;
+    s_lds = 0;
+  } else {
+    s_tok = w < 4;
+    if (s_tok) {
+      const int rr = w * 64 + lane;
+      voff[TL + WL] = row0 + rr < seg_end ? rr * kb : kOobOffset;
+      s_lds = kMxSAOff + w * 256;
+    } else {
+      voff[TL + WL] = wrow((w - 4) * 64 + lane) * kb;
+      s_lds = kMxSWOff + (w - 4) * 256;
+    }
   }
   auto dma = [&](int step, int stage) {
-    const int k = min(step, nk - 1);
+    // steps past the last one load nothing (out-of-range offsets)
+    const bool live = step < nk;
+    const int k = live ? step : 0;
     uint8_t* base = smem + stage * kMxStageBytes;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr_t)(base + (w * 4 + q) * 1024), 16,
-                                               voff[q], k * kMxK, 0, 0);
+    for (int q = 0; q < TL; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr_t)(base + (w * TL + q) * 1024), 16,
+                                               live ? voff[q] : kOobOffset, k * kMxK, 0, 0);
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, (lds_ptr_t)(base + kMxWOff + (w * 4 + q) * 1024),
-                                               16, voff[4 + q], k * (kMxK / 2), 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rWS, (lds_ptr_t)(base + kMxSWOff + w * 256), 4,
-                                             voff[8], k * 4, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rAS, (lds_ptr_t)(base + kMxSAOff + (w & 1) * 256),
-                                             4, voff[9], k * 4, 0, 0);
+    for (int q = 0; q < WL; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, (lds_ptr_t)(base + kMxWOff + (w * WL + q) * 1024),
+                                               16, live ? voff[TL + q] : kOobOffset,
+                                               k * (kMxK / 2), 0, 0);
+    if constexpr (kMxBM == 128) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rWS, (lds_ptr_t)(base + kMxSWOff + w * 256), 4,
+                                               live ? voff[TL + WL] : kOobOffset, k * 4, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rAS, (lds_ptr_t)(base + kMxSAOff + (w & 1) * 256),
+                                               4, live ? voff[TL + WL + 1] : kOobOffset, k * 4, 0,
+                                               0);
+    } else {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(s_tok ? rAS : rWS, (lds_ptr_t)(base + s_lds), 4,
+                                               live ? voff[TL + WL] : kOobOffset, k * 4, 0, 0);
+    }
   };
 
   // Fragment addresses: wave (wm, wn) holds tokens wm*64.. and weight rows
@@ -1010,10 +1052,17 @@ __global__ __launch_bounds__(kMxThreads, 1) void gemm_mx_kernel(const GemmArgs g
   }
 }
 
-template <int MODE>
+template <int MODE, int BM>
+__global__ __launch_bounds__(MxShape<BM>::THREADS, 1) void gemm_mx_kernel(const GemmArgs g) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  mx_tile<MODE, MxShape<BM>>(g, smem);
+}
+
+template <int MODE, int BM>
 hipError_t launch_mx(const GemmArgs& g, int64_t max_tiles, hipStream_t s) {
-  auto kern = gemm_mx_kernel<MODE>;
-  const size_t lds = kMxStages * kMxStageBytes;
+  using SH = MxShape<BM>;
+  auto kern = gemm_mx_kernel<MODE, BM>;
+  const size_t lds = SH::STAGES * SH::STAGE_BYTES;
   static bool attr_set = false;
   if (!attr_set) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -1023,7 +1072,7 @@ hipError_t launch_mx(const GemmArgs& g, int64_t max_tiles, hipStream_t s) {
     attr_set = true;
   }
   const int64_t blocks = (max_tiles * g.nt_n + kXcds - 1) / kXcds * kXcds + kXcds;
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(kMxThreads), lds, s, g);
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(SH::THREADS), lds, s, g);
   return hipGetLastError();
 }
 
@@ -1725,7 +1774,8 @@ int gemm_path_rows(GemmPath path) {
     case GEMM_PIPELINED: return kBM;
     case GEMM_LARGE: return kBigBM;
     case GEMM_LARGE_FP8: return kF8BM;
-    case GEMM_MX: return kMxBM;
+    case GEMM_MX: return 128;
+    case GEMM_MX_LARGE: return 256;
   }
   return kBM;
 }
@@ -1780,7 +1830,7 @@ static hipError_t make_args(const GemmLaunch& L, GemmArgs& g) {
   g.Nout = L.Nout;
   g.NW = L.swiglu ? 2 * L.Nout : L.Nout;
   g.nt_n = gemm_n_tiles(L.swiglu, L.Nout);
-  if (L.mx != (L.path == GEMM_MX)) return hipErrorInvalidValue;
+  if (L.mx != (L.path == GEMM_MX || L.path == GEMM_MX_LARGE)) return hipErrorInvalidValue;
   if (L.mx) {  // E4M3 tokens, E2M1 weights, E8M0 bytes per 32 along K; row major
     if (L.fp8 || L.a_panel || L.w_panel || L.c_panel || L.a_index || L.gelu || L.K % kMxK)
       return hipErrorInvalidValue;
@@ -1826,8 +1876,11 @@ hipError_t launch_grouped_gemm(const GemmLaunch& L, hipStream_t s) {
     case GEMM_SKINNY:
       return hipErrorInvalidValue;  // both GEMMs at once: launch_ffn_fused
     case GEMM_MX:
-      return L.swiglu ? launch_mx<MODE_SWIGLU_MX8OUT>(g, L.max_tiles, s)
-                      : launch_mx<MODE_PLAIN>(g, L.max_tiles, s);
+      return L.swiglu ? launch_mx<MODE_SWIGLU_MX8OUT, 128>(g, L.max_tiles, s)
+                      : launch_mx<MODE_PLAIN, 128>(g, L.max_tiles, s);
+    case GEMM_MX_LARGE:
+      return L.swiglu ? launch_mx<MODE_SWIGLU_MX8OUT, 256>(g, L.max_tiles, s)
+                      : launch_mx<MODE_PLAIN, 256>(g, L.max_tiles, s);
     case GEMM_LARGE_FP8:
       if (!L.swiglu) return launch_big_fp8<MODE_PLAIN>(g, L.max_tiles, s);
       if (!L.C_scale) return hipErrorInvalidValue;  // block-FP8 h only

@@ -51,6 +51,7 @@ enum GemmPath {
   GEMM_LARGE = 2,      // bf16: 256 x 256 tiles, 128 x 512 for segment remainders
   GEMM_LARGE_FP8 = 3,  // block-FP8: 256 x 256 tiles
   GEMM_MX = 4,         // MXFP4 weights x MXFP8 activations: 128 x 256 tiles
+  GEMM_MX_LARGE = 5,   // the same, more than 256 rows per expert: 256 x 256 tiles
 };
 GemmPath gemm_path(bool fp8, int64_t rows_per_expert);
 // Token rows of the path's tiles (of its full tiles, for GEMM_LARGE).

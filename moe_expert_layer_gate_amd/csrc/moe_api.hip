@@ -131,7 +131,8 @@ FfnShape ffn_shape(const moe_problem* p) {
   // layout of the buffers
   const int64_t N = n_pairs(p);
   FfnShape f{};
-  f.path = is_mx(p) ? GEMM_MX : gemm_path(is_fp8(p), N / p->num_local);
+  f.path = is_mx(p) ? (N / p->num_local > 256 ? GEMM_MX_LARGE : GEMM_MX)
+                    : gemm_path(is_fp8(p), N / p->num_local);
   f.nt_up = gemm_n_tiles(!is_gelu(p), p->inter);
   f.nt_dn = gemm_n_tiles(false, p->hidden);
   f.cap_up = schedule_entries(N, p->num_local, f.path, f.nt_up);

@@ -87,6 +87,9 @@ SMALL_MX = {
     "mx_shared": (small_cfg(T=150, H=1024, E=64, E_L=16, e_lo=16, k=8, I=512, I_s=256,
                             mx=True), 43),
     "mx_decode": (small_cfg(T=16, H=1024, E=64, E_L=16, e_lo=0, k=8, I=256, mx=True), 44),
+    # more than 256 rows per expert: the 256-row MX tiles, ragged segment ends
+    "mx_large_tiles": (small_cfg(T=1300, H=384, E=8, E_L=4, e_lo=2, k=2, I=640, I_s=256,
+                                 mx=True), 45),
 }
 
 

@@ -88,11 +88,13 @@ def gemm_rows(counts, fp8: bool, max_pairs: int, E_L: int, mx: bool = False) -> 
     """Token rows the GEMMs compute, padding included, under the library's
     tile choice (from the most pairs per expert on average, T min(k, E_L) /
     E_L): bf16 32-row tiles up to 32; 128-row tiles up to 256; else 256-row
-    tiles (bf16: a last remainder of 1..128 rows takes a 128-row wide tile)."""
+    tiles (bf16: a last remainder of 1..128 rows takes a 128-row wide tile).
+    MX: 32-row tiles up to 32, 128-row up to 256, else 256-row tiles."""
     rows = 0
     for c in (int(x) for x in counts):
-        if mx:                   # MX: 128-row tiles, 256-row beyond 256 rows per expert
-            tm = 256 if max_pairs // E_L > 256 else 128
+        if mx:
+            r = max_pairs // E_L
+            tm = 256 if r > 256 else 128 if r > 32 else 32
             rows += -(-c // tm) * tm
         elif not fp8 and max_pairs // E_L <= 32:
             rows += -(-c // 32) * 32
@@ -245,7 +247,7 @@ def main():
 
     traffic = stored_traffic(cfg.name + ("_masked" if cap else ""))
     act = "SwiGLU" if cfg.act == "swiglu" else "GELU"
-    skinny = not quant and p.T * min(p.k, p.E_L) // p.E_L <= 32
+    skinny = (cfg.mx or not quant) and p.T * min(p.k, p.E_L) // p.E_L <= 32
     kernel = ((f"grouped FFN: work table + one launch of up GEMM/{act} and down GEMM" if skinny
                else f"grouped FFN: work table + up GEMM/{act} + down GEMM")
               + (" (+ shared expert: x quantisation and its FFN)" if p.I_s else ""))

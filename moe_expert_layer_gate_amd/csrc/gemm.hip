@@ -694,89 +694,6 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& g, int t, uint8_t* s
 }
 
 // ---------------------------------------------------------------------------
-// Both GEMMs of a decode-sized FFN in one launch.  Two launches leave each
-// GEMM's last wave of tiles partly empty (448 up and 784 down tiles on 256
-// CUs for the DeepSeek-V3 shard's decode batch: 1.75 and 3.06 waves) and
-// leave a gap between them; here every block takes the next ticket of one
-// queue -- all up tiles, then all down tiles -- so CUs freed by the up GEMM go
-// straight on to down tiles and the weights stream without a break.
-//  * An up tile stores its h columns, waits for its stores (workgroup-scope
-//    release), meets at a block barrier, and one thread then releases at
-//    device scope (which writes the XCD's L2 back) and adds one to its
-//    m-tile's counter.
-//  * A down tile's first thread polls its m-tile's counter until it equals
-//    the number of up n-tiles and then acquires at device scope (which
-//    invalidates the CU's and the XCD's caches) before the block barrier, so
-//    the tile's h loads see the up tiles' stores.
-//  One release per up tile and one acquire per down tile: with a device fence
-//  in every thread the cache write-backs and invalidations cost the decode
-//  FFN 35 % (0.548 against 0.403 ms for the DeepSeek-V3 decode batch).
-// Tickets are taken in order and every up ticket precedes every down ticket,
-// so a down tile waits only on up tiles that blocks already running hold,
-// and up tiles wait on nothing: every wait ends.  (The wait is still bounded;
-// past the bound the tile proceeds, which can only happen if that argument
-// failed.)  The grid has a block for every possible ticket; blocks whose
-// ticket is past the live work return at once.
-// ---------------------------------------------------------------------------
-constexpr int kSpinLimit = 1 << 22;  // about half a second of s_sleep 2 polls
-
-template <int UPMODE>
-__global__ __launch_bounds__(kSkThreads, 1) void ffn_fused_skinny_kernel(const GemmArgs gu,
-                                                                        const GemmArgs gd,
-                                                                        int32_t* sync) {
-  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
-  __shared__ int s_ticket;
-  const int n_m = *gu.n_tiles;  // live m-tiles (one table for both GEMMs)
-  const int n_up = n_m * gu.nt_n, total = n_up + n_m * gd.nt_n;
-  if (threadIdx.x == 0) s_ticket = atomicAdd(sync, 1);
-  __syncthreads();
-  const int t = s_ticket;
-  if (t >= total) return;
-  int32_t* done = sync + 1;
-  if (t < n_up) {
-    skinny_tile<UPMODE>(gu, t, smem);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      atomicAdd(done + skinny_decode(gu, t).w, 1);
-    }
-    return;
-  }
-  const int td = t - n_up;
-  if (threadIdx.x == 0) {
-    const int32_t* c = done + skinny_decode(gd, td).w;
-    for (int it = 0; it < kSpinLimit; ++it) {
-      if (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= gu.nt_n) break;
-      __builtin_amdgcn_s_sleep(2);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  }
-  __syncthreads();
-  skinny_tile<MODE_PLAIN>(gd, td, smem);
-}
-
-template <int UPMODE>
-hipError_t launch_fused(const GemmArgs& gu, const GemmArgs& gd, int64_t max_tiles, int32_t* sync,
-                        hipStream_t s) {
-  static_assert(kSkStages * kSkStageBytes <= 160 * 1024, "the ring fits the CU's LDS");
-  auto kern = ffn_fused_skinny_kernel<UPMODE>;
-  const size_t lds = kSkStages * kSkStageBytes;
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                            static_cast<int>(lds)) != hipSuccess)
-      (void)hipGetLastError();
-    attr_set = true;
-  }
-  const int64_t blocks = max_tiles * (gu.nt_n + gd.nt_n);
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(kSkThreads), lds, s, gu, gd,
-                     sync);
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
 // MXFP4 weights x MXFP8 activations (OCP MX formats: E2M1 and E4M3 elements,
 // one E8M0 scale 2^(e - 127) per 32 consecutive K elements of a row) on the
 // block-scaled matrix instruction v_mfma_scale_f32_32x32x64_f8f6f4, which
@@ -1073,6 +990,286 @@ hipError_t launch_mx(const GemmArgs& g, int64_t max_tiles, hipStream_t s) {
   }
   const int64_t blocks = (max_tiles * g.nt_n + kXcds - 1) / kXcds * kXcds + kXcds;
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(SH::THREADS), lds, s, g);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Skinny MX kernel for a few rows per expert (decode with MXFP4 weights):
+// 32 token rows x 256 weight rows per block, 4 waves each holding 32 x 64
+// (two 32 x 32 instruction tiles; SwiGLU: the gate and up rows of the same
+// 32 h columns, i.e. one MX block of h per token).  As in the bf16 skinny
+// kernel the work is weight streaming and the LDS goes to depth: K steps of
+// 128 (64 bytes of E2M1 per weight row, 16 KB per step) through a seven-stage
+// ring of 21 KB stages, loads six steps ahead (96 KB of weights in flight per
+// CU).  Operand placement, swizzles and the MXFP8 h epilogue are those of the
+// 128-row MX tile.  A stage holds the token rows [32][128 B], the weight rows
+// [256][64 B], 64 token-scale dwords (rows 32..63 read as zeros) and 256
+// weight-scale dwords.
+// ---------------------------------------------------------------------------
+constexpr int kMsBM = 32, kMsStages = 7;
+constexpr int kMsWOff = kMsBM * kMxK;                       // 4 KB
+constexpr int kMsTSOff = kMsWOff + kMxBN * (kMxK / 2);      // + 16 KB
+constexpr int kMsWSOff = kMsTSOff + 64 * 4;
+constexpr int kMsStageBytes = kMsWSOff + kMxBN * 4;         // 21760
+// per wave and step: one token row group (8 rows), four weight row groups
+// (16 rows), one weight-scale load and one token-scale load (every wave
+// writes the same token scales to the same place)
+constexpr int kMsLoads = 7;
+static_assert(kMsStages * kMsStageBytes <= 160 * 1024, "the ring fits the CU's LDS");
+static_assert((kMsStages - 1) * kMsLoads < 64, "loads in flight fit the vmcnt counter");
+
+template <int MODE>
+__device__ __forceinline__ void mx_skinny_tile(const GemmArgs& g, int t, uint8_t* smem) {
+  constexpr bool kSwiglu = MODE == MODE_SWIGLU_MX8OUT;
+  const int4 td = skinny_decode(g, t);
+  const int e = td.x, mt = td.y, nt = td.z;
+  const int2 sg = segment(g.seg, g.seg_cap, e);
+  const int seg_end = sg.y;
+  const int row0 = sg.x + mt * kMsBM;
+  const int K = g.K, kb = K / 32, nk = K / kMxK;
+  const uint8_t* As = reinterpret_cast<const uint8_t*>(g.A_scale);
+  const uint8_t* Ws = reinterpret_cast<const uint8_t*>(g.W_scale);
+  const int64_t a_skip = static_cast<int64_t>(row0) * K;
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(g.A + a_skip, g.a_bytes - a_skip);
+  const __amdgpu_buffer_rsrc_t rW = make_rsrc(g.W + e * g.w_stride, g.w_stride);
+  const __amdgpu_buffer_rsrc_t rAS =
+      make_rsrc(As + static_cast<int64_t>(row0) * kb, (g.a_bytes / K - row0) * kb);
+  const __amdgpu_buffer_rsrc_t rWS = make_rsrc(Ws + e * g.ws_stride, g.ws_stride);
+  const int nbase = kSwiglu ? nt * (kMxBN / 2) : nt * kMxBN;
+  auto wrow = [&](int r) {  // weight row (within the expert) of tile row r
+    if (kSwiglu)
+      return r < kMxBN / 2 ? min(nbase + r, g.Nout - 1)
+                           : g.Nout + min(nbase + (r - kMxBN / 2), g.Nout - 1);
+    return min(nbase + r, g.NW - 1);
+  };
+
+  const int lane = lane_id(), w = threadIdx.x >> 6;
+  int voff[kMsLoads];
+  {
+    const int rr = w * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((rr >> 1) & 7);
+    voff[0] = row0 + rr < seg_end ? rr * K + c * 16 : kOobOffset;
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = (w * 4 + q) * 16 + (lane >> 2);
+    const int cw = (lane & 3) ^ ((r >> 2) & 3);
+    voff[1 + q] = wrow(r) * (K / 2) + cw * 16;
+  }
+  voff[5] = wrow(w * 64 + lane) * kb;
+  voff[6] = lane < kMsBM && row0 + lane < seg_end ? lane * kb : kOobOffset;
+  auto dma = [&](int step, int stage) {
+    // steps past the last one load nothing (out-of-range offsets)
+    const bool live = step < nk;
+    const int k = live ? step : 0;
+    uint8_t* base = smem + stage * kMsStageBytes;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr_t)(base + w * 1024), 16,
+                                             live ? voff[0] : kOobOffset, k * kMxK, 0, 0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, (lds_ptr_t)(base + kMsWOff + (w * 4 + q) * 1024),
+                                               16, live ? voff[1 + q] : kOobOffset,
+                                               k * (kMxK / 2), 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rWS, (lds_ptr_t)(base + kMsWSOff + w * 256), 4,
+                                             live ? voff[5] : kOobOffset, k * 4, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rAS, (lds_ptr_t)(base + kMsTSOff), 4,
+                                             live ? voff[6] : kOobOffset, k * 4, 0, 0);
+  };
+
+  // fragments: weight tiles i = 0, 1 of wave w (SwiGLU: gate rows w*32.. and
+  // up rows 128 + w*32..; plain: rows w*64 + i*32..), token lane % 32
+  const int lr = lane & 31, hi = lane >> 5;
+  int wfr[2][2], wsc[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = (kSwiglu ? i * (kMxBN / 2) + w * 32 : w * 64 + i * 32) + lr;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+      wfr[i][hh] = kMsWOff + r * 64 + (((2 * hh + hi) ^ ((r >> 2) & 3)) * 16);
+    wsc[i] = kMsWSOff + r * 4;
+  }
+  int tfr[2][2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    tfr[hh][0] = lr * kMxK + (((4 * hh + hi) ^ ((lr >> 1) & 7)) * 16);
+    tfr[hh][1] = lr * kMxK + (((4 * hh + 2 + hi) ^ ((lr >> 1) & 7)) * 16);
+  }
+  const int tsc = kMsTSOff + lr * 4;
+
+  f32x16 acc[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.0f;
+
+#pragma unroll
+  for (int st = 0; st < kMsStages - 1; ++st) dma(st, st);
+  WAIT_VMCNT((kMsStages - 2) * kMsLoads);
+  __builtin_amdgcn_s_barrier();
+
+  int s_cur = 0;
+  for (int kt = 0; kt < nk; ++kt) {
+    const uint8_t* st = smem + s_cur * kMsStageBytes;
+    dma(kt + kMsStages - 1, s_cur == 0 ? kMsStages - 1 : s_cur - 1);
+    const uint32_t ts = *reinterpret_cast<const uint32_t*>(st + tsc);
+    uint32_t ws[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) ws[i] = *reinterpret_cast<const uint32_t*>(st + wsc[i]);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const i32x4 p0 = *reinterpret_cast<const i32x4*>(st + tfr[hh][0]);
+      const i32x4 p1 = *reinterpret_cast<const i32x4*>(st + tfr[hh][1]);
+      const i32x8 tb = i32x8{p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+      const int sb = static_cast<int>((ts >> (16 * hh + 8 * hi)) & 0xff);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const i32x4 p = *reinterpret_cast<const i32x4*>(st + wfr[i][hh]);
+        const i32x8 wa = i32x8{p[0], p[1], p[2], p[3], 0, 0, 0, 0};
+        const int sa = static_cast<int>((ws[i] >> (16 * hh + 8 * hi)) & 0xff);
+        acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wa, tb, acc[i], 4, 0, 0, sa, 0,
+                                                                  sb);
+      }
+    }
+    WAIT_VMCNT_LDS((kMsStages - 2) * kMsLoads);
+    __builtin_amdgcn_s_barrier();
+    s_cur = s_cur + 1 == kMsStages ? 0 : s_cur + 1;
+  }
+  WAIT_VMCNT(0);
+
+  // accumulator element q*4 + r: weight row q*8 + (lane/32)*4 + r of the
+  // tile, token lane % 32
+  const int cq = hi * 4;
+  const int m = row0 + lr;
+  const bool live = m < seg_end;
+  uint8_t* C8 = static_cast<uint8_t*>(g.C);
+  if constexpr (MODE == MODE_PLAIN) {
+    if (!live) return;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = nbase + w * 64 + i * 32 + q * 8 + cq;
+        if (col >= g.Nout) continue;
+        uint2 o;
+        o.x = pack_bf16x2(acc[i][q * 4 + 0], acc[i][q * 4 + 1]);
+        o.y = pack_bf16x2(acc[i][q * 4 + 2], acc[i][q * 4 + 3]);
+        *reinterpret_cast<uint2*>(C8 + (static_cast<int64_t>(m) * g.Nout + col) * 2) = o;
+      }
+  } else {
+    // h = silu(gate) * up: the wave's 32 h columns of one token are one MX
+    // block, held by lanes l and l ^ 32 (the shuffle runs in every lane)
+    float hv[16];
+    float amax = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      hv[r] = silu_mul(acc[0][r], acc[1][r]);
+      amax = fmaxf(amax, fabsf(hv[r]));
+    }
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    const int code = mx_scale_code(amax, 8);
+    const int c0 = nbase + w * 32;
+    if (!live || c0 >= g.Nout) return;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float* v = hv + q * 4;
+      const uint32_t p = f32x4_to_e4m3x4(ldexpf(v[0], 127 - code), ldexpf(v[1], 127 - code),
+                                         ldexpf(v[2], 127 - code), ldexpf(v[3], 127 - code));
+      *reinterpret_cast<uint32_t*>(C8 + static_cast<int64_t>(m) * g.Nout + c0 + q * 8 + cq) = p;
+    }
+    if (hi == 0)
+      reinterpret_cast<uint8_t*>(g.C_scale)[static_cast<int64_t>(m) * (g.Nout / 32) + c0 / 32] =
+          static_cast<uint8_t>(code);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Both GEMMs of a decode-sized FFN in one launch.  Two launches leave each
+// GEMM's last wave of tiles partly empty (448 up and 784 down tiles on 256
+// CUs for the DeepSeek-V3 shard's decode batch: 1.75 and 3.06 waves) and
+// leave a gap between them; here every block takes the next ticket of one
+// queue -- all up tiles, then all down tiles -- so CUs freed by the up GEMM go
+// straight on to down tiles and the weights stream without a break.
+//  * An up tile stores its h columns, waits for its stores (workgroup-scope
+//    release), meets at a block barrier, and one thread then releases at
+//    device scope (which writes the XCD's L2 back) and adds one to its
+//    m-tile's counter.
+//  * A down tile's first thread polls its m-tile's counter until it equals
+//    the number of up n-tiles and then acquires at device scope (which
+//    invalidates the CU's and the XCD's caches) before the block barrier, so
+//    the tile's h loads see the up tiles' stores.
+//  One release per up tile and one acquire per down tile: with a device fence
+//  in every thread the cache write-backs and invalidations cost the decode
+//  FFN 35 % (0.548 against 0.403 ms for the DeepSeek-V3 decode batch).
+// Tickets are taken in order and every up ticket precedes every down ticket,
+// so a down tile waits only on up tiles that blocks already running hold,
+// and up tiles wait on nothing: every wait ends.  (The wait is still bounded;
+// past the bound the tile proceeds, which can only happen if that argument
+// failed.)  The grid has a block for every possible ticket; blocks whose
+// ticket is past the live work return at once.
+// ---------------------------------------------------------------------------
+constexpr int kSpinLimit = 1 << 22;  // about half a second of s_sleep 2 polls
+
+// MX: the skinny MX tiles (MXFP4 weights, MXFP8 tokens and h), else the
+// bf16 skinny tiles.
+template <int UPMODE, bool MX>
+__global__ __launch_bounds__(kSkThreads, 1) void ffn_fused_skinny_kernel(const GemmArgs gu,
+                                                                        const GemmArgs gd,
+                                                                        int32_t* sync) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  __shared__ int s_ticket;
+  const int n_m = *gu.n_tiles;  // live m-tiles (one table for both GEMMs)
+  const int n_up = n_m * gu.nt_n, total = n_up + n_m * gd.nt_n;
+  if (threadIdx.x == 0) s_ticket = atomicAdd(sync, 1);
+  __syncthreads();
+  const int t = s_ticket;
+  if (t >= total) return;
+  int32_t* done = sync + 1;
+  if (t < n_up) {
+    if constexpr (MX)
+      mx_skinny_tile<UPMODE>(gu, t, smem);
+    else
+      skinny_tile<UPMODE>(gu, t, smem);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      atomicAdd(done + skinny_decode(gu, t).w, 1);
+    }
+    return;
+  }
+  const int td = t - n_up;
+  if (threadIdx.x == 0) {
+    const int32_t* c = done + skinny_decode(gd, td).w;
+    for (int it = 0; it < kSpinLimit; ++it) {
+      if (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= gu.nt_n) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
+  if constexpr (MX)
+    mx_skinny_tile<MODE_PLAIN>(gd, td, smem);
+  else
+    skinny_tile<MODE_PLAIN>(gd, td, smem);
+}
+
+template <int UPMODE, bool MX>
+hipError_t launch_fused(const GemmArgs& gu, const GemmArgs& gd, int64_t max_tiles, int32_t* sync,
+                        hipStream_t s) {
+  static_assert(kSkStages * kSkStageBytes <= 160 * 1024, "the ring fits the CU's LDS");
+  auto kern = ffn_fused_skinny_kernel<UPMODE, MX>;
+  const size_t lds = MX ? kMsStages * kMsStageBytes : kSkStages * kSkStageBytes;
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(lds)) != hipSuccess)
+      (void)hipGetLastError();
+    attr_set = true;
+  }
+  const int64_t blocks = max_tiles * (gu.nt_n + gd.nt_n);
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(kSkThreads), lds, s, gu, gd,
+                     sync);
   return hipGetLastError();
 }
 
@@ -1776,6 +1973,7 @@ int gemm_path_rows(GemmPath path) {
     case GEMM_LARGE_FP8: return kF8BM;
     case GEMM_MX: return 128;
     case GEMM_MX_LARGE: return 256;
+    case GEMM_MX_SKINNY: return kMsBM;
   }
   return kBM;
 }
@@ -1830,7 +2028,8 @@ static hipError_t make_args(const GemmLaunch& L, GemmArgs& g) {
   g.Nout = L.Nout;
   g.NW = L.swiglu ? 2 * L.Nout : L.Nout;
   g.nt_n = gemm_n_tiles(L.swiglu, L.Nout);
-  if (L.mx != (L.path == GEMM_MX || L.path == GEMM_MX_LARGE)) return hipErrorInvalidValue;
+  if (L.mx != (L.path == GEMM_MX || L.path == GEMM_MX_LARGE || L.path == GEMM_MX_SKINNY))
+    return hipErrorInvalidValue;
   if (L.mx) {  // E4M3 tokens, E2M1 weights, E8M0 bytes per 32 along K; row major
     if (L.fp8 || L.a_panel || L.w_panel || L.c_panel || L.a_index || L.gelu || L.K % kMxK)
       return hipErrorInvalidValue;
@@ -1874,6 +2073,7 @@ hipError_t launch_grouped_gemm(const GemmLaunch& L, hipStream_t s) {
       return L.swiglu ? launch_big<MODE_SWIGLU>(g, L.max_tiles, s)
                       : launch_big<MODE_PLAIN>(g, L.max_tiles, s);
     case GEMM_SKINNY:
+    case GEMM_MX_SKINNY:
       return hipErrorInvalidValue;  // both GEMMs at once: launch_ffn_fused
     case GEMM_MX:
       return L.swiglu ? launch_mx<MODE_SWIGLU_MX8OUT, 128>(g, L.max_tiles, s)
@@ -1902,17 +2102,22 @@ hipError_t launch_grouped_gemm(const GemmLaunch& L, hipStream_t s) {
 
 hipError_t launch_ffn_fused(const GemmLaunch& up, const GemmLaunch& down, int32_t* sync,
                             hipStream_t s) {
-  if (up.path != GEMM_SKINNY || down.path != GEMM_SKINNY || up.fp8 || down.fp8 || !sync ||
-      down.swiglu || down.gelu || up.info != down.info || up.n_tiles != down.n_tiles ||
+  const bool skinny = up.path == GEMM_SKINNY || up.path == GEMM_MX_SKINNY;
+  if (!skinny || down.path != up.path || up.fp8 || down.fp8 || !sync || down.swiglu ||
+      down.gelu || up.info != down.info || up.n_tiles != down.n_tiles ||
       up.max_tiles != down.max_tiles)
     return hipErrorInvalidValue;
   GemmArgs gu, gd;
   hipError_t err = make_args(up, gu);
   if (err == hipSuccess) err = make_args(down, gd);
   if (err != hipSuccess) return err;
-  if (up.gelu) return launch_fused<MODE_GELU>(gu, gd, up.max_tiles, sync, s);
-  if (up.swiglu) return launch_fused<MODE_SWIGLU>(gu, gd, up.max_tiles, sync, s);
-  return launch_fused<MODE_PLAIN>(gu, gd, up.max_tiles, sync, s);
+  if (up.path == GEMM_MX_SKINNY) {  // SwiGLU with MXFP8 h only
+    if (!up.swiglu) return hipErrorInvalidValue;
+    return launch_fused<MODE_SWIGLU_MX8OUT, true>(gu, gd, up.max_tiles, sync, s);
+  }
+  if (up.gelu) return launch_fused<MODE_GELU, false>(gu, gd, up.max_tiles, sync, s);
+  if (up.swiglu) return launch_fused<MODE_SWIGLU, false>(gu, gd, up.max_tiles, sync, s);
+  return launch_fused<MODE_PLAIN, false>(gu, gd, up.max_tiles, sync, s);
 }
 
 }  // namespace moe

@@ -52,6 +52,7 @@ enum GemmPath {
   GEMM_LARGE_FP8 = 3,  // block-FP8: 256 x 256 tiles
   GEMM_MX = 4,         // MXFP4 weights x MXFP8 activations: 128 x 256 tiles
   GEMM_MX_LARGE = 5,   // the same, more than 256 rows per expert: 256 x 256 tiles
+  GEMM_MX_SKINNY = 6,  // the same, up to 32 rows per expert: 32 x 256 tiles (decode)
 };
 GemmPath gemm_path(bool fp8, int64_t rows_per_expert);
 // Token rows of the path's tiles (of its full tiles, for GEMM_LARGE).
@@ -68,7 +69,7 @@ int64_t schedule_entries(int64_t n_pairs, int E_L, GemmPath path, int nt);
 // (contiguous layout, expert e's rows [offsets[e], offsets[e+1])); seg_cap > 0:
 // seg = counts [E_L] (masked layout, rows [e seg_cap, e seg_cap + counts[e])).
 // Builds the work tables on the device (m-tile table: only tab_up / n_up are
-// written).  sync (GEMM_SKINNY only, else null): the fused FFN's ticket and
+// written).  sync (skinny paths only, else null): the fused FFN's ticket and
 // per-m-tile counters, [1 + schedule_entries], cleared here for the launch
 // that follows.
 hipError_t launch_schedule(const int32_t* seg, int seg_cap, int E_L, GemmPath path, int nt_up,
@@ -78,7 +79,7 @@ struct GemmLaunch {
   bool fp8;              // e4m3 operands with block scales, else bf16
   bool mx;               // MXFP4 weights (E2M1, two per byte) x MXFP8 activations,
                          // scales E8M0 bytes per 32 along K (A_scale / W_scale /
-                         // C_scale point to bytes); path GEMM_MX
+                         // C_scale point to bytes); the GEMM_MX* paths
   bool swiglu;           // up GEMM with the SwiGLU epilogue (W = gate and up rows)
   bool gelu;             // up GEMM with the GELU epilogue (bf16); neither: plain
   const void* A;         // [N_cap, K] permuted activations
@@ -105,7 +106,8 @@ struct GemmLaunch {
   const int32_t* a_index;
 };
 hipError_t launch_grouped_gemm(const GemmLaunch& L, hipStream_t s);
-// Both GEMMs of the FFN in one launch (GEMM_SKINNY only): up tiles first, and
+// Both GEMMs of the FFN in one launch (GEMM_SKINNY, or GEMM_MX_SKINNY with the
+// SwiGLU up GEMM): up tiles first, and
 // each down tile starts once every up tile of its rows has published h.
 // `up` and `down` as for two launch_grouped_gemm calls sharing one m-tile
 // table; sync as cleared by launch_schedule.

@@ -126,13 +126,21 @@ struct FfnShape {
   int64_t cap_up, cap_dn;
 };
 
+// GEMM kernel family for a mean of `rows` live rows per expert.
+GemmPath problem_path(const moe_problem* p, int64_t rows) {
+  if (is_mx(p)) return rows > 256 ? GEMM_MX_LARGE : rows > 32 ? GEMM_MX : GEMM_MX_SKINNY;
+  return gemm_path(is_fp8(p), rows);
+}
+
+// Both GEMMs in one launch (the skinny decode kernels).
+bool fused_ffn(GemmPath path) { return path == GEMM_SKINNY || path == GEMM_MX_SKINNY; }
+
 FfnShape ffn_shape(const moe_problem* p) {
   // the kernel family follows the mean live rows per expert, whatever the
   // layout of the buffers
   const int64_t N = n_pairs(p);
   FfnShape f{};
-  f.path = is_mx(p) ? (N / p->num_local > 256 ? GEMM_MX_LARGE : GEMM_MX)
-                    : gemm_path(is_fp8(p), N / p->num_local);
+  f.path = problem_path(p, N / p->num_local);
   f.nt_up = gemm_n_tiles(!is_gelu(p), p->inter);
   f.nt_dn = gemm_n_tiles(false, p->hidden);
   f.cap_up = schedule_entries(N, p->num_local, f.path, f.nt_up);
@@ -146,7 +154,7 @@ FfnScratch carve_ffn(Carve& c, const moe_problem* p) {
   FfnScratch f{};
   f.tab_up = c.take<int4>(sizeof(int4) * sh.cap_up);
   f.n_up = c.take<int32_t>(sizeof(int32_t));
-  if (sh.path == GEMM_SKINNY) f.sync = c.take<int32_t>(sizeof(int32_t) * (1 + sh.cap_up));
+  if (fused_ffn(sh.path)) f.sync = c.take<int32_t>(sizeof(int32_t) * (1 + sh.cap_up));
   if (!gemm_unit_tables(sh.path)) {  // one m-tile table for both GEMMs
     f.tab_dn = f.tab_up;
     f.n_dn = f.n_up;
@@ -305,7 +313,7 @@ moe_status run_ffn(const moe_problem* p, const FfnSource& src, const int32_t* se
   down.c_panel = false;
   down.a_rows = N;
   down.a_index = nullptr;
-  if (sh.path == GEMM_SKINNY) {
+  if (fused_ffn(sh.path)) {
     MOE_TRY(launch_ffn_fused(up, down, f.sync, s));
   } else {
     MOE_TRY(launch_grouped_gemm(up, s));
@@ -637,10 +645,9 @@ static size_t streamed_slice(const moe_problem* p, int32_t max_group_tokens) {
   moe_problem q = *p;
   q.num_tokens = max_group_tokens;
   size_t b = moe_workspace_bytes(&q, MOE_STAGE_LAYER);
-  const bool fp8 = p->dtype != MOE_BF16;
   const int64_t kk = p->top_k < p->num_local ? p->top_k : p->num_local;
   for (int64_t r = 0; r < 4096; ++r) {
-    if (gemm_path(fp8, r) == gemm_path(fp8, r + 1)) continue;
+    if (problem_path(p, r) == problem_path(p, r + 1)) continue;
     // routed experts: rows per expert T kk / E_L; the shared expert: T
     const int64_t cands[2] = {((r + 1) * p->num_local - 1) / kk, r};
     for (const int64_t t : cands) {

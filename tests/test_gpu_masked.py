@@ -72,6 +72,10 @@ CASES = {
     "large_tiles": (small_cfg(T=1300, H=384, E=8, E_L=4, e_lo=2, k=2, I=384), 1300, 24),
     "fp8_shared": (small_cfg(T=150, H=512, E=32, E_L=8, e_lo=8, k=4, I=256, I_s=256,
                              fp8=True), 160, 25),
+    # MXFP4 weights, decode-sized: the fused skinny MX kernel over the blocks
+    "mx_decode": (small_cfg(T=64, H=512, E=64, E_L=16, e_lo=8, k=8, I=384, I_s=128,
+                            mx=True), 64, 26),
+    "mx_pipelined": (small_cfg(T=300, H=256, E=8, E_L=8, k=2, I=384, mx=True), 301, 27),
 }
 
 
@@ -80,16 +84,17 @@ def check_masked(torch, name, cfg, C, d, dev):
     p = ml.Problem.from_config(cfg, capacity=C)
     say("masked layer", name)
     st = run_staged(torch, p, dev)
-    ow = OracleWeights(d, cfg.fp8)
+    quant = cfg.fp8 or cfg.mx
+    ow = OracleWeights(d, cfg.fp8, cfg.mx)
     ref = O.moe_layer(d["logits"], d["x"], ow.as_layer_dict(cfg.E_L), k=cfg.k, e_lo=cfg.e_lo,
-                      E_L=cfg.E_L, fp8=cfg.fp8, quantize_activations=cfg.fp8,
-                      activation=cfg.act, capacity=C)
+                      E_L=cfg.E_L, fp8=cfg.fp8, quantize_activations=quant,
+                      activation=cfg.act, capacity=C, mx=cfg.mx)
 
     def ok(got, want):
         e = rel_rows_all(got, want)
         if e.size == 0:
             return True
-        if not cfg.fp8:
+        if not quant:
             return e.max() <= TOL_BF16
         return e.max() <= TOL_FP8 and np.percentile(e, 99) <= TOL_BF16
 
@@ -99,7 +104,12 @@ def check_masked(torch, name, cfg, C, d, dev):
     np.testing.assert_array_equal(st["tsr"].cpu().numpy(), ref["token_slot_row"])
     used = ref["row_token"] >= 0
     np.testing.assert_array_equal(st["row_token"].cpu().numpy()[used], ref["row_token"][used])
-    if cfg.fp8:
+    if cfg.mx:
+        # only the used rows: the others are never written (any bytes)
+        h = O.mx_dequantize(st["h"].cpu().numpy()[used], st["h_scale"].cpu().numpy()[used],
+                            "e4m3")
+        assert ok(h, O.mx8_activation(ref["h"][used]))
+    elif cfg.fp8:
         h = (O.e4m3_value(st["h"].cpu().numpy()[used]) *
              np.repeat(st["h_scale"].cpu().numpy()[used].astype(np.float64), 128, axis=1))
         assert ok(h, O.fp8_activation(ref["h"][used]))
@@ -112,7 +122,7 @@ def check_masked(torch, name, cfg, C, d, dev):
     np.testing.assert_array_equal(dv.bits_from_bf16(y), dv.bits_from_bf16(st["y"]))
     yc = run_layer(torch, dataclasses.replace(p, capacity=0), dev)
     np.testing.assert_array_equal(dv.bits_from_bf16(yc), dv.bits_from_bf16(st["y"]))
-    if not cfg.fp8:
+    if not quant:
         say("masked gather path", name)
         if cfg.I_s == 0:
             yg = run_gather_path(torch, p, dev)
@@ -133,7 +143,7 @@ def test_masked_layer(name):
     ml, dv = _mods()
     cfg, C, seed = CASES[name]
     d = synth.make_inputs(cfg, seed, x_std=1.0, std=0.05)
-    dev = dv.upload(d, cfg.fp8)
+    dev = dv.upload(d, cfg.fp8, mx=cfg.mx)
     check_masked(torch, name, cfg, C, d, dev)
 
 

@@ -87,6 +87,10 @@ SMALL_MX = {
     "mx_shared": (small_cfg(T=150, H=1024, E=64, E_L=16, e_lo=16, k=8, I=512, I_s=256,
                             mx=True), 43),
     "mx_decode": (small_cfg(T=16, H=1024, E=64, E_L=16, e_lo=0, k=8, I=256, mx=True), 44),
+    # up to 32 rows per expert on average: the fused skinny MX kernel, some
+    # experts over 32 rows (two m-tiles), the shared expert on 128-row tiles
+    "mx_skinny_tiles": (small_cfg(T=100, H=512, E=16, E_L=8, e_lo=4, k=4, I=384, I_s=128,
+                                  mx=True), 46),
     # more than 256 rows per expert: the 256-row MX tiles, ragged segment ends
     "mx_large_tiles": (small_cfg(T=1300, H=384, E=8, E_L=4, e_lo=2, k=2, I=640, I_s=256,
                                  mx=True), 45),
@@ -134,23 +138,27 @@ def test_mx_gate_at_workload_spread(name):
     assert e <= TOL_MX
 
 
-def test_mx_dsv3_shard_full_size_sampled():
+@pytest.mark.parametrize("workload,n_sample", [("dsv3_ep8_prefill_mxfp4", 30),
+                                                ("dsv3_ep8_decode_mxfp4", 14)])
+def test_mx_dsv3_shard_full_size_sampled(workload, n_sample):
     """The DeepSeek-V3 EP8 shard with MXFP4 weights and its shared expert at
-    full size: sampled rows (segment edges and random tokens) against the
+    full size (prefill batch: 128- and 256-row tiles; decode batch: the fused
+    skinny kernel): sampled rows (first, last and random tokens) against the
     oracle with the same activation quantisation."""
     torch = torch_cuda()
     ml, dv = _mods()
-    cfg = synth.config("dsv3_ep8_prefill_mxfp4")
+    cfg = synth.config(workload)
     d = synth.make_inputs(cfg, 2)
     dev = dv.upload(d, False, mx=True)
     p = ml.Problem.from_config(cfg)
-    say("mx dsv3 shard full size")
+    say("mx dsv3 shard full size", workload)
     y = run_layer(torch, p, dev)
     rng = np.random.default_rng(8)
-    toks = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, 30, replace=False)]))
+    toks = np.unique(np.concatenate([[0, cfg.T - 1],
+                                     rng.choice(cfg.T, n_sample, replace=False)]))
     ow = OracleWeights(d, False, mx=True)
     ref = O.moe_layer_tokens(d["logits"], d["x"], ow.as_layer_dict(cfg.E_L), toks, k=cfg.k,
                              e_lo=cfg.e_lo, E_L=cfg.E_L, mx=True, quantize_activations=True)
     e = rel_rows(y[toks].float().cpu().numpy().astype(np.float64), ref)
-    print(f"mx dsv3 sampled rows: {e:.2e}")
+    print(f"mx {workload} sampled rows: {e:.2e}")
     assert e <= TOL_FP8

@@ -40,9 +40,10 @@ def parse():
     ap.add_argument("--cpu-sample-tokens", type=int, default=None,
                     help="tokens of the workload the CPU oracle runs on (0 = skip)")
     ap.add_argument("--layout", choices=("panel", "rows"), default="panel",
-                    help="bf16 storage: panel = weights packed once at load time and panel "
-                         "activations in the staged calls (moe_layer always keeps its own "
-                         "activations in panel layout); rows = everything row major")
+                    help="panel = weights packed once at load time (bf16 and MXFP4) and, "
+                         "bf16, panel activations in the staged calls (moe_layer always keeps "
+                         "its own bf16 activations in panel layout); rows = everything row "
+                         "major.  Block-FP8 is always row major")
     ap.add_argument("--masked", action="store_true",
                     help="masked fixed-capacity expert layout (capacity = tokens) instead of "
                          "contiguous segments")
@@ -128,13 +129,14 @@ def main():
     torch.cuda.set_device(dev_id)
     d = synth.make_inputs(cfg, seed)
     quant = cfg.fp8 or cfg.mx          # quantised GEMM activations with per-row scales
-    panel = args.layout == "panel" and not quant
+    panel = args.layout == "panel" and not cfg.fp8   # bf16 and MXFP4 weights
     dev = dv.upload(d, cfg.fp8, panel=panel, mx=cfg.mx)   # load-time conversion, untimed
-    # Layouts of moe_layer's own path: panel weights as loaded, panel h.
+    # Layouts of moe_layer's own path: panel weights as loaded, panel h (bf16;
+    # MXFP4 activations stay row major).
     cap = cfg.T if args.masked else 0
+    wlay = ml.LAYOUT_PANEL_WEIGHTS if panel else 0
     p = ml.Problem.from_config(
-        cfg, layout=(ml.LAYOUT_PANEL_WEIGHTS | ml.LAYOUT_PANEL_ACTS) if panel else 0,
-        capacity=cap)
+        cfg, layout=wlay | (ml.LAYOUT_PANEL_ACTS if panel and not quant else 0), capacity=cap)
     p_layer = ml.Problem.from_config(cfg, layout=ml.LAYOUT_PANEL_WEIGHTS if panel else 0,
                                      capacity=cap)
     W = dv.weights_of(dev, quant)
@@ -157,7 +159,8 @@ def main():
         xp = torch.empty((N, H), dtype=torch.uint8, device="cuda")
         xs = torch.empty((N, H // g), **sc)
         if p.I_s:
-            q = ml.Problem(T=T, H=H, E=1, k=1, e_lo=0, E_L=1, I=p.I_s, fp8=cfg.fp8, mx=cfg.mx)
+            q = ml.Problem(T=T, H=H, E=1, k=1, e_lo=0, E_L=1, I=p.I_s, fp8=cfg.fp8, mx=cfg.mx,
+                           layout=wlay)
             off2 = torch.tensor([0, T], **i32)
             sw = ml.weights_struct(dev["ws13_q"], dev["ws2_q"], None, None, dev["ws13_s"],
                                    dev["ws2_s"])

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 6
+#define MOE_ABI_VERSION 7
 
 typedef enum {
   MOE_OK = 0,
@@ -82,8 +82,9 @@ typedef enum {
 #define MOE_MX_E2M1 0
 #define MOE_MX_E4M3 1
 
-/* Storage layouts (moe_problem.layout bits; bf16 problems only, values are
- * never changed by a layout).  The panel layout of an [R, K] bf16 matrix
+/* Storage layouts (moe_problem.layout bits; values are never changed by a
+ * layout).  bf16: both bits; MOE_MXFP4: MOE_LAYOUT_PANEL_WEIGHTS only;
+ * MOE_FP8_E4M3: none.  The panel layout of an [R, K] bf16 matrix
  * cuts its columns into panels of 32 consecutive elements (64 bytes) and
  * stores the panels one after another, each as an [R, 32] row-major block:
  *   element (r, c) lives at index ((c / 32) * R + r) * 32 + c % 32.
@@ -96,7 +97,13 @@ typedef enum {
  *   MOE_LAYOUT_PANEL_ACTS: x_perm [N_cap, H] written by moe_dispatch and read
  *     by moe_grouped_ffn, and h [N_cap, I], are in panel layout with
  *     R = N_cap.  moe_layer keeps its own x_perm and h in panel layout
- *     whatever this bit says.                                               */
+ *     whatever this bit says.
+ * MXFP4 panel weights: each matrix's E2M1 codes [R, K/2 bytes] are cut into
+ * 64-byte (128-element) panels, [K/128, R, 64 bytes], and its E8M0 scales
+ * [R, K/32] into 4-byte pieces, [K/128, R, 4 bytes]: byte j of row r's codes
+ * lives at ((j / 64) * R + r) * 64 + j % 64, scale byte j at
+ * ((j / 4) * R + r) * 4 + j % 4.  A decode-sized GEMM step then reads each
+ * operand tile's weights as one contiguous run.  See moe_pack_panel_mx.     */
 #define MOE_LAYOUT_PANEL_WEIGHTS 1
 #define MOE_LAYOUT_PANEL_ACTS 2
 
@@ -314,6 +321,18 @@ moe_status moe_quantize_mx(const void* src, int64_t batch, int64_t rows,
  * time, like moe_quantize_fp8: the weights are packed once.               */
 moe_status moe_pack_panel(const void* src, int64_t batch, int64_t rows,
                           int64_t cols, void* dst, void* stream);
+
+/* Panel packing of MXFP4 weights (see MOE_LAYOUT_PANEL_WEIGHTS): for each of
+ * `batch` matrices of `rows` rows and K = cols elements, as moe_quantize_mx
+ * writes them -- codes [rows, cols/2] bytes, scales [rows, cols/32] E8M0
+ * bytes -- codes_dst receives the codes as [cols/128, rows, 64 bytes] and
+ * scales_dst the scales as [cols/128, rows, 4 bytes].  cols % 128 == 0,
+ * 128 <= cols <= 2^20, batch * rows * cols < 2^40; no two of the four
+ * buffers may overlap; all 16-byte aligned.  Load time, like
+ * moe_quantize_mx.  MOE_OK, or MOE_ERR_INVALID_ARG (nothing launched).     */
+moe_status moe_pack_panel_mx(const void* codes, const void* scales, int64_t batch,
+                             int64_t rows, int64_t cols, void* codes_dst,
+                             void* scales_dst, void* stream);
 
 /* Streaming FFN, host side (page "CascadeEP ...", section 3.2 "Launch
  * threshold" and Appendix C: ready work accumulates, an invocation is launched

@@ -294,6 +294,23 @@ __global__ __launch_bounds__(256) void pack_panel_kernel(const uint4* __restrict
   }
 }
 
+// Panel packing of MX weight scales, [batch][rows][cols/128] dwords (four
+// E8M0 bytes: one 128-element K step of a row) -> [batch][cols/128][rows].
+// Threads walk the destination in order, so writes are contiguous.
+__global__ __launch_bounds__(256) void pack_scales_mx_kernel(const uint32_t* __restrict__ src,
+                                                             int64_t batch, int64_t rows,
+                                                             int64_t steps,
+                                                             uint32_t* __restrict__ dst) {
+  const int64_t per_mat = rows * steps;
+  const int64_t total = batch * per_mat;
+  for (int64_t u = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; u < total;
+       u += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t b = u / per_mat, v = u - b * per_mat;
+    const int64_t k = v / rows, r = v - k * rows;
+    dst[u] = src[b * per_mat + r * steps + k];
+  }
+}
+
 // Row gather with per-128 group E4M3 quantisation: scale = amax/448 (1 for an
 // all-zero group), code = RNE(v / scale) (IEEE fp32 division) saturated.
 // A group of 128 bf16 is 16 lanes x 8 values; a wave covers 4 groups per step.
@@ -556,6 +573,17 @@ hipError_t launch_pack_panel(const void* src, int64_t batch, int64_t rows, int64
   hipLaunchKernelGGL(pack_panel_kernel, dim3(static_cast<unsigned>(blocks < 16384 ? blocks : 16384)),
                      dim3(256), 0, s, static_cast<const uint4*>(src), batch, rows, cols,
                      static_cast<uint4*>(dst));
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_scales_mx(const void* src, int64_t batch, int64_t rows, int64_t cols,
+                                 void* dst, hipStream_t s) {
+  const int64_t units = batch * rows * (cols / 128);
+  const int64_t blocks = (units + 255) / 256;
+  hipLaunchKernelGGL(pack_scales_mx_kernel,
+                     dim3(static_cast<unsigned>(blocks < 16384 ? blocks : 16384)), dim3(256), 0, s,
+                     static_cast<const uint32_t*>(src), batch, rows, cols / 128,
+                     static_cast<uint32_t*>(dst));
   return hipGetLastError();
 }
 

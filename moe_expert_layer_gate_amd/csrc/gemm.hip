@@ -80,12 +80,15 @@ struct GemmArgs {
   const int32_t* n_tiles;  // live m-tiles
   int K, Nout, NW, nt_n;   // NW = 2 Nout (SwiGLU) or Nout; nt_n n-tiles per expert
   int64_t w_stride;        // bytes per expert of W
-  int64_t ws_stride;       // floats per expert of W_scale
+  int64_t ws_stride;       // floats (MX: bytes) per expert of W_scale
   // Operand addressing: byte (row, c) of A or W is at row * rs + (c / 64) * cs
   // + c % 64 -- row major: rs = row bytes, cs = 64; panel layout: rs = 64,
   // cs = 64 * rows of the matrix.
   int a_rs, w_rs;
   int a_cs, w_cs;          // (a buffer's whole span stays below 2 GiB, see the host)
+  // MX weight scales: byte (row, 4-byte piece p) at row * ws_rs + p * ws_cs --
+  // row major: ws_rs = K / 32, ws_cs = 4; panel: ws_rs = 4, ws_cs = 4 NW.
+  int ws_rs, ws_cs;
   int64_t a_bytes;         // size of the A buffer
   int64_t c_cs;            // SwiGLU bf16 output: 0 = row major, else panel stride
   const int32_t* a_index;  // fused gather: GEMM row j reads A row a_index[j]
@@ -796,12 +799,12 @@ __device__ __forceinline__ void mx_tile(const GemmArgs& g, uint8_t* smem) {
   for (int q = 0; q < WL; ++q) {
     const int r = (w * WL + q) * 16 + (lane >> 2);
     const int cw = (lane & 3) ^ ((r >> 2) & 3);
-    voff[TL + q] = wrow(r) * (K / 2) + cw * 16;
+    voff[TL + q] = wrow(r) * g.w_rs + cw * 16;
   }
   bool s_tok;      // 256 rows: this wave's scale load is a token-scale one
   int s_lds;
   if constexpr (kMxBM == 128) {
-    voff[TL + WL] = wrow(w * 64 + lane) * kb;
+    voff[TL + WL] = wrow(w * 64 + lane) * g.ws_rs;
     const int rr = (w & 1) * 64 + lane;
     voff[TL + WL + 1] = row0 + rr < seg_end ? rr * kb : kOobOffset;
     s_tok = false;
@@ -813,7 +816,7 @@ __device__ __forceinline__ void mx_tile(const GemmArgs& g, uint8_t* smem) {
       voff[TL + WL] = row0 + rr < seg_end ? rr * kb : kOobOffset;
       s_lds = kMxSAOff + w * 256;
     } else {
-      voff[TL + WL] = wrow((w - 4) * 64 + lane) * kb;
+      voff[TL + WL] = wrow((w - 4) * 64 + lane) * g.ws_rs;
       s_lds = kMxSWOff + (w - 4) * 256;
     }
   }
@@ -829,17 +832,19 @@ __device__ __forceinline__ void mx_tile(const GemmArgs& g, uint8_t* smem) {
 #pragma unroll
     for (int q = 0; q < WL; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, (lds_ptr_t)(base + kMxWOff + (w * WL + q) * 1024),
-                                               16, live ? voff[TL + q] : kOobOffset,
-                                               k * (kMxK / 2), 0, 0);
+                                               16, live ? voff[TL + q] : kOobOffset, k * g.w_cs, 0,
+                                               0);
     if constexpr (kMxBM == 128) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rWS, (lds_ptr_t)(base + kMxSWOff + w * 256), 4,
-                                               live ? voff[TL + WL] : kOobOffset, k * 4, 0, 0);
+                                               live ? voff[TL + WL] : kOobOffset, k * g.ws_cs, 0,
+                                               0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rAS, (lds_ptr_t)(base + kMxSAOff + (w & 1) * 256),
                                                4, live ? voff[TL + WL + 1] : kOobOffset, k * 4, 0,
                                                0);
     } else {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(s_tok ? rAS : rWS, (lds_ptr_t)(base + s_lds), 4,
-                                               live ? voff[TL + WL] : kOobOffset, k * 4, 0, 0);
+                                               live ? voff[TL + WL] : kOobOffset,
+                                               k * (s_tok ? 4 : g.ws_cs), 0, 0);
     }
   };
 
@@ -1054,9 +1059,9 @@ __device__ __forceinline__ void mx_skinny_tile(const GemmArgs& g, int t, uint8_t
   for (int q = 0; q < 4; ++q) {
     const int r = (w * 4 + q) * 16 + (lane >> 2);
     const int cw = (lane & 3) ^ ((r >> 2) & 3);
-    voff[1 + q] = wrow(r) * (K / 2) + cw * 16;
+    voff[1 + q] = wrow(r) * g.w_rs + cw * 16;
   }
-  voff[5] = wrow(w * 64 + lane) * kb;
+  voff[5] = wrow(w * 64 + lane) * g.ws_rs;
   voff[6] = lane < kMsBM && row0 + lane < seg_end ? lane * kb : kOobOffset;
   auto dma = [&](int step, int stage) {
     // steps past the last one load nothing (out-of-range offsets)
@@ -1068,10 +1073,10 @@ __device__ __forceinline__ void mx_skinny_tile(const GemmArgs& g, int t, uint8_t
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, (lds_ptr_t)(base + kMsWOff + (w * 4 + q) * 1024),
-                                               16, live ? voff[1 + q] : kOobOffset,
-                                               k * (kMxK / 2), 0, 0);
+                                               16, live ? voff[1 + q] : kOobOffset, k * g.w_cs,
+                                               0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rWS, (lds_ptr_t)(base + kMsWSOff + w * 256), 4,
-                                             live ? voff[5] : kOobOffset, k * 4, 0, 0);
+                                             live ? voff[5] : kOobOffset, k * g.ws_cs, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rAS, (lds_ptr_t)(base + kMsTSOff), 4,
                                              live ? voff[6] : kOobOffset, k * 4, 0, 0);
   };
@@ -2030,16 +2035,19 @@ static hipError_t make_args(const GemmLaunch& L, GemmArgs& g) {
   g.nt_n = gemm_n_tiles(L.swiglu, L.Nout);
   if (L.mx != (L.path == GEMM_MX || L.path == GEMM_MX_LARGE || L.path == GEMM_MX_SKINNY))
     return hipErrorInvalidValue;
-  if (L.mx) {  // E4M3 tokens, E2M1 weights, E8M0 bytes per 32 along K; row major
-    if (L.fp8 || L.a_panel || L.w_panel || L.c_panel || L.a_index || L.gelu || L.K % kMxK)
+  if (L.mx) {  // E4M3 tokens, E2M1 weights, E8M0 bytes per 32 along K; tokens row
+               // major, weights row major or in 128-element panels
+    if (L.fp8 || L.a_panel || L.c_panel || L.a_index || L.gelu || L.K % kMxK)
       return hipErrorInvalidValue;
     if (L.swiglu && !L.C_scale) return hipErrorInvalidValue;
     g.w_stride = static_cast<int64_t>(g.NW) * (L.K / 2);
     g.ws_stride = static_cast<int64_t>(g.NW) * (L.K / 32);
     g.a_rs = L.K;
     g.a_cs = 64;
-    g.w_rs = L.K / 2;
-    g.w_cs = 64;
+    g.w_rs = L.w_panel ? 64 : L.K / 2;
+    g.w_cs = L.w_panel ? 64 * g.NW : 64;
+    g.ws_rs = L.w_panel ? 4 : L.K / 32;
+    g.ws_cs = L.w_panel ? 4 * g.NW : 4;
     g.a_bytes = L.a_rows * L.K;
     return hipSuccess;
   }

@@ -29,6 +29,10 @@ hipError_t launch_gather_bf16(const void* src, const int32_t* rows, const int32_
 // bf16 [batch][rows][cols] row major -> [batch][cols/32][rows][32].
 hipError_t launch_pack_panel(const void* src, int64_t batch, int64_t rows, int64_t cols,
                              void* dst, hipStream_t s);
+// MX weight scales [batch][rows][cols/32] bytes -> [batch][cols/128][rows][4]
+// (cols % 128 == 0).
+hipError_t launch_pack_scales_mx(const void* src, int64_t batch, int64_t rows, int64_t cols,
+                                 void* dst, hipStream_t s);
 hipError_t launch_gather_fp8(const void* src, const int32_t* rows, const int32_t* n_rows,
                              int64_t max_rows, int H, void* dst, float* dst_scale, hipStream_t s,
                              const int32_t* counts = nullptr, int cap = 0);

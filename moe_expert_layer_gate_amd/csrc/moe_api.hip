@@ -36,7 +36,9 @@ moe_status check_problem(const moe_problem* p) {
   if (p->dtype != MOE_BF16 && p->dtype != MOE_FP8_E4M3 && p->dtype != MOE_MXFP4)
     return MOE_ERR_INVALID_ARG;
   if (p->layout & ~(MOE_LAYOUT_PANEL_WEIGHTS | MOE_LAYOUT_PANEL_ACTS)) return MOE_ERR_INVALID_ARG;
-  if (p->layout && p->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  // block-FP8: row major only; MXFP4: panel weights, row-major activations
+  if (p->layout && p->dtype == MOE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;
+  if ((p->layout & MOE_LAYOUT_PANEL_ACTS) && p->dtype == MOE_MXFP4) return MOE_ERR_UNSUPPORTED;
   if (p->activation != MOE_ACT_SWIGLU && p->activation != MOE_ACT_GELU) return MOE_ERR_INVALID_ARG;
   if (p->activation == MOE_ACT_GELU && p->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   // One expert's weight matrix must stay below 2 GiB (32-bit buffer offsets).
@@ -596,6 +598,31 @@ moe_status moe_pack_panel(const void* src, int64_t batch, int64_t rows, int64_t 
   if (bytes > 0 && a < b + bytes && b < a + bytes) return MOE_ERR_INVALID_ARG;
   if (batch == 0 || rows == 0) return MOE_OK;
   return hip_status(launch_pack_panel(src, batch, rows, cols, dst, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_pack_panel_mx(const void* codes, const void* scales, int64_t batch, int64_t rows,
+                             int64_t cols, void* codes_dst, void* scales_dst, void* stream) {
+  const void* ptrs[] = {codes, scales, codes_dst, scales_dst};
+  for (const void* q : ptrs)
+    if (!q || !aligned16(q)) return MOE_ERR_INVALID_ARG;
+  if (batch < 0 || rows < 0 || cols < 128 || cols % 128 || cols > (1 << 20))
+    return MOE_ERR_INVALID_ARG;
+  if (rows > 0 && batch > ((int64_t(1) << 40) / cols) / rows) return MOE_ERR_INVALID_ARG;
+  const int64_t cb = batch * rows * (cols / 2), sb = batch * rows * (cols / 32);
+  auto overlap = [](const void* x, int64_t nx, const void* y, int64_t ny) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(x), b = reinterpret_cast<uintptr_t>(y);
+    return nx > 0 && ny > 0 && a < b + ny && b < a + nx;
+  };
+  if (overlap(codes, cb, codes_dst, cb) || overlap(codes, cb, scales_dst, sb) ||
+      overlap(scales, sb, codes_dst, cb) || overlap(scales, sb, scales_dst, sb) ||
+      overlap(codes_dst, cb, scales_dst, sb))
+    return MOE_ERR_INVALID_ARG;
+  if (batch == 0 || rows == 0) return MOE_OK;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  // the code bytes of a row are cols / 4 two-byte units: bf16 panels of 32
+  // units are the 64-byte (128-element) MX panels
+  MOE_TRY(launch_pack_panel(codes, batch, rows, cols / 4, codes_dst, s));
+  return hip_status(launch_pack_scales_mx(scales, batch, rows, cols, scales_dst, s));
 }
 
 // ---------------------------------------------------------------------------

@@ -67,12 +67,24 @@ def pack_panel(w: torch.Tensor) -> torch.Tensor:
     return out
 
 
+def pack_panel_mx(codes: torch.Tensor, scales: torch.Tensor):
+    """MXFP4 codes [B, R, C/2] and scales [B, R, C/32] (or without B) -> the
+    MX panel layout ([B, C/128, R, 64] and [B, C/128, R, 4] bytes), made by
+    moe_pack_panel_mx; returned with the inputs' shapes."""
+    c3 = codes.unsqueeze(0) if codes.dim() == 2 else codes
+    s3 = scales.unsqueeze(0) if scales.dim() == 2 else scales
+    B, R, half = c3.shape
+    oc, os_ = torch.empty_like(codes), torch.empty_like(scales)
+    ml.moe_pack_panel_mx(c3.contiguous(), s3.contiguous(), B, R, 2 * half, oc, os_)
+    return oc, os_
+
+
 def upload(d: Dict[str, np.ndarray], fp8: bool, keep_bf16: bool = False,
            panel: bool = False, mx: bool = False) -> Dict[str, torch.Tensor]:
     """Move a make_inputs() batch to the GPU.  With fp8, the weights are
     converted to E4M3 + 128x128 block scales on the device (load-time
     conversion) and the bf16 copies are dropped unless keep_bf16.  With
-    panel (bf16 only), the weights are repacked into panel layout at load
+    panel (bf16 or mx), the weights are repacked into panel layout at load
     time (use the problem's LAYOUT_PANEL_WEIGHTS bit with them).  With mx,
     the weights become MXFP4 (E2M1 codes and E8M0 scales, load-time
     conversion by the library)."""
@@ -85,6 +97,9 @@ def upload(d: Dict[str, np.ndarray], fp8: bool, keep_bf16: bool = False,
         wb = bf16_from_bits(d[name])
         if mx:
             out[name + "_q"], out[name + "_s"] = quantize_mx4(wb)
+            if panel:
+                out[name + "_q"], out[name + "_s"] = pack_panel_mx(out[name + "_q"],
+                                                                   out[name + "_s"])
             if keep_bf16:
                 out[name] = wb
             else:

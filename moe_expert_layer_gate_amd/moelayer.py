@@ -51,6 +51,7 @@ SIGNATURES = {
     "moe_layer": (_i32, [_P, _vp, _vp, _W, _vp, _vp, _sz, _vp]),
     "moe_quantize_fp8": (_i32, [_vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp]),
     "moe_pack_panel": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp]),
+    "moe_pack_panel_mx": (_i32, [_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),
     "moe_quantize_mx": (_i32, [_vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp]),
     "moe_workspace_bytes": (_sz, [_P, _i32]),
     "moe_stream_threshold": (_i64, [_vp, _vp, _i32, ctypes.c_double]),
@@ -233,6 +234,13 @@ def moe_quantize_fp8(src, batch: int, rows: int, cols: int, block_rows: int, cod
 def moe_pack_panel(src, batch: int, rows: int, cols: int, dst, stream=None) -> None:
     _check("moe_pack_panel", lib().moe_pack_panel(
         _ptr(src), batch, rows, cols, _ptr(dst), _stream(stream)))
+
+
+def moe_pack_panel_mx(codes, scales, batch: int, rows: int, cols: int, codes_dst, scales_dst,
+                      stream=None) -> None:
+    _check("moe_pack_panel_mx", lib().moe_pack_panel_mx(
+        _ptr(codes), _ptr(scales), batch, rows, cols, _ptr(codes_dst), _ptr(scales_dst),
+        _stream(stream)))
 
 
 def stream_threshold(counts, throughput, rho: float) -> int:

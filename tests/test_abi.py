@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert ml.lib().moe_abi_version() == 6
+    assert ml.lib().moe_abi_version() == 7
     assert ml.status_str(0) == "MOE_OK"
     assert ml.status_str(3) == "MOE_ERR_WORKSPACE"
     assert ml.status_str(99) == "MOE_ERR_UNKNOWN"
@@ -124,7 +124,7 @@ def test_quantize_argument_checks():
 
 def test_layout_checks():
     L = ml.lib()
-    # panel layouts are bf16-only
+    # no panel layouts for block-FP8
     pf = ml.Problem(T=16, H=256, E=8, k=2, e_lo=0, E_L=8, I=256, fp8=True,
                     layout=ml.LAYOUT_PANEL_WEIGHTS)
     assert ml.workspace_bytes(pf) == 0
@@ -219,12 +219,16 @@ def test_capacity_checks():
 
 
 def test_mxfp4_checks():
-    """MXFP4: row-major layouts and the gated MLP only; scale pointers are
-    required like block-FP8's; moe_quantize_mx argument checks."""
+    """MXFP4: panel weights but row-major activations, and the gated MLP
+    only; scale pointers are required like block-FP8's; moe_quantize_mx and
+    moe_pack_panel_mx argument checks."""
     L = ml.lib()
     base = dict(T=16, H=256, E=8, k=2, e_lo=0, E_L=8, I=256, mx=True)
     assert ml.workspace_bytes(ml.Problem(**base)) > 0
-    for bad, want in ((dict(layout=ml.LAYOUT_PANEL_WEIGHTS), ml.MOE_ERR_UNSUPPORTED),
+    assert ml.workspace_bytes(ml.Problem(**base, layout=ml.LAYOUT_PANEL_WEIGHTS)) == \
+        ml.workspace_bytes(ml.Problem(**base))
+    for bad, want in ((dict(layout=ml.LAYOUT_PANEL_ACTS), ml.MOE_ERR_UNSUPPORTED),
+                      (dict(layout=3), ml.MOE_ERR_UNSUPPORTED),
                       (dict(act="gelu"), ml.MOE_ERR_UNSUPPORTED)):
         pc = ml.Problem(**base, **bad).c()
         assert L.moe_route(ctypes.byref(pc), 16, 16, 16, None) == want
@@ -248,3 +252,15 @@ def test_mxfp4_checks():
     assert L.moe_quantize_mx(256, 1, 4, 64, 1, 256, 256, None) == ml.MOE_ERR_INVALID_ARG   # e4m3: cols % 128
     assert L.moe_quantize_mx(None, 1, 4, 64, 0, 256, 256, None) == ml.MOE_ERR_INVALID_ARG
     assert L.moe_quantize_mx(256, 0, 4, 64, 0, 256, 256, None) == ml.MOE_OK
+    # moe_pack_panel_mx: cols % 128, alignment, disjoint buffers
+    a, b, c, d = 1 << 20, 2 << 20, 3 << 20, 4 << 20
+    assert L.moe_pack_panel_mx(a, b, 1, 4, 64, c, d, None) == ml.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_panel_mx(a, b, 1, 4, 192, c, d, None) == ml.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_panel_mx(a, b, 1, 4, 1 << 21, c, d, None) == ml.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_panel_mx(a + 8, b, 1, 4, 128, c, d, None) == ml.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_panel_mx(None, b, 1, 4, 128, c, d, None) == ml.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_panel_mx(a, b, 1, 4, 128, a + 128, d, None) == ml.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_panel_mx(a, b, 1, 4, 128, c, c + 16, None) == ml.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_panel_mx(a, b, -1, 4, 128, c, d, None) == ml.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_panel_mx(a, b, 0, 4, 128, c, d, None) == ml.MOE_OK
+    assert L.moe_pack_panel_mx(a, b, 3, 0, 128, c, d, None) == ml.MOE_OK

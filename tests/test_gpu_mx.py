@@ -107,6 +107,42 @@ def test_mx_layer_small(name):
     check_small_case(name, cfg, d, dev)
 
 
+@pytest.mark.parametrize("B,R,C", [(1, 5, 128), (3, 96, 640), (2, 300, 7168)])
+def test_mx_pack_panel_bit_exact(B, R, C):
+    """moe_pack_panel_mx against the layout's definition: codes [R, C/2] bytes
+    -> [C/128, R, 64], scales [R, C/32] -> [C/128, R, 4] (numpy reshapes)."""
+    torch = torch_cuda()
+    ml, dv = _mods()
+    rng = np.random.default_rng(B * R + C)
+    codes = rng.integers(0, 256, size=(B, R, C // 2), dtype=np.uint8)
+    scales = rng.integers(0, 256, size=(B, R, C // 32), dtype=np.uint8)
+    say("mx pack panel", B, R, C)
+    pc, ps = dv.pack_panel_mx(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda())
+    torch.cuda.synchronize()
+    want_c = codes.reshape(B, R, C // 128, 64).transpose(0, 2, 1, 3).reshape(B, R, C // 2)
+    want_s = scales.reshape(B, R, C // 128, 4).transpose(0, 2, 1, 3).reshape(B, R, C // 32)
+    np.testing.assert_array_equal(pc.cpu().numpy(), want_c)
+    np.testing.assert_array_equal(ps.cpu().numpy(), want_s)
+
+
+@pytest.mark.parametrize("name", ["mx_small", "mx_shared", "mx_decode", "mx_skinny_tiles",
+                                  "mx_large_tiles"])
+def test_mx_panel_weights_bit_identical(name):
+    """MXFP4 weights in panel layout (LAYOUT_PANEL_WEIGHTS): every kernel
+    family reads the same values in the same order, so the output is the
+    row-major layout's, bit for bit."""
+    torch = torch_cuda()
+    ml, dv = _mods()
+    cfg, seed = SMALL_MX[name]
+    d = synth.make_inputs(cfg, seed, x_std=1.0, std=0.05)
+    p = ml.Problem.from_config(cfg)
+    say("mx panel weights", name)
+    y = run_layer(torch, p, dv.upload(d, False, mx=True))
+    pp = ml.Problem.from_config(cfg, layout=ml.LAYOUT_PANEL_WEIGHTS)
+    yp = run_layer(torch, pp, dv.upload(d, False, mx=True, panel=True), guard=2)
+    np.testing.assert_array_equal(dv.bits_from_bf16(yp), dv.bits_from_bf16(y))
+
+
 # Output gate of the MX path against the exact-activation oracle (the MXFP4
 # weights are the parameters, so the error is that of packing x and h as
 # MXFP8): E4M3 rounding is within 1/16 of each element, and the MX scale, a

@@ -39,6 +39,7 @@
 // Block-FP8 operands: one K step is one 128-wide scale block; its products go
 // to a zeroed temporary that is added to the accumulator times
 // (weight block scale x token group scale).
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -194,6 +195,22 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Raises a kernel's dynamic-LDS limit to `bytes` once per device (the
+// attribute belongs to the current device; `set` records the devices done).
+// A failure is left to the launch to report.
+inline void allow_dynamic_lds(const void* kern, int bytes, std::atomic<uint64_t>& set) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return;
+  }
+  const uint64_t bit = uint64_t(1) << dev;
+  if (set.load(std::memory_order_acquire) & bit) return;
+  if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess)
+    (void)hipGetLastError();
+  set.fetch_or(bit, std::memory_order_acq_rel);
+}
 
 template <bool FP8, int MODE>
 __global__ __launch_bounds__(kThreads, 1) void gemm_pipelined_kernel(const GemmArgs g) {
@@ -538,14 +555,8 @@ hipError_t launch_pipelined(const GemmArgs& g, int64_t max_tiles, hipStream_t s)
   static_assert(kStages * kStageBytes + 2 * kBM * 4 <= 160 * 1024, "the ring fits the CU's LDS");
   auto kern = gemm_pipelined_kernel<FP8, MODE>;
   const size_t lds = kStages * kStageBytes;
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                            static_cast<int>(lds)) != hipSuccess)
-      (void)hipGetLastError();
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  allow_dynamic_lds(reinterpret_cast<const void*>(kern), static_cast<int>(lds), lds_set);
   const int64_t blocks = (max_tiles * g.nt_n + kXcds - 1) / kXcds * kXcds + kXcds;
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), lds, s, g);
   return hipGetLastError();
@@ -985,14 +996,8 @@ hipError_t launch_mx(const GemmArgs& g, int64_t max_tiles, hipStream_t s) {
   using SH = MxShape<BM>;
   auto kern = gemm_mx_kernel<MODE, BM>;
   const size_t lds = SH::STAGES * SH::STAGE_BYTES;
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                            static_cast<int>(lds)) != hipSuccess)
-      (void)hipGetLastError();
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  allow_dynamic_lds(reinterpret_cast<const void*>(kern), static_cast<int>(lds), lds_set);
   const int64_t blocks = (max_tiles * g.nt_n + kXcds - 1) / kXcds * kXcds + kXcds;
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(SH::THREADS), lds, s, g);
   return hipGetLastError();
@@ -1264,14 +1269,8 @@ hipError_t launch_fused(const GemmArgs& gu, const GemmArgs& gd, int64_t max_tile
   static_assert(kSkStages * kSkStageBytes <= 160 * 1024, "the ring fits the CU's LDS");
   auto kern = ffn_fused_skinny_kernel<UPMODE, MX>;
   const size_t lds = MX ? kMsStages * kMsStageBytes : kSkStages * kSkStageBytes;
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                            static_cast<int>(lds)) != hipSuccess)
-      (void)hipGetLastError();
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  allow_dynamic_lds(reinterpret_cast<const void*>(kern), static_cast<int>(lds), lds_set);
   const int64_t blocks = max_tiles * (gu.nt_n + gd.nt_n);
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(kSkThreads), lds, s, gu, gd,
                      sync);
@@ -1633,14 +1632,8 @@ hipError_t launch_big(const GemmArgs& g, int64_t max_units, hipStream_t s) {
   static_assert(kBigStages * kBigStageBytes <= 160 * 1024, "the ring fits the CU's LDS");
   auto kern = gemm_big_kernel<MODE>;
   const size_t lds = kBigStages * kBigStageBytes;
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                            static_cast<int>(lds)) != hipSuccess)
-      (void)hipGetLastError();
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  allow_dynamic_lds(reinterpret_cast<const void*>(kern), static_cast<int>(lds), lds_set);
   const int64_t blocks = (max_units + kXcds - 1) / kXcds * kXcds + kXcds;
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(kBigThreads), lds, s, g);
   return hipGetLastError();
@@ -1945,14 +1938,8 @@ __global__ __launch_bounds__(kF8Threads, 1) void gemm_big_fp8_kernel(const GemmA
 template <int MODE>
 hipError_t launch_big_fp8(const GemmArgs& g, int64_t max_units, hipStream_t s) {
   auto kern = gemm_big_fp8_kernel<MODE>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                            F8Tile<kF8WM>::kLds) != hipSuccess)
-      (void)hipGetLastError();
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  allow_dynamic_lds(reinterpret_cast<const void*>(kern), F8Tile<kF8WM>::kLds, lds_set);
   const int64_t blocks = (max_units + kXcds - 1) / kXcds * kXcds + kXcds;
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(kF8Threads),
                      F8Tile<kF8WM>::kLds, s, g);

@@ -746,6 +746,23 @@ struct MxShape {
   static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "the ring fits the CU's LDS");
 };
 
+// Unit u of an expert's tiles (tiles m-tiles, nt_n n-tiles) in L2-friendly
+// order: groups of kMxGroup m-tiles, n-tile by n-tile within a group, m-tile
+// fastest.  An XCD runs 32 consecutive units at once; one K step of an MX
+// unit reads 32 KB of token rows (BM = 256) and 16 KB of weight rows, so
+// 4 m-tiles x 8 n-tiles read 256 KB of distinct operand bytes per step where
+// m-tile-fastest order over ~10 m-tiles x 3 n-tiles read 368 KB (the L2
+// hit rate of its operand loads measured 72 %).  DeepSeek-V3 shard with
+// MXFP4 weights: FFN 4.90 -> 4.52 ms (groups of 2 and 8: 4.59, 4.58).
+constexpr int kMxGroup = 4;
+__device__ __forceinline__ void mx_unit(int u, int tiles, int nt_n, int& mt, int& nt) {
+  const int grp = u / (kMxGroup * nt_n);
+  const int rem = u - grp * kMxGroup * nt_n;
+  const int gs = min(kMxGroup, tiles - grp * kMxGroup);
+  nt = rem / gs;
+  mt = grp * kMxGroup + rem % gs;
+}
+
 // E8M0 exponent (biased) of a block whose largest magnitude is amax, for an
 // element format whose largest normal has exponent emax: floor(log2 amax) -
 // emax, clamped to the scale's range (an all-zero block takes 2^-127).
@@ -770,7 +787,8 @@ __device__ __forceinline__ void mx_tile(const GemmArgs& g, uint8_t* smem) {
   if (t >= total) return;
   const int4 inf = g.info[t / g.nt_n];
   const int e = inf.x, u = t - inf.y * g.nt_n;
-  const int nt = u / inf.z, mt = u % inf.z;
+  int mt, nt;
+  mx_unit(u, inf.z, g.nt_n, mt, nt);
   const int2 sg = segment(g.seg, g.seg_cap, e);
   const int seg_end = sg.y;
   const int row0 = sg.x + mt * kMxBM;

@@ -89,7 +89,8 @@ def gemm_rows(counts, fp8: bool, max_pairs: int, E_L: int, mx: bool = False) -> 
     """Token rows the GEMMs compute, padding included, under the library's
     tile choice (from the most pairs per expert on average, T min(k, E_L) /
     E_L): bf16 32-row tiles up to 32; 128-row tiles up to 256; else 256-row
-    tiles (bf16: a last remainder of 1..128 rows takes a 128-row wide tile).
+    tiles (bf16: a last remainder of 1..128 rows takes a 128-row wide tile;
+    block-FP8 takes 32-row tiles up to 32 too).
     MX: 32-row tiles up to 32, 128-row up to 256, else 256-row tiles."""
     rows = 0
     for c in (int(x) for x in counts):
@@ -97,7 +98,7 @@ def gemm_rows(counts, fp8: bool, max_pairs: int, E_L: int, mx: bool = False) -> 
             r = max_pairs // E_L
             tm = 256 if r > 256 else 128 if r > 32 else 32
             rows += -(-c // tm) * tm
-        elif not fp8 and max_pairs // E_L <= 32:
+        elif max_pairs // E_L <= 32:
             rows += -(-c // 32) * 32
         elif max_pairs // E_L <= 256:
             rows += -(-c // 128) * 128
@@ -250,7 +251,7 @@ def main():
 
     traffic = stored_traffic(cfg.name + ("_masked" if cap else ""))
     act = "SwiGLU" if cfg.act == "swiglu" else "GELU"
-    skinny = (cfg.mx or not quant) and p.T * min(p.k, p.E_L) // p.E_L <= 32
+    skinny = p.T * min(p.k, p.E_L) // p.E_L <= 32
     kernel = ((f"grouped FFN: work table + one launch of up GEMM/{act} and down GEMM" if skinny
                else f"grouped FFN: work table + up GEMM/{act} + down GEMM")
               + (" (+ shared expert: x quantisation and its FFN)" if p.I_s else ""))
@@ -279,7 +280,8 @@ def main():
     if sample is None:
         sample = {"tiny": 256, "qwen3_30b_prefill": 4096, "dsv3_ep8_prefill": 128,
                   "dsv3_ep8_prefill_fp8": 64, "dsv3_ep8_decode": 64,
-                  "dsv3_ep8_prefill_mxfp4": 64, "dsv3_ep8_decode_mxfp4": 64}.get(cfg.name, 256)
+                  "dsv3_ep8_prefill_mxfp4": 64, "dsv3_ep8_decode_mxfp4": 64,
+                  "dsv3_ep8_decode_fp8": 64}.get(cfg.name, 256)
     if sample > 0:
         cpu = cpu_baseline(cfg, d, sample)
 

@@ -708,6 +708,205 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& g, int t, uint8_t* s
 }
 
 // ---------------------------------------------------------------------------
+// Skinny block-FP8 tile for a few rows per expert (decode with block-FP8
+// weights): the bf16 skinny tile's geometry -- 32 token rows x 256 weight
+// rows, 4 waves of 32 x 64, four 36 KB stages three K steps ahead -- with
+// 128-byte K steps of E4M3 (one 128-wide scale block each) and the
+// pipelined FP8 kernel's arithmetic: a step's two MFMAs per 32 x 32 tile run
+// into a zeroed temporary that is added to the sum times (weight block scale
+// x token group scale).  Weight scales by scalar loads; the step's 32 token
+// scales travel with the operands.  The up tile's 128 h columns are one
+// quantisation group: the four waves exchange their row maxima in LDS and
+// write E4M3 codes and the group scale amax / 448.
+// ---------------------------------------------------------------------------
+constexpr int kF8sScaleOff = (kSkBM + kSkBN) * kRowBytes;   // token scales after the rows
+constexpr int kF8sStageBytes = kF8sScaleOff + 256;           // 32 floats, padded to a lane load
+constexpr int kF8sLoads = kSkLoads + 1;                      // + one token-scale load per wave
+static_assert(kSkStages * kF8sStageBytes <= 160 * 1024 - 1024, "the ring fits the CU's LDS");
+
+template <int MODE>
+__device__ __forceinline__ void f8_skinny_tile(const GemmArgs& g, int t, uint8_t* smem) {
+  constexpr bool kSwiglu = MODE == MODE_SWIGLU_FP8OUT;
+  __shared__ float row_amax[4][kSkBM];
+  const int4 td = skinny_decode(g, t);
+  const int e = td.x, mt = td.y, nt = td.z;
+  const int2 sg = segment(g.seg, g.seg_cap, e);
+  const int seg_end = sg.y;
+  const int row0 = sg.x + mt * kSkBM;
+  const int nk = g.K / kRowBytes;  // one E4M3 byte per element
+  const int kb_n = g.K / 128;      // scale blocks per row
+  const int64_t a_skip = static_cast<int64_t>(row0) * g.a_rs;
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(g.A + a_skip, g.a_bytes - a_skip);
+  const __amdgpu_buffer_rsrc_t rW = make_rsrc(g.W + e * g.w_stride, g.w_stride);
+  const __amdgpu_buffer_rsrc_t rS =
+      make_rsrc(g.A_scale + static_cast<int64_t>(row0) * kb_n,
+                static_cast<int64_t>(min(seg_end - row0, kSkBM)) * kb_n * 4);
+  const int nbase = kSwiglu ? nt * (kSkBN / 2) : nt * kSkBN;
+
+  const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
+  // direct loads: wave w moves A group w (8 of the 32 rows), W groups
+  // 4 + 8w .. 4 + 8w + 7, and the step's 32 token scales (every wave the
+  // same values to the same place)
+  int voff[kSkLoads], ldst[kSkLoads];
+#pragma unroll
+  for (int q = 0; q < kSkLoads; ++q) {
+    const int grp = q == 0 ? w : kSkBM / 8 + w * 8 + (q - 1);
+    const int rr = grp * 8 + (lane >> 3);
+    const int chunk = (lane & 7) ^ ((rr >> 1) & 7);
+    if (rr < kSkBM) {
+      voff[q] = row0 + rr < seg_end ? rr * g.a_rs + chunk * 16 : kOobOffset;
+    } else {
+      const int r = rr - kSkBM;
+      int grow;
+      if (kSwiglu)
+        grow = r < kSkBN / 2 ? min(nbase + r, g.Nout - 1)
+                             : g.Nout + min(nbase + (r - kSkBN / 2), g.Nout - 1);
+      else
+        grow = min(nbase + r, g.NW - 1);
+      voff[q] = grow * g.w_rs + chunk * 16;
+    }
+    ldst[q] = grp * 1024;
+  }
+  const int soff = lane < kSkBM ? lane * kb_n * 4 : kOobOffset;
+  auto dma = [&](int step, int stage) {
+    // steps past the last one load nothing (out-of-range offsets)
+    const bool live = step < nk;
+    const int k = live ? step : 0;
+    uint8_t* base = smem + stage * kF8sStageBytes;
+#pragma unroll
+    for (int q = 0; q < kSkLoads; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(q == 0 ? rA : rW, (lds_ptr_t)(base + ldst[q]), 16,
+                                               live ? voff[q] : kOobOffset, k * kRowBytes, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_ptr_t)(base + kF8sScaleOff), 4,
+                                             live ? soff : kOobOffset, k * 4, 0, 0);
+  };
+
+  // fragments: a lane holds 32 contiguous K bytes, [64 kk + 32 hi, +32), of
+  // its row (chunks c and c ^ 1 after the swizzle); weight tiles i = 0, 1
+  // (SwiGLU: gate rows w*32.., up rows 128 + w*32..; plain: w*64 + i*32..)
+  const int lr = lane & 31, hi = lane >> 5, sl = (lr >> 1) & 7;
+  int foff[4];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const int c0 = (4 * kk + 2 * hi) ^ sl;
+    foff[2 * kk] = lr * kRowBytes + c0 * 16;
+    foff[2 * kk + 1] = lr * kRowBytes + (c0 ^ 1) * 16;
+  }
+  int wbase[2];
+  const float* swp[2];
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const float* wsc = g.W_scale + e * g.ws_stride;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int lrow = kSwiglu ? i * (kSkBN / 2) + w * 32 : w * 64 + i * 32;
+    wbase[i] = (kSkBM + lrow) * kRowBytes;
+    const int lrow_u = kSwiglu ? i * (kSkBN / 2) + wu * 32 : wu * 64 + i * 32;
+    int grow;
+    if (kSwiglu)
+      grow = lrow_u < kSkBN / 2 ? nbase + lrow_u : g.Nout + nbase + (lrow_u - kSkBN / 2);
+    else
+      grow = min(nbase + lrow_u, g.NW - 1);
+    swp[i] = wsc + static_cast<int64_t>(grow / 128) * kb_n;
+  }
+
+  f32x16 acc[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.0f;
+
+#pragma unroll
+  for (int st = 0; st < kSkStages - 1; ++st) dma(st, st);
+  WAIT_VMCNT((kSkStages - 2) * kF8sLoads);
+  __builtin_amdgcn_s_barrier();
+
+  int s_cur = 0;
+  for (int kt = 0; kt < nk; ++kt) {
+    const uint8_t* st = smem + s_cur * kF8sStageBytes;
+    dma(kt + kSkStages - 1, s_cur == 0 ? kSkStages - 1 : s_cur - 1);
+    // weight block scales through the constant address space (scalar loads,
+    // outside the vector-memory wait count)
+    float sw[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      sw[i] = ((const __attribute__((address_space(4))) float*)(uintptr_t)swp[i])[kt];
+    const float sx = *reinterpret_cast<const float*>(st + kF8sScaleOff + lr * 4);
+    f32x16 tmp[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) tmp[i][r] = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const i32x4 b0 = *reinterpret_cast<const i32x4*>(st + foff[2 * kk]);
+      const i32x4 b1 = *reinterpret_cast<const i32x4*>(st + foff[2 * kk + 1]);
+      const i32x8 fb = i32x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const i32x4 a0 = *reinterpret_cast<const i32x4*>(st + wbase[i] + foff[2 * kk]);
+        const i32x4 a1 = *reinterpret_cast<const i32x4*>(st + wbase[i] + foff[2 * kk + 1]);
+        const i32x8 fa = i32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+        tmp[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb, tmp[i], 0, 0, 0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const float sc = sw[i] * sx;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][r] += tmp[i][r] * sc;
+    }
+    WAIT_VMCNT_LDS((kSkStages - 2) * kF8sLoads);
+    __builtin_amdgcn_s_barrier();
+    s_cur = s_cur + 1 == kSkStages ? 0 : s_cur + 1;
+  }
+  WAIT_VMCNT(0);
+
+  // accumulator element q*4 + r: weight row q*8 + (lane/32)*4 + r of the
+  // tile, token row lane % 32
+  const int cq = hi * 4;
+  const int m = row0 + lr;
+  if constexpr (MODE == MODE_PLAIN) {
+    if (m >= seg_end) return;
+    uint8_t* C8 = static_cast<uint8_t*>(g.C);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = nbase + w * 64 + i * 32 + q * 8 + cq;
+        if (col >= g.Nout) continue;
+        uint2 o;
+        o.x = pack_bf16x2(acc[i][q * 4 + 0], acc[i][q * 4 + 1]);
+        o.y = pack_bf16x2(acc[i][q * 4 + 2], acc[i][q * 4 + 3]);
+        *reinterpret_cast<uint2*>(C8 + out_offset(g, m, col)) = o;
+      }
+  } else {
+    // h = silu(gate) * up; the tile's 128 h columns of a token (32 per wave)
+    // are one group: row maxima over the four waves through LDS
+    float hv[16];
+    float am = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      hv[r] = silu_mul(acc[0][r], acc[1][r]);
+      am = fmaxf(am, fabsf(hv[r]));
+    }
+    am = fmaxf(am, __shfl_xor(am, 32));
+    if (lane < 32) row_amax[w][lr] = am;
+    __syncthreads();
+    am = fmaxf(fmaxf(row_amax[0][lr], row_amax[1][lr]), fmaxf(row_amax[2][lr], row_amax[3][lr]));
+    const float sc = am > 0.0f ? am / 448.0f : 1.0f;
+    if (m >= seg_end) return;
+    uint8_t* crow = static_cast<uint8_t*>(g.C) + static_cast<int64_t>(m) * g.Nout;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float* v = hv + q * 4;
+      *reinterpret_cast<uint32_t*>(crow + nbase + w * 32 + q * 8 + cq) =
+          f32x4_to_e4m3x4(v[0] / sc, v[1] / sc, v[2] / sc, v[3] / sc);
+    }
+    if (w == 0 && lane < 32) g.C_scale[static_cast<int64_t>(m) * (g.Nout / 128) + nt] = sc;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // MXFP4 weights x MXFP8 activations (OCP MX formats: E2M1 and E4M3 elements,
 // one E8M0 scale 2^(e - 127) per 32 consecutive K elements of a row) on the
 // block-scaled matrix instruction v_mfma_scale_f32_32x32x64_f8f6f4, which
@@ -1237,9 +1436,10 @@ __device__ __forceinline__ void mx_skinny_tile(const GemmArgs& g, int t, uint8_t
 // ---------------------------------------------------------------------------
 constexpr int kSpinLimit = 1 << 22;  // about half a second of s_sleep 2 polls
 
-// MX: the skinny MX tiles (MXFP4 weights, MXFP8 tokens and h), else the
-// bf16 skinny tiles.
-template <int UPMODE, bool MX>
+// KIND: the skinny tiles of one element type -- kSkBf16, kSkMx (MXFP4
+// weights, MXFP8 tokens and h) or kSkFp8 (block-FP8).
+enum { kSkBf16 = 0, kSkMx = 1, kSkFp8 = 2 };
+template <int UPMODE, int KIND>
 __global__ __launch_bounds__(kSkThreads, 1) void ffn_fused_skinny_kernel(const GemmArgs gu,
                                                                         const GemmArgs gd,
                                                                         int32_t* sync) {
@@ -1253,8 +1453,10 @@ __global__ __launch_bounds__(kSkThreads, 1) void ffn_fused_skinny_kernel(const G
   if (t >= total) return;
   int32_t* done = sync + 1;
   if (t < n_up) {
-    if constexpr (MX)
+    if constexpr (KIND == kSkMx)
       mx_skinny_tile<UPMODE>(gu, t, smem);
+    else if constexpr (KIND == kSkFp8)
+      f8_skinny_tile<UPMODE>(gu, t, smem);
     else
       skinny_tile<UPMODE>(gu, t, smem);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -1275,18 +1477,22 @@ __global__ __launch_bounds__(kSkThreads, 1) void ffn_fused_skinny_kernel(const G
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
-  if constexpr (MX)
+  if constexpr (KIND == kSkMx)
     mx_skinny_tile<MODE_PLAIN>(gd, td, smem);
+  else if constexpr (KIND == kSkFp8)
+    f8_skinny_tile<MODE_PLAIN>(gd, td, smem);
   else
     skinny_tile<MODE_PLAIN>(gd, td, smem);
 }
 
-template <int UPMODE, bool MX>
+template <int UPMODE, int KIND>
 hipError_t launch_fused(const GemmArgs& gu, const GemmArgs& gd, int64_t max_tiles, int32_t* sync,
                         hipStream_t s) {
   static_assert(kSkStages * kSkStageBytes <= 160 * 1024, "the ring fits the CU's LDS");
-  auto kern = ffn_fused_skinny_kernel<UPMODE, MX>;
-  const size_t lds = MX ? kMsStages * kMsStageBytes : kSkStages * kSkStageBytes;
+  auto kern = ffn_fused_skinny_kernel<UPMODE, KIND>;
+  const size_t lds = KIND == kSkMx    ? kMsStages * kMsStageBytes
+                     : KIND == kSkFp8 ? kSkStages * kF8sStageBytes
+                                      : kSkStages * kSkStageBytes;
   static std::atomic<uint64_t> lds_set{0};
   allow_dynamic_lds(reinterpret_cast<const void*>(kern), static_cast<int>(lds), lds_set);
   const int64_t blocks = max_tiles * (gu.nt_n + gd.nt_n);
@@ -1969,8 +2175,8 @@ hipError_t launch_big_fp8(const GemmArgs& g, int64_t max_units, hipStream_t s) {
 GemmPath gemm_path(bool fp8, int64_t rows_per_expert) {
   // Few rows per expert (decode-sized batches): large tiles would spend most
   // of their matrix-core time on padding while the work is weight streaming.
-  if (fp8) return (kF8BM == kBM || rows_per_expert > 2 * kBM) ? GEMM_LARGE_FP8 : GEMM_PIPELINED;
   if (rows_per_expert <= kSkBM) return GEMM_SKINNY;
+  if (fp8) return (kF8BM == kBM || rows_per_expert > 2 * kBM) ? GEMM_LARGE_FP8 : GEMM_PIPELINED;
   if (rows_per_expert <= 2 * kBM) return GEMM_PIPELINED;
   return GEMM_LARGE;
 }
@@ -2070,7 +2276,8 @@ static hipError_t make_args(const GemmLaunch& L, GemmArgs& g) {
   g.a_bytes = L.a_rows * ldb;
   g.c_cs = L.c_panel ? 64 * L.c_rows : 0;
   g.a_index = L.a_index;
-  const bool fp8_path = L.path == GEMM_LARGE_FP8 || L.path == GEMM_PIPELINED;
+  const bool fp8_path =
+      L.path == GEMM_LARGE_FP8 || L.path == GEMM_PIPELINED || L.path == GEMM_SKINNY;
   if ((L.fp8 && !fp8_path) || (!L.fp8 && L.path == GEMM_LARGE_FP8)) return hipErrorInvalidValue;
   if (L.gelu && (L.fp8 || L.swiglu)) return hipErrorInvalidValue;
   return hipSuccess;
@@ -2116,7 +2323,7 @@ hipError_t launch_grouped_gemm(const GemmLaunch& L, hipStream_t s) {
 hipError_t launch_ffn_fused(const GemmLaunch& up, const GemmLaunch& down, int32_t* sync,
                             hipStream_t s) {
   const bool skinny = up.path == GEMM_SKINNY || up.path == GEMM_MX_SKINNY;
-  if (!skinny || down.path != up.path || up.fp8 || down.fp8 || !sync || down.swiglu ||
+  if (!skinny || down.path != up.path || up.fp8 != down.fp8 || !sync || down.swiglu ||
       down.gelu || up.info != down.info || up.n_tiles != down.n_tiles ||
       up.max_tiles != down.max_tiles)
     return hipErrorInvalidValue;
@@ -2126,11 +2333,15 @@ hipError_t launch_ffn_fused(const GemmLaunch& up, const GemmLaunch& down, int32_
   if (err != hipSuccess) return err;
   if (up.path == GEMM_MX_SKINNY) {  // SwiGLU with MXFP8 h only
     if (!up.swiglu) return hipErrorInvalidValue;
-    return launch_fused<MODE_SWIGLU_MX8OUT, true>(gu, gd, up.max_tiles, sync, s);
+    return launch_fused<MODE_SWIGLU_MX8OUT, kSkMx>(gu, gd, up.max_tiles, sync, s);
   }
-  if (up.gelu) return launch_fused<MODE_GELU, false>(gu, gd, up.max_tiles, sync, s);
-  if (up.swiglu) return launch_fused<MODE_SWIGLU, false>(gu, gd, up.max_tiles, sync, s);
-  return launch_fused<MODE_PLAIN, false>(gu, gd, up.max_tiles, sync, s);
+  if (up.fp8) {  // SwiGLU with block-FP8 h only
+    if (!up.swiglu || !up.C_scale) return hipErrorInvalidValue;
+    return launch_fused<MODE_SWIGLU_FP8OUT, kSkFp8>(gu, gd, up.max_tiles, sync, s);
+  }
+  if (up.gelu) return launch_fused<MODE_GELU, kSkBf16>(gu, gd, up.max_tiles, sync, s);
+  if (up.swiglu) return launch_fused<MODE_SWIGLU, kSkBf16>(gu, gd, up.max_tiles, sync, s);
+  return launch_fused<MODE_PLAIN, kSkBf16>(gu, gd, up.max_tiles, sync, s);
 }
 
 }  // namespace moe

@@ -50,7 +50,7 @@ hipError_t launch_quant_blocks(const void* src, int64_t batch, int64_t rows, int
 
 // GEMM kernels, chosen per problem from the mean rows per expert.
 enum GemmPath {
-  GEMM_SKINNY = 0,     // bf16, up to 32 rows: 32 x 256 tiles (decode)
+  GEMM_SKINNY = 0,     // bf16 or block-FP8, up to 32 rows: 32 x 256 tiles (decode)
   GEMM_PIPELINED = 1,  // up to 256 rows: 128 x 256 tiles (bf16 and block-FP8)
   GEMM_LARGE = 2,      // bf16: 256 x 256 tiles, 128 x 512 for segment remainders
   GEMM_LARGE_FP8 = 3,  // block-FP8: 256 x 256 tiles
@@ -110,8 +110,9 @@ struct GemmLaunch {
   const int32_t* a_index;
 };
 hipError_t launch_grouped_gemm(const GemmLaunch& L, hipStream_t s);
-// Both GEMMs of the FFN in one launch (GEMM_SKINNY, or GEMM_MX_SKINNY with the
-// SwiGLU up GEMM): up tiles first, and
+// Both GEMMs of the FFN in one launch (GEMM_SKINNY -- bf16, or block-FP8
+// with the SwiGLU up GEMM -- or GEMM_MX_SKINNY with the SwiGLU up GEMM): up
+// tiles first, and
 // each down tile starts once every up tile of its rows has published h.
 // `up` and `down` as for two launch_grouped_gemm calls sharing one m-tile
 // table; sync as cleared by launch_schedule.

@@ -89,6 +89,9 @@ CONFIGS: Dict[str, MoEConfig] = {
     # Decode-sized batch on the same shard shape with uniform routing.
     "dsv3_ep8_decode": MoEConfig("dsv3_ep8_decode", T=64, H=7168, E=256, E_L=32,
                                  e_lo=0, k=8, I=2048),
+    # The decode batch with block-FP8 weights and activations.
+    "dsv3_ep8_decode_fp8": MoEConfig("dsv3_ep8_decode_fp8", T=64, H=7168, E=256, E_L=32,
+                                     e_lo=0, k=8, I=2048, fp8=True),
     # The same shard with MXFP4 routed-expert weights (MXFP8 activations) and
     # its shared expert in the same format.
     "dsv3_ep8_prefill_mxfp4": MoEConfig("dsv3_ep8_prefill_mxfp4", T=16384, H=7168,

@@ -141,6 +141,10 @@ SMALL_FP8 = {
     # segments, and a shared expert over all 1300 tokens
     "fp8_big_tiles": (small_cfg(T=1300, H=512, E=8, E_L=4, e_lo=2, k=2, I=384, I_s=256,
                                 fp8=True, logits="gumbel_zipf"), 14),
+    # at most 32 rows per expert on average: the fused skinny block-FP8 kernel;
+    # Zipf routing gives the hot experts two or more 32-row tiles
+    "fp8_skinny": (small_cfg(T=64, H=512, E=32, E_L=8, e_lo=8, k=8, I=384, fp8=True,
+                             logits="gumbel_zipf"), 15),
 }
 
 
@@ -389,6 +393,34 @@ def test_workload_full_size_sampled(cid):
     devp = dv.upload(d, False, panel=True)
     y3 = run_layer(torch, dataclasses.replace(p, layout=ml.LAYOUT_PANEL_WEIGHTS), devp)
     np.testing.assert_array_equal(dv.bits_from_bf16(y3), dv.bits_from_bf16(st["y"]))
+
+
+def test_workload_fp8_decode_full_size_sampled():
+    """The DeepSeek-V3 shard's decode batch with block-FP8 weights (the fused
+    skinny FP8 kernel) at full size: routing exact; the outputs of sampled
+    tokens (first, last and random ones) against the oracle with the same
+    activation quantisation; the one-call layer bit-identical to the staged
+    calls."""
+    torch = torch_cuda()
+    ml, dv = _mods()
+    cfg = synth.config("dsv3_ep8_decode_fp8")
+    d, dev = upload(cfg, 5)
+    p = ml.Problem.from_config(cfg)
+    say("full size fp8 decode staged")
+    st = run_staged(torch, p, dev)
+    rid, _ = O.route(d["logits"], cfg.k)
+    np.testing.assert_array_equal(st["ids"].cpu().numpy(), rid)
+    rng = np.random.default_rng(5)
+    toks = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, 14, replace=False)]))
+    ow = OracleWeights(d, True)
+    ref = O.moe_layer_tokens(d["logits"], d["x"], ow.as_layer_dict(cfg.E_L), toks, k=cfg.k,
+                             e_lo=cfg.e_lo, E_L=cfg.E_L, fp8=True, quantize_activations=True)
+    e = rel_rows(f64(st["y"][torch.from_numpy(toks).cuda()]), ref)
+    print(f"fp8 decode sampled rows: {e:.2e}")
+    assert e <= TOL_FP8
+    say("full size fp8 decode fused")
+    y = run_layer(torch, p, dev)
+    np.testing.assert_array_equal(dv.bits_from_bf16(y), dv.bits_from_bf16(st["y"]))
 
 
 def test_workload_fp8_full_size_sampled():

@@ -236,6 +236,26 @@ def main():
     torch.cuda.synchronize()
     layer_tps = T * args.steps / (time.perf_counter() - t1)
 
+    # The one-call layer captured once in a HIP graph and replayed K times
+    # (how a serving loop replays a step): no per-launch host work.  Same
+    # output bits as the calls above.
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ml.moe_layer(p_layer, dev["logits"], dev["x"], W, y_l, ws_l)
+    y_l.zero_()
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    same_graph = bool(torch.equal(y_l.view(torch.int16), y_steps.view(torch.int16)))
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    graph_tps = T * args.steps / (time.perf_counter() - t2)
+
     cnt = counts.cpu().numpy()
     n_pairs = int(cnt.sum())
     # 2 m H I (up, m first-layer matrices) + 2 H I (down) per row (Eq. 8)
@@ -308,6 +328,7 @@ def main():
         "grouped_ffn_frac_of_peak": round(ffn_tflops / PEAK_TFLOPS[dtype], 4),
         "stage_ms": {k2: round(v, 4) for k2, v in stage_ms.items()},
         "moe_layer_call": {"tokens_per_s": round(layer_tps, 1), "same_output_bits": same},
+        "moe_layer_graph": {"tokens_per_s": round(graph_tps, 1), "same_output_bits": same_graph},
         "routing": {"local_pairs": n_pairs, "active_experts": active,
                     "rows_per_expert_max": int(cnt.max()), "rows_per_expert_mean": round(float(cnt.mean()), 1),
                     "gemm_rows_computed": padded_rows,

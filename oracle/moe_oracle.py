@@ -503,7 +503,9 @@ def grouped_ffn(x_perm: np.ndarray, offsets: np.ndarray, w13, w2, h_fn=None,
         h_all[a:b] = h
         y_perm[a:b] = y
     if h_all is None:
-        h_all = np.zeros((N, 0), dtype=np.float64)
+        # no local rows: h is still [0, I], I read from the expert weights
+        I = get2(0).shape[1] if E_L > 0 else 0
+        h_all = np.zeros((N, I), dtype=np.float64)
     return h_all, y_perm
 
 
@@ -532,7 +534,9 @@ def grouped_ffn_masked(x_perm: np.ndarray, counts: np.ndarray, capacity: int,
         h_all[a:a + n] = h
         y_perm[a:a + n] = y
     if h_all is None:
-        h_all = np.zeros((E_L * C, 0), dtype=np.float64)
+        # every block empty: h keeps its [E_L * capacity, I] shape, all zero
+        I = get2(0).shape[1] if E_L > 0 else 0
+        h_all = np.zeros((E_L * C, I), dtype=np.float64)
     return h_all, y_perm
 
 

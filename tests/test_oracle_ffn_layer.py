@@ -232,6 +232,21 @@ def test_empty_batch_layer():
     d = draw(cfg, 0)
     out = O.moe_layer(d["logits"], d["x"], d, k=2, e_lo=0, E_L=8)
     assert out["y"].shape == (0, cfg.H) and out["offsets"][-1] == 0
+    assert out["h"].shape == (0, cfg.I)
+
+
+def test_no_local_rows_keeps_h_width():
+    """Every pick lands off the shard: h is [0, I] (contiguous) or all-zero
+    [E_L * capacity, I] (masked), and y is zero."""
+    cfg = small_cfg(T=5, H=16, E=8, E_L=2, e_lo=6, k=2, I=12)
+    d = draw(cfg, 3)
+    d["logits"][:, 6:] = -1e4                         # experts 6 and 7 never picked
+    out = O.moe_layer(d["logits"], d["x"], d, k=2, e_lo=6, E_L=2)
+    assert out["offsets"][-1] == 0 and out["h"].shape == (0, cfg.I)
+    assert np.all(out["y"] == 0)
+    h, y = O.grouped_ffn_masked(np.zeros((2 * 4, cfg.H)), np.zeros(2, np.int64), 4,
+                                d["w13"], d["w2"])
+    assert h.shape == (8, cfg.I) and not h.any() and not y.any()
 
 
 @pytest.mark.parametrize("e_lo,E_L", [(0, 8), (4, 2)])

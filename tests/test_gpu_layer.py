@@ -23,8 +23,11 @@ def _mods():
 
 def f64(t):
     import torch
-    return t.float().cpu().numpy().astype(np.float64) if t.dtype == torch.bfloat16 else \
-        t.cpu().numpy().astype(np.float64)
+    a = t.float().cpu().numpy() if t.dtype == torch.bfloat16 else t.cpu().numpy()
+    # unused rows of a masked layout are never written and may hold
+    # signalling-NaN patterns; widening them raises numpy's invalid flag
+    with np.errstate(invalid="ignore"):
+        return a.astype(np.float64)
 
 
 def run_layer(torch, p, dev, guard=0):

@@ -1864,50 +1864,59 @@ hipError_t launch_big(const GemmArgs& g, int64_t max_units, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// Large-tile block-FP8 kernel: 4 waves (one per SIMD) as 2 (token rows) x 2
-// (weight rows) over a BM x 256 tile, each wave WM x 128 (WM/32 x 4 MFMA
-// 32x32 tiles; BM = 2 WM).  One K step is one 128-wide scale block: 128 bytes
-// of every row through an LDS ring (codes plus the step's token scales, all
-// by direct loads).
+// Large-tile block-FP8 kernel: 8 waves (two per SIMD) as 4 (token rows) x 2
+// (weight rows) over a 256 x 256 tile, each wave 64 x 128 (2 x 4 MFMA 32x32
+// tiles).  One K step is one 128-wide scale block: 128 bytes of every row
+// through an LDS ring (codes plus the step's token scales, all by direct
+// loads).
 //  * Scales: for each 32x32 tile the two MFMAs of the step (K 0..63, 64..127)
 //    run into a fresh accumulator (the MFMA's zero input) that is then added
-//    to the tile's sum times (weight block scale x token group scale).  With
-//    WM = 128 the sums (256 registers per lane) live in AGPRs and each add
-//    moves them through VGPRs; WM = 64 would keep them in VGPRs but moves
-//    twice the operand bytes per FLOP, and measures slower.
+//    to the tile's sum times (weight block scale x token group scale).  At
+//    64 x 128 per wave the sums (128 registers per lane) stay in VGPRs, so a
+//    tile's promotion is 16 FMAs; the two waves of a SIMD overlap one's
+//    promotion with the other's MFMAs.  (With 128 x 128 per wave the 256 sums
+//    could not all be VGPRs and every promotion moved them through AGPRs:
+//    about 60 VALU instructions per tile and step, more issue time than the
+//    step's MFMAs.)
 //  * Fused gather: with a_index, token row j is row a_index[j] of the codes
 //    and of the scales.
 // ---------------------------------------------------------------------------
-constexpr int kF8BN = 256, kF8Threads = 256;
+constexpr int kF8BN = 256;
 constexpr int kF8RowBytes = 128;
 constexpr int kF8Pitch = 272;  // bf16 epilogue rows
 constexpr int kCuLds = 160 * 1024;  // LDS of a CU: static plus dynamic must fit
 
-template <int WM>
+template <int WM, int WAVES_M>
 struct F8Tile {
-  static constexpr int BM = 2 * WM;
+  static constexpr int BM = WAVES_M * WM;
+  static constexpr int kWaves = 2 * WAVES_M;
+  static constexpr int kThreads = 64 * kWaves;
   static constexpr int kScaleOff = (BM + kF8BN) * kF8RowBytes;
   static constexpr int kStageBytes = kScaleOff + BM * 4 + 512;
   static constexpr int kStatic = 2 * BM * 4;         // row_amax
   static constexpr int kRoom = kCuLds - kStatic;
   static constexpr int kStages = kRoom / kStageBytes < 3 ? kRoom / kStageBytes : 3;
-  static constexpr int kEpilogue = 4 * WM * kF8Pitch;
+  static constexpr int kEpilogue = kWaves * WM * kF8Pitch;
   // dynamic LDS: the ring, or the bf16 epilogue tile if larger
   static constexpr int kLds =
       kStages * kStageBytes > kEpilogue ? kStages * kStageBytes : kEpilogue;
-  static constexpr int kALoads = BM / 8 / 4;          // 8-row groups of A per wave
-  static constexpr int kLoads = kALoads + kF8BN / 8 / 4;
+  static constexpr int kALoads = BM / 8 / kWaves;     // 8-row groups of A per wave
+  static constexpr int kWLoads = kF8BN / 8 / kWaves;  // 8-row groups of W per wave
+  static constexpr int kLoads = kALoads + kWLoads;
   static constexpr int kJ = WM / 32;                  // token blocks per wave
   static_assert(kStages >= 2, "LDS ring");
   static_assert(kLds + kStatic <= kCuLds, "static plus dynamic LDS fit the CU");
+  static_assert(BM % (8 * kWaves) == 0 && kF8BN % (8 * kWaves) == 0, "whole load groups");
+  static_assert(BM % 64 == 0, "token scales in 64-row pieces");
 };
 
-template <int MODE, int WM>
+template <int MODE, int WM, int WAVES_M>
 __device__ __forceinline__ void big_fp8_tile(const GemmArgs& g) {
-  using TT = F8Tile<WM>;
+  using TT = F8Tile<WM, WAVES_M>;
   constexpr int BM = TT::BM;
   constexpr int kStages = TT::kStages, kAhead = kStages - 1;
-  constexpr int kLoads = TT::kLoads, kALoads = TT::kALoads, kJ = TT::kJ;
+  constexpr int kLoads = TT::kLoads, kALoads = TT::kALoads, kWLoads = TT::kWLoads;
+  constexpr int kJ = TT::kJ;
   constexpr int kDma = kLoads + 1;  // + the token-scale load
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   __shared__ float row_amax[2][BM];
@@ -1936,12 +1945,12 @@ __device__ __forceinline__ void big_fp8_tile(const GemmArgs& g) {
 
   const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
   // direct loads: wave w moves A groups w*kALoads.. and W groups
-  // BM/8 + w*8 .. (8 rows of 128 bytes each), and the token scales of 64 rows
-  // ((w % (BM/64)) * 64 ..; with BM = 128 two waves load the same rows).
+  // BM/8 + w*kWLoads .. (8 rows of 128 bytes each), and the token scales of
+  // 64 rows ((w % (BM/64)) * 64 ..; waves w and w + BM/64 load the same rows).
   int voff[kLoads], ldst[kLoads];
 #pragma unroll
   for (int q = 0; q < kLoads; ++q) {
-    const int grp = q < kALoads ? w * kALoads + q : BM / 8 + w * 8 + (q - kALoads);
+    const int grp = q < kALoads ? w * kALoads + q : BM / 8 + w * kWLoads + (q - kALoads);
     const int rr = grp * 8 + (lane >> 3);
     const int chunk = (lane & 7) ^ ((rr >> 1) & 7);
     if (rr < BM) {
@@ -1981,7 +1990,7 @@ __device__ __forceinline__ void big_fp8_tile(const GemmArgs& g) {
 
   // ---- fragments: lane reads 32 bytes (K 32 hi .. 32 hi + 31 of the
   // sub-step's 64) of row lr of a 32-row block, as two swizzled 16-byte chunks
-  const int wm = w & 1, wn = w >> 1;
+  const int wm = w % WAVES_M, wn = w / WAVES_M;
   const int lr = lane & 31, hi = lane >> 5, sl = (lr >> 1) & 7;
   int foff[2][2];
 #pragma unroll
@@ -2006,7 +2015,8 @@ __device__ __forceinline__ void big_fp8_tile(const GemmArgs& g) {
     swp[1] = wsc + static_cast<int64_t>((g.Nout + min(nbase, g.Nout - 1)) / 128) * kb_n;
   } else {
     swp[0] = swp[1] =
-        wsc + static_cast<int64_t>(min(nbase + __builtin_amdgcn_readfirstlane(wn) * 128, g.NW - 1) / 128) * kb_n;
+        wsc + static_cast<int64_t>(min(nbase + __builtin_amdgcn_readfirstlane(wn) * 128,
+                                       g.NW - 1) / 128) * kb_n;
   }
   auto wscale = [&](int which, int k) {
     return ((const __attribute__((address_space(4))) float*)(uintptr_t)swp[which])[k];
@@ -2037,34 +2047,42 @@ __device__ __forceinline__ void big_fp8_tile(const GemmArgs& g) {
     // step kt - 1; it takes step kt + kAhead
     dma(kt + kAhead, s_cur == 0 ? kStages - 1 : s_cur - 1);
     const float sw0 = wscale(0, kt), sw1 = wscale(1, kt);
-    i32x8 fa[2][4], fb[2][kJ];
+    // token fragments for the whole step; weight fragments one 32-row block
+    // at a time (fewer live registers: the sums take 128)
+    i32x8 fb[2][kJ];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int j = 0; j < kJ; ++j)
         fb[kk][j] = rd32(st + abase[j] + foff[kk][0], st + abase[j] + foff[kk][1]);
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        fa[kk][i] = rd32(st + wbase[i] + foff[kk][0], st + wbase[i] + foff[kk][1]);
     float sx[kJ];
 #pragma unroll
     for (int j = 0; j < kJ; ++j)
       sx[j] = *reinterpret_cast<const float*>(st + TT::kScaleOff + (wm * WM + j * 32 + lr) * 4);
     const f32x16 zero = {0};
 #pragma unroll
-    for (int j = 0; j < kJ; ++j)
+    for (int i = 0; i < 4; ++i) {
+      const i32x8 fa0 = rd32(st + wbase[i] + foff[0][0], st + wbase[i] + foff[0][1]);
+      const i32x8 fa1 = rd32(st + wbase[i] + foff[1][0], st + wbase[i] + foff[1][1]);
+      // both token blocks' MFMAs before either promotion: one tile's
+      // result latency hides behind the other's MFMAs
+      f32x16 tt[kJ];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f32x16 tt = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[0][i], fb[0][j], zero, 0, 0,
-                                                                   0, 0, 0, 0);
-        tt = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[1][i], fb[1][j], tt, 0, 0, 0, 0, 0,
-                                                            0);
-        const float c = (kSwiglu && i >= 2 ? sw1 : sw0) * sx[j];
+      for (int j = 0; j < kJ; ++j)
+        tt[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa0, fb[0][j], zero, 0, 0, 0, 0,
+                                                               0, 0);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] += tt[r] * c;
+      for (int j = 0; j < kJ; ++j)
+        tt[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa1, fb[1][j], tt[j], 0, 0, 0, 0,
+                                                               0, 0);
+      const float swi = kSwiglu && i >= 2 ? sw1 : sw0;
+#pragma unroll
+      for (int j = 0; j < kJ; ++j) {
+        const float c = swi * sx[j];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] += tt[j][r] * c;
       }
+    }
     // Step boundary: step kt+1 has landed once only the later steps' loads
     // are in flight, and this wave's reads of stage kt are done; the barrier
     // publishes both.
@@ -2147,26 +2165,28 @@ __device__ __forceinline__ void big_fp8_tile(const GemmArgs& g) {
   }
 }
 
-// Rows per wave of the block-FP8 large-tile kernel (its row tile is twice
-// that).  128 (a 256 x 256 tile) against 64 (128 x 256, three stages, the
-// sums in VGPRs): 5.6 ms against 7.0 ms for the DeepSeek-V3 fp8 shard's FFN.
-constexpr int kF8WM = 128;
-constexpr int kF8BM = 2 * kF8WM;
+// Geometry of the block-FP8 large-tile kernel: 64 rows per wave, 4 waves
+// along the rows, so a 256 x 256 tile.  (4 waves of 128 x 128 on the same
+// tile spent more VALU issue on the scale promotion than MFMA time.)
+constexpr int kF8WM = 64, kF8WavesM = 4;
+using F8Big = F8Tile<kF8WM, kF8WavesM>;
+constexpr int kF8BM = F8Big::BM;
+constexpr int kF8Threads = F8Big::kThreads;
 
 // (A kernel template over MODE only: the tile body takes the geometry.)
 template <int MODE>
 __global__ __launch_bounds__(kF8Threads, 1) void gemm_big_fp8_kernel(const GemmArgs g) {
-  big_fp8_tile<MODE, kF8WM>(g);
+  big_fp8_tile<MODE, kF8WM, kF8WavesM>(g);
 }
 
 template <int MODE>
 hipError_t launch_big_fp8(const GemmArgs& g, int64_t max_units, hipStream_t s) {
   auto kern = gemm_big_fp8_kernel<MODE>;
   static std::atomic<uint64_t> lds_set{0};
-  allow_dynamic_lds(reinterpret_cast<const void*>(kern), F8Tile<kF8WM>::kLds, lds_set);
+  allow_dynamic_lds(reinterpret_cast<const void*>(kern), F8Big::kLds, lds_set);
   const int64_t blocks = (max_units + kXcds - 1) / kXcds * kXcds + kXcds;
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(kF8Threads),
-                     F8Tile<kF8WM>::kLds, s, g);
+                     F8Big::kLds, s, g);
   return hipGetLastError();
 }
 

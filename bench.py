@@ -113,7 +113,7 @@ def gemm_rows(counts, fp8: bool, max_pairs: int, E_L: int, mx: bool = False) -> 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+        print(f"bench.py measures one GPU: the library runs on one GPU per process "
               f"(asked for --gpus {args.gpus})", file=sys.stderr)
         sys.exit(2)
 

@@ -61,7 +61,7 @@ extern "C" {
 typedef enum {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARG = 1,  /* null pointer, size out of range, misalignment */
-  MOE_ERR_UNSUPPORTED = 2,  /* valid request this build does not implement   */
+  MOE_ERR_UNSUPPORTED = 2,  /* valid request the library does not implement  */
   MOE_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required     */
   MOE_ERR_HIP = 4           /* a HIP launch or runtime call failed            */
 } moe_status;

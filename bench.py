@@ -157,16 +157,20 @@ def main():
         sc = dict(dtype=torch.uint8, device="cuda") if cfg.mx else \
             dict(dtype=torch.float32, device="cuda")
         g = 32 if cfg.mx else 128
-        xp = torch.empty((N, H), dtype=torch.uint8, device="cuda")
-        xs = torch.empty((N, H // g), **sc)
+        if cfg.mx:   # MX: the dispatch gathers and quantises the rows
+            xp = torch.empty((N, H), dtype=torch.uint8, device="cuda")
+            xs = torch.empty((N, H // g), **sc)
+        else:        # block-FP8: the tokens quantised once, gathered by the FFN
+            xq = torch.empty((T, H), dtype=torch.uint8, device="cuda")
+            xqs = torch.empty((T, H // g), **sc)
         if p.I_s:
             q = ml.Problem(T=T, H=H, E=1, k=1, e_lo=0, E_L=1, I=p.I_s, fp8=cfg.fp8, mx=cfg.mx,
                            layout=wlay)
             off2 = torch.tensor([0, T], **i32)
             sw = ml.weights_struct(dev["ws13_q"], dev["ws2_q"], None, None, dev["ws13_s"],
                                    dev["ws2_s"])
-            sx = torch.empty((T, H), dtype=torch.uint8, device="cuda")
-            sxs = torch.empty((T, H // g), **sc)
+            sx, sxs = (torch.empty((T, H), dtype=torch.uint8, device="cuda"),
+                       torch.empty((T, H // g), **sc)) if cfg.mx else (xq, xqs)
             shared = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
             ws_s = dv.workspace(q, ml.STAGE_FFN)
 
@@ -175,7 +179,9 @@ def main():
     # One step: moe_layer's kernels, one library call per stage, so that the
     # grouped FFN's launches inside the timed region can be bracketed with
     # HIP events on the stream they run on.  bf16: route, index-only
-    # dispatch, the FFN gathering its rows from x, combine.  fp8: route,
+    # dispatch, the FFN gathering its rows from x, combine.  block-FP8:
+    # route, index-only dispatch and x quantised once, the FFN gathering its
+    # rows from those codes, the shared expert on them, combine.  MX: route,
     # dispatch with quantisation, FFN, shared expert (quantise x, dense FFN),
     # combine.
     def step(ev=None):
@@ -187,19 +193,28 @@ def main():
             ml.moe_dispatch(p, dev["x"], ids, counts, offsets, rt, rs, tsr, None, None, ws_d,
                             stream)
             rec(2)
-            ml.moe_grouped_ffn_gather(p, dev["x"], rt, seg, W, None, yp, ws_f, stream)
+            ml.moe_grouped_ffn_gather(p, dev["x"], None, rt, seg, W, None, None, yp, ws_f,
+                                      stream)
             rec(3)
             sh = None
+        elif not cfg.mx:
+            ml.moe_dispatch(p, dev["x"], ids, counts, offsets, rt, rs, tsr, None, None, ws_d,
+                            stream)
+            ml.moe_quantize_fp8(dev["x"], 1, T, H, 1, xq, xqs, stream)
+            rec(2)
+            ml.moe_grouped_ffn_gather(p, xq, xqs, rt, seg, W, None, None, yp, ws_f, stream)
+            sh = None
+            if p.I_s:
+                ml.moe_grouped_ffn(q, xq, xqs, off2, sw, None, None, shared, ws_s, stream)
+                sh = shared
+            rec(3)
         else:
             ml.moe_dispatch(p, dev["x"], ids, counts, offsets, rt, rs, tsr, xp, xs, ws_d, stream)
             rec(2)
             ml.moe_grouped_ffn(p, xp, xs, seg, W, None, None, yp, ws_f, stream)
             sh = None
             if p.I_s:
-                if cfg.mx:
-                    ml.moe_quantize_mx(dev["x"], 1, T, H, ml.MX_E4M3, sx, sxs, stream)
-                else:
-                    ml.moe_quantize_fp8(dev["x"], 1, T, H, 1, sx, sxs, stream)
+                ml.moe_quantize_mx(dev["x"], 1, T, H, ml.MX_E4M3, sx, sxs, stream)
                 ml.moe_grouped_ffn(q, sx, sxs, off2, sw, None, None, shared, ws_s, stream)
                 sh = shared
             rec(3)
@@ -403,18 +418,16 @@ def stream_bench(args, cfg, d, p_layer, W, dev):
         cnt, offs = torch.empty(q.E_L, **i32), torch.empty(q.E_L + 1, **i32)
         rt, rs, tsr = torch.empty(N, **i32), torch.empty(N, **i32), torch.empty((tp, k), **i32)
         yp = torch.empty((N, H), dtype=torch.bfloat16, device="cuda")
-        if q.fp8:
-            xp = torch.empty((N, H), dtype=torch.uint8, device="cuda")
-            xs = torch.empty((N, H // 128), dtype=torch.float32, device="cuda")
-            ml.moe_dispatch(q, x, ids, cnt, offs, rt, rs, tsr, xp, xs,
-                            dv.workspace(q, ml.STAGE_DISPATCH))
-            wsf = dv.workspace(q, ml.STAGE_FFN)
-            fn = lambda: ml.moe_grouped_ffn(q, xp, xs, offs, W, None, None, yp, wsf)
+        ml.moe_dispatch(q, x, ids, cnt, offs, rt, rs, tsr, None, None,
+                        dv.workspace(q, ml.STAGE_DISPATCH))
+        wsf = dv.workspace(q, ml.STAGE_FFN)
+        if q.fp8:   # the FFN gathers from the tokens quantised once
+            xq = torch.empty((tp, H), dtype=torch.uint8, device="cuda")
+            xqs = torch.empty((tp, H // 128), dtype=torch.float32, device="cuda")
+            ml.moe_quantize_fp8(x, 1, tp, H, 1, xq, xqs)
+            fn = lambda: ml.moe_grouped_ffn_gather(q, xq, xqs, rt, offs, W, None, None, yp, wsf)
         else:
-            ml.moe_dispatch(q, x, ids, cnt, offs, rt, rs, tsr, None, None,
-                            dv.workspace(q, ml.STAGE_DISPATCH))
-            wsf = dv.workspace(q, ml.STAGE_FFN)
-            fn = lambda: ml.moe_grouped_ffn_gather(q, x, rt, offs, W, None, yp, wsf)
+            fn = lambda: ml.moe_grouped_ffn_gather(q, x, None, rt, offs, W, None, None, yp, wsf)
         fn()
         ms = _time_ms(fn, 7)
         pairs = int(cnt.sum().item())

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 7
+#define MOE_ABI_VERSION 8
 
 typedef enum {
   MOE_OK = 0,
@@ -246,22 +246,26 @@ moe_status moe_grouped_ffn(const moe_problem* p, const void* x_perm,
                            void* y_perm, void* ws, size_t ws_bytes,
                            void* stream);
 
-/* The grouped FFN reading its rows straight from the layer input: row j of
- * the permutation is x[row_token[j]] (bf16 only; the page passages are those
- * of moe_grouped_ffn).  Together with moe_dispatch(..., x_perm = NULL, ...)
- * this is the bf16 path of moe_layer, kernel for kernel: the permuted
+/* The grouped FFN reading its rows straight from the unpermuted tokens: row
+ * j of the permutation is x[row_token[j]] (the page passages are those of
+ * moe_grouped_ffn).  Together with moe_dispatch(..., x_perm = NULL, ...)
+ * this is the path of moe_layer, kernel for kernel: the permuted
  * activations are never written.
- *   x [T, H] bf16 row major, row_token [N_cap] (from moe_dispatch), offsets
- *   (counts for the masked layout),
- *   w, h (optional, as in moe_grouped_ffn, layout per MOE_LAYOUT_PANEL_ACTS),
- *   y_perm [N_cap, H] bf16 (output).
- * MOE_ERR_UNSUPPORTED for MOE_FP8_E4M3 and for x of 2 GiB or more.
+ *   x [T, H] row major: bf16; for MOE_FP8_E4M3 the E4M3 codes of the
+ *   tokens with x_scale [T, H/128] fp32 (moe_quantize_fp8 of the bf16
+ *   tokens: a row's codes depend on that row alone, so the result has the
+ *   bits of moe_grouped_ffn on moe_dispatch's x_perm); x_scale NULL for bf16.
+ *   row_token [N_cap] (from moe_dispatch), offsets (counts for the masked
+ *   layout), w, h and h_scale (optional, as in moe_grouped_ffn; bf16 h in
+ *   the layout of MOE_LAYOUT_PANEL_ACTS), y_perm [N_cap, H] bf16 (output).
+ * MOE_ERR_UNSUPPORTED for MOE_MXFP4 and for x of 2 GiB or more.
  * Workspace: moe_workspace_bytes(p, MOE_STAGE_FFN).                        */
 moe_status moe_grouped_ffn_gather(const moe_problem* p, const void* x,
+                                  const float* x_scale,
                                   const int32_t* row_token,
                                   const int32_t* offsets, const moe_weights* w,
-                                  void* h, void* y_perm, void* ws,
-                                  size_t ws_bytes, void* stream);
+                                  void* h, float* h_scale, void* y_perm,
+                                  void* ws, size_t ws_bytes, void* stream);
 
 /* Combine.  Page "CascadeEP ...", Appendix C, "Output return and combine"
  * (each routed contribution weighted by its routing coefficient exactly once,

@@ -275,13 +275,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pipelined_kernel(const GemmA
   }
   // fp8: token scales of the step, 128 rows x 4 bytes, land beside the
   // operands (waves 0/1 and 2/3 load the same two halves; the duplicate
-  // writes carry identical values).
+  // writes carry identical values).  With a fused gather the view spans
+  // every source row's scales and each lane's offset names its row.
   const int kb_n = g.K / 128;
+  const int srr = (w & 1) * 64 + lane;
   const __amdgpu_buffer_rsrc_t rS =
-      FP8 ? make_rsrc(g.A_scale + static_cast<int64_t>(row0) * kb_n,
-                      static_cast<int64_t>(min(seg_end - row0, kBM)) * kb_n * 4)
-          : make_rsrc(g.A, 0);
-  const int soffs = ((w & 1) * 64 + lane) * kb_n * 4;
+      !FP8        ? make_rsrc(g.A, 0)
+      : g.a_index ? make_rsrc(g.A_scale, g.a_bytes / g.K * kb_n * 4)
+                  : make_rsrc(g.A_scale + static_cast<int64_t>(row0) * kb_n,
+                              static_cast<int64_t>(min(seg_end - row0, kBM)) * kb_n * 4);
+  const int soffs = !g.a_index ? srr * kb_n * 4
+                    : row0 + srr < seg_end ? g.a_index[row0 + srr] * kb_n * 4
+                                           : kOobOffset;
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(a_base, a_left);
   const __amdgpu_buffer_rsrc_t rW = make_rsrc(w_base, g.w_stride);
   auto dma = [&](int step, int stage) {
@@ -735,12 +740,15 @@ __device__ __forceinline__ void f8_skinny_tile(const GemmArgs& g, int t, uint8_t
   const int row0 = sg.x + mt * kSkBM;
   const int nk = g.K / kRowBytes;  // one E4M3 byte per element
   const int kb_n = g.K / 128;      // scale blocks per row
-  const int64_t a_skip = static_cast<int64_t>(row0) * g.a_rs;
+  // with a fused gather (a_index) the views span the whole source and each
+  // lane's offset names its row
+  const int64_t a_skip = g.a_index ? 0 : static_cast<int64_t>(row0) * g.a_rs;
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(g.A + a_skip, g.a_bytes - a_skip);
   const __amdgpu_buffer_rsrc_t rW = make_rsrc(g.W + e * g.w_stride, g.w_stride);
   const __amdgpu_buffer_rsrc_t rS =
-      make_rsrc(g.A_scale + static_cast<int64_t>(row0) * kb_n,
-                static_cast<int64_t>(min(seg_end - row0, kSkBM)) * kb_n * 4);
+      g.a_index ? make_rsrc(g.A_scale, g.a_bytes / g.K * kb_n * 4)
+                : make_rsrc(g.A_scale + static_cast<int64_t>(row0) * kb_n,
+                            static_cast<int64_t>(min(seg_end - row0, kSkBM)) * kb_n * 4);
   const int nbase = kSwiglu ? nt * (kSkBN / 2) : nt * kSkBN;
 
   const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
@@ -754,7 +762,9 @@ __device__ __forceinline__ void f8_skinny_tile(const GemmArgs& g, int t, uint8_t
     const int rr = grp * 8 + (lane >> 3);
     const int chunk = (lane & 7) ^ ((rr >> 1) & 7);
     if (rr < kSkBM) {
-      voff[q] = row0 + rr < seg_end ? rr * g.a_rs + chunk * 16 : kOobOffset;
+      const bool valid = row0 + rr < seg_end;
+      const int arow = g.a_index && valid ? g.a_index[row0 + rr] : rr;
+      voff[q] = valid ? arow * g.a_rs + chunk * 16 : kOobOffset;
     } else {
       const int r = rr - kSkBM;
       int grow;
@@ -767,7 +777,9 @@ __device__ __forceinline__ void f8_skinny_tile(const GemmArgs& g, int t, uint8_t
     }
     ldst[q] = grp * 1024;
   }
-  const int soff = lane < kSkBM ? lane * kb_n * 4 : kOobOffset;
+  int soff = lane < kSkBM ? lane * kb_n * 4 : kOobOffset;
+  if (g.a_index && lane < kSkBM)
+    soff = row0 + lane < seg_end ? g.a_index[row0 + lane] * kb_n * 4 : kOobOffset;
   auto dma = [&](int step, int stage) {
     // steps past the last one load nothing (out-of-range offsets)
     const bool live = step < nk;
@@ -2244,10 +2256,11 @@ hipError_t launch_schedule(const int32_t* seg, int seg_cap, int E_L, GemmPath pa
 // Kernel arguments of one grouped GEMM; hipErrorInvalidValue for requests the
 // kernels cannot address.
 static hipError_t make_args(const GemmLaunch& L, GemmArgs& g) {
-  // The fused gather reads bf16 row-major sources whose lane offsets fit
-  // below the buffer cap.
+  // The fused gather reads bf16 or E4M3 row-major sources whose lane
+  // offsets fit below the buffer cap (not MX).
   static_assert(kGemmGatherMaxBytes <= kBufMax, "gather offsets must stay below the range cap");
-  if (L.a_index && (L.fp8 || L.a_panel || L.a_rows * 2 * L.K > kGemmGatherMaxBytes))
+  if (L.a_index &&
+      (L.mx || L.a_panel || L.a_rows * (L.fp8 ? 1 : 2) * L.K > kGemmGatherMaxBytes))
     return hipErrorInvalidValue;
   g = GemmArgs{};
   g.A = static_cast<const uint8_t*>(L.A);

@@ -107,9 +107,11 @@ struct Carve {
 
 // Fused gather of bf16 sources whose byte size fits the GEMM's 32-bit lane
 // offsets.
+// The up GEMM can read its rows from the unpermuted tokens (bf16, or the
+// E4M3 codes of block-FP8) through row_token.
 bool can_fuse_gather(const moe_problem* p) {
-  return !quant_acts(p) &&
-         static_cast<int64_t>(p->num_tokens) * p->hidden * 2 <= kGemmGatherMaxBytes;
+  return !is_mx(p) && static_cast<int64_t>(p->num_tokens) * p->hidden * (is_fp8(p) ? 1 : 2) <=
+                          kGemmGatherMaxBytes;
 }
 
 struct FfnScratch {
@@ -183,6 +185,8 @@ struct LayerScratch {
   int32_t* tsr;
   void* x_perm;
   float* x_perm_scale;
+  void* xq;          // block-FP8 with the fused gather: the tokens quantised
+  float* xq_scale;   // once, [T, H] codes and [T, H/128] scales
   void* y_perm;
   void* index_scratch;
   FfnScratch ffn;
@@ -217,16 +221,22 @@ LayerScratch carve_layer(Carve& c, const moe_problem* p) {
   s.row_token = c.take<int32_t>(4 * N);
   s.row_slot = c.take<int32_t>(4 * N);
   s.tsr = c.take<int32_t>(4 * T * k);
-  // x_perm only where the up GEMM does not gather from x itself
-  s.x_perm = can_fuse_gather(p) ? nullptr : c.take<void>((quant_acts(p) ? 1 : 2) * N * H);
-  s.x_perm_scale = quant_acts(p) ? c.take<float>(act_scale_bytes(p, N, H)) : nullptr;
+  // x_perm only where the up GEMM does not gather from the tokens itself;
+  // block-FP8 gathers from the tokens quantised once
+  const bool fuse = can_fuse_gather(p);
+  s.x_perm = fuse ? nullptr : c.take<void>((quant_acts(p) ? 1 : 2) * N * H);
+  s.x_perm_scale = quant_acts(p) && !fuse ? c.take<float>(act_scale_bytes(p, N, H)) : nullptr;
+  if (fuse && is_fp8(p)) {
+    s.xq = c.take<void>(T * H);
+    s.xq_scale = c.take<float>(act_scale_bytes(p, T, H));
+  }
   s.y_perm = c.take<void>(2 * N * H);
   s.index_scratch = c.take<void>(index_scratch_bytes(static_cast<int>(T), static_cast<int>(EL)));
   s.ffn = carve_ffn(c, p);
   if (p->shared_inter > 0) {
     const moe_problem q = shared_problem(p);
     s.s_offsets = c.take<int32_t>(8);
-    if (quant_acts(p)) {
+    if (quant_acts(p) && !s.xq) {
       s.s_x = c.take<void>(T * H);
       s.s_x_scale = c.take<float>(act_scale_bytes(p, T, H));
     }
@@ -447,23 +457,26 @@ moe_status moe_grouped_ffn(const moe_problem* p, const void* x_perm, const float
   return run_ffn(p, src, offsets, w, h, h_scale, y_perm, f, static_cast<hipStream_t>(stream));
 }
 
-moe_status moe_grouped_ffn_gather(const moe_problem* p, const void* x, const int32_t* row_token,
-                                  const int32_t* offsets, const moe_weights* w, void* h,
-                                  void* y_perm, void* ws, size_t ws_bytes, void* stream) {
+moe_status moe_grouped_ffn_gather(const moe_problem* p, const void* x, const float* x_scale,
+                                  const int32_t* row_token, const int32_t* offsets,
+                                  const moe_weights* w, void* h, float* h_scale, void* y_perm,
+                                  void* ws, size_t ws_bytes, void* stream) {
   moe_status st = check_problem(p);
   if (st != MOE_OK) return st;
-  if (quant_acts(p) || !can_fuse_gather(p)) return MOE_ERR_UNSUPPORTED;
+  if (!can_fuse_gather(p)) return MOE_ERR_UNSUPPORTED;
   const void* ptrs[] = {x, row_token, offsets, y_perm};
   for (const void* q : ptrs)
     if (!q || !aligned16(q)) return MOE_ERR_INVALID_ARG;
   if (!weights_ok(p, w, false)) return MOE_ERR_INVALID_ARG;
+  if (quant_acts(p) && (!x_scale || !aligned16(x_scale))) return MOE_ERR_INVALID_ARG;
   if (h && !aligned16(h)) return MOE_ERR_INVALID_ARG;
+  if (h && quant_acts(p) && (!h_scale || !aligned16(h_scale))) return MOE_ERR_INVALID_ARG;
   if (!ws || ws_bytes < moe_workspace_bytes(p, MOE_STAGE_FFN)) return MOE_ERR_WORKSPACE;
   if (p->num_tokens == 0) return MOE_OK;
   Carve c(align_ws(ws));
   const FfnScratch f = carve_ffn(c, p);
-  const FfnSource src{x, nullptr, true, row_token, p->num_tokens};
-  return run_ffn(p, src, offsets, w, h, nullptr, y_perm, f, static_cast<hipStream_t>(stream));
+  const FfnSource src{x, quant_acts(p) ? x_scale : nullptr, true, row_token, p->num_tokens};
+  return run_ffn(p, src, offsets, w, h, h_scale, y_perm, f, static_cast<hipStream_t>(stream));
 }
 
 moe_status moe_combine(const moe_problem* p, const void* y_perm, const int32_t* token_slot_row,
@@ -506,14 +519,23 @@ moe_status enqueue_layer(const moe_problem* p, const float* logits, const void* 
   const int T = p->num_tokens;
   const moe_problem pi = layer_internal(p);
 
-  // bf16: the up GEMM gathers its rows from x through row_token, so the
-  // permuted activations are never written; fp8 gathers and quantises first.
+  // The up GEMM gathers its rows from the tokens through row_token, so the
+  // permuted activations are never written: bf16 from x, block-FP8 from x
+  // quantised once (which the shared expert reads too); MX gathers and
+  // quantises in the dispatch.
   const bool fuse = can_fuse_gather(p);
   MOE_TRY(launch_route_topk(logits, T, p->num_experts, p->top_k, L.ids, L.w, s));
   st = run_dispatch(&pi, x, L.ids, L.counts, L.offsets, L.row_token, L.row_slot, L.tsr,
                     fuse ? nullptr : L.x_perm, L.x_perm_scale, L.index_scratch, s);
   if (st != MOE_OK) return st;
-  const FfnSource rsrc = fuse ? FfnSource{x, nullptr, true, L.row_token, T}
+  const void* xa = x;
+  const float* xa_scale = nullptr;
+  if (fuse && is_fp8(p)) {
+    MOE_TRY(launch_gather_fp8(x, nullptr, nullptr, T, p->hidden, L.xq, L.xq_scale, s));
+    xa = L.xq;
+    xa_scale = L.xq_scale;
+  }
+  const FfnSource rsrc = fuse ? FfnSource{xa, xa_scale, true, L.row_token, T}
                               : FfnSource{L.x_perm, L.x_perm_scale, false, nullptr, 0};
   st = run_ffn(&pi, rsrc, p->capacity > 0 ? L.counts : L.offsets, w, nullptr, nullptr, L.y_perm,
                L.ffn, s);
@@ -529,15 +551,21 @@ moe_status enqueue_layer(const moe_problem* p, const float* logits, const void* 
     hipLaunchKernelGGL(fill_offsets_kernel, dim3(1), dim3(64), 0, s, L.s_offsets, T);
     MOE_TRY(hipGetLastError());
     const void* sx = x;
+    const float* sx_scale = nullptr;
     if (is_mx(p)) {
       MOE_TRY(launch_gather_mx8(x, nullptr, nullptr, T, p->hidden, L.s_x,
                                 reinterpret_cast<uint8_t*>(L.s_x_scale), s));
       sx = L.s_x;
+      sx_scale = L.s_x_scale;
+    } else if (is_fp8(p) && L.xq) {
+      sx = L.xq;
+      sx_scale = L.xq_scale;
     } else if (is_fp8(p)) {
       MOE_TRY(launch_gather_fp8(x, nullptr, nullptr, T, p->hidden, L.s_x, L.s_x_scale, s));
       sx = L.s_x;
+      sx_scale = L.s_x_scale;
     }
-    const FfnSource ssrc{sx, L.s_x_scale, true, nullptr, 0};
+    const FfnSource ssrc{sx, sx_scale, true, nullptr, 0};
     st = run_ffn(&q, ssrc, L.s_offsets, &sw, nullptr, nullptr, L.s_out, L.s_ffn, s);
     if (st != MOE_OK) return st;
   }

@@ -46,7 +46,7 @@ SIGNATURES = {
     "moe_route": (_i32, [_P, _vp, _vp, _vp, _vp]),
     "moe_dispatch": (_i32, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_grouped_ffn": (_i32, [_P, _vp, _vp, _vp, _W, _vp, _vp, _vp, _vp, _sz, _vp]),
-    "moe_grouped_ffn_gather": (_i32, [_P, _vp, _vp, _vp, _W, _vp, _vp, _vp, _sz, _vp]),
+    "moe_grouped_ffn_gather": (_i32, [_P, _vp, _vp, _vp, _vp, _W, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_combine": (_i32, [_P, _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_layer": (_i32, [_P, _vp, _vp, _W, _vp, _vp, _sz, _vp]),
     "moe_quantize_fp8": (_i32, [_vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp]),
@@ -203,12 +203,13 @@ def moe_grouped_ffn(p: Problem, x_perm, x_perm_scale, offsets, weights: moe_weig
         ws.numel() * ws.element_size(), _stream(stream)))
 
 
-def moe_grouped_ffn_gather(p: Problem, x, row_token, offsets, weights: moe_weights, h, y_perm,
-                           ws, stream=None) -> None:
+def moe_grouped_ffn_gather(p: Problem, x, x_scale, row_token, offsets, weights: moe_weights, h,
+                           h_scale, y_perm, ws, stream=None) -> None:
     pc = p.c()
     _check("moe_grouped_ffn_gather", lib().moe_grouped_ffn_gather(
-        ctypes.byref(pc), _ptr(x), _ptr(row_token), _ptr(offsets), ctypes.byref(weights), _ptr(h),
-        _ptr(y_perm), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+        ctypes.byref(pc), _ptr(x), _ptr(x_scale), _ptr(row_token), _ptr(offsets),
+        ctypes.byref(weights), _ptr(h), _ptr(h_scale), _ptr(y_perm), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def moe_combine(p: Problem, y_perm, token_slot_row, topk_w, shared_out, y, stream=None) -> None:

@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert ml.lib().moe_abi_version() == 7
+    assert ml.lib().moe_abi_version() == 8
     assert ml.status_str(0) == "MOE_OK"
     assert ml.status_str(3) == "MOE_ERR_WORKSPACE"
     assert ml.status_str(99) == "MOE_ERR_UNKNOWN"
@@ -55,10 +55,11 @@ def test_workspace_sizes(cid):
     ffn = ml.workspace_bytes(p, ml.STAGE_FFN)
     assert layer > 0 and disp > 0 and ffn > 0
     assert layer > disp and layer > ffn
-    # the layer workspace holds at least the expert outputs and h (bf16 gathers
-    # its GEMM rows straight from x; fp8 also holds the quantised x_perm)
+    # the layer workspace holds at least the expert outputs and h (the up GEMM
+    # gathers its rows straight from the tokens; block-FP8 also holds the
+    # tokens quantised once, T rows)
     beta = 1 if p.fp8 else 2
-    assert layer >= p.n_cap * (2 * p.H + beta * p.I + (p.H if p.fp8 else 0))
+    assert layer >= p.n_cap * (2 * p.H + beta * p.I) + (p.T * p.H if p.fp8 else 0)
     assert ml.workspace_bytes(p, 7) == 0
 
 
@@ -159,17 +160,29 @@ def test_gather_ffn_argument_checks():
     p = ml.Problem(T=16, H=256, E=8, k=2, e_lo=0, E_L=8, I=256).c()
     w = ml.moe_weights(256, 256, None, None, None, None, None, None)
     n = ml.workspace_bytes(ml.Problem(T=16, H=256, E=8, k=2, e_lo=0, E_L=8, I=256), ml.STAGE_FFN)
-    ok_args = [256, 256, 256, ctypes.byref(w), None, 256, 256, n, None]
-    # fp8 is not supported by the gathering FFN
-    pf = ml.Problem(T=16, H=256, E=8, k=2, e_lo=0, E_L=8, I=256, fp8=True).c()
-    assert L.moe_grouped_ffn_gather(ctypes.byref(pf), *ok_args) == ml.MOE_ERR_UNSUPPORTED
-    for i in (0, 1, 2, 5):      # x, row_token, offsets, y_perm
+    # x, x_scale, row_token, offsets, w, h, h_scale, y_perm, ws, ws_bytes, stream
+    ok_args = [256, None, 256, 256, ctypes.byref(w), None, None, 256, 256, n, None]
+    for i in (0, 2, 3, 7):      # x, row_token, offsets, y_perm
         bad = list(ok_args)
         bad[i] = None
         assert L.moe_grouped_ffn_gather(ctypes.byref(p), *bad) == ml.MOE_ERR_INVALID_ARG
     bad = list(ok_args)
-    bad[7] = 16                 # workspace too small
+    bad[9] = 16                 # workspace too small
     assert L.moe_grouped_ffn_gather(ctypes.byref(p), *bad) == ml.MOE_ERR_WORKSPACE
+    # block-FP8: the token scales (and, with h, the h scales) are required
+    pq = ml.Problem(T=16, H=256, E=8, k=2, e_lo=0, E_L=8, I=256, fp8=True)
+    wq = ml.moe_weights(256, 256, None, None, 256, 256, None, None)
+    nq = ml.workspace_bytes(pq, ml.STAGE_FFN)
+    fq = [256, 256, 256, 256, ctypes.byref(wq), None, None, 256, 256, nq, None]
+    pqc = pq.c()
+    bad = list(fq)
+    bad[1] = None
+    assert L.moe_grouped_ffn_gather(ctypes.byref(pqc), *bad) == ml.MOE_ERR_INVALID_ARG
+    bad = list(fq)
+    bad[5] = 256                # h without h_scale
+    assert L.moe_grouped_ffn_gather(ctypes.byref(pqc), *bad) == ml.MOE_ERR_INVALID_ARG
+    p0q = ml.Problem(T=0, H=256, E=8, k=2, e_lo=0, E_L=8, I=256, fp8=True).c()
+    assert L.moe_grouped_ffn_gather(ctypes.byref(p0q), *fq) == ml.MOE_OK
     # T = 0: nothing to do
     p0 = ml.Problem(T=0, H=256, E=8, k=2, e_lo=0, E_L=8, I=256).c()
     assert L.moe_grouped_ffn_gather(ctypes.byref(p0), *ok_args) == ml.MOE_OK
@@ -235,12 +248,12 @@ def test_mxfp4_checks():
     pc = ml.Problem(**base).c()
     pc.dtype = 3
     assert L.moe_route(ctypes.byref(pc), 16, 16, 16, None) == ml.MOE_ERR_INVALID_ARG
-    # the gathering FFN is bf16 only
+    # the gathering FFN takes bf16 or block-FP8 tokens, not MX
     p = ml.Problem(**base).c()
     w = ml.moe_weights(256, 256, None, None, 256, 256, None, None)
     n = ml.workspace_bytes(ml.Problem(**base), ml.STAGE_FFN)
-    assert L.moe_grouped_ffn_gather(ctypes.byref(p), 256, 256, 256, ctypes.byref(w), None, 256,
-                                    256, n, None) == ml.MOE_ERR_UNSUPPORTED
+    assert L.moe_grouped_ffn_gather(ctypes.byref(p), 256, 256, 256, 256, ctypes.byref(w), None,
+                                    None, 256, 256, n, None) == ml.MOE_ERR_UNSUPPORTED
     # moe_grouped_ffn needs the activation scales
     assert L.moe_grouped_ffn(ctypes.byref(p), 256, None, 256, ctypes.byref(w), None, None, 256,
                              256, n, None) == ml.MOE_ERR_INVALID_ARG

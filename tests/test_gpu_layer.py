@@ -239,12 +239,14 @@ def check_small_case(name, cfg, d, dev):
     np.testing.assert_array_equal(dv.bits_from_bf16(y), dv.bits_from_bf16(st["y"]))
     if not quant:
         check_panel_layouts(torch, p, d, st)
+    if not cfg.mx:
         check_gather_path(torch, p, dev, st)
 
 
 def run_gather_path(torch, p, dev, shared=None):
-    """route -> index-only dispatch -> moe_grouped_ffn_gather -> combine: the
-    bf16 kernels of moe_layer, one call each."""
+    """route -> index-only dispatch (block-FP8: and moe_quantize_fp8 of x) ->
+    moe_grouped_ffn_gather -> combine: the kernels of moe_layer, one call
+    each."""
     ml, dv = _mods()
     T, k, N = p.T, p.k, p.n_cap
     i32 = dict(dtype=torch.int32, device="cuda")
@@ -258,7 +260,12 @@ def run_gather_path(torch, p, dev, shared=None):
                     dv.workspace(p, ml.STAGE_DISPATCH))
     y_perm = torch.empty((N, p.H), dtype=torch.bfloat16, device="cuda")
     seg = counts if p.capacity else offsets
-    ml.moe_grouped_ffn_gather(p, dev["x"], row_token, seg, dv.weights_of(dev, False), None,
+    xa, xs = dev["x"], None
+    if p.fp8:
+        xa = torch.empty((T, p.H), dtype=torch.uint8, device="cuda")
+        xs = torch.empty((T, p.H // 128), dtype=torch.float32, device="cuda")
+        ml.moe_quantize_fp8(dev["x"], 1, T, p.H, 1, xa, xs)
+    ml.moe_grouped_ffn_gather(p, xa, xs, row_token, seg, dv.weights_of(dev, p.fp8), None, None,
                               y_perm, dv.workspace(p, ml.STAGE_FFN))
     y = torch.empty((T, p.H), dtype=torch.bfloat16, device="cuda")
     ml.moe_combine(p, y_perm, tsr, w, shared, y)
@@ -267,12 +274,11 @@ def run_gather_path(torch, p, dev, shared=None):
 
 
 def check_gather_path(torch, p, dev, st):
-    """moe_grouped_ffn_gather on x gives the same bits as moe_grouped_ffn on
-    the gathered x_perm (and so as moe_layer)."""
-    if p.I_s > 0:
-        return  # the shared expert is checked through the staged calls
+    """moe_grouped_ffn_gather on x (block-FP8: on x quantised once) gives the
+    same bits as moe_grouped_ffn on the gathered x_perm (and so as
+    moe_layer); the shared expert's output is the staged one."""
     say("gather path", p)
-    y = run_gather_path(torch, p, dev)
+    y = run_gather_path(torch, p, dev, st["shared"] if p.I_s > 0 else None)
     np.testing.assert_array_equal(dv_bits(y), dv_bits(st["y"]))
 
 

@@ -157,20 +157,15 @@ def main():
         sc = dict(dtype=torch.uint8, device="cuda") if cfg.mx else \
             dict(dtype=torch.float32, device="cuda")
         g = 32 if cfg.mx else 128
-        if cfg.mx:   # MX: the dispatch gathers and quantises the rows
-            xp = torch.empty((N, H), dtype=torch.uint8, device="cuda")
-            xs = torch.empty((N, H // g), **sc)
-        else:        # block-FP8: the tokens quantised once, gathered by the FFN
-            xq = torch.empty((T, H), dtype=torch.uint8, device="cuda")
-            xqs = torch.empty((T, H // g), **sc)
+        # the tokens quantised once, gathered by the FFN
+        xq = torch.empty((T, H), dtype=torch.uint8, device="cuda")
+        xqs = torch.empty((T, H // g), **sc)
         if p.I_s:
             q = ml.Problem(T=T, H=H, E=1, k=1, e_lo=0, E_L=1, I=p.I_s, fp8=cfg.fp8, mx=cfg.mx,
                            layout=wlay)
             off2 = torch.tensor([0, T], **i32)
             sw = ml.weights_struct(dev["ws13_q"], dev["ws2_q"], None, None, dev["ws13_s"],
                                    dev["ws2_s"])
-            sx, sxs = (torch.empty((T, H), dtype=torch.uint8, device="cuda"),
-                       torch.empty((T, H // g), **sc)) if cfg.mx else (xq, xqs)
             shared = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
             ws_s = dv.workspace(q, ml.STAGE_FFN)
 
@@ -179,11 +174,9 @@ def main():
     # One step: moe_layer's kernels, one library call per stage, so that the
     # grouped FFN's launches inside the timed region can be bracketed with
     # HIP events on the stream they run on.  bf16: route, index-only
-    # dispatch, the FFN gathering its rows from x, combine.  block-FP8:
-    # route, index-only dispatch and x quantised once, the FFN gathering its
-    # rows from those codes, the shared expert on them, combine.  MX: route,
-    # dispatch with quantisation, FFN, shared expert (quantise x, dense FFN),
-    # combine.
+    # dispatch, the FFN gathering its rows from x, combine.  block-FP8 and
+    # MX: route, index-only dispatch and x quantised once, the FFN gathering
+    # its rows from those codes, the shared expert on them, combine.
     def step(ev=None):
         rec = (lambda i: ev[i].record(stream)) if ev else (lambda i: None)
         rec(0)
@@ -197,25 +190,18 @@ def main():
                                       stream)
             rec(3)
             sh = None
-        elif not cfg.mx:
+        else:
             ml.moe_dispatch(p, dev["x"], ids, counts, offsets, rt, rs, tsr, None, None, ws_d,
                             stream)
-            ml.moe_quantize_fp8(dev["x"], 1, T, H, 1, xq, xqs, stream)
+            if cfg.mx:
+                ml.moe_quantize_mx(dev["x"], 1, T, H, ml.MX_E4M3, xq, xqs, stream)
+            else:
+                ml.moe_quantize_fp8(dev["x"], 1, T, H, 1, xq, xqs, stream)
             rec(2)
             ml.moe_grouped_ffn_gather(p, xq, xqs, rt, seg, W, None, None, yp, ws_f, stream)
             sh = None
             if p.I_s:
                 ml.moe_grouped_ffn(q, xq, xqs, off2, sw, None, None, shared, ws_s, stream)
-                sh = shared
-            rec(3)
-        else:
-            ml.moe_dispatch(p, dev["x"], ids, counts, offsets, rt, rs, tsr, xp, xs, ws_d, stream)
-            rec(2)
-            ml.moe_grouped_ffn(p, xp, xs, seg, W, None, None, yp, ws_f, stream)
-            sh = None
-            if p.I_s:
-                ml.moe_quantize_mx(dev["x"], 1, T, H, ml.MX_E4M3, sx, sxs, stream)
-                ml.moe_grouped_ffn(q, sx, sxs, off2, sw, None, None, shared, ws_s, stream)
                 sh = shared
             rec(3)
         ml.moe_combine(p, yp, tsr, tw, sh, y, stream)

@@ -253,12 +253,14 @@ moe_status moe_grouped_ffn(const moe_problem* p, const void* x_perm,
  * activations are never written.
  *   x [T, H] row major: bf16; for MOE_FP8_E4M3 the E4M3 codes of the
  *   tokens with x_scale [T, H/128] fp32 (moe_quantize_fp8 of the bf16
- *   tokens: a row's codes depend on that row alone, so the result has the
- *   bits of moe_grouped_ffn on moe_dispatch's x_perm); x_scale NULL for bf16.
+ *   tokens; MOE_MXFP4: the MXFP8 codes with x_scale holding E8M0 bytes
+ *   [T, H/32], moe_quantize_mx with MOE_MX_E4M3): a row's codes depend on
+ *   that row alone, so the result has the bits of moe_grouped_ffn on
+ *   moe_dispatch's x_perm; x_scale NULL for bf16.
  *   row_token [N_cap] (from moe_dispatch), offsets (counts for the masked
  *   layout), w, h and h_scale (optional, as in moe_grouped_ffn; bf16 h in
  *   the layout of MOE_LAYOUT_PANEL_ACTS), y_perm [N_cap, H] bf16 (output).
- * MOE_ERR_UNSUPPORTED for MOE_MXFP4 and for x of 2 GiB or more.
+ * MOE_ERR_UNSUPPORTED for x of 2 GiB or more.
  * Workspace: moe_workspace_bytes(p, MOE_STAGE_FFN).                        */
 moe_status moe_grouped_ffn_gather(const moe_problem* p, const void* x,
                                   const float* x_scale,

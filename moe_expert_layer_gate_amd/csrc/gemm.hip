@@ -1007,13 +1007,16 @@ __device__ __forceinline__ void mx_tile(const GemmArgs& g, uint8_t* smem) {
   const int nk = K / kMxK;
   const uint8_t* As = reinterpret_cast<const uint8_t*>(g.A_scale);
   const uint8_t* Ws = reinterpret_cast<const uint8_t*>(g.W_scale);
-  const int64_t a_skip = static_cast<int64_t>(row0) * K;
+  // with a fused gather (a_index) the token views span the whole source and
+  // each lane's offset names its row (arow: valid rows only)
+  const int64_t a_skip = g.a_index ? 0 : static_cast<int64_t>(row0) * K;
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(g.A + a_skip, g.a_bytes - a_skip);
   const __amdgpu_buffer_rsrc_t rW = make_rsrc(g.W + e * g.w_stride, g.w_stride);
   const __amdgpu_buffer_rsrc_t rAS =
-      make_rsrc(As + static_cast<int64_t>(row0) * kb, (g.a_bytes / K - row0) * kb);
+      make_rsrc(As + a_skip / K * kb, (g.a_bytes - a_skip) / K * kb);
   const __amdgpu_buffer_rsrc_t rWS = make_rsrc(Ws + e * g.ws_stride, g.ws_stride);
   const int nbase = kSwiglu ? nt * (kMxBN / 2) : nt * kMxBN;
+  auto arow = [&](int rr) { return g.a_index ? g.a_index[row0 + rr] : rr; };
   auto wrow = [&](int r) {  // weight row (within the expert) of tile row r
     if (kSwiglu)
       return r < kMxBN / 2 ? min(nbase + r, g.Nout - 1)
@@ -1033,7 +1036,7 @@ __device__ __forceinline__ void mx_tile(const GemmArgs& g, uint8_t* smem) {
   for (int q = 0; q < TL; ++q) {
     const int rr = (w * TL + q) * 8 + (lane >> 3);
     const int c = (lane & 7) ^ ((rr >> 1) & 7);
-    voff[q] = row0 + rr < seg_end ? rr * K + c * 16 : kOobOffset;
+    voff[q] = row0 + rr < seg_end ? arow(rr) * K + c * 16 : kOobOffset;
   }
 #pragma unroll
   for (int q = 0; q < WL; ++q) {
@@ -1046,14 +1049,14 @@ __device__ __forceinline__ void mx_tile(const GemmArgs& g, uint8_t* smem) {
   if constexpr (kMxBM == 128) {
     voff[TL + WL] = wrow(w * 64 + lane) * g.ws_rs;
     const int rr = (w & 1) * 64 + lane;
-    voff[TL + WL + 1] = row0 + rr < seg_end ? rr * kb : kOobOffset;
+    voff[TL + WL + 1] = row0 + rr < seg_end ? arow(rr) * kb : kOobOffset;
     s_tok = false;
     s_lds = 0;
   } else {
     s_tok = w < 4;
     if (s_tok) {
       const int rr = w * 64 + lane;
-      voff[TL + WL] = row0 + rr < seg_end ? rr * kb : kOobOffset;
+      voff[TL + WL] = row0 + rr < seg_end ? arow(rr) * kb : kOobOffset;
       s_lds = kMxSAOff + w * 256;
     } else {
       voff[TL + WL] = wrow((w - 4) * 64 + lane) * g.ws_rs;
@@ -1268,13 +1271,16 @@ __device__ __forceinline__ void mx_skinny_tile(const GemmArgs& g, int t, uint8_t
   const int K = g.K, kb = K / 32, nk = K / kMxK;
   const uint8_t* As = reinterpret_cast<const uint8_t*>(g.A_scale);
   const uint8_t* Ws = reinterpret_cast<const uint8_t*>(g.W_scale);
-  const int64_t a_skip = static_cast<int64_t>(row0) * K;
+  // with a fused gather (a_index) the token views span the whole source and
+  // each lane's offset names its row (arow: valid rows only)
+  const int64_t a_skip = g.a_index ? 0 : static_cast<int64_t>(row0) * K;
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(g.A + a_skip, g.a_bytes - a_skip);
   const __amdgpu_buffer_rsrc_t rW = make_rsrc(g.W + e * g.w_stride, g.w_stride);
   const __amdgpu_buffer_rsrc_t rAS =
-      make_rsrc(As + static_cast<int64_t>(row0) * kb, (g.a_bytes / K - row0) * kb);
+      make_rsrc(As + a_skip / K * kb, (g.a_bytes - a_skip) / K * kb);
   const __amdgpu_buffer_rsrc_t rWS = make_rsrc(Ws + e * g.ws_stride, g.ws_stride);
   const int nbase = kSwiglu ? nt * (kMxBN / 2) : nt * kMxBN;
+  auto arow = [&](int rr) { return g.a_index ? g.a_index[row0 + rr] : rr; };
   auto wrow = [&](int r) {  // weight row (within the expert) of tile row r
     if (kSwiglu)
       return r < kMxBN / 2 ? min(nbase + r, g.Nout - 1)
@@ -1287,7 +1293,7 @@ __device__ __forceinline__ void mx_skinny_tile(const GemmArgs& g, int t, uint8_t
   {
     const int rr = w * 8 + (lane >> 3);
     const int c = (lane & 7) ^ ((rr >> 1) & 7);
-    voff[0] = row0 + rr < seg_end ? rr * K + c * 16 : kOobOffset;
+    voff[0] = row0 + rr < seg_end ? arow(rr) * K + c * 16 : kOobOffset;
   }
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -1296,7 +1302,7 @@ __device__ __forceinline__ void mx_skinny_tile(const GemmArgs& g, int t, uint8_t
     voff[1 + q] = wrow(r) * g.w_rs + cw * 16;
   }
   voff[5] = wrow(w * 64 + lane) * g.ws_rs;
-  voff[6] = lane < kMsBM && row0 + lane < seg_end ? lane * kb : kOobOffset;
+  voff[6] = lane < kMsBM && row0 + lane < seg_end ? arow(lane) * kb : kOobOffset;
   auto dma = [&](int step, int stage) {
     // steps past the last one load nothing (out-of-range offsets)
     const bool live = step < nk;
@@ -2256,11 +2262,11 @@ hipError_t launch_schedule(const int32_t* seg, int seg_cap, int E_L, GemmPath pa
 // Kernel arguments of one grouped GEMM; hipErrorInvalidValue for requests the
 // kernels cannot address.
 static hipError_t make_args(const GemmLaunch& L, GemmArgs& g) {
-  // The fused gather reads bf16 or E4M3 row-major sources whose lane
-  // offsets fit below the buffer cap (not MX).
+  // The fused gather reads bf16 or E4M3 (block-FP8, MXFP8) row-major
+  // sources whose lane offsets fit below the buffer cap.
   static_assert(kGemmGatherMaxBytes <= kBufMax, "gather offsets must stay below the range cap");
   if (L.a_index &&
-      (L.mx || L.a_panel || L.a_rows * (L.fp8 ? 1 : 2) * L.K > kGemmGatherMaxBytes))
+      (L.a_panel || L.a_rows * (L.fp8 || L.mx ? 1 : 2) * L.K > kGemmGatherMaxBytes))
     return hipErrorInvalidValue;
   g = GemmArgs{};
   g.A = static_cast<const uint8_t*>(L.A);
@@ -2281,7 +2287,7 @@ static hipError_t make_args(const GemmLaunch& L, GemmArgs& g) {
     return hipErrorInvalidValue;
   if (L.mx) {  // E4M3 tokens, E2M1 weights, E8M0 bytes per 32 along K; tokens row
                // major, weights row major or in 128-element panels
-    if (L.fp8 || L.a_panel || L.c_panel || L.a_index || L.gelu || L.K % kMxK)
+    if (L.fp8 || L.a_panel || L.c_panel || L.gelu || L.K % kMxK)
       return hipErrorInvalidValue;
     if (L.swiglu && !L.C_scale) return hipErrorInvalidValue;
     g.w_stride = static_cast<int64_t>(g.NW) * (L.K / 2);
@@ -2293,6 +2299,7 @@ static hipError_t make_args(const GemmLaunch& L, GemmArgs& g) {
     g.ws_rs = L.w_panel ? 4 : L.K / 32;
     g.ws_cs = L.w_panel ? 4 * g.NW : 4;
     g.a_bytes = L.a_rows * L.K;
+    g.a_index = L.a_index;
     return hipSuccess;
   }
   const int64_t elem = L.fp8 ? 1 : 2;

@@ -108,10 +108,10 @@ struct Carve {
 // Fused gather of bf16 sources whose byte size fits the GEMM's 32-bit lane
 // offsets.
 // The up GEMM can read its rows from the unpermuted tokens (bf16, or the
-// E4M3 codes of block-FP8) through row_token.
+// E4M3 codes of block-FP8 or MXFP8) through row_token.
 bool can_fuse_gather(const moe_problem* p) {
-  return !is_mx(p) && static_cast<int64_t>(p->num_tokens) * p->hidden * (is_fp8(p) ? 1 : 2) <=
-                          kGemmGatherMaxBytes;
+  return static_cast<int64_t>(p->num_tokens) * p->hidden * (quant_acts(p) ? 1 : 2) <=
+         kGemmGatherMaxBytes;
 }
 
 struct FfnScratch {
@@ -186,7 +186,7 @@ struct LayerScratch {
   void* x_perm;
   float* x_perm_scale;
   void* xq;          // block-FP8 with the fused gather: the tokens quantised
-  float* xq_scale;   // once, [T, H] codes and [T, H/128] scales
+  float* xq_scale;   // once, [T, H] codes and their scales
   void* y_perm;
   void* index_scratch;
   FfnScratch ffn;
@@ -222,11 +222,11 @@ LayerScratch carve_layer(Carve& c, const moe_problem* p) {
   s.row_slot = c.take<int32_t>(4 * N);
   s.tsr = c.take<int32_t>(4 * T * k);
   // x_perm only where the up GEMM does not gather from the tokens itself;
-  // block-FP8 gathers from the tokens quantised once
+  // block-FP8 and MX gather from the tokens quantised once
   const bool fuse = can_fuse_gather(p);
   s.x_perm = fuse ? nullptr : c.take<void>((quant_acts(p) ? 1 : 2) * N * H);
   s.x_perm_scale = quant_acts(p) && !fuse ? c.take<float>(act_scale_bytes(p, N, H)) : nullptr;
-  if (fuse && is_fp8(p)) {
+  if (fuse && quant_acts(p)) {
     s.xq = c.take<void>(T * H);
     s.xq_scale = c.take<float>(act_scale_bytes(p, T, H));
   }
@@ -520,9 +520,8 @@ moe_status enqueue_layer(const moe_problem* p, const float* logits, const void* 
   const moe_problem pi = layer_internal(p);
 
   // The up GEMM gathers its rows from the tokens through row_token, so the
-  // permuted activations are never written: bf16 from x, block-FP8 from x
-  // quantised once (which the shared expert reads too); MX gathers and
-  // quantises in the dispatch.
+  // permuted activations are never written: bf16 from x, block-FP8 and MX
+  // from x quantised once (which the shared expert reads too).
   const bool fuse = can_fuse_gather(p);
   MOE_TRY(launch_route_topk(logits, T, p->num_experts, p->top_k, L.ids, L.w, s));
   st = run_dispatch(&pi, x, L.ids, L.counts, L.offsets, L.row_token, L.row_slot, L.tsr,
@@ -530,8 +529,12 @@ moe_status enqueue_layer(const moe_problem* p, const float* logits, const void* 
   if (st != MOE_OK) return st;
   const void* xa = x;
   const float* xa_scale = nullptr;
-  if (fuse && is_fp8(p)) {
+  if (fuse && is_fp8(p))
     MOE_TRY(launch_gather_fp8(x, nullptr, nullptr, T, p->hidden, L.xq, L.xq_scale, s));
+  else if (fuse && is_mx(p))
+    MOE_TRY(launch_gather_mx8(x, nullptr, nullptr, T, p->hidden, L.xq,
+                              reinterpret_cast<uint8_t*>(L.xq_scale), s));
+  if (fuse && quant_acts(p)) {
     xa = L.xq;
     xa_scale = L.xq_scale;
   }
@@ -552,14 +555,14 @@ moe_status enqueue_layer(const moe_problem* p, const float* logits, const void* 
     MOE_TRY(hipGetLastError());
     const void* sx = x;
     const float* sx_scale = nullptr;
-    if (is_mx(p)) {
+    if (L.xq) {
+      sx = L.xq;
+      sx_scale = L.xq_scale;
+    } else if (is_mx(p)) {
       MOE_TRY(launch_gather_mx8(x, nullptr, nullptr, T, p->hidden, L.s_x,
                                 reinterpret_cast<uint8_t*>(L.s_x_scale), s));
       sx = L.s_x;
       sx_scale = L.s_x_scale;
-    } else if (is_fp8(p) && L.xq) {
-      sx = L.xq;
-      sx_scale = L.xq_scale;
     } else if (is_fp8(p)) {
       MOE_TRY(launch_gather_fp8(x, nullptr, nullptr, T, p->hidden, L.s_x, L.s_x_scale, s));
       sx = L.s_x;

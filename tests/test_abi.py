@@ -248,12 +248,12 @@ def test_mxfp4_checks():
     pc = ml.Problem(**base).c()
     pc.dtype = 3
     assert L.moe_route(ctypes.byref(pc), 16, 16, 16, None) == ml.MOE_ERR_INVALID_ARG
-    # the gathering FFN takes bf16 or block-FP8 tokens, not MX
+    # the gathering FFN needs the MX token scales
     p = ml.Problem(**base).c()
     w = ml.moe_weights(256, 256, None, None, 256, 256, None, None)
     n = ml.workspace_bytes(ml.Problem(**base), ml.STAGE_FFN)
-    assert L.moe_grouped_ffn_gather(ctypes.byref(p), 256, 256, 256, 256, ctypes.byref(w), None,
-                                    None, 256, 256, n, None) == ml.MOE_ERR_UNSUPPORTED
+    assert L.moe_grouped_ffn_gather(ctypes.byref(p), 256, None, 256, 256, ctypes.byref(w), None,
+                                    None, 256, 256, n, None) == ml.MOE_ERR_INVALID_ARG
     # moe_grouped_ffn needs the activation scales
     assert L.moe_grouped_ffn(ctypes.byref(p), 256, None, 256, ctypes.byref(w), None, None, 256,
                              256, n, None) == ml.MOE_ERR_INVALID_ARG

@@ -239,12 +239,11 @@ def check_small_case(name, cfg, d, dev):
     np.testing.assert_array_equal(dv.bits_from_bf16(y), dv.bits_from_bf16(st["y"]))
     if not quant:
         check_panel_layouts(torch, p, d, st)
-    if not cfg.mx:
-        check_gather_path(torch, p, dev, st)
+    check_gather_path(torch, p, dev, st)
 
 
 def run_gather_path(torch, p, dev, shared=None):
-    """route -> index-only dispatch (block-FP8: and moe_quantize_fp8 of x) ->
+    """route -> index-only dispatch (block-FP8, MX: and x quantised once) ->
     moe_grouped_ffn_gather -> combine: the kernels of moe_layer, one call
     each."""
     ml, dv = _mods()
@@ -265,8 +264,12 @@ def run_gather_path(torch, p, dev, shared=None):
         xa = torch.empty((T, p.H), dtype=torch.uint8, device="cuda")
         xs = torch.empty((T, p.H // 128), dtype=torch.float32, device="cuda")
         ml.moe_quantize_fp8(dev["x"], 1, T, p.H, 1, xa, xs)
-    ml.moe_grouped_ffn_gather(p, xa, xs, row_token, seg, dv.weights_of(dev, p.fp8), None, None,
-                              y_perm, dv.workspace(p, ml.STAGE_FFN))
+    elif p.mx:
+        xa = torch.empty((T, p.H), dtype=torch.uint8, device="cuda")
+        xs = torch.empty((T, p.H // 32), dtype=torch.uint8, device="cuda")
+        ml.moe_quantize_mx(dev["x"], 1, T, p.H, ml.MX_E4M3, xa, xs)
+    ml.moe_grouped_ffn_gather(p, xa, xs, row_token, seg, dv.weights_of(dev, p.fp8 or p.mx), None,
+                              None, y_perm, dv.workspace(p, ml.STAGE_FFN))
     y = torch.empty((T, p.H), dtype=torch.bfloat16, device="cuda")
     ml.moe_combine(p, y_perm, tsr, w, shared, y)
     torch.cuda.synchronize()
@@ -274,7 +277,7 @@ def run_gather_path(torch, p, dev, shared=None):
 
 
 def check_gather_path(torch, p, dev, st):
-    """moe_grouped_ffn_gather on x (block-FP8: on x quantised once) gives the
+    """moe_grouped_ffn_gather on x (block-FP8, MX: on x quantised once) gives the
     same bits as moe_grouped_ffn on the gathered x_perm (and so as
     moe_layer); the shared expert's output is the staged one."""
     say("gather path", p)

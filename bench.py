@@ -2,16 +2,22 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
+Default workload: the DeepSeek-V3-shaped shard of an 8-way expert-parallel
+layer (16384 tokens, hidden 7168, 32 of 256 experts local, top-8,
+intermediate 2048, bf16), the largest configuration that runs on one GPU.
+
 One step is one pass of the layer -- route, dispatch, grouped SwiGLU FFN (and
 shared expert), combine -- over one batch of the workload, with inputs
-already resident in HBM, issued as moe_layer's kernels one library call per
-stage so that the grouped FFN's launches in the timed region are bracketed by
-HIP events on their stream (the line also reports the one-call moe_layer's
-throughput and that it gives the same output bits).  Prints ONE JSON line:
-MoE-layer tokens/s as `value`, the grouped FFN's TFLOP/s against the MFMA
-peak (or, for the decode workload, its bytes/s against HBM) as `roofline`,
-and the CPU oracle on a bounded sample of the same workload as
-`cpu_baseline`.
+already resident in HBM.  The timed region is K calls of the one-call
+moe_layer between two synchronisations; `value` is tokens x K / wall time,
+and HIP events around each call give the per-step median, min and mean.
+The same kernels are then issued one library call per stage, so that the
+grouped FFN's launches can be bracketed by HIP events on their stream: that
+gives `stage_ms`, the small stages' GB/s, and the grouped FFN's TFLOP/s
+against the MFMA peak (or, for few rows per expert, its bytes/s against HBM)
+as `roofline`.  Prints ONE JSON line, with the GPU's clock and power under
+load, the host, and the CPU oracle on a bounded sample of the same workload
+as `cpu_baseline`.
 """
 from __future__ import annotations
 
@@ -35,7 +41,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="qwen3_30b_prefill")
+    ap.add_argument("--workload", default="dsv3_ep8_prefill")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--cpu-sample-tokens", type=int, default=None,
                     help="tokens of the workload the CPU oracle runs on (0 = skip)")
@@ -207,39 +213,51 @@ def main():
         ml.moe_combine(p, yp, tsr, tw, sh, y, stream)
         rec(4)
 
+    # ---- the headline: the one-call moe_layer, K calls between two
+    # synchronisations, each bracketed by HIP events on its stream ----
+    ws_l = dv.workspace(p_layer)
+    y_l = torch.empty_like(y)
+
+    def layer():
+        ml.moe_layer(p_layer, dev["logits"], dev["x"], W, y_l, ws_l, stream)
+
     for _ in range(args.warmup):
-        step()
+        layer()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    lev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(evs[i])
+        lev[i].record(stream)
+        layer()
+    lev[args.steps].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
     tokens_per_s = T * args.steps / elapsed
+    layer_ms = [lev[i].elapsed_time(lev[i + 1]) for i in range(args.steps)]
+
+    # ---- the same kernels one library call per stage, so that the grouped
+    # FFN's launches can be bracketed by events on their stream ----
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    t1 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    staged_tps = T * args.steps / (time.perf_counter() - t1)
     names = ("route", "dispatch", "grouped_ffn", "combine")
     per = {n: [e[i].elapsed_time(e[i + 1]) for e in evs] for i, n in enumerate(names)}
     stage_ms = {n: float(np.median(v)) for n, v in per.items()}
-    ffn_ms = float(np.mean(per["grouped_ffn"]))   # the FFN launches of the timed region
-
-    # The same work through the one-call moe_layer: same output bits, and its
-    # own throughput for reference.
+    ffn_ms = float(np.mean(per["grouped_ffn"]))   # the FFN launches of the timed steps
     y_steps = y.clone()
-    ws_l = dv.workspace(p_layer)
-    y_l = torch.empty_like(y)
-    ml.moe_layer(p_layer, dev["logits"], dev["x"], W, y_l, ws_l, stream)
-    torch.cuda.synchronize()
     same = bool(torch.equal(y_l.view(torch.int16), y_steps.view(torch.int16)))
-    t1 = time.perf_counter()
-    for _ in range(args.steps):
-        ml.moe_layer(p_layer, dev["logits"], dev["x"], W, y_l, ws_l, stream)
-    torch.cuda.synchronize()
-    layer_tps = T * args.steps / (time.perf_counter() - t1)
 
     # The one-call layer captured once in a HIP graph and replayed K times
     # (how a serving loop replays a step): no per-launch host work.  Same
-    # output bits as the calls above.
+    # output bits as the calls above.  The clock and power of the GPU are
+    # sampled while it replays.
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         ml.moe_layer(p_layer, dev["logits"], dev["x"], W, y_l, ws_l)
@@ -256,6 +274,7 @@ def main():
         graph.replay()
     torch.cuda.synchronize()
     graph_tps = T * args.steps / (time.perf_counter() - t2)
+    gpu = gpu_under_load(lambda: graph.replay(), float(np.median(layer_ms)))
 
     cnt = counts.cpu().numpy()
     n_pairs = int(cnt.sum())
@@ -269,6 +288,19 @@ def main():
     active = int((cnt > 0).sum())
     ffn_tflops = flops / (ffn_ms * 1e-3) / 1e12
     padded_rows = gemm_rows(cnt, quant, p.T * min(p.k, p.E_L), p.E_L, cfg.mx)
+
+    # HBM bytes of the small stages (what each must move at least) and their
+    # rates over the stage's median time: route T E 4 + T k 8; dispatch (the
+    # index build: ids in, row_token / row_slot / token_slot_row out, T k 16;
+    # quantised paths also read x once and write its codes and scales);
+    # combine N H 2 + T H 2 (+ the shared expert's T H 2) + T k 8.
+    a_scale = (1 / 32 if cfg.mx else 4 / 128) if quant else 0
+    stage_bytes = {
+        "route": p.T * p.E * 4 + p.T * p.k * 8,
+        "dispatch": p.T * p.k * 16 + (p.T * p.H * (2 + 1 + a_scale) if quant else 0),
+        "combine": n_pairs * p.H * 2 + p.T * p.H * 2 * (2 if p.I_s else 1) + p.T * p.k * 8,
+    }
+    stage_rates = {n: round(b / (stage_ms[n] * 1e-3) / 1e9, 1) for n, b in stage_bytes.items()}
 
     traffic = stored_traffic(cfg.name + ("_masked" if cap else ""))
     act = "SwiGLU" if cfg.act == "swiglu" else "GELU"
@@ -299,9 +331,10 @@ def main():
     cpu = None
     sample = args.cpu_sample_tokens
     if sample is None:
-        sample = {"tiny": 256, "qwen3_30b_prefill": 4096, "dsv3_ep8_prefill": 128,
-                  "dsv3_ep8_prefill_fp8": 64, "dsv3_ep8_decode": 64,
-                  "dsv3_ep8_prefill_mxfp4": 64, "dsv3_ep8_decode_mxfp4": 64,
+        # about 10-30 s of CPU work
+        sample = {"tiny": 256, "qwen3_30b_prefill": 8192, "dsv3_ep8_prefill": 4096,
+                  "dsv3_ep8_prefill_fp8": 2048, "dsv3_ep8_decode": 64,
+                  "dsv3_ep8_prefill_mxfp4": 2048, "dsv3_ep8_decode_mxfp4": 64,
                   "dsv3_ep8_decode_fp8": 64}.get(cfg.name, 256)
     if sample > 0:
         cpu = cpu_baseline(cfg, d, sample)
@@ -327,9 +360,17 @@ def main():
                    "expert_layout": f"masked (capacity {cap})" if cap else "contiguous"},
         "grouped_ffn_tflops": round(ffn_tflops, 2),
         "grouped_ffn_frac_of_peak": round(ffn_tflops / PEAK_TFLOPS[dtype], 4),
+        "timed": "moe_layer, one call per step; value = tokens x steps / wall time "
+                 "between synchronisations",
+        "step_ms": {"median": round(float(np.median(layer_ms)), 4),
+                    "min": round(float(np.min(layer_ms)), 4),
+                    "mean": round(float(np.mean(layer_ms)), 4)},
         "stage_ms": {k2: round(v, 4) for k2, v in stage_ms.items()},
-        "moe_layer_call": {"tokens_per_s": round(layer_tps, 1), "same_output_bits": same},
+        "stage_gbs": stage_rates,
+        "staged_calls": {"tokens_per_s": round(staged_tps, 1), "same_output_bits": same},
         "moe_layer_graph": {"tokens_per_s": round(graph_tps, 1), "same_output_bits": same_graph},
+        "gpu": gpu,
+        "host": host_info(),
         "routing": {"local_pairs": n_pairs, "active_experts": active,
                     "rows_per_expert_max": int(cnt.max()), "rows_per_expert_mean": round(float(cnt.mean()), 1),
                     "gemm_rows_computed": padded_rows,
@@ -346,6 +387,77 @@ def main():
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
+
+
+def host_info():
+    """The host the CPU baseline runs on: logical CPUs, those this process
+    may use, and the CPU model."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"nproc": len(os.sched_getaffinity(0)), "cpu_count": os.cpu_count(),
+            "cpu_model": model}
+
+
+def _smi(args):
+    """rocm-smi's JSON for the first card, or None."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", *args, "--json"], capture_output=True, text=True,
+                           timeout=30)
+        d = json.loads(r.stdout[r.stdout.index("{"):])
+        return next(iter(d.values()))
+    except Exception:
+        return None
+
+
+def _num(v):
+    import re
+    m = re.search(r"[-+]?[0-9]*\.?[0-9]+", str(v))
+    return float(m.group(0)) if m else None
+
+
+def gpu_under_load(replay, step_ms):
+    """The GPU's name, power cap, and its graphics clock and socket power
+    sampled by rocm-smi while `replay` keeps it busy (about two seconds of
+    replays)."""
+    import threading
+
+    import torch
+    props = torch.cuda.get_device_properties(0)
+    out = {"name": props.name, "arch": getattr(props, "gcnArchName", None),
+           "compute_units": props.multi_processor_count, "power_cap_w": None,
+           "sclk_mhz_under_load": None, "power_w_under_load": None}
+    cap = _smi(["--showmaxpower"])
+    if cap:
+        out["power_cap_w"] = next((_num(v) for k, v in cap.items() if "Max" in k and "Power" in k),
+                                  None)
+    sample = {}
+
+    def probe():
+        time.sleep(0.5)
+        sample.update(_smi(["--showclocks", "--showpower"]) or {})
+
+    th = threading.Thread(target=probe)
+    th.start()
+    t_end = time.perf_counter() + 2.5
+    n = max(1, int(50.0 / max(step_ms, 1e-3)))      # ~50 ms of GPU work per batch
+    while th.is_alive() and time.perf_counter() < t_end + 30:
+        for _ in range(n):
+            replay()
+        torch.cuda.synchronize()
+    th.join()
+    for k, v in sample.items():
+        if "sclk" in k and "speed" in k:
+            out["sclk_mhz_under_load"] = _num(v)
+        if "Power" in k and "Max" not in k:
+            out["power_w_under_load"] = _num(v)
+    return out
 
 
 def _time_ms(fn, reps):
@@ -466,12 +578,15 @@ def cpu_baseline(cfg, d, sample):
     """The oracle, as it stands, on the first `sample` tokens."""
     import numpy as np
 
+    from threadpoolctl import threadpool_info, threadpool_limits
+
     from oracle import moe_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+    # every CPU this process may use (the host's share of the GPU box), capped
+    # by OMP_NUM_THREADS where the environment sets one
+    ncpu = len(os.sched_getaffinity(0))
+    want = min(ncpu, int(os.environ.get("OMP_NUM_THREADS", ncpu) or ncpu))
+    limiter = threadpool_limits(limits=want)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     T = min(sample, cfg.T)
     wd = d
     if cfg.mx:
@@ -496,9 +611,12 @@ def cpu_baseline(cfg, d, sample):
     O.moe_layer(d["logits"][:T], d["x"][:T], wd, k=cfg.k, e_lo=cfg.e_lo, E_L=cfg.E_L, fp8=cfg.fp8,
                 mx=cfg.mx)
     dt = time.perf_counter() - t0
+    limiter.restore_original_limits()
+    host = host_info()
     return {"value": round(T / dt, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {T} of {cfg.T} tokens of {cfg.name}, whole layer (float64 numpy), "
-                      f"{dt:.1f} s"}
+            "sample": f"first {T} of {cfg.T} tokens of {cfg.name}, whole layer (float64 numpy, "
+                      f"BLAS on {threads} threads), {dt:.1f} s",
+            "nproc": host["nproc"], "cpu_model": host["cpu_model"]}
 
 
 if __name__ == "__main__":

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 8
+#define MOE_ABI_VERSION 9
 
 typedef enum {
   MOE_OK = 0,
@@ -162,16 +162,17 @@ typedef struct {
  * MOE_MXFP4: the scale pointers carry E8M0 bytes (uint8, value 2^(e-127)),
  * one per 32 K elements of a row: w13_scale [E_L, 2I, H/32], w2_scale
  * [E_L, H, I/32], ws13_scale [2 I_s, H/32], ws2_scale [H, I_s/32] (see
- * moe_quantize_mx).                                                        */
+ * moe_quantize_mx).  The scale pointers are untyped for that reason: fp32
+ * (float*) for MOE_FP8_E4M3, bytes (uint8_t*) for MOE_MXFP4.               */
 typedef struct {
   const void* w13;
   const void* w2;
   const void* ws13;
   const void* ws2;
-  const float* w13_scale;
-  const float* w2_scale;
-  const float* ws13_scale;
-  const float* ws2_scale;
+  const void* w13_scale;
+  const void* w2_scale;
+  const void* ws13_scale;
+  const void* ws2_scale;
 } moe_weights;
 
 /* Top-k gate.  Page "OverlapAdvisor ...", section 2.1 (top-k experts per
@@ -394,6 +395,29 @@ moe_status moe_layer_streamed(const moe_problem* p, const float* logits,
 
 /* Bytes of workspace a stage needs for problem p (0 if p is invalid). */
 size_t moe_workspace_bytes(const moe_problem* p, int32_t stage);
+
+/* Flags of the last grouped FFN run on a workspace (bits, 0 = none).
+ *   MOE_FLAG_WAIT_TIMEOUT: in the one-launch decode FFN (the masked-layout
+ *   and few-rows-per-expert path, where a down tile waits for the up tiles of
+ *   its rows: page "OverlapAdvisor ...", Table 7, fused
+ *   GroupGEMM + Act + GroupGEMM), a down tile's bounded wait gave up and the
+ *   tile was skipped: y_perm (and so y) of that call is incomplete.  The
+ *   ordering of the launch makes every wait end, so this flag reports a
+ *   broken assumption (for instance a scheduler that runs a later block
+ *   while an earlier one never starts); a test forces it by setting the
+ *   environment variable MOE_TEST_FUSED_WAIT_UNREACHABLE=1 before the call.
+ * Every moe_grouped_ffn / moe_grouped_ffn_gather / moe_layer call clears its
+ * workspace's flags when its FFN starts, so the flags describe the most
+ * recent call on that workspace (moe_layer: its routed and shared FFNs).
+ * moe_workspace_flags enqueues on `stream` a one-thread kernel that writes
+ * the flags of workspace ws (as used with problem p by the calls of `stage`,
+ * MOE_STAGE_LAYER or MOE_STAGE_FFN) to *flags (a device int32, 16-byte
+ * aligned); read it after the stream has reached that point.  It reports
+ * nothing about moe_layer_streamed's per-stream slices.
+ * MOE_OK, or MOE_ERR_INVALID_ARG / MOE_ERR_WORKSPACE (nothing enqueued).   */
+#define MOE_FLAG_WAIT_TIMEOUT 1
+moe_status moe_workspace_flags(const moe_problem* p, int32_t stage, const void* ws,
+                               size_t ws_bytes, int32_t* flags, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* moe_status_str(moe_status s);

@@ -111,9 +111,11 @@ __device__ __forceinline__ int2 segment(const int32_t* seg, int cap, int e) {
 
 // sync (fused FFN only): sync[0] is the launch's ticket counter and
 // sync[1 + i] the count of up tiles finished for m-tile i; both start at 0.
+// status (may be null): the FFN's flag word, cleared for the launch that
+// follows.
 __global__ __launch_bounds__(1024) void tile_schedule_kernel(
     const int32_t* __restrict__ seg, int seg_cap, int E_L, int tile_m, int4* __restrict__ info,
-    int32_t* __restrict__ n_tiles, int32_t* __restrict__ sync) {
+    int32_t* __restrict__ n_tiles, int32_t* __restrict__ sync, int32_t* __restrict__ status) {
   const int e = threadIdx.x;
   int cnt = 0;
   if (e < E_L) {
@@ -131,6 +133,7 @@ __global__ __launch_bounds__(1024) void tile_schedule_kernel(
   if (e == 0) {
     *n_tiles = total;
     if (sync) sync[0] = 0;
+    if (status) *status = 0;
   }
 }
 
@@ -1447,10 +1450,15 @@ __device__ __forceinline__ void mx_skinny_tile(const GemmArgs& g, int t, uint8_t
 //  FFN 35 % (0.548 against 0.403 ms for the DeepSeek-V3 decode batch).
 // Tickets are taken in order and every up ticket precedes every down ticket,
 // so a down tile waits only on up tiles that blocks already running hold,
-// and up tiles wait on nothing: every wait ends.  (The wait is still bounded;
-// past the bound the tile proceeds, which can only happen if that argument
-// failed.)  The grid has a block for every possible ticket; blocks whose
-// ticket is past the live work return at once.
+// and up tiles wait on nothing: every wait ends.  The wait is still bounded:
+// a down tile whose m-tile is not complete after spin_limit polls (which can
+// only happen if that argument failed) sets kFlagWaitTimeout in the FFN's
+// status word and skips its tile, so the kernel always ends and the caller
+// learns that the output is incomplete.  wait_extra raises the count a down
+// tile waits for (0 in normal use; a count no up tile can reach lets a test
+// drive every down tile into the timeout with every kernel still ending).
+// The grid has a block for every possible ticket; blocks whose ticket is past
+// the live work return at once.
 // ---------------------------------------------------------------------------
 constexpr int kSpinLimit = 1 << 22;  // about half a second of s_sleep 2 polls
 
@@ -1458,11 +1466,11 @@ constexpr int kSpinLimit = 1 << 22;  // about half a second of s_sleep 2 polls
 // weights, MXFP8 tokens and h) or kSkFp8 (block-FP8).
 enum { kSkBf16 = 0, kSkMx = 1, kSkFp8 = 2 };
 template <int UPMODE, int KIND>
-__global__ __launch_bounds__(kSkThreads, 1) void ffn_fused_skinny_kernel(const GemmArgs gu,
-                                                                        const GemmArgs gd,
-                                                                        int32_t* sync) {
+__global__ __launch_bounds__(kSkThreads, 1) void ffn_fused_skinny_kernel(
+    const GemmArgs gu, const GemmArgs gd, int32_t* sync, int32_t* status, int wait_extra,
+    int spin_limit) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
-  __shared__ int s_ticket;
+  __shared__ int s_ticket, s_ready;
   const int n_m = *gu.n_tiles;  // live m-tiles (one table for both GEMMs)
   const int n_up = n_m * gu.nt_n, total = n_up + n_m * gd.nt_n;
   if (threadIdx.x == 0) s_ticket = atomicAdd(sync, 1);
@@ -1488,13 +1496,22 @@ __global__ __launch_bounds__(kSkThreads, 1) void ffn_fused_skinny_kernel(const G
   const int td = t - n_up;
   if (threadIdx.x == 0) {
     const int32_t* c = done + skinny_decode(gd, td).w;
-    for (int it = 0; it < kSpinLimit; ++it) {
-      if (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= gu.nt_n) break;
+    const int need = gu.nt_n + wait_extra;
+    int ready = 0;
+    for (int it = 0;; ++it) {
+      if (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need) {
+        ready = 1;
+        break;
+      }
+      if (it >= spin_limit) break;
       __builtin_amdgcn_s_sleep(2);
     }
+    if (!ready) atomicOr(status, kFlagWaitTimeout);
+    s_ready = ready;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
+  if (!s_ready) return;  // reported through the status word
   if constexpr (KIND == kSkMx)
     mx_skinny_tile<MODE_PLAIN>(gd, td, smem);
   else if constexpr (KIND == kSkFp8)
@@ -1505,7 +1522,7 @@ __global__ __launch_bounds__(kSkThreads, 1) void ffn_fused_skinny_kernel(const G
 
 template <int UPMODE, int KIND>
 hipError_t launch_fused(const GemmArgs& gu, const GemmArgs& gd, int64_t max_tiles, int32_t* sync,
-                        hipStream_t s) {
+                        int32_t* status, hipStream_t s) {
   static_assert(kSkStages * kSkStageBytes <= 160 * 1024, "the ring fits the CU's LDS");
   auto kern = ffn_fused_skinny_kernel<UPMODE, KIND>;
   const size_t lds = KIND == kSkMx    ? kMsStages * kMsStageBytes
@@ -1514,8 +1531,15 @@ hipError_t launch_fused(const GemmArgs& gu, const GemmArgs& gd, int64_t max_tile
   static std::atomic<uint64_t> lds_set{0};
   allow_dynamic_lds(reinterpret_cast<const void*>(kern), static_cast<int>(lds), lds_set);
   const int64_t blocks = max_tiles * (gu.nt_n + gd.nt_n);
+  // A test drives every down tile into the bounded wait's timeout by setting
+  // MOE_TEST_FUSED_WAIT_UNREACHABLE=1: the down tiles then wait for one more
+  // up tile than exists, for a few polls only (every kernel still ends).
+  const char* unreachable = getenv("MOE_TEST_FUSED_WAIT_UNREACHABLE");
+  const bool test_timeout = unreachable && unreachable[0] == '1';
+  const int wait_extra = test_timeout ? 1 : 0;
+  const int spin_limit = test_timeout ? 16 : kSpinLimit;
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(kSkThreads), lds, s, gu, gd,
-                     sync);
+                     sync, status, wait_extra, spin_limit);
   return hipGetLastError();
 }
 
@@ -1605,7 +1629,7 @@ __device__ __forceinline__ void write_units(const int* s_start, const int* s_off
 __global__ __launch_bounds__(1024) void unit_schedule_kernel(
     const int32_t* __restrict__ seg, int seg_cap, int E_L, int nt_a, int nt_b, int bm, bool allow_wide,
     int4* __restrict__ units_a, int32_t* __restrict__ n_a, int4* __restrict__ units_b,
-    int32_t* __restrict__ n_b) {
+    int32_t* __restrict__ n_b, int32_t* __restrict__ status) {
   __shared__ int s_off[1024], s_full[1024], s_sa[1024], s_sb[1024];
   const int e = threadIdx.x;
   int cnt = 0, off = 0;
@@ -1632,6 +1656,7 @@ __global__ __launch_bounds__(1024) void unit_schedule_kernel(
   if (e == 0) {
     *n_a = tot_a;
     *n_b = tot_b;
+    if (status) *status = 0;
   }
 }
 
@@ -2248,14 +2273,14 @@ int64_t schedule_entries(int64_t n_pairs, int E_L, GemmPath path, int nt) {
 
 hipError_t launch_schedule(const int32_t* seg, int seg_cap, int E_L, GemmPath path, int nt_up,
                            int nt_dn, int4* tab_up, int32_t* n_up, int4* tab_dn, int32_t* n_dn,
-                           int32_t* sync, hipStream_t s) {
+                           int32_t* sync, int32_t* status, hipStream_t s) {
   const int bm = gemm_path_rows(path);
   if (gemm_unit_tables(path))  // only the bf16 256-row path has wide tiles
     hipLaunchKernelGGL(unit_schedule_kernel, dim3(1), dim3(1024), 0, s, seg, seg_cap, E_L, nt_up,
-                       nt_dn, bm, path == GEMM_LARGE, tab_up, n_up, tab_dn, n_dn);
+                       nt_dn, bm, path == GEMM_LARGE, tab_up, n_up, tab_dn, n_dn, status);
   else
     hipLaunchKernelGGL(tile_schedule_kernel, dim3(1), dim3(1024), 0, s, seg, seg_cap, E_L, bm,
-                       tab_up, n_up, sync);
+                       tab_up, n_up, sync, status);
   return hipGetLastError();
 }
 
@@ -2361,9 +2386,9 @@ hipError_t launch_grouped_gemm(const GemmLaunch& L, hipStream_t s) {
 }
 
 hipError_t launch_ffn_fused(const GemmLaunch& up, const GemmLaunch& down, int32_t* sync,
-                            hipStream_t s) {
+                            int32_t* status, hipStream_t s) {
   const bool skinny = up.path == GEMM_SKINNY || up.path == GEMM_MX_SKINNY;
-  if (!skinny || down.path != up.path || up.fp8 != down.fp8 || !sync || down.swiglu ||
+  if (!skinny || down.path != up.path || up.fp8 != down.fp8 || !sync || !status || down.swiglu ||
       down.gelu || up.info != down.info || up.n_tiles != down.n_tiles ||
       up.max_tiles != down.max_tiles)
     return hipErrorInvalidValue;
@@ -2373,15 +2398,15 @@ hipError_t launch_ffn_fused(const GemmLaunch& up, const GemmLaunch& down, int32_
   if (err != hipSuccess) return err;
   if (up.path == GEMM_MX_SKINNY) {  // SwiGLU with MXFP8 h only
     if (!up.swiglu) return hipErrorInvalidValue;
-    return launch_fused<MODE_SWIGLU_MX8OUT, kSkMx>(gu, gd, up.max_tiles, sync, s);
+    return launch_fused<MODE_SWIGLU_MX8OUT, kSkMx>(gu, gd, up.max_tiles, sync, status, s);
   }
   if (up.fp8) {  // SwiGLU with block-FP8 h only
     if (!up.swiglu || !up.C_scale) return hipErrorInvalidValue;
-    return launch_fused<MODE_SWIGLU_FP8OUT, kSkFp8>(gu, gd, up.max_tiles, sync, s);
+    return launch_fused<MODE_SWIGLU_FP8OUT, kSkFp8>(gu, gd, up.max_tiles, sync, status, s);
   }
-  if (up.gelu) return launch_fused<MODE_GELU, kSkBf16>(gu, gd, up.max_tiles, sync, s);
-  if (up.swiglu) return launch_fused<MODE_SWIGLU, kSkBf16>(gu, gd, up.max_tiles, sync, s);
-  return launch_fused<MODE_PLAIN, kSkBf16>(gu, gd, up.max_tiles, sync, s);
+  if (up.gelu) return launch_fused<MODE_GELU, kSkBf16>(gu, gd, up.max_tiles, sync, status, s);
+  if (up.swiglu) return launch_fused<MODE_SWIGLU, kSkBf16>(gu, gd, up.max_tiles, sync, status, s);
+  return launch_fused<MODE_PLAIN, kSkBf16>(gu, gd, up.max_tiles, sync, status, s);
 }
 
 }  // namespace moe

@@ -75,10 +75,13 @@ int64_t schedule_entries(int64_t n_pairs, int E_L, GemmPath path, int nt);
 // Builds the work tables on the device (m-tile table: only tab_up / n_up are
 // written).  sync (skinny paths only, else null): the fused FFN's ticket and
 // per-m-tile counters, [1 + schedule_entries], cleared here for the launch
-// that follows.
+// that follows.  status (may be null): the FFN's flag word (kFlag*), cleared
+// here.
 hipError_t launch_schedule(const int32_t* seg, int seg_cap, int E_L, GemmPath path, int nt_up,
                            int nt_dn, int4* tab_up, int32_t* n_up, int4* tab_dn, int32_t* n_dn,
-                           int32_t* sync, hipStream_t s);
+                           int32_t* sync, int32_t* status, hipStream_t s);
+// Flag bits of an FFN's status word (the values of MOE_FLAG_* in the ABI).
+constexpr int32_t kFlagWaitTimeout = 1;
 struct GemmLaunch {
   bool fp8;              // e4m3 operands with block scales, else bf16
   bool mx;               // MXFP4 weights (E2M1, two per byte) x MXFP8 activations,
@@ -115,9 +118,12 @@ hipError_t launch_grouped_gemm(const GemmLaunch& L, hipStream_t s);
 // tiles first, and
 // each down tile starts once every up tile of its rows has published h.
 // `up` and `down` as for two launch_grouped_gemm calls sharing one m-tile
-// table; sync as cleared by launch_schedule.
+// table; sync and status as cleared by launch_schedule (a down tile whose
+// bounded wait gives up sets kFlagWaitTimeout in *status and is skipped).
 hipError_t launch_ffn_fused(const GemmLaunch& up, const GemmLaunch& down, int32_t* sync,
-                            hipStream_t s);
+                            int32_t* status, hipStream_t s);
+// *flags = OR of the n status words (device pointers), one thread.
+hipError_t launch_read_flags(const int32_t* const* words, int n, int32_t* flags, hipStream_t s);
 // Largest fused-gather source and largest panel-layout activation matrix
 // (bytes) that the GEMM's 32-bit buffer offsets reach.
 constexpr int64_t kGemmGatherMaxBytes = 0x7ffffe00;

@@ -19,6 +19,20 @@ __global__ void fill_offsets_kernel(int32_t* offsets, int n) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Status words of up to two FFNs (routed and shared expert), by value.
+struct FlagWords {
+  const int32_t* w[2];
+  int n;
+};
+
+__global__ void read_flags_kernel(FlagWords words, int32_t* flags) {
+  if (threadIdx.x == 0) {
+    int32_t f = 0;
+    for (int i = 0; i < words.n; ++i) f |= words.w[i][0];
+    *flags = f;
+  }
+}
+
 constexpr int32_t kMaxStreams = 64;  // streams of one streamed layer call
 
 // Validate the problem; returns MOE_OK or MOE_ERR_INVALID_ARG/UNSUPPORTED.
@@ -120,6 +134,7 @@ struct FfnScratch {
   int32_t* n_up;
   int32_t* n_dn;
   int32_t* sync;    // fused decode FFN: ticket + per-m-tile counters
+  int32_t* status;  // flag word of the last FFN run on this workspace (MOE_FLAG_*)
   void* h;          // [N_cap, I] bf16 or e4m3
   float* h_scale;   // fp8 only
 };
@@ -156,6 +171,7 @@ FfnScratch carve_ffn(Carve& c, const moe_problem* p) {
   const int64_t N = n_cap(p), I = p->inter;
   const FfnShape sh = ffn_shape(p);
   FfnScratch f{};
+  f.status = c.take<int32_t>(sizeof(int32_t));
   f.tab_up = c.take<int4>(sizeof(int4) * sh.cap_up);
   f.n_up = c.take<int32_t>(sizeof(int32_t));
   if (fused_ffn(sh.path)) f.sync = c.take<int32_t>(sizeof(int32_t) * (1 + sh.cap_up));
@@ -236,7 +252,10 @@ LayerScratch carve_layer(Carve& c, const moe_problem* p) {
   if (p->shared_inter > 0) {
     const moe_problem q = shared_problem(p);
     s.s_offsets = c.take<int32_t>(8);
-    if (quant_acts(p) && !s.xq) {
+    // the shared expert reads the tokens quantised once (s.xq) whenever the
+    // routed experts gather from them; decided on the condition, not on the
+    // pointer, which is null while the carve only measures
+    if (quant_acts(p) && !fuse) {
       s.s_x = c.take<void>(T * H);
       s.s_x_scale = c.take<float>(act_scale_bytes(p, T, H));
     }
@@ -281,7 +300,7 @@ moe_status run_ffn(const moe_problem* p, const FfnSource& src, const int32_t* se
   void* hb = h ? h : f.h;
   float* hs = h ? h_scale : f.h_scale;
   MOE_TRY(launch_schedule(seg, p->capacity, E_L, sh.path, sh.nt_up, sh.nt_dn, f.tab_up, f.n_up,
-                          f.tab_dn, f.n_dn, f.sync, s));
+                          f.tab_dn, f.n_dn, f.sync, f.status, s));
   GemmLaunch up{};
   up.fp8 = is_fp8(p);
   up.mx = is_mx(p);
@@ -290,7 +309,7 @@ moe_status run_ffn(const moe_problem* p, const FfnSource& src, const int32_t* se
   up.A = src.x;
   up.A_scale = src.x_scale;
   up.W = w->w13;
-  up.W_scale = w->w13_scale;
+  up.W_scale = static_cast<const float*>(w->w13_scale);
   up.C = hb;
   up.C_scale = quant_acts(p) ? hs : nullptr;
   up.seg = seg;
@@ -313,7 +332,7 @@ moe_status run_ffn(const moe_problem* p, const FfnSource& src, const int32_t* se
   down.A = hb;
   down.A_scale = hs;
   down.W = w->w2;
-  down.W_scale = w->w2_scale;
+  down.W_scale = static_cast<const float*>(w->w2_scale);
   down.info = f.tab_dn;
   down.n_tiles = f.n_dn;
   down.max_tiles = sh.cap_dn;
@@ -326,7 +345,7 @@ moe_status run_ffn(const moe_problem* p, const FfnSource& src, const int32_t* se
   down.a_rows = N;
   down.a_index = nullptr;
   if (fused_ffn(sh.path)) {
-    MOE_TRY(launch_ffn_fused(up, down, f.sync, s));
+    MOE_TRY(launch_ffn_fused(up, down, f.sync, f.status, s));
   } else {
     MOE_TRY(launch_grouped_gemm(up, s));
     MOE_TRY(launch_grouped_gemm(down, s));
@@ -368,6 +387,16 @@ moe_status enqueue_layer(const moe_problem* p, const float* logits, const void* 
                          const moe_weights* w, void* y, void* ws, hipStream_t s);
 
 }  // namespace
+
+hipError_t launch_read_flags(const int32_t* const* words, int n, int32_t* flags, hipStream_t s) {
+  if (n < 0 || n > 2) return hipErrorInvalidValue;
+  FlagWords fw{};
+  for (int i = 0; i < n; ++i) fw.w[i] = words[i];
+  fw.n = n;
+  hipLaunchKernelGGL(read_flags_kernel, dim3(1), dim3(64), 0, s, fw, flags);
+  return hipGetLastError();
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -387,6 +416,11 @@ const char* moe_status_str(moe_status s) {
   return "MOE_ERR_UNKNOWN";
 }
 
+static void* align_ws(void* ws) {
+  const uintptr_t a = (reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255);
+  return reinterpret_cast<void*>(a);
+}
+
 size_t moe_workspace_bytes(const moe_problem* p, int32_t stage) {
   if (check_problem(p) != MOE_OK) return 0;
   Carve c(nullptr);
@@ -401,6 +435,26 @@ size_t moe_workspace_bytes(const moe_problem* p, int32_t stage) {
   return c.used + 256;  // room to round the base up to 256 bytes
 }
 
+moe_status moe_workspace_flags(const moe_problem* p, int32_t stage, const void* ws,
+                               size_t ws_bytes, int32_t* flags, void* stream) {
+  moe_status st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (stage != MOE_STAGE_LAYER && stage != MOE_STAGE_FFN) return MOE_ERR_INVALID_ARG;
+  if (!flags || !aligned16(flags)) return MOE_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < moe_workspace_bytes(p, stage)) return MOE_ERR_WORKSPACE;
+  const int32_t* words[2] = {nullptr, nullptr};
+  int n = 0;
+  Carve c(align_ws(const_cast<void*>(ws)));
+  if (stage == MOE_STAGE_FFN) {
+    words[n++] = carve_ffn(c, p).status;
+  } else {
+    const LayerScratch L = carve_layer(c, p);
+    words[n++] = L.ffn.status;
+    if (p->shared_inter > 0) words[n++] = L.s_ffn.status;
+  }
+  return hip_status(launch_read_flags(words, n, flags, static_cast<hipStream_t>(stream)));
+}
+
 moe_status moe_route(const moe_problem* p, const float* logits, int32_t* topk_ids,
                      float* topk_w, void* stream) {
   moe_status st = check_problem(p);
@@ -410,11 +464,6 @@ moe_status moe_route(const moe_problem* p, const float* logits, int32_t* topk_id
   if (p->num_tokens == 0) return MOE_OK;
   return hip_status(launch_route_topk(logits, p->num_tokens, p->num_experts, p->top_k, topk_ids,
                                       topk_w, static_cast<hipStream_t>(stream)));
-}
-
-static void* align_ws(void* ws) {
-  const uintptr_t a = (reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255);
-  return reinterpret_cast<void*>(a);
 }
 
 moe_status moe_dispatch(const moe_problem* p, const void* x, const int32_t* topk_ids,

@@ -54,6 +54,7 @@ SIGNATURES = {
     "moe_pack_panel_mx": (_i32, [_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),
     "moe_quantize_mx": (_i32, [_vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp]),
     "moe_workspace_bytes": (_sz, [_P, _i32]),
+    "moe_workspace_flags": (_i32, [_P, _i32, _vp, _sz, _vp, _vp]),
     "moe_stream_threshold": (_i64, [_vp, _vp, _i32, ctypes.c_double]),
     "moe_stream_plan": (_i32, [_vp, _i32, _i64, _vp, _vp]),
     "moe_workspace_bytes_streamed": (_sz, [_P, _i32, _i32]),
@@ -177,6 +178,18 @@ def weights_struct(w13, w2, ws13=None, ws2=None, w13_scale=None, w2_scale=None,
 def workspace_bytes(p: Problem, stage: int = STAGE_LAYER) -> int:
     pc = p.c()
     return int(lib().moe_workspace_bytes(ctypes.byref(pc), stage))
+
+
+FLAG_WAIT_TIMEOUT = 1
+
+
+def moe_workspace_flags(p: Problem, stage: int, ws, flags, stream=None) -> None:
+    """Enqueue the copy of workspace ws's FFN flags into the device int32
+    tensor `flags` (see moe_workspace_flags in the header)."""
+    pc = p.c()
+    _check("moe_workspace_flags", lib().moe_workspace_flags(
+        ctypes.byref(pc), stage, _ptr(ws), ws.numel() * ws.element_size(), _ptr(flags),
+        _stream(stream)))
 
 
 def moe_route(p: Problem, logits, topk_ids, topk_w, stream=None) -> None:

@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert ml.lib().moe_abi_version() == 8
+    assert ml.lib().moe_abi_version() == 9
     assert ml.status_str(0) == "MOE_OK"
     assert ml.status_str(3) == "MOE_ERR_WORKSPACE"
     assert ml.status_str(99) == "MOE_ERR_UNKNOWN"
@@ -61,6 +61,43 @@ def test_workspace_sizes(cid):
     beta = 1 if p.fp8 else 2
     assert layer >= p.n_cap * (2 * p.H + beta * p.I) + (p.T * p.H if p.fp8 else 0)
     assert ml.workspace_bytes(p, 7) == 0
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mx"])
+def test_quantised_layer_workspace_holds_the_tokens_once(fmt):
+    """Block-FP8 and MX layers with a shared expert quantise the tokens once
+    ([T, H] codes plus scales, read by the routed and the shared expert): the
+    shared expert adds its own FFN scratch and its [T, H] bf16 output to the
+    workspace, not a second copy of the quantised tokens."""
+    kw = dict(T=4096, H=1024, E=16, k=4, e_lo=0, E_L=8, I=256, fp8=fmt == "fp8", mx=fmt == "mx")
+    with_shared = ml.workspace_bytes(ml.Problem(I_s=256, **kw))
+    without = ml.workspace_bytes(ml.Problem(I_s=0, **kw))
+    q = ml.Problem(T=kw["T"], H=kw["H"], E=1, k=1, e_lo=0, E_L=1, I=256, fp8=kw["fp8"],
+                   mx=kw["mx"])
+    shared_ffn = ml.workspace_bytes(q, ml.STAGE_FFN)
+    T, H = kw["T"], kw["H"]
+    extra = with_shared - without
+    assert extra >= shared_ffn - 256 + 2 * T * H
+    # alignment of a few carved buffers at most; a second quantised copy of
+    # the tokens would add T * H bytes more
+    assert extra <= shared_ffn + 2 * T * H + 2048 < shared_ffn + 3 * T * H
+
+
+def test_workspace_flags_argument_checks():
+    p = ml.Problem(T=16, H=256, E=8, k=2, e_lo=0, E_L=8, I=256)
+    pc = p.c()
+    L = ml.lib()
+    n = ml.workspace_bytes(p)
+    # the dispatch stage has no FFN flags; null or misaligned flag pointer;
+    # short workspace (all rejected before anything is enqueued)
+    assert L.moe_workspace_flags(ctypes.byref(pc), ml.STAGE_DISPATCH, 256, n, 256,
+                                 None) == ml.MOE_ERR_INVALID_ARG
+    assert L.moe_workspace_flags(ctypes.byref(pc), ml.STAGE_LAYER, 256, n, None,
+                                 None) == ml.MOE_ERR_INVALID_ARG
+    assert L.moe_workspace_flags(ctypes.byref(pc), ml.STAGE_LAYER, 256, n, 258,
+                                 None) == ml.MOE_ERR_INVALID_ARG
+    assert L.moe_workspace_flags(ctypes.byref(pc), ml.STAGE_LAYER, 256, 16, 256,
+                                 None) == ml.MOE_ERR_WORKSPACE
 
 
 @pytest.mark.parametrize("bad", [

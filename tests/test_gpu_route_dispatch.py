@@ -44,7 +44,11 @@ def test_route_workloads(cid):
 
 
 @pytest.mark.parametrize("E,k", [(1, 1), (8, 2), (8, 8), (65, 3), (128, 8), (200, 12),
-                                 (256, 32), (1024, 8), (1000, 1)])
+                                 (256, 32), (1024, 8), (1000, 1),
+                                 # 16-lane rows: vector loads (E % 4 == 0) or not, up
+                                 # to 32 keys per lane, slots past 16, the last size
+                                 # before one token per wave
+                                 (12, 5), (300, 17), (511, 32), (512, 20), (513, 4)])
 def test_route_shapes(E, k):
     torch = torch_cuda()
     ml = _ml()

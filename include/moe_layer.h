@@ -293,6 +293,25 @@ moe_status moe_layer(const moe_problem* p, const float* logits, const void* x,
                      const moe_weights* w, void* y, void* ws, size_t ws_bytes,
                      void* stream);
 
+/* moe_layer without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments, results and kernels as moe_layer
+ * (bit-identical output); the workspace is a static device array of
+ * MOE_STATIC_SCRATCH_BYTES (64 MiB) that the library holds on every device it
+ * runs on until the process ends.  The call itself allocates nothing; its
+ * first call on a device resolves that device's copy of the array
+ * (hipGetSymbolAddress), so make one call per device before a graph capture.
+ * Every call on a device shares the array and leaves its contents behind
+ * (every kernel initialises what it reads), so calls that overlap on one
+ * device -- two streams, or two host threads -- race and must be serialised
+ * by the caller.
+ *   MOE_ERR_WORKSPACE if moe_workspace_bytes(p, MOE_STAGE_LAYER) - 256 exceeds
+ *   MOE_STATIC_SCRATCH_BYTES (decode-sized batches fit: the DeepSeek-V3-shaped
+ *   shard with 64 tokens needs about 10 MB); other errors as moe_layer.     */
+#define MOE_STATIC_SCRATCH_BYTES (64u << 20)
+moe_status moe_layer_static(const moe_problem* p, const float* logits, const void* x,
+                            const moe_weights* w, void* y, void* stream);
+
 /* Block-FP8 quantisation (page "OverlapAdvisor ...", section 4.4: BF16
  * checkpoints are quantised to block-FP8 at load time; the same rule makes
  * the per-token activation scales).  For each block_rows x 128 block of the

@@ -3,6 +3,9 @@
 // allocates device memory or synchronises the host.
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "../../include/moe_layer.h"
 #include "common.h"
 #include "kernels.h"
@@ -386,6 +389,40 @@ bool weights_ok(const moe_problem* p, const moe_weights* w, bool need_shared) {
 moe_status enqueue_layer(const moe_problem* p, const float* logits, const void* x,
                          const moe_weights* w, void* y, void* ws, hipStream_t s);
 
+// The workspace of moe_layer_static: one array per device, held until the
+// process ends.  In host code `scratch` names a host-side stand-in, not the
+// device memory: kernels get the device address that hipGetSymbolAddress
+// returns for the current device, resolved once per device and kept in
+// g_scratch (every device holds its own copy of the array).
+__device__ __align__(256) uint8_t scratch[MOE_STATIC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::atomic<uintptr_t> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's array (resolved on the first call
+// on that device).
+hipError_t static_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  uintptr_t v = g_scratch[dev].load(std::memory_order_acquire);
+  if (!v) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    v = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!v) {
+      void* ptr = nullptr;
+      e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (!ptr || (reinterpret_cast<uintptr_t>(ptr) & 255)) return hipErrorInvalidValue;
+      v = reinterpret_cast<uintptr_t>(ptr);
+      g_scratch[dev].store(v, std::memory_order_release);
+    }
+  }
+  *out = reinterpret_cast<void*>(v);
+  return hipSuccess;
+}
+
 }  // namespace
 
 hipError_t launch_read_flags(const int32_t* const* words, int n, int32_t* flags, hipStream_t s) {
@@ -539,6 +576,23 @@ moe_status moe_combine(const moe_problem* p, const void* y_perm, const int32_t* 
   if (p->num_tokens == 0) return MOE_OK;
   return hip_status(launch_combine(y_perm, token_slot_row, topk_w, shared_out, p->num_tokens,
                                    p->top_k, p->hidden, y, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_layer_static(const moe_problem* p, const float* logits, const void* x,
+                            const moe_weights* w, void* y, void* stream) {
+  moe_status st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!logits || !x || !y || !aligned16(logits) || !aligned16(x) || !aligned16(y))
+    return MOE_ERR_INVALID_ARG;
+  if (!weights_ok(p, w, p->shared_inter > 0)) return MOE_ERR_INVALID_ARG;
+  // moe_workspace_bytes adds 256 bytes for rounding a caller's base; the
+  // array is 256-byte aligned already
+  if (moe_workspace_bytes(p, MOE_STAGE_LAYER) - 256 > MOE_STATIC_SCRATCH_BYTES)
+    return MOE_ERR_WORKSPACE;
+  if (p->num_tokens == 0) return MOE_OK;
+  void* ws = nullptr;
+  if (static_scratch(&ws) != hipSuccess) return MOE_ERR_HIP;
+  return enqueue_layer(p, logits, x, w, y, ws, static_cast<hipStream_t>(stream));
 }
 
 moe_status moe_layer(const moe_problem* p, const float* logits, const void* x,

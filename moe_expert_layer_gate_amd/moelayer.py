@@ -49,6 +49,7 @@ SIGNATURES = {
     "moe_grouped_ffn_gather": (_i32, [_P, _vp, _vp, _vp, _vp, _W, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_combine": (_i32, [_P, _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_layer": (_i32, [_P, _vp, _vp, _W, _vp, _vp, _sz, _vp]),
+    "moe_layer_static": (_i32, [_P, _vp, _vp, _W, _vp, _vp]),
     "moe_quantize_fp8": (_i32, [_vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp]),
     "moe_pack_panel": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp]),
     "moe_pack_panel_mx": (_i32, [_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),
@@ -237,6 +238,18 @@ def moe_layer(p: Problem, logits, x, weights: moe_weights, y, ws, stream=None) -
     _check("moe_layer", lib().moe_layer(
         ctypes.byref(pc), _ptr(logits), _ptr(x), ctypes.byref(weights), _ptr(y), _ptr(ws),
         ws.numel() * ws.element_size(), _stream(stream)))
+
+
+STATIC_SCRATCH_BYTES = 64 << 20
+
+
+def moe_layer_static(p: Problem, logits, x, weights: moe_weights, y, stream=None) -> None:
+    """moe_layer on the library's static per-device workspace (no workspace
+    argument; see moe_layer_static in the header)."""
+    pc = p.c()
+    _check("moe_layer_static", lib().moe_layer_static(
+        ctypes.byref(pc), _ptr(logits), _ptr(x), ctypes.byref(weights), _ptr(y),
+        _stream(stream)))
 
 
 def moe_quantize_fp8(src, batch: int, rows: int, cols: int, block_rows: int, codes, scales,

@@ -59,9 +59,13 @@ def parse():
                          "against the one-call layer")
     ap.add_argument("--rho", type=float, default=0.90)
     ap.add_argument("--streams", type=int, default=2)
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the HIP-graph replay and the clock/power sampling (for runs "
+                         "under a profiler)")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="finish with three 1 GiB device copies (a known-size reference "
-                         "for the FETCH_SIZE / WRITE_SIZE counters)")
+                    help="finish with three passes of an elementwise kernel over 1 GiB in "
+                         "and 1 GiB out (a known-size reference for the FETCH_SIZE / WRITE_SIZE "
+                         "counters)")
     return ap.parse_args()
 
 
@@ -258,23 +262,25 @@ def main():
     # (how a serving loop replays a step): no per-launch host work.  Same
     # output bits as the calls above.  The clock and power of the GPU are
     # sampled while it replays.
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        ml.moe_layer(p_layer, dev["logits"], dev["x"], W, y_l, ws_l)
-    y_l.zero_()
-    torch.cuda.synchronize()
-    graph.replay()
-    torch.cuda.synchronize()
-    same_graph = bool(torch.equal(y_l.view(torch.int16), y_steps.view(torch.int16)))
-    for _ in range(args.warmup):
+    graph_tps = same_graph = gpu = None
+    if not args.no_extras:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            ml.moe_layer(p_layer, dev["logits"], dev["x"], W, y_l, ws_l)
+        y_l.zero_()
+        torch.cuda.synchronize()
         graph.replay()
-    torch.cuda.synchronize()
-    t2 = time.perf_counter()
-    for _ in range(args.steps):
-        graph.replay()
-    torch.cuda.synchronize()
-    graph_tps = T * args.steps / (time.perf_counter() - t2)
-    gpu = gpu_under_load(lambda: graph.replay(), float(np.median(layer_ms)))
+        torch.cuda.synchronize()
+        same_graph = bool(torch.equal(y_l.view(torch.int16), y_steps.view(torch.int16)))
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        graph_tps = T * args.steps / (time.perf_counter() - t2)
+        gpu = gpu_under_load(lambda: graph.replay(), float(np.median(layer_ms)))
 
     cnt = counts.cpu().numpy()
     n_pairs = int(cnt.sum())
@@ -368,7 +374,8 @@ def main():
         "stage_ms": {k2: round(v, 4) for k2, v in stage_ms.items()},
         "stage_gbs": stage_rates,
         "staged_calls": {"tokens_per_s": round(staged_tps, 1), "same_output_bits": same},
-        "moe_layer_graph": {"tokens_per_s": round(graph_tps, 1), "same_output_bits": same_graph},
+        "moe_layer_graph": ({"tokens_per_s": round(graph_tps, 1), "same_output_bits": same_graph}
+                            if graph_tps else None),
         "gpu": gpu,
         "host": host_info(),
         "routing": {"local_pairs": n_pairs, "active_experts": active,
@@ -382,10 +389,12 @@ def main():
         out["streamffn"] = stream_bench(args, cfg, d, p_layer, W, dev)
     print(json.dumps(out), flush=True)
     if args.copy_calibration:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        # a plain elementwise kernel over 1 GiB in and 1 GiB out (three times):
+        # the known-size reference of the FETCH_SIZE / WRITE_SIZE counters
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            torch.mul(src, 2.0, out=dst)
         torch.cuda.synchronize()
 
 

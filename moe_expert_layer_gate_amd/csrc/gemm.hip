@@ -93,6 +93,8 @@ struct GemmArgs {
   int64_t a_bytes;         // size of the A buffer
   int64_t c_cs;            // SwiGLU bf16 output: 0 = row major, else panel stride
   const int32_t* a_index;  // fused gather: GEMM row j reads A row a_index[j]
+  int32_t* tickets;        // persistent large-tile GEMM: one unit counter per XCD (zeroed
+                           // by the schedule kernel), else null
 };
 
 // Byte offset of element (m, col) of a bf16 output with Nout columns.
@@ -1629,7 +1631,7 @@ __device__ __forceinline__ void write_units(const int* s_start, const int* s_off
 __global__ __launch_bounds__(1024) void unit_schedule_kernel(
     const int32_t* __restrict__ seg, int seg_cap, int E_L, int nt_a, int nt_b, int bm, bool allow_wide,
     int4* __restrict__ units_a, int32_t* __restrict__ n_a, int4* __restrict__ units_b,
-    int32_t* __restrict__ n_b, int32_t* __restrict__ status) {
+    int32_t* __restrict__ n_b, int32_t* __restrict__ status, int32_t* __restrict__ tickets) {
   __shared__ int s_off[1024], s_full[1024], s_sa[1024], s_sb[1024];
   const int e = threadIdx.x;
   int cnt = 0, off = 0;
@@ -1658,7 +1660,97 @@ __global__ __launch_bounds__(1024) void unit_schedule_kernel(
     *n_b = tot_b;
     if (status) *status = 0;
   }
+  if (tickets && e < 2 * kXcds) tickets[e] = 0;  // per-XCD unit counters of both GEMMs
 }
+
+// Epilogue of a large-tile unit: the wave's 64 x 128 accumulators (token
+// rows wm*64.., weight rows wn*128.. of the tile) become bf16 y (staged
+// through LDS for whole 256-byte row pieces), GELU h or SwiGLU h.  Every
+// wave must be past its last direct load and fragment read of the ring.
+template <int MODE, class SH>
+__device__ __forceinline__ void big_epilogue(const GemmArgs& g, f32x16 (&acc)[4][2], int row0,
+                                             int seg_end, int nbase, uint8_t* smem) {
+  constexpr int NW = SH::NW, kWaveRows = SH::BM / 64;
+  constexpr int kStages = SH::kStages, kStageBytes = SH::kStageBytes;
+  const int lane = lane_id(), w = threadIdx.x >> 6;
+  const int wm = w % kWaveRows, wn = w / kWaveRows;
+  const int lr = lane & 31;
+  const int cq = (lane >> 5) * 4;
+  uint16_t* C = static_cast<uint16_t*>(g.C);
+  if constexpr (MODE == MODE_PLAIN) {
+    // The wave's 64 x 128 result goes through LDS so that the stores write
+    // whole 256-byte row pieces (16 lanes per row, 4 rows per instruction)
+    // instead of 16 bytes of 32 rows each.  Every wave is past its last
+    // fragment read and direct load once all have reached the barrier.
+    constexpr int kPitch = 272;  // 256 bytes + 16: rows start 4 banks apart
+    static_assert(NW * 64 * kPitch <= kStages * kStageBytes, "epilogue tile fits the ring");
+    __builtin_amdgcn_s_barrier();
+    uint8_t* stile = smem + w * 64 * kPitch;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint2 o;
+          o.x = pack_bf16x2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]);
+          o.y = pack_bf16x2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
+          *reinterpret_cast<uint2*>(stile + (j * 32 + lr) * kPitch + (i * 32 + q * 8 + cq) * 2) = o;
+        }
+    const int col = nbase + wn * 128 + (lane & 15) * 8;
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int rl = it * 4 + (lane >> 4);
+      const uint4 v = *reinterpret_cast<const uint4*>(stile + rl * kPitch + (lane & 15) * 16);
+      const int m = row0 + wm * 64 + rl;
+      if (m < seg_end && col < g.Nout)
+        *reinterpret_cast<uint4*>(C + static_cast<int64_t>(m) * g.Nout + col) = v;
+    }
+  } else if constexpr (MODE == MODE_GELU) {
+    // h = gelu(x W1^T), panel or row major
+    uint8_t* C8 = reinterpret_cast<uint8_t*>(C);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int m = row0 + wm * 64 + j * 32 + lr;
+      if (m >= seg_end) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = nbase + wn * 128 + i * 32 + q * 8 + cq;
+          if (col >= g.Nout) continue;
+          uint2 o;
+          o.x = pack_bf16x2(gelu_f(acc[i][j][q * 4 + 0]), gelu_f(acc[i][j][q * 4 + 1]));
+          o.y = pack_bf16x2(gelu_f(acc[i][j][q * 4 + 2]), gelu_f(acc[i][j][q * 4 + 3]));
+          *reinterpret_cast<uint2*>(C8 + out_offset(g, m, col)) = o;
+        }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int m = row0 + wm * 64 + j * 32 + lr;
+      if (m >= seg_end) continue;
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = nbase + wn * 64 + hb * 32 + q * 8 + cq;
+          if (col >= g.Nout) continue;
+          float hv[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float gt = acc[hb][j][q * 4 + r], up = acc[hb + 2][j][q * 4 + r];
+            hv[r] = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
+          }
+          uint2 o;
+          o.x = pack_bf16x2(hv[0], hv[1]);
+          o.y = pack_bf16x2(hv[2], hv[3]);
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(C) + out_offset(g, m, col)) = o;
+        }
+    }
+  }
+}
+
 
 template <int MODE, class SH>
 __device__ __forceinline__ void big_tile(const GemmArgs& g, const int4 unit, uint8_t* smem) {
@@ -1800,79 +1892,235 @@ __device__ __forceinline__ void big_tile(const GemmArgs& g, const int4 unit, uin
     s_cur = s_nxt;
   }
   WAIT_VMCNT(0);
+  big_epilogue<MODE, SH>(g, acc, row0, seg_end, nbase, smem);
+}
 
-  const int cq = (lane >> 5) * 4;
-  uint16_t* C = static_cast<uint16_t*>(g.C);
-  if constexpr (MODE == MODE_PLAIN) {
-    // The wave's 64 x 128 result goes through LDS so that the stores write
-    // whole 256-byte row pieces (16 lanes per row, 4 rows per instruction)
-    // instead of 16 bytes of 32 rows each.  Every wave is past its last
-    // fragment read and direct load once all have reached the barrier.
-    constexpr int kPitch = 272;  // 256 bytes + 16: rows start 4 banks apart
-    static_assert(NW * 64 * kPitch <= kStages * kStageBytes, "epilogue tile fits the ring");
+// ---------------------------------------------------------------------------
+// Persistent large-tile GEMM with the SwiGLU or GELU epilogue (the up GEMM,
+// whose epilogue stores h straight from the accumulators and leaves the LDS
+// alone).  One block per CU pulls units from its XCD's queue -- the XCD's
+// contiguous range of the unit table, handed out by an atomic counter -- so
+// that CUs that finish early take more units (the tile-granular work of page
+// "ExpertPlex"'s persistent kernels; the tail effect of page "CascadeEP
+// ...", section 3.2, is the last round of units).  Between two full units
+// the load ring runs on: the last three K steps of a unit load the first
+// three steps of the next one, whose ticket the block took when it began the
+// unit, so those loads are in flight while the unit's epilogue runs and the
+// next unit starts without an empty pipeline.  A wide unit (a segment's
+// remainder, different tile shape) never chains: before it the ring drains
+// and it runs as in the one-unit-per-block kernel.
+// ---------------------------------------------------------------------------
+// The wide unit of both large-tile kernels (one call site of the big_tile
+// specialisation: the host pass of hipcc rejects a second one).
+template <int MODE>
+__device__ __forceinline__ void big_tile_wide(const GemmArgs& g, const int4 unit, uint8_t* smem) {
+  big_tile<MODE, WideShape>(g, unit, smem);
+}
+
+template <int MODE>
+struct BigChain {
+  using SH = FullShape;
+  static constexpr bool kSwiglu = MODE == MODE_SWIGLU;
+  static constexpr int BM = SH::BM, BN = SH::BN, NW = SH::NW;
+  static constexpr int kStages = SH::kStages, kStageBytes = SH::kStageBytes;
+  static constexpr int kAhead = kStages - 1;
+  static constexpr int kWRegion = BM * kBigRowBytes;
+  static constexpr int kAGroups = BM / 16;
+  static constexpr int kLoads = (BM + BN) / 16 / NW;   // 4
+  static constexpr int kALoads = kAGroups / NW;        // 2
+
+  // Load addressing of one unit (lane offsets, buffer views) and its place.
+  struct Unit {
+    int row0, seg_end, nbase;
+    int voff[kLoads];
+    __amdgpu_buffer_rsrc_t rA, rW;
+  };
+
+  __device__ static Unit setup(const GemmArgs& g, const int4 unit) {
+    Unit u;
+    const int e = unit.x;
+    u.row0 = unit.y;
+    u.seg_end = segment(g.seg, g.seg_cap, e).y;
+    u.nbase = kSwiglu ? unit.z * (BN / 2) : unit.z * BN;
+    const int64_t a_skip = g.a_index ? 0 : static_cast<int64_t>(u.row0) * g.a_rs;
+    const int lane = lane_id(), w = threadIdx.x >> 6;
+#pragma unroll
+    for (int q = 0; q < kLoads; ++q) {
+      const int grp = q < kALoads ? w * kALoads + q : kAGroups + w * (kLoads - kALoads) + (q - kALoads);
+      const int rr = grp * 16 + (lane >> 2);
+      const int chunk = (lane & 3) ^ ((rr >> 2) & 3);
+      if (rr < BM) {
+        const bool valid = u.row0 + rr < u.seg_end;
+        const int arow = g.a_index && valid ? g.a_index[u.row0 + rr] : rr;
+        u.voff[q] = valid ? arow * g.a_rs + chunk * 16 : kOobOffset;
+      } else {
+        const int r = rr - BM;
+        int grow;
+        if (kSwiglu)
+          grow = r < BN / 2 ? min(u.nbase + r, g.Nout - 1)
+                            : g.Nout + min(u.nbase + (r - BN / 2), g.Nout - 1);
+        else
+          grow = min(u.nbase + r, g.NW - 1);
+        u.voff[q] = grow * g.w_rs + chunk * 16;
+      }
+    }
+    u.rA = make_rsrc(g.A + a_skip, g.a_bytes - a_skip);
+    u.rW = make_rsrc(g.W + e * g.w_stride, g.w_stride);
+    return u;
+  }
+
+  // The loads of K step `step` of unit u into `stage` (live == false: the
+  // same number of loads, out of range, so the wait counts hold).
+  __device__ static void dma(const GemmArgs& g, const Unit& u, bool live, int step, int stage,
+                             uint8_t* smem) {
+    const int lane_grp = threadIdx.x >> 6;
+    uint8_t* base = smem + stage * kStageBytes;
+#pragma unroll
+    for (int q = 0; q < kLoads; ++q) {
+      const int grp = q < kALoads ? lane_grp * kALoads + q
+                                  : kAGroups + lane_grp * (kLoads - kALoads) + (q - kALoads);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(q < kALoads ? u.rA : u.rW,
+                                               (lds_ptr_t)(base + grp * 1024), 16,
+                                               live ? u.voff[q] : kOobOffset,
+                                               live ? step * (q < kALoads ? g.a_cs : g.w_cs) : 0,
+                                               0, 0);
+    }
+  }
+};
+
+template <int MODE>
+__global__ __launch_bounds__(kBigThreads, 1) void gemm_big_persistent_kernel(const GemmArgs g) {
+  using C = BigChain<MODE>;
+  using SH = typename C::SH;
+  constexpr int kStages = C::kStages, kStageBytes = C::kStageBytes, kAhead = C::kAhead;
+  constexpr int kLoads = C::kLoads;
+  constexpr bool kSwiglu = C::kSwiglu;
+  // The ring takes the whole LDS (no static __shared__ variable fits beside
+  // it): the ticket is passed through a word of a stage that holds nothing
+  // in flight or still to be read (slot, a byte offset).
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  const int total = *g.n_tiles;
+  const int per_xcd = ceil_div(total, kXcds);
+  const int x = blockIdx.x % kXcds;  // blocks go to the XCDs round-robin by id
+  const int q0 = x * per_xcd, q1 = min(total, q0 + per_xcd);
+  int32_t* ctr = g.tickets + x;
+  // the next unit of this XCD's queue (-1: none left); every thread calls it
+  auto take = [&](int slot) -> int {
+    int* tk = reinterpret_cast<int*>(smem + slot);
+    __syncthreads();  // every earlier LDS read of the block is done
+    if (threadIdx.x == 0) *tk = atomicAdd(ctr, 1);
+    __syncthreads();
+    const int t = q0 + *tk;
+    __syncthreads();  // every thread has the ticket before the slot is reused
+    return t < q1 ? t : -1;
+  };
+  const int nk = 2 * g.K / kBigRowBytes;
+
+  const int lane = lane_id(), w = threadIdx.x >> 6;
+  const int wm = w % 4, wn = w / 4;
+  const int lr = lane & 31, hi = lane >> 5, sl = (lr >> 2) & 3;
+  int foff[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) foff[kk] = lr * kBigRowBytes + (((2 * kk) | hi) ^ sl) * 16;
+  int wbase[4], abase[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = kSwiglu ? (i < 2 ? 0 : SH::BN / 2) + wn * 64 + (i & 1) * 32 : wn * 128 + i * 32;
+    wbase[i] = C::kWRegion + row * kBigRowBytes;
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) abase[j] = (wm * 64 + j * 32) * kBigRowBytes;
+
+  f32x16 acc[4][2];
+  bf16x8 fa[2][4], fb[2][2];
+  auto lfrag = [&](const uint8_t* st, int kk, int set) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[set][i] = *reinterpret_cast<const bf16x8*>(st + wbase[i] + foff[kk]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) fb[set][j] = *reinterpret_cast<const bf16x8*>(st + abase[j] + foff[kk]);
+  };
+  auto mma = [&](int set, int first, int count) {
+#pragma unroll
+    for (int q = first; q < first + count; ++q) {
+      const int i = q >> 1, j = q & 1;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j], acc[i][j], 0, 0, 0);
+    }
+  };
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  };
+
+  int t = take(0);  // nothing in flight yet
+  while (t >= 0) {
+    int4 unit = g.info[t];
+    if (unit.w) {  // a wide unit: its own prologue, loop and epilogue
+      big_tile_wide<MODE>(g, unit, smem);
+      t = take(0);  // its loads have all landed and its epilogue uses no LDS
+      continue;
+    }
+    // A chain of full units.  Prologue of the first one.
+    typename C::Unit cur = C::setup(g, unit);
+#pragma unroll
+    for (int st = 0; st < kAhead; ++st) C::dma(g, cur, true, st, st, smem);
+    WAIT_VMCNT((kAhead - 1) * kLoads);
     __builtin_amdgcn_s_barrier();
-    uint8_t* stile = smem + w * 64 * kPitch;
+    lfrag(smem, 0, 0);
+    int s_cur = 0;  // ring stage of the current step
+    for (;;) {
+      zero_acc();
+      // the next unit: chained if it is a full one.  The stage before the
+      // current step's (the previous unit's last step, or the one the
+      // prologue left empty) is free until this unit's step 3 is loaded.
+      const int tn = take((s_cur == 0 ? kStages - 1 : s_cur - 1) * kStageBytes);
+      const int4 un = tn >= 0 ? g.info[tn] : make_int4(0, 0, 0, 1);
+      const bool chain = tn >= 0 && !un.w;
+      typename C::Unit nxt = chain ? C::setup(g, un) : cur;
+      for (int kt = 0; kt < nk; ++kt) {
+        const int s_nxt = s_cur + 1 == kStages ? 0 : s_cur + 1;
+        const uint8_t* st_cur = smem + s_cur * kStageBytes;
+        const uint8_t* st_nxt = smem + s_nxt * kStageBytes;
+        // step kt + kAhead of the stream: this unit's, else the next unit's
+        // first steps (or out-of-range loads at the end of a chain)
+        const int ls = kt + kAhead;
+        const int lstage = s_cur == 0 ? kStages - 1 : s_cur - 1;
+        if (ls < nk)
+          C::dma(g, cur, true, ls, lstage, smem);
+        else
+          C::dma(g, nxt, chain, ls - nk, lstage, smem);
+        lfrag(st_cur, 1, 1);
+        mma(0, 0, 8);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int q = 0; q < 6; ++q) {
+          SCHED(kSchedMfma, 1);
+          SCHED(kSchedDsRead, 1);
+          if (q < kLoads) SCHED(kSchedVmemRead, 1);
+        }
+        SCHED(kSchedMfma, 2);
+        mma(1, 0, 4);
+        WAIT_VMCNT_LDS((kAhead - 1) * kLoads);
+        __builtin_amdgcn_s_barrier();
+        lfrag(st_nxt, 0, 0);
+        mma(1, 4, 4);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          uint2 o;
-          o.x = pack_bf16x2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]);
-          o.y = pack_bf16x2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
-          *reinterpret_cast<uint2*>(stile + (j * 32 + lr) * kPitch + (i * 32 + q * 8 + cq) * 2) = o;
+          SCHED(kSchedDsRead, 2);
+          SCHED(kSchedMfma, 1);
         }
-    const int col = nbase + wn * 128 + (lane & 15) * 8;
-#pragma unroll
-    for (int it = 0; it < 16; ++it) {
-      const int rl = it * 4 + (lane >> 4);
-      const uint4 v = *reinterpret_cast<const uint4*>(stile + rl * kPitch + (lane & 15) * 16);
-      const int m = row0 + wm * 64 + rl;
-      if (m < seg_end && col < g.Nout)
-        *reinterpret_cast<uint4*>(C + static_cast<int64_t>(m) * g.Nout + col) = v;
-    }
-  } else if constexpr (MODE == MODE_GELU) {
-    // h = gelu(x W1^T), panel or row major
-    uint8_t* C8 = reinterpret_cast<uint8_t*>(C);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int m = row0 + wm * 64 + j * 32 + lr;
-      if (m >= seg_end) continue;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = nbase + wn * 128 + i * 32 + q * 8 + cq;
-          if (col >= g.Nout) continue;
-          uint2 o;
-          o.x = pack_bf16x2(gelu_f(acc[i][j][q * 4 + 0]), gelu_f(acc[i][j][q * 4 + 1]));
-          o.y = pack_bf16x2(gelu_f(acc[i][j][q * 4 + 2]), gelu_f(acc[i][j][q * 4 + 3]));
-          *reinterpret_cast<uint2*>(C8 + out_offset(g, m, col)) = o;
-        }
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int m = row0 + wm * 64 + j * 32 + lr;
-      if (m >= seg_end) continue;
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = nbase + wn * 64 + hb * 32 + q * 8 + cq;
-          if (col >= g.Nout) continue;
-          float hv[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float gt = acc[hb][j][q * 4 + r], up = acc[hb + 2][j][q * 4 + r];
-            hv[r] = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
-          }
-          uint2 o;
-          o.x = pack_bf16x2(hv[0], hv[1]);
-          o.y = pack_bf16x2(hv[2], hv[3]);
-          *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(C) + out_offset(g, m, col)) = o;
-        }
+        s_cur = s_nxt;
+      }
+      if (!chain) WAIT_VMCNT(0);  // the out-of-range loads of the chain's end
+      // SwiGLU / GELU epilogue: stores from the accumulators, no LDS
+      big_epilogue<MODE, SH>(g, acc, cur.row0, cur.seg_end, cur.nbase, smem);
+      if (!chain) {
+        t = tn;
+        break;
+      }
+      cur = nxt;
     }
   }
 }
@@ -1888,17 +2136,47 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const GemmArgs
   if (t >= total) return;
   const int4 unit = g.info[t];
   if (unit.w)
-    big_tile<MODE, WideShape>(g, unit, smem);
+    big_tile_wide<MODE>(g, unit, smem);
   else
     big_tile<MODE, FullShape>(g, unit, smem);
 }
 
 
+// Compute units of the current device (looked up once per device).
+inline int device_cus() {
+  static std::atomic<int> cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  int n = cus[dev].load(std::memory_order_acquire);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    n = 256;
+  }
+  cus[dev].store(n, std::memory_order_release);
+  return n;
+}
+
 template <int MODE>
 hipError_t launch_big(const GemmArgs& g, int64_t max_units, hipStream_t s) {
   static_assert(kBigStages * kBigStageBytes <= 160 * 1024, "the ring fits the CU's LDS");
-  auto kern = gemm_big_kernel<MODE>;
   const size_t lds = kBigStages * kBigStageBytes;
+  auto kern = gemm_big_kernel<MODE>;
+  if constexpr (MODE == MODE_SWIGLU || MODE == MODE_GELU) {
+    if (g.tickets) {  // persistent: one block per CU (at most one unit each, at least 8)
+      auto pkern = gemm_big_persistent_kernel<MODE>;
+      static std::atomic<uint64_t> lds_set_p{0};
+      allow_dynamic_lds(reinterpret_cast<const void*>(pkern), static_cast<int>(lds), lds_set_p);
+      int64_t blocks = device_cus();
+      blocks = blocks < max_units ? blocks : max_units;
+      blocks = (blocks + kXcds - 1) / kXcds * kXcds;
+      hipLaunchKernelGGL(pkern, dim3(static_cast<unsigned>(blocks)), dim3(kBigThreads), lds, s, g);
+      return hipGetLastError();
+    }
+  }
   static std::atomic<uint64_t> lds_set{0};
   allow_dynamic_lds(reinterpret_cast<const void*>(kern), static_cast<int>(lds), lds_set);
   const int64_t blocks = (max_units + kXcds - 1) / kXcds * kXcds + kXcds;
@@ -2277,7 +2555,7 @@ hipError_t launch_schedule(const int32_t* seg, int seg_cap, int E_L, GemmPath pa
   const int bm = gemm_path_rows(path);
   if (gemm_unit_tables(path))  // only the bf16 256-row path has wide tiles
     hipLaunchKernelGGL(unit_schedule_kernel, dim3(1), dim3(1024), 0, s, seg, seg_cap, E_L, nt_up,
-                       nt_dn, bm, path == GEMM_LARGE, tab_up, n_up, tab_dn, n_dn, status);
+                       nt_dn, bm, path == GEMM_LARGE, tab_up, n_up, tab_dn, n_dn, status, sync);
   else
     hipLaunchKernelGGL(tile_schedule_kernel, dim3(1), dim3(1024), 0, s, seg, seg_cap, E_L, bm,
                        tab_up, n_up, sync, status);
@@ -2341,6 +2619,7 @@ static hipError_t make_args(const GemmLaunch& L, GemmArgs& g) {
   g.a_bytes = L.a_rows * ldb;
   g.c_cs = L.c_panel ? 64 * L.c_rows : 0;
   g.a_index = L.a_index;
+  g.tickets = L.tickets;
   const bool fp8_path =
       L.path == GEMM_LARGE_FP8 || L.path == GEMM_PIPELINED || L.path == GEMM_SKINNY;
   if ((L.fp8 && !fp8_path) || (!L.fp8 && L.path == GEMM_LARGE_FP8)) return hipErrorInvalidValue;

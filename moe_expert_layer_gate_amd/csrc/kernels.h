@@ -73,15 +73,18 @@ int64_t schedule_entries(int64_t n_pairs, int E_L, GemmPath path, int nt);
 // (contiguous layout, expert e's rows [offsets[e], offsets[e+1])); seg_cap > 0:
 // seg = counts [E_L] (masked layout, rows [e seg_cap, e seg_cap + counts[e])).
 // Builds the work tables on the device (m-tile table: only tab_up / n_up are
-// written).  sync (skinny paths only, else null): the fused FFN's ticket and
-// per-m-tile counters, [1 + schedule_entries], cleared here for the launch
-// that follows.  status (may be null): the FFN's flag word (kFlag*), cleared
-// here.
+// written).  sync: skinny paths: the fused FFN's ticket and per-m-tile
+// counters, [1 + schedule_entries]; large-tile paths: the persistent GEMMs'
+// per-XCD unit counters, [kTicketWords] (null: none); cleared here for the
+// launches that follow.  status (may be null): the FFN's flag word (kFlag*),
+// cleared here.
 hipError_t launch_schedule(const int32_t* seg, int seg_cap, int E_L, GemmPath path, int nt_up,
                            int nt_dn, int4* tab_up, int32_t* n_up, int4* tab_dn, int32_t* n_dn,
                            int32_t* sync, int32_t* status, hipStream_t s);
 // Flag bits of an FFN's status word (the values of MOE_FLAG_* in the ABI).
 constexpr int32_t kFlagWaitTimeout = 1;
+// Unit counters of the large-tile paths: 8 per GEMM (one per XCD), up then down.
+constexpr int kTicketWords = 16;
 struct GemmLaunch {
   bool fp8;              // e4m3 operands with block scales, else bf16
   bool mx;               // MXFP4 weights (E2M1, two per byte) x MXFP8 activations,
@@ -111,6 +114,9 @@ struct GemmLaunch {
   // Fused gather (bf16, row-major A only): permuted row j of the GEMM is row
   // a_index[j] of A, e.g. A = the layer input x and a_index = row_token.
   const int32_t* a_index;
+  // GEMM_LARGE: this GEMM's 8 per-XCD unit counters (from launch_schedule's
+  // sync), for the persistent kernel; null runs one block per unit.
+  int32_t* tickets;
 };
 hipError_t launch_grouped_gemm(const GemmLaunch& L, hipStream_t s);
 // Both GEMMs of the FFN in one launch (GEMM_SKINNY -- bf16, or block-FP8

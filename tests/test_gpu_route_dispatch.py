@@ -59,6 +59,19 @@ def test_route_shapes(E, k):
     check_route(torch, ml.Problem(T=T, H=128, E=E, k=k, e_lo=0, E_L=E, I=128), lg)
 
 
+@pytest.mark.parametrize("T,E,k", [(16401, 256, 8), (16384, 65, 3), (20000, 512, 20),
+                                   (16413, 12, 5)])
+def test_route_large_ragged(T, E, k):
+    """Prefill-sized token counts, ragged against the 16 tokens of a block (the
+    last rows run on the last token and store nothing)."""
+    torch = torch_cuda()
+    ml = _ml()
+    rng = np.random.default_rng(T + E * 7 + k)
+    lg = rng.standard_normal((T, E)).astype(np.float32) * 3
+    say("route large", T, E, k)
+    check_route(torch, ml.Problem(T=T, H=128, E=E, k=k, e_lo=0, E_L=E, I=128), lg)
+
+
 def test_route_ties_signed_zero_and_large():
     torch = torch_cuda()
     ml = _ml()

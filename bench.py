@@ -337,10 +337,11 @@ def main():
     cpu = None
     sample = args.cpu_sample_tokens
     if sample is None:
-        # about 10-30 s of CPU work
-        sample = {"tiny": 256, "qwen3_30b_prefill": 8192, "dsv3_ep8_prefill": 4096,
-                  "dsv3_ep8_prefill_fp8": 2048, "dsv3_ep8_decode": 64,
-                  "dsv3_ep8_prefill_mxfp4": 2048, "dsv3_ep8_decode_mxfp4": 64,
+        # about 10-30 s of CPU work on the GPU host (the block-FP8 and MX oracles
+        # dequantise every active expert's weights in float64 first: a fixed cost)
+        sample = {"tiny": 256, "qwen3_30b_prefill": 8192, "dsv3_ep8_prefill": 16384,
+                  "dsv3_ep8_prefill_fp8": 256, "dsv3_ep8_decode": 64,
+                  "dsv3_ep8_prefill_mxfp4": 256, "dsv3_ep8_decode_mxfp4": 64,
                   "dsv3_ep8_decode_fp8": 64}.get(cfg.name, 256)
     if sample > 0:
         cpu = cpu_baseline(cfg, d, sample)

@@ -99,10 +99,11 @@ def gemm_rows(counts, fp8: bool, max_pairs: int, E_L: int, mx: bool = False) -> 
     """Token rows the GEMMs compute, padding included, under the library's
     tile choice (from the most pairs per expert on average, T min(k, E_L) /
     E_L): bf16 32-row tiles up to 32; 128-row tiles up to 256; else 256-row
-    tiles (bf16: a last remainder of 1..128 rows takes a 128-row wide tile;
-    block-FP8 takes 32-row tiles up to 32 too).
+    tiles, 384-row from 2048 (bf16: a last remainder of 1..128 rows takes a
+    128-row wide tile; block-FP8 takes 32-row tiles up to 32 too).
     MX: 32-row tiles up to 32, 128-row up to 256, else 256-row tiles."""
     rows = 0
+    tall = max_pairs // E_L >= 2048
     for c in (int(x) for x in counts):
         if mx:
             r = max_pairs // E_L
@@ -115,8 +116,9 @@ def gemm_rows(counts, fp8: bool, max_pairs: int, E_L: int, mx: bool = False) -> 
         elif fp8:
             rows += -(-c // 256) * 256
         else:
-            rem = c % 256
-            rows += c - rem + (256 if rem > 128 else 128 if rem else 0)
+            bm = 384 if tall else 256
+            rem = c % bm
+            rows += c - rem + (bm if rem > 128 else 128 if rem else 0)
     return rows
 
 

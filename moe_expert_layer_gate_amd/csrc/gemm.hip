@@ -1546,14 +1546,20 @@ hipError_t launch_fused(const GemmArgs& gu, const GemmArgs& gd, int64_t max_tile
 }
 
 // ---------------------------------------------------------------------------
-// Large-tile bf16 kernel, 8 waves (two per SIMD), each wave 64 x 128 output
-// elements (2 x 4 MFMA 32x32 tiles).  Two block shapes share the code:
-//   full tile: 256 token rows x 256 weight rows, waves 4 (rows) x 2 (weights);
-//   wide tile: 128 token rows x 512 weight rows, waves 2 x 4 -- used for the
-//              last 1..128 rows of an expert's segment, which a full tile
-//              would cover with as much padding as work.
+// Large-tile bf16 kernel, 8 waves (two per SIMD), each wave WM x 128 output
+// elements (WM/32 x 4 MFMA 32x32 tiles).  Three block shapes share the code:
+//   full tile: 256 token rows x 256 weight rows, waves 4 (rows) x 2 (weights)
+//              of 64 x 128;
+//   tall tile: 384 token rows x 256 weight rows, waves 4 x 2 of 96 x 128 --
+//              the full tile of problems with many rows per expert;
+//   wide tile: 128 token rows x 512 weight rows, waves 2 x 4 of 64 x 128 --
+//              used for the last 1..128 rows of an expert's segment, which a
+//              full or tall tile would cover with as much padding as work.
 //  * Tile size: relative to a 128 x 256 tile the full tile moves a third
-//    fewer bytes from L2 per FLOP.
+//    fewer bytes from L2 per FLOP, the tall tile 17 % fewer again and reads
+//    22 % fewer fragment bytes from LDS per MFMA (a timing variant that ran
+//    1.5 times the MFMAs per K step on the same loads took 8 % (up GEMM) and
+//    13 % (down GEMM) less time per FLOP on the DeepSeek-V3-shaped shard).
 //  * Eight waves: direct-to-LDS loads complete at a rate set by how many
 //    waves have loads in flight (about 30 B/clk per CU from four waves, 50
 //    from eight, measured on the MI355X), and this tile needs ~32 B/clk per
@@ -1569,25 +1575,38 @@ hipError_t launch_fused(const GemmArgs& gu, const GemmArgs& gd, int64_t max_tile
 //    together on one XCD and share its weights in L2.
 // ---------------------------------------------------------------------------
 constexpr int kBigBM = 256, kBigBN = 256;
+constexpr int kTallBM = 384;
+// Rows per expert (the host's bound, N_cap / E_L) from which the tall tile
+// is the full tile.
+constexpr int kTallMinRows = 2048;
 constexpr int kWideBM = 128, kWideBN = 512;
 constexpr int kBigThreads = 512;
 constexpr int kBigRowBytes = 64;
 constexpr int kBigStages = 4;
 constexpr int kBigStageBytes = (kWideBM + kWideBN) * kBigRowBytes;  // 40 KB
 
-// Block shapes of the large-tile kernel body: token rows, weight rows, waves
-// (each 64 x 128), LDS stage size and ring depth.  Full and wide tiles share
-// one kernel and so one ring (40 KB stages).  (A 128 x 256 shape with four
+// Block shapes of the large-tile kernel body: token rows, weight rows, token
+// rows per wave (eight waves of WM x 128), LDS stage size and ring depth.
+// Full (or tall) and wide tiles share one kernel and so one ring (40 KB
+// stages).  (A 128 x 256 shape with four
 // waves and 72 KB, two blocks per CU so that one block's first loads and
 // epilogue overlap the other's main loop, measured 5-7 % slower.)
-template <int BM_, int BN_, int NW_, int STAGE_, int STAGES_>
+template <int BM_, int BN_, int WM_, int STAGE_, int STAGES_>
 struct TileShape {
-  static constexpr int BM = BM_, BN = BN_, NW = NW_, kStageBytes = STAGE_, kStages = STAGES_;
-  static_assert((BM / 64) * (BN / 128) == NW, "64 x 128 per wave");
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, kStageBytes = STAGE_, kStages = STAGES_;
+  static constexpr int kJ = WM / 32;          // 32-row token blocks per wave
+  static constexpr int kWaveRows = BM / WM;   // waves along the token rows
+  static constexpr int NW = kWaveRows * (BN / 128);
+  static_assert(NW == 8 && WM % 32 == 0 && BM % WM == 0, "eight waves of WM x 128");
   static_assert((BM + BN) * kBigRowBytes <= STAGE_, "a K step fits a stage");
+  static_assert(BM % (16 * NW) == 0 && BN % (16 * NW) == 0, "whole 16-row load groups per wave");
 };
-using FullShape = TileShape<kBigBM, kBigBN, 8, kBigStageBytes, kBigStages>;
-using WideShape = TileShape<kWideBM, kWideBN, 8, kBigStageBytes, kBigStages>;
+using FullShape = TileShape<kBigBM, kBigBN, 64, kBigStageBytes, kBigStages>;
+using TallShape = TileShape<kTallBM, kBigBN, 96, kBigStageBytes, kBigStages>;
+using WideShape = TileShape<kWideBM, kWideBN, 64, kBigStageBytes, kBigStages>;
+// The full-tile shape of BM token rows (256: full, 384: tall).
+template <int BM> struct FullTile { using type = FullShape; };
+template <> struct FullTile<kTallBM> { using type = TallShape; };
 
 
 // Work units of the large-tile GEMMs (see above).  Entry {expert, first row,
@@ -1663,14 +1682,14 @@ __global__ __launch_bounds__(1024) void unit_schedule_kernel(
   if (tickets && e < 2 * kXcds) tickets[e] = 0;  // per-XCD unit counters of both GEMMs
 }
 
-// Epilogue of a large-tile unit: the wave's 64 x 128 accumulators (token
-// rows wm*64.., weight rows wn*128.. of the tile) become bf16 y (staged
+// Epilogue of a large-tile unit: the wave's WM x 128 accumulators (token
+// rows wm*WM.., weight rows wn*128.. of the tile) become bf16 y (staged
 // through LDS for whole 256-byte row pieces), GELU h or SwiGLU h.  Every
 // wave must be past its last direct load and fragment read of the ring.
 template <int MODE, class SH>
-__device__ __forceinline__ void big_epilogue(const GemmArgs& g, f32x16 (&acc)[4][2], int row0,
+__device__ __forceinline__ void big_epilogue(const GemmArgs& g, f32x16 (&acc)[4][SH::kJ], int row0,
                                              int seg_end, int nbase, uint8_t* smem) {
-  constexpr int NW = SH::NW, kWaveRows = SH::BM / 64;
+  constexpr int NW = SH::NW, kWaveRows = SH::kWaveRows, WM = SH::WM, kJ = SH::kJ;
   constexpr int kStages = SH::kStages, kStageBytes = SH::kStageBytes;
   const int lane = lane_id(), w = threadIdx.x >> 6;
   const int wm = w % kWaveRows, wn = w / kWaveRows;
@@ -1678,40 +1697,51 @@ __device__ __forceinline__ void big_epilogue(const GemmArgs& g, f32x16 (&acc)[4]
   const int cq = (lane >> 5) * 4;
   uint16_t* C = static_cast<uint16_t*>(g.C);
   if constexpr (MODE == MODE_PLAIN) {
-    // The wave's 64 x 128 result goes through LDS so that the stores write
-    // whole 256-byte row pieces (16 lanes per row, 4 rows per instruction)
-    // instead of 16 bytes of 32 rows each.  Every wave is past its last
-    // fragment read and direct load once all have reached the barrier.
+    // The wave's WM x 128 result goes through LDS, 64 rows at a time, so
+    // that the stores write whole 256-byte row pieces (16 lanes per row, 4
+    // rows per instruction) instead of 16 bytes of 32 rows each.  Every wave
+    // is past its last fragment read and direct load once all have reached
+    // the barrier; then each wave uses its own 64-row region (its reads of a
+    // piece are done before it writes the next: LDS runs a wave's accesses
+    // in order).
     constexpr int kPitch = 272;  // 256 bytes + 16: rows start 4 banks apart
     static_assert(NW * 64 * kPitch <= kStages * kStageBytes, "epilogue tile fits the ring");
     __builtin_amdgcn_s_barrier();
     uint8_t* stile = smem + w * 64 * kPitch;
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          uint2 o;
-          o.x = pack_bf16x2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]);
-          o.y = pack_bf16x2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]);
-          *reinterpret_cast<uint2*>(stile + (j * 32 + lr) * kPitch + (i * 32 + q * 8 + cq) * 2) = o;
-        }
     const int col = nbase + wn * 128 + (lane & 15) * 8;
 #pragma unroll
-    for (int it = 0; it < 16; ++it) {
-      const int rl = it * 4 + (lane >> 4);
-      const uint4 v = *reinterpret_cast<const uint4*>(stile + rl * kPitch + (lane & 15) * 16);
-      const int m = row0 + wm * 64 + rl;
-      if (m < seg_end && col < g.Nout)
-        *reinterpret_cast<uint4*>(C + static_cast<int64_t>(m) * g.Nout + col) = v;
+    for (int j0 = 0; j0 < kJ; j0 += 2) {
+      constexpr int kPiece = 2;  // token blocks per piece (the last may hold one)
+      const int jn = kJ - j0 < kPiece ? kJ - j0 : kPiece;
+#pragma unroll
+      for (int jj = 0; jj < kPiece; ++jj) {
+        if (jj >= jn) break;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            uint2 o;
+            o.x = pack_bf16x2(acc[i][j0 + jj][q * 4 + 0], acc[i][j0 + jj][q * 4 + 1]);
+            o.y = pack_bf16x2(acc[i][j0 + jj][q * 4 + 2], acc[i][j0 + jj][q * 4 + 3]);
+            *reinterpret_cast<uint2*>(stile + (jj * 32 + lr) * kPitch + (i * 32 + q * 8 + cq) * 2) = o;
+          }
+      }
+#pragma unroll
+      for (int it = 0; it < 16; ++it) {
+        if (it >= jn * 8) break;
+        const int rl = it * 4 + (lane >> 4);
+        const uint4 v = *reinterpret_cast<const uint4*>(stile + rl * kPitch + (lane & 15) * 16);
+        const int m = row0 + wm * WM + j0 * 32 + rl;
+        if (m < seg_end && col < g.Nout)
+          *reinterpret_cast<uint4*>(C + static_cast<int64_t>(m) * g.Nout + col) = v;
+      }
     }
   } else if constexpr (MODE == MODE_GELU) {
     // h = gelu(x W1^T), panel or row major
     uint8_t* C8 = reinterpret_cast<uint8_t*>(C);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int m = row0 + wm * 64 + j * 32 + lr;
+    for (int j = 0; j < kJ; ++j) {
+      const int m = row0 + wm * WM + j * 32 + lr;
       if (m >= seg_end) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -1727,8 +1757,8 @@ __device__ __forceinline__ void big_epilogue(const GemmArgs& g, f32x16 (&acc)[4]
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int m = row0 + wm * 64 + j * 32 + lr;
+    for (int j = 0; j < kJ; ++j) {
+      const int m = row0 + wm * WM + j * 32 + lr;
       if (m >= seg_end) continue;
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb)
@@ -1759,9 +1789,10 @@ __device__ __forceinline__ void big_tile(const GemmArgs& g, const int4 unit, uin
   constexpr int kStages = SH::kStages, kStageBytes = SH::kStageBytes, kAhead = kStages - 1;
   constexpr int kWRegion = BM * kBigRowBytes;
   constexpr int kAGroups = BM / 16;                        // 16-row load groups
-  constexpr int kLoads = (BM + BN) / 16 / NW;              // per wave and step: 4, 5 or 6
-  constexpr int kALoads = kAGroups / NW;                   // of which A: 2, 1 or 2
-  constexpr int kWaveRows = BM / 64;                       // waves along the token rows
+  constexpr int kLoads = (BM + BN) / 16 / NW;              // per wave and step: 4 or 5
+  constexpr int kALoads = kAGroups / NW;                   // of which A: 2, 3 or 1
+  constexpr int kWaveRows = SH::kWaveRows, WM = SH::WM, kJ = SH::kJ;
+  constexpr int kFrag = 4 + kJ;                            // fragment reads per K half
 
   const int e = unit.x, row0 = unit.y, nidx = unit.z;
   const int seg_end = segment(g.seg, g.seg_cap, e).y;
@@ -1822,34 +1853,34 @@ __device__ __forceinline__ void big_tile(const GemmArgs& g, const int4 unit, uin
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) foff[kk] = lr * kBigRowBytes + (((2 * kk) | hi) ^ sl) * 16;
   // LDS row (in the weight region) of the wave's weight block i
-  int wbase[4], abase[2];
+  int wbase[4], abase[kJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = kSwiglu ? (i < 2 ? 0 : BN / 2) + wn * 64 + (i & 1) * 32 : wn * 128 + i * 32;
     wbase[i] = kWRegion + row * kBigRowBytes;
   }
 #pragma unroll
-  for (int j = 0; j < 2; ++j) abase[j] = (wm * 64 + j * 32) * kBigRowBytes;
+  for (int j = 0; j < kJ; ++j) abase[j] = (wm * WM + j * 32) * kBigRowBytes;
 
-  f32x16 acc[4][2];
+  f32x16 acc[4][kJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < kJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  bf16x8 fa[2][4], fb[2][2];
+  bf16x8 fa[2][4], fb[2][kJ];
   auto lfrag = [&](const uint8_t* st, int kk, int set) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) fa[set][i] = *reinterpret_cast<const bf16x8*>(st + wbase[i] + foff[kk]);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) fb[set][j] = *reinterpret_cast<const bf16x8*>(st + abase[j] + foff[kk]);
+    for (int j = 0; j < kJ; ++j) fb[set][j] = *reinterpret_cast<const bf16x8*>(st + abase[j] + foff[kk]);
   };
   auto mma = [&](int set, int first, int count) {
 #pragma unroll
     for (int q = first; q < first + count; ++q) {
-      const int i = q >> 1, j = q & 1;
+      const int i = q / kJ, j = q % kJ;
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j], acc[i][j], 0, 0, 0);
     }
   };
@@ -1858,6 +1889,27 @@ __device__ __forceinline__ void big_tile(const GemmArgs& g, const int4 unit, uin
   for (int st = 0; st < kAhead; ++st) dma(st, st);
   WAIT_VMCNT((kAhead - 1) * kLoads);
   __builtin_amdgcn_s_barrier();
+  if constexpr (kJ > 2) {
+    // 96-row waves: the 192 sums leave room for one set of fragments, so
+    // each K half reads its fragments and then runs its MFMAs (the other
+    // wave of the SIMD covers the read latency).
+    int s_cur = 0;
+    for (int kt = 0; kt < nk; ++kt) {
+      const uint8_t* cur = smem + s_cur * kStageBytes;
+      dma(kt + kAhead, s_cur == 0 ? kStages - 1 : s_cur - 1);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        lfrag(cur, kk, 0);
+        mma(0, 0, 4 * kJ);
+      }
+      WAIT_VMCNT_LDS((kAhead - 1) * kLoads);
+      __builtin_amdgcn_s_barrier();
+      s_cur = s_cur + 1 == kStages ? 0 : s_cur + 1;
+    }
+    WAIT_VMCNT(0);
+    big_epilogue<MODE, SH>(g, acc, row0, seg_end, nbase, smem);
+    return;
+  }
   lfrag(smem, 0, 0);
 
   int s_cur = 0;  // stage of step kt
@@ -1869,23 +1921,25 @@ __device__ __forceinline__ void big_tile(const GemmArgs& g, const int4 unit, uin
     // step; it takes step kt + kAhead.
     dma(kt + kAhead, s_cur == 0 ? kStages - 1 : s_cur - 1);
     lfrag(cur, 1, 1);
-    mma(0, 0, 8);
+    mma(0, 0, 4 * kJ);
+    // the second K half's fragment reads and the step's loads go between
+    // the first half's MFMAs
 #pragma unroll
-    for (int q = 0; q < 6; ++q) {
+    for (int q = 0; q < kFrag; ++q) {
       SCHED(kSchedMfma, 1);
       SCHED(kSchedDsRead, 1);
       if (q < kLoads) SCHED(kSchedVmemRead, 1);
     }
-    SCHED(kSchedMfma, 2);
-    mma(1, 0, 4);
+    SCHED(kSchedMfma, 4 * kJ - kFrag);
+    mma(1, 0, 2 * kJ);
     // Step boundary: step kt+1 has landed once only the later steps are in
     // flight; this wave's reads of stage kt are done.
     WAIT_VMCNT_LDS((kAhead - 1) * kLoads);
     __builtin_amdgcn_s_barrier();
     lfrag(nxt, 0, 0);
-    mma(1, 4, 4);
+    mma(1, 2 * kJ, 2 * kJ);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 2 * kJ; ++q) {
       SCHED(kSchedDsRead, 2);
       SCHED(kSchedMfma, 1);
     }
@@ -1920,17 +1974,17 @@ __device__ __forceinline__ void big_tile_wide(const GemmArgs& g, const int4 unit
   big_tile<MODE, WideShape>(g, unit, smem);
 }
 
-template <int MODE>
+template <int MODE, int BM_>
 struct BigChain {
-  using SH = FullShape;
+  using SH = typename FullTile<BM_>::type;
   static constexpr bool kSwiglu = MODE == MODE_SWIGLU;
   static constexpr int BM = SH::BM, BN = SH::BN, NW = SH::NW;
   static constexpr int kStages = SH::kStages, kStageBytes = SH::kStageBytes;
   static constexpr int kAhead = kStages - 1;
   static constexpr int kWRegion = BM * kBigRowBytes;
   static constexpr int kAGroups = BM / 16;
-  static constexpr int kLoads = (BM + BN) / 16 / NW;   // 4
-  static constexpr int kALoads = kAGroups / NW;        // 2
+  static constexpr int kLoads = (BM + BN) / 16 / NW;   // 4 (full) or 5 (tall)
+  static constexpr int kALoads = kAGroups / NW;        // 2 or 3
 
   // Load addressing of one unit (lane offsets, buffer views) and its place.
   struct Unit {
@@ -1991,13 +2045,15 @@ struct BigChain {
   }
 };
 
-template <int MODE>
+template <int MODE, int BM>
 __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_persistent_kernel(const GemmArgs g) {
-  using C = BigChain<MODE>;
+  using C = BigChain<MODE, BM>;
   using SH = typename C::SH;
   constexpr int kStages = C::kStages, kStageBytes = C::kStageBytes, kAhead = C::kAhead;
   constexpr int kLoads = C::kLoads;
   constexpr bool kSwiglu = C::kSwiglu;
+  constexpr int WM = SH::WM, kJ = SH::kJ, kFrag = 4 + kJ;
+  static_assert(kJ == 2, "the chained kernel runs 64-row waves (two fragment sets)");
   // The ring takes the whole LDS (no static __shared__ variable fits beside
   // it): the ticket is passed through a word of a stage that holds nothing
   // in flight or still to be read (slot, a byte offset).
@@ -2020,32 +2076,32 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_persistent_kernel(con
   const int nk = 2 * g.K / kBigRowBytes;
 
   const int lane = lane_id(), w = threadIdx.x >> 6;
-  const int wm = w % 4, wn = w / 4;
+  const int wm = w % SH::kWaveRows, wn = w / SH::kWaveRows;
   const int lr = lane & 31, hi = lane >> 5, sl = (lr >> 2) & 3;
   int foff[2];
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) foff[kk] = lr * kBigRowBytes + (((2 * kk) | hi) ^ sl) * 16;
-  int wbase[4], abase[2];
+  int wbase[4], abase[kJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = kSwiglu ? (i < 2 ? 0 : SH::BN / 2) + wn * 64 + (i & 1) * 32 : wn * 128 + i * 32;
     wbase[i] = C::kWRegion + row * kBigRowBytes;
   }
 #pragma unroll
-  for (int j = 0; j < 2; ++j) abase[j] = (wm * 64 + j * 32) * kBigRowBytes;
+  for (int j = 0; j < kJ; ++j) abase[j] = (wm * WM + j * 32) * kBigRowBytes;
 
-  f32x16 acc[4][2];
-  bf16x8 fa[2][4], fb[2][2];
+  f32x16 acc[4][kJ];
+  bf16x8 fa[2][4], fb[2][kJ];
   auto lfrag = [&](const uint8_t* st, int kk, int set) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) fa[set][i] = *reinterpret_cast<const bf16x8*>(st + wbase[i] + foff[kk]);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) fb[set][j] = *reinterpret_cast<const bf16x8*>(st + abase[j] + foff[kk]);
+    for (int j = 0; j < kJ; ++j) fb[set][j] = *reinterpret_cast<const bf16x8*>(st + abase[j] + foff[kk]);
   };
   auto mma = [&](int set, int first, int count) {
 #pragma unroll
     for (int q = first; q < first + count; ++q) {
-      const int i = q >> 1, j = q & 1;
+      const int i = q / kJ, j = q % kJ;
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j], acc[i][j], 0, 0, 0);
     }
   };
@@ -2053,7 +2109,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_persistent_kernel(con
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < kJ; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
   };
@@ -2096,21 +2152,21 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_persistent_kernel(con
         else
           C::dma(g, nxt, chain, ls - nk, lstage, smem);
         lfrag(st_cur, 1, 1);
-        mma(0, 0, 8);
+        mma(0, 0, 4 * kJ);
 #pragma unroll
-        for (int q = 0; q < 6; ++q) {
+        for (int q = 0; q < kFrag; ++q) {
           SCHED(kSchedMfma, 1);
           SCHED(kSchedDsRead, 1);
           if (q < kLoads) SCHED(kSchedVmemRead, 1);
         }
-        SCHED(kSchedMfma, 2);
-        mma(1, 0, 4);
+        SCHED(kSchedMfma, 4 * kJ - kFrag);
+        mma(1, 0, 2 * kJ);
         WAIT_VMCNT_LDS((kAhead - 1) * kLoads);
         __builtin_amdgcn_s_barrier();
         lfrag(st_nxt, 0, 0);
-        mma(1, 4, 4);
+        mma(1, 2 * kJ, 2 * kJ);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < 2 * kJ; ++q) {
           SCHED(kSchedDsRead, 2);
           SCHED(kSchedMfma, 1);
         }
@@ -2128,7 +2184,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_persistent_kernel(con
   }
 }
 
-template <int MODE>
+template <int MODE, int BM>
 __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const GemmArgs g) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   const int total = *g.n_tiles;
@@ -2141,7 +2197,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void gemm_big_kernel(const GemmArgs
   if (unit.w)
     big_tile_wide<MODE>(g, unit, smem);
   else
-    big_tile<MODE, FullShape>(g, unit, smem);
+    big_tile<MODE, typename FullTile<BM>::type>(g, unit, smem);
 }
 
 
@@ -2163,14 +2219,17 @@ inline int device_cus() {
   return n;
 }
 
-template <int MODE>
+template <int MODE, int BM>
 hipError_t launch_big(const GemmArgs& g, int64_t max_units, hipStream_t s) {
   static_assert(kBigStages * kBigStageBytes <= 160 * 1024, "the ring fits the CU's LDS");
   const size_t lds = kBigStages * kBigStageBytes;
-  auto kern = gemm_big_kernel<MODE>;
-  if constexpr (MODE == MODE_SWIGLU || MODE == MODE_GELU) {
+  auto kern = gemm_big_kernel<MODE, BM>;
+  // Persistent for the 256-row tile only: with 96-row waves the two units'
+  // load state the chain holds does not fit beside the 192 sums (it spilled
+  // to scratch and ran 9 % slower than one block per unit).
+  if constexpr ((MODE == MODE_SWIGLU || MODE == MODE_GELU) && BM == kBigBM) {
     if (g.tickets) {  // persistent: one block per CU (at most one unit each, at least 8)
-      auto pkern = gemm_big_persistent_kernel<MODE>;
+      auto pkern = gemm_big_persistent_kernel<MODE, BM>;
       static std::atomic<uint64_t> lds_set_p{0};
       allow_dynamic_lds(reinterpret_cast<const void*>(pkern), static_cast<int>(lds), lds_set_p);
       int64_t blocks = device_cus();
@@ -2522,7 +2581,9 @@ GemmPath gemm_path(bool fp8, int64_t rows_per_expert) {
   if (rows_per_expert <= kSkBM) return GEMM_SKINNY;
   if (fp8) return (kF8BM == kBM || rows_per_expert > 2 * kBM) ? GEMM_LARGE_FP8 : GEMM_PIPELINED;
   if (rows_per_expert <= 2 * kBM) return GEMM_PIPELINED;
-  return GEMM_LARGE;
+  // Many rows per expert: 384-row tiles (fewer bytes per FLOP; their
+  // padding, a segment's last 129..383 rows, is then a small share).
+  return rows_per_expert >= kTallMinRows ? GEMM_LARGE_TALL : GEMM_LARGE;
 }
 
 int gemm_path_rows(GemmPath path) {
@@ -2530,6 +2591,7 @@ int gemm_path_rows(GemmPath path) {
     case GEMM_SKINNY: return kSkBM;
     case GEMM_PIPELINED: return kBM;
     case GEMM_LARGE: return kBigBM;
+    case GEMM_LARGE_TALL: return kTallBM;
     case GEMM_LARGE_FP8: return kF8BM;
     case GEMM_MX: return 128;
     case GEMM_MX_LARGE: return 256;
@@ -2539,7 +2601,7 @@ int gemm_path_rows(GemmPath path) {
 }
 
 bool gemm_unit_tables(GemmPath path) {
-  return path == GEMM_LARGE || path == GEMM_LARGE_FP8;
+  return path == GEMM_LARGE || path == GEMM_LARGE_TALL || path == GEMM_LARGE_FP8;
 }
 
 int gemm_n_tiles(bool swiglu, int Nout) {
@@ -2556,9 +2618,9 @@ hipError_t launch_schedule(const int32_t* seg, int seg_cap, int E_L, GemmPath pa
                            int nt_dn, int4* tab_up, int32_t* n_up, int4* tab_dn, int32_t* n_dn,
                            int32_t* sync, int32_t* status, hipStream_t s) {
   const int bm = gemm_path_rows(path);
-  if (gemm_unit_tables(path))  // only the bf16 256-row path has wide tiles
+  if (gemm_unit_tables(path))  // only the bf16 paths have wide tiles
     hipLaunchKernelGGL(unit_schedule_kernel, dim3(1), dim3(1024), 0, s, seg, seg_cap, E_L, nt_up,
-                       nt_dn, bm, path == GEMM_LARGE, tab_up, n_up, tab_dn, n_dn, status, sync);
+                       nt_dn, bm, gemm_large_bf16(path), tab_up, n_up, tab_dn, n_dn, status, sync);
   else
     hipLaunchKernelGGL(tile_schedule_kernel, dim3(1), dim3(1024), 0, s, seg, seg_cap, E_L, bm,
                        tab_up, n_up, sync, status);
@@ -2636,9 +2698,13 @@ hipError_t launch_grouped_gemm(const GemmLaunch& L, hipStream_t s) {
   if (err != hipSuccess) return err;
   switch (L.path) {
     case GEMM_LARGE:
-      if (L.gelu) return launch_big<MODE_GELU>(g, L.max_tiles, s);
-      return L.swiglu ? launch_big<MODE_SWIGLU>(g, L.max_tiles, s)
-                      : launch_big<MODE_PLAIN>(g, L.max_tiles, s);
+      if (L.gelu) return launch_big<MODE_GELU, kBigBM>(g, L.max_tiles, s);
+      return L.swiglu ? launch_big<MODE_SWIGLU, kBigBM>(g, L.max_tiles, s)
+                      : launch_big<MODE_PLAIN, kBigBM>(g, L.max_tiles, s);
+    case GEMM_LARGE_TALL:
+      if (L.gelu) return launch_big<MODE_GELU, kTallBM>(g, L.max_tiles, s);
+      return L.swiglu ? launch_big<MODE_SWIGLU, kTallBM>(g, L.max_tiles, s)
+                      : launch_big<MODE_PLAIN, kTallBM>(g, L.max_tiles, s);
     case GEMM_SKINNY:
     case GEMM_MX_SKINNY:
       return hipErrorInvalidValue;  // both GEMMs at once: launch_ffn_fused

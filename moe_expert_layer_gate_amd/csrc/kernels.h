@@ -57,9 +57,14 @@ enum GemmPath {
   GEMM_MX = 4,         // MXFP4 weights x MXFP8 activations: 128 x 256 tiles
   GEMM_MX_LARGE = 5,   // the same, more than 256 rows per expert: 256 x 256 tiles
   GEMM_MX_SKINNY = 6,  // the same, up to 32 rows per expert: 32 x 256 tiles (decode)
+  GEMM_LARGE_TALL = 7, // bf16, many rows per expert: 384 x 256 tiles, 128 x 512 remainders
 };
+// The bf16 large-tile paths (per-XCD unit counters, wide remainder tiles).
+inline bool gemm_large_bf16(GemmPath path) {
+  return path == GEMM_LARGE || path == GEMM_LARGE_TALL;
+}
 GemmPath gemm_path(bool fp8, int64_t rows_per_expert);
-// Token rows of the path's tiles (of its full tiles, for GEMM_LARGE).
+// Token rows of the path's tiles (of its full tiles, for the bf16 large-tile paths).
 int gemm_path_rows(GemmPath path);
 // Whether the GEMMs run from per-GEMM unit tables (large-tile kernels) or
 // from one m-tile table shared by both GEMMs (skinny and pipelined kernels).
@@ -114,7 +119,7 @@ struct GemmLaunch {
   // Fused gather (bf16, row-major A only): permuted row j of the GEMM is row
   // a_index[j] of A, e.g. A = the layer input x and a_index = row_token.
   const int32_t* a_index;
-  // GEMM_LARGE: this GEMM's 8 per-XCD unit counters (from launch_schedule's
+  // bf16 large tiles: this GEMM's 8 per-XCD unit counters (from launch_schedule's
   // sync), for the persistent kernel; null runs one block per unit.
   int32_t* tickets;
 };

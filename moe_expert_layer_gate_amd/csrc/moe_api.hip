@@ -178,7 +178,7 @@ FfnScratch carve_ffn(Carve& c, const moe_problem* p) {
   f.tab_up = c.take<int4>(sizeof(int4) * sh.cap_up);
   f.n_up = c.take<int32_t>(sizeof(int32_t));
   if (fused_ffn(sh.path)) f.sync = c.take<int32_t>(sizeof(int32_t) * (1 + sh.cap_up));
-  if (sh.path == GEMM_LARGE) f.sync = c.take<int32_t>(sizeof(int32_t) * kTicketWords);
+  if (gemm_large_bf16(sh.path)) f.sync = c.take<int32_t>(sizeof(int32_t) * kTicketWords);
   if (!gemm_unit_tables(sh.path)) {  // one m-tile table for both GEMMs
     f.tab_dn = f.tab_up;
     f.n_dn = f.n_up;
@@ -330,7 +330,7 @@ moe_status run_ffn(const moe_problem* p, const FfnSource& src, const int32_t* se
   up.a_rows = src.index ? src.src_rows : N;
   up.c_rows = N;
   up.a_index = src.index;
-  up.tickets = sh.path == GEMM_LARGE ? f.sync : nullptr;
+  up.tickets = gemm_large_bf16(sh.path) ? f.sync : nullptr;
   GemmLaunch down = up;
   down.swiglu = false;
   down.gelu = false;
@@ -349,7 +349,7 @@ moe_status run_ffn(const moe_problem* p, const FfnSource& src, const int32_t* se
   down.c_panel = false;
   down.a_rows = N;
   down.a_index = nullptr;
-  down.tickets = sh.path == GEMM_LARGE ? f.sync + kTicketWords / 2 : nullptr;
+  down.tickets = gemm_large_bf16(sh.path) ? f.sync + kTicketWords / 2 : nullptr;
   if (fused_ffn(sh.path)) {
     MOE_TRY(launch_ffn_fused(up, down, f.sync, f.status, s));
   } else {

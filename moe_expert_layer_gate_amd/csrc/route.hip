@@ -12,12 +12,12 @@
 // and remove it; slot s holds the key of round s.
 //
 // Up to 512 experts: one token per 16-lane row of a wave (four tokens per
-// wave), each lane holding E/16 keys in registers.  A round is a max over the
-// lane's keys and four DPP steps inside the row (no cross-row exchange, so no
-// LDS-routed shuffles on the dependent chain), and the wave works on four
-// tokens at once.  A row's loads are 16-byte pieces of its token's logits,
-// 256 contiguous bytes per instruction.  Beyond 512 experts: one token per
-// wave (keys E/64 per lane, the max over the whole wave).
+// wave), each lane holding E/16 keys in registers, sorted once.  A round is
+// four DPP max steps over the lanes' first keys inside the row (no cross-row
+// exchange, so no LDS-routed shuffles on the dependent chain), and the wave
+// works on four tokens at once.  A row's loads are 16-byte pieces of its
+// token's logits, 256 contiguous bytes per instruction.  Beyond 512 experts:
+// one token per wave (keys E/64 per lane, the max over the whole wave).
 #include "common.h"
 #include "kernels.h"
 

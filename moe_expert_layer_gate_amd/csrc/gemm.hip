@@ -1570,9 +1570,10 @@ hipError_t launch_fused(const GemmArgs& gu, const GemmArgs& gd, int64_t max_tile
 //    chunk ^ ((row >> 2) & 3): the 16 rows read together by one fragment load
 //    cover every (row mod 4, chunk) pair, i.e. all LDS banks once.
 //  * Work table: one entry per (tile, n-range) unit, built on the device:
-//    for each expert, its full tiles for every n-tile (m-tile fastest), then
-//    its wide tile for every 512-row n-range, so an expert's units run
-//    together on one XCD and share its weights in L2.
+//    for each expert, its full tiles for every n-tile (in groups of 8
+//    m-tiles, n-tile-major inside a group), then its wide tile for every
+//    512-row n-range, cut into 8 contiguous ranges, one per XCD, so an
+//    expert's units run together on one XCD and share its operands in L2.
 // ---------------------------------------------------------------------------
 constexpr int kBigBM = 256, kBigBN = 256;
 constexpr int kTallBM = 384;
@@ -1610,9 +1611,9 @@ template <> struct FullTile<kTallBM> { using type = TallShape; };
 
 
 // Work units of the large-tile GEMMs (see above).  Entry {expert, first row,
-// n-index, wide}: the n-index counts 256-row weight tiles of a full tile or
-// 512-row ranges of a wide one.  An expert with 129..255 rows past its last
-// full tile gets one more full tile instead of a wide one.
+// n-index, wide}: the n-index counts 256-row weight tiles of a full (or tall)
+// tile or 512-row ranges of a wide one.  An expert with 129..bm-1 rows past
+// its last full tile gets one more full tile instead of a wide one.
 __device__ __forceinline__ void expert_units(int cnt, int bm, bool allow_wide, int& full,
                                              int& wide) {
   full = cnt / bm;

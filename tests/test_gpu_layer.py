@@ -188,16 +188,18 @@ def test_large_tile_segment_remainders(H, I, fp8):
     check_small_case(f"remainders H={H} I={I} fp8={fp8}", cfg, d, dev)
 
 
-@pytest.mark.parametrize("H,I", [(384, 384), (640, 256)])
-def test_tall_tile_segment_remainders(H, I):
+@pytest.mark.parametrize("H,I,act", [(384, 384, "swiglu"), (640, 256, "swiglu"),
+                                     (640, 256, "gelu")])
+def test_tall_tile_segment_remainders(H, I, act):
     """bf16 with at least 2048 rows per expert (the host's bound T k / E_L)
     takes 384-row tiles: segments whose remainders past the last one are 1,
     44, 128 (128-row wide tiles), 129, 255, 256, 383 (one more tall tile) and
-    0, with the odd n-tile counts of the test above."""
+    0, with the odd n-tile counts of the test above; SwiGLU and GELU
+    epilogues."""
     torch_cuda()
     ml, dv = _mods()
     counts = [5 * 384 + r for r in (1, 44, 128, 129, 255, 383, 384, 256)]
-    cfg = small_cfg(T=sum(counts), H=H, E=8, E_L=8, k=1, I=I)
+    cfg = small_cfg(T=sum(counts), H=H, E=8, E_L=8, k=1, I=I, act=act)
     assert cfg.T // 8 >= 2048
     d = synth.make_inputs(cfg, 17, x_std=1.0, std=0.05)
     rng = np.random.default_rng(17)
@@ -207,7 +209,7 @@ def test_tall_tile_segment_remainders(H, I):
     lg[np.arange(cfg.T), expert] += 20.0
     d["logits"] = lg
     dev = dv.upload(d, False)
-    check_small_case(f"tall remainders H={H} I={I}", cfg, d, dev)
+    check_small_case(f"tall remainders H={H} I={I} {act}", cfg, d, dev)
 
 
 def check_small_case(name, cfg, d, dev):

@@ -593,7 +593,7 @@ def cpu_baseline(cfg, d, sample):
     from threadpoolctl import threadpool_info, threadpool_limits
 
     from oracle import moe_oracle as O
-    # every CPU this process may use (the host's share of the GPU machine), capped
+    # every CPU this process may use (this host's share for the GPU), capped
     # by OMP_NUM_THREADS where the environment sets one
     ncpu = len(os.sched_getaffinity(0))
     want = min(ncpu, int(os.environ.get("OMP_NUM_THREADS", ncpu) or ncpu))

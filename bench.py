@@ -15,9 +15,11 @@ The same kernels are then issued one library call per stage, so that the
 grouped FFN's launches can be bracketed by HIP events on their stream: that
 gives `stage_ms`, the small stages' GB/s, and the grouped FFN's TFLOP/s
 against the MFMA peak (or, for few rows per expert, its bytes/s against HBM)
-as `roofline`.  Prints ONE JSON line, with the GPU's clock and power under
-load, the host, and the CPU oracle on a bounded sample of the same workload
-as `cpu_baseline`.
+as `roofline`.  Decode-sized batches also report the whole layer's bytes/s
+against HBM.  A working set below 512 MB (it would stay in the MALL between
+back-to-back calls) is also timed call by call after a 512 MB write.  Prints
+ONE JSON line, with the GPU's clock and power under load, the host, and the
+CPU oracle on a bounded sample of the same workload as `cpu_baseline`.
 """
 from __future__ import annotations
 
@@ -39,7 +41,8 @@ PEAK_HBM_GBS = 8000.0
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 20; 200 for the latency-bound tiny workload)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dsv3_ep8_prefill")
     ap.add_argument("--seed", type=int, default=None)
@@ -138,6 +141,8 @@ def main():
 
     cfg = synth.config(args.workload)
     seed = args.seed if args.seed is not None else 2
+    if args.steps is None:
+        args.steps = 200 if cfg.name == "tiny" else 20
     dev_id = int(os.environ.get("LOCAL_RANK", "0"))
     torch.cuda.set_device(dev_id)
     d = synth.make_inputs(cfg, seed)
@@ -242,6 +247,28 @@ def main():
     tokens_per_s = T * args.steps / elapsed
     layer_ms = [lev[i].elapsed_time(lev[i + 1]) for i in range(args.steps)]
 
+    # A working set that fits the 256 MB MALL would be timed from the cache
+    # by back-to-back calls: then each call is also timed alone after a
+    # 512 MB write that evicts it (reported beside the headline).
+    ws_bytes = sum(t_.numel() * t_.element_size() for t_ in dev.values()
+                   if isinstance(t_, torch.Tensor))
+    flushed = None
+    if ws_bytes < (512 << 20) and not args.no_extras:
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        fl = []
+        for _ in range(min(args.steps, 50)):
+            scratch.fill_(1)
+            a_ = torch.cuda.Event(enable_timing=True)
+            b_ = torch.cuda.Event(enable_timing=True)
+            a_.record(stream)
+            layer()
+            b_.record(stream)
+            torch.cuda.synchronize()
+            fl.append(a_.elapsed_time(b_))
+        del scratch
+        flushed = {"median": round(float(np.median(fl)), 4), "min": round(float(np.min(fl)), 4),
+                   "working_set_bytes": int(ws_bytes)}
+
     # ---- the same kernels one library call per stage, so that the grouped
     # FFN's launches can be bracketed by events on their stream ----
     for _ in range(args.warmup):
@@ -318,12 +345,20 @@ def main():
               + (" (+ shared expert: x quantisation and its FFN)" if p.I_s else ""))
     # Few rows per expert: the FFN streams weights and is bound by HBM.
     decode = n_pairs < 64 * max(active, 1)
+    decode_layer = None
     if decode:
         # weight streaming: every active expert's W13 and W2 once, plus the
         # token rows in and out of both GEMMs
         bytes_ = int(active * (p.m + 1) * p.H * p.I * beta_w
                      + n_pairs * (p.H * beta_a + 2 * p.I * beta_a + 2 * p.H))
         achieved = bytes_ / (ffn_ms * 1e-3) / 1e9
+        # the whole layer against HBM: those weights, x in, y out, the
+        # logits and the index bytes, over the one-call layer's median step
+        layer_bytes = int(active * (p.m + 1) * p.H * p.I * beta_w + 2 * p.T * p.H * 2
+                          + p.T * p.E * 4 + p.T * p.k * 16)
+        layer_gbs = layer_bytes / (float(np.median(layer_ms)) * 1e-3) / 1e9
+        decode_layer = {"bytes": layer_bytes, "gbs": round(layer_gbs, 1),
+                        "frac_hbm": round(layer_gbs / PEAK_HBM_GBS, 4)}
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
                 "kernel": kernel, "work_per_launch": {"bytes": bytes_},
@@ -374,6 +409,8 @@ def main():
         "step_ms": {"median": round(float(np.median(layer_ms)), 4),
                     "min": round(float(np.min(layer_ms)), 4),
                     "mean": round(float(np.mean(layer_ms)), 4)},
+        "step_ms_mall_flushed": flushed,
+        "decode_layer_hbm": decode_layer,
         "stage_ms": {k2: round(v, 4) for k2, v in stage_ms.items()},
         "stage_gbs": stage_rates,
         "staged_calls": {"tokens_per_s": round(staged_tps, 1), "same_output_bits": same},

@@ -404,6 +404,8 @@ def main():
                    "expert_layout": f"masked (capacity {cap})" if cap else "contiguous"},
         "grouped_ffn_tflops": round(ffn_tflops, 2),
         "grouped_ffn_frac_of_peak": round(ffn_tflops / PEAK_TFLOPS[dtype], 4),
+        # quantised paths: the same rate against the bf16 peak as well
+        "grouped_ffn_frac_of_bf16_peak": round(ffn_tflops / PEAK_TFLOPS["bf16"], 4),
         "timed": "moe_layer, one call per step; value = tokens x steps / wall time "
                  "between synchronisations",
         "step_ms": {"median": round(float(np.median(layer_ms)), 4),

@@ -124,8 +124,9 @@ __global__ __launch_bounds__(1024) void index_scan_kernel(
     }
   }
   int total;
-  const int off = block_exclusive_scan(threadIdx.x < E_L ? run : 0, &total);
-  if (threadIdx.x < E_L) {
+  const bool first_part = static_cast<int>(threadIdx.x) < E_L;  // part 0: one thread per expert
+  const int off = block_exclusive_scan(first_part ? run : 0, &total);
+  if (first_part) {
     counts[e] = run;
     offsets[e] = cap ? e * cap : off;
   }

@@ -46,6 +46,32 @@ def _draw_cases(n=24, seed=20261203):
 CASES = _draw_cases()
 
 
+def _draw_tall_cases(n=4, seed=20261204):
+    """bf16 cases with at least 2048 rows per local expert by the host's bound
+    (T min(k, E_L) / E_L, or the capacity C in the masked layout), so the
+    large-tile GEMMs run 384-row tiles: ragged T, small H and I."""
+    rng = np.random.default_rng(seed)
+    cases = {}
+    for i in range(n):
+        E = int(rng.choice([4, 8]))
+        E_L = int(rng.choice([d for d in (1, 2, 4) if d <= E]))
+        k = int(rng.integers(1, 3))
+        kk = min(k, E_L)
+        T = int(2048 * E_L / kk) + int(rng.integers(1, 700))
+        H = int(rng.choice([128, 256]))
+        I = int(rng.choice([128, 384]))
+        act = "gelu" if i % 2 else "swiglu"
+        cap = T + int(rng.integers(0, 9)) if i == n - 1 else None
+        cfg = small_cfg(T=T, H=H, E=E, E_L=E_L, e_lo=int(rng.integers(0, E - E_L + 1)), k=k,
+                        I=I, act=act, logits="gumbel_zipf")
+        name = (f"tall{i}_{act}_T{T}_H{H}_I{I}_E{E}_L{E_L}_k{k}" + (f"_C{cap}" if cap else ""))
+        cases[name] = (cfg, cap, 2000 + i)
+    return cases
+
+
+CASES.update(_draw_tall_cases())
+
+
 @pytest.mark.parametrize("name", list(CASES))
 def test_random_config(name):
     torch = torch_cuda()

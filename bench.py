@@ -102,11 +102,11 @@ def gemm_rows(counts, fp8: bool, max_pairs: int, E_L: int, mx: bool = False) -> 
     """Token rows the GEMMs compute, padding included, under the library's
     tile choice (from the most pairs per expert on average, T min(k, E_L) /
     E_L): bf16 32-row tiles up to 32; 128-row tiles up to 256; else 256-row
-    tiles, 384-row from 2048 (bf16: a last remainder of 1..128 rows takes a
+    tiles, 384-row from 1536 (bf16: a last remainder of 1..128 rows takes a
     128-row wide tile; block-FP8 takes 32-row tiles up to 32 too).
     MX: 32-row tiles up to 32, 128-row up to 256, else 256-row tiles."""
     rows = 0
-    tall = max_pairs // E_L >= 2048
+    tall = max_pairs // E_L >= 1536
     for c in (int(x) for x in counts):
         if mx:
             r = max_pairs // E_L

@@ -191,7 +191,7 @@ def test_large_tile_segment_remainders(H, I, fp8):
 @pytest.mark.parametrize("H,I,act", [(384, 384, "swiglu"), (640, 256, "swiglu"),
                                      (640, 256, "gelu")])
 def test_tall_tile_segment_remainders(H, I, act):
-    """bf16 with at least 2048 rows per expert (the host's bound T k / E_L)
+    """bf16 with at least 1536 rows per expert (the host's bound T k / E_L)
     takes 384-row tiles: segments whose remainders past the last one are 1,
     44, 128 (128-row wide tiles), 129, 255, 256, 383 (one more tall tile) and
     0, with the odd n-tile counts of the test above; SwiGLU and GELU
@@ -200,7 +200,7 @@ def test_tall_tile_segment_remainders(H, I, act):
     ml, dv = _mods()
     counts = [5 * 384 + r for r in (1, 44, 128, 129, 255, 383, 384, 256)]
     cfg = small_cfg(T=sum(counts), H=H, E=8, E_L=8, k=1, I=I, act=act)
-    assert cfg.T // 8 >= 2048
+    assert cfg.T // 8 >= 1536
     d = synth.make_inputs(cfg, 17, x_std=1.0, std=0.05)
     rng = np.random.default_rng(17)
     expert = np.repeat(np.arange(8), counts)

@@ -47,7 +47,7 @@ CASES = _draw_cases()
 
 
 def _draw_tall_cases(n=4, seed=20261204):
-    """bf16 cases with at least 2048 rows per local expert by the host's bound
+    """bf16 cases with at least 1536 rows per local expert by the host's bound
     (T min(k, E_L) / E_L, or the capacity C in the masked layout), so the
     large-tile GEMMs run 384-row tiles: ragged T, small H and I."""
     rng = np.random.default_rng(seed)

@@ -315,9 +315,12 @@ __global__ __launch_bounds__(256) void pack_scales_mx_kernel(const uint32_t* __r
 // Row gather with per-128 group E4M3 quantisation: scale = amax/448 (1 for an
 // all-zero group), code = RNE(v / scale) (IEEE fp32 division) saturated.
 // A group of 128 bf16 is 16 lanes x 8 values; a wave covers 4 groups per step.
+// `parts` waves share a row, each taking every parts-th 64-lane pass of it (a
+// few rows -- a decode batch -- would otherwise run their passes one after
+// another in one wave each).
 __global__ __launch_bounds__(256) void gather_rows_fp8_kernel(
     const uint4* __restrict__ src, const int32_t* __restrict__ rows,
-    const int32_t* __restrict__ n_rows, int n_rows_host, int H,
+    const int32_t* __restrict__ n_rows, int n_rows_host, int H, int parts,
     const int32_t* __restrict__ counts, int cap,
     uint2* __restrict__ dst, float* __restrict__ dst_scale) {
   const int n = n_rows ? *n_rows : n_rows_host;
@@ -325,14 +328,17 @@ __global__ __launch_bounds__(256) void gather_rows_fp8_kernel(
   const int groups = H >> 7;
   const int wpb = blockDim.x >> 6;
   const int lane = lane_id();
-  for (int j = blockIdx.x * wpb + (threadIdx.x >> 6); j < n; j += gridDim.x * wpb) {
+  const int gw = blockIdx.x * wpb + (threadIdx.x >> 6);
+  const int part = gw % parts, slot = gw / parts, slots = gridDim.x * wpb / parts;
+  if (slot >= slots) return;  // uniform over the wave
+  for (int j = slot; j < n; j += slots) {
     if (!masked_row_used(counts, cap, j)) continue;  // uniform over the wave
     const int r = rows ? rows[j] : j;
     const uint4* s = src + static_cast<size_t>(r) * chunks;
     uint2* d = dst + static_cast<size_t>(j) * chunks;
     // chunks is a multiple of 16, so the 16 lanes of a group are all active or
     // all idle in every step, and the xor-shuffles below stay inside a group.
-    for (int c = lane; c < chunks; c += kWave) {
+    for (int c = part * kWave + lane; c < chunks; c += kWave * parts) {
       const uint4 v = s[c];
       float f[8];
       const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
@@ -470,24 +476,27 @@ __global__ __launch_bounds__(256) void quant_mx4_kernel(const uint4* __restrict_
 
 // Row gather with MXFP8 packing: dst[j] = E4M3 codes of src[rows[j]] with one
 // E8M0 scale per 32 elements (rows == nullptr: identity); masked-layout rows
-// that hold no pair are skipped.  One wavefront per row; four lanes (8
-// elements each) make a block.
+// that hold no pair are skipped.  `parts` wavefronts per row (as in the
+// block-FP8 gather); four lanes (8 elements each) make a block.
 __global__ __launch_bounds__(256) void gather_rows_mx8_kernel(
     const uint4* __restrict__ src, const int32_t* __restrict__ rows,
-    const int32_t* __restrict__ n_rows, int n_rows_host, int H,
+    const int32_t* __restrict__ n_rows, int n_rows_host, int H, int parts,
     const int32_t* __restrict__ counts, int cap,
     uint2* __restrict__ dst, uint8_t* __restrict__ dst_scale) {
   const int n = n_rows ? *n_rows : n_rows_host;
   const int chunks = H >> 3;
   const int wpb = blockDim.x >> 6;
   const int lane = lane_id();
-  for (int j = blockIdx.x * wpb + (threadIdx.x >> 6); j < n; j += gridDim.x * wpb) {
+  const int gw = blockIdx.x * wpb + (threadIdx.x >> 6);
+  const int part = gw % parts, slot = gw / parts, slots = gridDim.x * wpb / parts;
+  if (slot >= slots) return;  // uniform over the wave
+  for (int j = slot; j < n; j += slots) {
     if (!masked_row_used(counts, cap, j)) continue;  // uniform over the wave
     const int r = rows ? rows[j] : j;
     const uint4* s = src + static_cast<size_t>(r) * chunks;
     uint2* d = dst + static_cast<size_t>(j) * chunks;
     // chunks is a multiple of 16, so the four lanes of a block are all active
-    for (int c = lane; c < chunks; c += kWave) {
+    for (int c = part * kWave + lane; c < chunks; c += kWave * parts) {
       const uint4 v = s[c];
       float f[8];
       const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
@@ -551,6 +560,21 @@ static int gather_grid(int64_t max_rows) {
   return static_cast<int>(blocks < 8192 ? (blocks > 0 ? blocks : 1) : 8192);
 }
 
+// Waves per row of the quantising gathers: enough for ~2048 waves in all, at
+// most one per 64-lane pass of a row (H / 512 passes).
+static int gather_parts(int64_t max_rows, int H) {
+  const int64_t passes = (H / 8 + kWave - 1) / kWave;
+  const int64_t want = (2048 + max_rows - 1) / (max_rows > 0 ? max_rows : 1);
+  const int64_t p = want < passes ? want : passes;
+  return static_cast<int>(p > 1 ? p : 1);
+}
+
+// Blocks of 4 waves for max_rows rows of `parts` waves each.
+static int gather_grid_parts(int64_t max_rows, int parts) {
+  const int64_t blocks = (max_rows * parts + 3) / 4;
+  return static_cast<int>(blocks < 8192 ? (blocks > 0 ? blocks : 1) : 8192);
+}
+
 hipError_t launch_gather_bf16(const void* src, const int32_t* rows, const int32_t* n_rows,
                               int64_t max_rows, int H, void* dst, int64_t panel_rows,
                               hipStream_t s, const int32_t* counts, int cap) {
@@ -591,9 +615,11 @@ hipError_t launch_pack_scales_mx(const void* src, int64_t batch, int64_t rows, i
 hipError_t launch_gather_fp8(const void* src, const int32_t* rows, const int32_t* n_rows,
                              int64_t max_rows, int H, void* dst, float* dst_scale,
                              hipStream_t s, const int32_t* counts, int cap) {
-  hipLaunchKernelGGL(gather_rows_fp8_kernel, dim3(gather_grid(max_rows)), dim3(256), 0, s,
-                     static_cast<const uint4*>(src), rows, n_rows, static_cast<int>(max_rows), H,
-                     counts, cap, static_cast<uint2*>(dst), dst_scale);
+  const int parts = gather_parts(max_rows, H);
+  hipLaunchKernelGGL(gather_rows_fp8_kernel, dim3(gather_grid_parts(max_rows, parts)), dim3(256),
+                     0, s, static_cast<const uint4*>(src), rows, n_rows,
+                     static_cast<int>(max_rows), H, parts, counts, cap,
+                     static_cast<uint2*>(dst), dst_scale);
   return hipGetLastError();
 }
 
@@ -620,9 +646,11 @@ hipError_t launch_quant_mx4(const void* src, int64_t rows, int64_t cols, void* c
 hipError_t launch_gather_mx8(const void* src, const int32_t* rows, const int32_t* n_rows,
                              int64_t max_rows, int H, void* dst, uint8_t* dst_scale,
                              hipStream_t s, const int32_t* counts, int cap) {
-  hipLaunchKernelGGL(gather_rows_mx8_kernel, dim3(gather_grid(max_rows)), dim3(256), 0, s,
-                     static_cast<const uint4*>(src), rows, n_rows, static_cast<int>(max_rows), H,
-                     counts, cap, static_cast<uint2*>(dst), dst_scale);
+  const int parts = gather_parts(max_rows, H);
+  hipLaunchKernelGGL(gather_rows_mx8_kernel, dim3(gather_grid_parts(max_rows, parts)), dim3(256),
+                     0, s, static_cast<const uint4*>(src), rows, n_rows,
+                     static_cast<int>(max_rows), H, parts, counts, cap,
+                     static_cast<uint2*>(dst), dst_scale);
   return hipGetLastError();
 }
 

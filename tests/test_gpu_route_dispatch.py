@@ -45,10 +45,12 @@ def test_route_workloads(cid):
 
 @pytest.mark.parametrize("E,k", [(1, 1), (8, 2), (8, 8), (65, 3), (128, 8), (200, 12),
                                  (256, 32), (1024, 8), (1000, 1),
-                                 # 16-lane rows: vector loads (E % 4 == 0) or not, up
-                                 # to 32 keys per lane, slots past 16, the last size
-                                 # before one token per wave
-                                 (12, 5), (300, 17), (511, 32), (512, 20), (513, 4)])
+                                 # rows of 8 lanes (E <= 256) and of 16: vector loads
+                                 # (E % 4 == 0) or not, up to 32 keys per lane, one to
+                                 # four slots per lane, the first and last sizes of each
+                                 # row width, the last size before one token per wave
+                                 (12, 5), (201, 12), (250, 30), (256, 9), (257, 9),
+                                 (300, 17), (400, 8), (511, 32), (512, 20), (513, 4)])
 def test_route_shapes(E, k):
     torch = torch_cuda()
     ml = _ml()
@@ -62,8 +64,8 @@ def test_route_shapes(E, k):
 @pytest.mark.parametrize("T,E,k", [(16401, 256, 8), (16384, 65, 3), (20000, 512, 20),
                                    (16413, 12, 5)])
 def test_route_large_ragged(T, E, k):
-    """Prefill-sized token counts, ragged against the 16 tokens of a block (the
-    last rows run on the last token and store nothing)."""
+    """Prefill-sized token counts, ragged against the 32 or 16 tokens of a block
+    (the last rows run on the last token and store nothing)."""
     torch = torch_cuda()
     ml = _ml()
     rng = np.random.default_rng(T + E * 7 + k)

@@ -72,4 +72,30 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* total_out) {
 template <typename T>
 __host__ __device__ __forceinline__ T ceil_div(T a, T b) { return (a + b - 1) / b; }
 
+// m-tile table of the GEMM paths that run one block per tile (skinny,
+// pipelined, MX), built by one block whose thread e < E_L owns local expert e
+// with cnt rows; every thread of the block calls it.  Entries [start, start +
+// tiles) of expert e hold {e, start, tiles, 0} and *n_tiles the total.  sync
+// (fused decode FFN; may be null): sync[0], the ticket counter, and sync[1 +
+// i], the up tiles finished for m-tile i, start at 0.  status (may be null):
+// the FFN's flag word, cleared for the launch that follows.
+__device__ __forceinline__ void build_tile_table(int e, int E_L, int cnt, int tile_m,
+                                                 int4* __restrict__ info, int32_t* __restrict__ n_tiles,
+                                                 int32_t* __restrict__ sync,
+                                                 int32_t* __restrict__ status) {
+  const int tiles = e < E_L ? ceil_div(cnt, tile_m) : 0;
+  int total;
+  const int start = block_exclusive_scan(tiles, &total);
+  if (e < E_L)
+    for (int i = 0; i < tiles; ++i) {
+      info[start + i] = make_int4(e, start, tiles, 0);
+      if (sync) sync[1 + start + i] = 0;
+    }
+  if (threadIdx.x == 0) {
+    *n_tiles = total;
+    if (sync) sync[0] = 0;
+    if (status) *status = 0;
+  }
+}
+
 }  // namespace moe

@@ -144,13 +144,16 @@ __device__ __forceinline__ int mask_rank(const uint32_t* m, int tb) {
 
 // Count, scan and scatter of at most 256 tokens in one block of 1024 threads
 // (thread e < E_L owns expert e in the scan; thread t < T owns token t).
+// With tile_m > 0 the block also writes the m-tile table of the GEMMs that
+// read these segments (build_tile_table).  mask: E_L * (kMaskWords + 1)
+// words of LDS.
 template <int KMAX>
-__global__ __launch_bounds__(1024) void index_small_kernel(
+__device__ __forceinline__ void index_small_block(
     const int32_t* __restrict__ topk_ids, int T, int k, int e_lo, int E_L, int cap,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ row_token, int32_t* __restrict__ row_slot,
-    int32_t* __restrict__ token_slot_row) {
-  extern __shared__ uint32_t mask[];
+    int32_t* __restrict__ token_slot_row, uint32_t* mask, int tile_m, int4* __restrict__ info,
+    int32_t* __restrict__ n_tiles, int32_t* __restrict__ sync, int32_t* __restrict__ status) {
   int* s_off = reinterpret_cast<int*>(mask + E_L * kMaskWords);
   int le[KMAX];
   if (static_cast<int>(threadIdx.x) < T) token_local_experts<KMAX>(topk_ids, threadIdx.x, k, e_lo, E_L, le);
@@ -169,6 +172,7 @@ __global__ __launch_bounds__(1024) void index_small_kernel(
     s_off[e] = o;
   }
   if (e == 0) offsets[E_L] = cap ? E_L * cap : total;
+  if (tile_m > 0) build_tile_table(e, E_L, c, tile_m, info, n_tiles, sync, status);
   __syncthreads();
   const int t = threadIdx.x;
   if (t >= T) return;
@@ -184,6 +188,17 @@ __global__ __launch_bounds__(1024) void index_small_kernel(
       token_slot_row[static_cast<size_t>(t) * k + s] = pos;
     }
   }
+}
+
+template <int KMAX>
+__global__ __launch_bounds__(1024) void index_small_kernel(
+    const int32_t* __restrict__ topk_ids, int T, int k, int e_lo, int E_L, int cap,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ row_token, int32_t* __restrict__ row_slot,
+    int32_t* __restrict__ token_slot_row) {
+  extern __shared__ uint32_t mask[];
+  index_small_block<KMAX>(topk_ids, T, k, e_lo, E_L, cap, counts, offsets, row_token, row_slot,
+                          token_slot_row, mask, 0, nullptr, nullptr, nullptr, nullptr);
 }
 
 template <int KMAX>
@@ -318,18 +333,17 @@ __global__ __launch_bounds__(256) void pack_scales_mx_kernel(const uint32_t* __r
 // `parts` waves share a row, each taking every parts-th 64-lane pass of it (a
 // few rows -- a decode batch -- would otherwise run their passes one after
 // another in one wave each).
-__global__ __launch_bounds__(256) void gather_rows_fp8_kernel(
-    const uint4* __restrict__ src, const int32_t* __restrict__ rows,
+// Wave gw of nwaves.
+__device__ __forceinline__ void quant_rows_fp8(
+    int gw, int nwaves, const uint4* __restrict__ src, const int32_t* __restrict__ rows,
     const int32_t* __restrict__ n_rows, int n_rows_host, int H, int parts,
     const int32_t* __restrict__ counts, int cap,
     uint2* __restrict__ dst, float* __restrict__ dst_scale) {
   const int n = n_rows ? *n_rows : n_rows_host;
   const int chunks = H >> 3;  // 8 bf16 per chunk
   const int groups = H >> 7;
-  const int wpb = blockDim.x >> 6;
   const int lane = lane_id();
-  const int gw = blockIdx.x * wpb + (threadIdx.x >> 6);
-  const int part = gw % parts, slot = gw / parts, slots = gridDim.x * wpb / parts;
+  const int part = gw % parts, slot = gw / parts, slots = nwaves / parts;
   if (slot >= slots) return;  // uniform over the wave
   for (int j = slot; j < n; j += slots) {
     if (!masked_row_used(counts, cap, j)) continue;  // uniform over the wave
@@ -478,17 +492,16 @@ __global__ __launch_bounds__(256) void quant_mx4_kernel(const uint4* __restrict_
 // E8M0 scale per 32 elements (rows == nullptr: identity); masked-layout rows
 // that hold no pair are skipped.  `parts` wavefronts per row (as in the
 // block-FP8 gather); four lanes (8 elements each) make a block.
-__global__ __launch_bounds__(256) void gather_rows_mx8_kernel(
-    const uint4* __restrict__ src, const int32_t* __restrict__ rows,
+// Wave gw of nwaves.
+__device__ __forceinline__ void quant_rows_mx8(
+    int gw, int nwaves, const uint4* __restrict__ src, const int32_t* __restrict__ rows,
     const int32_t* __restrict__ n_rows, int n_rows_host, int H, int parts,
     const int32_t* __restrict__ counts, int cap,
     uint2* __restrict__ dst, uint8_t* __restrict__ dst_scale) {
   const int n = n_rows ? *n_rows : n_rows_host;
   const int chunks = H >> 3;
-  const int wpb = blockDim.x >> 6;
   const int lane = lane_id();
-  const int gw = blockIdx.x * wpb + (threadIdx.x >> 6);
-  const int part = gw % parts, slot = gw / parts, slots = gridDim.x * wpb / parts;
+  const int part = gw % parts, slot = gw / parts, slots = nwaves / parts;
   if (slot >= slots) return;  // uniform over the wave
   for (int j = slot; j < n; j += slots) {
     if (!masked_row_used(counts, cap, j)) continue;  // uniform over the wave
@@ -518,6 +531,57 @@ __global__ __launch_bounds__(256) void gather_rows_mx8_kernel(
       d[c] = q;
       if ((lane & 3) == 0) dst_scale[static_cast<size_t>(j) * (H >> 5) + (c >> 2)] = code;
     }
+  }
+}
+
+__global__ __launch_bounds__(256) void gather_rows_fp8_kernel(
+    const uint4* __restrict__ src, const int32_t* __restrict__ rows,
+    const int32_t* __restrict__ n_rows, int n_rows_host, int H, int parts,
+    const int32_t* __restrict__ counts, int cap,
+    uint2* __restrict__ dst, float* __restrict__ dst_scale) {
+  const int wpb = blockDim.x >> 6;
+  quant_rows_fp8(blockIdx.x * wpb + (threadIdx.x >> 6), gridDim.x * wpb, src, rows, n_rows,
+                 n_rows_host, H, parts, counts, cap, dst, dst_scale);
+}
+
+__global__ __launch_bounds__(256) void gather_rows_mx8_kernel(
+    const uint4* __restrict__ src, const int32_t* __restrict__ rows,
+    const int32_t* __restrict__ n_rows, int n_rows_host, int H, int parts,
+    const int32_t* __restrict__ counts, int cap,
+    uint2* __restrict__ dst, uint8_t* __restrict__ dst_scale) {
+  const int wpb = blockDim.x >> 6;
+  quant_rows_mx8(blockIdx.x * wpb + (threadIdx.x >> 6), gridDim.x * wpb, src, rows, n_rows,
+                 n_rows_host, H, parts, counts, cap, dst, dst_scale);
+}
+
+// The layer's front for at most 256 tokens in one launch: block 0 builds the
+// index and the m-tile table (index_small_block); the other blocks quantise
+// the T token rows of x (QK 1: block-FP8, 2: MXFP8; QK 0: none, one block),
+// `parts` waves per row.  The two parts share no data.
+template <int KMAX, int QK>
+__global__ __launch_bounds__(1024) void index_front_kernel(
+    const int32_t* __restrict__ topk_ids, int T, int k, int e_lo, int E_L, int cap,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ row_token, int32_t* __restrict__ row_slot,
+    int32_t* __restrict__ token_slot_row, int tile_m, int4* __restrict__ info,
+    int32_t* __restrict__ n_tiles, int32_t* __restrict__ sync, int32_t* __restrict__ status,
+    const uint4* __restrict__ x, int H, int parts, uint2* __restrict__ xq, void* xq_scale) {
+  extern __shared__ uint32_t mask[];
+  if (blockIdx.x == 0) {
+    index_small_block<KMAX>(topk_ids, T, k, e_lo, E_L, cap, counts, offsets, row_token, row_slot,
+                            token_slot_row, mask, tile_m, info, n_tiles, sync, status);
+    return;
+  }
+  if constexpr (QK != 0) {
+    const int wpb = blockDim.x >> 6;
+    const int gw = (blockIdx.x - 1) * wpb + (threadIdx.x >> 6);
+    const int nw = (gridDim.x - 1) * wpb;
+    if constexpr (QK == 1)
+      quant_rows_fp8(gw, nw, x, nullptr, nullptr, T, H, parts, nullptr, 0, xq,
+                     static_cast<float*>(xq_scale));
+    else
+      quant_rows_mx8(gw, nw, x, nullptr, nullptr, T, H, parts, nullptr, 0, xq,
+                     static_cast<uint8_t*>(xq_scale));
   }
 }
 
@@ -573,6 +637,44 @@ static int gather_parts(int64_t max_rows, int H) {
 static int gather_grid_parts(int64_t max_rows, int parts) {
   const int64_t blocks = (max_rows * parts + 3) / 4;
   return static_cast<int>(blocks < 8192 ? (blocks > 0 ? blocks : 1) : 8192);
+}
+
+template <int KMAX>
+static void launch_front_k(int qkind, dim3 grid, size_t lds, hipStream_t s,
+                           const int32_t* topk_ids, int T, int k, int e_lo, int E_L, int cap,
+                           int32_t* counts, int32_t* offsets, int32_t* row_token,
+                           int32_t* row_slot, int32_t* token_slot_row, int tile_m, int4* info,
+                           int32_t* n_tiles, int32_t* sync, int32_t* status, const uint4* x,
+                           int H, int parts, uint2* xq, void* xq_scale) {
+  auto kern = qkind == 1 ? index_front_kernel<KMAX, 1>
+            : qkind == 2 ? index_front_kernel<KMAX, 2> : index_front_kernel<KMAX, 0>;
+  hipLaunchKernelGGL(kern, grid, dim3(1024), lds, s, topk_ids, T, k, e_lo, E_L, cap, counts,
+                     offsets, row_token, row_slot, token_slot_row, tile_m, info, n_tiles, sync,
+                     status, x, H, parts, xq, xq_scale);
+}
+
+hipError_t launch_index_front(const int32_t* topk_ids, int T, int k, int e_lo, int E_L, int cap,
+                              int32_t* counts, int32_t* offsets, int32_t* row_token,
+                              int32_t* row_slot, int32_t* token_slot_row, int tile_m, int4* info,
+                              int32_t* n_tiles, int32_t* sync, int32_t* status, int qkind,
+                              const void* x, int H, void* xq, void* xq_scale, hipStream_t s) {
+  if (T < 1 || T > kTokBlock || E_L < 1 || E_L > 1024 || tile_m < 1 || qkind < 0 || qkind > 2)
+    return hipErrorInvalidValue;
+  const size_t lds = static_cast<size_t>(E_L) * (kMaskWords + 1) * sizeof(uint32_t);
+  const int parts = qkind ? gather_parts(T, H) : 1;
+  const int qblocks = qkind ? ceil_div(T * parts, 16) : 0;
+  const dim3 grid(static_cast<unsigned>(1 + qblocks));
+  const uint4* xs = static_cast<const uint4*>(x);
+  uint2* xd = static_cast<uint2*>(xq);
+  if (k <= 8)
+    launch_front_k<8>(qkind, grid, lds, s, topk_ids, T, k, e_lo, E_L, cap, counts, offsets,
+                      row_token, row_slot, token_slot_row, tile_m, info, n_tiles, sync, status,
+                      xs, H, parts, xd, xq_scale);
+  else
+    launch_front_k<32>(qkind, grid, lds, s, topk_ids, T, k, e_lo, E_L, cap, counts, offsets,
+                       row_token, row_slot, token_slot_row, tile_m, info, n_tiles, sync, status,
+                       xs, H, parts, xd, xq_scale);
+  return hipGetLastError();
 }
 
 hipError_t launch_gather_bf16(const void* src, const int32_t* rows, const int32_t* n_rows,

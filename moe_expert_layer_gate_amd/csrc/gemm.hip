@@ -123,10 +123,8 @@ __device__ __forceinline__ int2 segment(const int32_t* seg, int cap, int e) {
   return make_int2(seg[e], seg[e + 1]);
 }
 
-// sync (fused FFN only): sync[0] is the launch's ticket counter and
-// sync[1 + i] the count of up tiles finished for m-tile i; both start at 0.
-// status (may be null): the FFN's flag word, cleared for the launch that
-// follows.
+// The m-tile table of the paths without unit tables, from the segments
+// (build_tile_table).
 __global__ __launch_bounds__(1024) void tile_schedule_kernel(
     const int32_t* __restrict__ seg, int seg_cap, int E_L, int tile_m, int4* __restrict__ info,
     int32_t* __restrict__ n_tiles, int32_t* __restrict__ sync, int32_t* __restrict__ status) {
@@ -136,19 +134,7 @@ __global__ __launch_bounds__(1024) void tile_schedule_kernel(
     const int2 sg = segment(seg, seg_cap, e);
     cnt = sg.y - sg.x;
   }
-  const int tiles = ceil_div(cnt, tile_m);
-  int total;
-  const int start = block_exclusive_scan(tiles, &total);
-  if (e < E_L)
-    for (int i = 0; i < tiles; ++i) {
-      info[start + i] = make_int4(e, start, tiles, 0);
-      if (sync) sync[1 + start + i] = 0;
-    }
-  if (e == 0) {
-    *n_tiles = total;
-    if (sync) sync[0] = 0;
-    if (status) *status = 0;
-  }
+  build_tile_table(e, E_L, cnt, tile_m, info, n_tiles, sync, status);
 }
 
 __device__ __forceinline__ float silu_mul(float g, float u) {

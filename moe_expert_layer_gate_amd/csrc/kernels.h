@@ -18,6 +18,18 @@ hipError_t launch_index_build(const int32_t* topk_ids, int T, int k, int e_lo, i
                               int32_t* counts, int32_t* offsets, int32_t* row_token,
                               int32_t* row_slot, int32_t* token_slot_row, void* scratch,
                               hipStream_t s);
+constexpr int kIndexFrontMaxTokens = 256;
+// The layer's front for 1 <= T <= 256 tokens in one launch: the index build
+// of launch_index_build, the m-tile table of the GEMMs without unit tables
+// (rows per tile tile_m; sync and status as the schedule kernels take them)
+// and, qkind 1 (block-FP8) or 2 (MXFP8), the quantisation of the T rows of
+// x [T, H] into xq / xq_scale as launch_gather_fp8 / launch_gather_mx8 with
+// the identity map.  hipErrorInvalidValue outside those bounds.
+hipError_t launch_index_front(const int32_t* topk_ids, int T, int k, int e_lo, int E_L, int cap,
+                              int32_t* counts, int32_t* offsets, int32_t* row_token,
+                              int32_t* row_slot, int32_t* token_slot_row, int tile_m, int4* info,
+                              int32_t* n_tiles, int32_t* sync, int32_t* status, int qkind,
+                              const void* x, int H, void* xq, void* xq_scale, hipStream_t s);
 // dst[j] = src[rows[j]] (rows == nullptr: identity) for j < *n_rows, or for
 // j < max_rows when n_rows == nullptr.
 // With panel_rows > 0, dst is in panel layout [H/32][panel_rows][32].  With

@@ -294,17 +294,19 @@ struct FfnSource {
 
 // Enqueue the grouped FFN (no argument checks).  h follows p->layout's
 // activation bit.  seg: offsets [E_L + 1], or counts [E_L] when p->capacity
-// > 0 (masked layout).
+// > 0 (masked layout).  scheduled: the work tables, sync and status were
+// already written for these segments (the layer's one-launch front).
 moe_status run_ffn(const moe_problem* p, const FfnSource& src, const int32_t* seg,
                    const moe_weights* w, void* h, float* h_scale, void* y_perm,
-                   const FfnScratch& f, hipStream_t s) {
+                   const FfnScratch& f, hipStream_t s, bool scheduled = false) {
   const int64_t N = n_cap(p);
   const int E_L = p->num_local, H = p->hidden, I = p->inter;
   const FfnShape sh = ffn_shape(p);
   void* hb = h ? h : f.h;
   float* hs = h ? h_scale : f.h_scale;
-  MOE_TRY(launch_schedule(seg, p->capacity, E_L, sh.path, sh.nt_up, sh.nt_dn, f.tab_up, f.n_up,
-                          f.tab_dn, f.n_dn, f.sync, f.status, s));
+  if (!scheduled)
+    MOE_TRY(launch_schedule(seg, p->capacity, E_L, sh.path, sh.nt_up, sh.nt_dn, f.tab_up, f.n_up,
+                            f.tab_dn, f.n_dn, f.sync, f.status, s));
   GemmLaunch up{};
   up.fp8 = is_fp8(p);
   up.mx = is_mx(p);
@@ -630,16 +632,28 @@ moe_status enqueue_layer(const moe_problem* p, const float* logits, const void* 
   // from x quantised once (which the shared expert reads too).
   const bool fuse = can_fuse_gather(p);
   MOE_TRY(launch_route_topk(logits, T, p->num_experts, p->top_k, L.ids, L.w, s));
-  st = run_dispatch(&pi, x, L.ids, L.counts, L.offsets, L.row_token, L.row_slot, L.tsr,
-                    fuse ? nullptr : L.x_perm, L.x_perm_scale, L.index_scratch, s);
-  if (st != MOE_OK) return st;
+  // Up to 256 tokens (decode): the index build, the FFN's work table and the
+  // quantisation of x in one launch (they share no data).
+  const GemmPath path = ffn_shape(&pi).path;
+  const bool front = fuse && T <= kIndexFrontMaxTokens && !gemm_unit_tables(path);
+  if (front) {
+    const int qkind = is_fp8(p) ? 1 : is_mx(p) ? 2 : 0;
+    MOE_TRY(launch_index_front(L.ids, T, p->top_k, p->expert_begin, p->num_local, p->capacity,
+                               L.counts, L.offsets, L.row_token, L.row_slot, L.tsr,
+                               gemm_path_rows(path), L.ffn.tab_up, L.ffn.n_up, L.ffn.sync,
+                               L.ffn.status, qkind, x, p->hidden, L.xq, L.xq_scale, s));
+  } else {
+    st = run_dispatch(&pi, x, L.ids, L.counts, L.offsets, L.row_token, L.row_slot, L.tsr,
+                      fuse ? nullptr : L.x_perm, L.x_perm_scale, L.index_scratch, s);
+    if (st != MOE_OK) return st;
+    if (fuse && is_fp8(p))
+      MOE_TRY(launch_gather_fp8(x, nullptr, nullptr, T, p->hidden, L.xq, L.xq_scale, s));
+    else if (fuse && is_mx(p))
+      MOE_TRY(launch_gather_mx8(x, nullptr, nullptr, T, p->hidden, L.xq,
+                                reinterpret_cast<uint8_t*>(L.xq_scale), s));
+  }
   const void* xa = x;
   const float* xa_scale = nullptr;
-  if (fuse && is_fp8(p))
-    MOE_TRY(launch_gather_fp8(x, nullptr, nullptr, T, p->hidden, L.xq, L.xq_scale, s));
-  else if (fuse && is_mx(p))
-    MOE_TRY(launch_gather_mx8(x, nullptr, nullptr, T, p->hidden, L.xq,
-                              reinterpret_cast<uint8_t*>(L.xq_scale), s));
   if (fuse && quant_acts(p)) {
     xa = L.xq;
     xa_scale = L.xq_scale;
@@ -647,7 +661,7 @@ moe_status enqueue_layer(const moe_problem* p, const float* logits, const void* 
   const FfnSource rsrc = fuse ? FfnSource{xa, xa_scale, true, L.row_token, T}
                               : FfnSource{L.x_perm, L.x_perm_scale, false, nullptr, 0};
   st = run_ffn(&pi, rsrc, p->capacity > 0 ? L.counts : L.offsets, w, nullptr, nullptr, L.y_perm,
-               L.ffn, s);
+               L.ffn, s, front);
   if (st != MOE_OK) return st;
   if (p->shared_inter > 0) {
     const moe_problem sq = shared_problem(p);

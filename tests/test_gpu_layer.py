@@ -508,17 +508,25 @@ def test_workload_fp8_full_size_sampled():
     np.testing.assert_array_equal(dv.bits_from_bf16(y), dv.bits_from_bf16(st["y"]))
 
 
-def test_identity_like_combine_of_generated_rows():
+# (H, k, shared): rows read 2 KB a pass (H <= 2048) or 4 KB a pass, the last
+# pass partial (H = 2560: one 1 KB piece of four; 4224: 16 lanes of the first
+# piece), the unrolled slot loop (k <= 8) and the any-k one (k = 12), with and
+# without the shared-expert rows
+@pytest.mark.parametrize("H,k,shared", [(384, 4, False), (2560, 8, True), (4224, 12, True),
+                                        (7168, 8, False)])
+def test_identity_like_combine_of_generated_rows(H, k, shared):
     """Combine alone on generated expert rows: the GPU's own route/dispatch
-    indices with y_perm drawn from the generator, against the oracle's
-    combine over its own indices."""
+    indices with y_perm (and the shared rows) drawn from the generator,
+    against the oracle's combine over its own indices."""
     torch = torch_cuda()
     ml, dv = _mods()
-    cfg = small_cfg(T=333, H=384, E=16, E_L=8, e_lo=8, k=4, I=128)
+    cfg = small_cfg(T=333, H=H, E=16, E_L=8, e_lo=8, k=k, I=128)
     d = synth.make_inputs(cfg, 11, weights=False, x_std=1.0)
     p = ml.Problem.from_config(cfg)
     dev = {"logits": torch.from_numpy(d["logits"]).cuda(), "x": dv.bf16_from_bits(d["x"])}
     yp_bits = synth.make_inputs(small_cfg(T=p.n_cap, H=cfg.H), 12, weights=False, x_std=1.0)["x"]
+    sh_bits = (synth.make_inputs(small_cfg(T=p.T, H=cfg.H), 13, weights=False, x_std=1.0)["x"]
+               if shared else None)
     ids = torch.empty((p.T, p.k), dtype=torch.int32, device="cuda")
     w = torch.empty((p.T, p.k), dtype=torch.float32, device="cuda")
     ml.moe_route(p, dev["logits"], ids, w)
@@ -530,14 +538,16 @@ def test_identity_like_combine_of_generated_rows():
     ml.moe_dispatch(p, dev["x"], ids, counts, offsets, rt, rs, tsr, xp, None,
                     dv.workspace(p, ml.STAGE_DISPATCH))
     y = torch.empty((p.T, p.H), dtype=torch.bfloat16, device="cuda")
-    say("combine generated rows")
-    ml.moe_combine(p, dv.bf16_from_bits(yp_bits), tsr, w, None, y)
+    say("combine generated rows", H, k, shared)
+    ml.moe_combine(p, dv.bf16_from_bits(yp_bits), tsr, w,
+                   dv.bf16_from_bits(sh_bits) if shared else None, y)
     torch.cuda.synchronize()
     rid, rw = O.route(d["logits"], cfg.k)
     ix = O.index_build(rid, cfg.e_lo, cfg.E_L)
-    ref = O.combine(O.bf16_to_f64(yp_bits), ix["token_slot_row"], rw)
+    ref = O.combine(O.bf16_to_f64(yp_bits), ix["token_slot_row"], rw,
+                    O.bf16_to_f64(sh_bits) if shared else None)
     e = rel_rows(f64(y), ref)
-    print(f"combine: {e:.2e}")
+    print(f"combine H={H} k={k} shared={shared}: {e:.2e}")
     # fp32 accumulation and one bf16 rounding: within a few bf16 ulps
     assert e <= 8e-3
 

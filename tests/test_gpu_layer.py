@@ -135,6 +135,11 @@ SMALL = {
     "gelu_pipelined": (small_cfg(T=300, H=256, E=8, E_L=8, k=2, I=640, I_s=256, act="gelu"), 19),
     "gelu_skinny": (small_cfg(T=60, H=384, E=16, E_L=8, e_lo=0, k=4, I=384, act="gelu",
                               logits="gumbel_zipf"), 20),
+    # k above 8 (the kernels' any-k forms: index build, the one-launch layer
+    # front, combine): pipelined and skinny FFN tiles
+    "k12_pipelined": (small_cfg(T=48, H=256, E=32, E_L=16, e_lo=8, k=12, I=256,
+                                logits="gumbel_zipf"), 21),
+    "k10_skinny": (small_cfg(T=20, H=384, E=64, E_L=16, e_lo=16, k=10, I=384), 22),
 }
 SMALL_FP8 = {
     "fp8_small": (small_cfg(T=200, H=512, E=16, E_L=8, e_lo=0, k=4, I=256, fp8=True), 8),
@@ -148,6 +153,8 @@ SMALL_FP8 = {
     # Zipf routing gives the hot experts two or more 32-row tiles
     "fp8_skinny": (small_cfg(T=64, H=512, E=32, E_L=8, e_lo=8, k=8, I=384, fp8=True,
                              logits="gumbel_zipf"), 15),
+    "fp8_k12_skinny": (small_cfg(T=40, H=512, E=32, E_L=16, e_lo=0, k=12, I=256, fp8=True,
+                                 logits="gumbel_zipf"), 23),
 }
 
 

@@ -87,6 +87,8 @@ SMALL_MX = {
     "mx_shared": (small_cfg(T=150, H=1024, E=64, E_L=16, e_lo=16, k=8, I=512, I_s=256,
                             mx=True), 43),
     "mx_decode": (small_cfg(T=16, H=1024, E=64, E_L=16, e_lo=0, k=8, I=256, mx=True), 44),
+    # k above 8: the any-k index build and the one-launch layer front
+    "mx_k12_decode": (small_cfg(T=24, H=512, E=64, E_L=16, e_lo=8, k=12, I=256, mx=True), 47),
     # up to 32 rows per expert on average: the fused skinny MX kernel, some
     # experts over 32 rows (two m-tiles), the shared expert on 128-row tiles
     "mx_skinny_tiles": (small_cfg(T=100, H=512, E=16, E_L=8, e_lo=4, k=4, I=384, I_s=128,

@@ -72,25 +72,43 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* total_out) {
 template <typename T>
 __host__ __device__ __forceinline__ T ceil_div(T a, T b) { return (a + b - 1) / b; }
 
+// Owner of entry u of a table whose experts hold consecutive runs starting at
+// s_start[0..E_L) (non-decreasing; u below the total): the last expert whose
+// run starts at or before u, which is never an empty one.
+__device__ __forceinline__ int run_owner(const int* s_start, int E_L, int u) {
+  int lo = 0, hi = E_L - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (s_start[mid] <= u) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
 // m-tile table of the GEMM paths that run one block per tile (skinny,
 // pipelined, MX), built by one block whose thread e < E_L owns local expert e
 // with cnt rows; every thread of the block calls it.  Entries [start, start +
-// tiles) of expert e hold {e, start, tiles, 0} and *n_tiles the total.  sync
-// (fused decode FFN; may be null): sync[0], the ticket counter, and sync[1 +
-// i], the up tiles finished for m-tile i, start at 0.  status (may be null):
-// the FFN's flag word, cleared for the launch that follows.
+// tiles) of expert e hold {e, start, tiles, 0} and *n_tiles the total; the
+// block's threads write the entries together.  sync (fused decode FFN; may be
+// null): sync[0], the ticket counter, and sync[1 + i], the up tiles finished
+// for m-tile i, start at 0.  status (may be null): the FFN's flag word,
+// cleared for the launch that follows.
 __device__ __forceinline__ void build_tile_table(int e, int E_L, int cnt, int tile_m,
                                                  int4* __restrict__ info, int32_t* __restrict__ n_tiles,
                                                  int32_t* __restrict__ sync,
                                                  int32_t* __restrict__ status) {
+  __shared__ int s_start[1024];
   const int tiles = e < E_L ? ceil_div(cnt, tile_m) : 0;
   int total;
   const int start = block_exclusive_scan(tiles, &total);
-  if (e < E_L)
-    for (int i = 0; i < tiles; ++i) {
-      info[start + i] = make_int4(e, start, tiles, 0);
-      if (sync) sync[1 + start + i] = 0;
-    }
+  if (e < E_L) s_start[e] = start;
+  __syncthreads();
+  for (int u = threadIdx.x; u < total; u += blockDim.x) {
+    const int o = run_owner(s_start, E_L, u);
+    const int first = s_start[o];
+    const int n = (o + 1 < E_L ? s_start[o + 1] : total) - first;
+    info[u] = make_int4(o, first, n, 0);
+    if (sync) sync[1 + u] = 0;
+  }
   if (threadIdx.x == 0) {
     *n_tiles = total;
     if (sync) sync[0] = 0;

@@ -1637,18 +1637,15 @@ __device__ __forceinline__ void expert_units(int cnt, int bm, bool allow_wide, i
 
 constexpr int kGroupM = 8;
 
-// Writes one table; every thread takes units u = tid, tid + 1024, ... and
-// finds the unit's expert by binary search over the experts' first units.
+// Writes one table; the grid's threads take units u = gtid, gtid + threads,
+// ... and find the unit's expert by binary search over the experts' first
+// units.
 __device__ __forceinline__ void write_units(const int* s_start, const int* s_off,
                                             const int* s_full, int E_L, int nt, int total, int bm,
                                             int4* __restrict__ units) {
-  for (int u = threadIdx.x; u < total; u += blockDim.x) {
-    int lo = 0, hi = E_L - 1;  // last expert whose first unit is <= u
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_start[mid] <= u) lo = mid; else hi = mid - 1;
-    }
-    const int e = lo, v = u - s_start[e], full = s_full[e];
+  const int step = gridDim.x * blockDim.x;
+  for (int u = blockIdx.x * blockDim.x + threadIdx.x; u < total; u += step) {
+    const int e = run_owner(s_start, E_L, u), v = u - s_start[e], full = s_full[e];
     if (v < full * nt) {
       // groups of kGroupM m-tiles, n-tile-major inside a group, so the 32
       // CUs of an XCD work on about 8 m-tiles x 4 n-tiles of an expert at
@@ -1688,6 +1685,7 @@ __global__ __launch_bounds__(1024) void unit_schedule_kernel(
   __syncthreads();
   write_units(s_sa, s_off, s_full, E_L, nt_a, tot_a, bm, units_a);
   write_units(s_sb, s_off, s_full, E_L, nt_b, tot_b, bm, units_b);
+  if (blockIdx.x != 0) return;
   if (e == 0) {
     *n_a = tot_a;
     *n_b = tot_b;
@@ -2630,11 +2628,17 @@ int64_t schedule_entries(int64_t n_pairs, int E_L, GemmPath path, int nt) {
 
 hipError_t launch_schedule(const int32_t* seg, int seg_cap, int E_L, GemmPath path, int nt_up,
                            int nt_dn, int4* tab_up, int32_t* n_up, int4* tab_dn, int32_t* n_dn,
-                           int32_t* sync, int32_t* status, hipStream_t s) {
+                           int32_t* sync, int32_t* status, int64_t max_units, hipStream_t s) {
   const int bm = gemm_path_rows(path);
-  if (gemm_unit_tables(path))  // only the bf16 paths have wide tiles
-    hipLaunchKernelGGL(unit_schedule_kernel, dim3(1), dim3(1024), 0, s, seg, seg_cap, E_L, nt_up,
-                       nt_dn, bm, gemm_large_bf16(path), tab_up, n_up, tab_dn, n_dn, status, sync);
+  if (gemm_unit_tables(path)) {  // only the bf16 paths have wide tiles
+    // every block redoes the per-expert scan and writes its share of the
+    // units (one block wrote some ten thousand entries in 13 us)
+    const int64_t want = (max_units + 1023) / 1024;
+    const int blocks = static_cast<int>(want < 1 ? 1 : (want > 32 ? 32 : want));
+    hipLaunchKernelGGL(unit_schedule_kernel, dim3(blocks), dim3(1024), 0, s, seg, seg_cap, E_L,
+                       nt_up, nt_dn, bm, gemm_large_bf16(path), tab_up, n_up, tab_dn, n_dn,
+                       status, sync);
+  }
   else
     hipLaunchKernelGGL(tile_schedule_kernel, dim3(1), dim3(1024), 0, s, seg, seg_cap, E_L, bm,
                        tab_up, n_up, sync, status);

@@ -94,10 +94,10 @@ int64_t schedule_entries(int64_t n_pairs, int E_L, GemmPath path, int nt);
 // counters, [1 + schedule_entries]; large-tile paths: the persistent GEMMs'
 // per-XCD unit counters, [kTicketWords] (null: none); cleared here for the
 // launches that follow.  status (may be null): the FFN's flag word (kFlag*),
-// cleared here.
+// cleared here.  max_units: the larger table's capacity (schedule_entries).
 hipError_t launch_schedule(const int32_t* seg, int seg_cap, int E_L, GemmPath path, int nt_up,
                            int nt_dn, int4* tab_up, int32_t* n_up, int4* tab_dn, int32_t* n_dn,
-                           int32_t* sync, int32_t* status, hipStream_t s);
+                           int32_t* sync, int32_t* status, int64_t max_units, hipStream_t s);
 // Flag bits of an FFN's status word (the values of MOE_FLAG_* in the ABI).
 constexpr int32_t kFlagWaitTimeout = 1;
 // Unit counters of the large-tile paths: 8 per GEMM (one per XCD), up then down.

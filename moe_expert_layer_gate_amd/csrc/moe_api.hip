@@ -306,7 +306,8 @@ moe_status run_ffn(const moe_problem* p, const FfnSource& src, const int32_t* se
   float* hs = h ? h_scale : f.h_scale;
   if (!scheduled)
     MOE_TRY(launch_schedule(seg, p->capacity, E_L, sh.path, sh.nt_up, sh.nt_dn, f.tab_up, f.n_up,
-                            f.tab_dn, f.n_dn, f.sync, f.status, s));
+                            f.tab_dn, f.n_dn, f.sync, f.status,
+                            sh.cap_up > sh.cap_dn ? sh.cap_up : sh.cap_dn, s));
   GemmLaunch up{};
   up.fp8 = is_fp8(p);
   up.mx = is_mx(p);

@@ -8,8 +8,10 @@
 // each row to its token and routing slot.  Page "OverlapAdvisor ...", section
 // 4.2.1: permute groups tokens by expert.
 //
-// The permutation is a stable counting sort done in three launches, with no
-// float and no order-dependent atomics (the result is deterministic):
+// The permutation is a stable counting sort done in three launches (two when
+// the histogram below has at most 64 Ki entries: the scatter blocks then do
+// the scan themselves), with no float and no order-dependent atomics (the
+// result is deterministic):
 //   1. count:   each block of 256 tokens builds, in LDS, one 256-bit mask per
 //               local expert (bit i = token i of the block picked it) and
 //               writes the popcounts as its per-expert histogram;
@@ -221,6 +223,80 @@ __global__ __launch_bounds__(kTokBlock) void index_scatter_kernel(
       if (e >= 0) {
         pos = offsets[e] + blk_base[static_cast<size_t>(blockIdx.x) * E_L + e] +
               mask_rank(mask + e * kMaskWords, threadIdx.x);
+        row_token[pos] = t;
+        row_slot[pos] = s;
+      }
+      token_slot_row[static_cast<size_t>(t) * k + s] = pos;
+    }
+  }
+}
+
+// The scan folded into the scatter, for histograms of at most kFoldHist
+// entries: every block reads the whole [nblk x E_L] histogram and derives what
+// it needs -- the experts' offsets and, per expert, the count of its pairs in
+// earlier blocks -- then scatters its tokens like index_scatter_kernel (block
+// b's tokens are threads 0..255); block 0 also writes counts and offsets.
+// Thread (part, e) of the 1024 sums expert e over the part's run of blocks,
+// as index_scan_kernel does.  mask: E_L * (kMaskWords + 1) words of LDS.
+constexpr int kFoldHist = 1 << 16;
+
+template <int KMAX>
+__global__ __launch_bounds__(1024) void index_scan_scatter_kernel(
+    const int32_t* __restrict__ topk_ids, int T, int k, int e_lo, int E_L, int cap,
+    const int32_t* __restrict__ blk_hist, int nblk, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ row_token,
+    int32_t* __restrict__ row_slot, int32_t* __restrict__ token_slot_row) {
+  extern __shared__ uint32_t mask[];
+  int* s_base = reinterpret_cast<int*>(mask + E_L * kMaskWords);
+  __shared__ int part_all[1024], part_before[1024];
+  const int b = blockIdx.x;
+  const int parts = 1024 / E_L;
+  const int e = threadIdx.x % E_L, part = threadIdx.x / E_L;
+  const int chunk = ceil_div(nblk, parts);
+  const int b0 = part * chunk, b1 = min(nblk, b0 + chunk);
+  int all = 0, before = 0;
+  if (part < parts)
+    for (int bb = b0; bb < b1; ++bb) {
+      const int v = blk_hist[static_cast<size_t>(bb) * E_L + e];
+      all += v;
+      before += bb < b ? v : 0;
+    }
+  part_all[threadIdx.x] = part < parts ? all : 0;
+  part_before[threadIdx.x] = part < parts ? before : 0;
+  __syncthreads();
+  const bool first_part = static_cast<int>(threadIdx.x) < E_L;  // thread e owns expert e
+  int total_e = 0, before_e = 0;
+  if (first_part)
+    for (int q = 0; q < parts; ++q) {
+      total_e += part_all[q * E_L + e];
+      before_e += part_before[q * E_L + e];
+    }
+  int total;
+  const int off = block_exclusive_scan(first_part ? total_e : 0, &total);
+  if (first_part) {
+    const int o = cap ? e * cap : off;
+    s_base[e] = o + before_e;
+    if (b == 0) {
+      counts[e] = total_e;
+      offsets[e] = o;
+    }
+  }
+  if (b == 0 && threadIdx.x == 0) offsets[E_L] = cap ? E_L * cap : total;
+  // this block's tokens
+  const int tb = static_cast<int>(threadIdx.x);
+  const int t = b * kTokBlock + tb;
+  const bool has_token = tb < kTokBlock && t < T;
+  int le[KMAX];
+  if (has_token) token_local_experts<KMAX>(topk_ids, t, k, e_lo, E_L, le);
+  build_masks<KMAX>(mask, le, has_token, E_L);
+  if (!has_token) return;
+#pragma unroll
+  for (int s = 0; s < KMAX; ++s) {
+    if (s < k) {
+      const int x = le[s];
+      int pos = -1;
+      if (x >= 0) {
+        pos = s_base[x] + mask_rank(mask + x * kMaskWords, tb);
         row_token[pos] = t;
         row_slot[pos] = s;
       }
@@ -610,6 +686,13 @@ hipError_t launch_index_build(const int32_t* topk_ids, int T, int k, int e_lo, i
   hipLaunchKernelGGL(k <= 8 ? index_count_kernel<8> : index_count_kernel<32>, dim3(nblk),
                      dim3(kTokBlock), lds, s,
                      topk_ids, T, k, e_lo, E_L, blk_hist);
+  if (static_cast<int64_t>(nblk) * E_L <= kFoldHist) {  // two launches
+    const size_t lds2 = static_cast<size_t>(E_L) * (kMaskWords + 1) * sizeof(uint32_t);
+    hipLaunchKernelGGL(k <= 8 ? index_scan_scatter_kernel<8> : index_scan_scatter_kernel<32>,
+                       dim3(nblk), dim3(1024), lds2, s, topk_ids, T, k, e_lo, E_L, cap, blk_hist,
+                       nblk, counts, offsets, row_token, row_slot, token_slot_row);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(index_scan_kernel, dim3(1), dim3(1024), 0, s,
                      blk_hist, nblk, E_L, cap, blk_base, counts, offsets);
   hipLaunchKernelGGL(k <= 8 ? index_scatter_kernel<8> : index_scatter_kernel<32>, dim3(nblk),

@@ -185,6 +185,34 @@ def test_dispatch_edges(case, fp8):
     check_dispatch(torch, p, x, ids)
 
 
+@pytest.mark.parametrize("T,E,E_L,k,cap", [
+    (16384 + 17, 64, 64, 4, 0),      # 65 blocks x 64 experts: the scan folded into the scatter
+    (33000, 512, 512, 2, 0),         # 129 x 512 histogram entries, past the fold: three launches
+    (33000, 512, 512, 2, 33000),     # the same in the masked layout
+    (20000, 1024, 1024, 3, 0)])      # 79 x 1024: three launches, the widest expert range
+def test_dispatch_index_large(T, E, E_L, k, cap):
+    """Index build past 256 tokens at both histogram sizes (two launches, or
+    three with a separate scan kernel), bit-exact against the oracle."""
+    torch = torch_cuda()
+    ml = _ml()
+    rng = np.random.default_rng(T + E + k)
+    ids = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+    x = np.zeros((T, 128), dtype=np.uint16)
+    p = ml.Problem(T=T, H=128, E=E, k=k, e_lo=0, E_L=E_L, I=128, capacity=cap)
+    say("dispatch index large", T, E, E_L, k, cap)
+    if cap:
+        g = run_dispatch(torch, p, x, ids)
+        r = O.index_build_masked(ids, 0, E_L, cap)
+        np.testing.assert_array_equal(g["counts"], r["counts"])
+        np.testing.assert_array_equal(g["offsets"], r["offsets"])
+        np.testing.assert_array_equal(g["tsr"], r["token_slot_row"])
+        used = r["row_token"] >= 0
+        np.testing.assert_array_equal(g["row_token"][used], r["row_token"][used])
+        np.testing.assert_array_equal(g["row_slot"][used], r["row_slot"][used])
+    else:
+        check_dispatch(torch, p, x, ids)
+
+
 def test_dispatch_repeated_ids_are_skipped():
     """A slot repeating an expert already chosen by an earlier slot of the
     same token is treated as non-local (memory-safe for any ids)."""

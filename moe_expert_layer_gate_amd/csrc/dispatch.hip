@@ -8,10 +8,10 @@
 // each row to its token and routing slot.  Page "OverlapAdvisor ...", section
 // 4.2.1: permute groups tokens by expert.
 //
-// The permutation is a stable counting sort done in three launches (two when
-// the histogram below has at most 64 Ki entries: the scatter blocks then do
-// the scan themselves), with no float and no order-dependent atomics (the
-// result is deterministic):
+// The permutation is a stable counting sort done in three launches (two while
+// the histogram below is small enough for every scatter block to read it: the
+// scatter blocks then do the scan themselves), with no float and no
+// order-dependent atomics (the result is deterministic):
 //   1. count:   each block of 256 tokens builds, in LDS, one 256-bit mask per
 //               local expert (bit i = token i of the block picked it) and
 //               writes the popcounts as its per-expert histogram;
@@ -231,14 +231,15 @@ __global__ __launch_bounds__(kTokBlock) void index_scatter_kernel(
   }
 }
 
-// The scan folded into the scatter, for histograms of at most kFoldHist
-// entries: every block reads the whole [nblk x E_L] histogram and derives what
-// it needs -- the experts' offsets and, per expert, the count of its pairs in
-// earlier blocks -- then scatters its tokens like index_scatter_kernel (block
-// b's tokens are threads 0..255); block 0 also writes counts and offsets.
+// The scan folded into the scatter while nblk x (the histogram's nblk x E_L
+// entries) is at most kFoldReads: every block reads the whole histogram and
+// derives what it needs -- the experts' offsets and, per expert, the count of
+// its pairs in earlier blocks -- then scatters its tokens like
+// index_scatter_kernel (block b's tokens are threads 0..255); block 0 also
+// writes counts and offsets.
 // Thread (part, e) of the 1024 sums expert e over the part's run of blocks,
 // as index_scan_kernel does.  mask: E_L * (kMaskWords + 1) words of LDS.
-constexpr int kFoldHist = 1 << 16;
+constexpr int64_t kFoldReads = 1 << 22;   // 16 MB of histogram reads in all
 
 template <int KMAX>
 __global__ __launch_bounds__(1024) void index_scan_scatter_kernel(
@@ -686,7 +687,7 @@ hipError_t launch_index_build(const int32_t* topk_ids, int T, int k, int e_lo, i
   hipLaunchKernelGGL(k <= 8 ? index_count_kernel<8> : index_count_kernel<32>, dim3(nblk),
                      dim3(kTokBlock), lds, s,
                      topk_ids, T, k, e_lo, E_L, blk_hist);
-  if (static_cast<int64_t>(nblk) * E_L <= kFoldHist) {  // two launches
+  if (static_cast<int64_t>(nblk) * nblk * E_L <= kFoldReads) {  // two launches
     const size_t lds2 = static_cast<size_t>(E_L) * (kMaskWords + 1) * sizeof(uint32_t);
     hipLaunchKernelGGL(k <= 8 ? index_scan_scatter_kernel<8> : index_scan_scatter_kernel<32>,
                        dim3(nblk), dim3(1024), lds2, s, topk_ids, T, k, e_lo, E_L, cap, blk_hist,

@@ -186,10 +186,10 @@ def test_dispatch_edges(case, fp8):
 
 
 @pytest.mark.parametrize("T,E,E_L,k,cap", [
-    (16384 + 17, 64, 64, 4, 0),      # 65 blocks x 64 experts: the scan folded into the scatter
-    (33000, 512, 512, 2, 0),         # 129 x 512 histogram entries, past the fold: three launches
+    (16384 + 17, 64, 64, 4, 0),      # 65 blocks, 65 x 65 x 64 reads: the scan folded in
+    (33000, 512, 512, 2, 0),         # 129 x 129 x 512 reads, past the fold: three launches
     (33000, 512, 512, 2, 33000),     # the same in the masked layout
-    (20000, 1024, 1024, 3, 0)])      # 79 x 1024: three launches, the widest expert range
+    (20000, 1024, 1024, 3, 0)])      # 79 x 79 x 1024: three launches, the widest expert range
 def test_dispatch_index_large(T, E, E_L, k, cap):
     """Index build past 256 tokens at both histogram sizes (two launches, or
     three with a separate scan kernel), bit-exact against the oracle."""

@@ -137,8 +137,12 @@ __global__ __launch_bounds__(1024) void tile_schedule_kernel(
   build_tile_table(e, E_L, cnt, tile_m, info, n_tiles, sync, status);
 }
 
+// silu(g) u = g u / (1 + exp(-g)) with the hardware reciprocal (1 ulp)
+// instead of an IEEE division: h is rounded to bf16 or an 8-bit code at once.
+// Large negative g: exp(-g) = inf, the reciprocal 0 and h -0, as the division
+// gives.
 __device__ __forceinline__ float silu_mul(float g, float u) {
-  return g / (1.0f + __expf(-g)) * u;
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
 // LDS row (within the weight tile) of the wave's weight block i (0..3).
@@ -578,8 +582,12 @@ hipError_t launch_pipelined(const GemmArgs& g, int64_t max_tiles, hipStream_t s)
 // stages of 128-byte K steps, loads three steps ahead (96 KB of weights in
 // flight per CU).  Same addressing, gather and output layouts as the other
 // kernels; rows past the segment load nothing.
+// A block may have NW = 8 waves: waves 0-3 compute as above, and every wave
+// issues its share of each step's direct loads (waves 4-7 only load and meet
+// the barriers).  Direct-to-LDS loads complete at a rate set by the waves
+// that have loads in flight, and a decode tile is nothing but its load stream.
 // ---------------------------------------------------------------------------
-constexpr int kSkBM = 32, kSkBN = 256, kSkThreads = 256;
+constexpr int kSkBM = 32, kSkBN = 256;
 // Cache policy of the skinny tiles' weight loads: non-temporal.  A decode
 // FFN reads every active expert's weights once (GBs, far past the 256 MB
 // MALL), so they need not stay in L2; the hint took the DeepSeek-V3 decode
@@ -589,7 +597,6 @@ constexpr int kSkBM = 32, kSkBN = 256, kSkThreads = 256;
 constexpr int kCpolStream = 2;
 constexpr int kSkStages = 4;
 constexpr int kSkStageBytes = (kSkBM + kSkBN) * kRowBytes;  // 36 KB
-constexpr int kSkLoads = (kSkBM + kSkBN) / 8 / 4;            // 1 A + 8 W per wave
 
 // Tile t of a skinny GEMM (t < m-tiles x nt_n): the m-tile table entry holds
 // the expert's first m-tile and m-tile count, and an expert's tiles run n-tile
@@ -602,7 +609,7 @@ __device__ __forceinline__ int4 skinny_decode(const GemmArgs& g, int t) {
   return make_int4(inf.x, mt, u / inf.z, inf.y + mt);
 }
 
-template <int MODE>
+template <int MODE, int NW>
 __device__ __forceinline__ void skinny_tile(const GemmArgs& g, int t, uint8_t* smem) {
   constexpr bool kSwiglu = MODE == MODE_SWIGLU || MODE == MODE_SWIGLU_FP8OUT;
   const int4 td = skinny_decode(g, t);
@@ -617,13 +624,18 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& g, int t, uint8_t* s
   const __amdgpu_buffer_rsrc_t rW = make_rsrc(g.W + e * g.w_stride, g.w_stride);
   const int nbase = kSwiglu ? nt * (kSkBN / 2) : nt * kSkBN;
 
-  const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
-  // direct loads: wave w moves A group w (8 of the 32 rows) and W groups
-  // 4 + 8w .. 4 + 8w + 7
-  int voff[kSkLoads], ldst[kSkLoads];
+  const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // direct loads: waves 0-3 move A group w (8 of the 32 rows); wave w moves
+  // W groups 4 + kWPer w .. 4 + kWPer (w + 1) - 1
+  constexpr int kWPer = kSkBN / 8 / NW;
+  const bool loads_a = w < kSkBM / 8, computes = w < 4;
+  const int wc = w & 3;  // the compute role (every wave's offsets stay in range)
+  // (sized for four waves: an array bound that depends on NW trips the host
+  // pass's check of the 16-byte direct load)
+  int voff[1 + kSkBN / 8 / 4], ldst[1 + kSkBN / 8 / 4];
 #pragma unroll
-  for (int q = 0; q < kSkLoads; ++q) {
-    const int grp = q == 0 ? w : kSkBM / 8 + w * 8 + (q - 1);
+  for (int q = 0; q < 1 + kWPer; ++q) {
+    const int grp = q == 0 ? wc : kSkBM / 8 + w * kWPer + (q - 1);
     const int rr = grp * 8 + (lane >> 3);
     const int chunk = (lane & 7) ^ ((rr >> 1) & 7);
     if (rr < kSkBM) {
@@ -645,13 +657,16 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& g, int t, uint8_t* s
   auto dma = [&](int step, int stage) {
     const int k = min(step, nk - 1);  // step k starts at 64-byte K piece 2k
     uint8_t* base = smem + stage * kSkStageBytes;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr_t)(base + ldst[0]), 16, voff[0],
-                                             2 * k * g.a_cs, 0, 0);
+    if (loads_a)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr_t)(base + ldst[0]), 16, voff[0],
+                                               2 * k * g.a_cs, 0, 0);
 #pragma unroll
-    for (int q = 1; q < kSkLoads; ++q)
+    for (int q = 1; q < 1 + kWPer; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, (lds_ptr_t)(base + ldst[q]), 16, voff[q],
                                                2 * k * g.w_cs, 0, kCpolStream);
   };
+  // the wave's loads of kSkStages - 2 steps may stay in flight
+  constexpr int kLa = (kSkStages - 2) * (1 + kWPer), kLw = (kSkStages - 2) * kWPer;
 
   const int lr = lane & 31, hi = lane >> 5, sl = (lr >> 1) & 7;
   int foff[4];
@@ -660,7 +675,7 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& g, int t, uint8_t* s
   int wbase[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
-    wbase[i] = (kSkBM + (kSwiglu ? i * (kSkBN / 2) + w * 32 : w * 64 + i * 32)) * kRowBytes;
+    wbase[i] = (kSkBM + (kSwiglu ? i * (kSkBN / 2) + wc * 32 : wc * 64 + i * 32)) * kRowBytes;
 
   f32x16 acc[2];
 #pragma unroll
@@ -670,27 +685,36 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& g, int t, uint8_t* s
 
 #pragma unroll
   for (int st = 0; st < kSkStages - 1; ++st) dma(st, st);
-  WAIT_VMCNT((kSkStages - 2) * kSkLoads);
+  if (loads_a)
+    WAIT_VMCNT(kLa);
+  else
+    WAIT_VMCNT(kLw);
   __builtin_amdgcn_s_barrier();
 
   int s_cur = 0;
   for (int kt = 0; kt < nk; ++kt) {
     const uint8_t* st = smem + s_cur * kSkStageBytes;
     dma(kt + kSkStages - 1, s_cur == 0 ? kSkStages - 1 : s_cur - 1);
+    if (computes) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const bf16x8 fb = *reinterpret_cast<const bf16x8*>(st + foff[kk]);
+      for (int kk = 0; kk < 4; ++kk) {
+        const bf16x8 fb = *reinterpret_cast<const bf16x8*>(st + foff[kk]);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const bf16x8 fa = *reinterpret_cast<const bf16x8*>(st + wbase[i] + foff[kk]);
-        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb, acc[i], 0, 0, 0);
+        for (int i = 0; i < 2; ++i) {
+          const bf16x8 fa = *reinterpret_cast<const bf16x8*>(st + wbase[i] + foff[kk]);
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb, acc[i], 0, 0, 0);
+        }
       }
     }
-    WAIT_VMCNT_LDS((kSkStages - 2) * kSkLoads);
+    if (loads_a)
+      WAIT_VMCNT_LDS(kLa);
+    else
+      WAIT_VMCNT_LDS(kLw);
     __builtin_amdgcn_s_barrier();
     s_cur = s_cur + 1 == kSkStages ? 0 : s_cur + 1;
   }
   WAIT_VMCNT(0);
+  if (!computes) return;  // the epilogue has no barrier
 
   // accumulator element q*4 + r: weight row q*8 + (lane/32)*4 + r of the
   // block, token row lane % 32
@@ -738,10 +762,9 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& g, int t, uint8_t* s
 // ---------------------------------------------------------------------------
 constexpr int kF8sScaleOff = (kSkBM + kSkBN) * kRowBytes;   // token scales after the rows
 constexpr int kF8sStageBytes = kF8sScaleOff + 256;           // 32 floats, padded to a lane load
-constexpr int kF8sLoads = kSkLoads + 1;                      // + one token-scale load per wave
 static_assert(kSkStages * kF8sStageBytes <= 160 * 1024 - 1024, "the ring fits the CU's LDS");
 
-template <int MODE>
+template <int MODE, int NW>
 __device__ __forceinline__ void f8_skinny_tile(const GemmArgs& g, int t, uint8_t* smem) {
   constexpr bool kSwiglu = MODE == MODE_SWIGLU_FP8OUT;
   __shared__ float row_amax[4][kSkBM];
@@ -763,14 +786,19 @@ __device__ __forceinline__ void f8_skinny_tile(const GemmArgs& g, int t, uint8_t
                             static_cast<int64_t>(min(seg_end - row0, kSkBM)) * kb_n * 4);
   const int nbase = kSwiglu ? nt * (kSkBN / 2) : nt * kSkBN;
 
-  const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
-  // direct loads: wave w moves A group w (8 of the 32 rows), W groups
-  // 4 + 8w .. 4 + 8w + 7, and the step's 32 token scales (every wave the
-  // same values to the same place)
-  int voff[kSkLoads], ldst[kSkLoads];
+  const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // direct loads: waves 0-3 move A group w (8 of the 32 rows), wave w W
+  // groups 4 + kWPer w .. 4 + kWPer (w + 1) - 1, and every wave the step's
+  // 32 token scales (the same values to the same place)
+  constexpr int kWPer = kSkBN / 8 / NW;
+  const bool loads_a = w < kSkBM / 8, computes = w < 4;
+  const int wc = w & 3;  // the compute role (every wave's offsets stay in range)
+  // (sized for four waves: an array bound that depends on NW trips the host
+  // pass's check of the 16-byte direct load)
+  int voff[1 + kSkBN / 8 / 4], ldst[1 + kSkBN / 8 / 4];
 #pragma unroll
-  for (int q = 0; q < kSkLoads; ++q) {
-    const int grp = q == 0 ? w : kSkBM / 8 + w * 8 + (q - 1);
+  for (int q = 0; q < 1 + kWPer; ++q) {
+    const int grp = q == 0 ? wc : kSkBM / 8 + w * kWPer + (q - 1);
     const int rr = grp * 8 + (lane >> 3);
     const int chunk = (lane & 7) ^ ((rr >> 1) & 7);
     if (rr < kSkBM) {
@@ -797,16 +825,19 @@ __device__ __forceinline__ void f8_skinny_tile(const GemmArgs& g, int t, uint8_t
     const bool live = step < nk;
     const int k = live ? step : 0;
     uint8_t* base = smem + stage * kF8sStageBytes;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr_t)(base + ldst[0]), 16,
-                                             live ? voff[0] : kOobOffset, k * kRowBytes, 0, 0);
+    if (loads_a)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr_t)(base + ldst[0]), 16,
+                                               live ? voff[0] : kOobOffset, k * kRowBytes, 0, 0);
 #pragma unroll
-    for (int q = 1; q < kSkLoads; ++q)
+    for (int q = 1; q < 1 + kWPer; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, (lds_ptr_t)(base + ldst[q]), 16,
                                                live ? voff[q] : kOobOffset, k * kRowBytes, 0,
                                                kCpolStream);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_ptr_t)(base + kF8sScaleOff), 4,
                                              live ? soff : kOobOffset, k * 4, 0, 0);
   };
+  // the wave's loads of kSkStages - 2 steps may stay in flight
+  constexpr int kLa = (kSkStages - 2) * (2 + kWPer), kLw = (kSkStages - 2) * (1 + kWPer);
 
   // fragments: a lane holds 32 contiguous K bytes, [64 kk + 32 hi, +32), of
   // its row (chunks c and c ^ 1 after the swizzle); weight tiles i = 0, 1
@@ -821,18 +852,16 @@ __device__ __forceinline__ void f8_skinny_tile(const GemmArgs& g, int t, uint8_t
   }
   int wbase[2];
   const float* swp[2];
-  const int wu = __builtin_amdgcn_readfirstlane(w);
   const float* wsc = g.W_scale + e * g.ws_stride;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int lrow = kSwiglu ? i * (kSkBN / 2) + w * 32 : w * 64 + i * 32;
+    const int lrow = kSwiglu ? i * (kSkBN / 2) + wc * 32 : wc * 64 + i * 32;
     wbase[i] = (kSkBM + lrow) * kRowBytes;
-    const int lrow_u = kSwiglu ? i * (kSkBN / 2) + wu * 32 : wu * 64 + i * 32;
     int grow;
     if (kSwiglu)
-      grow = lrow_u < kSkBN / 2 ? nbase + lrow_u : g.Nout + nbase + (lrow_u - kSkBN / 2);
+      grow = lrow < kSkBN / 2 ? nbase + lrow : g.Nout + nbase + (lrow - kSkBN / 2);
     else
-      grow = min(nbase + lrow_u, g.NW - 1);
+      grow = min(nbase + lrow, g.NW - 1);
     swp[i] = wsc + static_cast<int64_t>(grow / 128) * kb_n;
   }
 
@@ -844,45 +873,54 @@ __device__ __forceinline__ void f8_skinny_tile(const GemmArgs& g, int t, uint8_t
 
 #pragma unroll
   for (int st = 0; st < kSkStages - 1; ++st) dma(st, st);
-  WAIT_VMCNT((kSkStages - 2) * kF8sLoads);
+  if (loads_a)
+    WAIT_VMCNT(kLa);
+  else
+    WAIT_VMCNT(kLw);
   __builtin_amdgcn_s_barrier();
 
   int s_cur = 0;
   for (int kt = 0; kt < nk; ++kt) {
     const uint8_t* st = smem + s_cur * kF8sStageBytes;
     dma(kt + kSkStages - 1, s_cur == 0 ? kSkStages - 1 : s_cur - 1);
-    // weight block scales through the constant address space (scalar loads,
-    // outside the vector-memory wait count)
-    float sw[2];
+    if (computes) {
+      // weight block scales through the constant address space (scalar loads,
+      // outside the vector-memory wait count)
+      float sw[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      sw[i] = ((const __attribute__((address_space(4))) float*)(uintptr_t)swp[i])[kt];
-    const float sx = *reinterpret_cast<const float*>(st + kF8sScaleOff + lr * 4);
-    f32x16 tmp[2];
+      for (int i = 0; i < 2; ++i)
+        sw[i] = ((const __attribute__((address_space(4))) float*)(uintptr_t)swp[i])[kt];
+      const float sx = *reinterpret_cast<const float*>(st + kF8sScaleOff + lr * 4);
+      f32x16 tmp[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) tmp[i][r] = 0.0f;
+        for (int r = 0; r < 16; ++r) tmp[i][r] = 0.0f;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const i32x4 b0 = *reinterpret_cast<const i32x4*>(st + foff[2 * kk]);
-      const i32x4 b1 = *reinterpret_cast<const i32x4*>(st + foff[2 * kk + 1]);
-      const i32x8 fb = i32x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+      for (int kk = 0; kk < 2; ++kk) {
+        const i32x4 b0 = *reinterpret_cast<const i32x4*>(st + foff[2 * kk]);
+        const i32x4 b1 = *reinterpret_cast<const i32x4*>(st + foff[2 * kk + 1]);
+        const i32x8 fb = i32x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const i32x4 a0 = *reinterpret_cast<const i32x4*>(st + wbase[i] + foff[2 * kk]);
+          const i32x4 a1 = *reinterpret_cast<const i32x4*>(st + wbase[i] + foff[2 * kk + 1]);
+          const i32x8 fa = i32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+          tmp[i] =
+              __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb, tmp[i], 0, 0, 0, 0, 0, 0);
+        }
+      }
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const i32x4 a0 = *reinterpret_cast<const i32x4*>(st + wbase[i] + foff[2 * kk]);
-        const i32x4 a1 = *reinterpret_cast<const i32x4*>(st + wbase[i] + foff[2 * kk + 1]);
-        const i32x8 fa = i32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-        tmp[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa, fb, tmp[i], 0, 0, 0, 0, 0, 0);
+        const float sc = sw[i] * sx;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][r] += tmp[i][r] * sc;
       }
     }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const float sc = sw[i] * sx;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][r] += tmp[i][r] * sc;
-    }
-    WAIT_VMCNT_LDS((kSkStages - 2) * kF8sLoads);
+    if (loads_a)
+      WAIT_VMCNT_LDS(kLa);
+    else
+      WAIT_VMCNT_LDS(kLw);
     __builtin_amdgcn_s_barrier();
     s_cur = s_cur + 1 == kSkStages ? 0 : s_cur + 1;
   }
@@ -893,7 +931,7 @@ __device__ __forceinline__ void f8_skinny_tile(const GemmArgs& g, int t, uint8_t
   const int cq = hi * 4;
   const int m = row0 + lr;
   if constexpr (MODE == MODE_PLAIN) {
-    if (m >= seg_end) return;
+    if (!computes || m >= seg_end) return;
     uint8_t* C8 = static_cast<uint8_t*>(g.C);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -917,11 +955,11 @@ __device__ __forceinline__ void f8_skinny_tile(const GemmArgs& g, int t, uint8_t
       am = fmaxf(am, fabsf(hv[r]));
     }
     am = fmaxf(am, __shfl_xor(am, 32));
-    if (lane < 32) row_amax[w][lr] = am;
-    __syncthreads();
+    if (computes && lane < 32) row_amax[w][lr] = am;
+    __syncthreads();  // every wave of the block meets it
     am = fmaxf(fmaxf(row_amax[0][lr], row_amax[1][lr]), fmaxf(row_amax[2][lr], row_amax[3][lr]));
     const float sc = am > 0.0f ? am / 448.0f : 1.0f;
-    if (m >= seg_end) return;
+    if (!computes || m >= seg_end) return;
     uint8_t* crow = static_cast<uint8_t*>(g.C) + static_cast<int64_t>(m) * g.Nout;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -1268,14 +1306,17 @@ constexpr int kMsWOff = kMsBM * kMxK;                       // 4 KB
 constexpr int kMsTSOff = kMsWOff + kMxBN * (kMxK / 2);      // + 16 KB
 constexpr int kMsWSOff = kMsTSOff + 64 * 4;
 constexpr int kMsStageBytes = kMsWSOff + kMxBN * 4;         // 21760
-// per wave and step: one token row group (8 rows), four weight row groups
-// (16 rows), one weight-scale load and one token-scale load (every wave
-// writes the same token scales to the same place)
-constexpr int kMsLoads = 7;
+// A step's loads: 4 token row groups (8 rows), 16 weight row groups (16
+// rows), 4 weight-scale loads (64 rows) and the token scales, which every
+// wave loads (the same values to the same place).  With 4 waves a wave takes
+// one of each and 4 weight groups (7 loads); with 8 waves, 2 weight groups,
+// a token group (waves 0-3) or a weight-scale load (waves 4-7), and the
+// token scales (4 loads).
+template <int NW> constexpr int kMsLoads = NW == 4 ? 7 : 4;
 static_assert(kMsStages * kMsStageBytes <= 160 * 1024, "the ring fits the CU's LDS");
-static_assert((kMsStages - 1) * kMsLoads < 64, "loads in flight fit the vmcnt counter");
+static_assert((kMsStages - 1) * kMsLoads<4> < 64, "loads in flight fit the vmcnt counter");
 
-template <int MODE>
+template <int MODE, int NW>
 __device__ __forceinline__ void mx_skinny_tile(const GemmArgs& g, int t, uint8_t* smem) {
   constexpr bool kSwiglu = MODE == MODE_SWIGLU_MX8OUT;
   const int4 td = skinny_decode(g, t);
@@ -1303,39 +1344,48 @@ __device__ __forceinline__ void mx_skinny_tile(const GemmArgs& g, int t, uint8_t
     return min(nbase + r, g.NW - 1);
   };
 
-  const int lane = lane_id(), w = threadIdx.x >> 6;
-  int voff[kMsLoads];
+  const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  constexpr int kWPer = 16 / NW;  // weight row groups per wave
+  const bool computes = w < 4;
+  const bool loads_a = NW == 4 || w < 4, loads_ws = NW == 4 || w >= 4;
+  const int wc = w & 3;                  // the compute role and token row group
+  const int wsw = NW == 4 ? w : w & 3;   // the weight-scale load's 64 rows
+  int voff[16 / 4 + 3];  // sized for four waves (see the bf16 tile)
   {
-    const int rr = w * 8 + (lane >> 3);
+    const int rr = wc * 8 + (lane >> 3);
     const int c = (lane & 7) ^ ((rr >> 1) & 7);
     voff[0] = row0 + rr < seg_end ? arow(rr) * K + c * 16 : kOobOffset;
   }
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int r = (w * 4 + q) * 16 + (lane >> 2);
+  for (int q = 0; q < kWPer; ++q) {
+    const int r = (w * kWPer + q) * 16 + (lane >> 2);
     const int cw = (lane & 3) ^ ((r >> 2) & 3);
     voff[1 + q] = wrow(r) * g.w_rs + cw * 16;
   }
-  voff[5] = wrow(w * 64 + lane) * g.ws_rs;
-  voff[6] = lane < kMsBM && row0 + lane < seg_end ? arow(lane) * kb : kOobOffset;
+  voff[kWPer + 1] = wrow(wsw * 64 + lane) * g.ws_rs;
+  voff[kWPer + 2] = lane < kMsBM && row0 + lane < seg_end ? arow(lane) * kb : kOobOffset;
   auto dma = [&](int step, int stage) {
     // steps past the last one load nothing (out-of-range offsets)
     const bool live = step < nk;
     const int k = live ? step : 0;
     uint8_t* base = smem + stage * kMsStageBytes;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr_t)(base + w * 1024), 16,
-                                             live ? voff[0] : kOobOffset, k * kMxK, 0, 0);
+    if (loads_a)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr_t)(base + wc * 1024), 16,
+                                               live ? voff[0] : kOobOffset, k * kMxK, 0, 0);
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, (lds_ptr_t)(base + kMsWOff + (w * 4 + q) * 1024),
-                                               16, live ? voff[1 + q] : kOobOffset, k * g.w_cs,
+    for (int q = 0; q < kWPer; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rW, (lds_ptr_t)(base + kMsWOff + (w * kWPer + q) * 1024), 16,
+          live ? voff[1 + q] : kOobOffset, k * g.w_cs, 0, kCpolStream);
+    if (loads_ws)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rWS, (lds_ptr_t)(base + kMsWSOff + wsw * 256), 4,
+                                               live ? voff[kWPer + 1] : kOobOffset, k * g.ws_cs,
                                                0, kCpolStream);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rWS, (lds_ptr_t)(base + kMsWSOff + w * 256), 4,
-                                             live ? voff[5] : kOobOffset, k * g.ws_cs, 0,
-                                             kCpolStream);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rAS, (lds_ptr_t)(base + kMsTSOff), 4,
-                                             live ? voff[6] : kOobOffset, k * 4, 0, 0);
+                                             live ? voff[kWPer + 2] : kOobOffset, k * 4, 0, 0);
   };
+  // the wave's loads of kMsStages - 2 steps may stay in flight
+  constexpr int kWait = (kMsStages - 2) * kMsLoads<NW>;
 
   // fragments: weight tiles i = 0, 1 of wave w (SwiGLU: gate rows w*32.. and
   // up rows 128 + w*32..; plain: rows w*64 + i*32..), token lane % 32
@@ -1343,7 +1393,7 @@ __device__ __forceinline__ void mx_skinny_tile(const GemmArgs& g, int t, uint8_t
   int wfr[2][2], wsc[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int r = (kSwiglu ? i * (kMxBN / 2) + w * 32 : w * 64 + i * 32) + lr;
+    const int r = (kSwiglu ? i * (kMxBN / 2) + wc * 32 : wc * 64 + i * 32) + lr;
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
       wfr[i][hh] = kMsWOff + r * 64 + (((2 * hh + hi) ^ ((r >> 2) & 3)) * 16);
@@ -1365,37 +1415,40 @@ __device__ __forceinline__ void mx_skinny_tile(const GemmArgs& g, int t, uint8_t
 
 #pragma unroll
   for (int st = 0; st < kMsStages - 1; ++st) dma(st, st);
-  WAIT_VMCNT((kMsStages - 2) * kMsLoads);
+  WAIT_VMCNT(kWait);
   __builtin_amdgcn_s_barrier();
 
   int s_cur = 0;
   for (int kt = 0; kt < nk; ++kt) {
     const uint8_t* st = smem + s_cur * kMsStageBytes;
     dma(kt + kMsStages - 1, s_cur == 0 ? kMsStages - 1 : s_cur - 1);
-    const uint32_t ts = *reinterpret_cast<const uint32_t*>(st + tsc);
-    uint32_t ws[2];
+    if (computes) {
+      const uint32_t ts = *reinterpret_cast<const uint32_t*>(st + tsc);
+      uint32_t ws[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) ws[i] = *reinterpret_cast<const uint32_t*>(st + wsc[i]);
+      for (int i = 0; i < 2; ++i) ws[i] = *reinterpret_cast<const uint32_t*>(st + wsc[i]);
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const i32x4 p0 = *reinterpret_cast<const i32x4*>(st + tfr[hh][0]);
-      const i32x4 p1 = *reinterpret_cast<const i32x4*>(st + tfr[hh][1]);
-      const i32x8 tb = i32x8{p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
-      const int sb = static_cast<int>((ts >> (16 * hh + 8 * hi)) & 0xff);
+      for (int hh = 0; hh < 2; ++hh) {
+        const i32x4 p0 = *reinterpret_cast<const i32x4*>(st + tfr[hh][0]);
+        const i32x4 p1 = *reinterpret_cast<const i32x4*>(st + tfr[hh][1]);
+        const i32x8 tb = i32x8{p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+        const int sb = static_cast<int>((ts >> (16 * hh + 8 * hi)) & 0xff);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const i32x4 p = *reinterpret_cast<const i32x4*>(st + wfr[i][hh]);
-        const i32x8 wa = i32x8{p[0], p[1], p[2], p[3], 0, 0, 0, 0};
-        const int sa = static_cast<int>((ws[i] >> (16 * hh + 8 * hi)) & 0xff);
-        acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wa, tb, acc[i], 4, 0, 0, sa, 0,
-                                                                  sb);
+        for (int i = 0; i < 2; ++i) {
+          const i32x4 p = *reinterpret_cast<const i32x4*>(st + wfr[i][hh]);
+          const i32x8 wa = i32x8{p[0], p[1], p[2], p[3], 0, 0, 0, 0};
+          const int sa = static_cast<int>((ws[i] >> (16 * hh + 8 * hi)) & 0xff);
+          acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wa, tb, acc[i], 4, 0, 0, sa,
+                                                                    0, sb);
+        }
       }
     }
-    WAIT_VMCNT_LDS((kMsStages - 2) * kMsLoads);
+    WAIT_VMCNT_LDS(kWait);
     __builtin_amdgcn_s_barrier();
     s_cur = s_cur + 1 == kMsStages ? 0 : s_cur + 1;
   }
   WAIT_VMCNT(0);
+  if (!computes) return;  // the epilogue has no barrier
 
   // accumulator element q*4 + r: weight row q*8 + (lane/32)*4 + r of the
   // tile, token lane % 32
@@ -1478,8 +1531,14 @@ constexpr int kSpinLimit = 1 << 22;  // about half a second of s_sleep 2 polls
 // KIND: the skinny tiles of one element type -- kSkBf16, kSkMx (MXFP4
 // weights, MXFP8 tokens and h) or kSkFp8 (block-FP8).
 enum { kSkBf16 = 0, kSkMx = 1, kSkFp8 = 2 };
+// Waves per block of the skinny tiles of each element type (waves 0-3
+// compute, the others only load).  Measured on the DeepSeek-V3 decode batch
+// (FFN, 8 against 4 waves, alternating runs on one GPU): block-FP8 0.214 ->
+// 0.211 ms, MXFP4 0.1345 -> 0.1336 ms, bf16 0.3778 -> 0.3789 ms; so the
+// load stream of these tiles is not bound by the waves that issue it.
+constexpr int sk_waves(int kind) { return kind == kSkBf16 ? 4 : 8; }
 template <int UPMODE, int KIND>
-__global__ __launch_bounds__(kSkThreads, 1) void ffn_fused_skinny_kernel(
+__global__ __launch_bounds__(64 * sk_waves(KIND), 1) void ffn_fused_skinny_kernel(
     const GemmArgs gu, const GemmArgs gd, int32_t* sync, int32_t* status, int wait_extra,
     int spin_limit) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
@@ -1491,13 +1550,14 @@ __global__ __launch_bounds__(kSkThreads, 1) void ffn_fused_skinny_kernel(
   const int t = s_ticket;
   if (t >= total) return;
   int32_t* done = sync + 1;
+  constexpr int NW = sk_waves(KIND);
   if (t < n_up) {
     if constexpr (KIND == kSkMx)
-      mx_skinny_tile<UPMODE>(gu, t, smem);
+      mx_skinny_tile<UPMODE, NW>(gu, t, smem);
     else if constexpr (KIND == kSkFp8)
-      f8_skinny_tile<UPMODE>(gu, t, smem);
+      f8_skinny_tile<UPMODE, NW>(gu, t, smem);
     else
-      skinny_tile<UPMODE>(gu, t, smem);
+      skinny_tile<UPMODE, NW>(gu, t, smem);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -1526,11 +1586,11 @@ __global__ __launch_bounds__(kSkThreads, 1) void ffn_fused_skinny_kernel(
   __syncthreads();
   if (!s_ready) return;  // reported through the status word
   if constexpr (KIND == kSkMx)
-    mx_skinny_tile<MODE_PLAIN>(gd, td, smem);
+    mx_skinny_tile<MODE_PLAIN, NW>(gd, td, smem);
   else if constexpr (KIND == kSkFp8)
-    f8_skinny_tile<MODE_PLAIN>(gd, td, smem);
+    f8_skinny_tile<MODE_PLAIN, NW>(gd, td, smem);
   else
-    skinny_tile<MODE_PLAIN>(gd, td, smem);
+    skinny_tile<MODE_PLAIN, NW>(gd, td, smem);
 }
 
 template <int UPMODE, int KIND>
@@ -1551,8 +1611,8 @@ hipError_t launch_fused(const GemmArgs& gu, const GemmArgs& gd, int64_t max_tile
   const bool test_timeout = unreachable && unreachable[0] == '1';
   const int wait_extra = test_timeout ? 1 : 0;
   const int spin_limit = test_timeout ? 16 : kSpinLimit;
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(kSkThreads), lds, s, gu, gd,
-                     sync, status, wait_extra, spin_limit);
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(64 * sk_waves(KIND)), lds, s,
+                     gu, gd, sync, status, wait_extra, spin_limit);
   return hipGetLastError();
 }
 
@@ -1782,7 +1842,7 @@ __device__ __forceinline__ void big_epilogue(const GemmArgs& g, f32x16 (&acc)[4]
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float gt = acc[hb][j][q * 4 + r], up = acc[hb + 2][j][q * 4 + r];
-            hv[r] = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
+            hv[r] = silu_mul(gt, up);
           }
           uint2 o;
           o.x = pack_bf16x2(hv[0], hv[1]);

@@ -1301,24 +1301,41 @@ hipError_t launch_mx(const GemmArgs& g, int64_t max_tiles, hipStream_t s) {
 // [256][64 B], 64 token-scale dwords (rows 32..63 read as zeros) and 256
 // weight-scale dwords.
 // ---------------------------------------------------------------------------
-constexpr int kMsBM = 32, kMsStages = 7;
-constexpr int kMsWOff = kMsBM * kMxK;                       // 4 KB
-constexpr int kMsTSOff = kMsWOff + kMxBN * (kMxK / 2);      // + 16 KB
-constexpr int kMsWSOff = kMsTSOff + 64 * 4;
-constexpr int kMsStageBytes = kMsWSOff + kMxBN * 4;         // 21760
-// A step's loads: 4 token row groups (8 rows), 16 weight row groups (16
-// rows), 4 weight-scale loads (64 rows) and the token scales, which every
-// wave loads (the same values to the same place).  With 4 waves a wave takes
-// one of each and 4 weight groups (7 loads); with 8 waves, 2 weight groups,
-// a token group (waves 0-3) or a weight-scale load (waves 4-7), and the
-// token scales (4 loads).
-template <int NW> constexpr int kMsLoads = NW == 4 ? 7 : 4;
-static_assert(kMsStages * kMsStageBytes <= 160 * 1024, "the ring fits the CU's LDS");
-static_assert((kMsStages - 1) * kMsLoads<4> < 64, "loads in flight fit the vmcnt counter");
+constexpr int kMsBM = 32;
+// Ring of the skinny MX tile with BN weight rows: a stage holds the token
+// rows [32][128 B], the weight rows [BN][64 B], 64 token-scale dwords and BN
+// weight-scale dwords; seven stages of 21 KB (BN = 256) or four of 38 KB
+// (BN = 512, the down GEMM's tile: half the tiles, so half the per-tile
+// costs -- ticket, table reads, first loads, the acquire that invalidates the
+// XCD's L2 -- for the same weight bytes in flight).
+template <int BN> struct MsGeom {
+  static constexpr int kWOff = kMsBM * kMxK;               // 4 KB of token rows
+  static constexpr int kTSOff = kWOff + BN * (kMxK / 2);   // weight rows
+  static constexpr int kWSOff = kTSOff + 64 * 4;           // token scales
+  static constexpr int kStageBytes = kWSOff + BN * 4;      // weight scales
+  static constexpr int kStages = BN == 256 ? 7 : 4;
+  static_assert(kStages * kStageBytes <= 160 * 1024 - 1024, "the ring fits the CU's LDS");
+};
+constexpr size_t kMsRingBytes =
+    MsGeom<256>::kStages * MsGeom<256>::kStageBytes > MsGeom<512>::kStages * MsGeom<512>::kStageBytes
+        ? MsGeom<256>::kStages * MsGeom<256>::kStageBytes
+        : MsGeom<512>::kStages * MsGeom<512>::kStageBytes;
+// A step's loads: 4 token row groups (8 rows), BN / 16 weight row groups (16
+// rows), BN / 64 weight-scale loads (64 rows) and the token scales, which
+// every wave loads (the same values to the same place).  BN = 256, 4 waves:
+// a wave takes one of each and 4 weight groups (7 loads); 8 waves: 2 weight
+// groups and a token group (waves 0-3) or a weight-scale load (waves 4-7)
+// (4 loads).  BN = 512, 8 waves: 4 weight groups, a weight-scale load and a
+// token group (waves 0-3: 7 loads, the others 6).
 
-template <int MODE, int NW>
+template <int MODE, int NW, int BN>
 __device__ __forceinline__ void mx_skinny_tile(const GemmArgs& g, int t, uint8_t* smem) {
   constexpr bool kSwiglu = MODE == MODE_SWIGLU_MX8OUT;
+  static_assert(BN == 256 || (BN == 512 && NW == 8 && MODE == MODE_PLAIN),
+                "512-row tiles: the plain (down) GEMM, eight computing waves");
+  using G = MsGeom<BN>;
+  constexpr int kMsStages = G::kStages, kMsStageBytes = G::kStageBytes;
+  constexpr int kMsWOff = G::kWOff, kMsTSOff = G::kTSOff, kMsWSOff = G::kWSOff;
   const int4 td = skinny_decode(g, t);
   const int e = td.x, mt = td.y, nt = td.z;
   const int2 sg = segment(g.seg, g.seg_cap, e);
@@ -1335,7 +1352,7 @@ __device__ __forceinline__ void mx_skinny_tile(const GemmArgs& g, int t, uint8_t
   const __amdgpu_buffer_rsrc_t rAS =
       make_rsrc(As + a_skip / K * kb, (g.a_bytes - a_skip) / K * kb);
   const __amdgpu_buffer_rsrc_t rWS = make_rsrc(Ws + e * g.ws_stride, g.ws_stride);
-  const int nbase = kSwiglu ? nt * (kMxBN / 2) : nt * kMxBN;
+  const int nbase = kSwiglu ? nt * (kMxBN / 2) : nt * BN;
   auto arow = [&](int rr) { return g.a_index ? g.a_index[row0 + rr] : rr; };
   auto wrow = [&](int r) {  // weight row (within the expert) of tile row r
     if (kSwiglu)
@@ -1345,12 +1362,14 @@ __device__ __forceinline__ void mx_skinny_tile(const GemmArgs& g, int t, uint8_t
   };
 
   const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  constexpr int kWPer = 16 / NW;  // weight row groups per wave
-  const bool computes = w < 4;
-  const bool loads_a = NW == 4 || w < 4, loads_ws = NW == 4 || w >= 4;
-  const int wc = w & 3;                  // the compute role and token row group
-  const int wsw = NW == 4 ? w : w & 3;   // the weight-scale load's 64 rows
-  int voff[16 / 4 + 3];  // sized for four waves (see the bf16 tile)
+  constexpr int kWPer = BN / 16 / NW;  // weight row groups per wave
+  const bool computes = BN == 512 || w < 4;
+  const bool loads_a = NW == 4 || w < 4;
+  const bool loads_ws = NW == 4 || BN == 512 || w >= 4;
+  const int wc = w & 3;                                  // token row group
+  const int wr = BN == 512 ? w : wc;                     // the compute role
+  const int wsw = NW == 4 || BN == 512 ? w : w & 3;      // the weight-scale load's 64 rows
+  int voff[16 / 4 + 3];  // sized for the largest count, 7 (see the bf16 tile)
   {
     const int rr = wc * 8 + (lane >> 3);
     const int c = (lane & 7) ^ ((rr >> 1) & 7);
@@ -1385,7 +1404,9 @@ __device__ __forceinline__ void mx_skinny_tile(const GemmArgs& g, int t, uint8_t
                                              live ? voff[kWPer + 2] : kOobOffset, k * 4, 0, 0);
   };
   // the wave's loads of kMsStages - 2 steps may stay in flight
-  constexpr int kWait = (kMsStages - 2) * kMsLoads<NW>;
+  constexpr int kWaitAll = (kMsStages - 2) * (kWPer + 3), kWaitOne = (kMsStages - 2) * (kWPer + 2);
+  static_assert((kMsStages - 1) * (kWPer + 3) < 64, "loads in flight fit the vmcnt counter");
+  const bool all_loads = loads_a && loads_ws;
 
   // fragments: weight tiles i = 0, 1 of wave w (SwiGLU: gate rows w*32.. and
   // up rows 128 + w*32..; plain: rows w*64 + i*32..), token lane % 32
@@ -1393,7 +1414,7 @@ __device__ __forceinline__ void mx_skinny_tile(const GemmArgs& g, int t, uint8_t
   int wfr[2][2], wsc[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int r = (kSwiglu ? i * (kMxBN / 2) + wc * 32 : wc * 64 + i * 32) + lr;
+    const int r = (kSwiglu ? i * (kMxBN / 2) + wr * 32 : wr * 64 + i * 32) + lr;
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
       wfr[i][hh] = kMsWOff + r * 64 + (((2 * hh + hi) ^ ((r >> 2) & 3)) * 16);
@@ -1415,7 +1436,10 @@ __device__ __forceinline__ void mx_skinny_tile(const GemmArgs& g, int t, uint8_t
 
 #pragma unroll
   for (int st = 0; st < kMsStages - 1; ++st) dma(st, st);
-  WAIT_VMCNT(kWait);
+  if (all_loads)
+    WAIT_VMCNT(kWaitAll);
+  else
+    WAIT_VMCNT(kWaitOne);
   __builtin_amdgcn_s_barrier();
 
   int s_cur = 0;
@@ -1443,7 +1467,10 @@ __device__ __forceinline__ void mx_skinny_tile(const GemmArgs& g, int t, uint8_t
         }
       }
     }
-    WAIT_VMCNT_LDS(kWait);
+    if (all_loads)
+      WAIT_VMCNT_LDS(kWaitAll);
+    else
+      WAIT_VMCNT_LDS(kWaitOne);
     __builtin_amdgcn_s_barrier();
     s_cur = s_cur + 1 == kMsStages ? 0 : s_cur + 1;
   }
@@ -1537,6 +1564,8 @@ enum { kSkBf16 = 0, kSkMx = 1, kSkFp8 = 2 };
 // 0.211 ms, MXFP4 0.1345 -> 0.1336 ms, bf16 0.3778 -> 0.3789 ms; so the
 // load stream of these tiles is not bound by the waves that issue it.
 constexpr int sk_waves(int kind) { return kind == kSkBf16 ? 4 : 8; }
+// Weight rows of the MX down GEMM's skinny tile (the up GEMM's are 256).
+constexpr int kMsDownBN = 512;
 template <int UPMODE, int KIND>
 __global__ __launch_bounds__(64 * sk_waves(KIND), 1) void ffn_fused_skinny_kernel(
     const GemmArgs gu, const GemmArgs gd, int32_t* sync, int32_t* status, int wait_extra,
@@ -1553,7 +1582,7 @@ __global__ __launch_bounds__(64 * sk_waves(KIND), 1) void ffn_fused_skinny_kerne
   constexpr int NW = sk_waves(KIND);
   if (t < n_up) {
     if constexpr (KIND == kSkMx)
-      mx_skinny_tile<UPMODE, NW>(gu, t, smem);
+      mx_skinny_tile<UPMODE, NW, 256>(gu, t, smem);
     else if constexpr (KIND == kSkFp8)
       f8_skinny_tile<UPMODE, NW>(gu, t, smem);
     else
@@ -1586,7 +1615,7 @@ __global__ __launch_bounds__(64 * sk_waves(KIND), 1) void ffn_fused_skinny_kerne
   __syncthreads();
   if (!s_ready) return;  // reported through the status word
   if constexpr (KIND == kSkMx)
-    mx_skinny_tile<MODE_PLAIN, NW>(gd, td, smem);
+    mx_skinny_tile<MODE_PLAIN, NW, kMsDownBN>(gd, td, smem);
   else if constexpr (KIND == kSkFp8)
     f8_skinny_tile<MODE_PLAIN, NW>(gd, td, smem);
   else
@@ -1598,7 +1627,7 @@ hipError_t launch_fused(const GemmArgs& gu, const GemmArgs& gd, int64_t max_tile
                         int32_t* status, hipStream_t s) {
   static_assert(kSkStages * kSkStageBytes <= 160 * 1024, "the ring fits the CU's LDS");
   auto kern = ffn_fused_skinny_kernel<UPMODE, KIND>;
-  const size_t lds = KIND == kSkMx    ? kMsStages * kMsStageBytes
+  const size_t lds = KIND == kSkMx    ? kMsRingBytes
                      : KIND == kSkFp8 ? kSkStages * kF8sStageBytes
                                       : kSkStages * kSkStageBytes;
   static std::atomic<uint64_t> lds_set{0};
@@ -2824,6 +2853,7 @@ hipError_t launch_ffn_fused(const GemmLaunch& up, const GemmLaunch& down, int32_
   if (err != hipSuccess) return err;
   if (up.path == GEMM_MX_SKINNY) {  // SwiGLU with MXFP8 h only
     if (!up.swiglu) return hipErrorInvalidValue;
+    gd.nt_n = ceil_div(down.Nout, kMsDownBN);  // the down GEMM's wider tiles
     return launch_fused<MODE_SWIGLU_MX8OUT, kSkMx>(gu, gd, up.max_tiles, sync, status, s);
   }
   if (up.fp8) {  // SwiGLU with block-FP8 h only

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 9
+#define MOE_ABI_VERSION 10
 
 typedef enum {
   MOE_OK = 0,
@@ -217,7 +217,7 @@ moe_status moe_dispatch(const moe_problem* p, const void* x,
                         const int32_t* topk_ids, int32_t* counts,
                         int32_t* offsets, int32_t* row_token,
                         int32_t* row_slot, int32_t* token_slot_row,
-                        void* x_perm, float* x_perm_scale, void* ws,
+                        void* x_perm, void* x_perm_scale, void* ws,
                         size_t ws_bytes, void* stream);
 
 /* Grouped expert FFN.  Page "OverlapAdvisor ...", section 4.2.2 and Eq. 8
@@ -235,15 +235,19 @@ moe_status moe_dispatch(const moe_problem* p, const void* x,
  *   x_perm, x_perm_scale, offsets: as produced by moe_dispatch (counts for
  *              the masked layout)
  *   h          [N_cap, I] (optional, NULL = kept in the workspace): bf16,
- *              or E4M3 with h_scale [N_cap, I/128] fp32 for MOE_FP8_E4M3
+ *              or E4M3 with h_scale [N_cap, I/128] fp32 for MOE_FP8_E4M3,
+ *              or MXFP8 (E4M3) with h_scale E8M0 bytes [N_cap, I/32] for
+ *              MOE_MXFP4.  The scale pointers of this call, of moe_dispatch
+ *              and of moe_grouped_ffn_gather are untyped: they carry fp32
+ *              (block-FP8) or E8M0 bytes (MXFP4) by element type
  *   y_perm     [N_cap, H] bf16 (output)
  * Routing weights are NOT applied here (moe_combine applies them).
  * Only the segments' rows are read or written.  With E_L = 1 and
  * offsets = {0, T} this is a dense SwiGLU FFN (how a shared expert is run).
  * Workspace: moe_workspace_bytes(p, MOE_STAGE_FFN).                        */
 moe_status moe_grouped_ffn(const moe_problem* p, const void* x_perm,
-                           const float* x_perm_scale, const int32_t* offsets,
-                           const moe_weights* w, void* h, float* h_scale,
+                           const void* x_perm_scale, const int32_t* offsets,
+                           const moe_weights* w, void* h, void* h_scale,
                            void* y_perm, void* ws, size_t ws_bytes,
                            void* stream);
 
@@ -264,10 +268,10 @@ moe_status moe_grouped_ffn(const moe_problem* p, const void* x_perm,
  * MOE_ERR_UNSUPPORTED for x of 2 GiB or more.
  * Workspace: moe_workspace_bytes(p, MOE_STAGE_FFN).                        */
 moe_status moe_grouped_ffn_gather(const moe_problem* p, const void* x,
-                                  const float* x_scale,
+                                  const void* x_scale,
                                   const int32_t* row_token,
                                   const int32_t* offsets, const moe_weights* w,
-                                  void* h, float* h_scale, void* y_perm,
+                                  void* h, void* h_scale, void* y_perm,
                                   void* ws, size_t ws_bytes, void* stream);
 
 /* Combine.  Page "CascadeEP ...", Appendix C, "Output return and combine"

@@ -511,7 +511,7 @@ moe_status moe_route(const moe_problem* p, const float* logits, int32_t* topk_id
 
 moe_status moe_dispatch(const moe_problem* p, const void* x, const int32_t* topk_ids,
                         int32_t* counts, int32_t* offsets, int32_t* row_token, int32_t* row_slot,
-                        int32_t* token_slot_row, void* x_perm, float* x_perm_scale, void* ws,
+                        int32_t* token_slot_row, void* x_perm, void* x_perm_scale, void* ws,
                         size_t ws_bytes, void* stream) {
   moe_status st = check_problem(p);
   if (st != MOE_OK) return st;
@@ -525,12 +525,15 @@ moe_status moe_dispatch(const moe_problem* p, const void* x, const int32_t* topk
     return MOE_ERR_INVALID_ARG;
   if (!ws || ws_bytes < moe_workspace_bytes(p, MOE_STAGE_DISPATCH)) return MOE_ERR_WORKSPACE;
   if (p->num_tokens == 0) return MOE_OK;
+  // scales: fp32 (block-FP8) or E8M0 bytes (MXFP4); the kernels take either
+  // through one float pointer and read it by the element type
   return run_dispatch(p, x, topk_ids, counts, offsets, row_token, row_slot, token_slot_row, x_perm,
-                      x_perm_scale, align_ws(ws), static_cast<hipStream_t>(stream));
+                      static_cast<float*>(x_perm_scale), align_ws(ws),
+                      static_cast<hipStream_t>(stream));
 }
 
-moe_status moe_grouped_ffn(const moe_problem* p, const void* x_perm, const float* x_perm_scale,
-                           const int32_t* offsets, const moe_weights* w, void* h, float* h_scale,
+moe_status moe_grouped_ffn(const moe_problem* p, const void* x_perm, const void* x_perm_scale,
+                           const int32_t* offsets, const moe_weights* w, void* h, void* h_scale,
                            void* y_perm, void* ws, size_t ws_bytes, void* stream) {
   moe_status st = check_problem(p);
   if (st != MOE_OK) return st;
@@ -545,13 +548,14 @@ moe_status moe_grouped_ffn(const moe_problem* p, const void* x_perm, const float
   if (p->num_tokens == 0) return MOE_OK;
   Carve c(align_ws(ws));
   const FfnScratch f = carve_ffn(c, p);
-  const FfnSource src{x_perm, x_perm_scale, false, nullptr, 0};
-  return run_ffn(p, src, offsets, w, h, h_scale, y_perm, f, static_cast<hipStream_t>(stream));
+  const FfnSource src{x_perm, static_cast<const float*>(x_perm_scale), false, nullptr, 0};
+  return run_ffn(p, src, offsets, w, h, static_cast<float*>(h_scale), y_perm, f,
+                 static_cast<hipStream_t>(stream));
 }
 
-moe_status moe_grouped_ffn_gather(const moe_problem* p, const void* x, const float* x_scale,
+moe_status moe_grouped_ffn_gather(const moe_problem* p, const void* x, const void* x_scale,
                                   const int32_t* row_token, const int32_t* offsets,
-                                  const moe_weights* w, void* h, float* h_scale, void* y_perm,
+                                  const moe_weights* w, void* h, void* h_scale, void* y_perm,
                                   void* ws, size_t ws_bytes, void* stream) {
   moe_status st = check_problem(p);
   if (st != MOE_OK) return st;
@@ -567,8 +571,10 @@ moe_status moe_grouped_ffn_gather(const moe_problem* p, const void* x, const flo
   if (p->num_tokens == 0) return MOE_OK;
   Carve c(align_ws(ws));
   const FfnScratch f = carve_ffn(c, p);
-  const FfnSource src{x, quant_acts(p) ? x_scale : nullptr, true, row_token, p->num_tokens};
-  return run_ffn(p, src, offsets, w, h, h_scale, y_perm, f, static_cast<hipStream_t>(stream));
+  const FfnSource src{x, quant_acts(p) ? static_cast<const float*>(x_scale) : nullptr, true,
+                      row_token, p->num_tokens};
+  return run_ffn(p, src, offsets, w, h, static_cast<float*>(h_scale), y_perm, f,
+                 static_cast<hipStream_t>(stream));
 }
 
 moe_status moe_combine(const moe_problem* p, const void* y_perm, const int32_t* token_slot_row,

@@ -87,6 +87,9 @@ SMALL_MX = {
     "mx_shared": (small_cfg(T=150, H=1024, E=64, E_L=16, e_lo=16, k=8, I=512, I_s=256,
                             mx=True), 43),
     "mx_decode": (small_cfg(T=16, H=1024, E=64, E_L=16, e_lo=0, k=8, I=256, mx=True), 44),
+    # the down GEMM's 512-row skinny tiles: H = 2 x 512 + 128, so the last
+    # tile of every m-tile has 128 live weight rows
+    "mx_decode_h1152": (small_cfg(T=20, H=1152, E=32, E_L=8, e_lo=0, k=6, I=256, mx=True), 48),
     # k above 8: the any-k index build and the one-launch layer front
     "mx_k12_decode": (small_cfg(T=24, H=512, E=64, E_L=16, e_lo=8, k=12, I=256, mx=True), 47),
     # up to 32 rows per expert on average: the fused skinny MX kernel, some

@@ -584,8 +584,7 @@ hipError_t launch_pipelined(const GemmArgs& g, int64_t max_tiles, hipStream_t s)
 // kernels; rows past the segment load nothing.
 // A block may have NW = 8 waves: waves 0-3 compute as above, and every wave
 // issues its share of each step's direct loads (waves 4-7 only load and meet
-// the barriers).  Direct-to-LDS loads complete at a rate set by the waves
-// that have loads in flight, and a decode tile is nothing but its load stream.
+// the barriers); sk_waves below says which element types use them.
 // ---------------------------------------------------------------------------
 constexpr int kSkBM = 32, kSkBN = 256;
 // Cache policy of the skinny tiles' weight loads: non-temporal.  A decode

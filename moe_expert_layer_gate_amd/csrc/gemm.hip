@@ -595,7 +595,6 @@ constexpr int kSkBM = 32, kSkBN = 256;
 // of an m-tile reads them.
 constexpr int kCpolStream = 2;
 constexpr int kSkStages = 4;
-constexpr int kSkStageBytes = (kSkBM + kSkBN) * kRowBytes;  // 36 KB
 
 // Tile t of a skinny GEMM (t < m-tiles x nt_n): the m-tile table entry holds
 // the expert's first m-tile and m-tile count, and an expert's tiles run n-tile
@@ -608,9 +607,15 @@ __device__ __forceinline__ int4 skinny_decode(const GemmArgs& g, int t) {
   return make_int4(inf.x, mt, u / inf.z, inf.y + mt);
 }
 
-template <int MODE, int NW>
+template <int MODE, int NW, int BN>
 __device__ __forceinline__ void skinny_tile(const GemmArgs& g, int t, uint8_t* smem) {
   constexpr bool kSwiglu = MODE == MODE_SWIGLU || MODE == MODE_SWIGLU_FP8OUT;
+  static_assert(BN == kSkBN || (NW == 8 && MODE == MODE_PLAIN && (BN == 384 || BN == 512)),
+                "wider tiles: the plain (down) GEMM, eight waves");
+  // ring: four 36 KB stages (256 weight rows), three of 52 KB (384) or two of
+  // 68 KB (512)
+  constexpr int kStg = BN == 256 ? kSkStages : BN == 384 ? 3 : 2;
+  constexpr int kStageB = (kSkBM + BN) * kRowBytes;
   const int4 td = skinny_decode(g, t);
   const int e = td.x, mt = td.y, nt = td.z;
   const int2 sg = segment(g.seg, g.seg_cap, e);
@@ -621,14 +626,15 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& g, int t, uint8_t* s
   const int64_t a_skip = g.a_index ? 0 : static_cast<int64_t>(row0) * g.a_rs;
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(g.A + a_skip, g.a_bytes - a_skip);
   const __amdgpu_buffer_rsrc_t rW = make_rsrc(g.W + e * g.w_stride, g.w_stride);
-  const int nbase = kSwiglu ? nt * (kSkBN / 2) : nt * kSkBN;
+  const int nbase = kSwiglu ? nt * (kSkBN / 2) : nt * BN;
 
   const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // direct loads: waves 0-3 move A group w (8 of the 32 rows); wave w moves
   // W groups 4 + kWPer w .. 4 + kWPer (w + 1) - 1
-  constexpr int kWPer = kSkBN / 8 / NW;
-  const bool loads_a = w < kSkBM / 8, computes = w < 4;
-  const int wc = w & 3;  // the compute role (every wave's offsets stay in range)
+  constexpr int kWPer = BN / 8 / NW;
+  const bool loads_a = w < kSkBM / 8, computes = w < BN / 64;
+  const int wc = w & 3;                   // token row group
+  const int wr = min(w, BN / 64 - 1);     // the compute role (offsets stay in range)
   // (sized for four waves: an array bound that depends on NW trips the host
   // pass's check of the 16-byte direct load)
   int voff[1 + kSkBN / 8 / 4], ldst[1 + kSkBN / 8 / 4];
@@ -655,7 +661,7 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& g, int t, uint8_t* s
   }
   auto dma = [&](int step, int stage) {
     const int k = min(step, nk - 1);  // step k starts at 64-byte K piece 2k
-    uint8_t* base = smem + stage * kSkStageBytes;
+    uint8_t* base = smem + stage * kStageB;
     if (loads_a)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr_t)(base + ldst[0]), 16, voff[0],
                                                2 * k * g.a_cs, 0, 0);
@@ -665,7 +671,7 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& g, int t, uint8_t* s
                                                2 * k * g.w_cs, 0, kCpolStream);
   };
   // the wave's loads of kSkStages - 2 steps may stay in flight
-  constexpr int kLa = (kSkStages - 2) * (1 + kWPer), kLw = (kSkStages - 2) * kWPer;
+  constexpr int kLa = (kStg - 2) * (1 + kWPer), kLw = (kStg - 2) * kWPer;
 
   const int lr = lane & 31, hi = lane >> 5, sl = (lr >> 1) & 7;
   int foff[4];
@@ -674,7 +680,7 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& g, int t, uint8_t* s
   int wbase[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
-    wbase[i] = (kSkBM + (kSwiglu ? i * (kSkBN / 2) + wc * 32 : wc * 64 + i * 32)) * kRowBytes;
+    wbase[i] = (kSkBM + (kSwiglu ? i * (kSkBN / 2) + wr * 32 : wr * 64 + i * 32)) * kRowBytes;
 
   f32x16 acc[2];
 #pragma unroll
@@ -683,7 +689,7 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& g, int t, uint8_t* s
     for (int r = 0; r < 16; ++r) acc[i][r] = 0.0f;
 
 #pragma unroll
-  for (int st = 0; st < kSkStages - 1; ++st) dma(st, st);
+  for (int st = 0; st < kStg - 1; ++st) dma(st, st);
   if (loads_a)
     WAIT_VMCNT(kLa);
   else
@@ -692,8 +698,8 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& g, int t, uint8_t* s
 
   int s_cur = 0;
   for (int kt = 0; kt < nk; ++kt) {
-    const uint8_t* st = smem + s_cur * kSkStageBytes;
-    dma(kt + kSkStages - 1, s_cur == 0 ? kSkStages - 1 : s_cur - 1);
+    const uint8_t* st = smem + s_cur * kStageB;
+    dma(kt + kStg - 1, s_cur == 0 ? kStg - 1 : s_cur - 1);
     if (computes) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
@@ -710,7 +716,7 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& g, int t, uint8_t* s
     else
       WAIT_VMCNT_LDS(kLw);
     __builtin_amdgcn_s_barrier();
-    s_cur = s_cur + 1 == kSkStages ? 0 : s_cur + 1;
+    s_cur = s_cur + 1 == kStg ? 0 : s_cur + 1;
   }
   WAIT_VMCNT(0);
   if (!computes) return;  // the epilogue has no barrier
@@ -757,15 +763,19 @@ __device__ __forceinline__ void skinny_tile(const GemmArgs& g, int t, uint8_t* s
 // x token group scale).  Weight scales by scalar loads; the step's 32 token
 // scales travel with the operands.  The up tile's 128 h columns are one
 // quantisation group: the four waves exchange their row maxima in LDS and
-// write E4M3 codes and the group scale amax / 448.
+// write E4M3 codes and the group scale amax / 448.  Both skinny tiles also
+// come BN = 384 or 512 weight rows wide for the plain (down) GEMM: BN / 64
+// computing waves of eight, three 52 KB or two 68 KB stages.
 // ---------------------------------------------------------------------------
-constexpr int kF8sScaleOff = (kSkBM + kSkBN) * kRowBytes;   // token scales after the rows
-constexpr int kF8sStageBytes = kF8sScaleOff + 256;           // 32 floats, padded to a lane load
-static_assert(kSkStages * kF8sStageBytes <= 160 * 1024 - 1024, "the ring fits the CU's LDS");
 
-template <int MODE, int NW>
+template <int MODE, int NW, int BN>
 __device__ __forceinline__ void f8_skinny_tile(const GemmArgs& g, int t, uint8_t* smem) {
   constexpr bool kSwiglu = MODE == MODE_SWIGLU_FP8OUT;
+  static_assert(BN == kSkBN || (NW == 8 && MODE == MODE_PLAIN && (BN == 384 || BN == 512)),
+                "wider tiles: the plain (down) GEMM, eight waves");
+  constexpr int kStg = BN == 256 ? kSkStages : BN == 384 ? 3 : 2;
+  constexpr int kScaleOff = (kSkBM + BN) * kRowBytes;   // token scales after the rows
+  constexpr int kStageB = kScaleOff + 256;
   __shared__ float row_amax[4][kSkBM];
   const int4 td = skinny_decode(g, t);
   const int e = td.x, mt = td.y, nt = td.z;
@@ -783,15 +793,16 @@ __device__ __forceinline__ void f8_skinny_tile(const GemmArgs& g, int t, uint8_t
       g.a_index ? make_rsrc(g.A_scale, g.a_bytes / g.K * kb_n * 4)
                 : make_rsrc(g.A_scale + static_cast<int64_t>(row0) * kb_n,
                             static_cast<int64_t>(min(seg_end - row0, kSkBM)) * kb_n * 4);
-  const int nbase = kSwiglu ? nt * (kSkBN / 2) : nt * kSkBN;
+  const int nbase = kSwiglu ? nt * (kSkBN / 2) : nt * BN;
 
   const int lane = lane_id(), w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // direct loads: waves 0-3 move A group w (8 of the 32 rows), wave w W
   // groups 4 + kWPer w .. 4 + kWPer (w + 1) - 1, and every wave the step's
   // 32 token scales (the same values to the same place)
-  constexpr int kWPer = kSkBN / 8 / NW;
-  const bool loads_a = w < kSkBM / 8, computes = w < 4;
-  const int wc = w & 3;  // the compute role (every wave's offsets stay in range)
+  constexpr int kWPer = BN / 8 / NW;
+  const bool loads_a = w < kSkBM / 8, computes = w < BN / 64;
+  const int wc = w & 3;                   // token row group
+  const int wr = min(w, BN / 64 - 1);     // the compute role (offsets stay in range)
   // (sized for four waves: an array bound that depends on NW trips the host
   // pass's check of the 16-byte direct load)
   int voff[1 + kSkBN / 8 / 4], ldst[1 + kSkBN / 8 / 4];
@@ -823,7 +834,7 @@ __device__ __forceinline__ void f8_skinny_tile(const GemmArgs& g, int t, uint8_t
     // steps past the last one load nothing (out-of-range offsets)
     const bool live = step < nk;
     const int k = live ? step : 0;
-    uint8_t* base = smem + stage * kF8sStageBytes;
+    uint8_t* base = smem + stage * kStageB;
     if (loads_a)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr_t)(base + ldst[0]), 16,
                                                live ? voff[0] : kOobOffset, k * kRowBytes, 0, 0);
@@ -832,11 +843,11 @@ __device__ __forceinline__ void f8_skinny_tile(const GemmArgs& g, int t, uint8_t
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rW, (lds_ptr_t)(base + ldst[q]), 16,
                                                live ? voff[q] : kOobOffset, k * kRowBytes, 0,
                                                kCpolStream);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_ptr_t)(base + kF8sScaleOff), 4,
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_ptr_t)(base + kScaleOff), 4,
                                              live ? soff : kOobOffset, k * 4, 0, 0);
   };
   // the wave's loads of kSkStages - 2 steps may stay in flight
-  constexpr int kLa = (kSkStages - 2) * (2 + kWPer), kLw = (kSkStages - 2) * (1 + kWPer);
+  constexpr int kLa = (kStg - 2) * (2 + kWPer), kLw = (kStg - 2) * (1 + kWPer);
 
   // fragments: a lane holds 32 contiguous K bytes, [64 kk + 32 hi, +32), of
   // its row (chunks c and c ^ 1 after the swizzle); weight tiles i = 0, 1
@@ -854,7 +865,7 @@ __device__ __forceinline__ void f8_skinny_tile(const GemmArgs& g, int t, uint8_t
   const float* wsc = g.W_scale + e * g.ws_stride;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int lrow = kSwiglu ? i * (kSkBN / 2) + wc * 32 : wc * 64 + i * 32;
+    const int lrow = kSwiglu ? i * (kSkBN / 2) + wr * 32 : wr * 64 + i * 32;
     wbase[i] = (kSkBM + lrow) * kRowBytes;
     int grow;
     if (kSwiglu)
@@ -871,7 +882,7 @@ __device__ __forceinline__ void f8_skinny_tile(const GemmArgs& g, int t, uint8_t
     for (int r = 0; r < 16; ++r) acc[i][r] = 0.0f;
 
 #pragma unroll
-  for (int st = 0; st < kSkStages - 1; ++st) dma(st, st);
+  for (int st = 0; st < kStg - 1; ++st) dma(st, st);
   if (loads_a)
     WAIT_VMCNT(kLa);
   else
@@ -880,8 +891,8 @@ __device__ __forceinline__ void f8_skinny_tile(const GemmArgs& g, int t, uint8_t
 
   int s_cur = 0;
   for (int kt = 0; kt < nk; ++kt) {
-    const uint8_t* st = smem + s_cur * kF8sStageBytes;
-    dma(kt + kSkStages - 1, s_cur == 0 ? kSkStages - 1 : s_cur - 1);
+    const uint8_t* st = smem + s_cur * kStageB;
+    dma(kt + kStg - 1, s_cur == 0 ? kStg - 1 : s_cur - 1);
     if (computes) {
       // weight block scales through the constant address space (scalar loads,
       // outside the vector-memory wait count)
@@ -889,7 +900,7 @@ __device__ __forceinline__ void f8_skinny_tile(const GemmArgs& g, int t, uint8_t
 #pragma unroll
       for (int i = 0; i < 2; ++i)
         sw[i] = ((const __attribute__((address_space(4))) float*)(uintptr_t)swp[i])[kt];
-      const float sx = *reinterpret_cast<const float*>(st + kF8sScaleOff + lr * 4);
+      const float sx = *reinterpret_cast<const float*>(st + kScaleOff + lr * 4);
       f32x16 tmp[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -921,7 +932,7 @@ __device__ __forceinline__ void f8_skinny_tile(const GemmArgs& g, int t, uint8_t
     else
       WAIT_VMCNT_LDS(kLw);
     __builtin_amdgcn_s_barrier();
-    s_cur = s_cur + 1 == kSkStages ? 0 : s_cur + 1;
+    s_cur = s_cur + 1 == kStg ? 0 : s_cur + 1;
   }
   WAIT_VMCNT(0);
 
@@ -1563,6 +1574,17 @@ enum { kSkBf16 = 0, kSkMx = 1, kSkFp8 = 2 };
 // 0.211 ms, MXFP4 0.1345 -> 0.1336 ms, bf16 0.3778 -> 0.3789 ms; so the
 // load stream of these tiles is not bound by the waves that issue it.
 constexpr int sk_waves(int kind) { return kind == kSkBf16 ? 4 : 8; }
+// Weight rows of the bf16 and block-FP8 down GEMM's skinny tile (the up
+// GEMM's are 256).  Block-FP8 takes 384 (six computing waves, three 52 KB
+// stages: the same 96 KB in flight, a third fewer down tiles): DeepSeek-V3
+// decode FFN 0.2110 -> 0.2091 ms; 512 rows (two 68 KB stages, one step
+// ahead) 0.2177 ms.  bf16: 384 rows 0.3776 -> 0.3823 ms, 512 rows 0.4045 ms.
+constexpr int sk_down_bn(int kind) { return kind == kSkFp8 ? 384 : kSkBN; }
+// LDS ring of a bf16 / block-FP8 skinny tile with bn weight rows.
+constexpr size_t sk_ring(int bn, bool fp8) {
+  return static_cast<size_t>(bn == 256 ? kSkStages : bn == 384 ? 3 : 2) *
+         ((kSkBM + bn) * kRowBytes + (fp8 ? 256 : 0));
+}
 // Weight rows of the MX down GEMM's skinny tile (the up GEMM's are 256).
 constexpr int kMsDownBN = 512;
 template <int UPMODE, int KIND>
@@ -1583,9 +1605,9 @@ __global__ __launch_bounds__(64 * sk_waves(KIND), 1) void ffn_fused_skinny_kerne
     if constexpr (KIND == kSkMx)
       mx_skinny_tile<UPMODE, NW, 256>(gu, t, smem);
     else if constexpr (KIND == kSkFp8)
-      f8_skinny_tile<UPMODE, NW>(gu, t, smem);
+      f8_skinny_tile<UPMODE, NW, kSkBN>(gu, t, smem);
     else
-      skinny_tile<UPMODE, NW>(gu, t, smem);
+      skinny_tile<UPMODE, NW, kSkBN>(gu, t, smem);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -1616,19 +1638,21 @@ __global__ __launch_bounds__(64 * sk_waves(KIND), 1) void ffn_fused_skinny_kerne
   if constexpr (KIND == kSkMx)
     mx_skinny_tile<MODE_PLAIN, NW, kMsDownBN>(gd, td, smem);
   else if constexpr (KIND == kSkFp8)
-    f8_skinny_tile<MODE_PLAIN, NW>(gd, td, smem);
+    f8_skinny_tile<MODE_PLAIN, NW, sk_down_bn(kSkFp8)>(gd, td, smem);
   else
-    skinny_tile<MODE_PLAIN, NW>(gd, td, smem);
+    skinny_tile<MODE_PLAIN, NW, sk_down_bn(kSkBf16)>(gd, td, smem);
 }
 
 template <int UPMODE, int KIND>
 hipError_t launch_fused(const GemmArgs& gu, const GemmArgs& gd, int64_t max_tiles, int32_t* sync,
                         int32_t* status, hipStream_t s) {
-  static_assert(kSkStages * kSkStageBytes <= 160 * 1024, "the ring fits the CU's LDS");
+  static_assert(sk_ring(kSkBN, true) <= 160 * 1024 - 1024 &&
+                    sk_ring(sk_down_bn(KIND), KIND == kSkFp8) <= 160 * 1024 - 1024,
+                "the rings fit the CU's LDS");
   auto kern = ffn_fused_skinny_kernel<UPMODE, KIND>;
   const size_t lds = KIND == kSkMx    ? kMsRingBytes
-                     : KIND == kSkFp8 ? kSkStages * kF8sStageBytes
-                                      : kSkStages * kSkStageBytes;
+                     : std::max(sk_ring(kSkBN, KIND == kSkFp8),
+                                sk_ring(sk_down_bn(KIND), KIND == kSkFp8));
   static std::atomic<uint64_t> lds_set{0};
   allow_dynamic_lds(reinterpret_cast<const void*>(kern), static_cast<int>(lds), lds_set);
   const int64_t blocks = max_tiles * (gu.nt_n + gd.nt_n);
@@ -2855,7 +2879,8 @@ hipError_t launch_ffn_fused(const GemmLaunch& up, const GemmLaunch& down, int32_
     gd.nt_n = ceil_div(down.Nout, kMsDownBN);  // the down GEMM's wider tiles
     return launch_fused<MODE_SWIGLU_MX8OUT, kSkMx>(gu, gd, up.max_tiles, sync, status, s);
   }
-  if (up.fp8) {  // SwiGLU with block-FP8 h only
+  if (up.fp8) {
+    gd.nt_n = ceil_div(down.Nout, sk_down_bn(kSkFp8));  // the down GEMM's wider tiles  // SwiGLU with block-FP8 h only
     if (!up.swiglu || !up.C_scale) return hipErrorInvalidValue;
     return launch_fused<MODE_SWIGLU_FP8OUT, kSkFp8>(gu, gd, up.max_tiles, sync, status, s);
   }
